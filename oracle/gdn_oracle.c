@@ -1,0 +1,171 @@
+/*
+ * fp64 CPU oracle for causal linear attention in its gated delta-rule form (Gated DeltaNet)
+ * and for plain causal linear attention.
+ *
+ * TEST INFRASTRUCTURE ONLY. Only the tests, the smoke check and the benchmark's CPU-baseline
+ * leg may load this library. It shares no code, header, table or helper with the HIP library;
+ * the product path never calls it.
+ *
+ * What it computes (per batch b and head h independently, token by token, in fp64):
+ *
+ *   Gated delta rule. The state S is a Dv x Dk matrix (math orientation, S[j][i]).
+ *       S_t = a_t * S_{t-1} (I - beta_t k_t k_t^T) + beta_t v_t k_t^T,   a_t = exp(log_alpha_t)
+ *       o_t = S_t q_t
+ *   written out with the rank-1 product expanded, as the code below does:
+ *       s = S_{t-1} k_t;  S_t = a_t (S_{t-1} - beta_t s k_t^T) + beta_t v_t k_t^T.
+ *   The forget gate a_t multiplies the decayed old state only, not the new write.
+ *
+ *   Plain causal linear attention (the alpha = 1 case with no delta term), the update printed
+ *   in the AI RnD Day channel post (tgstat.ru, section "Linear attention"):
+ *       S_t = S_{t-1} + v_t k_t^T,   o_t = S_t q_t.
+ *   The output uses the state that already contains token t (inclusive causality) and no
+ *   softmax scale or normaliser is applied.
+ *
+ *   Decode step: the gated delta-rule update above applied once to a stored state.
+ *
+ * Storage orientation. Initial, final and decode states are stored key-major: element
+ * [i][j] of a [Dk][Dv] block equals S[j][i]. This matches the chunk-level map S -> A S + B of
+ * the SparseGDN article's skip-scan illustration (fileenergy.com, section on embedding the
+ * selector into an FLA pipeline), with the state's key dimension as the row index.
+ *
+ * Layouts (all row-major, fp64):
+ *   q, k [B,H,L,Dk]; v, o [B,H,L,Dv]; beta, log_alpha [B,H,L]; h0, h_final [B,H,Dk,Dv].
+ *   h0 == NULL means a zero initial state.
+ * nthreads <= 0 uses the OpenMP default. Returns the number of threads used.
+ */
+#include <math.h>
+#include <stdlib.h>
+#include <string.h>
+#ifdef _OPENMP
+#include <omp.h>
+#endif
+
+static int set_threads(int nthreads)
+{
+#ifdef _OPENMP
+    if (nthreads > 0) omp_set_num_threads(nthreads);
+    return omp_get_max_threads();
+#else
+    (void)nthreads;
+    return 1;
+#endif
+}
+
+/* S (Dv x Dk) <- key-major block X (Dk x Dv), or zeros. */
+static void load_state(double *S, const double *X, int Dk, int Dv)
+{
+    for (int j = 0; j < Dv; ++j)
+        for (int i = 0; i < Dk; ++i)
+            S[(size_t)j * Dk + i] = X ? X[(size_t)i * Dv + j] : 0.0;
+}
+
+static void store_state(double *X, const double *S, int Dk, int Dv)
+{
+    for (int i = 0; i < Dk; ++i)
+        for (int j = 0; j < Dv; ++j)
+            X[(size_t)i * Dv + j] = S[(size_t)j * Dk + i];
+}
+
+/* o = S q */
+static void read_out(double *o, const double *S, const double *q, int Dk, int Dv)
+{
+    for (int j = 0; j < Dv; ++j) {
+        double acc = 0.0;
+        const double *row = S + (size_t)j * Dk;
+        for (int i = 0; i < Dk; ++i) acc += row[i] * q[i];
+        o[j] = acc;
+    }
+}
+
+/* One gated delta-rule token: S <- a (S - beta (S k) k^T) + beta v k^T. `sk` is scratch (Dv). */
+static void gdn_token(double *S, double *sk, const double *k, const double *v,
+                      double beta, double log_alpha, int Dk, int Dv)
+{
+    const double a = exp(log_alpha);
+    for (int j = 0; j < Dv; ++j) {
+        double acc = 0.0;
+        const double *row = S + (size_t)j * Dk;
+        for (int i = 0; i < Dk; ++i) acc += row[i] * k[i];
+        sk[j] = acc;
+    }
+    for (int j = 0; j < Dv; ++j) {
+        double *row = S + (size_t)j * Dk;
+        const double dj = beta * sk[j];
+        const double wj = beta * v[j];
+        for (int i = 0; i < Dk; ++i) row[i] = a * (row[i] - dj * k[i]) + wj * k[i];
+    }
+}
+
+/* One plain linear-attention token: S <- S + v k^T. */
+static void la_token(double *S, const double *k, const double *v, int Dk, int Dv)
+{
+    for (int j = 0; j < Dv; ++j) {
+        double *row = S + (size_t)j * Dk;
+        for (int i = 0; i < Dk; ++i) row[i] += v[j] * k[i];
+    }
+}
+
+int oracle_gdn_prefill(const double *q, const double *k, const double *v,
+                       const double *beta, const double *log_alpha, const double *h0,
+                       double *o, double *h_final,
+                       int B, int H, int L, int Dk, int Dv, int nthreads)
+{
+    const int used = set_threads(nthreads);
+    const long nslice = (long)B * H;
+#pragma omp parallel for schedule(dynamic, 1)
+    for (long s = 0; s < nslice; ++s) {
+        double *S = (double *)malloc(sizeof(double) * ((size_t)Dk * Dv + Dv));
+        double *sk = S + (size_t)Dk * Dv;
+        load_state(S, h0 ? h0 + (size_t)s * Dk * Dv : NULL, Dk, Dv);
+        for (int t = 0; t < L; ++t) {
+            const size_t tok = (size_t)s * L + t;
+            gdn_token(S, sk, k + tok * Dk, v + tok * Dv, beta[tok], log_alpha[tok], Dk, Dv);
+            read_out(o + tok * Dv, S, q + tok * Dk, Dk, Dv);
+        }
+        store_state(h_final + (size_t)s * Dk * Dv, S, Dk, Dv);
+        free(S);
+    }
+    return used;
+}
+
+int oracle_linattn_prefill(const double *q, const double *k, const double *v, const double *h0,
+                           double *o, double *h_final,
+                           int B, int H, int L, int Dk, int Dv, int nthreads)
+{
+    const int used = set_threads(nthreads);
+    const long nslice = (long)B * H;
+#pragma omp parallel for schedule(dynamic, 1)
+    for (long s = 0; s < nslice; ++s) {
+        double *S = (double *)malloc(sizeof(double) * (size_t)Dk * Dv);
+        load_state(S, h0 ? h0 + (size_t)s * Dk * Dv : NULL, Dk, Dv);
+        for (int t = 0; t < L; ++t) {
+            const size_t tok = (size_t)s * L + t;
+            la_token(S, k + tok * Dk, v + tok * Dv, Dk, Dv);
+            read_out(o + tok * Dv, S, q + tok * Dk, Dk, Dv);
+        }
+        store_state(h_final + (size_t)s * Dk * Dv, S, Dk, Dv);
+        free(S);
+    }
+    return used;
+}
+
+/* Decode: q,k [N,H,Dk]; v, o [N,H,Dv]; beta, log_alpha [N,H]; state [N,H,Dk,Dv] updated in place. */
+int oracle_gdn_decode_step(const double *q, const double *k, const double *v,
+                           const double *beta, const double *log_alpha, double *state,
+                           double *o, int N, int H, int Dk, int Dv, int nthreads)
+{
+    const int used = set_threads(nthreads);
+    const long nslice = (long)N * H;
+#pragma omp parallel for schedule(static)
+    for (long s = 0; s < nslice; ++s) {
+        double *S = (double *)malloc(sizeof(double) * ((size_t)Dk * Dv + Dv));
+        double *sk = S + (size_t)Dk * Dv;
+        double *st = state + (size_t)s * Dk * Dv;
+        load_state(S, st, Dk, Dv);
+        gdn_token(S, sk, k + (size_t)s * Dk, v + (size_t)s * Dv, beta[s], log_alpha[s], Dk, Dv);
+        read_out(o + (size_t)s * Dv, S, q + (size_t)s * Dk, Dk, Dv);
+        store_state(st, S, Dk, Dv);
+        free(S);
+    }
+    return used;
+}
