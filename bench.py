@@ -1,0 +1,268 @@
+#!/usr/bin/env python3
+"""Benchmark of the gated delta-rule hot path on one MI355X.
+
+A step is one chunked GDN prefill of the long-context workload (B=1, H=16, L=131072, d=128,
+chunk 64: bf16 q/k/v, fp32 gates and state) through the C ABI, inputs resident in HBM. The JSON
+line also carries the decode step (256 sequences x 32 heads, 100 in-place steps, state GB/s),
+plain causal linear attention (B=4, H=16, L=8192) and the 32K GDN workload as components, the
+roofline of the prefill, and the fp64 oracle timed on this host's cores on a bounded sample.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W]
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+from gated_deltanet_chunked_rule_amd import inputs  # noqa: E402
+
+PEAK_HBM_GBPS = 8000.0          # MI355X HBM3E
+PEAK_BF16_TFLOPS = 2500.0       # MI355X dense bf16 MFMA
+METRIC = "GDN prefill tokens/s at L=128K + % bf16 MFMA peak; decode state GB/s"
+
+
+# ---------------------------------------------------------------------------------------------
+# algorithmic work (what the method must compute / move), per workload
+# ---------------------------------------------------------------------------------------------
+def gdn_flops_per_chunk(C=64, d=128):
+    """Triangles counted exactly: 3 state GEMMs (W H, e^g Q H, Khat^T U), K K^T strictly lower,
+    Q K^T lower, T (beta e^g K), T (beta V), P U, and the triangular inverse."""
+    return (6 * C * d * d + C * (C - 1) * d + C * (C + 1) * d + C * (C - 1) * d + C * (C - 1) * d
+            + C * (C + 1) * d + C ** 3 / 3)
+
+
+def linattn_flops_per_chunk(C=64, d=128):
+    return 4 * C * d * d + 2 * C * (C + 1) * d
+
+
+def prefill_bytes(cfg, gates=True):
+    tok = cfg.B * cfg.H * cfg.L
+    e = 2 if cfg.dtype == "bf16" else 4
+    b = 3 * tok * cfg.Dk * e + tok * cfg.Dv * e          # q, k, v in; o out
+    if gates:
+        b += 2 * tok * 4                                   # beta, log_alpha
+    st = cfg.B * cfg.H * cfg.Dk * cfg.Dv * 4
+    b += st + (st if cfg.h0 is not None else 0)            # h_final out, h0 in
+    return b
+
+
+def decode_bytes(cfg):
+    S = cfg.N * cfg.H
+    e = 2 if cfg.dtype == "bf16" else 4
+    state = S * cfg.Dk * cfg.Dv * 4
+    return 2 * state + S * (2 * cfg.Dk + 2 * cfg.Dv) * e + 2 * S * 4, 2 * state
+
+
+# ---------------------------------------------------------------------------------------------
+# device inputs
+# ---------------------------------------------------------------------------------------------
+def to_dev(torch, x, dtype):
+    return torch.from_numpy(np.ascontiguousarray(x, dtype=np.float32)).to("cuda").to(dtype)
+
+
+def prefill_device_inputs(torch, cfg, gates=True):
+    dt = torch.bfloat16 if cfg.dtype == "bf16" else torch.float32
+    shp = (cfg.B, cfg.H, cfg.L)
+    q = torch.empty(shp + (cfg.Dk,), dtype=dt, device="cuda")
+    k, v = torch.empty_like(q), torch.empty_like(q)
+    beta = torch.empty(shp, device="cuda") if gates else None
+    la = torch.empty(shp, device="cuda") if gates else None
+    h0 = torch.empty((cfg.B, cfg.H, cfg.Dk, cfg.Dv), device="cuda") if cfg.h0 is not None else None
+    for b in range(cfg.B):
+        for h in range(cfg.H):
+            s = inputs.prefill_slice(cfg, b, h)
+            for name, t in (("q", q), ("k", k), ("v", v), ("beta", beta), ("log_alpha", la), ("h0", h0)):
+                if t is not None:
+                    t[b, h] = to_dev(torch, s[name], t.dtype)
+    return q, k, v, beta, la, h0
+
+
+def time_loop(torch, fn, steps, warmup):
+    for _ in range(warmup):
+        fn()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t0 = time.perf_counter()
+    e0.record()
+    for _ in range(steps):
+        fn()
+    e1.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    return e0.elapsed_time(e1) / steps, wall
+
+
+# ---------------------------------------------------------------------------------------------
+# components
+# ---------------------------------------------------------------------------------------------
+def bench_prefill(torch, ops, cfg, steps, warmup, gdn=True):
+    q, k, v, beta, la, h0 = prefill_device_inputs(torch, cfg, gates=gdn)
+    o = torch.empty_like(v)
+    hf = torch.empty((cfg.B, cfg.H, cfg.Dk, cfg.Dv), device="cuda")
+    ws = torch.empty(ops.prefill_workspace_size(cfg.B, cfg.H, cfg.L, cfg.Dk, q.dtype), dtype=torch.uint8,
+                     device="cuda")
+    if gdn:
+        fn = lambda: ops.gdn_prefill_fwd(q, k, v, beta, la, h0, o=o, h_final=hf, workspace=ws)
+    else:
+        fn = lambda: ops.linattn_prefill_fwd(q, k, v, h0, o=o, h_final=hf, workspace=ws)
+    ms, wall = time_loop(torch, fn, steps, warmup)
+    nchunk = cfg.B * cfg.H * ((cfg.L + 63) // 64)
+    flops = nchunk * (gdn_flops_per_chunk(64, cfg.Dk) if gdn else linattn_flops_per_chunk(64, cfg.Dk))
+    nbytes = prefill_bytes(cfg, gates=gdn)
+    res = {
+        "workload": cfg.name, "ms": ms, "tokens_per_s": cfg.B * cfg.L / (ms * 1e-3),
+        "alg_tflops": flops / (ms * 1e-3) / 1e12, "mfma_frac": flops / (ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS,
+        "alg_bytes": nbytes, "hbm_GBps": nbytes / (ms * 1e-3) / 1e9,
+        "hbm_frac": nbytes / (ms * 1e-3) / 1e9 / PEAK_HBM_GBPS, "wall_s": wall,
+    }
+    return res, (q, k, v, beta, la, h0, o, hf)
+
+
+def bench_decode(torch, ops, cfg, steps):
+    dt = torch.bfloat16 if cfg.dtype == "bf16" else torch.float32
+    state = to_dev(torch, inputs.decode_state(cfg), torch.float32)
+    toks = []
+    for s in range(steps):
+        x = inputs.decode_token(cfg, s)
+        toks.append([to_dev(torch, x[n], dt) for n in ("q", "k", "v")]
+                    + [to_dev(torch, x[n], torch.float32) for n in ("beta", "log_alpha")])
+    o = torch.empty_like(toks[0][2])
+    ops.gdn_decode_step(*toks[0], state, o=o)        # warm-up (the state keeps evolving in place)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for s in range(steps):
+        ops.gdn_decode_step(*toks[s], state, o=o)
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / steps
+    total, st_bytes = decode_bytes(cfg)
+    return {"workload": cfg.name, "steps": steps, "ms_per_step": ms,
+            "tokens_per_s": cfg.N / (ms * 1e-3), "state_GBps": st_bytes / (ms * 1e-3) / 1e9,
+            "hbm_GBps": total / (ms * 1e-3) / 1e9, "hbm_frac": total / (ms * 1e-3) / 1e9 / PEAK_HBM_GBPS}
+
+
+def cpu_baseline(cfg, target_s, gpu_out=None):
+    """The fp64 oracle on this host, all heads of the workload over its first L_s tokens, with
+    L_s calibrated so the run takes about `target_s` seconds."""
+    import oracle
+    threads = min(os.cpu_count() or 1, 16, cfg.B * cfg.H)
+
+    def sample(L):
+        sl = [inputs.prefill_slice(cfg, 0, h, L) for h in range(cfg.H)]
+        st = lambda key: np.stack([s[key] for s in sl])[None]
+        return st("q"), st("k"), st("v"), st("beta"), st("log_alpha"), st("h0")
+
+    L = 1024
+    x = sample(L)
+    t0 = time.perf_counter()
+    oracle.gdn_prefill(*x, nthreads=threads)
+    t = time.perf_counter() - t0
+    L = int(min(cfg.L, max(1024, (target_s / max(t, 1e-3)) * L)) // 1024 * 1024)
+    x = sample(L)
+    t0 = time.perf_counter()
+    ro, rh = oracle.gdn_prefill(*x, nthreads=threads)
+    t = time.perf_counter() - t0
+    used = oracle.last_threads
+    out = {"value": cfg.B * L / t, "unit": "tokens/s", "cores": used, "kind": "oracle",
+           "sample": f"{cfg.name}: all {cfg.H} heads, first {L} of {cfg.L} tokens, fp64 token recurrence, "
+                     f"{used} OpenMP threads, {t:.1f} s"}
+    parity = None
+    if gpu_out is not None:
+        o = gpu_out[0, :, :L].float().cpu().numpy()
+        err = np.abs(o - ro[0]).max(axis=(1, 2)) / np.abs(ro[0]).max(axis=(1, 2))
+        parity = {"max_rel_err_o": float(err.max()), "sample": f"first {L} tokens of all heads"}
+    return out, parity
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--no-components", action="store_true", help="time only the 128K prefill")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=15.0)
+    ap.add_argument("--profile-steps", type=int, default=0,
+                    help="only run this many prefill steps after warm-up (for profilers), no JSON")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print("bench.py measures one GPU: this build has no multi-GPU path (heads and sequences shard "
+              "across GPUs with no communication; see the design notes). Run with --gpus 1.", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    from gated_deltanet_chunked_rule_amd import ops
+    torch.cuda.set_device(0)
+    log = lambda m: print(m, file=sys.stderr, flush=True)
+
+    cfg = inputs.GDN_128K
+    if args.profile_steps:
+        log("generating inputs")
+        res, bufs = bench_prefill(torch, ops, cfg, args.profile_steps, args.warmup)
+        log(f"profiled {args.profile_steps} steps: {res['ms']:.3f} ms/step")
+        return
+
+    log(f"[bench] {cfg.name}: generating inputs")
+    res, bufs = bench_prefill(torch, ops, cfg, args.steps, args.warmup)
+    log(f"[bench] {cfg.name}: {res['ms']:.3f} ms/step, {res['tokens_per_s']:.3e} tokens/s")
+    gpu_o = bufs[6]
+
+    components = {}
+    if not args.no_components:
+        del bufs
+        torch.cuda.empty_cache()
+        log("[bench] decode")
+        components["decode"] = bench_decode(torch, ops, inputs.DECODE_256x32, inputs.DECODE_256x32.steps)
+        log(f"[bench] decode: {components['decode']['ms_per_step']:.4f} ms/step")
+        log("[bench] linear attention")
+        r, b = bench_prefill(torch, ops, inputs.LINATTN_8K, max(5, args.steps // 2), 2, gdn=False)
+        components["linattn"] = r
+        del b
+        log("[bench] gdn 32K")
+        r, b = bench_prefill(torch, ops, inputs.GDN_32K, max(5, args.steps // 2), 2)
+        components["gdn_32k"] = r
+        del b
+
+    cpu, parity = (None, None)
+    if not args.no_cpu_baseline:
+        log("[bench] cpu baseline (fp64 oracle)")
+        cpu, parity = cpu_baseline(cfg, args.cpu_seconds, gpu_out=gpu_o)
+
+    line = {
+        "metric": METRIC,
+        "value": res["tokens_per_s"],
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": res["ms"],
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic (seeded; q,k L2-normalised N(0,1), v N(0,1), beta=sigmoid(N), "
+                "log a=-softplus(N+2), h0 N(0,0.01))",
+        "config": {"workload": "gdn_prefill_B1_H16_L131072_d128_chunk64", "B": cfg.B, "H": cfg.H,
+                   "L": cfg.L, "d_k": cfg.Dk, "d_v": cfg.Dv, "chunk": 64, "qkv": "bf16", "gates_state": "fp32"},
+        "mfma": {"alg_tflops": res["alg_tflops"], "peak_tflops": PEAK_BF16_TFLOPS, "frac": res["mfma_frac"]},
+        "roofline": {"bound": "hbm", "kernel": "gdn_prefill_fwd (prep, chain, output launches)",
+                     "achieved": res["hbm_GBps"], "peak": PEAK_HBM_GBPS, "unit": "GB/s",
+                     "frac": res["hbm_frac"], "traffic": None, "alg_bytes_per_launch": res["alg_bytes"]},
+        "cpu_baseline": cpu,
+        "parity_sample": parity,
+        "components": components,
+    }
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

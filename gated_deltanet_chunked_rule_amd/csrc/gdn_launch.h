@@ -1,0 +1,17 @@
+// Kernel launchers behind the C ABI (internal to libgdn; arguments are validated by the caller).
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+
+namespace gdn {
+
+int launch_decode(const void* q, const void* k, const void* v, const float* beta, const float* log_alpha,
+                  float* state, void* o, long slices, int D, int dtype, hipStream_t stream);
+
+size_t prefill_workspace_bytes(long BH, long L, int D, int dtype);
+
+int launch_prefill(const void* q, const void* k, const void* v, const float* beta, const float* log_alpha,
+                   const float* h0, void* o, float* h_final, int BH, long L, int D, int dtype, bool delta,
+                   void* ws, hipStream_t stream);
+
+}  // namespace gdn

@@ -1,0 +1,126 @@
+// MFMA fragment conventions for the gfx950 prefill kernels.
+//
+// A "fragment" is one 16-byte register quad per lane of a 64-lane wave (1 KB per wave) holding
+// a 16 x KB operand block of v_mfma_f32_16x16x32_bf16 (KB = 32) or of four chained
+// v_mfma_f32_16x16x4_f32 (KB = 16). Lane l = 16 j + m holds row m (A operand) or column m
+// (B operand) and the KB/4 k-indices kofs(j, e), e = 0 .. KB/4 - 1.
+//
+// The k-order is chosen so that the fp32 accumulator of a 16 x 16 MFMA tile (lane 16 j + n
+// holds rows 4 j .. 4 j + 3 of column n) converts to an operand fragment in registers with no
+// data movement: for bf16 a fragment packs two row-adjacent accumulator tiles, for fp32 one.
+// Because the hardware pairs element e of A's lane (j, m) with element e of B's lane (j, n),
+// any k-order gives the exact product as long as both operands use the same one.
+#pragma once
+#include "gdn_device.h"
+
+namespace gdn {
+
+constexpr int CH = 64;  // chunk length in tokens
+
+template <class E>
+struct MM;
+
+template <>
+struct MM<BF16> {
+    static constexpr int KB = 32;  // k extent of one fragment
+    static constexpr int EPF = 8;  // elements per lane
+    using frag = bf16x8;
+    static __device__ __forceinline__ f32x4 mma(const frag& a, const frag& b, f32x4 c) {
+        return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+    }
+    // k offset (within the fragment's KB-block) of element e held by lane group j
+    static __device__ __forceinline__ int kofs(int j, int e) { return e < 4 ? 4 * j + e : 12 + 4 * j + e; }
+    static __device__ __forceinline__ frag pack(const float (&x)[8]) {
+        frag f;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) f[e] = (short)f2bf(x[e]);
+        return f;
+    }
+    // fragment of k-block kb from accumulator tiles t[2 kb], t[2 kb + 1], times s
+    static __device__ __forceinline__ frag from_acc(const f32x4* t, int kb, float s = 1.f) {
+        const float x[8] = {t[2 * kb][0] * s, t[2 * kb][1] * s, t[2 * kb][2] * s, t[2 * kb][3] * s,
+                            t[2 * kb + 1][0] * s, t[2 * kb + 1][1] * s, t[2 * kb + 1][2] * s, t[2 * kb + 1][3] * s};
+        return pack(x);
+    }
+};
+
+template <>
+struct MM<F32> {
+    static constexpr int KB = 16;
+    static constexpr int EPF = 4;
+    using frag = f32x4;
+    static __device__ __forceinline__ f32x4 mma(const frag& a, const frag& b, f32x4 c) {
+        c = __builtin_amdgcn_mfma_f32_16x16x4f32(a[0], b[0], c, 0, 0, 0);
+        c = __builtin_amdgcn_mfma_f32_16x16x4f32(a[1], b[1], c, 0, 0, 0);
+        c = __builtin_amdgcn_mfma_f32_16x16x4f32(a[2], b[2], c, 0, 0, 0);
+        c = __builtin_amdgcn_mfma_f32_16x16x4f32(a[3], b[3], c, 0, 0, 0);
+        return c;
+    }
+    static __device__ __forceinline__ int kofs(int j, int e) { return 4 * j + e; }
+    static __device__ __forceinline__ frag pack(const float (&x)[4]) { return frag{x[0], x[1], x[2], x[3]}; }
+    static __device__ __forceinline__ frag from_acc(const f32x4* t, int kb, float s = 1.f) {
+        return frag{t[kb][0] * s, t[kb][1] * s, t[kb][2] * s, t[kb][3] * s};
+    }
+};
+
+// 16-byte fragment store / load (lane-contiguous, 1 KB per fragment)
+template <class F>
+__device__ __forceinline__ void st_frag(void* base, int lane, const F& f) {
+    *reinterpret_cast<F*>(static_cast<char*>(base) + lane * 16) = f;
+}
+template <class F>
+__device__ __forceinline__ F ld_frag(const void* base, int lane) {
+    return *reinterpret_cast<const F*>(static_cast<const char*>(base) + lane * 16);
+}
+
+// Fragment whose lane (j, m) takes row `rp` (row m of the operand, k contiguous in memory)
+// at k = k0 + kofs(j, e), every element multiplied by `s`. rp == nullptr gives zeros.
+template <class E>
+__device__ __forceinline__ typename MM<E>::frag row_frag(const typename E::T* rp, int k0, int j, float s) {
+    using M = MM<E>;
+    float x[M::EPF];
+    if (rp) {
+        const float4 a = load4(rp + k0 + 4 * j);
+        x[0] = a.x * s; x[1] = a.y * s; x[2] = a.z * s; x[3] = a.w * s;
+        if constexpr (M::EPF == 8) {
+            const float4 b = load4(rp + k0 + 16 + 4 * j);
+            x[4] = b.x * s; x[5] = b.y * s; x[6] = b.z * s; x[7] = b.w * s;
+        }
+    } else {
+#pragma unroll
+        for (int e = 0; e < M::EPF; ++e) x[e] = 0.f;
+    }
+    return M::pack(x);
+}
+
+// Same, with a per-k scale sk[k] (k = k0 + kofs(j, e)) instead of one scalar.
+template <class E>
+__device__ __forceinline__ typename MM<E>::frag row_frag_ks(const typename E::T* rp, int k0, int j, const float* sk) {
+    using M = MM<E>;
+    float x[M::EPF];
+    const float4 a = load4(rp + k0 + 4 * j);
+    const float4 sa = *reinterpret_cast<const float4*>(sk + k0 + 4 * j);
+    x[0] = a.x * sa.x; x[1] = a.y * sa.y; x[2] = a.z * sa.z; x[3] = a.w * sa.w;
+    if constexpr (M::EPF == 8) {
+        const float4 b = load4(rp + k0 + 16 + 4 * j);
+        const float4 sb = *reinterpret_cast<const float4*>(sk + k0 + 16 + 4 * j);
+        x[4] = b.x * sb.x; x[5] = b.y * sb.y; x[6] = b.z * sb.z; x[7] = b.w * sb.w;
+    }
+    return M::pack(x);
+}
+
+// Fragment from an fp32 row (LDS) at k = k0 + kofs(j, e).
+template <class E>
+__device__ __forceinline__ typename MM<E>::frag row_frag_f32(const float* rp, int k0, int j) {
+    using M = MM<E>;
+    float x[M::EPF];
+    const float4 a = *reinterpret_cast<const float4*>(rp + k0 + 4 * j);
+    x[0] = a.x; x[1] = a.y; x[2] = a.z; x[3] = a.w;
+    if constexpr (M::EPF == 8) {
+        const float4 b = *reinterpret_cast<const float4*>(rp + k0 + 16 + 4 * j);
+        x[4] = b.x; x[5] = b.y; x[6] = b.z; x[7] = b.w;
+    }
+    return M::pack(x);
+}
+
+}  // namespace gdn

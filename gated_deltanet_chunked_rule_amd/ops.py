@@ -1,0 +1,115 @@
+"""PyTorch-facing wrappers of the C ABI (include/gdn.h).
+
+PyTorch supplies device memory and the current stream; every step of the computation runs in
+libgdn's HIP kernels. These functions only check tensors and pass pointers. There is no CPU or
+PyTorch fallback: if libgdn.so is missing or the device is not gfx950 they raise.
+
+Layouts (row-major, contiguous):
+    q, k [B,H,L,D]; v, o [B,H,L,D]; beta, log_alpha [B,H,L] fp32; h0, h_final [B,H,D,D] fp32,
+    key-major (element [i][j] is S[j][i]). Decode: q, k, v, o [N,H,D]; beta, log_alpha [N,H];
+    state [N,H,D,D] fp32 updated in place.
+"""
+from __future__ import annotations
+
+from typing import Optional, Tuple
+
+import torch
+
+from . import _lib
+
+_DT = {torch.bfloat16: _lib.GDN_BF16, torch.float32: _lib.GDN_F32}
+
+
+def _code(dtype: torch.dtype) -> int:
+    if dtype not in _DT:
+        raise TypeError(f"q/k/v must be bfloat16 or float32, got {dtype}")
+    return _DT[dtype]
+
+
+def _req(name, t, shape, dtype, device):
+    if t is None:
+        raise ValueError(f"{name} is required")
+    if not t.is_cuda or t.device != device:
+        raise ValueError(f"{name} must be on {device}")
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} has shape {tuple(t.shape)}, expected {tuple(shape)}")
+    if t.dtype != dtype:
+        raise TypeError(f"{name} has dtype {t.dtype}, expected {dtype}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    return t
+
+
+def _p(t) -> Optional[int]:
+    return None if t is None else t.data_ptr()
+
+
+def _stream(device, stream) -> int:
+    s = torch.cuda.current_stream(device) if stream is None else stream
+    return s.cuda_stream
+
+
+def prefill_workspace_size(B: int, H: int, L: int, D: int, dtype: torch.dtype) -> int:
+    return int(_lib.load().gdn_prefill_workspace_size(B, H, L, D, D, _code(dtype)))
+
+
+def _prefill(entry, q, k, v, beta, log_alpha, h0, o, h_final, workspace, stream, delta):
+    B, H, L, D = q.shape
+    dev, dt = q.device, q.dtype
+    _req("q", q, (B, H, L, D), dt, dev)
+    _req("k", k, (B, H, L, D), dt, dev)
+    _req("v", v, (B, H, L, D), dt, dev)
+    if delta:
+        _req("beta", beta, (B, H, L), torch.float32, dev)
+        _req("log_alpha", log_alpha, (B, H, L), torch.float32, dev)
+    if h0 is not None:
+        _req("h0", h0, (B, H, D, D), torch.float32, dev)
+    o = torch.empty_like(v) if o is None else _req("o", o, (B, H, L, D), dt, dev)
+    if h_final is None:
+        h_final = torch.empty((B, H, D, D), dtype=torch.float32, device=dev)
+    _req("h_final", h_final, (B, H, D, D), torch.float32, dev)
+    need = prefill_workspace_size(B, H, L, D, dt)
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
+    elif workspace.numel() * workspace.element_size() < need:
+        raise ValueError(f"workspace has {workspace.numel() * workspace.element_size()} bytes, needs {need}")
+    lib = _lib.load()
+    rc = getattr(lib, entry)(_p(q), _p(k), _p(v), _p(beta), _p(log_alpha), _p(h0), _p(o), _p(h_final),
+                             B, H, L, D, D, _code(dt), _p(workspace),
+                             workspace.numel() * workspace.element_size(), _stream(dev, stream))
+    _lib.check(rc, entry)
+    return o, h_final
+
+
+def gdn_prefill_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, beta: torch.Tensor,
+                    log_alpha: torch.Tensor, h0: Optional[torch.Tensor] = None, *,
+                    o: Optional[torch.Tensor] = None, h_final: Optional[torch.Tensor] = None,
+                    workspace: Optional[torch.Tensor] = None, stream=None) -> Tuple[torch.Tensor, torch.Tensor]:
+    """Chunked gated delta-rule prefill. Returns (o, h_final)."""
+    return _prefill("gdn_prefill_fwd", q, k, v, beta, log_alpha, h0, o, h_final, workspace, stream, True)
+
+
+def linattn_prefill_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, h0: Optional[torch.Tensor] = None, *,
+                        o: Optional[torch.Tensor] = None, h_final: Optional[torch.Tensor] = None,
+                        workspace: Optional[torch.Tensor] = None, stream=None) -> Tuple[torch.Tensor, torch.Tensor]:
+    """Chunked plain causal linear attention (S_t = S_{t-1} + v_t k_t^T). Returns (o, h_final)."""
+    return _prefill("linattn_prefill_fwd", q, k, v, None, None, h0, o, h_final, workspace, stream, False)
+
+
+def gdn_decode_step(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, beta: torch.Tensor,
+                    log_alpha: torch.Tensor, state: torch.Tensor, *, o: Optional[torch.Tensor] = None,
+                    stream=None) -> torch.Tensor:
+    """One decode token per (sequence, head); `state` is updated in place. Returns o."""
+    N, H, D = q.shape
+    dev, dt = q.device, q.dtype
+    _req("q", q, (N, H, D), dt, dev)
+    _req("k", k, (N, H, D), dt, dev)
+    _req("v", v, (N, H, D), dt, dev)
+    _req("beta", beta, (N, H), torch.float32, dev)
+    _req("log_alpha", log_alpha, (N, H), torch.float32, dev)
+    _req("state", state, (N, H, D, D), torch.float32, dev)
+    o = torch.empty_like(v) if o is None else _req("o", o, (N, H, D), dt, dev)
+    rc = _lib.load().gdn_decode_step(_p(q), _p(k), _p(v), _p(beta), _p(log_alpha), _p(state), _p(o),
+                                     N, H, D, D, _code(dt), _stream(dev, stream))
+    _lib.check(rc, "gdn_decode_step")
+    return o

@@ -1,0 +1,110 @@
+/*
+ * gdn.h - C ABI of libgdn.so: causal linear attention in its gated delta-rule form
+ * (Gated DeltaNet) and plain causal linear attention, as hand-written HIP for gfx950.
+ *
+ * The operations (per batch b and head h, state S a Dv x Dk matrix, t = 1..L):
+ *
+ *   gated delta rule   S_t = a_t S_{t-1} (I - beta_t k_t k_t^T) + beta_t v_t k_t^T,
+ *                      o_t = S_t q_t,  a_t = exp(log_alpha_t).
+ *       Gated DeltaNet is the layer the forpes.ru GigaChat linearisation article names among
+ *       linear-attention variants (section "Overview") and whose prefill the SparseGDN article
+ *       (fileenergy.com) analyses. Its prefill here is chunked exactly as that article's
+ *       section "Why GDN prefill is expensive" describes: an intra-chunk delta-system solve, a
+ *       sequential pass over chunks for each head, and outputs from each chunk's start state.
+ *   plain linear attn  S_t = S_{t-1} + v_t k_t^T, o_t = S_t q_t  (AI RnD Day channel post,
+ *       tgstat.ru, section "Linear attention"; the associativity trick of the datadaily.news
+ *       overview, section "Linear attention").
+ *   decode step        one token of the gated delta rule applied to a stored state in place
+ *       (constant work per generated token, AI RnD Day post, section "Linear attention").
+ *
+ * Conventions shared by every entry point
+ *   - All tensor pointers are DEVICE pointers owned by the caller, contiguous row-major, and
+ *     16-byte aligned. The library never allocates, frees or synchronises device memory.
+ *   - States are stored key-major: element [i][j] of a [Dk][Dv] block is S[j][i].
+ *   - Outputs use the state that already contains token t (inclusive causality). No softmax
+ *     scale and no normaliser are applied; q and k are used exactly as given.
+ *   - dtype (GDN_BF16 or GDN_F32) is the element type of q, k, v and o. beta, log_alpha and
+ *     every state are always fp32.
+ *   - Launches are asynchronous on `stream` (a hipStream_t passed as void*; NULL = the null
+ *     stream). A return of GDN_OK means the work was enqueued.
+ *   - Errors are returned as negative status codes; validation happens before any launch, so
+ *     on an error nothing was enqueued and no output was touched.
+ *   - Supported sizes: Dk = Dv in {64, 128}; the chunk length is fixed at 64 tokens; any
+ *     L >= 0 (a ragged last chunk is handled exactly).
+ *   - Concurrent calls on different streams must not share output or workspace buffers.
+ */
+#ifndef GDN_H
+#define GDN_H
+
+#include <stddef.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum { GDN_BF16 = 0, GDN_F32 = 1 } gdn_dtype;
+
+enum {
+    GDN_OK = 0,
+    GDN_ERR_NULL = -1,       /* a required pointer is NULL, or a forbidden one is not */
+    GDN_ERR_SHAPE = -2,      /* unsupported B, H, L, N, Dk or Dv */
+    GDN_ERR_DTYPE = -3,      /* dtype not GDN_BF16 / GDN_F32 */
+    GDN_ERR_ALIGN = -4,      /* a pointer is not 16-byte aligned */
+    GDN_ERR_ALIAS = -5,      /* an output overlaps an input or another output */
+    GDN_ERR_WORKSPACE = -6,  /* workspace missing or smaller than the size query returned */
+    GDN_ERR_LAUNCH = -7,     /* the HIP runtime refused a launch or a device query */
+    GDN_ERR_DEVICE = -8      /* the current device is not a gfx950 GPU */
+};
+
+/* Human-readable name of a status code (static string, never NULL). */
+const char *gdn_status_string(int status);
+
+/* Bytes of device workspace gdn_prefill_fwd / linattn_prefill_fwd need for this shape
+ * (the per-chunk operands handed from the intra-chunk stage to the chunk-to-chunk pass).
+ * Returns 0 for an unsupported shape. */
+size_t gdn_prefill_workspace_size(int B, int H, int L, int Dk, int Dv, int dtype);
+
+/*
+ * Chunked prefill of the gated delta rule.
+ *   q, k        [B,H,L,Dk] dtype        v, o   [B,H,L,Dv] dtype   (may be NULL when L = 0)
+ *   beta        [B,H,L] fp32            log_alpha [B,H,L] fp32 (log of the forget gate, <= 0
+ *                                        in normal use; exp(log_alpha) is the gate)
+ *   h0          [B,H,Dk,Dv] fp32 initial state, or NULL for zeros
+ *   h_final     [B,H,Dk,Dv] fp32 final state; may equal h0 (in-place update), any other
+ *               overlap is GDN_ERR_ALIAS
+ *   workspace   device buffer of at least gdn_prefill_workspace_size(...) bytes, 256-byte
+ *               aligned; its contents are scratch and may be reused after the call completes
+ * L = 0 copies h0 (or zeros) into h_final. Non-finite inputs propagate; they are not checked.
+ */
+int gdn_prefill_fwd(const void *q, const void *k, const void *v,
+                    const float *beta, const float *log_alpha, const float *h0,
+                    void *o, float *h_final,
+                    int B, int H, int L, int Dk, int Dv, int dtype,
+                    void *workspace, size_t workspace_bytes, void *stream);
+
+/*
+ * Chunked prefill of plain causal linear attention (a = 1, no delta term):
+ *   O_chunk = Q H0 + (Q K^T masked causally, diagonal included) V,   H <- H0 + K^T V.
+ * Same argument list as gdn_prefill_fwd; beta and log_alpha must both be NULL.
+ */
+int linattn_prefill_fwd(const void *q, const void *k, const void *v,
+                        const float *beta, const float *log_alpha, const float *h0,
+                        void *o, float *h_final,
+                        int B, int H, int L, int Dk, int Dv, int dtype,
+                        void *workspace, size_t workspace_bytes, void *stream);
+
+/*
+ * One recurrent decode step of the gated delta rule for N independent sequences:
+ *   q, k [N,H,Dk] dtype;  v, o [N,H,Dv] dtype;  beta, log_alpha [N,H] fp32;
+ *   state [N,H,Dk,Dv] fp32, read and overwritten IN PLACE with the state after the token.
+ * Each call streams the state from HBM once and writes it back once.
+ */
+int gdn_decode_step(const void *q, const void *k, const void *v,
+                    const float *beta, const float *log_alpha, float *state,
+                    void *o, int N, int H, int Dk, int Dv, int dtype, void *stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* GDN_H */

@@ -1,0 +1,91 @@
+"""The C-ABI library loads, exports every declared symbol, and rejects bad arguments on the
+host before touching a GPU (fake pointer values are never dereferenced)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+from gated_deltanet_chunked_rule_amd import _lib
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "gdn.h")
+
+OK, NULL, SHAPE, DTYPE, ALIGN, ALIAS, WORKSPACE = 0, -1, -2, -3, -4, -5, -6
+
+
+@pytest.fixture(scope="module")
+def lib():
+    return _lib.load()
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b([a-z_]+)\s*\(", text)) - {"if", "sizeof", "defined"})
+
+
+def test_header_symbols_exported(lib):
+    names = declared_functions()
+    assert set(names) == set(_lib.SIGNATURES), names
+    for n in names:
+        assert getattr(lib, n) is not None
+
+
+def test_status_strings(lib):
+    for code in (0, -1, -2, -3, -4, -5, -6, -7, -8):
+        assert _lib.status_string(code).startswith("GDN_")
+    assert _lib.status_string(17) == "unknown status"
+
+
+def test_workspace_size_query(lib):
+    f = lib.gdn_prefill_workspace_size
+    assert f(1, 16, 131072, 128, 128, 0) > 0
+    assert f(1, 1, 64, 128, 128, 0) * 2048 == f(1, 1, 131072, 128, 128, 0)
+    assert f(1, 1, 65, 64, 64, 1) == 2 * f(1, 1, 64, 64, 64, 1)   # a ragged tail costs a whole chunk
+    assert f(1, 2, 0, 128, 128, 0) == 0
+    assert f(1, 1, 64, 96, 96, 0) == 0        # unsupported head size
+    assert f(1, 1, 64, 128, 64, 0) == 0       # Dk != Dv
+    assert f(1, 1, 64, 128, 128, 2) == 0      # bad dtype
+    assert f(0, 1, 64, 128, 128, 0) == 0
+
+
+def _prefill(lib, q=0x10000, k=0x20000000, v=0x40000000, beta=0x60000000, la=0x60100000, h0=None,
+             o=0x70000000, hf=0x7f000000, B=1, H=1, L=64, D=128, dt=0, ws=0x100000000, wsb=1 << 30, gdn=True):
+    f = lib.gdn_prefill_fwd if gdn else lib.linattn_prefill_fwd
+    return f(q, k, v, beta, la, h0, o, hf, B, H, L, D, D, dt, ws, wsb, None)
+
+
+def test_prefill_host_validation(lib):
+    assert _prefill(lib, q=None) == NULL
+    assert _prefill(lib, beta=None) == NULL
+    assert _prefill(lib, gdn=False) == NULL            # linear attention takes no gates
+    assert _prefill(lib, D=96) == SHAPE
+    assert _prefill(lib, L=-1) == SHAPE
+    assert _prefill(lib, B=0) == SHAPE
+    assert _prefill(lib, dt=5) == DTYPE
+    assert _prefill(lib, q=0x10008) == ALIGN
+    assert _prefill(lib, ws=0x100000010) == ALIGN      # workspace needs 256-byte alignment
+    assert _prefill(lib, ws=None) == WORKSPACE
+    assert _prefill(lib, wsb=1000) == WORKSPACE
+    assert _prefill(lib, o=0x20000000) == ALIAS        # o == k
+    assert _prefill(lib, hf=0x40000000 + 4096) == ALIAS  # h_final inside v
+    assert _prefill(lib, h0=0x7f000000 + 16) == ALIAS  # partial h0 / h_final overlap
+
+
+def test_decode_host_validation(lib):
+    f = lib.gdn_decode_step
+    args = dict(q=0x10000, k=0x20000, v=0x30000, beta=0x40000, la=0x50000, st=0x1000000, o=0x60000)
+
+    def call(**kw):
+        a = dict(args)
+        a.update(kw)
+        return f(a["q"], a["k"], a["v"], a["beta"], a["la"], a["st"], a["o"], kw.get("N", 4), 2, 128, 128,
+                 kw.get("dt", 0), None)
+
+    assert call(st=None) == NULL
+    assert call(N=0) == SHAPE
+    assert call(dt=3) == DTYPE
+    assert call(o=0x60004) == ALIGN
+    assert call(o=0x1000000 + 4096) == ALIAS           # o inside the state
+    assert call(q=0x1000000) == ALIAS
