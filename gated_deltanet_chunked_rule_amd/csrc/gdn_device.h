@@ -10,14 +10,18 @@ typedef __attribute__((__vector_size__(8 * sizeof(short)))) short bf16x8;
 typedef __attribute__((__vector_size__(4 * sizeof(short)))) short bf16x4;
 typedef __attribute__((__vector_size__(4 * sizeof(float)))) float f32x4;
 
-// bf16 <-> fp32. bf16 is the top half of an fp32; rounding is to nearest, ties to even,
-// and NaN stays NaN.
+typedef __attribute__((__vector_size__(2 * sizeof(__bf16)))) __bf16 bf16x2_t;
+typedef __attribute__((__vector_size__(2 * sizeof(float)))) float f32x2_t;
+
+// bf16 <-> fp32. bf16 is the top half of an fp32. fp32 -> bf16 uses gfx950's conversion
+// instruction (v_cvt_pk_bf16_f32: round to nearest even, two values per instruction).
 __device__ __forceinline__ float bf2f(uint16_t h) { return __uint_as_float((uint32_t)h << 16); }
 
-__device__ __forceinline__ uint16_t f2bf(float f) {
-    uint32_t u = __float_as_uint(f);
-    if ((u & 0x7fffffffu) > 0x7f800000u) return (uint16_t)((u >> 16) | 0x40u);
-    return (uint16_t)((u + 0x7fffu + ((u >> 16) & 1u)) >> 16);
+__device__ __forceinline__ uint16_t f2bf(float f) { return __builtin_bit_cast(uint16_t, (__bf16)f); }
+
+// two floats -> packed bf16 pair (low half = a)
+__device__ __forceinline__ uint32_t f2bf2(float a, float b) {
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2_t{a, b}, bf16x2_t));
 }
 
 // storage element types of q, k, v and o
@@ -42,8 +46,8 @@ __device__ __forceinline__ float4 load4(const float* p) { return *reinterpret_ca
 
 __device__ __forceinline__ void store4(uint16_t* p, float4 x) {
     uint2 r;
-    r.x = (uint32_t)f2bf(x.x) | ((uint32_t)f2bf(x.y) << 16);
-    r.y = (uint32_t)f2bf(x.z) | ((uint32_t)f2bf(x.w) << 16);
+    r.x = f2bf2(x.x, x.y);
+    r.y = f2bf2(x.z, x.w);
     *reinterpret_cast<uint2*>(p) = r;
 }
 __device__ __forceinline__ void store4(float* p, float4 x) { *reinterpret_cast<float4*>(p) = x; }

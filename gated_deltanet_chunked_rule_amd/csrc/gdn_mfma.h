@@ -31,10 +31,8 @@ struct MM<BF16> {
     // k offset (within the fragment's KB-block) of element e held by lane group j
     static __device__ __forceinline__ int kofs(int j, int e) { return e < 4 ? 4 * j + e : 12 + 4 * j + e; }
     static __device__ __forceinline__ frag pack(const float (&x)[8]) {
-        frag f;
-#pragma unroll
-        for (int e = 0; e < 8; ++e) f[e] = (short)f2bf(x[e]);
-        return f;
+        const uint4 u = {f2bf2(x[0], x[1]), f2bf2(x[2], x[3]), f2bf2(x[4], x[5]), f2bf2(x[6], x[7])};
+        return __builtin_bit_cast(frag, u);
     }
     // fragment of k-block kb from accumulator tiles t[2 kb], t[2 kb + 1], times s
     static __device__ __forceinline__ frag from_acc(const f32x4* t, int kb, float s = 1.f) {

@@ -18,11 +18,12 @@
 // Only exponentials of non-positive differences are ever formed, so strong gates underflow to
 // exact zeros instead of overflowing.
 //
-//   prep_kernel   (one workgroup per chunk and head, fully parallel): g, A, T by forward
-//                 substitution in LDS, -W, Khat^T and Ut, written as MFMA-ready fragments.
-//   chain_kernel  (one wave per head and 16 value columns): the sequential pass. The fp32
-//                 state slice stays in accumulator registers for the whole sequence; per chunk
-//                 it emits the chunk-start state and U as fragments for the output stage.
+//   prep_kernel   (one workgroup per chunk and head, fully parallel): g, A, T = (I + A)^-1 by
+//                 a blocked inverse in LDS, -W, Khat^T and Ut, written as MFMA-ready fragments.
+//   chain_kernel  (one workgroup per head and 32 value columns): the sequential pass. The fp32
+//                 state stays in accumulator registers for the whole sequence while loader
+//                 waves stream the next chunks' operands into an LDS ring; per chunk it emits
+//                 the chunk-start state and U as fragments for the output stage.
 //   output_kernel (one workgroup per chunk and head): P = (Q K^T) gated and masked, then
 //                 O^T = H^T (e^g Q)^T + U^T P^T, stored four value columns per lane.
 // Plain linear attention uses the same kernels with T = I, W = 0, Ut = V, g = 0.
@@ -90,6 +91,27 @@ __device__ __forceinline__ float wave_scan(float x, int lane) {
     return x;
 }
 
+
+// Off-diagonal block (bi, bj), bi > bj, of T = (I + A)^-1 (16 x 16 blocks, fp32, row stride AS):
+//     T_ij = -T_ii * sum_{k=j}^{i-1} A_ik T_kj
+// on fp32 MFMA. Every T_kj with k < i must be final. Called by one whole wave.
+template <int AS>
+__device__ __forceinline__ void inverse_block_t(const float* Am, float* Tm, int bi, int bj, int j, int m) {
+    f32x4 x = {0.f, 0.f, 0.f, 0.f};
+    for (int bk = bj; bk < bi; ++bk) {
+        // A_ik rows (lane (j, m): A[m][4 j + e]) times T_kj as B (lane (j, n): T[4 j + e][n])
+        const float4 a = *reinterpret_cast<const float4*>(Am + (16 * bi + m) * AS + 16 * bk + 4 * j);
+        f32x4 b;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) b[e] = Tm[(16 * bk + 4 * j + e) * AS + 16 * bj + m];
+        x = MM<F32>::mma(f32x4{a.x, a.y, a.z, a.w}, b, x);
+    }
+    const float4 t = *reinterpret_cast<const float4*>(Tm + (16 * bi + m) * AS + 16 * bi + 4 * j);
+    const f32x4 y = MM<F32>::mma(f32x4{t.x, t.y, t.z, t.w}, x, f32x4{0.f, 0.f, 0.f, 0.f});
+#pragma unroll
+    for (int e = 0; e < 4; ++e) Tm[(16 * bi + 4 * j + e) * AS + 16 * bj + m] = -y[e];
+}
+
 // ---------------------------------------------------------------------------------------------
 // stage 1: intra-chunk delta-system solve and WY/UT transform
 // ---------------------------------------------------------------------------------------------
@@ -106,8 +128,9 @@ __global__ __launch_bounds__(256) void prep_kernel(PrefArgs a) {
     extern __shared__ __align__(16) unsigned char smem[];
     T* Kt = reinterpret_cast<T*>(smem);            // [D][TP]  K^T
     T* Vt = Kt + D * TP;                           // [D][TP]  V^T
-    float* Am = reinterpret_cast<float*>(Vt + D * TP);  // [CH][AS] A, then T
-    float* sg = Am + CH * AS;                      // g
+    float* Am = reinterpret_cast<float*>(Vt + D * TP);  // [CH][AS] A (strictly lower)
+    float* Tm = Am + CH * AS;                      // [CH][AS] T = (I + A)^-1
+    float* sg = Tm + CH * AS;                      // g
     float* sbe = sg + CH;                          // beta e^g
     float* sb = sbe + CH;                          // beta
     float* skh = sb + CH;                          // e^{g_C - g}
@@ -172,39 +195,48 @@ __global__ __launch_bounds__(256) void prep_kernel(PrefArgs a) {
                 Am[r * AS + s] = (s < r) ? sb[r] * __expf(sg[r] - sg[s]) * acc[e] : 0.f;
             }
         }
-        __syncthreads();
-        if (w == 0) {
-            // T = (I + A)^-1 by forward substitution, lane c owns column c of T
-            float tc[CH];
-#pragma unroll
-            for (int r = 0; r < CH; ++r) tc[r] = 0.f;
-#pragma unroll
-            for (int r = 0; r < CH; ++r) {
-                float acc = 0.f;
-#pragma unroll
-                for (int s = 0; s < r; s += 4) {
-                    const float4 a4 = *reinterpret_cast<const float4*>(Am + r * AS + s);
-                    acc += a4.x * tc[s] + a4.y * tc[s + 1] + a4.z * tc[s + 2] + a4.w * tc[s + 3];
-                }
-                tc[r] = (r == lane) ? 1.f : ((r < lane) ? 0.f : -acc);
-            }
-#pragma unroll
-            for (int r = 0; r < CH; ++r) Am[r * AS + lane] = tc[r];
-        } else {
-            // Khat^T fragments (d-tile dt, token block kb), waves 1..3 while wave 0 solves
-            for (int f = w - 1; f < NDT * NKT; f += 3) {
-                const int dt = f / NKT, kb = f % NKT;
-                st_frag(rec + Ly::A_KH + (size_t)f * Ly::FR, lane,
-                        row_frag_ks<E>(Kt + (16 * dt + m) * TP, kb * KB, j, skh));
-            }
+        // zero the above-diagonal 16 x 16 blocks of T (fragments of 32 tokens read some of them)
+        for (int i = tid; i < 6 * 256; i += 256) {
+            const int b = i >> 8, e = i & 255;
+            const int bi = b < 3 ? 0 : (b < 5 ? 1 : 2), bj = b < 3 ? b + 1 : (b < 5 ? b - 1 : 3);
+            Tm[(16 * bi + (e >> 4)) * AS + 16 * bj + (e & 15)] = 0.f;
         }
         __syncthreads();
+        // T = (I + A)^-1, blocked by 16: diagonal blocks by forward substitution (wave i inverts
+        // block i, lane c < 16 owns column c), then T_ij = -T_ii sum_{k=j}^{i-1} A_ik T_kj level
+        // by level on fp32 MFMA.
+        {
+            const int i0 = 16 * w, c = lane & 15;
+            float tc[16];
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+                float acc = 0.f;
+#pragma unroll
+                for (int s2 = 0; s2 < r; ++s2) acc += Am[(i0 + r) * AS + i0 + s2] * tc[s2];
+                tc[r] = (r == c) ? 1.f : ((r < c) ? 0.f : -acc);
+            }
+            if (lane < 16) {
+#pragma unroll
+                for (int r = 0; r < 16; ++r) Tm[(i0 + r) * AS + i0 + c] = tc[r];
+            }
+        }
+#pragma unroll
+        for (int lvl = 1; lvl < 4; ++lvl) {
+            __syncthreads();
+            if (w + lvl < 4) inverse_block_t<AS>(Am, Tm, w + lvl, w, j, m);
+        }
+        __syncthreads();
+        // Khat^T fragments (d-tile dt, token block kb)
+        for (int f = w; f < NDT * NKT; f += 4) {
+            const int dt = f / NKT, kb = f % NKT;
+            st_frag(rec + Ly::A_KH + (size_t)f * Ly::FR, lane, row_frag_ks<E>(Kt + (16 * dt + m) * TP, kb * KB, j, skh));
+        }
         // wave w: token tile rt = w. T rows 16 rt .. 16 rt + 15 are zero beyond column 16 rt + 15.
         const int rt = w;
         const int kbmax = (16 * rt + 15) / KB;
         frag Tf[NKT];
 #pragma unroll
-        for (int kb = 0; kb < NKT; ++kb) Tf[kb] = row_frag_f32<E>(Am + (16 * rt + m) * AS, kb * KB, j);
+        for (int kb = 0; kb < NKT; ++kb) Tf[kb] = row_frag_f32<E>(Tm + (16 * rt + m) * AS, kb * KB, j);
         // -W fragments: W^T tile (dt, rt) = sum_s (beta e^g K)^T[d][s] T^T[s][r]
         f32x4 wt[NDT];
 #pragma unroll
@@ -247,71 +279,186 @@ __global__ __launch_bounds__(256) void prep_kernel(PrefArgs a) {
 // ---------------------------------------------------------------------------------------------
 // stage 2: the sequential chunk-to-chunk pass, state resident in registers
 // ---------------------------------------------------------------------------------------------
+// Chain workgroup: one slice (batch, head) and 32 value columns, four waves. Waves 0 and 1 each
+// own 16 columns of the fp32 state (all Dk rows) in accumulator registers for the whole
+// sequence. Waves 2 and 3 stream the per-chunk operands (-W and Khat^T fragments, shared by all
+// columns, plus this workgroup's Ut columns and the chunk decay) from the workspace into a ring
+// of NS LDS slots, NS - 1 chunks ahead of the compute waves, so the sequential chain never waits
+// on a global-memory round trip.
+template <int D, class E>
+struct ChainCfg {
+    using Ly = Layout<D, E>;
+    static constexpr int CGW = 32;                                       // columns per workgroup
+    static constexpr int NCW = D / CGW;                                  // workgroups per slice
+    static constexpr size_t UTSUB = (size_t)2 * 4 * 64 * 4 * sizeof(typename E::T);  // Ut bytes of 32 columns
+    static constexpr size_t S_UT = Ly::A_UT;                             // -W and Khat^T precede
+    static constexpr size_t S_DEC = S_UT + UTSUB;
+    static constexpr int UNITS = (int)((S_DEC + 16) / 16);               // 16-byte units per slot
+    static constexpr int NBLK = (UNITS + 63) / 64;                       // 1 KB wave blocks per slot
+    static constexpr int BPW = (NBLK + 1) / 2;                           // blocks per loader wave
+    static constexpr size_t SLOT = (size_t)NBLK * 1024;
+    static constexpr int NS = SLOT * 4 <= 152 * 1024 ? 4 : (SLOT * 3 <= 152 * 1024 ? 3 : 2);
+    static constexpr int INFLIGHT = NS - 2;                              // chunks still loading at a barrier
+};
+
+// Barrier of the chain workgroup. Only LDS is shared between its waves, and only the loader
+// waves write it, through direct-to-LDS loads whose completion they establish themselves with
+// wait_vmcnt before arriving; so the barrier waits for LDS reads (lgkmcnt) and nothing else:
+// neither outstanding global stores nor the loads still in flight for later chunks.
+__device__ __forceinline__ void lds_barrier() {
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_waitcnt(15 | (7 << 4) | (0 << 8) | (3 << 14));   // lgkmcnt(0)
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+}
+
+// Wait until at most N vector-memory operations of this wave are outstanding (gfx9 encoding:
+// vmcnt split over bits 3:0 and 15:14, expcnt and lgkmcnt left at their maxima).
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+    static_assert(N >= 0 && N < 64, "vmcnt is 6 bits");
+    __builtin_amdgcn_s_waitcnt((N & 15) | (7 << 4) | (15 << 8) | ((N >> 4) << 14));
+}
+
+template <int D, class E>
+__device__ __forceinline__ const unsigned char* chain_src(const unsigned char* recA, int cgw, int u) {
+    using C = ChainCfg<D, E>;
+    using Ly = Layout<D, E>;
+    constexpr int U1 = (int)(C::S_UT / 16), U2 = (int)(C::UTSUB / 16);
+    u = u < C::UNITS ? u : C::UNITS - 1;
+    if (u < U1) return recA + (size_t)u * 16;
+    if (u < U1 + U2) return recA + Ly::A_UT + (size_t)cgw * C::UTSUB + (size_t)(u - U1) * 16;
+    return recA + Ly::A_DEC;   // the decay (one unit; the 12 bytes after it are not used)
+}
+
+// Direct-to-LDS load of 16 bytes per lane: lane l's bytes land at LDS address lds_base + 16 l.
+// Issued as inline assembly so that the compiler does not track it: the loader waves account
+// for these loads themselves (wait_vmcnt), and the compute waves, which only read LDS, must not
+// be made to wait on them or on their own global stores.
+// M0 is a reserved register, so clang warns about the clobber; the kernels that call dma16 use
+// M0 for nothing else, and the asm sets it before each load.
+#pragma clang diagnostic push
+#pragma clang diagnostic ignored "-Winline-asm"
+__device__ __forceinline__ void dma16(const void* src, unsigned lds_base) {
+    lds_base = __builtin_amdgcn_readfirstlane(lds_base);   // wave-uniform by construction
+    asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(src), "s"(lds_base)
+                 : "memory", "m0");
+}
+#pragma clang diagnostic pop
+
+__device__ __forceinline__ unsigned lds_addr(const void* p) {
+    return (unsigned)(size_t)(const __attribute__((address_space(3))) void*)p;
+}
+
+// One loader wave's share of a chunk: BPW 1 KB blocks. Blocks past the slot's end repeat the
+// last block, so both loader waves issue the same count.
+template <int D, class E>
+__device__ __forceinline__ void chain_issue_slot(unsigned char* slot, const unsigned char* recA, int cgw, int lw,
+                                                 int lane) {
+    using C = ChainCfg<D, E>;
+    const unsigned base = lds_addr(slot);
+#pragma unroll
+    for (int i = 0; i < C::BPW; ++i) {
+        int blk = lw + 2 * i;
+        blk = blk < C::NBLK ? blk : C::NBLK - 1;
+        dma16(chain_src<D, E>(recA, cgw, blk * 64 + lane), base + (unsigned)blk * 1024u);
+    }
+}
+
 template <int D, class E, bool DELTA>
-__global__ __launch_bounds__(64) void chain_kernel(PrefArgs a) {
+__global__ __launch_bounds__(256) void chain_kernel(PrefArgs a) {
     using T = typename E::T;
     using M = MM<E>;
     using Ly = Layout<D, E>;
+    using C = ChainCfg<D, E>;
     using frag = typename M::frag;
-    constexpr int NKD = Ly::NKD, NKT = Ly::NKT, NDT = Ly::NDT;
+    constexpr int NKD = Ly::NKD, NKT = Ly::NKT, NDT = Ly::NDT, NS = C::NS;
+    extern __shared__ __align__(16) unsigned char smem[];
     // blockIdx -> (slice, column group) so that all column groups of one slice run on the same
     // XCD (workgroups are dealt to the 8 XCDs round-robin) and share its L2.
-    const int xcd = blockIdx.x & 7, slot = blockIdx.x >> 3;
-    const int cg = slot % NDT, bh = (slot / NDT) * 8 + xcd;
+    const int xcd = blockIdx.x & 7, sl = blockIdx.x >> 3;
+    const int cgw = sl % C::NCW, bh = (sl / C::NCW) * 8 + xcd;
     if (bh >= a.BH) return;
-    const int lane = threadIdx.x, j = lane >> 4, m = lane & 15;
-    const int col = 16 * cg + m;
+    const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63, j = lane >> 4, m = lane & 15;
+    const int nch = a.nchunks;
+    const unsigned char* rec0 = a.ws + (size_t)bh * nch * Ly::REC;
 
-    f32x4 H[NDT];  // lane (j, m): H[16 dt + 4 j + e][col]
-#pragma unroll
-    for (int dt = 0; dt < NDT; ++dt)
-#pragma unroll
-        for (int e = 0; e < 4; ++e)
-            H[dt][e] = a.h0 ? a.h0[((size_t)bh * D + 16 * dt + 4 * j + e) * D + col] : 0.f;
-
-    const unsigned char* recA = a.ws + (size_t)bh * a.nchunks * Ly::REC;
-    for (int c = 0; c < a.nchunks; ++c, recA += Ly::REC) {
-        unsigned char* recB = const_cast<unsigned char*>(recA) + Ly::REC_A;
-        frag Hf[NKD];
-#pragma unroll
-        for (int kd = 0; kd < NKD; ++kd) {
-            Hf[kd] = M::from_acc(H, kd);
-            st_frag(recB + Ly::B_H + (size_t)(cg * NKD + kd) * Ly::FR, lane, Hf[kd]);
-        }
-        f32x4 U[4];
-#pragma unroll
-        for (int rt = 0; rt < 4; ++rt) {
-            const float4 x = load4(reinterpret_cast<const T*>(recA + Ly::A_UT) + ((size_t)(cg * 4 + rt) * 64 + lane) * 4);
-            U[rt] = f32x4{x.x, x.y, x.z, x.w};
-        }
-        if constexpr (DELTA) {
-#pragma unroll
-            for (int rt = 0; rt < 4; ++rt)
-#pragma unroll
-                for (int kd = 0; kd < NKD; ++kd)
-                    U[rt] = M::mma(ld_frag<frag>(recA + Ly::A_W + (size_t)(rt * NKD + kd) * Ly::FR, lane), Hf[kd], U[rt]);
-        }
-        frag Uf[NKT];
-#pragma unroll
-        for (int kt = 0; kt < NKT; ++kt) {
-            Uf[kt] = M::from_acc(U, kt);
-            st_frag(recB + Ly::B_U + (size_t)(cg * NKT + kt) * Ly::FR, lane, Uf[kt]);
-        }
-        const float dec = *reinterpret_cast<const float*>(recA + Ly::A_DEC);
-#pragma unroll
-        for (int dt = 0; dt < NDT; ++dt) {
-            f32x4 h = H[dt];
-            if constexpr (DELTA) h = f32x4{h[0] * dec, h[1] * dec, h[2] * dec, h[3] * dec};
-#pragma unroll
-            for (int kt = 0; kt < NKT; ++kt)
-                h = M::mma(ld_frag<frag>(recA + Ly::A_KH + (size_t)(dt * NKT + kt) * Ly::FR, lane), Uf[kt], h);
-            H[dt] = h;
-        }
+    // loader waves: chunk c + NS - 1 is issued at step c into the slot freed at step c - 1;
+    // before each barrier a loader waits only for the chunk the compute waves need next
+    if (w >= 2) {
+        for (int c = 0; c < NS - 1; ++c)
+            chain_issue_slot<D, E>(smem + (size_t)c * C::SLOT, rec0 + (size_t)min(c, nch - 1) * Ly::REC, cgw, w - 2,
+                                   lane);
+        wait_vmcnt<C::INFLIGHT * C::BPW>();
     }
+    const int cg = 2 * cgw + (w & 1);          // 16-column group of a compute wave
+    const int col = 16 * cg + m;
+    f32x4 H[NDT];                              // lane (j, m): H[16 dt + 4 j + e][col]
+    if (w < 2) {
 #pragma unroll
-    for (int dt = 0; dt < NDT; ++dt)
+        for (int dt = 0; dt < NDT; ++dt)
 #pragma unroll
-        for (int e = 0; e < 4; ++e) a.h_final[((size_t)bh * D + 16 * dt + 4 * j + e) * D + col] = H[dt][e];
+            for (int e = 0; e < 4; ++e)
+                H[dt][e] = a.h0 ? a.h0[((size_t)bh * D + 16 * dt + 4 * j + e) * D + col] : 0.f;
+    }
+    lds_barrier();
+
+    for (int c = 0; c < nch; ++c) {
+        if (w >= 2) {
+            // always issue (clamped to the last chunk) so the outstanding count stays fixed
+            const int cn = c + NS - 1;
+            chain_issue_slot<D, E>(smem + (size_t)(cn % NS) * C::SLOT, rec0 + (size_t)min(cn, nch - 1) * Ly::REC, cgw,
+                                   w - 2, lane);
+            wait_vmcnt<C::INFLIGHT * C::BPW>();
+        } else {
+            const unsigned char* slot = smem + (size_t)(c % NS) * C::SLOT;
+            unsigned char* recB = const_cast<unsigned char*>(rec0) + (size_t)c * Ly::REC + Ly::REC_A;
+            frag Hf[NKD];
+#pragma unroll
+            for (int kd = 0; kd < NKD; ++kd) {
+                Hf[kd] = M::from_acc(H, kd);
+                st_frag(recB + Ly::B_H + (size_t)(cg * NKD + kd) * Ly::FR, lane, Hf[kd]);
+            }
+            f32x4 U[4];
+#pragma unroll
+            for (int rt = 0; rt < 4; ++rt) {
+                const float4 x = load4(reinterpret_cast<const T*>(slot + C::S_UT) + ((size_t)((w & 1) * 4 + rt) * 64 + lane) * 4);
+                U[rt] = f32x4{x.x, x.y, x.z, x.w};
+            }
+            if constexpr (DELTA) {
+#pragma unroll
+                for (int rt = 0; rt < 4; ++rt)
+#pragma unroll
+                    for (int kd = 0; kd < NKD; ++kd)
+                        U[rt] = M::mma(ld_frag<frag>(slot + Ly::A_W + (size_t)(rt * NKD + kd) * Ly::FR, lane), Hf[kd], U[rt]);
+            }
+            frag Uf[NKT];
+#pragma unroll
+            for (int kt = 0; kt < NKT; ++kt) {
+                Uf[kt] = M::from_acc(U, kt);
+                st_frag(recB + Ly::B_U + (size_t)(cg * NKT + kt) * Ly::FR, lane, Uf[kt]);
+            }
+            const float dec = *reinterpret_cast<const float*>(slot + C::S_DEC);
+#pragma unroll
+            for (int dt = 0; dt < NDT; ++dt) {
+                f32x4 h = H[dt];
+                if constexpr (DELTA) h = f32x4{h[0] * dec, h[1] * dec, h[2] * dec, h[3] * dec};
+#pragma unroll
+                for (int kt = 0; kt < NKT; ++kt)
+                    h = M::mma(ld_frag<frag>(slot + Ly::A_KH + (size_t)(dt * NKT + kt) * Ly::FR, lane), Uf[kt], h);
+                H[dt] = h;
+            }
+        }
+        lds_barrier();
+    }
+    if (w < 2) {
+#pragma unroll
+        for (int dt = 0; dt < NDT; ++dt)
+#pragma unroll
+            for (int e = 0; e < 4; ++e) a.h_final[((size_t)bh * D + 16 * dt + 4 * j + e) * D + col] = H[dt][e];
+    } else {
+        wait_vmcnt<0>();   // no LDS write may land after the workgroup ends
+    }
 }
 
 // ---------------------------------------------------------------------------------------------
@@ -338,6 +485,22 @@ __global__ __launch_bounds__(256) void output_kernel(PrefArgs a) {
     T* op = static_cast<T*>(a.o) + tok0 * D;
     const unsigned char* recB = a.ws + ((size_t)bh * a.nchunks + c) * Ly::REC + Ly::REC_A;
 
+    // this wave's value tiles vt = w, w + 4, ...: fetch the chunk-start state and U fragments
+    // first so their latency overlaps the P computation
+    constexpr int NVW = (NDT + 3) / 4;
+    frag Hc[NVW][NKD], Uf[NVW][NKT];
+#pragma unroll
+    for (int iv = 0; iv < NVW; ++iv) {
+        const int vt = w + 4 * iv;
+        if (vt < NDT) {
+#pragma unroll
+            for (int kd = 0; kd < NKD; ++kd)
+                Hc[iv][kd] = ld_frag<frag>(recB + Ly::B_H + (size_t)(vt * NKD + kd) * Ly::FR, lane);
+#pragma unroll
+            for (int kt = 0; kt < NKT; ++kt)
+                Uf[iv][kt] = ld_frag<frag>(recB + Ly::B_U + (size_t)(vt * NKT + kt) * Ly::FR, lane);
+        }
+    }
     if (w == 0) {
         float la = 0.f;
         if (DELTA && lane < n) la = a.log_alpha[tok0 + lane];
@@ -373,21 +536,19 @@ __global__ __launch_bounds__(256) void output_kernel(PrefArgs a) {
     }
     __syncthreads();
     // wave w: value tiles vt = w, w + 4, ...; all four token tiles
-    for (int vt = w; vt < NDT; vt += 4) {
-        frag Hc[NKD], Uf[NKT];
 #pragma unroll
-        for (int kd = 0; kd < NKD; ++kd) Hc[kd] = ld_frag<frag>(recB + Ly::B_H + (size_t)(vt * NKD + kd) * Ly::FR, lane);
-#pragma unroll
-        for (int kt = 0; kt < NKT; ++kt) Uf[kt] = ld_frag<frag>(recB + Ly::B_U + (size_t)(vt * NKT + kt) * Ly::FR, lane);
+    for (int iv = 0; iv < NVW; ++iv) {
+        const int vt = w + 4 * iv;
+        if (vt >= NDT) break;
 #pragma unroll
         for (int rt = 0; rt < 4; ++rt) {
             f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-            for (int kd = 0; kd < NKD; ++kd) acc = M::mma(Hc[kd], ld_frag<frag>(sQ + (rt * NKD + kd) * 1024, lane), acc);
+            for (int kd = 0; kd < NKD; ++kd) acc = M::mma(Hc[iv][kd], ld_frag<frag>(sQ + (rt * NKD + kd) * 1024, lane), acc);
             const int kbmax = (16 * rt + 15) / KB;
 #pragma unroll
             for (int kt = 0; kt < NKT; ++kt)
-                if (kt <= kbmax) acc = M::mma(Uf[kt], ld_frag<frag>(sP + (rt * NKT + kt) * 1024, lane), acc);
+                if (kt <= kbmax) acc = M::mma(Uf[iv][kt], ld_frag<frag>(sP + (rt * NKT + kt) * 1024, lane), acc);
             // lane (j, m): O[token 16 rt + m][16 vt + 4 j .. + 3]
             const int r = 16 * rt + m;
             if (r < n) store4(op + (size_t)r * D + 16 * vt + 4 * j, make_float4(acc[0], acc[1], acc[2], acc[3]));
@@ -403,10 +564,9 @@ __global__ void copy_state_kernel(const float* __restrict__ src, float* __restri
 
 template <int D, class E, bool DELTA>
 static int launch_prefill_t(const PrefArgs& a, hipStream_t stream) {
-    using Ly = Layout<D, E>;
     using T = typename E::T;
     constexpr int TP = CH + 8, AS = CH + 4;
-    const size_t lds = (size_t)2 * D * TP * sizeof(T) + (size_t)CH * AS * 4 + 4 * CH * 4;
+    const size_t lds = (size_t)2 * D * TP * sizeof(T) + (size_t)2 * CH * AS * 4 + 4 * CH * 4;
     static bool attr_done = false;  // benign race: every caller sets the same value
     if (!attr_done) {
         if (hipFuncSetAttribute(reinterpret_cast<const void*>(&prep_kernel<D, E, DELTA>),
@@ -415,8 +575,17 @@ static int launch_prefill_t(const PrefArgs& a, hipStream_t stream) {
         attr_done = true;
     }
     hipLaunchKernelGGL((prep_kernel<D, E, DELTA>), dim3(a.nchunks, a.BH), dim3(256), lds, stream, a);
+    using CC = ChainCfg<D, E>;
+    const size_t lds_chain = (size_t)CC::NS * CC::SLOT;
+    static bool attr_chain = false;
+    if (!attr_chain) {
+        if (hipFuncSetAttribute(reinterpret_cast<const void*>(&chain_kernel<D, E, DELTA>),
+                                hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds_chain) != hipSuccess)
+            return -1;
+        attr_chain = true;
+    }
     const int nslot = (a.BH + 7) / 8;
-    hipLaunchKernelGGL((chain_kernel<D, E, DELTA>), dim3(8 * nslot * Ly::NDT), dim3(64), 0, stream, a);
+    hipLaunchKernelGGL((chain_kernel<D, E, DELTA>), dim3(8 * nslot * CC::NCW), dim3(256), lds_chain, stream, a);
     hipLaunchKernelGGL((output_kernel<D, E, DELTA>), dim3(a.nchunks, a.BH), dim3(256), 0, stream, a);
     return hipGetLastError() == hipSuccess ? 0 : -1;
 }
