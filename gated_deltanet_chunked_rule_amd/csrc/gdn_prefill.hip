@@ -130,10 +130,15 @@ __global__ __launch_bounds__(256) void prep_kernel(PrefArgs a) {
     T* Vt = Kt + D * TP;                           // [D][TP]  V^T
     float* Am = reinterpret_cast<float*>(Vt + D * TP);  // [CH][AS] A (strictly lower)
     float* Tm = Am + CH * AS;                      // [CH][AS] T = (I + A)^-1
+    // K rows [CH][KP] for the Gram matrix: in T's space when it fits (T is written only after
+    // the Gram is done), else in a region of its own after the gate vectors
+    constexpr int KP = D + 8;
+    constexpr bool KROW_IN_T = (size_t)CH * KP * sizeof(T) <= (size_t)CH * AS * 4;
     float* sg = Tm + CH * AS;                      // g
     float* sbe = sg + CH;                          // beta e^g
     float* sb = sbe + CH;                          // beta
     float* skh = sb + CH;                          // e^{g_C - g}
+    T* Kr = KROW_IN_T ? reinterpret_cast<T*>(Tm) : reinterpret_cast<T*>(skh + CH);
 
     const int c = blockIdx.x, bh = blockIdx.y;
     const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63, j = lane >> 4, m = lane & 15;
@@ -173,6 +178,7 @@ __global__ __launch_bounds__(256) void prep_kernel(PrefArgs a) {
             Kt[(d + 2) * TP + r] = E::from(kk.z); Kt[(d + 3) * TP + r] = E::from(kk.w);
             Vt[(d + 0) * TP + r] = E::from(vv.x); Vt[(d + 1) * TP + r] = E::from(vv.y);
             Vt[(d + 2) * TP + r] = E::from(vv.z); Vt[(d + 3) * TP + r] = E::from(vv.w);
+            if (DELTA) store4(Kr + r * KP + d, kk);
         }
     }
     __syncthreads();
@@ -182,8 +188,8 @@ __global__ __launch_bounds__(256) void prep_kernel(PrefArgs a) {
         for (int ti = w; ti < 10; ti += 4) {
             int rt = 0, st = ti;
             while (st > rt) { st -= rt + 1; ++rt; }
-            const T* ra = (16 * rt + m < n) ? kp + (size_t)(16 * rt + m) * D : nullptr;
-            const T* rb = (16 * st + m < n) ? kp + (size_t)(16 * st + m) * D : nullptr;
+            const T* ra = Kr + (16 * rt + m) * KP;   // rows past the chunk's end are zero
+            const T* rb = Kr + (16 * st + m) * KP;
             f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
             for (int kb = 0; kb < NKD; ++kb)
@@ -195,6 +201,7 @@ __global__ __launch_bounds__(256) void prep_kernel(PrefArgs a) {
                 Am[r * AS + s] = (s < r) ? sb[r] * __expf(sg[r] - sg[s]) * acc[e] : 0.f;
             }
         }
+        __syncthreads();   // the Gram is done with the K rows (they may share T's space)
         // zero the above-diagonal 16 x 16 blocks of T (fragments of 32 tokens read some of them)
         for (int i = tid; i < 6 * 256; i += 256) {
             const int b = i >> 8, e = i & 255;
@@ -240,25 +247,30 @@ __global__ __launch_bounds__(256) void prep_kernel(PrefArgs a) {
         // -W fragments: W^T tile (dt, rt) = sum_s (beta e^g K)^T[d][s] T^T[s][r]
         f32x4 wt[NDT];
 #pragma unroll
-        for (int dt = 0; dt < NDT; ++dt) {
-            wt[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
+        for (int dt = 0; dt < NDT; ++dt) wt[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-            for (int kb = 0; kb < NKT; ++kb)
-                if (kb <= kbmax)
+        for (int kb = 0; kb < NKT; ++kb)
+            if (kb <= kbmax)
+#pragma unroll
+                for (int dt = 0; dt < NDT; ++dt)
                     wt[dt] = M::mma(row_frag_ks<E>(Kt + (16 * dt + m) * TP, kb * KB, j, sbe), Tf[kb], wt[dt]);
-        }
 #pragma unroll
         for (int kd = 0; kd < NKD; ++kd)
             st_frag(rec + Ly::A_W + (size_t)(rt * NKD + kd) * Ly::FR, lane, M::from_acc(wt, kd, -1.f));
         // Ut tile (rt, vt) = sum_s T[r][s] (beta V)[s][v], stored as accumulators
+        f32x4 ut[NDT];
+#pragma unroll
+        for (int vt = 0; vt < NDT; ++vt) ut[vt] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int kb = 0; kb < NKT; ++kb)
+            if (kb <= kbmax)
+#pragma unroll
+                for (int vt = 0; vt < NDT; ++vt)
+                    ut[vt] = M::mma(Tf[kb], row_frag_ks<E>(Vt + (16 * vt + m) * TP, kb * KB, j, sb), ut[vt]);
 #pragma unroll
         for (int vt = 0; vt < NDT; ++vt) {
-            f32x4 u = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-            for (int kb = 0; kb < NKT; ++kb)
-                if (kb <= kbmax) u = M::mma(Tf[kb], row_frag_ks<E>(Vt + (16 * vt + m) * TP, kb * KB, j, sb), u);
             T* dst = reinterpret_cast<T*>(rec + Ly::A_UT) + ((size_t)(vt * 4 + rt) * 64 + lane) * 4;
-            store4(dst, make_float4(u[0], u[1], u[2], u[3]));
+            store4(dst, make_float4(ut[vt][0], ut[vt][1], ut[vt][2], ut[vt][3]));
         }
     } else {
         // plain linear attention: Khat = K, Ut = V
@@ -320,15 +332,17 @@ __device__ __forceinline__ void wait_vmcnt() {
     __builtin_amdgcn_s_waitcnt((N & 15) | (7 << 4) | (15 << 8) | ((N >> 4) << 14));
 }
 
+// Byte offset, within a prep record, of 16-byte unit u of a chain slot: -W and Khat^T as they
+// are, then this workgroup's Ut columns, then the decay.
 template <int D, class E>
-__device__ __forceinline__ const unsigned char* chain_src(const unsigned char* recA, int cgw, int u) {
+__device__ __forceinline__ unsigned chain_ofs(int cgw, int u) {
     using C = ChainCfg<D, E>;
     using Ly = Layout<D, E>;
     constexpr int U1 = (int)(C::S_UT / 16), U2 = (int)(C::UTSUB / 16);
     u = u < C::UNITS ? u : C::UNITS - 1;
-    if (u < U1) return recA + (size_t)u * 16;
-    if (u < U1 + U2) return recA + Ly::A_UT + (size_t)cgw * C::UTSUB + (size_t)(u - U1) * 16;
-    return recA + Ly::A_DEC;   // the decay (one unit; the 12 bytes after it are not used)
+    if (u < U1) return (unsigned)u * 16u;
+    if (u < U1 + U2) return (unsigned)(Ly::A_UT + (size_t)cgw * C::UTSUB + (size_t)(u - U1) * 16);
+    return (unsigned)Ly::A_DEC;   // the decay (one unit; the 12 bytes after it are not used)
 }
 
 // Direct-to-LDS load of 16 bytes per lane: lane l's bytes land at LDS address lds_base + 16 l.
@@ -353,20 +367,21 @@ __device__ __forceinline__ unsigned lds_addr(const void* p) {
 // One loader wave's share of a chunk: BPW 1 KB blocks. Blocks past the slot's end repeat the
 // last block, so both loader waves issue the same count.
 template <int D, class E>
-__device__ __forceinline__ void chain_issue_slot(unsigned char* slot, const unsigned char* recA, int cgw, int lw,
-                                                 int lane) {
+__device__ __forceinline__ void chain_issue_slot(unsigned char* slot, const unsigned char* recA, const unsigned* srcofs,
+                                                 int lw) {
     using C = ChainCfg<D, E>;
     const unsigned base = lds_addr(slot);
 #pragma unroll
     for (int i = 0; i < C::BPW; ++i) {
-        int blk = lw + 2 * i;
-        blk = blk < C::NBLK ? blk : C::NBLK - 1;
-        dma16(chain_src<D, E>(recA, cgw, blk * 64 + lane), base + (unsigned)blk * 1024u);
+        const int blk = lw + 2 * i < C::NBLK ? lw + 2 * i : C::NBLK - 1;
+        dma16(recA + srcofs[i], base + (unsigned)blk * 1024u);
     }
 }
 
 template <int D, class E, bool DELTA>
-__global__ __launch_bounds__(256) void chain_kernel(PrefArgs a) {
+// One workgroup per CU (its LDS ring), so one wave per SIMD: let the compiler use the whole
+// register file, which keeps every fragment read of a chunk in flight at once.
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) void chain_kernel(PrefArgs a) {
     using T = typename E::T;
     using M = MM<E>;
     using Ly = Layout<D, E>;
@@ -379,16 +394,23 @@ __global__ __launch_bounds__(256) void chain_kernel(PrefArgs a) {
     const int xcd = blockIdx.x & 7, sl = blockIdx.x >> 3;
     const int cgw = sl % C::NCW, bh = (sl / C::NCW) * 8 + xcd;
     if (bh >= a.BH) return;
-    const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63, j = lane >> 4, m = lane & 15;
+    const int tid = threadIdx.x, lane = tid & 63, j = lane >> 4, m = lane & 15;
+    const int w = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave-uniform
     const int nch = a.nchunks;
     const unsigned char* rec0 = a.ws + (size_t)bh * nch * Ly::REC;
 
     // loader waves: chunk c + NS - 1 is issued at step c into the slot freed at step c - 1;
-    // before each barrier a loader waits only for the chunk the compute waves need next
+    // before each barrier a loader waits only for the chunk the compute waves need next. The
+    // per-lane source offsets within a record are the same for every chunk.
+    unsigned srcofs[C::BPW];
     if (w >= 2) {
+#pragma unroll
+        for (int i = 0; i < C::BPW; ++i) {
+            const int blk = w - 2 + 2 * i < C::NBLK ? w - 2 + 2 * i : C::NBLK - 1;
+            srcofs[i] = chain_ofs<D, E>(cgw, blk * 64 + lane);
+        }
         for (int c = 0; c < NS - 1; ++c)
-            chain_issue_slot<D, E>(smem + (size_t)c * C::SLOT, rec0 + (size_t)min(c, nch - 1) * Ly::REC, cgw, w - 2,
-                                   lane);
+            chain_issue_slot<D, E>(smem + (size_t)c * C::SLOT, rec0 + (size_t)min(c, nch - 1) * Ly::REC, srcofs, w - 2);
         wait_vmcnt<C::INFLIGHT * C::BPW>();
     }
     const int cg = 2 * cgw + (w & 1);          // 16-column group of a compute wave
@@ -407,8 +429,8 @@ __global__ __launch_bounds__(256) void chain_kernel(PrefArgs a) {
         if (w >= 2) {
             // always issue (clamped to the last chunk) so the outstanding count stays fixed
             const int cn = c + NS - 1;
-            chain_issue_slot<D, E>(smem + (size_t)(cn % NS) * C::SLOT, rec0 + (size_t)min(cn, nch - 1) * Ly::REC, cgw,
-                                   w - 2, lane);
+            chain_issue_slot<D, E>(smem + (size_t)(cn % NS) * C::SLOT, rec0 + (size_t)min(cn, nch - 1) * Ly::REC, srcofs,
+                                   w - 2);
             wait_vmcnt<C::INFLIGHT * C::BPW>();
         } else {
             const unsigned char* slot = smem + (size_t)(c % NS) * C::SLOT;
@@ -426,11 +448,15 @@ __global__ __launch_bounds__(256) void chain_kernel(PrefArgs a) {
                 U[rt] = f32x4{x.x, x.y, x.z, x.w};
             }
             if constexpr (DELTA) {
+                // k outer, the four independent token tiles inner: consecutive MFMAs never
+                // depend on each other, so the matrix pipe is not stalled on MFMA latency
+                frag wf[4 * NKD];   // all -W fragments first: one batch of LDS reads
 #pragma unroll
-                for (int rt = 0; rt < 4; ++rt)
+                for (int f = 0; f < 4 * NKD; ++f) wf[f] = ld_frag<frag>(slot + Ly::A_W + (size_t)f * Ly::FR, lane);
 #pragma unroll
-                    for (int kd = 0; kd < NKD; ++kd)
-                        U[rt] = M::mma(ld_frag<frag>(slot + Ly::A_W + (size_t)(rt * NKD + kd) * Ly::FR, lane), Hf[kd], U[rt]);
+                for (int kd = 0; kd < NKD; ++kd)
+#pragma unroll
+                    for (int rt = 0; rt < 4; ++rt) U[rt] = M::mma(wf[rt * NKD + kd], Hf[kd], U[rt]);
             }
             frag Uf[NKT];
 #pragma unroll
@@ -439,15 +465,17 @@ __global__ __launch_bounds__(256) void chain_kernel(PrefArgs a) {
                 st_frag(recB + Ly::B_U + (size_t)(cg * NKT + kt) * Ly::FR, lane, Uf[kt]);
             }
             const float dec = *reinterpret_cast<const float*>(slot + C::S_DEC);
+            if constexpr (DELTA) {
 #pragma unroll
-            for (int dt = 0; dt < NDT; ++dt) {
-                f32x4 h = H[dt];
-                if constexpr (DELTA) h = f32x4{h[0] * dec, h[1] * dec, h[2] * dec, h[3] * dec};
-#pragma unroll
-                for (int kt = 0; kt < NKT; ++kt)
-                    h = M::mma(ld_frag<frag>(slot + Ly::A_KH + (size_t)(dt * NKT + kt) * Ly::FR, lane), Uf[kt], h);
-                H[dt] = h;
+                for (int dt = 0; dt < NDT; ++dt) H[dt] = f32x4{H[dt][0] * dec, H[dt][1] * dec, H[dt][2] * dec, H[dt][3] * dec};
             }
+            frag kf[NDT * NKT];   // all Khat^T fragments first
+#pragma unroll
+            for (int f = 0; f < NDT * NKT; ++f) kf[f] = ld_frag<frag>(slot + Ly::A_KH + (size_t)f * Ly::FR, lane);
+#pragma unroll
+            for (int kt = 0; kt < NKT; ++kt)
+#pragma unroll
+                for (int dt = 0; dt < NDT; ++dt) H[dt] = M::mma(kf[dt * NKT + kt], Uf[kt], H[dt]);
         }
         lds_barrier();
     }
@@ -471,9 +499,13 @@ __global__ __launch_bounds__(256) void output_kernel(PrefArgs a) {
     using Ly = Layout<D, E>;
     using frag = typename M::frag;
     constexpr int KB = M::KB, NKD = Ly::NKD, NKT = Ly::NKT, NDT = Ly::NDT;
-    __shared__ float sg[CH];
-    __shared__ __align__(16) unsigned char sP[4 * NKT * 1024];   // P fragments [rt][kt]
-    __shared__ __align__(16) unsigned char sQ[4 * NKD * 1024];   // e^g Q fragments [rt][kd]
+    constexpr int KP = D + 8;   // row stride of the staged Q and K tiles (elements)
+    extern __shared__ __align__(16) unsigned char smem[];
+    unsigned char* sP = smem;                                    // P fragments [rt][kt]
+    unsigned char* sQ = sP + 4 * NKT * 1024;                     // e^g Q fragments [rt][kd]
+    T* Qr = reinterpret_cast<T*>(sQ + 4 * NKD * 1024);           // [CH][KP] Q rows
+    T* Kr = Qr + CH * KP;                                        // [CH][KP] K rows
+    float* sg = reinterpret_cast<float*>(Kr + CH * KP);          // g
 
     const int c = blockIdx.x, bh = blockIdx.y;
     const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63, j = lane >> 4, m = lane & 15;
@@ -501,6 +533,21 @@ __global__ __launch_bounds__(256) void output_kernel(PrefArgs a) {
                 Uf[iv][kt] = ld_frag<frag>(recB + Ly::B_U + (size_t)(vt * NKT + kt) * Ly::FR, lane);
         }
     }
+    {   // Q and K tiles into LDS, 16 bytes per lane; rows past the chunk's end are zero
+        constexpr int EPU = 16 / sizeof(T);          // elements per 16-byte unit
+        constexpr int UPR = D / EPU;                 // units per row
+#pragma unroll
+        for (int i = 0; i < CH * UPR / 256; ++i) {
+            const int u = tid + 256 * i, r = u / UPR, cu = u % UPR;
+            uint4 xq = {0u, 0u, 0u, 0u}, xk = xq;
+            if (r < n) {
+                xq = *reinterpret_cast<const uint4*>(qp + (size_t)r * D + cu * EPU);
+                xk = *reinterpret_cast<const uint4*>(kp + (size_t)r * D + cu * EPU);
+            }
+            *reinterpret_cast<uint4*>(Qr + r * KP + cu * EPU) = xq;
+            *reinterpret_cast<uint4*>(Kr + r * KP + cu * EPU) = xk;
+        }
+    }
     if (w == 0) {
         float la = 0.f;
         if (DELTA && lane < n) la = a.log_alpha[tok0 + lane];
@@ -511,13 +558,13 @@ __global__ __launch_bounds__(256) void output_kernel(PrefArgs a) {
         // wave w: token tile rt = w. P^T tiles (st, rt) for st <= rt, then P fragments.
         const int rt = w;
         const int r = 16 * rt + m;   // this lane's token as the B-operand column
-        const T* rq = (r < n) ? qp + (size_t)r * D : nullptr;
+        const T* rq = Qr + r * KP;
         f32x4 pt[4];
 #pragma unroll
         for (int st = 0; st < 4; ++st) {
             pt[st] = f32x4{0.f, 0.f, 0.f, 0.f};
             if (st <= rt) {
-                const T* rk = (16 * st + m < n) ? kp + (size_t)(16 * st + m) * D : nullptr;
+                const T* rk = Kr + (16 * st + m) * KP;
 #pragma unroll
                 for (int kd = 0; kd < NKD; ++kd)
                     pt[st] = M::mma(row_frag<E>(rk, kd * KB, j, 1.f), row_frag<E>(rq, kd * KB, j, 1.f), pt[st]);
@@ -540,18 +587,23 @@ __global__ __launch_bounds__(256) void output_kernel(PrefArgs a) {
     for (int iv = 0; iv < NVW; ++iv) {
         const int vt = w + 4 * iv;
         if (vt >= NDT) break;
+        f32x4 acc[4];
+#pragma unroll
+        for (int rt = 0; rt < 4; ++rt) acc[rt] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int kd = 0; kd < NKD; ++kd)
+#pragma unroll
+            for (int rt = 0; rt < 4; ++rt) acc[rt] = M::mma(Hc[iv][kd], ld_frag<frag>(sQ + (rt * NKD + kd) * 1024, lane), acc[rt]);
+#pragma unroll
+        for (int kt = 0; kt < NKT; ++kt)
+#pragma unroll
+            for (int rt = 0; rt < 4; ++rt)
+                if (kt <= (16 * rt + 15) / KB) acc[rt] = M::mma(Uf[iv][kt], ld_frag<frag>(sP + (rt * NKT + kt) * 1024, lane), acc[rt]);
 #pragma unroll
         for (int rt = 0; rt < 4; ++rt) {
-            f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-            for (int kd = 0; kd < NKD; ++kd) acc = M::mma(Hc[iv][kd], ld_frag<frag>(sQ + (rt * NKD + kd) * 1024, lane), acc);
-            const int kbmax = (16 * rt + 15) / KB;
-#pragma unroll
-            for (int kt = 0; kt < NKT; ++kt)
-                if (kt <= kbmax) acc = M::mma(Uf[iv][kt], ld_frag<frag>(sP + (rt * NKT + kt) * 1024, lane), acc);
             // lane (j, m): O[token 16 rt + m][16 vt + 4 j .. + 3]
             const int r = 16 * rt + m;
-            if (r < n) store4(op + (size_t)r * D + 16 * vt + 4 * j, make_float4(acc[0], acc[1], acc[2], acc[3]));
+            if (r < n) store4(op + (size_t)r * D + 16 * vt + 4 * j, make_float4(acc[rt][0], acc[rt][1], acc[rt][2], acc[rt][3]));
         }
     }
 }
@@ -565,8 +617,12 @@ __global__ void copy_state_kernel(const float* __restrict__ src, float* __restri
 template <int D, class E, bool DELTA>
 static int launch_prefill_t(const PrefArgs& a, hipStream_t stream) {
     using T = typename E::T;
+    using Ly = Layout<D, E>;
     constexpr int TP = CH + 8, AS = CH + 4;
-    const size_t lds = (size_t)2 * D * TP * sizeof(T) + (size_t)2 * CH * AS * 4 + 4 * CH * 4;
+    constexpr int KP = D + 8;
+    constexpr bool KROW_IN_T = (size_t)CH * KP * sizeof(T) <= (size_t)CH * AS * 4;
+    const size_t lds = (size_t)2 * D * TP * sizeof(T) + (size_t)2 * CH * AS * 4 + 4 * CH * 4 +
+                       (KROW_IN_T ? 0 : (size_t)CH * KP * sizeof(T));
     static bool attr_done = false;  // benign race: every caller sets the same value
     if (!attr_done) {
         if (hipFuncSetAttribute(reinterpret_cast<const void*>(&prep_kernel<D, E, DELTA>),
@@ -586,7 +642,15 @@ static int launch_prefill_t(const PrefArgs& a, hipStream_t stream) {
     }
     const int nslot = (a.BH + 7) / 8;
     hipLaunchKernelGGL((chain_kernel<D, E, DELTA>), dim3(8 * nslot * CC::NCW), dim3(256), lds_chain, stream, a);
-    hipLaunchKernelGGL((output_kernel<D, E, DELTA>), dim3(a.nchunks, a.BH), dim3(256), 0, stream, a);
+    const size_t lds_out = (size_t)4 * (Ly::NKT + Ly::NKD) * 1024 + (size_t)2 * CH * (D + 8) * sizeof(T) + CH * 4;
+    static bool attr_out = false;
+    if (!attr_out) {
+        if (hipFuncSetAttribute(reinterpret_cast<const void*>(&output_kernel<D, E, DELTA>),
+                                hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds_out) != hipSuccess)
+            return -1;
+        attr_out = true;
+    }
+    hipLaunchKernelGGL((output_kernel<D, E, DELTA>), dim3(a.nchunks, a.BH), dim3(256), lds_out, stream, a);
     return hipGetLastError() == hipSuccess ? 0 : -1;
 }
 
