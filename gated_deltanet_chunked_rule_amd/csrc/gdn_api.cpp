@@ -66,7 +66,7 @@ int validate_prefill(const void* q, const void* k, const void* v, const float* b
     const size_t esz = dtype == GDN_BF16 ? 2 : 4;
     const size_t BH = (size_t)B * H;
     const size_t tok = BH * (size_t)L;
-    const size_t need = gdn::prefill_workspace_bytes((long)BH, L, Dk, dtype);
+    const size_t need = gdn::prefill_workspace_min_bytes((long)BH, L, Dk, dtype);
     if (need > 0) {
         if (!workspace || workspace_bytes < need) return GDN_ERR_WORKSPACE;
         if (!aligned(workspace, 256)) return GDN_ERR_ALIGN;
@@ -75,7 +75,7 @@ int validate_prefill(const void* q, const void* k, const void* v, const float* b
                         rng(beta, beta ? tok * 4 : 0), rng(log_alpha, log_alpha ? tok * 4 : 0),
                         rng(h0, h0 ? BH * Dk * Dv * 4 : 0)};
     const Range ro = rng(o, tok * Dv * esz), rh = rng(h_final, BH * Dk * Dv * 4);
-    const Range rw = rng(workspace, workspace ? need : 0);
+    const Range rw = rng(workspace, workspace && need ? workspace_bytes : 0);
     for (int i = 0; i < 6; ++i) {
         if (overlap(ro, in[i]) || overlap(rw, in[i])) return GDN_ERR_ALIAS;
         if (i == 5 && h0 == h_final) continue;  // in-place state update is allowed
@@ -94,7 +94,7 @@ int prefill(const void* q, const void* k, const void* v, const float* beta, cons
     st = check_device();
     if (st != GDN_OK) return st;
     return gdn::launch_prefill(q, k, v, beta, log_alpha, h0, o, h_final, B * H, L, Dk, dtype, delta, workspace,
-                               static_cast<hipStream_t>(stream)) == 0
+                               workspace_bytes, static_cast<hipStream_t>(stream)) == 0
                ? GDN_OK
                : GDN_ERR_LAUNCH;
 }

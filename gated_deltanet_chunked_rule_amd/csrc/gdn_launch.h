@@ -8,10 +8,11 @@ namespace gdn {
 int launch_decode(const void* q, const void* k, const void* v, const float* beta, const float* log_alpha,
                   float* state, void* o, long slices, int D, int dtype, hipStream_t stream);
 
-size_t prefill_workspace_bytes(long BH, long L, int D, int dtype);
+size_t prefill_workspace_bytes(long BH, long L, int D, int dtype);      // preferred
+size_t prefill_workspace_min_bytes(long BH, long L, int D, int dtype);  // smallest accepted
 
 int launch_prefill(const void* q, const void* k, const void* v, const float* beta, const float* log_alpha,
                    const float* h0, void* o, float* h_final, int BH, long L, int D, int dtype, bool delta,
-                   void* ws, hipStream_t stream);
+                   void* ws, size_t ws_bytes, hipStream_t stream);
 
 }  // namespace gdn

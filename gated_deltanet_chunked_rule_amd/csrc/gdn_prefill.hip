@@ -27,6 +27,8 @@
 //   output_kernel (one workgroup per chunk and head): P = (Q K^T) gated and masked, then
 //                 O^T = H^T (e^g Q)^T + U^T P^T, stored four value columns per lane.
 // Plain linear attention uses the same kernels with T = I, W = 0, Ut = V, g = 0.
+#include <mutex>
+
 #include "gdn_mfma.h"
 #include "gdn_launch.h"
 
@@ -56,14 +58,35 @@ struct Layout {
     static constexpr size_t REC = REC_A + REC_B;
 };
 
+size_t prefill_record_bytes(int D, int dtype) {
+    if (D == 128 && dtype == 0) return Layout<128, BF16>::REC;
+    if (D == 128) return Layout<128, F32>::REC;
+    if (D == 64 && dtype == 0) return Layout<64, BF16>::REC;
+    return Layout<64, F32>::REC;
+}
+
+// Preferred workspace: the whole sequence if it is short, else NBUF segment buffers of about
+// SEG_TARGET bytes each, so that the three stages of consecutive segments overlap and the
+// buffers can stay resident in the 256 MB Infinity Cache between the stage that writes them
+// and the stage that reads them.
+static constexpr size_t SEG_TARGET = (size_t)96 << 20;
+static constexpr int NBUF = 2;
+
 size_t prefill_workspace_bytes(long BH, long L, int D, int dtype) {
-    const long nchunks = (L + CH - 1) / CH;
-    size_t rec = 0;
-    if (D == 128 && dtype == 0) rec = Layout<128, BF16>::REC;
-    else if (D == 128) rec = Layout<128, F32>::REC;
-    else if (D == 64 && dtype == 0) rec = Layout<64, BF16>::REC;
-    else rec = Layout<64, F32>::REC;
-    return (size_t)BH * nchunks * rec;
+    const long nch = (L + CH - 1) / CH;
+    const size_t rec = prefill_record_bytes(D, dtype) * (size_t)BH;   // one chunk of every slice
+    long seg = (long)(SEG_TARGET / rec);
+    seg = seg < 4 ? 4 : seg;
+    if (nch <= NBUF * seg) return (size_t)nch * rec;                   // one segment
+    return NBUF * (size_t)seg * rec;
+}
+
+// Smallest workspace a call accepts: NBUF segment buffers of one chunk each (or the whole
+// sequence when it is shorter than that).
+size_t prefill_workspace_min_bytes(long BH, long L, int D, int dtype) {
+    const long nch = (L + CH - 1) / CH;
+    const size_t rec = prefill_record_bytes(D, dtype) * (size_t)BH;
+    return (size_t)(nch < NBUF ? nch : NBUF) * rec;
 }
 
 struct PrefArgs {
@@ -75,10 +98,12 @@ struct PrefArgs {
     const float* h0;
     void* o;
     float* h_final;
-    unsigned char* ws;
+    unsigned char* ws;   // this segment's buffer: segcap records per slice
     long L;
     int BH;
-    int nchunks;
+    int c0;              // first chunk of the segment
+    int nseg;            // chunks in the segment
+    int segcap;          // records per slice in the buffer
 };
 
 // inclusive prefix sum over the 64 lanes of a wave
@@ -140,14 +165,14 @@ __global__ __launch_bounds__(256) void prep_kernel(PrefArgs a) {
     float* skh = sb + CH;                          // e^{g_C - g}
     T* Kr = KROW_IN_T ? reinterpret_cast<T*>(Tm) : reinterpret_cast<T*>(skh + CH);
 
-    const int c = blockIdx.x, bh = blockIdx.y;
+    const int cl = blockIdx.x, bh = blockIdx.y;     // chunk within the segment, slice
     const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63, j = lane >> 4, m = lane & 15;
-    const long t0 = (long)c * CH;
+    const long t0 = (long)(a.c0 + cl) * CH;
     const int n = (int)min((long)CH, a.L - t0);
     const size_t tok0 = (size_t)bh * a.L + t0;
     const T* kp = static_cast<const T*>(a.k) + tok0 * D;
     const T* vp = static_cast<const T*>(a.v) + tok0 * D;
-    unsigned char* rec = a.ws + ((size_t)bh * a.nchunks + c) * Ly::REC;
+    unsigned char* rec = a.ws + ((size_t)bh * a.segcap + cl) * Ly::REC;
 
     if (w == 0) {
         float la = 0.f, bt = 0.f;
@@ -291,32 +316,35 @@ __global__ __launch_bounds__(256) void prep_kernel(PrefArgs a) {
 // ---------------------------------------------------------------------------------------------
 // stage 2: the sequential chunk-to-chunk pass, state resident in registers
 // ---------------------------------------------------------------------------------------------
-// Chain workgroup: one slice (batch, head) and 32 value columns, four waves. Waves 0 and 1 each
-// own 16 columns of the fp32 state (all Dk rows) in accumulator registers for the whole
-// sequence. Waves 2 and 3 stream the per-chunk operands (-W and Khat^T fragments, shared by all
-// columns, plus this workgroup's Ut columns and the chunk decay) from the workspace into a ring
-// of NS LDS slots, NS - 1 chunks ahead of the compute waves, so the sequential chain never waits
-// on a global-memory round trip.
+// Chain workgroup: one slice (batch, head) and 16 value columns, four waves. The fp32 state of
+// those columns (Dk x 16) is split by rows between the two compute waves, each holding its half
+// in accumulator registers for the whole sequence; per chunk they exchange their fp32 partial
+// products W H through LDS (4 KB each), so each wave's chain step is half the MFMA work. Waves 2
+// and 3 stream the per-chunk operands (-W and Khat^T fragments, this workgroup's Ut columns, the
+// chunk decay) from the workspace into a ring of NS LDS slots, NS - 1 chunks ahead, so the
+// sequential chain never waits on a global-memory round trip.
 template <int D, class E>
 struct ChainCfg {
     using Ly = Layout<D, E>;
-    static constexpr int CGW = 32;                                       // columns per workgroup
+    static constexpr int CGW = 16;                                       // columns per workgroup
     static constexpr int NCW = D / CGW;                                  // workgroups per slice
-    static constexpr size_t UTSUB = (size_t)2 * 4 * 64 * 4 * sizeof(typename E::T);  // Ut bytes of 32 columns
+    static constexpr size_t UTSUB = (size_t)4 * 64 * 4 * sizeof(typename E::T);  // Ut bytes of 16 columns
     static constexpr size_t S_UT = Ly::A_UT;                             // -W and Khat^T precede
     static constexpr size_t S_DEC = S_UT + UTSUB;
     static constexpr int UNITS = (int)((S_DEC + 16) / 16);               // 16-byte units per slot
     static constexpr int NBLK = (UNITS + 63) / 64;                       // 1 KB wave blocks per slot
     static constexpr int BPW = (NBLK + 1) / 2;                           // blocks per loader wave
     static constexpr size_t SLOT = (size_t)NBLK * 1024;
-    static constexpr int NS = SLOT * 4 <= 152 * 1024 ? 4 : (SLOT * 3 <= 152 * 1024 ? 3 : 2);
+    static constexpr size_t XBYTES = (size_t)2 * 4 * 64 * 16;           // partial W H of both halves
+    static constexpr int NS = SLOT * 4 + XBYTES <= 156 * 1024 ? 4 : (SLOT * 3 + XBYTES <= 156 * 1024 ? 3 : 2);
     static constexpr int INFLIGHT = NS - 2;                              // chunks still loading at a barrier
 };
 
-// Barrier of the chain workgroup. Only LDS is shared between its waves, and only the loader
-// waves write it, through direct-to-LDS loads whose completion they establish themselves with
-// wait_vmcnt before arriving; so the barrier waits for LDS reads (lgkmcnt) and nothing else:
-// neither outstanding global stores nor the loads still in flight for later chunks.
+// Barrier of the chain workgroup. Only LDS is shared between its waves: the loader waves fill it
+// with direct-to-LDS loads whose completion they establish themselves (wait_vmcnt) before
+// arriving, the compute waves read it and exchange partial products through it with ordinary
+// LDS writes. So the barrier waits for LDS operations (lgkmcnt) and nothing else: neither
+// outstanding global stores nor the loads still in flight for later chunks.
 __device__ __forceinline__ void lds_barrier() {
     asm volatile("" ::: "memory");
     __builtin_amdgcn_s_waitcnt(15 | (7 << 4) | (0 << 8) | (3 << 14));   // lgkmcnt(0)
@@ -378,9 +406,9 @@ __device__ __forceinline__ void chain_issue_slot(unsigned char* slot, const unsi
     }
 }
 
-template <int D, class E, bool DELTA>
 // One workgroup per CU (its LDS ring), so one wave per SIMD: let the compiler use the whole
 // register file, which keeps every fragment read of a chunk in flight at once.
+template <int D, class E, bool DELTA>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) void chain_kernel(PrefArgs a) {
     using T = typename E::T;
     using M = MM<E>;
@@ -388,44 +416,50 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
     using C = ChainCfg<D, E>;
     using frag = typename M::frag;
     constexpr int NKD = Ly::NKD, NKT = Ly::NKT, NDT = Ly::NDT, NS = C::NS;
+    constexpr int HKD = NKD / 2, HDT = NDT / 2;   // fragments / tiles of one row half
     extern __shared__ __align__(16) unsigned char smem[];
+    f32x4* X = reinterpret_cast<f32x4*>(smem + (size_t)NS * C::SLOT);   // [half][rt][lane] partial W H
     // blockIdx -> (slice, column group) so that all column groups of one slice run on the same
     // XCD (workgroups are dealt to the 8 XCDs round-robin) and share its L2.
     const int xcd = blockIdx.x & 7, sl = blockIdx.x >> 3;
-    const int cgw = sl % C::NCW, bh = (sl / C::NCW) * 8 + xcd;
+    const int cg = sl % C::NCW, bh = (sl / C::NCW) * 8 + xcd;
     if (bh >= a.BH) return;
     const int tid = threadIdx.x, lane = tid & 63, j = lane >> 4, m = lane & 15;
     const int w = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave-uniform
-    const int nch = a.nchunks;
-    const unsigned char* rec0 = a.ws + (size_t)bh * nch * Ly::REC;
+    const int nch = a.nseg;
+    const unsigned char* rec0 = a.ws + (size_t)bh * a.segcap * Ly::REC;
 
     // loader waves: chunk c + NS - 1 is issued at step c into the slot freed at step c - 1;
-    // before each barrier a loader waits only for the chunk the compute waves need next. The
+    // before each chunk's first barrier a loader waits only for the chunk needed next. The
     // per-lane source offsets within a record are the same for every chunk.
     unsigned srcofs[C::BPW];
     if (w >= 2) {
 #pragma unroll
         for (int i = 0; i < C::BPW; ++i) {
             const int blk = w - 2 + 2 * i < C::NBLK ? w - 2 + 2 * i : C::NBLK - 1;
-            srcofs[i] = chain_ofs<D, E>(cgw, blk * 64 + lane);
+            srcofs[i] = chain_ofs<D, E>(cg, blk * 64 + lane);
         }
         for (int c = 0; c < NS - 1; ++c)
             chain_issue_slot<D, E>(smem + (size_t)c * C::SLOT, rec0 + (size_t)min(c, nch - 1) * Ly::REC, srcofs, w - 2);
         wait_vmcnt<C::INFLIGHT * C::BPW>();
     }
-    const int cg = 2 * cgw + (w & 1);          // 16-column group of a compute wave
+    const int hh = w & 1;                      // row half of a compute wave
     const int col = 16 * cg + m;
-    f32x4 H[NDT];                              // lane (j, m): H[16 dt + 4 j + e][col]
+    f32x4 H[HDT];                              // lane (j, m): H[16 (hh HDT + t) + 4 j + e][col]
     if (w < 2) {
 #pragma unroll
-        for (int dt = 0; dt < NDT; ++dt)
+        for (int t = 0; t < HDT; ++t)
 #pragma unroll
             for (int e = 0; e < 4; ++e)
-                H[dt][e] = a.h0 ? a.h0[((size_t)bh * D + 16 * dt + 4 * j + e) * D + col] : 0.f;
+                H[t][e] = a.h0 ? a.h0[((size_t)bh * D + 16 * (hh * HDT + t) + 4 * j + e) * D + col] : 0.f;
     }
     lds_barrier();
 
     for (int c = 0; c < nch; ++c) {
+        const unsigned char* slot = smem + (size_t)(c % NS) * C::SLOT;
+        unsigned char* recB = const_cast<unsigned char*>(rec0) + (size_t)c * Ly::REC + Ly::REC_A;
+        f32x4 U[4], Ut[4];
+        frag kf[HDT * NKT];
         if (w >= 2) {
             // always issue (clamped to the last chunk) so the outstanding count stays fixed
             const int cn = c + NS - 1;
@@ -433,57 +467,80 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
                                    w - 2);
             wait_vmcnt<C::INFLIGHT * C::BPW>();
         } else {
-            const unsigned char* slot = smem + (size_t)(c % NS) * C::SLOT;
-            unsigned char* recB = const_cast<unsigned char*>(rec0) + (size_t)c * Ly::REC + Ly::REC_A;
-            frag Hf[NKD];
+            // this half's chunk-start state fragments (also handed to the output stage)
+            frag Hf[HKD];
 #pragma unroll
-            for (int kd = 0; kd < NKD; ++kd) {
-                Hf[kd] = M::from_acc(H, kd);
-                st_frag(recB + Ly::B_H + (size_t)(cg * NKD + kd) * Ly::FR, lane, Hf[kd]);
-            }
-            f32x4 U[4];
-#pragma unroll
-            for (int rt = 0; rt < 4; ++rt) {
-                const float4 x = load4(reinterpret_cast<const T*>(slot + C::S_UT) + ((size_t)((w & 1) * 4 + rt) * 64 + lane) * 4);
-                U[rt] = f32x4{x.x, x.y, x.z, x.w};
+            for (int kk = 0; kk < HKD; ++kk) {
+                Hf[kk] = M::from_acc(H, kk);
+                st_frag(recB + Ly::B_H + (size_t)(cg * NKD + hh * HKD + kk) * Ly::FR, lane, Hf[kk]);
             }
             if constexpr (DELTA) {
-                // k outer, the four independent token tiles inner: consecutive MFMAs never
-                // depend on each other, so the matrix pipe is not stalled on MFMA latency
-                frag wf[4 * NKD];   // all -W fragments first: one batch of LDS reads
+                // partial (-W) H over this half's rows, all four token tiles
+                frag wf[4 * HKD];
 #pragma unroll
-                for (int f = 0; f < 4 * NKD; ++f) wf[f] = ld_frag<frag>(slot + Ly::A_W + (size_t)f * Ly::FR, lane);
+                for (int rt = 0; rt < 4; ++rt)
 #pragma unroll
-                for (int kd = 0; kd < NKD; ++kd)
+                    for (int kk = 0; kk < HKD; ++kk)
+                        wf[rt * HKD + kk] = ld_frag<frag>(slot + Ly::A_W + (size_t)(rt * NKD + hh * HKD + kk) * Ly::FR, lane);
 #pragma unroll
-                    for (int rt = 0; rt < 4; ++rt) U[rt] = M::mma(wf[rt * NKD + kd], Hf[kd], U[rt]);
+                for (int rt = 0; rt < 4; ++rt) U[rt] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                for (int kk = 0; kk < HKD; ++kk)
+#pragma unroll
+                    for (int rt = 0; rt < 4; ++rt) U[rt] = M::mma(wf[rt * HKD + kk], Hf[kk], U[rt]);
+#pragma unroll
+                for (int rt = 0; rt < 4; ++rt) X[(hh * 4 + rt) * 64 + lane] = U[rt];
+            }
+        }
+        lds_barrier();   // partial products exchanged
+        if (w < 2) {
+#pragma unroll
+            for (int rt = 0; rt < 4; ++rt) {
+                const float4 x = load4(reinterpret_cast<const T*>(slot + C::S_UT) + ((size_t)rt * 64 + lane) * 4);
+                Ut[rt] = f32x4{x.x, x.y, x.z, x.w};
+            }
+            // U = (Ut + P_0) + P_1 in this order in both waves, so both hold the same U; each
+            // wave has its own partial in registers and reads the other one
+#pragma unroll
+            for (int rt = 0; rt < 4; ++rt) {
+                f32x4 u = Ut[rt];
+                if constexpr (DELTA) {
+                    const f32x4 po = X[((1 - hh) * 4 + rt) * 64 + lane];
+                    const f32x4 p0 = hh == 0 ? U[rt] : po, p1 = hh == 0 ? po : U[rt];
+                    u = f32x4{(u[0] + p0[0]) + p1[0], (u[1] + p0[1]) + p1[1], (u[2] + p0[2]) + p1[2],
+                              (u[3] + p0[3]) + p1[3]};
+                }
+                U[rt] = u;
             }
             frag Uf[NKT];
 #pragma unroll
             for (int kt = 0; kt < NKT; ++kt) {
                 Uf[kt] = M::from_acc(U, kt);
-                st_frag(recB + Ly::B_U + (size_t)(cg * NKT + kt) * Ly::FR, lane, Uf[kt]);
+                if (hh == 0) st_frag(recB + Ly::B_U + (size_t)(cg * NKT + kt) * Ly::FR, lane, Uf[kt]);
             }
-            const float dec = *reinterpret_cast<const float*>(slot + C::S_DEC);
+#pragma unroll
+            for (int t = 0; t < HDT; ++t)
+#pragma unroll
+                for (int kt = 0; kt < NKT; ++kt)
+                    kf[t * NKT + kt] = ld_frag<frag>(slot + Ly::A_KH + (size_t)((hh * HDT + t) * NKT + kt) * Ly::FR, lane);
             if constexpr (DELTA) {
+                const float dec = *reinterpret_cast<const float*>(slot + C::S_DEC);
 #pragma unroll
-                for (int dt = 0; dt < NDT; ++dt) H[dt] = f32x4{H[dt][0] * dec, H[dt][1] * dec, H[dt][2] * dec, H[dt][3] * dec};
+                for (int t = 0; t < HDT; ++t) H[t] = f32x4{H[t][0] * dec, H[t][1] * dec, H[t][2] * dec, H[t][3] * dec};
             }
-            frag kf[NDT * NKT];   // all Khat^T fragments first
-#pragma unroll
-            for (int f = 0; f < NDT * NKT; ++f) kf[f] = ld_frag<frag>(slot + Ly::A_KH + (size_t)f * Ly::FR, lane);
 #pragma unroll
             for (int kt = 0; kt < NKT; ++kt)
 #pragma unroll
-                for (int dt = 0; dt < NDT; ++dt) H[dt] = M::mma(kf[dt * NKT + kt], Uf[kt], H[dt]);
+                for (int t = 0; t < HDT; ++t) H[t] = M::mma(kf[t * NKT + kt], Uf[kt], H[t]);
         }
-        lds_barrier();
+        lds_barrier();   // slot c and the exchange area may be reused
     }
     if (w < 2) {
 #pragma unroll
-        for (int dt = 0; dt < NDT; ++dt)
+        for (int t = 0; t < HDT; ++t)
 #pragma unroll
-            for (int e = 0; e < 4; ++e) a.h_final[((size_t)bh * D + 16 * dt + 4 * j + e) * D + col] = H[dt][e];
+            for (int e = 0; e < 4; ++e)
+                a.h_final[((size_t)bh * D + 16 * (hh * HDT + t) + 4 * j + e) * D + col] = H[t][e];
     } else {
         wait_vmcnt<0>();   // no LDS write may land after the workgroup ends
     }
@@ -507,15 +564,15 @@ __global__ __launch_bounds__(256) void output_kernel(PrefArgs a) {
     T* Kr = Qr + CH * KP;                                        // [CH][KP] K rows
     float* sg = reinterpret_cast<float*>(Kr + CH * KP);          // g
 
-    const int c = blockIdx.x, bh = blockIdx.y;
+    const int cl = blockIdx.x, bh = blockIdx.y;
     const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63, j = lane >> 4, m = lane & 15;
-    const long t0 = (long)c * CH;
+    const long t0 = (long)(a.c0 + cl) * CH;
     const int n = (int)min((long)CH, a.L - t0);
     const size_t tok0 = (size_t)bh * a.L + t0;
     const T* qp = static_cast<const T*>(a.q) + tok0 * D;
     const T* kp = static_cast<const T*>(a.k) + tok0 * D;
     T* op = static_cast<T*>(a.o) + tok0 * D;
-    const unsigned char* recB = a.ws + ((size_t)bh * a.nchunks + c) * Ly::REC + Ly::REC_A;
+    const unsigned char* recB = a.ws + ((size_t)bh * a.segcap + cl) * Ly::REC + Ly::REC_A;
 
     // this wave's value tiles vt = w, w + 4, ...: fetch the chunk-start state and U fragments
     // first so their latency overlaps the P computation
@@ -615,58 +672,128 @@ __global__ void copy_state_kernel(const float* __restrict__ src, float* __restri
 }
 
 template <int D, class E, bool DELTA>
-static int launch_prefill_t(const PrefArgs& a, hipStream_t stream) {
+struct Launch {
     using T = typename E::T;
     using Ly = Layout<D, E>;
-    constexpr int TP = CH + 8, AS = CH + 4;
-    constexpr int KP = D + 8;
-    constexpr bool KROW_IN_T = (size_t)CH * KP * sizeof(T) <= (size_t)CH * AS * 4;
-    const size_t lds = (size_t)2 * D * TP * sizeof(T) + (size_t)2 * CH * AS * 4 + 4 * CH * 4 +
-                       (KROW_IN_T ? 0 : (size_t)CH * KP * sizeof(T));
-    static bool attr_done = false;  // benign race: every caller sets the same value
-    if (!attr_done) {
-        if (hipFuncSetAttribute(reinterpret_cast<const void*>(&prep_kernel<D, E, DELTA>),
-                                hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds) != hipSuccess)
-            return -1;
-        attr_done = true;
-    }
-    hipLaunchKernelGGL((prep_kernel<D, E, DELTA>), dim3(a.nchunks, a.BH), dim3(256), lds, stream, a);
     using CC = ChainCfg<D, E>;
-    const size_t lds_chain = (size_t)CC::NS * CC::SLOT;
-    static bool attr_chain = false;
-    if (!attr_chain) {
-        if (hipFuncSetAttribute(reinterpret_cast<const void*>(&chain_kernel<D, E, DELTA>),
-                                hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds_chain) != hipSuccess)
-            return -1;
-        attr_chain = true;
+    static constexpr int TP = CH + 8, AS = CH + 4, KP = D + 8;
+    static constexpr bool KROW_IN_T = (size_t)CH * KP * sizeof(T) <= (size_t)CH * AS * 4;
+    static constexpr size_t LDS_PREP = (size_t)2 * D * TP * sizeof(T) + (size_t)2 * CH * AS * 4 + 4 * CH * 4 +
+                                       (KROW_IN_T ? 0 : (size_t)CH * KP * sizeof(T));
+    static constexpr size_t LDS_CHAIN = (size_t)CC::NS * CC::SLOT + CC::XBYTES;
+    static constexpr size_t LDS_OUT = (size_t)4 * (Ly::NKT + Ly::NKD) * 1024 + (size_t)2 * CH * KP * sizeof(T) + CH * 4;
+
+    // raise the dynamic-LDS limits once per process (every caller sets the same values)
+    static bool attributes() {
+        static const bool ok =
+            hipFuncSetAttribute(reinterpret_cast<const void*>(&prep_kernel<D, E, DELTA>),
+                                hipFuncAttributeMaxDynamicSharedMemorySize, (int)LDS_PREP) == hipSuccess &&
+            hipFuncSetAttribute(reinterpret_cast<const void*>(&chain_kernel<D, E, DELTA>),
+                                hipFuncAttributeMaxDynamicSharedMemorySize, (int)LDS_CHAIN) == hipSuccess &&
+            hipFuncSetAttribute(reinterpret_cast<const void*>(&output_kernel<D, E, DELTA>),
+                                hipFuncAttributeMaxDynamicSharedMemorySize, (int)LDS_OUT) == hipSuccess;
+        return ok;
     }
-    const int nslot = (a.BH + 7) / 8;
-    hipLaunchKernelGGL((chain_kernel<D, E, DELTA>), dim3(8 * nslot * CC::NCW), dim3(256), lds_chain, stream, a);
-    const size_t lds_out = (size_t)4 * (Ly::NKT + Ly::NKD) * 1024 + (size_t)2 * CH * (D + 8) * sizeof(T) + CH * 4;
-    static bool attr_out = false;
-    if (!attr_out) {
-        if (hipFuncSetAttribute(reinterpret_cast<const void*>(&output_kernel<D, E, DELTA>),
-                                hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds_out) != hipSuccess)
-            return -1;
-        attr_out = true;
+    static void prep(const PrefArgs& a, hipStream_t s) {
+        hipLaunchKernelGGL((prep_kernel<D, E, DELTA>), dim3(a.nseg, a.BH), dim3(256), LDS_PREP, s, a);
     }
-    hipLaunchKernelGGL((output_kernel<D, E, DELTA>), dim3(a.nchunks, a.BH), dim3(256), lds_out, stream, a);
-    return hipGetLastError() == hipSuccess ? 0 : -1;
+    static void chain(const PrefArgs& a, hipStream_t s) {
+        hipLaunchKernelGGL((chain_kernel<D, E, DELTA>), dim3(8 * ((a.BH + 7) / 8) * CC::NCW), dim3(256), LDS_CHAIN, s, a);
+    }
+    static void output(const PrefArgs& a, hipStream_t s) {
+        hipLaunchKernelGGL((output_kernel<D, E, DELTA>), dim3(a.nseg, a.BH), dim3(256), LDS_OUT, s, a);
+    }
+};
+
+// Two streams and a few events per device, created on first use and kept for the process: the
+// intra-chunk stage of later segments and the output stage of earlier ones run on them while
+// the chain works on the current segment on the caller's stream.
+struct StreamCtx {
+    static constexpr int R = NBUF + 1;   // event ring: an event is re-recorded only after its waits are enqueued
+    std::mutex mu;
+    bool ready = false;
+    hipStream_t sp = nullptr, so = nullptr;
+    hipEvent_t start = nullptr, ev_prep[R] = {}, ev_chain[R] = {}, ev_out[R] = {};
+};
+
+static StreamCtx g_ctx[64];
+
+static bool init_ctx(StreamCtx& c) {
+    if (c.ready) return true;
+    if (hipStreamCreateWithFlags(&c.sp, hipStreamNonBlocking) != hipSuccess) return false;
+    if (hipStreamCreateWithFlags(&c.so, hipStreamNonBlocking) != hipSuccess) return false;
+    if (hipEventCreateWithFlags(&c.start, hipEventDisableTiming) != hipSuccess) return false;
+    for (int i = 0; i < StreamCtx::R; ++i)
+        if (hipEventCreateWithFlags(&c.ev_prep[i], hipEventDisableTiming) != hipSuccess ||
+            hipEventCreateWithFlags(&c.ev_chain[i], hipEventDisableTiming) != hipSuccess ||
+            hipEventCreateWithFlags(&c.ev_out[i], hipEventDisableTiming) != hipSuccess)
+            return false;
+    c.ready = true;
+    return true;
+}
+
+template <int D, class E, bool DELTA>
+static int launch_prefill_t(PrefArgs a, long nch, size_t ws_bytes, hipStream_t stream) {
+    using LN = Launch<D, E, DELTA>;
+    if (!LN::attributes()) return -1;
+    const size_t rec = Layout<D, E>::REC * (size_t)a.BH;
+    if (ws_bytes >= (size_t)nch * rec) {   // whole sequence in one segment, caller's stream only
+        a.c0 = 0; a.nseg = (int)nch; a.segcap = (int)nch;
+        LN::prep(a, stream);
+        LN::chain(a, stream);
+        LN::output(a, stream);
+        return hipGetLastError() == hipSuccess ? 0 : -1;
+    }
+    const int seg = (int)(ws_bytes / (NBUF * rec));   // >= 1 (validated)
+    const size_t buf = (size_t)seg * rec;
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return -1;
+    StreamCtx& cx = g_ctx[dev];
+    std::lock_guard<std::mutex> lk(cx.mu);
+    if (!init_ctx(cx)) return -1;
+    constexpr int R = StreamCtx::R;
+    unsigned char* ws0 = a.ws;
+    const float* h0 = a.h0;
+    bool ok = hipEventRecord(cx.start, stream) == hipSuccess && hipStreamWaitEvent(cx.sp, cx.start, 0) == hipSuccess &&
+              hipStreamWaitEvent(cx.so, cx.start, 0) == hipSuccess;
+    const int nsegs = (int)((nch + seg - 1) / seg);
+    for (int sgi = 0; ok && sgi < nsegs; ++sgi) {
+        PrefArgs b = a;
+        b.c0 = sgi * seg;
+        b.nseg = (int)(nch - b.c0 < seg ? nch - b.c0 : seg);
+        b.segcap = seg;
+        b.ws = ws0 + (size_t)(sgi % NBUF) * buf;
+        b.h0 = sgi == 0 ? h0 : a.h_final;   // later segments continue from the running state
+        // the buffer is free once the output stage of the segment NBUF back has read it
+        if (sgi >= NBUF) ok = ok && hipStreamWaitEvent(cx.sp, cx.ev_out[(sgi - NBUF) % R], 0) == hipSuccess;
+        LN::prep(b, cx.sp);
+        ok = ok && hipEventRecord(cx.ev_prep[sgi % R], cx.sp) == hipSuccess;
+        ok = ok && hipStreamWaitEvent(stream, cx.ev_prep[sgi % R], 0) == hipSuccess;
+        LN::chain(b, stream);
+        ok = ok && hipEventRecord(cx.ev_chain[sgi % R], stream) == hipSuccess;
+        ok = ok && hipStreamWaitEvent(cx.so, cx.ev_chain[sgi % R], 0) == hipSuccess;
+        LN::output(b, cx.so);
+        ok = ok && hipEventRecord(cx.ev_out[sgi % R], cx.so) == hipSuccess;
+    }
+    // the caller's stream continues only after the last output stage
+    ok = ok && hipStreamWaitEvent(stream, cx.ev_out[(nsegs - 1) % R], 0) == hipSuccess;
+    return ok && hipGetLastError() == hipSuccess ? 0 : -1;
 }
 
 int launch_prefill(const void* q, const void* k, const void* v, const float* beta, const float* log_alpha,
                    const float* h0, void* o, float* h_final, int BH, long L, int D, int dtype, bool delta,
-                   void* ws, hipStream_t stream) {
+                   void* ws, size_t ws_bytes, hipStream_t stream) {
     if (L == 0) {
         const size_t n = (size_t)BH * D * D;
         if (h0 == h_final) return 0;
         hipLaunchKernelGGL(copy_state_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, stream, h0, h_final, n);
         return hipGetLastError() == hipSuccess ? 0 : -1;
     }
-    PrefArgs a{q, k, v, beta, log_alpha, h0, o, h_final, static_cast<unsigned char*>(ws), L, BH,
-               (int)((L + CH - 1) / CH)};
-#define GDN_PF(DD, EE)                                                                             \
-    return delta ? launch_prefill_t<DD, EE, true>(a, stream) : launch_prefill_t<DD, EE, false>(a, stream)
+    const long nch = (L + CH - 1) / CH;
+    PrefArgs a{q, k, v, beta, log_alpha, h0, o, h_final, static_cast<unsigned char*>(ws), L, BH, 0, 0, 0};
+#define GDN_PF(DD, EE)                                                                 \
+    return delta ? launch_prefill_t<DD, EE, true>(a, nch, ws_bytes, stream)            \
+                 : launch_prefill_t<DD, EE, false>(a, nch, ws_bytes, stream)
     if (D == 128 && dtype == 0) GDN_PF(128, BF16);
     if (D == 128) GDN_PF(128, F32);
     if (dtype == 0) GDN_PF(64, BF16);

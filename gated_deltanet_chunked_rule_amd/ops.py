@@ -68,11 +68,10 @@ def _prefill(entry, q, k, v, beta, log_alpha, h0, o, h_final, workspace, stream,
     if h_final is None:
         h_final = torch.empty((B, H, D, D), dtype=torch.float32, device=dev)
     _req("h_final", h_final, (B, H, D, D), torch.float32, dev)
-    need = prefill_workspace_size(B, H, L, D, dt)
-    if workspace is None:
-        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
-    elif workspace.numel() * workspace.element_size() < need:
-        raise ValueError(f"workspace has {workspace.numel() * workspace.element_size()} bytes, needs {need}")
+    if workspace is None:   # the preferred size; any size the C ABI accepts works (it checks)
+        workspace = torch.empty(max(prefill_workspace_size(B, H, L, D, dt), 1), dtype=torch.uint8, device=dev)
+    elif not workspace.is_cuda or not workspace.is_contiguous():
+        raise ValueError("workspace must be a contiguous device tensor")
     lib = _lib.load()
     rc = getattr(lib, entry)(_p(q), _p(k), _p(v), _p(beta), _p(log_alpha), _p(h0), _p(o), _p(h_final),
                              B, H, L, D, D, _code(dt), _p(workspace),

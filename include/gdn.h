@@ -26,7 +26,8 @@
  *   - dtype (GDN_BF16 or GDN_F32) is the element type of q, k, v and o. beta, log_alpha and
  *     every state are always fp32.
  *   - Launches are asynchronous on `stream` (a hipStream_t passed as void*; NULL = the null
- *     stream). A return of GDN_OK means the work was enqueued.
+ *     stream). A return of GDN_OK means the work was enqueued. The library never allocates
+ *     device memory; long prefills also use two internal streams (see gdn_prefill_fwd).
  *   - Errors are returned as negative status codes; validation happens before any launch, so
  *     on an error nothing was enqueued and no output was touched.
  *   - Supported sizes: Dk = Dv in {64, 128}; the chunk length is fixed at 64 tokens; any
@@ -59,9 +60,12 @@ enum {
 /* Human-readable name of a status code (static string, never NULL). */
 const char *gdn_status_string(int status);
 
-/* Bytes of device workspace gdn_prefill_fwd / linattn_prefill_fwd need for this shape
- * (the per-chunk operands handed from the intra-chunk stage to the chunk-to-chunk pass).
- * Returns 0 for an unsupported shape. */
+/* Preferred bytes of device workspace for gdn_prefill_fwd / linattn_prefill_fwd at this shape.
+ * The workspace holds the per-chunk operands handed between the three prefill stages. A short
+ * sequence is processed in one segment; a long one in segments whose stages overlap on two
+ * internal streams, with two segment buffers of about 96 MB each. Any workspace of at least
+ * two chunk records per (batch, head) is accepted (one when the sequence has one chunk);
+ * a smaller one just means shorter segments. Returns 0 for an unsupported shape or L = 0. */
 size_t gdn_prefill_workspace_size(int B, int H, int L, int Dk, int Dv, int dtype);
 
 /*
@@ -72,8 +76,12 @@ size_t gdn_prefill_workspace_size(int B, int H, int L, int Dk, int Dv, int dtype
  *   h0          [B,H,Dk,Dv] fp32 initial state, or NULL for zeros
  *   h_final     [B,H,Dk,Dv] fp32 final state; may equal h0 (in-place update), any other
  *               overlap is GDN_ERR_ALIAS
- *   workspace   device buffer of at least gdn_prefill_workspace_size(...) bytes, 256-byte
- *               aligned; its contents are scratch and may be reused after the call completes
+ *   workspace   device buffer, 256-byte aligned, gdn_prefill_workspace_size(...) bytes preferred
+ *               (see above for the minimum); scratch, reusable once the call's work completes
+ * Streams: a call that needs more than one segment also runs work on two internal streams of
+ * the current device (created on first use, default priority), ordered against `stream` with
+ * events: it starts after the work already queued on `stream`, and work queued on `stream`
+ * afterwards starts after all of it. Calls that run segments serialise on a per-device lock.
  * L = 0 copies h0 (or zeros) into h_final. Non-finite inputs propagate; they are not checked.
  */
 int gdn_prefill_fwd(const void *q, const void *k, const void *v,

@@ -40,8 +40,12 @@ def test_status_strings(lib):
 
 def test_workspace_size_query(lib):
     f = lib.gdn_prefill_workspace_size
-    assert f(1, 16, 131072, 128, 128, 0) > 0
-    assert f(1, 1, 64, 128, 128, 0) * 2048 == f(1, 1, 131072, 128, 128, 0)
+    rec = f(1, 1, 64, 128, 128, 0)                     # one chunk record of one slice
+    assert rec > 0
+    assert f(1, 1, 64 * 100, 128, 128, 0) == 100 * rec   # short: the whole sequence, one segment
+    big = f(1, 16, 131072, 128, 128, 0)                  # long: two segment buffers
+    assert big % (2 * 16 * rec) == 0 and big < 2048 * 16 * rec
+    assert 150 << 20 < big <= 200 << 20
     assert f(1, 1, 65, 64, 64, 1) == 2 * f(1, 1, 64, 64, 64, 1)   # a ragged tail costs a whole chunk
     assert f(1, 2, 0, 128, 128, 0) == 0
     assert f(1, 1, 64, 96, 96, 0) == 0        # unsupported head size

@@ -152,6 +152,27 @@ def test_in_place_state_and_chaining():
     assert torch.equal(h, hf_full)
 
 
+@pytest.mark.parametrize("gdn", [True, False])
+def test_segmented_schedule_is_bitwise_identical(gdn):
+    """A small workspace forces many segments (stages overlapped on internal streams); every
+    chunk computes exactly the same arithmetic, so the result equals the one-segment run."""
+    cfg = (inputs.GDN_32K if gdn else inputs.LINATTN_8K).with_(name="seg", B=1, H=3, L=64 * 13 + 5, seed=31)
+    x = inputs.prefill_inputs(cfg)
+    dt = torch.bfloat16
+    q, k, v = (dev_tensor(x[n], dt) for n in ("q", "k", "v"))
+    h0 = dev_tensor(x["h0"], torch.float32)
+    args = (dev_tensor(x["beta"], torch.float32), dev_tensor(x["log_alpha"], torch.float32)) if gdn else ()
+    fn = ops.gdn_prefill_fwd if gdn else ops.linattn_prefill_fwd
+    rec = ops.prefill_workspace_size(1, 1, 64, 128, dt) * cfg.H
+    say(f"case segmented gdn={gdn}")
+    o1, h1 = fn(q, k, v, *args, h0)
+    for seg in (1, 2, 5):   # segment length in chunks: workspace = two buffers of seg records
+        ws = torch.empty(2 * seg * rec, dtype=torch.uint8, device="cuda")
+        o2, h2 = fn(q, k, v, *args, h0, workspace=ws)
+        torch.cuda.synchronize()
+        assert torch.equal(o1, o2) and torch.equal(h1, h2), seg
+
+
 def test_deterministic():
     cfg = inputs.GDN_32K.with_(name="det", B=1, H=4, L=777, seed=5)
     x = inputs.prefill_inputs(cfg)
