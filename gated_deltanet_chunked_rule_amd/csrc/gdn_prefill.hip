@@ -406,10 +406,47 @@ __device__ __forceinline__ void chain_issue_slot(unsigned char* slot, const unsi
     }
 }
 
-// One workgroup per CU (its LDS ring), so one wave per SIMD: let the compiler use the whole
-// register file, which keeps every fragment read of a chunk in flight at once.
-template <int D, class E, bool DELTA>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) void chain_kernel(PrefArgs a) {
+// Loader wave lw (0 or 1) of a chain workgroup: chunk c + NS - 1 is issued at step c into the
+// slot freed at step c - 1; before each chunk's first barrier the loader waits only for the
+// chunk needed next. The per-lane source offsets within a record are the same for every chunk.
+// Two barriers per chunk, like the compute waves.
+template <int D, class E>
+__device__ __forceinline__ void chain_loader(unsigned char* smem, const unsigned char* rec0, int nch, int cg, int lw,
+                                             int lane) {
+    using Ly = Layout<D, E>;
+    using C = ChainCfg<D, E>;
+    constexpr int NS = C::NS;
+    unsigned srcofs[C::BPW];
+#pragma unroll
+    for (int i = 0; i < C::BPW; ++i) {
+        const int blk = lw + 2 * i < C::NBLK ? lw + 2 * i : C::NBLK - 1;
+        srcofs[i] = chain_ofs<D, E>(cg, blk * 64 + lane);
+    }
+    for (int c = 0; c < NS - 1; ++c)
+        chain_issue_slot<D, E>(smem + (size_t)c * C::SLOT, rec0 + (size_t)min(c, nch - 1) * Ly::REC, srcofs, lw);
+    wait_vmcnt<C::INFLIGHT * C::BPW>();
+    lds_barrier();
+    for (int c = 0; c < nch; ++c) {
+        // always issue (clamped to the last chunk) so the outstanding count stays fixed
+        const int cn = c + NS - 1;
+        chain_issue_slot<D, E>(smem + (size_t)(cn % NS) * C::SLOT, rec0 + (size_t)min(cn, nch - 1) * Ly::REC, srcofs, lw);
+        wait_vmcnt<C::INFLIGHT * C::BPW>();
+        lds_barrier();
+        lds_barrier();
+    }
+    wait_vmcnt<0>();   // no LDS write may land after the workgroup ends
+}
+
+// Compute wave HH of a chain workgroup: it owns state rows [HH Dk/2, (HH + 1) Dk/2) of the
+// workgroup's 16 columns. Per chunk:
+//   A  Hf = bf16(H) (also handed to the output stage); partial product P_HH = (-W)[:, half] Hf,
+//      with Ut folded into the accumulators of token tiles 2 HH and 2 HH + 1; P_HH -> LDS;
+//      H *= chunk decay.
+//   B  U = P_HH + P_other (fp32 addition is commutative, so both waves hold the same U);
+//      H += Khat^T[half, :] bf16(U).
+template <int D, class E, bool DELTA, int HH>
+__device__ __forceinline__ void chain_compute(const PrefArgs& a, unsigned char* smem, const unsigned char* rec0,
+                                              int nch, int bh, int cg, int lane) {
     using T = typename E::T;
     using M = MM<E>;
     using Ly = Layout<D, E>;
@@ -417,133 +454,113 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
     using frag = typename M::frag;
     constexpr int NKD = Ly::NKD, NKT = Ly::NKT, NDT = Ly::NDT, NS = C::NS;
     constexpr int HKD = NKD / 2, HDT = NDT / 2;   // fragments / tiles of one row half
-    extern __shared__ __align__(16) unsigned char smem[];
-    f32x4* X = reinterpret_cast<f32x4*>(smem + (size_t)NS * C::SLOT);   // [half][rt][lane] partial W H
-    // blockIdx -> (slice, column group) so that all column groups of one slice run on the same
-    // XCD (workgroups are dealt to the 8 XCDs round-robin) and share its L2.
-    const int xcd = blockIdx.x & 7, sl = blockIdx.x >> 3;
-    const int cg = sl % C::NCW, bh = (sl / C::NCW) * 8 + xcd;
-    if (bh >= a.BH) return;
-    const int tid = threadIdx.x, lane = tid & 63, j = lane >> 4, m = lane & 15;
-    const int w = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave-uniform
-    const int nch = a.nseg;
-    const unsigned char* rec0 = a.ws + (size_t)bh * a.segcap * Ly::REC;
-
-    // loader waves: chunk c + NS - 1 is issued at step c into the slot freed at step c - 1;
-    // before each chunk's first barrier a loader waits only for the chunk needed next. The
-    // per-lane source offsets within a record are the same for every chunk.
-    unsigned srcofs[C::BPW];
-    if (w >= 2) {
-#pragma unroll
-        for (int i = 0; i < C::BPW; ++i) {
-            const int blk = w - 2 + 2 * i < C::NBLK ? w - 2 + 2 * i : C::NBLK - 1;
-            srcofs[i] = chain_ofs<D, E>(cg, blk * 64 + lane);
-        }
-        for (int c = 0; c < NS - 1; ++c)
-            chain_issue_slot<D, E>(smem + (size_t)c * C::SLOT, rec0 + (size_t)min(c, nch - 1) * Ly::REC, srcofs, w - 2);
-        wait_vmcnt<C::INFLIGHT * C::BPW>();
-    }
-    const int hh = w & 1;                      // row half of a compute wave
+    f32x4* X = reinterpret_cast<f32x4*>(smem + (size_t)NS * C::SLOT);   // [half][rt][lane] partial products
+    const int j = lane >> 4, m = lane & 15;
     const int col = 16 * cg + m;
-    f32x4 H[HDT];                              // lane (j, m): H[16 (hh HDT + t) + 4 j + e][col]
-    if (w < 2) {
+    f32x4 H[HDT];   // lane (j, m): H[16 (HH HDT + t) + 4 j + e][col]
 #pragma unroll
-        for (int t = 0; t < HDT; ++t)
+    for (int t = 0; t < HDT; ++t)
 #pragma unroll
-            for (int e = 0; e < 4; ++e)
-                H[t][e] = a.h0 ? a.h0[((size_t)bh * D + 16 * (hh * HDT + t) + 4 * j + e) * D + col] : 0.f;
-    }
+        for (int e = 0; e < 4; ++e)
+            H[t][e] = a.h0 ? a.h0[((size_t)bh * D + 16 * (HH * HDT + t) + 4 * j + e) * D + col] : 0.f;
     lds_barrier();
 
     for (int c = 0; c < nch; ++c) {
         const unsigned char* slot = smem + (size_t)(c % NS) * C::SLOT;
         unsigned char* recB = const_cast<unsigned char*>(rec0) + (size_t)c * Ly::REC + Ly::REC_A;
-        f32x4 U[4], Ut[4];
-        frag kf[HDT * NKT];
-        if (w >= 2) {
-            // always issue (clamped to the last chunk) so the outstanding count stays fixed
-            const int cn = c + NS - 1;
-            chain_issue_slot<D, E>(smem + (size_t)(cn % NS) * C::SLOT, rec0 + (size_t)min(cn, nch - 1) * Ly::REC, srcofs,
-                                   w - 2);
-            wait_vmcnt<C::INFLIGHT * C::BPW>();
-        } else {
-            // this half's chunk-start state fragments (also handed to the output stage)
-            frag Hf[HKD];
+        const T* ut = reinterpret_cast<const T*>(slot + C::S_UT);   // [rt][lane][4]
+        frag Hf[HKD];
 #pragma unroll
-            for (int kk = 0; kk < HKD; ++kk) {
-                Hf[kk] = M::from_acc(H, kk);
-                st_frag(recB + Ly::B_H + (size_t)(cg * NKD + hh * HKD + kk) * Ly::FR, lane, Hf[kk]);
-            }
-            if constexpr (DELTA) {
-                // partial (-W) H over this half's rows, all four token tiles
-                frag wf[4 * HKD];
+        for (int kk = 0; kk < HKD; ++kk) {
+            Hf[kk] = M::from_acc(H, kk);
+            st_frag(recB + Ly::B_H + (size_t)(cg * NKD + HH * HKD + kk) * Ly::FR, lane, Hf[kk]);
+        }
+        f32x4 P[4];
+        if constexpr (DELTA) {
+            frag wf[4 * HKD];
 #pragma unroll
-                for (int rt = 0; rt < 4; ++rt)
-#pragma unroll
-                    for (int kk = 0; kk < HKD; ++kk)
-                        wf[rt * HKD + kk] = ld_frag<frag>(slot + Ly::A_W + (size_t)(rt * NKD + hh * HKD + kk) * Ly::FR, lane);
-#pragma unroll
-                for (int rt = 0; rt < 4; ++rt) U[rt] = f32x4{0.f, 0.f, 0.f, 0.f};
+            for (int rt = 0; rt < 4; ++rt)
 #pragma unroll
                 for (int kk = 0; kk < HKD; ++kk)
+                    wf[rt * HKD + kk] = ld_frag<frag>(slot + Ly::A_W + (size_t)(rt * NKD + HH * HKD + kk) * Ly::FR, lane);
+            const float dec = *reinterpret_cast<const float*>(slot + C::S_DEC);
 #pragma unroll
-                    for (int rt = 0; rt < 4; ++rt) U[rt] = M::mma(wf[rt * HKD + kk], Hf[kk], U[rt]);
-#pragma unroll
-                for (int rt = 0; rt < 4; ++rt) X[(hh * 4 + rt) * 64 + lane] = U[rt];
+            for (int rt = 0; rt < 4; ++rt) {
+                if ((rt >> 1) == HH) {
+                    const float4 x = load4(ut + ((size_t)rt * 64 + lane) * 4);
+                    P[rt] = f32x4{x.x, x.y, x.z, x.w};
+                } else {
+                    P[rt] = f32x4{0.f, 0.f, 0.f, 0.f};
+                }
             }
+#pragma unroll
+            for (int kk = 0; kk < HKD; ++kk)
+#pragma unroll
+                for (int rt = 0; rt < 4; ++rt) P[rt] = M::mma(wf[rt * HKD + kk], Hf[kk], P[rt]);
+#pragma unroll
+            for (int rt = 0; rt < 4; ++rt) X[(HH * 4 + rt) * 64 + lane] = P[rt];
+#pragma unroll
+            for (int t = 0; t < HDT; ++t) H[t] = f32x4{H[t][0] * dec, H[t][1] * dec, H[t][2] * dec, H[t][3] * dec};
         }
         lds_barrier();   // partial products exchanged
-        if (w < 2) {
+        f32x4 U[4];
 #pragma unroll
-            for (int rt = 0; rt < 4; ++rt) {
-                const float4 x = load4(reinterpret_cast<const T*>(slot + C::S_UT) + ((size_t)rt * 64 + lane) * 4);
-                Ut[rt] = f32x4{x.x, x.y, x.z, x.w};
-            }
-            // U = (Ut + P_0) + P_1 in this order in both waves, so both hold the same U; each
-            // wave has its own partial in registers and reads the other one
-#pragma unroll
-            for (int rt = 0; rt < 4; ++rt) {
-                f32x4 u = Ut[rt];
-                if constexpr (DELTA) {
-                    const f32x4 po = X[((1 - hh) * 4 + rt) * 64 + lane];
-                    const f32x4 p0 = hh == 0 ? U[rt] : po, p1 = hh == 0 ? po : U[rt];
-                    u = f32x4{(u[0] + p0[0]) + p1[0], (u[1] + p0[1]) + p1[1], (u[2] + p0[2]) + p1[2],
-                              (u[3] + p0[3]) + p1[3]};
-                }
-                U[rt] = u;
-            }
-            frag Uf[NKT];
-#pragma unroll
-            for (int kt = 0; kt < NKT; ++kt) {
-                Uf[kt] = M::from_acc(U, kt);
-                if (hh == 0) st_frag(recB + Ly::B_U + (size_t)(cg * NKT + kt) * Ly::FR, lane, Uf[kt]);
-            }
-#pragma unroll
-            for (int t = 0; t < HDT; ++t)
-#pragma unroll
-                for (int kt = 0; kt < NKT; ++kt)
-                    kf[t * NKT + kt] = ld_frag<frag>(slot + Ly::A_KH + (size_t)((hh * HDT + t) * NKT + kt) * Ly::FR, lane);
+        for (int rt = 0; rt < 4; ++rt) {
             if constexpr (DELTA) {
-                const float dec = *reinterpret_cast<const float*>(slot + C::S_DEC);
-#pragma unroll
-                for (int t = 0; t < HDT; ++t) H[t] = f32x4{H[t][0] * dec, H[t][1] * dec, H[t][2] * dec, H[t][3] * dec};
+                const f32x4 po = X[((1 - HH) * 4 + rt) * 64 + lane];
+                U[rt] = f32x4{P[rt][0] + po[0], P[rt][1] + po[1], P[rt][2] + po[2], P[rt][3] + po[3]};
+            } else {
+                const float4 x = load4(ut + ((size_t)rt * 64 + lane) * 4);
+                U[rt] = f32x4{x.x, x.y, x.z, x.w};
             }
-#pragma unroll
-            for (int kt = 0; kt < NKT; ++kt)
-#pragma unroll
-                for (int t = 0; t < HDT; ++t) H[t] = M::mma(kf[t * NKT + kt], Uf[kt], H[t]);
         }
-        lds_barrier();   // slot c and the exchange area may be reused
-    }
-    if (w < 2) {
+        frag kf[HDT * NKT];
 #pragma unroll
         for (int t = 0; t < HDT; ++t)
 #pragma unroll
-            for (int e = 0; e < 4; ++e)
-                a.h_final[((size_t)bh * D + 16 * (hh * HDT + t) + 4 * j + e) * D + col] = H[t][e];
-    } else {
-        wait_vmcnt<0>();   // no LDS write may land after the workgroup ends
+            for (int kt = 0; kt < NKT; ++kt)
+                kf[t * NKT + kt] = ld_frag<frag>(slot + Ly::A_KH + (size_t)((HH * HDT + t) * NKT + kt) * Ly::FR, lane);
+        frag Uf[NKT];
+#pragma unroll
+        for (int kt = 0; kt < NKT; ++kt) {
+            Uf[kt] = M::from_acc(U, kt);
+            if (kt % 2 == HH) st_frag(recB + Ly::B_U + (size_t)(cg * NKT + kt) * Ly::FR, lane, Uf[kt]);
+        }
+#pragma unroll
+        for (int kt = 0; kt < NKT; ++kt)
+#pragma unroll
+            for (int t = 0; t < HDT; ++t) H[t] = M::mma(kf[t * NKT + kt], Uf[kt], H[t]);
+        lds_barrier();   // slot c and the exchange area may be reused
     }
+#pragma unroll
+    for (int t = 0; t < HDT; ++t)
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+            a.h_final[((size_t)bh * D + 16 * (HH * HDT + t) + 4 * j + e) * D + col] = H[t][e];
+}
+
+// One workgroup per CU (its LDS ring), so one wave per SIMD: let the compiler use the whole
+// register file, which keeps every fragment read of a chunk in flight at once. Waves 0 and 1
+// compute, waves 2 and 3 load; the roles run separate loops with the same barrier sequence.
+template <int D, class E, bool DELTA>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) void chain_kernel(PrefArgs a) {
+    using Ly = Layout<D, E>;
+    using C = ChainCfg<D, E>;
+    extern __shared__ __align__(16) unsigned char smem[];
+    // blockIdx -> (slice, column group) so that all column groups of one slice run on the same
+    // XCD (workgroups are dealt to the 8 XCDs round-robin) and share its L2.
+    const int xcd = blockIdx.x & 7, sl = blockIdx.x >> 3;
+    const int cg = sl % C::NCW, bh = (sl / C::NCW) * 8 + xcd;
+    if (bh >= a.BH) return;
+    const int lane = threadIdx.x & 63;
+    const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);   // wave-uniform
+    const unsigned char* rec0 = a.ws + (size_t)bh * a.segcap * Ly::REC;
+    if (w >= 2)
+        chain_loader<D, E>(smem, rec0, a.nseg, cg, w - 2, lane);
+    else if (w == 0)
+        chain_compute<D, E, DELTA, 0>(a, smem, rec0, a.nseg, bh, cg, lane);
+    else
+        chain_compute<D, E, DELTA, 1>(a, smem, rec0, a.nseg, bh, cg, lane);
 }
 
 // ---------------------------------------------------------------------------------------------
