@@ -121,4 +121,53 @@ __device__ __forceinline__ typename MM<E>::frag row_frag_f32(const float* rp, in
     return M::pack(x);
 }
 
+// Fragment of a row (k contiguous in memory) at k = k0 + kofs(j, e), taken as stored.
+template <class E>
+__device__ __forceinline__ typename MM<E>::frag row_frag_raw(const typename E::T* rp, int k0, int j) {
+    if constexpr (MM<E>::EPF == 8) {
+        const uint2 a = *reinterpret_cast<const uint2*>(rp + k0 + 4 * j);
+        const uint2 b = *reinterpret_cast<const uint2*>(rp + k0 + 16 + 4 * j);
+        return __builtin_bit_cast(bf16x8, uint4{a.x, a.y, b.x, b.y});
+    } else {
+        return *reinterpret_cast<const f32x4*>(rp + k0 + 4 * j);
+    }
+}
+
+// B operand whose column n is the unit vector at k = n + 16 q. The product of a row fragment
+// with it is exact and lands the 16 selected columns in an accumulator tile, where lane (j, n)
+// holds rows 4 j .. 4 j + 3 of column n: a transpose done by the matrix core.
+template <class E>
+__device__ __forceinline__ typename MM<E>::frag unit_cols(int j, int n, int q) {
+    using M = MM<E>;
+    float x[M::EPF];
+#pragma unroll
+    for (int e = 0; e < M::EPF; ++e) x[e] = M::kofs(j, e) == n + 16 * q ? 1.f : 0.f;
+    return M::pack(x);
+}
+
+// Operand fragment whose k index runs over the rows of KB / 16 consecutive accumulator tiles
+// t[0], t[1], ... (16 rows each), row s scaled by sk[s] (sk indexed from the first tile's row 0).
+template <class E>
+__device__ __forceinline__ typename MM<E>::frag cols_frag(const f32x4* t, const float* sk, int j) {
+    using M = MM<E>;
+    float x[M::EPF];
+#pragma unroll
+    for (int i = 0; i < M::EPF / 4; ++i) {
+        const float4 s = *reinterpret_cast<const float4*>(sk + 16 * i + 4 * j);
+        x[4 * i + 0] = t[i][0] * s.x; x[4 * i + 1] = t[i][1] * s.y;
+        x[4 * i + 2] = t[i][2] * s.z; x[4 * i + 3] = t[i][3] * s.w;
+    }
+    return M::pack(x);
+}
+template <class E>
+__device__ __forceinline__ typename MM<E>::frag cols_frag(const f32x4* t) {
+    using M = MM<E>;
+    float x[M::EPF];
+#pragma unroll
+    for (int i = 0; i < M::EPF / 4; ++i)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) x[4 * i + e] = t[i][e];
+    return M::pack(x);
+}
+
 }  // namespace gdn

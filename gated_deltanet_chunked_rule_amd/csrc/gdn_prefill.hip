@@ -140,33 +140,50 @@ __device__ __forceinline__ void inverse_block_t(const float* Am, float* Tm, int 
 // ---------------------------------------------------------------------------------------------
 // stage 1: intra-chunk delta-system solve and WY/UT transform
 // ---------------------------------------------------------------------------------------------
+// Work split of the prep workgroup's four waves. The d extent is cut into fragment groups of
+// KB / 16 d-tiles (one operand fragment wide); a wave owns GPW groups, or shares one group with
+// WPG - 1 other waves and then takes RPW of the four token tiles.
+template <int D, class E>
+struct PrepCfg {
+    using Ly = Layout<D, E>;
+    static constexpr int FPD = MM<E>::KB / 16;                   // d tiles per fragment
+    static constexpr int WPG = Ly::NKD >= 4 ? 1 : 4 / Ly::NKD;   // waves per fragment group
+    static constexpr int GPW = Ly::NKD >= 4 ? Ly::NKD / 4 : 1;   // fragment groups per wave
+    static constexpr int RPW = 4 / WPG;                          // token tiles per wave
+    static constexpr int DPW = GPW * FPD;                        // d tiles per wave
+    static constexpr int KP = D + 8;                             // K / V row stride (elements)
+    static constexpr int AS = CH + 4;                            // A / T row stride (floats)
+    static constexpr size_t ROWS = (size_t)CH * KP * sizeof(typename E::T);
+    static constexpr size_t MAT = (size_t)CH * AS * 4;
+    // region 0: K rows, then T; region 1: V rows, then A
+    static constexpr size_t REGION = ((ROWS > MAT ? ROWS : MAT) + 15) / 16 * 16;
+    static constexpr size_t LDS = 2 * REGION + 4 * CH * 4;
+};
+
 template <int D, class E, bool DELTA>
 __global__ __launch_bounds__(256) void prep_kernel(PrefArgs a) {
     using T = typename E::T;
     using M = MM<E>;
     using Ly = Layout<D, E>;
+    using P = PrepCfg<D, E>;
     using frag = typename M::frag;
-    constexpr int KB = M::KB, NKD = Ly::NKD, NKT = Ly::NKT, NDT = Ly::NDT;
-    constexpr int TP = CH + 8;   // token stride of the transposed tiles (elements)
-    constexpr int AS = CH + 4;   // row stride of the A / T matrix (floats)
+    constexpr int KB = M::KB, NKD = Ly::NKD, NKT = Ly::NKT;
+    constexpr int FPD = P::FPD, WPG = P::WPG, GPW = P::GPW, RPW = P::RPW, DPW = P::DPW, KP = P::KP, AS = P::AS;
 
     extern __shared__ __align__(16) unsigned char smem[];
-    T* Kt = reinterpret_cast<T*>(smem);            // [D][TP]  K^T
-    T* Vt = Kt + D * TP;                           // [D][TP]  V^T
-    float* Am = reinterpret_cast<float*>(Vt + D * TP);  // [CH][AS] A (strictly lower)
-    float* Tm = Am + CH * AS;                      // [CH][AS] T = (I + A)^-1
-    // K rows [CH][KP] for the Gram matrix: in T's space when it fits (T is written only after
-    // the Gram is done), else in a region of its own after the gate vectors
-    constexpr int KP = D + 8;
-    constexpr bool KROW_IN_T = (size_t)CH * KP * sizeof(T) <= (size_t)CH * AS * 4;
-    float* sg = Tm + CH * AS;                      // g
-    float* sbe = sg + CH;                          // beta e^g
-    float* sb = sbe + CH;                          // beta
-    float* skh = sb + CH;                          // e^{g_C - g}
-    T* Kr = KROW_IN_T ? reinterpret_cast<T*>(Tm) : reinterpret_cast<T*>(skh + CH);
+    T* Kr = reinterpret_cast<T*>(smem);                               // [CH][KP] K rows
+    float* Tm = reinterpret_cast<float*>(smem);                       // [CH][AS] T = (I + A)^-1, after K
+    T* Vr = reinterpret_cast<T*>(smem + P::REGION);                   // [CH][KP] V rows
+    float* Am = reinterpret_cast<float*>(smem + P::REGION);           // [CH][AS] A (strictly lower), after V
+    float* sg = reinterpret_cast<float*>(smem + 2 * P::REGION);       // g
+    float* sbe = sg + CH;                                             // -beta e^g
+    float* sb = sbe + CH;                                             // beta
+    float* skh = sb + CH;                                             // e^{g_C - g}
 
     const int cl = blockIdx.x, bh = blockIdx.y;     // chunk within the segment, slice
     const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63, j = lane >> 4, m = lane & 15;
+    const int grp = GPW * (w / WPG);                // this wave's first d-fragment group
+    const int rt0 = RPW * (w % WPG);                // this wave's first token tile
     const long t0 = (long)(a.c0 + cl) * CH;
     const int n = (int)min((long)CH, a.L - t0);
     const size_t tok0 = (size_t)bh * a.L + t0;
@@ -184,49 +201,106 @@ __global__ __launch_bounds__(256) void prep_kernel(PrefArgs a) {
         const float gC = __shfl(g, 63);
         sg[lane] = g;
         sb[lane] = bt;
-        sbe[lane] = bt * __expf(g);
+        sbe[lane] = -bt * __expf(g);
         skh[lane] = __expf(gC - g);
         if (lane == 0) *reinterpret_cast<float*>(rec + Ly::A_DEC) = DELTA ? __expf(gC) : 1.f;
     }
-    {   // K^T and V^T into LDS; padded tokens are zero (identity steps)
-        const int r = tid >> 2, qd = tid & 3;
-        constexpr int DQ = D / 4;
+    {   // K and V rows, 16 bytes per lane; rows past the chunk's end are zero (identity steps)
+        constexpr int EPU = 16 / sizeof(T), UPR = D / EPU;
 #pragma unroll
-        for (int d0 = 0; d0 < DQ; d0 += 4) {
-            const int d = qd * DQ + d0;
-            float4 kk = make_float4(0.f, 0.f, 0.f, 0.f), vv = kk;
+        for (int i = 0; i < CH * UPR / 256; ++i) {
+            const int u = tid + 256 * i, r = u / UPR, cu = u % UPR;
+            uint4 xk = {0u, 0u, 0u, 0u}, xv = xk;
             if (r < n) {
-                kk = load4(kp + (size_t)r * D + d);
-                vv = load4(vp + (size_t)r * D + d);
+                xk = *reinterpret_cast<const uint4*>(kp + (size_t)r * D + cu * EPU);
+                xv = *reinterpret_cast<const uint4*>(vp + (size_t)r * D + cu * EPU);
             }
-            Kt[(d + 0) * TP + r] = E::from(kk.x); Kt[(d + 1) * TP + r] = E::from(kk.y);
-            Kt[(d + 2) * TP + r] = E::from(kk.z); Kt[(d + 3) * TP + r] = E::from(kk.w);
-            Vt[(d + 0) * TP + r] = E::from(vv.x); Vt[(d + 1) * TP + r] = E::from(vv.y);
-            Vt[(d + 2) * TP + r] = E::from(vv.z); Vt[(d + 3) * TP + r] = E::from(vv.w);
-            if (DELTA) store4(Kr + r * KP + d, kk);
+            *reinterpret_cast<uint4*>(Kr + r * KP + cu * EPU) = xk;
+            *reinterpret_cast<uint4*>(Vr + r * KP + cu * EPU) = xv;
         }
     }
     __syncthreads();
 
-    if constexpr (DELTA) {
-        // Gram tiles (rt, st), st <= rt, of A[r][s] = beta_r exp(g_r - g_s) k_r.k_s, s < r
-        for (int ti = w; ti < 10; ti += 4) {
-            int rt = 0, st = ti;
-            while (st > rt) { st -= rt + 1; ++rt; }
-            const T* ra = Kr + (16 * rt + m) * KP;   // rows past the chunk's end are zero
-            const T* rb = Kr + (16 * st + m) * KP;
-            f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+    // Rows to columns on the matrix core: kc[i][st] is the accumulator tile of tokens 16 st ..
+    // 16 st + 15 and d-tile dt = FPD grp + i of K (lane (j, n): K[16 st + 4 j + e][16 dt + n]);
+    // vc likewise for V. Fragments built from them have k = token, which the products over a
+    // chunk's tokens need.
+    f32x4 kc[DPW][4], vc[DPW][4];
 #pragma unroll
-            for (int kb = 0; kb < NKD; ++kb)
-                acc = M::mma(row_frag<E>(ra, kb * KB, j, 1.f), row_frag<E>(rb, kb * KB, j, 1.f), acc);
-            const int s = 16 * st + m;
+    for (int i = 0; i < DPW; ++i) {
+        const int dt = FPD * grp + i;
+        const frag sel = unit_cols<E>(j, m, dt % FPD);
 #pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                const int r = 16 * rt + 4 * j + e;
-                Am[r * AS + s] = (s < r) ? sb[r] * __expf(sg[r] - sg[s]) * acc[e] : 0.f;
+        for (int st = 0; st < 4; ++st) {
+            const f32x4 z = {0.f, 0.f, 0.f, 0.f};
+            kc[i][st] = M::mma(row_frag_raw<E>(Kr + (16 * st + m) * KP, KB * (dt / FPD), j), sel, z);
+            vc[i][st] = M::mma(row_frag_raw<E>(Vr + (16 * st + m) * KP, KB * (dt / FPD), j), sel, z);
+        }
+    }
+
+    if constexpr (!DELTA) {
+        // plain linear attention: Khat = K, Ut = V
+#pragma unroll
+        for (int i = 0; i < DPW; ++i) {
+            const int dt = FPD * grp + i;
+#pragma unroll
+            for (int kt = 0; kt < NKT; ++kt)
+                if (kt % WPG == w % WPG)
+                    st_frag(rec + Ly::A_KH + (size_t)(dt * NKT + kt) * Ly::FR, lane, cols_frag<E>(&kc[i][FPD * kt]));
+#pragma unroll
+            for (int r = 0; r < RPW; ++r) {
+                const int rt = rt0 + r;
+                T* dst = reinterpret_cast<T*>(rec + Ly::A_UT) + ((size_t)(dt * 4 + rt) * 64 + lane) * 4;
+                store4(dst, make_float4(vc[i][rt][0], vc[i][rt][1], vc[i][rt][2], vc[i][rt][3]));
             }
         }
-        __syncthreads();   // the Gram is done with the K rows (they may share T's space)
+        return;
+    } else {
+        // Gram tiles (rt, st), st <= rt, of K K^T: ten tiles over the four waves
+        f32x4 gacc[3];
+#pragma unroll
+        for (int x = 0; x < 3; ++x) {
+            const int ti = w + 4 * x;
+            gacc[x] = f32x4{0.f, 0.f, 0.f, 0.f};
+            if (ti < 10) {
+                int rt = 0, st = ti;
+                while (st > rt) { st -= rt + 1; ++rt; }
+#pragma unroll
+                for (int kb = 0; kb < NKD; ++kb)
+                    gacc[x] = M::mma(row_frag_raw<E>(Kr + (16 * rt + m) * KP, kb * KB, j),
+                                     row_frag_raw<E>(Kr + (16 * st + m) * KP, kb * KB, j), gacc[x]);
+            }
+        }
+        // Khat^T fragments (stored), -beta e^g K^T and beta V^T fragments (kept)
+        frag kbe[DPW][NKT], vb[DPW][NKT];
+#pragma unroll
+        for (int i = 0; i < DPW; ++i) {
+            const int dt = FPD * grp + i;
+#pragma unroll
+            for (int kt = 0; kt < NKT; ++kt) {
+                if (kt % WPG == w % WPG)
+                    st_frag(rec + Ly::A_KH + (size_t)(dt * NKT + kt) * Ly::FR, lane,
+                            cols_frag<E>(&kc[i][FPD * kt], skh + KB * kt, j));
+                kbe[i][kt] = cols_frag<E>(&kc[i][FPD * kt], sbe + KB * kt, j);
+                vb[i][kt] = cols_frag<E>(&vc[i][FPD * kt], sb + KB * kt, j);
+            }
+        }
+        __syncthreads();   // K and V rows are no longer read: their space takes T and A
+        // A[r][s] = beta_r exp(g_r - g_s) k_r.k_s for s < r
+#pragma unroll
+        for (int x = 0; x < 3; ++x) {
+            const int ti = w + 4 * x;
+            if (ti < 10) {
+                int rt = 0, st = ti;
+                while (st > rt) { st -= rt + 1; ++rt; }
+                const int s = 16 * st + m;
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    const int r = 16 * rt + 4 * j + e;
+                    Am[r * AS + s] = (s < r) ? sb[r] * __expf(sg[r] - sg[s]) * gacc[x][e] : 0.f;
+                }
+            }
+        }
         // zero the above-diagonal 16 x 16 blocks of T (fragments of 32 tokens read some of them)
         for (int i = tid; i < 6 * 256; i += 256) {
             const int b = i >> 8, e = i & 255;
@@ -258,57 +332,39 @@ __global__ __launch_bounds__(256) void prep_kernel(PrefArgs a) {
             if (w + lvl < 4) inverse_block_t<AS>(Am, Tm, w + lvl, w, j, m);
         }
         __syncthreads();
-        // Khat^T fragments (d-tile dt, token block kb)
-        for (int f = w; f < NDT * NKT; f += 4) {
-            const int dt = f / NKT, kb = f % NKT;
-            st_frag(rec + Ly::A_KH + (size_t)f * Ly::FR, lane, row_frag_ks<E>(Kt + (16 * dt + m) * TP, kb * KB, j, skh));
-        }
-        // wave w: token tile rt = w. T rows 16 rt .. 16 rt + 15 are zero beyond column 16 rt + 15.
-        const int rt = w;
-        const int kbmax = (16 * rt + 15) / KB;
-        frag Tf[NKT];
+        // this wave's token tiles: T rows as fragments (rows 16 rt .. 16 rt + 15 of T are zero
+        // beyond column 16 rt + 15, so token blocks past kbmax are skipped)
 #pragma unroll
-        for (int kb = 0; kb < NKT; ++kb) Tf[kb] = row_frag_f32<E>(Tm + (16 * rt + m) * AS, kb * KB, j);
-        // -W fragments: W^T tile (dt, rt) = sum_s (beta e^g K)^T[d][s] T^T[s][r]
-        f32x4 wt[NDT];
+        for (int r = 0; r < RPW; ++r) {
+            const int rt = rt0 + r;
+            const int kbmax = (16 * rt + 15) / KB;
+            frag Tf[NKT];
 #pragma unroll
-        for (int dt = 0; dt < NDT; ++dt) wt[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
+            for (int kt = 0; kt < NKT; ++kt)
+                if (kt <= kbmax) Tf[kt] = row_frag_f32<E>(Tm + (16 * rt + m) * AS, kt * KB, j);
+            // -W^T tiles (dt, rt) = sum_s (-beta e^g K)^T[d][s] T[r][s], then -W fragments [rt][kd]
+            f32x4 wt[DPW];
 #pragma unroll
-        for (int kb = 0; kb < NKT; ++kb)
-            if (kb <= kbmax)
+            for (int i = 0; i < DPW; ++i) {
+                wt[i] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-                for (int dt = 0; dt < NDT; ++dt)
-                    wt[dt] = M::mma(row_frag_ks<E>(Kt + (16 * dt + m) * TP, kb * KB, j, sbe), Tf[kb], wt[dt]);
+                for (int kt = 0; kt < NKT; ++kt)
+                    if (kt <= kbmax) wt[i] = M::mma(kbe[i][kt], Tf[kt], wt[i]);
+            }
 #pragma unroll
-        for (int kd = 0; kd < NKD; ++kd)
-            st_frag(rec + Ly::A_W + (size_t)(rt * NKD + kd) * Ly::FR, lane, M::from_acc(wt, kd, -1.f));
-        // Ut tile (rt, vt) = sum_s T[r][s] (beta V)[s][v], stored as accumulators
-        f32x4 ut[NDT];
+            for (int g2 = 0; g2 < GPW; ++g2)
+                st_frag(rec + Ly::A_W + (size_t)(rt * NKD + grp + g2) * Ly::FR, lane, M::from_acc(&wt[FPD * g2], 0));
+            // Ut tiles (rt, vt) = sum_s T[r][s] (beta V)[s][v], stored as accumulators
 #pragma unroll
-        for (int vt = 0; vt < NDT; ++vt) ut[vt] = f32x4{0.f, 0.f, 0.f, 0.f};
+            for (int i = 0; i < DPW; ++i) {
+                const int vt = FPD * grp + i;
+                f32x4 ut = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int kb = 0; kb < NKT; ++kb)
-            if (kb <= kbmax)
-#pragma unroll
-                for (int vt = 0; vt < NDT; ++vt)
-                    ut[vt] = M::mma(Tf[kb], row_frag_ks<E>(Vt + (16 * vt + m) * TP, kb * KB, j, sb), ut[vt]);
-#pragma unroll
-        for (int vt = 0; vt < NDT; ++vt) {
-            T* dst = reinterpret_cast<T*>(rec + Ly::A_UT) + ((size_t)(vt * 4 + rt) * 64 + lane) * 4;
-            store4(dst, make_float4(ut[vt][0], ut[vt][1], ut[vt][2], ut[vt][3]));
-        }
-    } else {
-        // plain linear attention: Khat = K, Ut = V
-        for (int f = w; f < NDT * NKT; f += 4) {
-            const int dt = f / NKT, kb = f % NKT;
-            st_frag(rec + Ly::A_KH + (size_t)f * Ly::FR, lane, row_frag<E>(Kt + (16 * dt + m) * TP, kb * KB, j, 1.f));
-        }
-        const int rt = w;
-#pragma unroll
-        for (int vt = 0; vt < NDT; ++vt) {
-            const float4 x = load4(Vt + (16 * vt + m) * TP + 16 * rt + 4 * j);
-            T* dst = reinterpret_cast<T*>(rec + Ly::A_UT) + ((size_t)(vt * 4 + rt) * 64 + lane) * 4;
-            store4(dst, x);
+                for (int kt = 0; kt < NKT; ++kt)
+                    if (kt <= kbmax) ut = M::mma(Tf[kt], vb[i][kt], ut);
+                T* dst = reinterpret_cast<T*>(rec + Ly::A_UT) + ((size_t)(vt * 4 + rt) * 64 + lane) * 4;
+                store4(dst, make_float4(ut[0], ut[1], ut[2], ut[3]));
+            }
         }
     }
 }
@@ -693,10 +749,8 @@ struct Launch {
     using T = typename E::T;
     using Ly = Layout<D, E>;
     using CC = ChainCfg<D, E>;
-    static constexpr int TP = CH + 8, AS = CH + 4, KP = D + 8;
-    static constexpr bool KROW_IN_T = (size_t)CH * KP * sizeof(T) <= (size_t)CH * AS * 4;
-    static constexpr size_t LDS_PREP = (size_t)2 * D * TP * sizeof(T) + (size_t)2 * CH * AS * 4 + 4 * CH * 4 +
-                                       (KROW_IN_T ? 0 : (size_t)CH * KP * sizeof(T));
+    static constexpr int KP = D + 8;
+    static constexpr size_t LDS_PREP = PrepCfg<D, E>::LDS;
     static constexpr size_t LDS_CHAIN = (size_t)CC::NS * CC::SLOT + CC::XBYTES;
     static constexpr size_t LDS_OUT = (size_t)4 * (Ly::NKT + Ly::NKD) * 1024 + (size_t)2 * CH * KP * sizeof(T) + CH * 4;
 
