@@ -28,6 +28,7 @@
 //                 O^T = H^T (e^g Q)^T + U^T P^T, stored four value columns per lane.
 // Plain linear attention uses the same kernels with T = I, W = 0, Ut = V, g = 0.
 #include <mutex>
+#include <type_traits>
 
 #include "gdn_mfma.h"
 #include "gdn_launch.h"
@@ -372,28 +373,31 @@ __global__ __launch_bounds__(256) void prep_kernel(PrefArgs a) {
 // ---------------------------------------------------------------------------------------------
 // stage 2: the sequential chunk-to-chunk pass, state resident in registers
 // ---------------------------------------------------------------------------------------------
-// Chain workgroup: one slice (batch, head) and 16 value columns, four waves. The fp32 state of
-// those columns (Dk x 16) is split by rows between the two compute waves, each holding its half
-// in accumulator registers for the whole sequence; per chunk they exchange their fp32 partial
-// products W H through LDS (4 KB each), so each wave's chain step is half the MFMA work. Waves 2
-// and 3 stream the per-chunk operands (-W and Khat^T fragments, this workgroup's Ut columns, the
-// chunk decay) from the workspace into a ring of NS LDS slots, NS - 1 chunks ahead, so the
-// sequential chain never waits on a global-memory round trip.
+// Chain workgroup: one slice (batch, head) and CPW groups of 16 value columns. The fp32 state of
+// a column group (Dk x 16) is split by rows between two compute waves, each holding its half in
+// accumulator registers for the whole sequence; per chunk they exchange their fp32 partial
+// products W H through LDS (4 KB each), so each wave's chain step is half the MFMA work. Two
+// loader waves stream the per-chunk -W and Khat^T fragments (contiguous at the start of each
+// prep record, shared by all column groups of the slice) into a ring of NS LDS slots, NS - 1
+// chunks ahead, so the sequential chain never waits on a global-memory round trip. For bf16 at
+// Dk = 128 a slot is 32 KB: direct-to-LDS loads stream at about twice the rate when no more
+// than that is requested per chunk. The compute waves fetch their few Ut columns and the chunk
+// decay themselves with ordinary loads, one chunk ahead.
 template <int D, class E>
 struct ChainCfg {
     using Ly = Layout<D, E>;
-    static constexpr int CGW = 16;                                       // columns per workgroup
-    static constexpr int NCW = D / CGW;                                  // workgroups per slice
+    static constexpr int CPW = 1;                                        // column groups per workgroup
+    static constexpr int NCW = D / 16 / CPW;                             // workgroups per slice
+    static constexpr int THREADS = 64 * (2 * CPW + 2);                   // compute waves, then 2 loaders
     static constexpr size_t UTSUB = (size_t)4 * 64 * 4 * sizeof(typename E::T);  // Ut bytes of 16 columns
-    static constexpr size_t S_UT = Ly::A_UT;                             // -W and Khat^T precede
-    static constexpr size_t S_DEC = S_UT + UTSUB;
-    static constexpr int UNITS = (int)((S_DEC + 16) / 16);               // 16-byte units per slot
-    static constexpr int NBLK = (UNITS + 63) / 64;                       // 1 KB wave blocks per slot
-    static constexpr int BPW = (NBLK + 1) / 2;                           // blocks per loader wave
-    static constexpr size_t SLOT = (size_t)NBLK * 1024;
-    static constexpr size_t XBYTES = (size_t)2 * 4 * 64 * 16;           // partial W H of both halves
+    static constexpr size_t SLOT = Ly::A_UT;                             // -W and Khat^T fragments
+    static constexpr int NBLK = (int)(SLOT / 1024);                      // 1 KB wave blocks per slot
+    static constexpr int BPW = NBLK / 2;                                 // blocks per loader wave
+    static_assert(SLOT % 2048 == 0, "slot splits into whole blocks per loader wave");
+    static constexpr size_t XBYTES = (size_t)CPW * 2 * 4 * 64 * 16;     // partial W H of both halves
     static constexpr int NS = SLOT * 4 + XBYTES <= 156 * 1024 ? 4 : (SLOT * 3 + XBYTES <= 156 * 1024 ? 3 : 2);
     static constexpr int INFLIGHT = NS - 2;                              // chunks still loading at a barrier
+    static_assert(INFLIGHT * BPW < 64, "vmcnt is 6 bits");
 };
 
 // Barrier of the chain workgroup. Only LDS is shared between its waves: the loader waves fill it
@@ -416,19 +420,6 @@ __device__ __forceinline__ void wait_vmcnt() {
     __builtin_amdgcn_s_waitcnt((N & 15) | (7 << 4) | (15 << 8) | ((N >> 4) << 14));
 }
 
-// Byte offset, within a prep record, of 16-byte unit u of a chain slot: -W and Khat^T as they
-// are, then this workgroup's Ut columns, then the decay.
-template <int D, class E>
-__device__ __forceinline__ unsigned chain_ofs(int cgw, int u) {
-    using C = ChainCfg<D, E>;
-    using Ly = Layout<D, E>;
-    constexpr int U1 = (int)(C::S_UT / 16), U2 = (int)(C::UTSUB / 16);
-    u = u < C::UNITS ? u : C::UNITS - 1;
-    if (u < U1) return (unsigned)u * 16u;
-    if (u < U1 + U2) return (unsigned)(Ly::A_UT + (size_t)cgw * C::UTSUB + (size_t)(u - U1) * 16);
-    return (unsigned)Ly::A_DEC;   // the decay (one unit; the 12 bytes after it are not used)
-}
-
 // Direct-to-LDS load of 16 bytes per lane: lane l's bytes land at LDS address lds_base + 16 l.
 // Issued as inline assembly so that the compiler does not track it: the loader waves account
 // for these loads themselves (wait_vmcnt), and the compute waves, which only read LDS, must not
@@ -448,44 +439,34 @@ __device__ __forceinline__ unsigned lds_addr(const void* p) {
     return (unsigned)(size_t)(const __attribute__((address_space(3))) void*)p;
 }
 
-// One loader wave's share of a chunk: BPW 1 KB blocks. Blocks past the slot's end repeat the
-// last block, so both loader waves issue the same count.
+// One loader wave's share of a chunk: BPW 1 KB blocks, interleaved with the other loader's.
 template <int D, class E>
-__device__ __forceinline__ void chain_issue_slot(unsigned char* slot, const unsigned char* recA, const unsigned* srcofs,
-                                                 int lw) {
+__device__ __forceinline__ void chain_issue_slot(unsigned char* slot, const unsigned char* recA, int lw, int lane) {
     using C = ChainCfg<D, E>;
     const unsigned base = lds_addr(slot);
 #pragma unroll
     for (int i = 0; i < C::BPW; ++i) {
-        const int blk = lw + 2 * i < C::NBLK ? lw + 2 * i : C::NBLK - 1;
-        dma16(recA + srcofs[i], base + (unsigned)blk * 1024u);
+        const unsigned blk = (unsigned)(lw + 2 * i) * 1024u;
+        dma16(recA + blk + lane * 16, base + blk);
     }
 }
 
 // Loader wave lw (0 or 1) of a chain workgroup: chunk c + NS - 1 is issued at step c into the
 // slot freed at step c - 1; before each chunk's first barrier the loader waits only for the
-// chunk needed next. The per-lane source offsets within a record are the same for every chunk.
-// Two barriers per chunk, like the compute waves.
+// chunk needed next. Two barriers per chunk, like the compute waves.
 template <int D, class E>
-__device__ __forceinline__ void chain_loader(unsigned char* smem, const unsigned char* rec0, int nch, int cg, int lw,
-                                             int lane) {
+__device__ __forceinline__ void chain_loader(unsigned char* smem, const unsigned char* rec0, int nch, int lw, int lane) {
     using Ly = Layout<D, E>;
     using C = ChainCfg<D, E>;
     constexpr int NS = C::NS;
-    unsigned srcofs[C::BPW];
-#pragma unroll
-    for (int i = 0; i < C::BPW; ++i) {
-        const int blk = lw + 2 * i < C::NBLK ? lw + 2 * i : C::NBLK - 1;
-        srcofs[i] = chain_ofs<D, E>(cg, blk * 64 + lane);
-    }
     for (int c = 0; c < NS - 1; ++c)
-        chain_issue_slot<D, E>(smem + (size_t)c * C::SLOT, rec0 + (size_t)min(c, nch - 1) * Ly::REC, srcofs, lw);
+        chain_issue_slot<D, E>(smem + (size_t)c * C::SLOT, rec0 + (size_t)min(c, nch - 1) * Ly::REC, lw, lane);
     wait_vmcnt<C::INFLIGHT * C::BPW>();
     lds_barrier();
     for (int c = 0; c < nch; ++c) {
         // always issue (clamped to the last chunk) so the outstanding count stays fixed
         const int cn = c + NS - 1;
-        chain_issue_slot<D, E>(smem + (size_t)(cn % NS) * C::SLOT, rec0 + (size_t)min(cn, nch - 1) * Ly::REC, srcofs, lw);
+        chain_issue_slot<D, E>(smem + (size_t)(cn % NS) * C::SLOT, rec0 + (size_t)min(cn, nch - 1) * Ly::REC, lw, lane);
         wait_vmcnt<C::INFLIGHT * C::BPW>();
         lds_barrier();
         lds_barrier();
@@ -493,24 +474,37 @@ __device__ __forceinline__ void chain_loader(unsigned char* smem, const unsigned
     wait_vmcnt<0>();   // no LDS write may land after the workgroup ends
 }
 
-// Compute wave HH of a chain workgroup: it owns state rows [HH Dk/2, (HH + 1) Dk/2) of the
-// workgroup's 16 columns. Per chunk:
+// Ut tile of 4 elements per lane as stored (bf16 or fp32), and as fp32
+__device__ __forceinline__ f32x4 ut_f32(uint2 r) {
+    return f32x4{__uint_as_float(r.x << 16), __uint_as_float(r.x & 0xffff0000u), __uint_as_float(r.y << 16),
+                 __uint_as_float(r.y & 0xffff0000u)};
+}
+__device__ __forceinline__ f32x4 ut_f32(float4 r) { return f32x4{r.x, r.y, r.z, r.w}; }
+
+// Compute wave HH of a chain workgroup: it owns state rows [HH Dk/2, (HH + 1) Dk/2) of column
+// group cg. Per chunk:
 //   A  Hf = bf16(H) (also handed to the output stage); partial product P_HH = (-W)[:, half] Hf,
 //      with Ut folded into the accumulators of token tiles 2 HH and 2 HH + 1; P_HH -> LDS;
 //      H *= chunk decay.
 //   B  U = P_HH + P_other (fp32 addition is commutative, so both waves hold the same U);
-//      H += Khat^T[half, :] bf16(U).
+//      H += Khat^T[half, :] bf16(U); then the next chunk's -W and Khat^T fragments are read from
+//      its slot (complete since this step's first barrier), so neither product of the next step
+//      waits on LDS.
+// Ut columns and the decay come from the workspace one chunk ahead, in registers.
 template <int D, class E, bool DELTA, int HH>
 __device__ __forceinline__ void chain_compute(const PrefArgs& a, unsigned char* smem, const unsigned char* rec0,
-                                              int nch, int bh, int cg, int lane) {
+                                              int nch, int bh, int cg, int cgl, int lane) {
     using T = typename E::T;
     using M = MM<E>;
     using Ly = Layout<D, E>;
     using C = ChainCfg<D, E>;
     using frag = typename M::frag;
+    using UR = typename std::conditional<sizeof(T) == 2, uint2, float4>::type;   // 4 Ut elements as stored
     constexpr int NKD = Ly::NKD, NKT = Ly::NKT, NDT = Ly::NDT, NS = C::NS;
     constexpr int HKD = NKD / 2, HDT = NDT / 2;   // fragments / tiles of one row half
-    f32x4* X = reinterpret_cast<f32x4*>(smem + (size_t)NS * C::SLOT);   // [half][rt][lane] partial products
+    constexpr int NUT = DELTA ? 2 : 4;            // Ut tiles this wave reads: its own two, or all
+    // [half][rt][lane] partial products of this column group
+    f32x4* X = reinterpret_cast<f32x4*>(smem + (size_t)NS * C::SLOT + (size_t)cgl * (C::XBYTES / C::CPW));
     const int j = lane >> 4, m = lane & 15;
     const int col = 16 * cg + m;
     f32x4 H[HDT];   // lane (j, m): H[16 (HH HDT + t) + 4 j + e][col]
@@ -519,12 +513,37 @@ __device__ __forceinline__ void chain_compute(const PrefArgs& a, unsigned char* 
 #pragma unroll
         for (int e = 0; e < 4; ++e)
             H[t][e] = a.h0 ? a.h0[((size_t)bh * D + 16 * (HH * HDT + t) + 4 * j + e) * D + col] : 0.f;
-    lds_barrier();
-
-    for (int c = 0; c < nch; ++c) {
-        const unsigned char* slot = smem + (size_t)(c % NS) * C::SLOT;
+    // Ut tiles and decay of chunk c, from its record
+    auto fetch = [&](int c, UR (&u)[NUT], float& dec) {
+        const unsigned char* r = rec0 + (size_t)c * Ly::REC;
+        const UR* ut = reinterpret_cast<const UR*>(r + Ly::A_UT + (size_t)cg * C::UTSUB);   // [rt][lane]
+#pragma unroll
+        for (int i = 0; i < NUT; ++i) u[i] = ut[(DELTA ? 2 * HH + i : i) * 64 + lane];
+        dec = DELTA ? *reinterpret_cast<const float*>(r + Ly::A_DEC) : 1.f;
+    };
+    // -W and Khat^T fragments of the chunk in slot s
+    frag wf[4 * HKD], kf[HDT * NKT];
+    auto read_slot = [&](int s) {
+        const unsigned char* slot = smem + (size_t)s * C::SLOT;
+        if constexpr (DELTA) {
+#pragma unroll
+            for (int rt = 0; rt < 4; ++rt)
+#pragma unroll
+                for (int kk = 0; kk < HKD; ++kk)
+                    wf[rt * HKD + kk] = ld_frag<frag>(slot + Ly::A_W + (size_t)(rt * NKD + HH * HKD + kk) * Ly::FR, lane);
+        }
+#pragma unroll
+        for (int t = 0; t < HDT; ++t)
+#pragma unroll
+            for (int kt = 0; kt < NKT; ++kt)
+                kf[t * NKT + kt] = ld_frag<frag>(slot + Ly::A_KH + (size_t)((HH * HDT + t) * NKT + kt) * Ly::FR, lane);
+    };
+    // one chain step on chunk c, whose Ut and decay are in (ut, dec); the next chunk's go into
+    // (ut_n, dec_n). The loop below alternates two register sets so that no prefetched value is
+    // ever copied (a copy would wait for its load).
+    auto step = [&](int c, const UR (&ut)[NUT], float dec, UR (&ut_n)[NUT], float& dec_n) {
         unsigned char* recB = const_cast<unsigned char*>(rec0) + (size_t)c * Ly::REC + Ly::REC_A;
-        const T* ut = reinterpret_cast<const T*>(slot + C::S_UT);   // [rt][lane][4]
+        fetch(min(c + 1, nch - 1), ut_n, dec_n);
         frag Hf[HKD];
 #pragma unroll
         for (int kk = 0; kk < HKD; ++kk) {
@@ -533,22 +552,8 @@ __device__ __forceinline__ void chain_compute(const PrefArgs& a, unsigned char* 
         }
         f32x4 P[4];
         if constexpr (DELTA) {
-            frag wf[4 * HKD];
 #pragma unroll
-            for (int rt = 0; rt < 4; ++rt)
-#pragma unroll
-                for (int kk = 0; kk < HKD; ++kk)
-                    wf[rt * HKD + kk] = ld_frag<frag>(slot + Ly::A_W + (size_t)(rt * NKD + HH * HKD + kk) * Ly::FR, lane);
-            const float dec = *reinterpret_cast<const float*>(slot + C::S_DEC);
-#pragma unroll
-            for (int rt = 0; rt < 4; ++rt) {
-                if ((rt >> 1) == HH) {
-                    const float4 x = load4(ut + ((size_t)rt * 64 + lane) * 4);
-                    P[rt] = f32x4{x.x, x.y, x.z, x.w};
-                } else {
-                    P[rt] = f32x4{0.f, 0.f, 0.f, 0.f};
-                }
-            }
+            for (int rt = 0; rt < 4; ++rt) P[rt] = (rt >> 1) == HH ? ut_f32(ut[rt & 1]) : f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
             for (int kk = 0; kk < HKD; ++kk)
 #pragma unroll
@@ -558,7 +563,7 @@ __device__ __forceinline__ void chain_compute(const PrefArgs& a, unsigned char* 
 #pragma unroll
             for (int t = 0; t < HDT; ++t) H[t] = f32x4{H[t][0] * dec, H[t][1] * dec, H[t][2] * dec, H[t][3] * dec};
         }
-        lds_barrier();   // partial products exchanged
+        lds_barrier();   // partial products exchanged; the next chunk's slot is complete
         f32x4 U[4];
 #pragma unroll
         for (int rt = 0; rt < 4; ++rt) {
@@ -566,16 +571,9 @@ __device__ __forceinline__ void chain_compute(const PrefArgs& a, unsigned char* 
                 const f32x4 po = X[((1 - HH) * 4 + rt) * 64 + lane];
                 U[rt] = f32x4{P[rt][0] + po[0], P[rt][1] + po[1], P[rt][2] + po[2], P[rt][3] + po[3]};
             } else {
-                const float4 x = load4(ut + ((size_t)rt * 64 + lane) * 4);
-                U[rt] = f32x4{x.x, x.y, x.z, x.w};
+                U[rt] = ut_f32(ut[rt]);
             }
         }
-        frag kf[HDT * NKT];
-#pragma unroll
-        for (int t = 0; t < HDT; ++t)
-#pragma unroll
-            for (int kt = 0; kt < NKT; ++kt)
-                kf[t * NKT + kt] = ld_frag<frag>(slot + Ly::A_KH + (size_t)((HH * HDT + t) * NKT + kt) * Ly::FR, lane);
         frag Uf[NKT];
 #pragma unroll
         for (int kt = 0; kt < NKT; ++kt) {
@@ -586,7 +584,18 @@ __device__ __forceinline__ void chain_compute(const PrefArgs& a, unsigned char* 
         for (int kt = 0; kt < NKT; ++kt)
 #pragma unroll
             for (int t = 0; t < HDT; ++t) H[t] = M::mma(kf[t * NKT + kt], Uf[kt], H[t]);
+        read_slot((c + 1) % NS);
         lds_barrier();   // slot c and the exchange area may be reused
+    };
+    UR ua[NUT], ub[NUT];
+    float da, db;
+    fetch(0, ua, da);
+    wait_vmcnt<0>();   // initial state and chunk 0's operands are in registers
+    lds_barrier();
+    read_slot(0);
+    for (int c = 0; c < nch; c += 2) {
+        step(c, ua, da, ub, db);
+        if (c + 1 < nch) step(c + 1, ub, db, ua, da);
     }
 #pragma unroll
     for (int t = 0; t < HDT; ++t)
@@ -595,45 +604,68 @@ __device__ __forceinline__ void chain_compute(const PrefArgs& a, unsigned char* 
             a.h_final[((size_t)bh * D + 16 * (HH * HDT + t) + 4 * j + e) * D + col] = H[t][e];
 }
 
-// One workgroup per CU (its LDS ring), so one wave per SIMD: let the compiler use the whole
-// register file, which keeps every fragment read of a chunk in flight at once. Waves 0 and 1
-// compute, waves 2 and 3 load; the roles run separate loops with the same barrier sequence.
+// One workgroup per CU (its LDS ring). Waves 0 .. 2 CPW - 1 compute (column group w / 2, row
+// half w % 2), the last two load; the roles run separate loops with the same barrier sequence.
 template <int D, class E, bool DELTA>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) void chain_kernel(PrefArgs a) {
+__global__ __attribute__((amdgpu_flat_work_group_size(1, ChainCfg<D, E>::THREADS))) void chain_kernel(PrefArgs a) {
     using Ly = Layout<D, E>;
     using C = ChainCfg<D, E>;
     extern __shared__ __align__(16) unsigned char smem[];
-    // blockIdx -> (slice, column group) so that all column groups of one slice run on the same
-    // XCD (workgroups are dealt to the 8 XCDs round-robin) and share its L2.
+    // blockIdx -> (slice, workgroup column block) so that all workgroups of one slice run on the
+    // same XCD (workgroups are dealt to the 8 XCDs round-robin) and share its L2.
     const int xcd = blockIdx.x & 7, sl = blockIdx.x >> 3;
-    const int cg = sl % C::NCW, bh = (sl / C::NCW) * 8 + xcd;
+    const int cgw = sl % C::NCW, bh = (sl / C::NCW) * 8 + xcd;
     if (bh >= a.BH) return;
     const int lane = threadIdx.x & 63;
     const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);   // wave-uniform
     const unsigned char* rec0 = a.ws + (size_t)bh * a.segcap * Ly::REC;
-    if (w >= 2)
-        chain_loader<D, E>(smem, rec0, a.nseg, cg, w - 2, lane);
-    else if (w == 0)
-        chain_compute<D, E, DELTA, 0>(a, smem, rec0, a.nseg, bh, cg, lane);
-    else
-        chain_compute<D, E, DELTA, 1>(a, smem, rec0, a.nseg, bh, cg, lane);
+    if (w >= 2 * C::CPW) {
+        chain_loader<D, E>(smem, rec0, a.nseg, w - 2 * C::CPW, lane);
+    } else {
+        const int cgl = w >> 1, cg = C::CPW * cgw + cgl;
+        if (w & 1)
+            chain_compute<D, E, DELTA, 1>(a, smem, rec0, a.nseg, bh, cg, cgl, lane);
+        else
+            chain_compute<D, E, DELTA, 0>(a, smem, rec0, a.nseg, bh, cg, cgl, lane);
+    }
 }
 
 // ---------------------------------------------------------------------------------------------
 // stage 3: outputs from the chunk-start state
 // ---------------------------------------------------------------------------------------------
+// P^T tiles (st, rt) the output stage needs: every tile inside a token block that some P
+// fragment of token tile rt reads (tiles above the diagonal come out as zeros)
+template <class E>
+struct OutTiles {
+    static constexpr int FPD = MM<E>::KB / 16;
+    static constexpr int kbmax(int rt) { return (16 * rt + 15) / MM<E>::KB; }
+    static constexpr int count() {
+        int c = 0;
+        for (int rt = 0; rt < 4; ++rt) c += FPD * (kbmax(rt) + 1);
+        return c;
+    }
+    static constexpr int N = count();
+    static constexpr int PER_WAVE = (N + 3) / 4;
+    // tile i -> (rt, st), in order of rt then st
+    static __device__ __forceinline__ void tile(int i, int& rt, int& st) {
+        rt = 0;
+        while (i >= FPD * (kbmax(rt) + 1)) { i -= FPD * (kbmax(rt) + 1); ++rt; }
+        st = i;
+    }
+};
+
 template <int D, class E, bool DELTA>
 __global__ __launch_bounds__(256) void output_kernel(PrefArgs a) {
     using T = typename E::T;
     using M = MM<E>;
     using Ly = Layout<D, E>;
+    using OT = OutTiles<E>;
     using frag = typename M::frag;
-    constexpr int KB = M::KB, NKD = Ly::NKD, NKT = Ly::NKT, NDT = Ly::NDT;
+    constexpr int KB = M::KB, NKD = Ly::NKD, NKT = Ly::NKT, NDT = Ly::NDT, FPD = OT::FPD;
     constexpr int KP = D + 8;   // row stride of the staged Q and K tiles (elements)
     extern __shared__ __align__(16) unsigned char smem[];
     unsigned char* sP = smem;                                    // P fragments [rt][kt]
-    unsigned char* sQ = sP + 4 * NKT * 1024;                     // e^g Q fragments [rt][kd]
-    T* Qr = reinterpret_cast<T*>(sQ + 4 * NKD * 1024);           // [CH][KP] Q rows
+    T* Qr = reinterpret_cast<T*>(sP + 4 * NKT * 1024);           // [CH][KP] Q rows
     T* Kr = Qr + CH * KP;                                        // [CH][KP] K rows
     float* sg = reinterpret_cast<float*>(Kr + CH * KP);          // g
 
@@ -684,35 +716,48 @@ __global__ __launch_bounds__(256) void output_kernel(PrefArgs a) {
         sg[lane] = wave_scan(la, lane);
     }
     __syncthreads();
-    {
-        // wave w: token tile rt = w. P^T tiles (st, rt) for st <= rt, then P fragments.
-        const int rt = w;
-        const int r = 16 * rt + m;   // this lane's token as the B-operand column
-        const T* rq = Qr + r * KP;
-        f32x4 pt[4];
+    // P^T tile (st, rt), lane (j, n): P[r = 16 rt + n][s = 16 st + 4 j + e] = exp(g_r - g_s) q_r.k_s
+    // for s <= r, else 0. Written straight into its half (bf16) or whole (fp32) of the P fragment
+    // [rt][st / FPD], whose lane (j, n) holds column r and k = s.
 #pragma unroll
-        for (int st = 0; st < 4; ++st) {
-            pt[st] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int x = 0; x < OT::PER_WAVE; ++x) {
+        const int ti = w + 4 * x;
+        if (ti < OT::N) {
+            int rt, st;
+            OT::tile(ti, rt, st);
+            f32x4 pt = {0.f, 0.f, 0.f, 0.f};
             if (st <= rt) {
-                const T* rk = Kr + (16 * st + m) * KP;
 #pragma unroll
                 for (int kd = 0; kd < NKD; ++kd)
-                    pt[st] = M::mma(row_frag<E>(rk, kd * KB, j, 1.f), row_frag<E>(rq, kd * KB, j, 1.f), pt[st]);
+                    pt = M::mma(row_frag_raw<E>(Kr + (16 * st + m) * KP, kd * KB, j),
+                                row_frag_raw<E>(Qr + (16 * rt + m) * KP, kd * KB, j), pt);
+                const int r = 16 * rt + m;
+                const float gr = sg[r];
 #pragma unroll
                 for (int e = 0; e < 4; ++e) {
-                    const int s = 16 * st + 4 * j + e;
-                    pt[st][e] = (s <= r) ? pt[st][e] * __expf(sg[r] - sg[s]) : 0.f;
+                    const int s2 = 16 * st + 4 * j + e;
+                    pt[e] = (s2 <= r) ? pt[e] * __expf(gr - sg[s2]) : 0.f;
                 }
             }
+            unsigned char* dst = sP + (size_t)(rt * NKT + st / FPD) * 1024 + lane * 16;
+            if constexpr (FPD == 2) {
+                *reinterpret_cast<uint2*>(dst + 8 * (st % 2)) = uint2{f2bf2(pt[0], pt[1]), f2bf2(pt[2], pt[3])};
+            } else {
+                *reinterpret_cast<f32x4*>(dst) = pt;
+            }
         }
-#pragma unroll
-        for (int kt = 0; kt < NKT; ++kt) st_frag(sP + (rt * NKT + kt) * 1024, lane, M::from_acc(pt, kt));
-        const float eg = __expf(sg[r]);
-#pragma unroll
-        for (int kd = 0; kd < NKD; ++kd) st_frag(sQ + (rt * NKD + kd) * 1024, lane, row_frag<E>(rq, kd * KB, j, eg));
     }
     __syncthreads();
-    // wave w: value tiles vt = w, w + 4, ...; all four token tiles
+    // O^T tiles (vt, rt) = H^T e^g Q^T + U^T P^T: the state product with raw Q fragments, scaled
+    // by e^{g_r} per token column, then the intra-chunk part accumulated on top
+    float eg[4];
+    frag Qf[4][NKD];
+#pragma unroll
+    for (int rt = 0; rt < 4; ++rt) {
+        eg[rt] = __expf(sg[16 * rt + m]);
+#pragma unroll
+        for (int kd = 0; kd < NKD; ++kd) Qf[rt][kd] = row_frag_raw<E>(Qr + (16 * rt + m) * KP, kd * KB, j);
+    }
 #pragma unroll
     for (int iv = 0; iv < NVW; ++iv) {
         const int vt = w + 4 * iv;
@@ -723,12 +768,15 @@ __global__ __launch_bounds__(256) void output_kernel(PrefArgs a) {
 #pragma unroll
         for (int kd = 0; kd < NKD; ++kd)
 #pragma unroll
-            for (int rt = 0; rt < 4; ++rt) acc[rt] = M::mma(Hc[iv][kd], ld_frag<frag>(sQ + (rt * NKD + kd) * 1024, lane), acc[rt]);
+            for (int rt = 0; rt < 4; ++rt) acc[rt] = M::mma(Hc[iv][kd], Qf[rt][kd], acc[rt]);
+#pragma unroll
+        for (int rt = 0; rt < 4; ++rt)
+            acc[rt] = f32x4{acc[rt][0] * eg[rt], acc[rt][1] * eg[rt], acc[rt][2] * eg[rt], acc[rt][3] * eg[rt]};
 #pragma unroll
         for (int kt = 0; kt < NKT; ++kt)
 #pragma unroll
             for (int rt = 0; rt < 4; ++rt)
-                if (kt <= (16 * rt + 15) / KB) acc[rt] = M::mma(Uf[iv][kt], ld_frag<frag>(sP + (rt * NKT + kt) * 1024, lane), acc[rt]);
+                if (kt <= OT::kbmax(rt)) acc[rt] = M::mma(Uf[iv][kt], ld_frag<frag>(sP + (rt * NKT + kt) * 1024, lane), acc[rt]);
 #pragma unroll
         for (int rt = 0; rt < 4; ++rt) {
             // lane (j, m): O[token 16 rt + m][16 vt + 4 j .. + 3]
@@ -752,7 +800,7 @@ struct Launch {
     static constexpr int KP = D + 8;
     static constexpr size_t LDS_PREP = PrepCfg<D, E>::LDS;
     static constexpr size_t LDS_CHAIN = (size_t)CC::NS * CC::SLOT + CC::XBYTES;
-    static constexpr size_t LDS_OUT = (size_t)4 * (Ly::NKT + Ly::NKD) * 1024 + (size_t)2 * CH * KP * sizeof(T) + CH * 4;
+    static constexpr size_t LDS_OUT = (size_t)4 * Ly::NKT * 1024 + (size_t)2 * CH * KP * sizeof(T) + CH * 4;
 
     // raise the dynamic-LDS limits once per process (every caller sets the same values)
     static bool attributes() {
@@ -769,7 +817,7 @@ struct Launch {
         hipLaunchKernelGGL((prep_kernel<D, E, DELTA>), dim3(a.nseg, a.BH), dim3(256), LDS_PREP, s, a);
     }
     static void chain(const PrefArgs& a, hipStream_t s) {
-        hipLaunchKernelGGL((chain_kernel<D, E, DELTA>), dim3(8 * ((a.BH + 7) / 8) * CC::NCW), dim3(256), LDS_CHAIN, s, a);
+        hipLaunchKernelGGL((chain_kernel<D, E, DELTA>), dim3(8 * ((a.BH + 7) / 8) * CC::NCW), dim3(CC::THREADS), LDS_CHAIN, s, a);
     }
     static void output(const PrefArgs& a, hipStream_t s) {
         hipLaunchKernelGGL((output_kernel<D, E, DELTA>), dim3(a.nseg, a.BH), dim3(256), LDS_OUT, s, a);
