@@ -12,6 +12,8 @@ roofline of the prefill, and the fp64 oracle timed on this host's cores on a bou
 from __future__ import annotations
 
 import argparse
+import glob
+import hashlib
 import json
 import os
 import sys
@@ -27,6 +29,25 @@ from gated_deltanet_chunked_rule_amd import inputs  # noqa: E402
 PEAK_HBM_GBPS = 8000.0          # MI355X HBM3E
 PEAK_BF16_TFLOPS = 2500.0       # MI355X dense bf16 MFMA
 METRIC = "GDN prefill tokens/s at L=128K + % bf16 MFMA peak; decode state GB/s"
+
+# Memory traffic of one 128K prefill call, from rocprofv3 counter runs (FETCH_SIZE and WRITE_SIZE
+# summed over the call's prep, chain and output dispatches, each divided by what the counter
+# reads per byte for a plain copy of known size); profiles/gdn_prefill_B1H16L131072_traffic.md
+# holds the commands and the raw figures. Valid only for the kernel sources it was taken on:
+# bench.py reports it only while kernel_source_hash() still matches.
+TRAFFIC_128K = {"source_hash": "e6c482f0f6b383c4", "bytes_per_call": 9240344821}
+
+
+def kernel_source_hash():
+    """sha256 over the HIP sources and headers of libgdn (sorted by name)."""
+    h = hashlib.sha256()
+    csrc = os.path.join(ROOT, "gated_deltanet_chunked_rule_amd", "csrc")
+    for f in sorted(glob.glob(os.path.join(csrc, "*"))):
+        if f.endswith((".hip", ".h", ".cpp")):
+            h.update(os.path.basename(f).encode())
+            with open(f, "rb") as fh:
+                h.update(fh.read())
+    return h.hexdigest()[:16]
 
 
 # ---------------------------------------------------------------------------------------------
@@ -68,7 +89,7 @@ def to_dev(torch, x, dtype):
     return torch.from_numpy(np.ascontiguousarray(x, dtype=np.float32)).to("cuda").to(dtype)
 
 
-def prefill_device_inputs(torch, cfg, gates=True):
+def prefill_device_inputs(torch, cfg, gates=True, verbose=False):
     dt = torch.bfloat16 if cfg.dtype == "bf16" else torch.float32
     shp = (cfg.B, cfg.H, cfg.L)
     q = torch.empty(shp + (cfg.Dk,), dtype=dt, device="cuda")
@@ -78,6 +99,8 @@ def prefill_device_inputs(torch, cfg, gates=True):
     h0 = torch.empty((cfg.B, cfg.H, cfg.Dk, cfg.Dv), device="cuda") if cfg.h0 is not None else None
     for b in range(cfg.B):
         for h in range(cfg.H):
+            if verbose:
+                print(f"inputs: slice {b * cfg.H + h + 1} of {cfg.B * cfg.H}", file=sys.stderr, flush=True)
             s = inputs.prefill_slice(cfg, b, h)
             for name, t in (("q", q), ("k", k), ("v", v), ("beta", beta), ("log_alpha", la), ("h0", h0)):
                 if t is not None:
@@ -103,8 +126,8 @@ def time_loop(torch, fn, steps, warmup):
 # ---------------------------------------------------------------------------------------------
 # components
 # ---------------------------------------------------------------------------------------------
-def bench_prefill(torch, ops, cfg, steps, warmup, gdn=True):
-    q, k, v, beta, la, h0 = prefill_device_inputs(torch, cfg, gates=gdn)
+def bench_prefill(torch, ops, cfg, steps, warmup, gdn=True, verbose=False):
+    q, k, v, beta, la, h0 = prefill_device_inputs(torch, cfg, gates=gdn, verbose=verbose)
     o = torch.empty_like(v)
     hf = torch.empty((cfg.B, cfg.H, cfg.Dk, cfg.Dv), device="cuda")
     ws = torch.empty(ops.prefill_workspace_size(cfg.B, cfg.H, cfg.L, cfg.Dk, q.dtype), dtype=torch.uint8,
@@ -193,7 +216,15 @@ def main():
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--profile-steps", type=int, default=0,
                     help="only run this many prefill steps after warm-up (for profilers), no JSON")
+    ap.add_argument("--profile-decode", type=int, default=0,
+                    help="only run this many decode steps (for profilers), no JSON")
+    ap.add_argument("--copy-calibrate", type=int, default=0, metavar="BYTES",
+                    help="only copy BYTES device-to-device three times (counter calibration), no JSON")
+    ap.add_argument("--source-hash", action="store_true", help="print kernel_source_hash() and exit")
     args = ap.parse_args()
+    if args.source_hash:
+        print(kernel_source_hash())
+        return
     if args.gpus != 1:
         print("bench.py measures one GPU: this build has no multi-GPU path (heads and sequences shard "
               "across GPUs with no communication; see the design notes). Run with --gpus 1.", file=sys.stderr)
@@ -205,9 +236,23 @@ def main():
     log = lambda m: print(m, file=sys.stderr, flush=True)
 
     cfg = inputs.GDN_128K
+    if args.copy_calibrate:
+        src = torch.ones(args.copy_calibrate // 4, dtype=torch.float32, device="cuda")
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        log(f"copied {src.numel() * 4} bytes three times")
+        return
+    if args.profile_decode:
+        c = inputs.DECODE_256x32
+        r = bench_decode(torch, ops, c, args.profile_decode)
+        log(f"profiled {args.profile_decode} decode steps: {r['ms_per_step']:.4f} ms/step")
+        return
     if args.profile_steps:
         log("generating inputs")
-        res, bufs = bench_prefill(torch, ops, cfg, args.profile_steps, args.warmup)
+        res, bufs = bench_prefill(torch, ops, cfg, args.profile_steps, args.warmup, verbose=True)
         log(f"profiled {args.profile_steps} steps: {res['ms']:.3f} ms/step")
         return
 
@@ -237,6 +282,9 @@ def main():
         log("[bench] cpu baseline (fp64 oracle)")
         cpu, parity = cpu_baseline(cfg, args.cpu_seconds, gpu_out=gpu_o)
 
+    traffic = None
+    if TRAFFIC_128K is not None and TRAFFIC_128K["source_hash"] == kernel_source_hash():
+        traffic = TRAFFIC_128K["bytes_per_call"]
     line = {
         "metric": METRIC,
         "value": res["tokens_per_s"],
@@ -254,9 +302,11 @@ def main():
         "config": {"workload": "gdn_prefill_B1_H16_L131072_d128_chunk64", "B": cfg.B, "H": cfg.H,
                    "L": cfg.L, "d_k": cfg.Dk, "d_v": cfg.Dv, "chunk": 64, "qkv": "bf16", "gates_state": "fp32"},
         "mfma": {"alg_tflops": res["alg_tflops"], "peak_tflops": PEAK_BF16_TFLOPS, "frac": res["mfma_frac"]},
-        "roofline": {"bound": "hbm", "kernel": "gdn_prefill_fwd (prep, chain, output launches)",
+        # one gdn_prefill_fwd call is the unit: its three kernels run concurrently on three
+        # streams, so the call (timed with HIP events on the caller's stream) is the launch
+        "roofline": {"bound": "hbm", "kernel": "gdn_prefill_fwd (prep, chain, output kernels)",
                      "achieved": res["hbm_GBps"], "peak": PEAK_HBM_GBPS, "unit": "GB/s",
-                     "frac": res["hbm_frac"], "traffic": None, "alg_bytes_per_launch": res["alg_bytes"]},
+                     "frac": res["hbm_frac"], "traffic": traffic, "alg_bytes_per_launch": res["alg_bytes"]},
         "cpu_baseline": cpu,
         "parity_sample": parity,
         "components": components,

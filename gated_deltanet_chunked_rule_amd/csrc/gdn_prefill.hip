@@ -394,7 +394,8 @@ struct ChainCfg {
     static constexpr int NBLK = (int)(SLOT / 1024);                      // 1 KB wave blocks per slot
     static constexpr int BPW = NBLK / 2;                                 // blocks per loader wave
     static_assert(SLOT % 2048 == 0, "slot splits into whole blocks per loader wave");
-    static constexpr size_t XBYTES = (size_t)CPW * 2 * 4 * 64 * 16;     // partial W H of both halves
+    static constexpr size_t XHALF = (size_t)4 * 64 * 16;                 // one wave's partial W H
+    static constexpr size_t XBYTES = (size_t)2 * CPW * 2 * XHALF;       // [step parity][group][half]
     static constexpr int NS = SLOT * 4 + XBYTES <= 156 * 1024 ? 4 : (SLOT * 3 + XBYTES <= 156 * 1024 ? 3 : 2);
     static constexpr int INFLIGHT = NS - 2;                              // chunks still loading at a barrier
     static_assert(INFLIGHT * BPW < 64, "vmcnt is 6 bits");
@@ -452,8 +453,9 @@ __device__ __forceinline__ void chain_issue_slot(unsigned char* slot, const unsi
 }
 
 // Loader wave lw (0 or 1) of a chain workgroup: chunk c + NS - 1 is issued at step c into the
-// slot freed at step c - 1; before each chunk's first barrier the loader waits only for the
-// chunk needed next. Two barriers per chunk, like the compute waves.
+// slot of chunk c - 1, whose fragments the compute waves read before barrier c - 1; before
+// barrier c the loader waits for chunk c + 1, which the compute waves read after it. One
+// barrier per chunk, like the compute waves.
 template <int D, class E>
 __device__ __forceinline__ void chain_loader(unsigned char* smem, const unsigned char* rec0, int nch, int lw, int lane) {
     using Ly = Layout<D, E>;
@@ -468,7 +470,6 @@ __device__ __forceinline__ void chain_loader(unsigned char* smem, const unsigned
         const int cn = c + NS - 1;
         chain_issue_slot<D, E>(smem + (size_t)(cn % NS) * C::SLOT, rec0 + (size_t)min(cn, nch - 1) * Ly::REC, lw, lane);
         wait_vmcnt<C::INFLIGHT * C::BPW>();
-        lds_barrier();
         lds_barrier();
     }
     wait_vmcnt<0>();   // no LDS write may land after the workgroup ends
@@ -488,8 +489,10 @@ __device__ __forceinline__ f32x4 ut_f32(float4 r) { return f32x4{r.x, r.y, r.z, 
 //      H *= chunk decay.
 //   B  U = P_HH + P_other (fp32 addition is commutative, so both waves hold the same U);
 //      H += Khat^T[half, :] bf16(U); then the next chunk's -W and Khat^T fragments are read from
-//      its slot (complete since this step's first barrier), so neither product of the next step
+//      its slot (complete since this step's barrier), so neither product of the next step
 //      waits on LDS.
+// One barrier per step, between A and B: the partial products alternate between two LDS areas
+// by step parity, so an area is rewritten only after the partner has passed the next barrier.
 // Ut columns and the decay come from the workspace one chunk ahead, in registers.
 template <int D, class E, bool DELTA, int HH>
 __device__ __forceinline__ void chain_compute(const PrefArgs& a, unsigned char* smem, const unsigned char* rec0,
@@ -503,8 +506,9 @@ __device__ __forceinline__ void chain_compute(const PrefArgs& a, unsigned char* 
     constexpr int NKD = Ly::NKD, NKT = Ly::NKT, NDT = Ly::NDT, NS = C::NS;
     constexpr int HKD = NKD / 2, HDT = NDT / 2;   // fragments / tiles of one row half
     constexpr int NUT = DELTA ? 2 : 4;            // Ut tiles this wave reads: its own two, or all
-    // [half][rt][lane] partial products of this column group
-    f32x4* X = reinterpret_cast<f32x4*>(smem + (size_t)NS * C::SLOT + (size_t)cgl * (C::XBYTES / C::CPW));
+    // [half][rt][lane] partial products of this column group, for even and odd steps
+    f32x4* X0 = reinterpret_cast<f32x4*>(smem + (size_t)NS * C::SLOT + (size_t)cgl * 2 * C::XHALF);
+    constexpr size_t XPAR = C::CPW * 2 * C::XHALF / sizeof(f32x4);   // f32x4 elements per parity
     const int j = lane >> 4, m = lane & 15;
     const int col = 16 * cg + m;
     f32x4 H[HDT];   // lane (j, m): H[16 (HH HDT + t) + 4 j + e][col]
@@ -543,6 +547,7 @@ __device__ __forceinline__ void chain_compute(const PrefArgs& a, unsigned char* 
     // ever copied (a copy would wait for its load).
     auto step = [&](int c, const UR (&ut)[NUT], float dec, UR (&ut_n)[NUT], float& dec_n) {
         unsigned char* recB = const_cast<unsigned char*>(rec0) + (size_t)c * Ly::REC + Ly::REC_A;
+        f32x4* X = X0 + (c & 1) * XPAR;
         fetch(min(c + 1, nch - 1), ut_n, dec_n);
         frag Hf[HKD];
 #pragma unroll
@@ -585,7 +590,6 @@ __device__ __forceinline__ void chain_compute(const PrefArgs& a, unsigned char* 
 #pragma unroll
             for (int t = 0; t < HDT; ++t) H[t] = M::mma(kf[t * NKT + kt], Uf[kt], H[t]);
         read_slot((c + 1) % NS);
-        lds_barrier();   // slot c and the exchange area may be reused
     };
     UR ua[NUT], ub[NUT];
     float da, db;
