@@ -373,32 +373,56 @@ __global__ __launch_bounds__(256) void prep_kernel(PrefArgs a) {
 // ---------------------------------------------------------------------------------------------
 // stage 2: the sequential chunk-to-chunk pass, state resident in registers
 // ---------------------------------------------------------------------------------------------
-// Chain workgroup: one slice (batch, head) and CPW groups of 16 value columns. The fp32 state of
-// a column group (Dk x 16) is split by rows between two compute waves, each holding its half in
-// accumulator registers for the whole sequence; per chunk they exchange their fp32 partial
-// products W H through LDS (4 KB each), so each wave's chain step is half the MFMA work. Two
-// loader waves stream the per-chunk -W and Khat^T fragments (contiguous at the start of each
-// prep record, shared by all column groups of the slice) into a ring of NS LDS slots, NS - 1
-// chunks ahead, so the sequential chain never waits on a global-memory round trip. For bf16 at
-// Dk = 128 a slot is 32 KB: direct-to-LDS loads stream at about twice the rate when no more
-// than that is requested per chunk. The compute waves fetch their few Ut columns and the chunk
-// decay themselves with ordinary loads, one chunk ahead.
-template <int D, class E>
+// Chain workgroup: one slice (batch, head) and 16 value columns (a column group), four waves.
+// The fp32 state of the column group (Dk x 16) is split by rows between the two compute waves,
+// each holding its half in accumulator registers for the whole sequence; per chunk they exchange
+// their fp32 partial products W H through LDS (4 KB each), so each wave's chain step is half the
+// MFMA work. The compute waves touch no global memory in their loop: the two loader waves
+//   - stream each chunk's -W and Khat^T fragments (contiguous at the start of its prep record,
+//     shared by all column groups of the slice), the group's Ut tiles and the decay into a ring
+//     of NS LDS slots, NS - 1 chunks ahead, and
+//   - store the chunk-start state and U fragments the compute waves leave in an LDS staging
+//     area (three steps deep) to the workspace for the output stage.
+// A CU's vector-memory path serves all its waves in order, so stores issued by the compute
+// waves would queue behind the loaders' streaming loads and stall the sequential chain; issued
+// by the loaders, they only delay loads that are steps ahead of their use.
+template <int D, class E, bool DELTA>
 struct ChainCfg {
     using Ly = Layout<D, E>;
-    static constexpr int CPW = 1;                                        // column groups per workgroup
-    static constexpr int NCW = D / 16 / CPW;                             // workgroups per slice
-    static constexpr int THREADS = 64 * (2 * CPW + 2);                   // compute waves, then 2 loaders
-    static constexpr size_t UTSUB = (size_t)4 * 64 * 4 * sizeof(typename E::T);  // Ut bytes of 16 columns
+    static constexpr int NCW = D / 16;                                   // workgroups per slice
+    static constexpr int THREADS = 256;                                  // 2 compute waves, then 2 loaders
     static constexpr size_t SLOT = Ly::A_UT;                             // -W and Khat^T fragments
     static constexpr int NBLK = (int)(SLOT / 1024);                      // 1 KB wave blocks per slot
     static constexpr int BPW = NBLK / 2;                                 // blocks per loader wave
     static_assert(SLOT % 2048 == 0, "slot splits into whole blocks per loader wave");
+    static constexpr size_t UTSUB = (size_t)4 * 64 * 4 * sizeof(typename E::T);  // Ut bytes of 16 columns
+    static constexpr int UTL = (int)(UTSUB / 2048);                      // Ut 1 KB loads per loader wave
+    static_assert(UTSUB % 2048 == 0, "Ut splits into whole blocks per loader wave");
+    static constexpr size_t USLOT = UTSUB + 256;                         // Ut, then the decay (a dword per lane)
+    static constexpr int DMA_OPS = BPW + UTL + 1;                        // loads per loader wave and chunk
     static constexpr size_t XHALF = (size_t)4 * 64 * 16;                 // one wave's partial W H
-    static constexpr size_t XBYTES = (size_t)2 * CPW * 2 * XHALF;       // [step parity][group][half]
-    static constexpr int NS = SLOT * 4 + XBYTES <= 156 * 1024 ? 4 : (SLOT * 3 + XBYTES <= 156 * 1024 ? 3 : 2);
+    static constexpr size_t XBYTES = DELTA ? (size_t)2 * 2 * XHALF : 0; // [step parity][half]
+    // per compute wave and step: its Dk/2 rows of the state (Ly::NKD / 2 fragments) and half of
+    // the U fragments
+    static constexpr int STG = Ly::NKD / 2 + Ly::NKT / 2;
+    static constexpr size_t STB = (size_t)STG * 1024;
+    // the loaders store them when the staging area fits beside two or more slots (not for fp32 at
+    // Dk = 128, whose compute waves store their own fragments)
+    static constexpr bool SL = (SLOT + USLOT) * 2 + XBYTES + 3 * 2 * STB <= 156 * 1024;
+    static constexpr size_t STAGE = SL ? 3 * 2 * STB : 0;                // [step % 3][wave][fragment]
+    static constexpr size_t FIXED = XBYTES + STAGE;
+    static constexpr int NS = (SLOT + USLOT) * 4 + FIXED <= 156 * 1024 ? 4 : ((SLOT + USLOT) * 3 + FIXED <= 156 * 1024 ? 3 : 2);
+    static constexpr size_t O_X = NS * SLOT;                             // LDS offsets of the areas
+    static constexpr size_t O_UT = O_X + XBYTES;
+    static constexpr size_t O_ST = O_UT + NS * USLOT;
+    static constexpr size_t LDS = O_ST + STAGE;
+    static_assert(LDS <= 156 * 1024, "chain LDS");
     static constexpr int INFLIGHT = NS - 2;                              // chunks still loading at a barrier
-    static_assert(INFLIGHT * BPW < 64, "vmcnt is 6 bits");
+    // a loader's vector-memory operations after chunk c + 1's loads when it waits for them:
+    // that chunk's iteration's stores, then INFLIGHT whole iterations
+    static constexpr int LST = SL ? STG : 0;                             // stores per loader iteration
+    static constexpr int WAITN = LST + INFLIGHT * (DMA_OPS + LST);
+    static_assert(WAITN < 64, "vmcnt is 6 bits");
 };
 
 // Barrier of the chain workgroup. Only LDS is shared between its waves: the loader waves fill it
@@ -434,81 +458,119 @@ __device__ __forceinline__ void dma16(const void* src, unsigned lds_base) {
     asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(src), "s"(lds_base)
                  : "memory", "m0");
 }
+// Same with 4 bytes per lane: lane l's dword lands at lds_base + 4 l.
+__device__ __forceinline__ void dma4(const void* src, unsigned lds_base) {
+    lds_base = __builtin_amdgcn_readfirstlane(lds_base);
+    asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dword %0, off" ::"v"(src), "s"(lds_base)
+                 : "memory", "m0");
+}
 #pragma clang diagnostic pop
 
 __device__ __forceinline__ unsigned lds_addr(const void* p) {
     return (unsigned)(size_t)(const __attribute__((address_space(3))) void*)p;
 }
 
-// One loader wave's share of a chunk: BPW 1 KB blocks, interleaved with the other loader's.
-template <int D, class E>
-__device__ __forceinline__ void chain_issue_slot(unsigned char* slot, const unsigned char* recA, int lw, int lane) {
-    using C = ChainCfg<D, E>;
-    const unsigned base = lds_addr(slot);
+// Loader wave lw's share of chunk c's loads into slot s: BPW 1 KB blocks of the -W / Khat^T
+// fragments (interleaved with the other loader's), its half of the Ut tiles, and the decay
+// (both loaders load it; same bytes, same place).
+template <int D, class E, bool DELTA>
+__device__ __forceinline__ void chain_issue(unsigned char* smem, const unsigned char* rec, int s, int cg, int lw,
+                                            int lane) {
+    using C = ChainCfg<D, E, DELTA>;
+    using Ly = Layout<D, E>;
+    const unsigned base = lds_addr(smem + (size_t)s * C::SLOT);
 #pragma unroll
     for (int i = 0; i < C::BPW; ++i) {
         const unsigned blk = (unsigned)(lw + 2 * i) * 1024u;
-        dma16(recA + blk + lane * 16, base + blk);
+        dma16(rec + blk + lane * 16, base + blk);
+    }
+    const unsigned ubase = lds_addr(smem + C::O_UT + (size_t)s * C::USLOT);
+    const unsigned char* ut = rec + Ly::A_UT + (size_t)cg * C::UTSUB;
+#pragma unroll
+    for (int i = 0; i < C::UTL; ++i) {
+        const unsigned blk = (unsigned)(lw * C::UTL + i) * 1024u;
+        dma16(ut + blk + lane * 16, ubase + blk);
+    }
+    dma4(rec + Ly::A_DEC, ubase + (unsigned)C::UTSUB);
+}
+
+// Loader wave lw's stores of step c's staged fragments (those of compute wave lw): its rows of
+// the chunk-start state, then its U fragments (kt = lw, lw + 2, ...).
+template <int D, class E, bool DELTA>
+__device__ __forceinline__ void chain_store(const unsigned char* smem, unsigned char* recB, int c, int cg, int lw,
+                                            int lane) {
+    using C = ChainCfg<D, E, DELTA>;
+    using Ly = Layout<D, E>;
+    constexpr int HKD = Ly::NKD / 2;
+    const unsigned char* st = smem + C::O_ST + ((size_t)(c % 3) * 2 + lw) * C::STB;
+#pragma unroll
+    for (int i = 0; i < C::STG; ++i) {
+        const uint4 x = *reinterpret_cast<const uint4*>(st + (size_t)i * 1024 + lane * 16);
+        const size_t off = i < HKD ? Ly::B_H + (size_t)(cg * Ly::NKD + lw * HKD + i) * Ly::FR
+                                   : Ly::B_U + (size_t)(cg * Ly::NKT + lw + 2 * (i - HKD)) * Ly::FR;
+        *reinterpret_cast<uint4*>(recB + off + lane * 16) = x;
     }
 }
 
-// Loader wave lw (0 or 1) of a chain workgroup: chunk c + NS - 1 is issued at step c into the
-// slot of chunk c - 1, whose fragments the compute waves read before barrier c - 1; before
-// barrier c the loader waits for chunk c + 1, which the compute waves read after it. One
-// barrier per chunk, like the compute waves.
-template <int D, class E>
-__device__ __forceinline__ void chain_loader(unsigned char* smem, const unsigned char* rec0, int nch, int lw, int lane) {
+// Loader wave lw (0 or 1) of a chain workgroup. Iteration c (after barrier c - 1): issue chunk
+// c + NS - 1 into the slot of chunk c - 1 (whose fragments the compute waves read before
+// barrier c - 1), store step c - 2's staged fragments (complete since barrier c - 1), wait for
+// chunk c + 1 (read by the compute waves after barrier c), barrier c. Every iteration issues the
+// same operations, so the wait is a fixed count once the first NS iterations are past (those
+// drain fully). After the last step, one more barrier and the last two steps' stores.
+template <int D, class E, bool DELTA>
+__device__ __forceinline__ void chain_loader(unsigned char* smem, const unsigned char* rec0, int nch, int cg, int lw,
+                                             int lane) {
     using Ly = Layout<D, E>;
-    using C = ChainCfg<D, E>;
+    using C = ChainCfg<D, E, DELTA>;
     constexpr int NS = C::NS;
+    auto recb = [&](int c) { return const_cast<unsigned char*>(rec0) + (size_t)c * Ly::REC + Ly::REC_A; };
     for (int c = 0; c < NS - 1; ++c)
-        chain_issue_slot<D, E>(smem + (size_t)c * C::SLOT, rec0 + (size_t)min(c, nch - 1) * Ly::REC, lw, lane);
-    wait_vmcnt<C::INFLIGHT * C::BPW>();
+        chain_issue<D, E, DELTA>(smem, rec0 + (size_t)min(c, nch - 1) * Ly::REC, c, cg, lw, lane);
+    wait_vmcnt<0>();
     lds_barrier();
     for (int c = 0; c < nch; ++c) {
-        // always issue (clamped to the last chunk) so the outstanding count stays fixed
-        const int cn = c + NS - 1;
-        chain_issue_slot<D, E>(smem + (size_t)(cn % NS) * C::SLOT, rec0 + (size_t)min(cn, nch - 1) * Ly::REC, lw, lane);
-        wait_vmcnt<C::INFLIGHT * C::BPW>();
+        const int cn = c + NS - 1;   // always issued (clamped to the last chunk): fixed counts
+        chain_issue<D, E, DELTA>(smem, rec0 + (size_t)min(cn, nch - 1) * Ly::REC, cn % NS, cg, lw, lane);
+        // step c - 2's fragments (before step 0: step 0's record, rewritten with the real ones
+        // two iterations later by this same wave, in order)
+        if constexpr (C::SL) chain_store<D, E, DELTA>(smem, recb(max(c - 2, 0)), max(c - 2, 0), cg, lw, lane);
+        if (c < NS)
+            wait_vmcnt<0>();
+        else
+            wait_vmcnt<C::WAITN>();
         lds_barrier();
     }
+    lds_barrier();   // the compute waves' last step is staged
+    if constexpr (C::SL)
+        for (int c = max(nch - 2, 0); c < nch; ++c) chain_store<D, E, DELTA>(smem, recb(c), c, cg, lw, lane);
     wait_vmcnt<0>();   // no LDS write may land after the workgroup ends
 }
 
-// Ut tile of 4 elements per lane as stored (bf16 or fp32), and as fp32
-__device__ __forceinline__ f32x4 ut_f32(uint2 r) {
-    return f32x4{__uint_as_float(r.x << 16), __uint_as_float(r.x & 0xffff0000u), __uint_as_float(r.y << 16),
-                 __uint_as_float(r.y & 0xffff0000u)};
-}
-__device__ __forceinline__ f32x4 ut_f32(float4 r) { return f32x4{r.x, r.y, r.z, r.w}; }
-
 // Compute wave HH of a chain workgroup: it owns state rows [HH Dk/2, (HH + 1) Dk/2) of column
-// group cg. Per chunk:
-//   A  Hf = bf16(H) (also handed to the output stage); partial product P_HH = (-W)[:, half] Hf,
-//      with Ut folded into the accumulators of token tiles 2 HH and 2 HH + 1; P_HH -> LDS;
+// group cg. Per chunk c:
+//   A  Hf = bf16(H), staged for the output stage; partial product P_HH = (-W)[:, half] Hf, with
+//      Ut folded into the accumulators of token tiles 2 HH and 2 HH + 1; P_HH -> LDS;
 //      H *= chunk decay.
-//   B  U = P_HH + P_other (fp32 addition is commutative, so both waves hold the same U);
-//      H += Khat^T[half, :] bf16(U); then the next chunk's -W and Khat^T fragments are read from
-//      its slot (complete since this step's barrier), so neither product of the next step
-//      waits on LDS.
+//   B  U = P_HH + P_other (fp32 addition is commutative, so both waves hold the same U), its
+//      fragments half staged; H += Khat^T[half, :] bf16(U); then chunk c + 1's -W and Khat^T
+//      fragments are read from its slot (complete since barrier c), so neither product of the
+//      next step waits on LDS.
 // One barrier per step, between A and B: the partial products alternate between two LDS areas
 // by step parity, so an area is rewritten only after the partner has passed the next barrier.
-// Ut columns and the decay come from the workspace one chunk ahead, in registers.
+// Ut and the decay are read in A, before the barrier after which their slot may be refilled.
 template <int D, class E, bool DELTA, int HH>
 __device__ __forceinline__ void chain_compute(const PrefArgs& a, unsigned char* smem, const unsigned char* rec0,
-                                              int nch, int bh, int cg, int cgl, int lane) {
+                                              int nch, int bh, int cg, int lane) {
     using T = typename E::T;
     using M = MM<E>;
     using Ly = Layout<D, E>;
-    using C = ChainCfg<D, E>;
+    using C = ChainCfg<D, E, DELTA>;
     using frag = typename M::frag;
-    using UR = typename std::conditional<sizeof(T) == 2, uint2, float4>::type;   // 4 Ut elements as stored
     constexpr int NKD = Ly::NKD, NKT = Ly::NKT, NDT = Ly::NDT, NS = C::NS;
     constexpr int HKD = NKD / 2, HDT = NDT / 2;   // fragments / tiles of one row half
-    constexpr int NUT = DELTA ? 2 : 4;            // Ut tiles this wave reads: its own two, or all
-    // [half][rt][lane] partial products of this column group, for even and odd steps
-    f32x4* X0 = reinterpret_cast<f32x4*>(smem + (size_t)NS * C::SLOT + (size_t)cgl * 2 * C::XHALF);
-    constexpr size_t XPAR = C::CPW * 2 * C::XHALF / sizeof(f32x4);   // f32x4 elements per parity
+    f32x4* X0 = reinterpret_cast<f32x4*>(smem + C::O_X);                   // [parity][half][rt][lane]
+    constexpr size_t XPAR = 2 * C::XHALF / sizeof(f32x4);
     const int j = lane >> 4, m = lane & 15;
     const int col = 16 * cg + m;
     f32x4 H[HDT];   // lane (j, m): H[16 (HH HDT + t) + 4 j + e][col]
@@ -517,14 +579,6 @@ __device__ __forceinline__ void chain_compute(const PrefArgs& a, unsigned char* 
 #pragma unroll
         for (int e = 0; e < 4; ++e)
             H[t][e] = a.h0 ? a.h0[((size_t)bh * D + 16 * (HH * HDT + t) + 4 * j + e) * D + col] : 0.f;
-    // Ut tiles and decay of chunk c, from its record
-    auto fetch = [&](int c, UR (&u)[NUT], float& dec) {
-        const unsigned char* r = rec0 + (size_t)c * Ly::REC;
-        const UR* ut = reinterpret_cast<const UR*>(r + Ly::A_UT + (size_t)cg * C::UTSUB);   // [rt][lane]
-#pragma unroll
-        for (int i = 0; i < NUT; ++i) u[i] = ut[(DELTA ? 2 * HH + i : i) * 64 + lane];
-        dec = DELTA ? *reinterpret_cast<const float*>(r + Ly::A_DEC) : 1.f;
-    };
     // -W and Khat^T fragments of the chunk in slot s
     frag wf[4 * HKD], kf[HDT * NKT];
     auto read_slot = [&](int s) {
@@ -542,23 +596,35 @@ __device__ __forceinline__ void chain_compute(const PrefArgs& a, unsigned char* 
             for (int kt = 0; kt < NKT; ++kt)
                 kf[t * NKT + kt] = ld_frag<frag>(slot + Ly::A_KH + (size_t)((HH * HDT + t) * NKT + kt) * Ly::FR, lane);
     };
-    // one chain step on chunk c, whose Ut and decay are in (ut, dec); the next chunk's go into
-    // (ut_n, dec_n). The loop below alternates two register sets so that no prefetched value is
-    // ever copied (a copy would wait for its load).
-    auto step = [&](int c, const UR (&ut)[NUT], float dec, UR (&ut_n)[NUT], float& dec_n) {
-        unsigned char* recB = const_cast<unsigned char*>(rec0) + (size_t)c * Ly::REC + Ly::REC_A;
+    lds_barrier();
+    read_slot(0);
+    for (int c = 0; c < nch; ++c) {
         f32x4* X = X0 + (c & 1) * XPAR;
-        fetch(min(c + 1, nch - 1), ut_n, dec_n);
+        const unsigned char* us = smem + C::O_UT + (size_t)(c % NS) * C::USLOT;
+        const T* ut = reinterpret_cast<const T*>(us);   // [rt][lane][4]
+        unsigned char* st = smem + C::O_ST + ((size_t)(c % 3) * 2 + HH) * C::STB;
+        unsigned char* recB = const_cast<unsigned char*>(rec0) + (size_t)c * Ly::REC + Ly::REC_A;
         frag Hf[HKD];
 #pragma unroll
         for (int kk = 0; kk < HKD; ++kk) {
             Hf[kk] = M::from_acc(H, kk);
-            st_frag(recB + Ly::B_H + (size_t)(cg * NKD + HH * HKD + kk) * Ly::FR, lane, Hf[kk]);
+            if constexpr (C::SL)
+                st_frag(st + (size_t)kk * 1024, lane, Hf[kk]);
+            else
+                st_frag(recB + Ly::B_H + (size_t)(cg * NKD + HH * HKD + kk) * Ly::FR, lane, Hf[kk]);
         }
         f32x4 P[4];
         if constexpr (DELTA) {
+            const float dec = *reinterpret_cast<const float*>(us + C::UTSUB);
 #pragma unroll
-            for (int rt = 0; rt < 4; ++rt) P[rt] = (rt >> 1) == HH ? ut_f32(ut[rt & 1]) : f32x4{0.f, 0.f, 0.f, 0.f};
+            for (int rt = 0; rt < 4; ++rt) {
+                if ((rt >> 1) == HH) {
+                    const float4 x = load4(ut + ((size_t)rt * 64 + lane) * 4);
+                    P[rt] = f32x4{x.x, x.y, x.z, x.w};
+                } else {
+                    P[rt] = f32x4{0.f, 0.f, 0.f, 0.f};
+                }
+            }
 #pragma unroll
             for (int kk = 0; kk < HKD; ++kk)
 #pragma unroll
@@ -567,8 +633,14 @@ __device__ __forceinline__ void chain_compute(const PrefArgs& a, unsigned char* 
             for (int rt = 0; rt < 4; ++rt) X[(HH * 4 + rt) * 64 + lane] = P[rt];
 #pragma unroll
             for (int t = 0; t < HDT; ++t) H[t] = f32x4{H[t][0] * dec, H[t][1] * dec, H[t][2] * dec, H[t][3] * dec};
+        } else {
+#pragma unroll
+            for (int rt = 0; rt < 4; ++rt) {
+                const float4 x = load4(ut + ((size_t)rt * 64 + lane) * 4);
+                P[rt] = f32x4{x.x, x.y, x.z, x.w};
+            }
         }
-        lds_barrier();   // partial products exchanged; the next chunk's slot is complete
+        lds_barrier();   // partial products exchanged; chunk c + 1's slot is complete
         f32x4 U[4];
 #pragma unroll
         for (int rt = 0; rt < 4; ++rt) {
@@ -576,31 +648,27 @@ __device__ __forceinline__ void chain_compute(const PrefArgs& a, unsigned char* 
                 const f32x4 po = X[((1 - HH) * 4 + rt) * 64 + lane];
                 U[rt] = f32x4{P[rt][0] + po[0], P[rt][1] + po[1], P[rt][2] + po[2], P[rt][3] + po[3]};
             } else {
-                U[rt] = ut_f32(ut[rt]);
+                U[rt] = P[rt];
             }
         }
         frag Uf[NKT];
 #pragma unroll
         for (int kt = 0; kt < NKT; ++kt) {
             Uf[kt] = M::from_acc(U, kt);
-            if (kt % 2 == HH) st_frag(recB + Ly::B_U + (size_t)(cg * NKT + kt) * Ly::FR, lane, Uf[kt]);
+            if (kt % 2 == HH) {
+                if constexpr (C::SL)
+                    st_frag(st + (size_t)(HKD + kt / 2) * 1024, lane, Uf[kt]);
+                else
+                    st_frag(recB + Ly::B_U + (size_t)(cg * NKT + kt) * Ly::FR, lane, Uf[kt]);
+            }
         }
 #pragma unroll
         for (int kt = 0; kt < NKT; ++kt)
 #pragma unroll
             for (int t = 0; t < HDT; ++t) H[t] = M::mma(kf[t * NKT + kt], Uf[kt], H[t]);
         read_slot((c + 1) % NS);
-    };
-    UR ua[NUT], ub[NUT];
-    float da, db;
-    fetch(0, ua, da);
-    wait_vmcnt<0>();   // initial state and chunk 0's operands are in registers
-    lds_barrier();
-    read_slot(0);
-    for (int c = 0; c < nch; c += 2) {
-        step(c, ua, da, ub, db);
-        if (c + 1 < nch) step(c + 1, ub, db, ua, da);
     }
+    lds_barrier();   // the last step's fragments are staged for the loaders
 #pragma unroll
     for (int t = 0; t < HDT; ++t)
 #pragma unroll
@@ -608,30 +676,27 @@ __device__ __forceinline__ void chain_compute(const PrefArgs& a, unsigned char* 
             a.h_final[((size_t)bh * D + 16 * (HH * HDT + t) + 4 * j + e) * D + col] = H[t][e];
 }
 
-// One workgroup per CU (its LDS ring). Waves 0 .. 2 CPW - 1 compute (column group w / 2, row
-// half w % 2), the last two load; the roles run separate loops with the same barrier sequence.
+// One workgroup per CU (its LDS ring). Waves 0 and 1 compute (row half w), waves 2 and 3 load
+// and store; the roles run separate loops with the same barrier sequence.
 template <int D, class E, bool DELTA>
-__global__ __attribute__((amdgpu_flat_work_group_size(1, ChainCfg<D, E>::THREADS))) void chain_kernel(PrefArgs a) {
+__global__ __launch_bounds__(256) void chain_kernel(PrefArgs a) {
     using Ly = Layout<D, E>;
-    using C = ChainCfg<D, E>;
+    using C = ChainCfg<D, E, DELTA>;
     extern __shared__ __align__(16) unsigned char smem[];
-    // blockIdx -> (slice, workgroup column block) so that all workgroups of one slice run on the
-    // same XCD (workgroups are dealt to the 8 XCDs round-robin) and share its L2.
+    // blockIdx -> (slice, column group) so that all column groups of one slice run on the same
+    // XCD (workgroups are dealt to the 8 XCDs round-robin) and share its L2.
     const int xcd = blockIdx.x & 7, sl = blockIdx.x >> 3;
-    const int cgw = sl % C::NCW, bh = (sl / C::NCW) * 8 + xcd;
+    const int cg = sl % C::NCW, bh = (sl / C::NCW) * 8 + xcd;
     if (bh >= a.BH) return;
     const int lane = threadIdx.x & 63;
     const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);   // wave-uniform
     const unsigned char* rec0 = a.ws + (size_t)bh * a.segcap * Ly::REC;
-    if (w >= 2 * C::CPW) {
-        chain_loader<D, E>(smem, rec0, a.nseg, w - 2 * C::CPW, lane);
-    } else {
-        const int cgl = w >> 1, cg = C::CPW * cgw + cgl;
-        if (w & 1)
-            chain_compute<D, E, DELTA, 1>(a, smem, rec0, a.nseg, bh, cg, cgl, lane);
-        else
-            chain_compute<D, E, DELTA, 0>(a, smem, rec0, a.nseg, bh, cg, cgl, lane);
-    }
+    if (w >= 2)
+        chain_loader<D, E, DELTA>(smem, rec0, a.nseg, cg, w - 2, lane);
+    else if (w == 1)
+        chain_compute<D, E, DELTA, 1>(a, smem, rec0, a.nseg, bh, cg, lane);
+    else
+        chain_compute<D, E, DELTA, 0>(a, smem, rec0, a.nseg, bh, cg, lane);
 }
 
 // ---------------------------------------------------------------------------------------------
@@ -800,10 +865,10 @@ template <int D, class E, bool DELTA>
 struct Launch {
     using T = typename E::T;
     using Ly = Layout<D, E>;
-    using CC = ChainCfg<D, E>;
+    using CC = ChainCfg<D, E, DELTA>;
     static constexpr int KP = D + 8;
     static constexpr size_t LDS_PREP = PrepCfg<D, E>::LDS;
-    static constexpr size_t LDS_CHAIN = (size_t)CC::NS * CC::SLOT + CC::XBYTES;
+    static constexpr size_t LDS_CHAIN = CC::LDS;
     static constexpr size_t LDS_OUT = (size_t)4 * Ly::NKT * 1024 + (size_t)2 * CH * KP * sizeof(T) + CH * 4;
 
     // raise the dynamic-LDS limits once per process (every caller sets the same values)
