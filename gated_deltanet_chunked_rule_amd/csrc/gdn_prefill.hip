@@ -70,7 +70,7 @@ size_t prefill_record_bytes(int D, int dtype) {
 // SEG_TARGET bytes each, so that the three stages of consecutive segments overlap and the
 // buffers can stay resident in the 256 MB Infinity Cache between the stage that writes them
 // and the stage that reads them.
-static constexpr size_t SEG_TARGET = (size_t)96 << 20;
+static constexpr size_t SEG_TARGET = (size_t)80 << 20;
 static constexpr int NBUF = 2;
 
 size_t prefill_workspace_bytes(long BH, long L, int D, int dtype) {
@@ -952,7 +952,10 @@ static int launch_prefill_t(PrefArgs a, long nch, size_t ws_bytes, hipStream_t s
         b.segcap = seg;
         b.ws = ws0 + (size_t)(sgi % NBUF) * buf;
         b.h0 = sgi == 0 ? h0 : a.h_final;   // later segments continue from the running state
-        // the buffer is free once the output stage of the segment NBUF back has read it
+        // the buffer is free once the output stage of the segment NBUF back has read it. (Its
+        // halves are used by different stages, but letting prep start once that segment's chain
+        // is done puts three kernels on the memory system at once and slows the chain more than
+        // it saves.)
         if (sgi >= NBUF) ok = ok && hipStreamWaitEvent(cx.sp, cx.ev_out[(sgi - NBUF) % R], 0) == hipSuccess;
         LN::prep(b, cx.sp);
         ok = ok && hipEventRecord(cx.ev_prep[sgi % R], cx.sp) == hipSuccess;
