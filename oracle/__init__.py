@@ -9,6 +9,9 @@ this module only compiles it with gcc on first use and marshals NumPy arrays.
 
     gdn_prefill(q, k, v, beta, log_alpha, h0)  -> (o, h_final)   gated delta rule
     linattn_prefill(q, k, v, h0)               -> (o, h_final)   S_t = S_{t-1} + v_t k_t^T
+    gla_prefill(q, k, v, log_alpha, h0)        -> (o, h_final)   S_t = a_t S_{t-1} + v_t k_t^T
+    gdn_prefill_skip(q, k, v, beta, log_alpha, keep, h0, chunk)  gated delta rule, skipped chunks
+                                                                 only decay the carried state
     gdn_decode_step(q, k, v, beta, log_alpha, state) -> (o, new_state)
 
 Shapes: q,k [B,H,L,Dk]; v [B,H,L,Dv]; beta, log_alpha [B,H,L]; h0/h_final [B,H,Dk,Dv]
@@ -54,7 +57,11 @@ def _load():
             lib.oracle_gdn_prefill.argtypes = [P, P, P, P, P, P, P, P, i, i, i, i, i, i]
             lib.oracle_linattn_prefill.argtypes = [P, P, P, P, P, P, i, i, i, i, i, i]
             lib.oracle_gdn_decode_step.argtypes = [P, P, P, P, P, P, P, i, i, i, i, i]
-            for f in (lib.oracle_gdn_prefill, lib.oracle_linattn_prefill, lib.oracle_gdn_decode_step):
+            lib.oracle_gla_prefill.argtypes = [P, P, P, P, P, P, P, i, i, i, i, i, i]
+            IP = ctypes.POINTER(ctypes.c_int)
+            lib.oracle_gdn_prefill_skip.argtypes = [P, P, P, P, P, P, IP, i, P, P, i, i, i, i, i, i]
+            for f in (lib.oracle_gdn_prefill, lib.oracle_linattn_prefill, lib.oracle_gdn_decode_step,
+                      lib.oracle_gla_prefill, lib.oracle_gdn_prefill_skip):
                 f.restype = ctypes.c_int
             _lib = lib
     return _lib
@@ -106,6 +113,45 @@ def linattn_prefill(q, k, v, h0=None, nthreads: int = 0):
     hf = np.empty((B, H, Dk, Dv))
     last_threads = _load().oracle_linattn_prefill(_ptr(q), _ptr(k), _ptr(v), _ptr(h0), _ptr(o), _ptr(hf),
                                                   B, H, L, Dk, Dv, nthreads)
+    return o, hf
+
+
+def gla_prefill(q, k, v, log_alpha, h0=None, nthreads: int = 0):
+    """Decay-only gated linear attention: S_t = exp(log_alpha_t) S_{t-1} + v_t k_t^T, o_t = S_t q_t."""
+    global last_threads
+    q, k, v = (_as4(_f64(t), 4) for t in (q, k, v))
+    log_alpha = _as4(_f64(log_alpha), 3)
+    B, H, L, Dk = q.shape
+    Dv = v.shape[-1]
+    assert k.shape == q.shape and v.shape[:3] == (B, H, L) and log_alpha.shape == (B, H, L)
+    if h0 is not None:
+        h0 = _as4(_f64(h0), 4)
+        assert h0.shape == (B, H, Dk, Dv)
+    o = np.empty((B, H, L, Dv))
+    hf = np.empty((B, H, Dk, Dv))
+    last_threads = _load().oracle_gla_prefill(_ptr(q), _ptr(k), _ptr(v), _ptr(log_alpha), _ptr(h0), _ptr(o),
+                                              _ptr(hf), B, H, L, Dk, Dv, nthreads)
+    return o, hf
+
+
+def gdn_prefill_skip(q, k, v, beta, log_alpha, keep, h0=None, chunk: int = 64, nthreads: int = 0):
+    """Gated delta rule with skipped chunk updates; keep [B,H,ceil(L/chunk)] (nonzero = keep)."""
+    global last_threads
+    q, k, v = (_as4(_f64(t), 4) for t in (q, k, v))
+    beta, log_alpha = (_as4(_f64(t), 3) for t in (beta, log_alpha))
+    B, H, L, Dk = q.shape
+    Dv = v.shape[-1]
+    nch = (L + chunk - 1) // chunk
+    keep = np.ascontiguousarray(_as4(np.asarray(keep), 3), dtype=np.int32)
+    assert keep.shape == (B, H, nch)
+    if h0 is not None:
+        h0 = _as4(_f64(h0), 4)
+        assert h0.shape == (B, H, Dk, Dv)
+    o = np.empty((B, H, L, Dv))
+    hf = np.empty((B, H, Dk, Dv))
+    last_threads = _load().oracle_gdn_prefill_skip(
+        _ptr(q), _ptr(k), _ptr(v), _ptr(beta), _ptr(log_alpha), _ptr(h0),
+        keep.ctypes.data_as(ctypes.POINTER(ctypes.c_int)), chunk, _ptr(o), _ptr(hf), B, H, L, Dk, Dv, nthreads)
     return o, hf
 
 

@@ -21,6 +21,18 @@
  *   The output uses the state that already contains token t (inclusive causality) and no
  *   softmax scale or normaliser is applied.
  *
+ *   Decay-only gated linear attention (linear attention with a per-token decay, one of the
+ *   modifications the forpes.ru article on linear attention lists after the recurrent form):
+ *       S_t = a_t S_{t-1} + v_t k_t^T,   o_t = S_t q_t,   a_t = exp(log_alpha_t).
+ *
+ *   Gated delta rule with skipped chunk updates (the SparseGDN article, fileenergy.com: the
+ *   selector's skipped events, and its scan_with_skips illustration in the section on embedding
+ *   the selector into an FLA pipeline). Tokens are grouped into chunks of C; at the start of
+ *   chunk c the state S_c is the chunk's snapshot. Every token's output is the gated delta rule
+ *   run token by token from the snapshot through the chunk (outputs exist for every token,
+ *   skipped chunk or not). The state carried to the next chunk is the result of that run when
+ *   keep[c] != 0, and otherwise the snapshot only decayed: exp(sum of the chunk's log_alpha) S_c.
+ *
  *   Decode step: the gated delta-rule update above applied once to a stored state.
  *
  * Storage orientation. Initial, final and decode states are stored key-major: element
@@ -96,6 +108,16 @@ static void gdn_token(double *S, double *sk, const double *k, const double *v,
     }
 }
 
+/* One decay-only gated linear-attention token: S <- a S + v k^T. */
+static void gla_token(double *S, const double *k, const double *v, double log_alpha, int Dk, int Dv)
+{
+    const double a = exp(log_alpha);
+    for (int j = 0; j < Dv; ++j) {
+        double *row = S + (size_t)j * Dk;
+        for (int i = 0; i < Dk; ++i) row[i] = a * row[i] + v[j] * k[i];
+    }
+}
+
 /* One plain linear-attention token: S <- S + v k^T. */
 static void la_token(double *S, const double *k, const double *v, int Dk, int Dv)
 {
@@ -142,6 +164,64 @@ int oracle_linattn_prefill(const double *q, const double *k, const double *v, co
             const size_t tok = (size_t)s * L + t;
             la_token(S, k + tok * Dk, v + tok * Dv, Dk, Dv);
             read_out(o + tok * Dv, S, q + tok * Dk, Dk, Dv);
+        }
+        store_state(h_final + (size_t)s * Dk * Dv, S, Dk, Dv);
+        free(S);
+    }
+    return used;
+}
+
+/* Decay-only gated linear attention: as oracle_linattn_prefill, with log_alpha [B,H,L]. */
+int oracle_gla_prefill(const double *q, const double *k, const double *v, const double *log_alpha,
+                       const double *h0, double *o, double *h_final,
+                       int B, int H, int L, int Dk, int Dv, int nthreads)
+{
+    const int used = set_threads(nthreads);
+    const long nslice = (long)B * H;
+#pragma omp parallel for schedule(dynamic, 1)
+    for (long s = 0; s < nslice; ++s) {
+        double *S = (double *)malloc(sizeof(double) * (size_t)Dk * Dv);
+        load_state(S, h0 ? h0 + (size_t)s * Dk * Dv : NULL, Dk, Dv);
+        for (int t = 0; t < L; ++t) {
+            const size_t tok = (size_t)s * L + t;
+            gla_token(S, k + tok * Dk, v + tok * Dv, log_alpha[tok], Dk, Dv);
+            read_out(o + tok * Dv, S, q + tok * Dk, Dk, Dv);
+        }
+        store_state(h_final + (size_t)s * Dk * Dv, S, Dk, Dv);
+        free(S);
+    }
+    return used;
+}
+
+/* Gated delta rule with skipped chunk updates. keep [B,H,ceil(L/C)] (nonzero = keep); the rest as
+ * oracle_gdn_prefill. */
+int oracle_gdn_prefill_skip(const double *q, const double *k, const double *v,
+                            const double *beta, const double *log_alpha, const double *h0,
+                            const int *keep, int C, double *o, double *h_final,
+                            int B, int H, int L, int Dk, int Dv, int nthreads)
+{
+    const int used = set_threads(nthreads);
+    const long nslice = (long)B * H;
+    const int nch = (L + C - 1) / C;
+#pragma omp parallel for schedule(dynamic, 1)
+    for (long s = 0; s < nslice; ++s) {
+        double *S = (double *)malloc(sizeof(double) * ((size_t)2 * Dk * Dv + Dv));
+        double *snap = S + (size_t)Dk * Dv;
+        double *sk = snap + (size_t)Dk * Dv;
+        load_state(S, h0 ? h0 + (size_t)s * Dk * Dv : NULL, Dk, Dv);
+        for (int c = 0; c < nch; ++c) {
+            memcpy(snap, S, sizeof(double) * (size_t)Dk * Dv);
+            double gsum = 0.0;
+            for (int t = c * C; t < L && t < (c + 1) * C; ++t) {
+                const size_t tok = (size_t)s * L + t;
+                gdn_token(S, sk, k + tok * Dk, v + tok * Dv, beta[tok], log_alpha[tok], Dk, Dv);
+                read_out(o + tok * Dv, S, q + tok * Dk, Dk, Dv);
+                gsum += log_alpha[tok];
+            }
+            if (!keep[(size_t)s * nch + c]) {
+                const double d = exp(gsum);
+                for (size_t e = 0; e < (size_t)Dk * Dv; ++e) S[e] = d * snap[e];
+            }
         }
         store_state(h_final + (size_t)s * Dk * Dv, S, Dk, Dv);
         free(S);
