@@ -52,14 +52,15 @@ int check_dims(long B, long H, long L, int Dk, int Dv, int dtype) {
 }
 
 int validate_prefill(const void* q, const void* k, const void* v, const float* beta, const float* log_alpha,
-                     const float* h0, void* o, float* h_final, int B, int H, int L, int Dk, int Dv, int dtype,
-                     void* workspace, size_t workspace_bytes, bool delta) {
+                     const unsigned char* keep, bool skip, const float* h0, void* o, float* h_final, int B, int H,
+                     int L, int Dk, int Dv, int dtype, void* workspace, size_t workspace_bytes, bool delta) {
     int st = check_dims(B, H, L, Dk, Dv, dtype);
     if (st != GDN_OK) return st;
     if (!h_final) return GDN_ERR_NULL;
     if (L > 0 && (!q || !k || !v || !o)) return GDN_ERR_NULL;   // L = 0 reads no token data
     if (delta && L > 0 && (!beta || !log_alpha)) return GDN_ERR_NULL;
-    if (!delta && (beta || log_alpha)) return GDN_ERR_NULL;
+    if (!delta && beta) return GDN_ERR_NULL;        // log_alpha is optional without the delta term
+    if (skip && L > 0 && !keep) return GDN_ERR_NULL;
     const void* ptrs[] = {q, k, v, beta, log_alpha, h0, o, h_final};
     for (const void* p : ptrs)
         if (p && !aligned(p, 16)) return GDN_ERR_ALIGN;
@@ -71,14 +72,15 @@ int validate_prefill(const void* q, const void* k, const void* v, const float* b
         if (!workspace || workspace_bytes < need) return GDN_ERR_WORKSPACE;
         if (!aligned(workspace, 256)) return GDN_ERR_ALIGN;
     }
+    const size_t nchk = ((size_t)L + 63) / 64;
     const Range in[] = {rng(q, tok * Dk * esz), rng(k, tok * Dk * esz), rng(v, tok * Dv * esz),
                         rng(beta, beta ? tok * 4 : 0), rng(log_alpha, log_alpha ? tok * 4 : 0),
-                        rng(h0, h0 ? BH * Dk * Dv * 4 : 0)};
+                        rng(keep, keep ? BH * nchk : 0), rng(h0, h0 ? BH * Dk * Dv * 4 : 0)};
     const Range ro = rng(o, tok * Dv * esz), rh = rng(h_final, BH * Dk * Dv * 4);
     const Range rw = rng(workspace, workspace && need ? workspace_bytes : 0);
-    for (int i = 0; i < 6; ++i) {
+    for (int i = 0; i < 7; ++i) {
         if (overlap(ro, in[i]) || overlap(rw, in[i])) return GDN_ERR_ALIAS;
-        if (i == 5 && h0 == h_final) continue;  // in-place state update is allowed
+        if (i == 6 && h0 == h_final) continue;  // in-place state update is allowed
         if (overlap(rh, in[i])) return GDN_ERR_ALIAS;
     }
     if (overlap(ro, rh) || overlap(ro, rw) || overlap(rh, rw)) return GDN_ERR_ALIAS;
@@ -86,15 +88,15 @@ int validate_prefill(const void* q, const void* k, const void* v, const float* b
 }
 
 int prefill(const void* q, const void* k, const void* v, const float* beta, const float* log_alpha,
-            const float* h0, void* o, float* h_final, int B, int H, int L, int Dk, int Dv, int dtype,
-            void* workspace, size_t workspace_bytes, void* stream, bool delta) {
-    int st = validate_prefill(q, k, v, beta, log_alpha, h0, o, h_final, B, H, L, Dk, Dv, dtype, workspace,
-                              workspace_bytes, delta);
+            const unsigned char* keep, bool skip, const float* h0, void* o, float* h_final, int B, int H, int L,
+            int Dk, int Dv, int dtype, void* workspace, size_t workspace_bytes, void* stream, bool delta) {
+    int st = validate_prefill(q, k, v, beta, log_alpha, keep, skip, h0, o, h_final, B, H, L, Dk, Dv, dtype,
+                              workspace, workspace_bytes, delta);
     if (st != GDN_OK) return st;
     st = check_device();
     if (st != GDN_OK) return st;
-    return gdn::launch_prefill(q, k, v, beta, log_alpha, h0, o, h_final, B * H, L, Dk, dtype, delta, workspace,
-                               workspace_bytes, static_cast<hipStream_t>(stream)) == 0
+    return gdn::launch_prefill(q, k, v, beta, log_alpha, keep, h0, o, h_final, B * H, L, Dk, dtype, delta,
+                               workspace, workspace_bytes, static_cast<hipStream_t>(stream)) == 0
                ? GDN_OK
                : GDN_ERR_LAUNCH;
 }
@@ -126,15 +128,22 @@ size_t gdn_prefill_workspace_size(int B, int H, int L, int Dk, int Dv, int dtype
 int gdn_prefill_fwd(const void* q, const void* k, const void* v, const float* beta, const float* log_alpha,
                     const float* h0, void* o, float* h_final, int B, int H, int L, int Dk, int Dv, int dtype,
                     void* workspace, size_t workspace_bytes, void* stream) {
-    return prefill(q, k, v, beta, log_alpha, h0, o, h_final, B, H, L, Dk, Dv, dtype, workspace, workspace_bytes,
-                   stream, true);
+    return prefill(q, k, v, beta, log_alpha, nullptr, false, h0, o, h_final, B, H, L, Dk, Dv, dtype, workspace,
+                   workspace_bytes, stream, true);
+}
+
+int gdn_prefill_skip_fwd(const void* q, const void* k, const void* v, const float* beta, const float* log_alpha,
+                         const unsigned char* keep, const float* h0, void* o, float* h_final, int B, int H, int L,
+                         int Dk, int Dv, int dtype, void* workspace, size_t workspace_bytes, void* stream) {
+    return prefill(q, k, v, beta, log_alpha, keep, true, h0, o, h_final, B, H, L, Dk, Dv, dtype, workspace,
+                   workspace_bytes, stream, true);
 }
 
 int linattn_prefill_fwd(const void* q, const void* k, const void* v, const float* beta, const float* log_alpha,
                         const float* h0, void* o, float* h_final, int B, int H, int L, int Dk, int Dv, int dtype,
                         void* workspace, size_t workspace_bytes, void* stream) {
-    return prefill(q, k, v, beta, log_alpha, h0, o, h_final, B, H, L, Dk, Dv, dtype, workspace, workspace_bytes,
-                   stream, false);
+    return prefill(q, k, v, beta, log_alpha, nullptr, false, h0, o, h_final, B, H, L, Dk, Dv, dtype, workspace,
+                   workspace_bytes, stream, false);
 }
 
 int gdn_decode_step(const void* q, const void* k, const void* v, const float* beta, const float* log_alpha,

@@ -11,8 +11,9 @@ int launch_decode(const void* q, const void* k, const void* v, const float* beta
 size_t prefill_workspace_bytes(long BH, long L, int D, int dtype);      // preferred
 size_t prefill_workspace_min_bytes(long BH, long L, int D, int dtype);  // smallest accepted
 
+// keep: [BH][ceil(L/64)] chunk keep mask (nonzero = apply the chunk's state update), or NULL (all)
 int launch_prefill(const void* q, const void* k, const void* v, const float* beta, const float* log_alpha,
-                   const float* h0, void* o, float* h_final, int BH, long L, int D, int dtype, bool delta,
-                   void* ws, size_t ws_bytes, hipStream_t stream);
+                   const unsigned char* keep, const float* h0, void* o, float* h_final, int BH, long L, int D,
+                   int dtype, bool delta, void* ws, size_t ws_bytes, hipStream_t stream);
 
 }  // namespace gdn

@@ -51,7 +51,8 @@ struct Layout {
     static constexpr size_t A_KH = A_W + (size_t)4 * NKD * FR;
     static constexpr size_t A_UT = A_KH + (size_t)NDT * NKT * FR;
     static constexpr size_t A_DEC = A_UT + (size_t)NDT * 4 * 64 * 4 * sizeof(typename E::T);
-    static constexpr size_t REC_A = (A_DEC + 4 + 255) / 256 * 256;
+    static constexpr size_t A_KEEP = A_DEC + 4;   // chunk keep flag (u32, 0 = skipped state update)
+    static constexpr size_t REC_A = (A_KEEP + 4 + 255) / 256 * 256;
     // chain record: chunk-start state [cg NDT][NKD], U [cg NDT][NKT]
     static constexpr size_t B_H = 0;
     static constexpr size_t B_U = (size_t)NDT * NKD * FR;
@@ -105,6 +106,8 @@ struct PrefArgs {
     int c0;              // first chunk of the segment
     int nseg;            // chunks in the segment
     int segcap;          // records per slice in the buffer
+    const unsigned char* keep;   // [BH][nchk] chunk keep mask, or NULL (keep all)
+    int nchk;                    // chunks per slice of the whole sequence
 };
 
 // inclusive prefix sum over the 64 lanes of a wave
@@ -194,9 +197,9 @@ __global__ __launch_bounds__(256) void prep_kernel(PrefArgs a) {
 
     if (w == 0) {
         float la = 0.f, bt = 0.f;
-        if (DELTA && lane < n) {
-            la = a.log_alpha[tok0 + lane];
-            bt = a.beta[tok0 + lane];
+        if (lane < n) {
+            if (a.log_alpha) la = a.log_alpha[tok0 + lane];   // optional without the delta term
+            if (DELTA) bt = a.beta[tok0 + lane];
         }
         const float g = wave_scan(la, lane);
         const float gC = __shfl(g, 63);
@@ -204,7 +207,11 @@ __global__ __launch_bounds__(256) void prep_kernel(PrefArgs a) {
         sb[lane] = bt;
         sbe[lane] = -bt * __expf(g);
         skh[lane] = __expf(gC - g);
-        if (lane == 0) *reinterpret_cast<float*>(rec + Ly::A_DEC) = DELTA ? __expf(gC) : 1.f;
+        if (lane == 0) {
+            *reinterpret_cast<float*>(rec + Ly::A_DEC) = a.log_alpha ? __expf(gC) : 1.f;
+            *reinterpret_cast<unsigned*>(rec + Ly::A_KEEP) =
+                a.keep ? (a.keep[(size_t)bh * a.nchk + a.c0 + cl] != 0 ? 1u : 0u) : 1u;
+        }
     }
     {   // K and V rows, 16 bytes per lane; rows past the chunk's end are zero (identity steps)
         constexpr int EPU = 16 / sizeof(T), UPR = D / EPU;
@@ -240,14 +247,15 @@ __global__ __launch_bounds__(256) void prep_kernel(PrefArgs a) {
     }
 
     if constexpr (!DELTA) {
-        // plain linear attention: Khat = K, Ut = V
+        // linear attention without the delta term: Khat = e^{g_C - g} K (K without gates), Ut = V
 #pragma unroll
         for (int i = 0; i < DPW; ++i) {
             const int dt = FPD * grp + i;
 #pragma unroll
             for (int kt = 0; kt < NKT; ++kt)
                 if (kt % WPG == w % WPG)
-                    st_frag(rec + Ly::A_KH + (size_t)(dt * NKT + kt) * Ly::FR, lane, cols_frag<E>(&kc[i][FPD * kt]));
+                    st_frag(rec + Ly::A_KH + (size_t)(dt * NKT + kt) * Ly::FR, lane,
+                            a.log_alpha ? cols_frag<E>(&kc[i][FPD * kt], skh + KB * kt, j) : cols_frag<E>(&kc[i][FPD * kt]));
 #pragma unroll
             for (int r = 0; r < RPW; ++r) {
                 const int rt = rt0 + r;
@@ -491,7 +499,7 @@ __device__ __forceinline__ void chain_issue(unsigned char* smem, const unsigned 
         const unsigned blk = (unsigned)(lw * C::UTL + i) * 1024u;
         dma16(ut + blk + lane * 16, ubase + blk);
     }
-    dma4(rec + Ly::A_DEC, ubase + (unsigned)C::UTSUB);
+    dma4(rec + Ly::A_DEC + 4 * (lane & 1), ubase + (unsigned)C::UTSUB);   // decay, keep flag, decay, ...
 }
 
 // Loader wave lw's stores of step c's staged fragments (those of compute wave lw): its rows of
@@ -614,8 +622,9 @@ __device__ __forceinline__ void chain_compute(const PrefArgs& a, unsigned char* 
                 st_frag(recB + Ly::B_H + (size_t)(cg * NKD + HH * HKD + kk) * Ly::FR, lane, Hf[kk]);
         }
         f32x4 P[4];
+        const float dec = *reinterpret_cast<const float*>(us + C::UTSUB);
+        const unsigned keep = __builtin_amdgcn_readfirstlane(*reinterpret_cast<const unsigned*>(us + C::UTSUB + 4));
         if constexpr (DELTA) {
-            const float dec = *reinterpret_cast<const float*>(us + C::UTSUB);
 #pragma unroll
             for (int rt = 0; rt < 4; ++rt) {
                 if ((rt >> 1) == HH) {
@@ -639,6 +648,8 @@ __device__ __forceinline__ void chain_compute(const PrefArgs& a, unsigned char* 
                 const float4 x = load4(ut + ((size_t)rt * 64 + lane) * 4);
                 P[rt] = f32x4{x.x, x.y, x.z, x.w};
             }
+#pragma unroll
+            for (int t = 0; t < HDT; ++t) H[t] = f32x4{H[t][0] * dec, H[t][1] * dec, H[t][2] * dec, H[t][3] * dec};
         }
         lds_barrier();   // partial products exchanged; chunk c + 1's slot is complete
         f32x4 U[4];
@@ -662,10 +673,12 @@ __device__ __forceinline__ void chain_compute(const PrefArgs& a, unsigned char* 
                     st_frag(recB + Ly::B_U + (size_t)(cg * NKT + kt) * Ly::FR, lane, Uf[kt]);
             }
         }
+        if (keep) {   // a skipped chunk's update leaves the decayed state (its U still feeds its outputs)
 #pragma unroll
-        for (int kt = 0; kt < NKT; ++kt)
+            for (int kt = 0; kt < NKT; ++kt)
 #pragma unroll
-            for (int t = 0; t < HDT; ++t) H[t] = M::mma(kf[t * NKT + kt], Uf[kt], H[t]);
+                for (int t = 0; t < HDT; ++t) H[t] = M::mma(kf[t * NKT + kt], Uf[kt], H[t]);
+        }
         read_slot((c + 1) % NS);
     }
     lds_barrier();   // the last step's fragments are staged for the loaders
@@ -781,7 +794,7 @@ __global__ __launch_bounds__(256) void output_kernel(PrefArgs a) {
     }
     if (w == 0) {
         float la = 0.f;
-        if (DELTA && lane < n) la = a.log_alpha[tok0 + lane];
+        if (a.log_alpha && lane < n) la = a.log_alpha[tok0 + lane];
         sg[lane] = wave_scan(la, lane);
     }
     __syncthreads();
@@ -972,8 +985,8 @@ static int launch_prefill_t(PrefArgs a, long nch, size_t ws_bytes, hipStream_t s
 }
 
 int launch_prefill(const void* q, const void* k, const void* v, const float* beta, const float* log_alpha,
-                   const float* h0, void* o, float* h_final, int BH, long L, int D, int dtype, bool delta,
-                   void* ws, size_t ws_bytes, hipStream_t stream) {
+                   const unsigned char* keep, const float* h0, void* o, float* h_final, int BH, long L, int D,
+                   int dtype, bool delta, void* ws, size_t ws_bytes, hipStream_t stream) {
     if (L == 0) {
         const size_t n = (size_t)BH * D * D;
         if (h0 == h_final) return 0;
@@ -981,7 +994,7 @@ int launch_prefill(const void* q, const void* k, const void* v, const float* bet
         return hipGetLastError() == hipSuccess ? 0 : -1;
     }
     const long nch = (L + CH - 1) / CH;
-    PrefArgs a{q, k, v, beta, log_alpha, h0, o, h_final, static_cast<unsigned char*>(ws), L, BH, 0, 0, 0};
+    PrefArgs a{q, k, v, beta, log_alpha, h0, o, h_final, static_cast<unsigned char*>(ws), L, BH, 0, 0, 0, keep, (int)nch};
 #define GDN_PF(DD, EE)                                                                 \
     return delta ? launch_prefill_t<DD, EE, true>(a, nch, ws_bytes, stream)            \
                  : launch_prefill_t<DD, EE, false>(a, nch, ws_bytes, stream)

@@ -53,7 +53,7 @@ def prefill_workspace_size(B: int, H: int, L: int, D: int, dtype: torch.dtype) -
     return int(_lib.load().gdn_prefill_workspace_size(B, H, L, D, D, _code(dtype)))
 
 
-def _prefill(entry, q, k, v, beta, log_alpha, h0, o, h_final, workspace, stream, delta):
+def _prefill(entry, q, k, v, beta, log_alpha, h0, o, h_final, workspace, stream, delta, keep=None):
     B, H, L, D = q.shape
     dev, dt = q.device, q.dtype
     _req("q", q, (B, H, L, D), dt, dev)
@@ -61,7 +61,10 @@ def _prefill(entry, q, k, v, beta, log_alpha, h0, o, h_final, workspace, stream,
     _req("v", v, (B, H, L, D), dt, dev)
     if delta:
         _req("beta", beta, (B, H, L), torch.float32, dev)
+    if delta or log_alpha is not None:
         _req("log_alpha", log_alpha, (B, H, L), torch.float32, dev)
+    if entry == "gdn_prefill_skip_fwd":
+        _req("keep", keep, (B, H, (L + 63) // 64), torch.uint8, dev)
     if h0 is not None:
         _req("h0", h0, (B, H, D, D), torch.float32, dev)
     o = torch.empty_like(v) if o is None else _req("o", o, (B, H, L, D), dt, dev)
@@ -73,7 +76,10 @@ def _prefill(entry, q, k, v, beta, log_alpha, h0, o, h_final, workspace, stream,
     elif not workspace.is_cuda or not workspace.is_contiguous():
         raise ValueError("workspace must be a contiguous device tensor")
     lib = _lib.load()
-    rc = getattr(lib, entry)(_p(q), _p(k), _p(v), _p(beta), _p(log_alpha), _p(h0), _p(o), _p(h_final),
+    gates = (_p(q), _p(k), _p(v), _p(beta), _p(log_alpha))
+    if entry == "gdn_prefill_skip_fwd":
+        gates = gates + (_p(keep),)
+    rc = getattr(lib, entry)(*gates, _p(h0), _p(o), _p(h_final),
                              B, H, L, D, D, _code(dt), _p(workspace),
                              workspace.numel() * workspace.element_size(), _stream(dev, stream))
     _lib.check(rc, entry)
@@ -88,11 +94,23 @@ def gdn_prefill_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, beta: tor
     return _prefill("gdn_prefill_fwd", q, k, v, beta, log_alpha, h0, o, h_final, workspace, stream, True)
 
 
+def gdn_prefill_skip_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, beta: torch.Tensor,
+                         log_alpha: torch.Tensor, keep: torch.Tensor, h0: Optional[torch.Tensor] = None, *,
+                         o: Optional[torch.Tensor] = None, h_final: Optional[torch.Tensor] = None,
+                         workspace: Optional[torch.Tensor] = None, stream=None) -> Tuple[torch.Tensor, torch.Tensor]:
+    """Gated delta rule whose chunks (64 tokens) with keep == 0 only decay the carried state; every
+    token still gets its output. keep: uint8 [B,H,ceil(L/64)]. Returns (o, h_final)."""
+    return _prefill("gdn_prefill_skip_fwd", q, k, v, beta, log_alpha, h0, o, h_final, workspace, stream, True,
+                    keep=keep)
+
+
 def linattn_prefill_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, h0: Optional[torch.Tensor] = None, *,
-                        o: Optional[torch.Tensor] = None, h_final: Optional[torch.Tensor] = None,
-                        workspace: Optional[torch.Tensor] = None, stream=None) -> Tuple[torch.Tensor, torch.Tensor]:
-    """Chunked plain causal linear attention (S_t = S_{t-1} + v_t k_t^T). Returns (o, h_final)."""
-    return _prefill("linattn_prefill_fwd", q, k, v, None, None, h0, o, h_final, workspace, stream, False)
+                        log_alpha: Optional[torch.Tensor] = None, o: Optional[torch.Tensor] = None,
+                        h_final: Optional[torch.Tensor] = None, workspace: Optional[torch.Tensor] = None,
+                        stream=None) -> Tuple[torch.Tensor, torch.Tensor]:
+    """Chunked causal linear attention S_t = a_t S_{t-1} + v_t k_t^T (a_t = exp(log_alpha), 1 when
+    log_alpha is None). Returns (o, h_final)."""
+    return _prefill("linattn_prefill_fwd", q, k, v, None, log_alpha, h0, o, h_final, workspace, stream, False)
 
 
 def gdn_decode_step(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, beta: torch.Tensor,

@@ -60,7 +60,8 @@ enum {
 /* Human-readable name of a status code (static string, never NULL). */
 const char *gdn_status_string(int status);
 
-/* Preferred bytes of device workspace for gdn_prefill_fwd / linattn_prefill_fwd at this shape.
+/* Preferred bytes of device workspace for gdn_prefill_fwd, gdn_prefill_skip_fwd and
+ * linattn_prefill_fwd at this shape.
  * The workspace holds the per-chunk operands handed between the three prefill stages. A short
  * sequence is processed in one segment; a long one in segments whose stages overlap on two
  * internal streams, with two segment buffers of about 80 MB each. Any workspace of at least
@@ -91,9 +92,33 @@ int gdn_prefill_fwd(const void *q, const void *k, const void *v,
                     void *workspace, size_t workspace_bytes, void *stream);
 
 /*
- * Chunked prefill of plain causal linear attention (a = 1, no delta term):
- *   O_chunk = Q H0 + (Q K^T masked causally, diagonal included) V,   H <- H0 + K^T V.
- * Same argument list as gdn_prefill_fwd; beta and log_alpha must both be NULL.
+ * The gated delta rule with skipped chunk updates (SparseGDN article, fileenergy.com: events the
+ * selector drops only decay the state; outputs exist for every token, taken from chunk-start
+ * snapshots; its scan_with_skips illustration). Tokens form chunks of 64 (the last one
+ * ragged); for chunk c of slice (b, h):
+ *   outputs: the gated delta rule run token by token from the chunk-start state;
+ *   next chunk-start state: that run's final state if keep[(b*H + h)*ceil(L/64) + c] != 0,
+ *                           else the chunk-start state times exp(sum of the chunk's log_alpha).
+ *   keep        [B,H,ceil(L/64)] uint8 device array (any alignment; read, never written); NULL
+ *               only when L = 0. A head-pair selector is expressed by repeating its mask.
+ * All other arguments, the workspace and the stream behaviour as gdn_prefill_fwd. With every
+ * keep byte nonzero the result equals gdn_prefill_fwd's bit for bit.
+ */
+int gdn_prefill_skip_fwd(const void *q, const void *k, const void *v,
+                         const float *beta, const float *log_alpha, const unsigned char *keep,
+                         const float *h0, void *o, float *h_final,
+                         int B, int H, int L, int Dk, int Dv, int dtype,
+                         void *workspace, size_t workspace_bytes, void *stream);
+
+/*
+ * Chunked prefill of causal linear attention without the delta term (the forpes.ru article on
+ * linear attention, its recurrent form and the decay modifications listed after it):
+ *   S_t = a_t S_{t-1} + v_t k_t^T,   o_t = S_t q_t,   a_t = exp(log_alpha_t),
+ * i.e. per chunk  O = diag(e^g) Q H0 + (Q K^T masked causally, diagonal included, times
+ * e^{g_r - g_s}) V  and  H <- e^{g_C} H0 + (e^{g_C - g} K)^T V  with g the in-chunk prefix
+ * sum of log_alpha. log_alpha NULL means a = 1 (plain linear attention, AI RnD Day channel
+ * post, tgstat.ru, section "Linear attention"). Same argument list as gdn_prefill_fwd; beta
+ * must be NULL.
  */
 int linattn_prefill_fwd(const void *q, const void *k, const void *v,
                         const float *beta, const float *log_alpha, const float *h0,

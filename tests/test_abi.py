@@ -63,7 +63,8 @@ def _prefill(lib, q=0x10000, k=0x20000000, v=0x40000000, beta=0x60000000, la=0x6
 def test_prefill_host_validation(lib):
     assert _prefill(lib, q=None) == NULL
     assert _prefill(lib, beta=None) == NULL
-    assert _prefill(lib, gdn=False) == NULL            # linear attention takes no gates
+    assert _prefill(lib, gdn=False) == NULL            # linear attention takes no beta
+    assert _prefill(lib, gdn=False, beta=None) not in (NULL, SHAPE, DTYPE, ALIGN, WORKSPACE, ALIAS)  # gates optional
     assert _prefill(lib, D=96) == SHAPE
     assert _prefill(lib, L=-1) == SHAPE
     assert _prefill(lib, B=0) == SHAPE
@@ -75,6 +76,22 @@ def test_prefill_host_validation(lib):
     assert _prefill(lib, o=0x20000000) == ALIAS        # o == k
     assert _prefill(lib, hf=0x40000000 + 4096) == ALIAS  # h_final inside v
     assert _prefill(lib, h0=0x7f000000 + 16) == ALIAS  # partial h0 / h_final overlap
+
+
+def _prefill_skip(lib, keep=0x60200000, o=0x70000000, **kw):
+    a = dict(q=0x10000, k=0x20000000, v=0x40000000, beta=0x60000000, la=0x60100000, h0=None, hf=0x7f000000,
+             L=200, ws=0x100000000, wsb=1 << 30)
+    a.update(kw)
+    return lib.gdn_prefill_skip_fwd(a["q"], a["k"], a["v"], a["beta"], a["la"], keep, a["h0"], o, a["hf"], 1, 2,
+                                    a["L"], 128, 128, 0, a["ws"], a["wsb"], None)
+
+
+def test_prefill_skip_host_validation(lib):
+    assert _prefill_skip(lib, keep=None) == NULL                 # the keep mask is required
+    assert _prefill_skip(lib, keep=None, L=0) != NULL            # ... unless there are no tokens
+    assert _prefill_skip(lib, beta=None) == NULL
+    assert _prefill_skip(lib, keep=0x70000000 + 8) == ALIAS      # mask inside o
+    assert _prefill_skip(lib, keep=0x60200003) not in (NULL, ALIGN, ALIAS)   # any alignment
 
 
 def test_decode_host_validation(lib):

@@ -1,0 +1,157 @@
+"""GPU parity of the two variants of the prefill, through the C ABI, against the fp64 oracle:
+
+- linear attention with a per-token decay (linattn_prefill_fwd with log_alpha):
+  S_t = a_t S_{t-1} + v_t k_t^T;
+- the gated delta rule with skipped chunk updates (gdn_prefill_skip_fwd): a chunk whose keep
+  byte is 0 only decays the carried state; every token still gets its output.
+
+Same error metric and bounds as test_gpu_parity.py. Keep masks are drawn from a seeded NumPy
+generator; the pages' average retention (about 29 percent of the events) is one of the rates.
+"""
+import numpy as np
+import pytest
+
+import oracle
+from gated_deltanet_chunked_rule_amd import inputs
+from gpu_util import TOL_BF16, TOL_F32, dev_tensor, host, max_rel_err, say
+
+torch = pytest.importorskip("torch")
+pytestmark = pytest.mark.gpu
+
+if not torch.cuda.is_available():  # collected on CPU-only hosts, skipped there
+    pytest.skip("needs a GPU", allow_module_level=True)
+
+from gated_deltanet_chunked_rule_amd import ops  # noqa: E402
+
+TD = {"bf16": torch.bfloat16, "f32": torch.float32}
+
+
+def _dev(cfg, x):
+    dt = TD[cfg.dtype]
+    q, k, v = (dev_tensor(x[n], dt) for n in ("q", "k", "v"))
+    beta = dev_tensor(x["beta"], torch.float32)
+    la = dev_tensor(x["log_alpha"], torch.float32)
+    h0 = dev_tensor(x["h0"], torch.float32)
+    return q, k, v, beta, la, h0
+
+
+def _keep(seed, B, H, L, rate):
+    nch = (L + 63) // 64
+    return (np.random.default_rng(seed).random((B, H, nch)) < rate).astype(np.uint8)
+
+
+def _check(o, hf, ro, rh, tol, what):
+    eo, eh = max_rel_err(o, ro), max_rel_err(hf, rh)
+    say(f"  {what}: max rel err o {eo:.3e}, h_final {eh:.3e} (bound {tol:g})")
+    assert eo <= tol and eh <= tol, (eo, eh)
+
+
+# ---------------------------------------------------------------------------------------------
+# linear attention with a per-token decay
+# ---------------------------------------------------------------------------------------------
+@pytest.mark.parametrize("dtype,D,L", [("bf16", 64, 1), ("bf16", 128, 65), ("bf16", 128, 1000),
+                                       ("bf16", 64, 700), ("f32", 128, 333), ("f32", 64, 130)])
+def test_gated_linattn(dtype, D, L):
+    cfg = inputs.GDN_32K.with_(name=f"gla_{dtype}_d{D}_L{L}", B=2, H=2, L=L, Dk=D, Dv=D, dtype=dtype,
+                               seed=6000 + D + L, gate_dist="long")
+    say(f"case {cfg.name}")
+    x = inputs.prefill_inputs(cfg)
+    q, k, v, _, la, h0 = _dev(cfg, x)
+    o, hf = ops.linattn_prefill_fwd(q, k, v, h0, log_alpha=la)
+    torch.cuda.synchronize()
+    ro, rh = oracle.gla_prefill(x["q"], x["k"], x["v"], x["log_alpha"], x["h0"])
+    _check(host(o), host(hf), ro, rh, TOL_BF16 if dtype == "bf16" else TOL_F32, cfg.name)
+
+
+def test_gated_linattn_zero_gate_matches_plain():
+    cfg = inputs.LINATTN_8K.with_(name="gla_zero_gate", B=1, H=2, L=300, seed=6100)
+    say(f"case {cfg.name}")
+    x = inputs.prefill_inputs(cfg)
+    dt = TD[cfg.dtype]
+    q, k, v = (dev_tensor(x[n], dt) for n in ("q", "k", "v"))
+    o1, h1 = ops.linattn_prefill_fwd(q, k, v)
+    o2, h2 = ops.linattn_prefill_fwd(q, k, v, log_alpha=torch.zeros((1, 2, 300), device="cuda"))
+    torch.cuda.synchronize()
+    assert max_rel_err(host(o2), host(o1)) <= 1e-6 and max_rel_err(host(h2), host(h1)) <= 1e-6
+
+
+def test_gated_linattn_full_size_sampled_heads():
+    """The linear-attention workload's shape (B=4, H=16, L=8192) with long-memory gates."""
+    cfg = inputs.LINATTN_8K
+    say(f"case {cfg.name} with gates")
+    x = inputs.prefill_inputs(cfg)
+    # long-memory gates, log a ~ -U(0, 0.01), rounded to fp32
+    la_np = (-np.random.default_rng(6200).uniform(0.0, 0.01, (cfg.B, cfg.H, cfg.L))).astype(np.float32).astype(np.float64)
+    dt = TD[cfg.dtype]
+    q, k, v = (dev_tensor(x[n], dt) for n in ("q", "k", "v"))
+    o, hf = ops.linattn_prefill_fwd(q, k, v, log_alpha=dev_tensor(la_np, torch.float32))
+    torch.cuda.synchronize()
+    o, hf = host(o), host(hf)
+    for b, h in ((0, 0), (3, 15), (2, 7)):
+        sl = (slice(b, b + 1), slice(h, h + 1))
+        ro, rh = oracle.gla_prefill(x["q"][sl], x["k"][sl], x["v"][sl], la_np[sl])
+        _check(o[sl], hf[sl], ro, rh, TOL_BF16, f"b{b} h{h}")
+
+
+# ---------------------------------------------------------------------------------------------
+# gated delta rule with skipped chunk updates
+# ---------------------------------------------------------------------------------------------
+@pytest.mark.parametrize("dtype,D,L,rate", [("bf16", 128, 65, 0.5), ("bf16", 128, 1000, 0.29),
+                                            ("bf16", 64, 1500, 0.29), ("bf16", 128, 700, 0.0),
+                                            ("f32", 128, 333, 0.5), ("f32", 64, 200, 0.29)])
+def test_skip(dtype, D, L, rate):
+    cfg = inputs.GDN_32K.with_(name=f"skip_{dtype}_d{D}_L{L}_r{rate}", B=2, H=2, L=L, Dk=D, Dv=D, dtype=dtype,
+                               seed=7000 + D + L, gate_dist="long")
+    say(f"case {cfg.name}")
+    x = inputs.prefill_inputs(cfg)
+    keep = _keep(cfg.seed, 2, 2, L, rate)
+    q, k, v, beta, la, h0 = _dev(cfg, x)
+    o, hf = ops.gdn_prefill_skip_fwd(q, k, v, beta, la, torch.from_numpy(keep).cuda(), h0)
+    torch.cuda.synchronize()
+    ro, rh = oracle.gdn_prefill_skip(x["q"], x["k"], x["v"], x["beta"], x["log_alpha"], keep, x["h0"])
+    _check(host(o), host(hf), ro, rh, TOL_BF16 if dtype == "bf16" else TOL_F32, cfg.name)
+
+
+def test_skip_all_kept_is_the_dense_path_bitwise():
+    cfg = inputs.GDN_32K.with_(name="skip_all_kept", B=1, H=3, L=900, seed=7100)
+    say(f"case {cfg.name}")
+    x = inputs.prefill_inputs(cfg)
+    q, k, v, beta, la, h0 = _dev(cfg, x)
+    keep = torch.ones((1, 3, (900 + 63) // 64), dtype=torch.uint8, device="cuda")
+    o1, h1 = ops.gdn_prefill_skip_fwd(q, k, v, beta, la, keep, h0)
+    o2, h2 = ops.gdn_prefill_fwd(q, k, v, beta, la, h0)
+    torch.cuda.synchronize()
+    assert torch.equal(o1, o2) and torch.equal(h1, h2)
+
+
+def test_skip_segmented_schedule_is_bitwise_identical():
+    """The keep mask is indexed across segment boundaries: short segments give the same bits."""
+    cfg = inputs.GDN_32K.with_(name="skip_segments", B=1, H=2, L=2000, seed=7200)
+    say(f"case {cfg.name}")
+    x = inputs.prefill_inputs(cfg)
+    q, k, v, beta, la, h0 = _dev(cfg, x)
+    keep = torch.from_numpy(_keep(7200, 1, 2, 2000, 0.4)).cuda()
+    o1, h1 = ops.gdn_prefill_skip_fwd(q, k, v, beta, la, keep, h0)
+    rec = ops.prefill_workspace_size(1, 2, 64, 128, torch.bfloat16)
+    for seg in (1, 3):
+        ws = torch.empty(2 * seg * rec, dtype=torch.uint8, device="cuda")
+        o2, h2 = ops.gdn_prefill_skip_fwd(q, k, v, beta, la, keep, h0, workspace=ws)
+        torch.cuda.synchronize()
+        assert torch.equal(o1, o2) and torch.equal(h1, h2), seg
+
+
+def test_skip_full_size_sampled_heads():
+    """The 32K GDN workload (B=1, H=32, L=32768) at the pages' average retention (29%)."""
+    cfg = inputs.GDN_32K
+    say(f"case {cfg.name} skip 0.29")
+    x = inputs.prefill_inputs(cfg)
+    keep = _keep(7300, cfg.B, cfg.H, cfg.L, 0.29)
+    q, k, v, beta, la, h0 = _dev(cfg, x)
+    o, hf = ops.gdn_prefill_skip_fwd(q, k, v, beta, la, torch.from_numpy(keep).cuda(), h0)
+    torch.cuda.synchronize()
+    o, hf = host(o), host(hf)
+    for h in (0, 17, 31):
+        sl = (slice(0, 1), slice(h, h + 1))
+        ro, rh = oracle.gdn_prefill_skip(x["q"][sl], x["k"][sl], x["v"][sl], x["beta"][sl], x["log_alpha"][sl],
+                                         keep[sl], x["h0"][sl])
+        _check(o[sl], hf[sl], ro, rh, TOL_BF16, f"head {h}")
