@@ -126,26 +126,46 @@ def time_loop(torch, fn, steps, warmup):
 # ---------------------------------------------------------------------------------------------
 # components
 # ---------------------------------------------------------------------------------------------
-def bench_prefill(torch, ops, cfg, steps, warmup, gdn=True, verbose=False):
-    q, k, v, beta, la, h0 = prefill_device_inputs(torch, cfg, gates=gdn, verbose=verbose)
+def bench_prefill(torch, ops, cfg, steps, warmup, gdn=True, verbose=False, variant=None, keep_rate=0.29):
+    """variant None: gdn_prefill_fwd (gdn) or plain linattn_prefill_fwd; "gla": linattn_prefill_fwd with
+    per-token gates; "skip": gdn_prefill_skip_fwd with a seeded keep mask at keep_rate."""
+    gates = gdn or variant == "gla"
+    q, k, v, beta, la, h0 = prefill_device_inputs(torch, cfg, gates=gates, verbose=verbose)
     o = torch.empty_like(v)
     hf = torch.empty((cfg.B, cfg.H, cfg.Dk, cfg.Dv), device="cuda")
     ws = torch.empty(ops.prefill_workspace_size(cfg.B, cfg.H, cfg.L, cfg.Dk, q.dtype), dtype=torch.uint8,
                      device="cuda")
-    if gdn:
+    nchk = (cfg.L + 63) // 64
+    nchunk = cfg.B * cfg.H * nchk
+    kept = nchunk
+    if variant == "skip":
+        keep_np = (np.random.default_rng(cfg.seed).random((cfg.B, cfg.H, nchk)) < keep_rate).astype(np.uint8)
+        kept = int(keep_np.sum())
+        keep = torch.from_numpy(keep_np).cuda()
+        fn = lambda: ops.gdn_prefill_skip_fwd(q, k, v, beta, la, keep, h0, o=o, h_final=hf, workspace=ws)
+    elif gdn:
         fn = lambda: ops.gdn_prefill_fwd(q, k, v, beta, la, h0, o=o, h_final=hf, workspace=ws)
+    elif variant == "gla":
+        fn = lambda: ops.linattn_prefill_fwd(q, k, v, h0, log_alpha=la, o=o, h_final=hf, workspace=ws)
     else:
         fn = lambda: ops.linattn_prefill_fwd(q, k, v, h0, o=o, h_final=hf, workspace=ws)
     ms, wall = time_loop(torch, fn, steps, warmup)
-    nchunk = cfg.B * cfg.H * ((cfg.L + 63) // 64)
-    flops = nchunk * (gdn_flops_per_chunk(64, cfg.Dk) if gdn else linattn_flops_per_chunk(64, cfg.Dk))
-    nbytes = prefill_bytes(cfg, gates=gdn)
+    if gdn:
+        # a skipped chunk saves its state write, Khat^T U (2 C d_k d_v flop)
+        flops = nchunk * gdn_flops_per_chunk(64, cfg.Dk) - (nchunk - kept) * 2 * 64 * cfg.Dk * cfg.Dv
+    else:
+        flops = nchunk * linattn_flops_per_chunk(64, cfg.Dk)
+    nbytes = prefill_bytes(cfg, gates=gdn) + (cfg.B * cfg.H * cfg.L * 4 if variant == "gla" else 0)
+    nbytes += nchunk if variant == "skip" else 0
     res = {
-        "workload": cfg.name, "ms": ms, "tokens_per_s": cfg.B * cfg.L / (ms * 1e-3),
+        "workload": cfg.name + ({"gla": "_gated", "skip": f"_skip_keep{keep_rate}"}.get(variant, "")),
+        "ms": ms, "tokens_per_s": cfg.B * cfg.L / (ms * 1e-3),
         "alg_tflops": flops / (ms * 1e-3) / 1e12, "mfma_frac": flops / (ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS,
         "alg_bytes": nbytes, "hbm_GBps": nbytes / (ms * 1e-3) / 1e9,
         "hbm_frac": nbytes / (ms * 1e-3) / 1e9 / PEAK_HBM_GBPS, "wall_s": wall,
     }
+    if variant == "skip":
+        res["kept_fraction"] = kept / nchunk
     return res, (q, k, v, beta, la, h0, o, hf)
 
 
@@ -275,6 +295,15 @@ def main():
         log("[bench] gdn 32K")
         r, b = bench_prefill(torch, ops, inputs.GDN_32K, max(5, args.steps // 2), 2)
         components["gdn_32k"] = r
+        del b
+        log("[bench] linear attention with per-token gates")
+        r, b = bench_prefill(torch, ops, inputs.LINATTN_8K.with_(gates=True, gate_dist="long"),
+                             max(5, args.steps // 2), 2, gdn=False, variant="gla")
+        components["linattn_gated"] = r
+        del b
+        log("[bench] gdn 128K with skipped chunk updates (29% kept)")
+        r, b = bench_prefill(torch, ops, cfg, max(5, args.steps // 2), 2, variant="skip")
+        components["gdn_128k_skip"] = r
         del b
 
     cpu, parity = (None, None)
