@@ -185,7 +185,11 @@ __global__ __launch_bounds__(256) void prep_kernel(PrefArgs a) {
     float* skh = sb + CH;                                             // e^{g_C - g}
 
     const int cl = blockIdx.x, bh = blockIdx.y;     // chunk within the segment, slice
-    const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63, j = lane >> 4, m = lane & 15;
+    // The wave index lives in a scalar register so that every branch on it (token tiles,
+    // fragment groups, tile bounds) is a scalar branch. Matrix-core instructions write their
+    // result whatever the lane mask, so none may sit in a block that is skipped by masking lanes.
+    const int tid = threadIdx.x, lane = tid & 63, j = lane >> 4, m = lane & 15;
+    const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int grp = GPW * (w / WPG);                // this wave's first d-fragment group
     const int rt0 = RPW * (w % WPG);                // this wave's first token tile
     const long t0 = (long)(a.c0 + cl) * CH;
@@ -752,7 +756,8 @@ __global__ __launch_bounds__(256) void output_kernel(PrefArgs a) {
     float* sg = reinterpret_cast<float*>(Kr + CH * KP);          // g
 
     const int cl = blockIdx.x, bh = blockIdx.y;
-    const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63, j = lane >> 4, m = lane & 15;
+    const int tid = threadIdx.x, lane = tid & 63, j = lane >> 4, m = lane & 15;
+    const int w = __builtin_amdgcn_readfirstlane(tid >> 6);   // scalar, as in prep_kernel
     const long t0 = (long)(a.c0 + cl) * CH;
     const int n = (int)min((long)CH, a.L - t0);
     const size_t tok0 = (size_t)bh * a.L + t0;
