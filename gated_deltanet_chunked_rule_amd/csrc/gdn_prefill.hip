@@ -141,6 +141,18 @@ __device__ __forceinline__ void inverse_block_t(const float* Am, float* Tm, int 
     for (int e = 0; e < 4; ++e) Tm[(16 * bi + 4 * j + e) * AS + 16 * bj + m] = -y[e];
 }
 
+// Workgroup barrier for kernels whose waves share only LDS: it waits for this wave's LDS
+// operations (lgkmcnt) and nothing else. __syncthreads also fences global memory, which makes
+// every wave first wait for all of its outstanding global stores and loads (vmcnt(0)); none of
+// the prefill kernels reads back through global memory what another wave of its workgroup
+// wrote, so that wait is pure latency.
+__device__ __forceinline__ void lds_barrier() {
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_waitcnt(15 | (7 << 4) | (0 << 8) | (3 << 14));   // lgkmcnt(0)
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+}
+
 // ---------------------------------------------------------------------------------------------
 // stage 1: intra-chunk delta-system solve and WY/UT transform
 // ---------------------------------------------------------------------------------------------
@@ -231,40 +243,39 @@ __global__ __launch_bounds__(256) void prep_kernel(PrefArgs a) {
             *reinterpret_cast<uint4*>(Vr + r * KP + cu * EPU) = xv;
         }
     }
-    __syncthreads();
+    lds_barrier();
 
     // Rows to columns on the matrix core: kc[i][st] is the accumulator tile of tokens 16 st ..
     // 16 st + 15 and d-tile dt = FPD grp + i of K (lane (j, n): K[16 st + 4 j + e][16 dt + n]);
     // vc likewise for V. Fragments built from them have k = token, which the products over a
     // chunk's tokens need.
-    f32x4 kc[DPW][4], vc[DPW][4];
-#pragma unroll
-    for (int i = 0; i < DPW; ++i) {
+    // tiles(R, i, t): the four token tiles of d-tile FPD grp + i of the rows R
+    auto tiles = [&](const T* R, int i, f32x4 (&t)[4]) {
         const int dt = FPD * grp + i;
         const frag sel = unit_cols<E>(j, m, dt % FPD);
 #pragma unroll
-        for (int st = 0; st < 4; ++st) {
-            const f32x4 z = {0.f, 0.f, 0.f, 0.f};
-            kc[i][st] = M::mma(row_frag_raw<E>(Kr + (16 * st + m) * KP, KB * (dt / FPD), j), sel, z);
-            vc[i][st] = M::mma(row_frag_raw<E>(Vr + (16 * st + m) * KP, KB * (dt / FPD), j), sel, z);
-        }
-    }
+        for (int st = 0; st < 4; ++st)
+            t[st] = M::mma(row_frag_raw<E>(R + (16 * st + m) * KP, KB * (dt / FPD), j), sel, f32x4{0.f, 0.f, 0.f, 0.f});
+    };
 
     if constexpr (!DELTA) {
         // linear attention without the delta term: Khat = e^{g_C - g} K (K without gates), Ut = V
 #pragma unroll
         for (int i = 0; i < DPW; ++i) {
             const int dt = FPD * grp + i;
+            f32x4 kc[4], vc[4];
+            tiles(Kr, i, kc);
+            tiles(Vr, i, vc);
 #pragma unroll
             for (int kt = 0; kt < NKT; ++kt)
                 if (kt % WPG == w % WPG)
                     st_frag(rec + Ly::A_KH + (size_t)(dt * NKT + kt) * Ly::FR, lane,
-                            a.log_alpha ? cols_frag<E>(&kc[i][FPD * kt], skh + KB * kt, j) : cols_frag<E>(&kc[i][FPD * kt]));
+                            a.log_alpha ? cols_frag<E>(&kc[FPD * kt], skh + KB * kt, j) : cols_frag<E>(&kc[FPD * kt]));
 #pragma unroll
             for (int r = 0; r < RPW; ++r) {
                 const int rt = rt0 + r;
                 T* dst = reinterpret_cast<T*>(rec + Ly::A_UT) + ((size_t)(dt * 4 + rt) * 64 + lane) * 4;
-                store4(dst, make_float4(vc[i][rt][0], vc[i][rt][1], vc[i][rt][2], vc[i][rt][3]));
+                store4(dst, make_float4(vc[rt][0], vc[rt][1], vc[rt][2], vc[rt][3]));
             }
         }
         return;
@@ -284,21 +295,44 @@ __global__ __launch_bounds__(256) void prep_kernel(PrefArgs a) {
                                      row_frag_raw<E>(Kr + (16 * st + m) * KP, kb * KB, j), gacc[x]);
             }
         }
-        // Khat^T fragments (stored), -beta e^g K^T and beta V^T fragments (kept)
+        // Register pressure sets how many prep workgroups share a CU (four need at most 128
+        // VGPRs). The scheduling barriers keep the compiler from hoisting the LDS reads of one
+        // phase (Gram, K transposes, V transposes) into the previous one, and the kept fragments
+        // are pinned packed in registers: left alone, the compiler sinks their scaling and
+        // packing to the end of the kernel and keeps the fp32 tiles alive across the solve.
+        __builtin_amdgcn_sched_barrier(0);
+        // Khat^T fragments (stored), -beta e^g K^T and beta V^T fragments (kept), one d-tile's
+        // transposed tiles live at a time
         frag kbe[DPW][NKT], vb[DPW][NKT];
 #pragma unroll
         for (int i = 0; i < DPW; ++i) {
             const int dt = FPD * grp + i;
+            f32x4 kc[4];
+            tiles(Kr, i, kc);
 #pragma unroll
             for (int kt = 0; kt < NKT; ++kt) {
                 if (kt % WPG == w % WPG)
                     st_frag(rec + Ly::A_KH + (size_t)(dt * NKT + kt) * Ly::FR, lane,
-                            cols_frag<E>(&kc[i][FPD * kt], skh + KB * kt, j));
-                kbe[i][kt] = cols_frag<E>(&kc[i][FPD * kt], sbe + KB * kt, j);
-                vb[i][kt] = cols_frag<E>(&vc[i][FPD * kt], sb + KB * kt, j);
+                            cols_frag<E>(&kc[FPD * kt], skh + KB * kt, j));
+                kbe[i][kt] = cols_frag<E>(&kc[FPD * kt], sbe + KB * kt, j);
             }
         }
-        __syncthreads();   // K and V rows are no longer read: their space takes T and A
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int i = 0; i < DPW; ++i) {
+            f32x4 vc[4];
+            tiles(Vr, i, vc);
+#pragma unroll
+            for (int kt = 0; kt < NKT; ++kt) vb[i][kt] = cols_frag<E>(&vc[FPD * kt], sb + KB * kt, j);
+        }
+#pragma unroll
+        for (int i = 0; i < DPW; ++i)
+#pragma unroll
+            for (int kt = 0; kt < NKT; ++kt) {
+                asm volatile("" : "+v"(kbe[i][kt]));
+                asm volatile("" : "+v"(vb[i][kt]));
+            }
+        lds_barrier();   // K and V rows are no longer read: their space takes T and A
         // A[r][s] = beta_r exp(g_r - g_s) k_r.k_s for s < r
 #pragma unroll
         for (int x = 0; x < 3; ++x) {
@@ -320,7 +354,7 @@ __global__ __launch_bounds__(256) void prep_kernel(PrefArgs a) {
             const int bi = b < 3 ? 0 : (b < 5 ? 1 : 2), bj = b < 3 ? b + 1 : (b < 5 ? b - 1 : 3);
             Tm[(16 * bi + (e >> 4)) * AS + 16 * bj + (e & 15)] = 0.f;
         }
-        __syncthreads();
+        lds_barrier();
         // T = (I + A)^-1, blocked by 16: diagonal blocks by forward substitution (wave i inverts
         // block i, lane c < 16 owns column c), then T_ij = -T_ii sum_{k=j}^{i-1} A_ik T_kj level
         // by level on fp32 MFMA.
@@ -341,10 +375,10 @@ __global__ __launch_bounds__(256) void prep_kernel(PrefArgs a) {
         }
 #pragma unroll
         for (int lvl = 1; lvl < 4; ++lvl) {
-            __syncthreads();
+            lds_barrier();
             if (w + lvl < 4) inverse_block_t<AS>(Am, Tm, w + lvl, w, j, m);
         }
-        __syncthreads();
+        lds_barrier();
         // this wave's token tiles: T rows as fragments (rows 16 rt .. 16 rt + 15 of T are zero
         // beyond column 16 rt + 15, so token blocks past kbmax are skipped)
 #pragma unroll
@@ -437,18 +471,10 @@ struct ChainCfg {
     static_assert(WAITN < 64, "vmcnt is 6 bits");
 };
 
-// Barrier of the chain workgroup. Only LDS is shared between its waves: the loader waves fill it
-// with direct-to-LDS loads whose completion they establish themselves (wait_vmcnt) before
-// arriving, the compute waves read it and exchange partial products through it with ordinary
-// LDS writes. So the barrier waits for LDS operations (lgkmcnt) and nothing else: neither
-// outstanding global stores nor the loads still in flight for later chunks.
-__device__ __forceinline__ void lds_barrier() {
-    asm volatile("" ::: "memory");
-    __builtin_amdgcn_s_waitcnt(15 | (7 << 4) | (0 << 8) | (3 << 14));   // lgkmcnt(0)
-    __builtin_amdgcn_s_barrier();
-    asm volatile("" ::: "memory");
-}
-
+// Barrier of the chain workgroup: see lds_barrier. Its loader waves fill the LDS ring with
+// direct-to-LDS loads whose completion they establish themselves (wait_vmcnt) before arriving,
+// and the compute waves exchange partial products through ordinary LDS writes, so the barrier
+// must not wait for the global stores and the loads still in flight for later chunks.
 // Wait until at most N vector-memory operations of this wave are outstanding (gfx9 encoding:
 // vmcnt split over bits 3:0 and 15:14, expcnt and lgkmcnt left at their maxima).
 template <int N>
@@ -802,7 +828,7 @@ __global__ __launch_bounds__(256) void output_kernel(PrefArgs a) {
         if (a.log_alpha && lane < n) la = a.log_alpha[tok0 + lane];
         sg[lane] = wave_scan(la, lane);
     }
-    __syncthreads();
+    lds_barrier();
     // P^T tile (st, rt), lane (j, n): P[r = 16 rt + n][s = 16 st + 4 j + e] = exp(g_r - g_s) q_r.k_s
     // for s <= r, else 0. Written straight into its half (bf16) or whole (fp32) of the P fragment
     // [rt][st / FPD], whose lane (j, n) holds column r and k = s.
@@ -834,7 +860,7 @@ __global__ __launch_bounds__(256) void output_kernel(PrefArgs a) {
             }
         }
     }
-    __syncthreads();
+    lds_barrier();
     // O^T tiles (vt, rt) = H^T e^g Q^T + U^T P^T: the state product with raw Q fragments, scaled
     // by e^{g_r} per token column, then the intra-chunk part accumulated on top
     float eg[4];
