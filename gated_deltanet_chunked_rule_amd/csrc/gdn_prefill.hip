@@ -776,10 +776,11 @@ __global__ __launch_bounds__(256) void output_kernel(PrefArgs a) {
     constexpr int KB = M::KB, NKD = Ly::NKD, NKT = Ly::NKT, NDT = Ly::NDT, FPD = OT::FPD;
     constexpr int KP = D + 8;   // row stride of the staged Q and K tiles (elements)
     extern __shared__ __align__(16) unsigned char smem[];
-    unsigned char* sP = smem;                                    // P fragments [rt][kt]
-    T* Qr = reinterpret_cast<T*>(sP + 4 * NKT * 1024);           // [CH][KP] Q rows
-    T* Kr = Qr + CH * KP;                                        // [CH][KP] K rows
+    T* Qr = reinterpret_cast<T*>(smem);                          // [CH][KP] Q rows
+    T* Kr = Qr + CH * KP;                                        // [CH][KP] K rows, then
+    unsigned char* sP = reinterpret_cast<unsigned char*>(Kr);    //   the P fragments [rt][kt]
     float* sg = reinterpret_cast<float*>(Kr + CH * KP);          // g
+    static_assert((size_t)4 * NKT * 1024 <= (size_t)CH * KP * sizeof(T), "P fragments fit in the K rows");
 
     const int cl = blockIdx.x, bh = blockIdx.y;
     const int tid = threadIdx.x, lane = tid & 63, j = lane >> 4, m = lane & 15;
@@ -831,14 +832,17 @@ __global__ __launch_bounds__(256) void output_kernel(PrefArgs a) {
     lds_barrier();
     // P^T tile (st, rt), lane (j, n): P[r = 16 rt + n][s = 16 st + 4 j + e] = exp(g_r - g_s) q_r.k_s
     // for s <= r, else 0. Written straight into its half (bf16) or whole (fp32) of the P fragment
-    // [rt][st / FPD], whose lane (j, n) holds column r and k = s.
+    // [rt][st / FPD], whose lane (j, n) holds column r and k = s; the fragments take the place of
+    // the K rows once every wave has read those (35 KB of LDS: four workgroups per CU, not three).
+    f32x4 pts[OT::PER_WAVE];
 #pragma unroll
     for (int x = 0; x < OT::PER_WAVE; ++x) {
         const int ti = w + 4 * x;
         if (ti < OT::N) {
             int rt, st;
             OT::tile(ti, rt, st);
-            f32x4 pt = {0.f, 0.f, 0.f, 0.f};
+            f32x4& pt = pts[x];
+            pt = f32x4{0.f, 0.f, 0.f, 0.f};
             if (st <= rt) {
 #pragma unroll
                 for (int kd = 0; kd < NKD; ++kd)
@@ -852,6 +856,16 @@ __global__ __launch_bounds__(256) void output_kernel(PrefArgs a) {
                     pt[e] = (s2 <= r) ? pt[e] * __expf(gr - sg[s2]) : 0.f;
                 }
             }
+        }
+    }
+    lds_barrier();   // the K rows are read
+#pragma unroll
+    for (int x = 0; x < OT::PER_WAVE; ++x) {
+        const int ti = w + 4 * x;
+        if (ti < OT::N) {
+            int rt, st;
+            OT::tile(ti, rt, st);
+            const f32x4 pt = pts[x];
             unsigned char* dst = sP + (size_t)(rt * NKT + st / FPD) * 1024 + lane * 16;
             if constexpr (FPD == 2) {
                 *reinterpret_cast<uint2*>(dst + 8 * (st % 2)) = uint2{f2bf2(pt[0], pt[1]), f2bf2(pt[2], pt[3])};
@@ -862,39 +876,48 @@ __global__ __launch_bounds__(256) void output_kernel(PrefArgs a) {
     }
     lds_barrier();
     // O^T tiles (vt, rt) = H^T e^g Q^T + U^T P^T: the state product with raw Q fragments, scaled
-    // by e^{g_r} per token column, then the intra-chunk part accumulated on top
+    // by e^{g_r} per token column, then the intra-chunk part accumulated on top. The Q fragments
+    // are read one token tile at a time (the scheduling barrier keeps the compiler from reading
+    // all sixteen ahead), which keeps the kernel within 128 VGPRs.
     float eg[4];
-    frag Qf[4][NKD];
+    f32x4 acc[NVW][4];
 #pragma unroll
     for (int rt = 0; rt < 4; ++rt) {
         eg[rt] = __expf(sg[16 * rt + m]);
+        frag qf[NKD];
 #pragma unroll
-        for (int kd = 0; kd < NKD; ++kd) Qf[rt][kd] = row_frag_raw<E>(Qr + (16 * rt + m) * KP, kd * KB, j);
+        for (int kd = 0; kd < NKD; ++kd) qf[kd] = row_frag_raw<E>(Qr + (16 * rt + m) * KP, kd * KB, j);
+#pragma unroll
+        for (int iv = 0; iv < NVW; ++iv) {
+            acc[iv][rt] = f32x4{0.f, 0.f, 0.f, 0.f};
+            if (w + 4 * iv < NDT) {
+#pragma unroll
+                for (int kd = 0; kd < NKD; ++kd) acc[iv][rt] = M::mma(Hc[iv][kd], qf[kd], acc[iv][rt]);
+            }
+        }
+        __builtin_amdgcn_sched_barrier(0);
     }
 #pragma unroll
     for (int iv = 0; iv < NVW; ++iv) {
         const int vt = w + 4 * iv;
         if (vt >= NDT) break;
-        f32x4 acc[4];
-#pragma unroll
-        for (int rt = 0; rt < 4; ++rt) acc[rt] = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int kd = 0; kd < NKD; ++kd)
-#pragma unroll
-            for (int rt = 0; rt < 4; ++rt) acc[rt] = M::mma(Hc[iv][kd], Qf[rt][kd], acc[rt]);
 #pragma unroll
         for (int rt = 0; rt < 4; ++rt)
-            acc[rt] = f32x4{acc[rt][0] * eg[rt], acc[rt][1] * eg[rt], acc[rt][2] * eg[rt], acc[rt][3] * eg[rt]};
+            acc[iv][rt] = f32x4{acc[iv][rt][0] * eg[rt], acc[iv][rt][1] * eg[rt], acc[iv][rt][2] * eg[rt],
+                                acc[iv][rt][3] * eg[rt]};
 #pragma unroll
         for (int kt = 0; kt < NKT; ++kt)
 #pragma unroll
             for (int rt = 0; rt < 4; ++rt)
-                if (kt <= OT::kbmax(rt)) acc[rt] = M::mma(Uf[iv][kt], ld_frag<frag>(sP + (rt * NKT + kt) * 1024, lane), acc[rt]);
+                if (kt <= OT::kbmax(rt))
+                    acc[iv][rt] = M::mma(Uf[iv][kt], ld_frag<frag>(sP + (rt * NKT + kt) * 1024, lane), acc[iv][rt]);
 #pragma unroll
         for (int rt = 0; rt < 4; ++rt) {
             // lane (j, m): O[token 16 rt + m][16 vt + 4 j .. + 3]
             const int r = 16 * rt + m;
-            if (r < n) store4(op + (size_t)r * D + 16 * vt + 4 * j, make_float4(acc[rt][0], acc[rt][1], acc[rt][2], acc[rt][3]));
+            if (r < n)
+                store4(op + (size_t)r * D + 16 * vt + 4 * j,
+                       make_float4(acc[iv][rt][0], acc[iv][rt][1], acc[iv][rt][2], acc[iv][rt][3]));
         }
     }
 }
@@ -913,27 +936,35 @@ struct Launch {
     static constexpr int KP = D + 8;
     static constexpr size_t LDS_PREP = PrepCfg<D, E>::LDS;
     static constexpr size_t LDS_CHAIN = CC::LDS;
-    static constexpr size_t LDS_OUT = (size_t)4 * Ly::NKT * 1024 + (size_t)2 * CH * KP * sizeof(T) + CH * 4;
+    static constexpr size_t LDS_OUT = (size_t)2 * CH * KP * sizeof(T) + CH * 4;   // Q rows, K rows / P, g
+    // While the chain runs on some of the CUs, the prep and output stages beside it are held to
+    // three workgroups per CU by asking for more than a quarter of the CU's 160 KB of LDS: more
+    // concurrent stage work slows the latency-bound chain by more than it gains (B=1, H=16,
+    // L=128K: 2.82 ms at four per CU, 2.75 ms at three, 2.87 ms at two).
+    static constexpr size_t LDS_BESIDE = 41 * 1024;
+    static constexpr size_t lds_prep(bool beside) { return beside && LDS_PREP < LDS_BESIDE ? LDS_BESIDE : LDS_PREP; }
+    static constexpr size_t lds_out(bool beside) { return beside && LDS_OUT < LDS_BESIDE ? LDS_BESIDE : LDS_OUT; }
 
     // raise the dynamic-LDS limits once per process (every caller sets the same values)
     static bool attributes() {
         static const bool ok =
             hipFuncSetAttribute(reinterpret_cast<const void*>(&prep_kernel<D, E, DELTA>),
-                                hipFuncAttributeMaxDynamicSharedMemorySize, (int)LDS_PREP) == hipSuccess &&
+                                hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds_prep(true)) == hipSuccess &&
             hipFuncSetAttribute(reinterpret_cast<const void*>(&chain_kernel<D, E, DELTA>),
                                 hipFuncAttributeMaxDynamicSharedMemorySize, (int)LDS_CHAIN) == hipSuccess &&
             hipFuncSetAttribute(reinterpret_cast<const void*>(&output_kernel<D, E, DELTA>),
-                                hipFuncAttributeMaxDynamicSharedMemorySize, (int)LDS_OUT) == hipSuccess;
+                                hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds_out(true)) == hipSuccess;
         return ok;
     }
-    static void prep(const PrefArgs& a, hipStream_t s) {
-        hipLaunchKernelGGL((prep_kernel<D, E, DELTA>), dim3(a.nseg, a.BH), dim3(256), LDS_PREP, s, a);
+    static int chain_blocks(int BH) { return 8 * ((BH + 7) / 8) * CC::NCW; }
+    static void prep(const PrefArgs& a, hipStream_t s, bool beside = false) {
+        hipLaunchKernelGGL((prep_kernel<D, E, DELTA>), dim3(a.nseg, a.BH), dim3(256), lds_prep(beside), s, a);
     }
     static void chain(const PrefArgs& a, hipStream_t s) {
-        hipLaunchKernelGGL((chain_kernel<D, E, DELTA>), dim3(8 * ((a.BH + 7) / 8) * CC::NCW), dim3(CC::THREADS), LDS_CHAIN, s, a);
+        hipLaunchKernelGGL((chain_kernel<D, E, DELTA>), dim3(chain_blocks(a.BH)), dim3(CC::THREADS), LDS_CHAIN, s, a);
     }
-    static void output(const PrefArgs& a, hipStream_t s) {
-        hipLaunchKernelGGL((output_kernel<D, E, DELTA>), dim3(a.nseg, a.BH), dim3(256), LDS_OUT, s, a);
+    static void output(const PrefArgs& a, hipStream_t s, bool beside = false) {
+        hipLaunchKernelGGL((output_kernel<D, E, DELTA>), dim3(a.nseg, a.BH), dim3(256), lds_out(beside), s, a);
     }
 };
 
@@ -944,14 +975,16 @@ struct StreamCtx {
     static constexpr int R = NBUF + 1;   // event ring: an event is re-recorded only after its waits are enqueued
     std::mutex mu;
     bool ready = false;
+    int ncu = 0;   // compute units of the device
     hipStream_t sp = nullptr, so = nullptr;
     hipEvent_t start = nullptr, ev_prep[R] = {}, ev_chain[R] = {}, ev_out[R] = {};
 };
 
 static StreamCtx g_ctx[64];
 
-static bool init_ctx(StreamCtx& c) {
+static bool init_ctx(StreamCtx& c, int dev) {
     if (c.ready) return true;
+    if (hipDeviceGetAttribute(&c.ncu, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return false;
     if (hipStreamCreateWithFlags(&c.sp, hipStreamNonBlocking) != hipSuccess) return false;
     if (hipStreamCreateWithFlags(&c.so, hipStreamNonBlocking) != hipSuccess) return false;
     if (hipEventCreateWithFlags(&c.start, hipEventDisableTiming) != hipSuccess) return false;
@@ -982,8 +1015,9 @@ static int launch_prefill_t(PrefArgs a, long nch, size_t ws_bytes, hipStream_t s
     if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return -1;
     StreamCtx& cx = g_ctx[dev];
     std::lock_guard<std::mutex> lk(cx.mu);
-    if (!init_ctx(cx)) return -1;
+    if (!init_ctx(cx, dev)) return -1;
     constexpr int R = StreamCtx::R;
+    const bool beside = LN::chain_blocks(a.BH) < cx.ncu;   // the chain leaves CUs to the other stages
     unsigned char* ws0 = a.ws;
     const float* h0 = a.h0;
     bool ok = hipEventRecord(cx.start, stream) == hipSuccess && hipStreamWaitEvent(cx.sp, cx.start, 0) == hipSuccess &&
@@ -1001,13 +1035,13 @@ static int launch_prefill_t(PrefArgs a, long nch, size_t ws_bytes, hipStream_t s
         // is done puts three kernels on the memory system at once and slows the chain more than
         // it saves.)
         if (sgi >= NBUF) ok = ok && hipStreamWaitEvent(cx.sp, cx.ev_out[(sgi - NBUF) % R], 0) == hipSuccess;
-        LN::prep(b, cx.sp);
+        LN::prep(b, cx.sp, beside);
         ok = ok && hipEventRecord(cx.ev_prep[sgi % R], cx.sp) == hipSuccess;
         ok = ok && hipStreamWaitEvent(stream, cx.ev_prep[sgi % R], 0) == hipSuccess;
         LN::chain(b, stream);
         ok = ok && hipEventRecord(cx.ev_chain[sgi % R], stream) == hipSuccess;
         ok = ok && hipStreamWaitEvent(cx.so, cx.ev_chain[sgi % R], 0) == hipSuccess;
-        LN::output(b, cx.so);
+        LN::output(b, cx.so, beside);
         ok = ok && hipEventRecord(cx.ev_out[sgi % R], cx.so) == hipSuccess;
     }
     // the caller's stream continues only after the last output stage
