@@ -13,6 +13,8 @@ this module only compiles it with gcc on first use and marshals NumPy arrays.
     gdn_prefill_skip(q, k, v, beta, log_alpha, keep, h0, chunk)  gated delta rule, skipped chunks
                                                                  only decay the carried state
     gdn_decode_step(q, k, v, beta, log_alpha, state) -> (o, new_state)
+    linattn_bidir(q, k, v, normalize, elu1)    -> (o, kv)        non-causal: KV = sum phi(k) v^T,
+                                                                 o = phi(q) KV [/ phi(q).sum phi(k)]
 
 Shapes: q,k [B,H,L,Dk]; v [B,H,L,Dv]; beta, log_alpha [B,H,L]; h0/h_final [B,H,Dk,Dv]
 (key-major, element [i][j] = S[j][i]); decode: q,k [N,H,Dk], v [N,H,Dv], beta/log_alpha
@@ -58,10 +60,11 @@ def _load():
             lib.oracle_linattn_prefill.argtypes = [P, P, P, P, P, P, i, i, i, i, i, i]
             lib.oracle_gdn_decode_step.argtypes = [P, P, P, P, P, P, P, i, i, i, i, i]
             lib.oracle_gla_prefill.argtypes = [P, P, P, P, P, P, P, i, i, i, i, i, i]
+            lib.oracle_linattn_bidir.argtypes = [P, P, P, P, P, i, i, i, i, i, i, i]
             IP = ctypes.POINTER(ctypes.c_int)
             lib.oracle_gdn_prefill_skip.argtypes = [P, P, P, P, P, P, IP, i, P, P, i, i, i, i, i, i]
             for f in (lib.oracle_gdn_prefill, lib.oracle_linattn_prefill, lib.oracle_gdn_decode_step,
-                      lib.oracle_gla_prefill, lib.oracle_gdn_prefill_skip):
+                      lib.oracle_gla_prefill, lib.oracle_gdn_prefill_skip, lib.oracle_linattn_bidir):
                 f.restype = ctypes.c_int
             _lib = lib
     return _lib
@@ -169,3 +172,20 @@ def gdn_decode_step(q, k, v, beta, log_alpha, state, nthreads: int = 0):
     last_threads = _load().oracle_gdn_decode_step(_ptr(q), _ptr(k), _ptr(v), _ptr(beta), _ptr(log_alpha),
                                                   _ptr(st), _ptr(o), N, H, Dk, Dv, nthreads)
     return o, st
+
+
+def linattn_bidir(q, k, v, normalize: bool = True, elu1: bool = True, nthreads: int = 0):
+    """Bidirectional linear attention (datadaily.news overview, section "Linear attention"):
+    KV = sum_n phi(k_n) v_n^T, o_n = phi(q_n)^T KV, divided by Z_n = phi(q_n) . sum_m phi(k_m)
+    when normalize; phi = elu + 1 when elu1, else the identity. Returns (o, kv), kv [B,H,Dk,Dv]."""
+    global last_threads
+    q, k, v = (_as4(_f64(t), 4) for t in (q, k, v))
+    B, H, L, Dk = q.shape
+    Dv = v.shape[-1]
+    assert k.shape == q.shape and v.shape[:3] == (B, H, L)
+    o = np.empty((B, H, L, Dv))
+    kv = np.empty((B, H, Dk, Dv))
+    flags = (1 if normalize else 0) | (2 if elu1 else 0)
+    last_threads = _load().oracle_linattn_bidir(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(kv), B, H, L, Dk, Dv,
+                                                flags, nthreads)
+    return o, kv

@@ -35,6 +35,13 @@
  *
  *   Decode step: the gated delta-rule update above applied once to a stored state.
  *
+ *   Bidirectional (non-causal) linear attention, the kernel-feature-map form of the datadaily.news
+ *   overview (section "Linear attention", its linear_attention function): every token sees the
+ *   whole sequence,
+ *       KV = sum_n phi(k_n) v_n^T (Dk x Dv),  out_n = KV^T phi(q_n),
+ *       Z_n = phi(q_n) . sum_m phi(k_m),      out_n / Z_n when normalising,
+ *   with phi the identity or elu(x) + 1 (x for x > 0, exp(x) otherwise).
+ *
  * Storage orientation. Initial, final and decode states are stored key-major: element
  * [i][j] of a [Dk][Dv] block equals S[j][i]. This matches the chunk-level map S -> A S + B of
  * the SparseGDN article's skip-scan illustration (fileenergy.com, section on embedding the
@@ -246,6 +253,57 @@ int oracle_gdn_decode_step(const double *q, const double *k, const double *v,
         read_out(o + (size_t)s * Dv, S, q + (size_t)s * Dk, Dk, Dv);
         store_state(st, S, Dk, Dv);
         free(S);
+    }
+    return used;
+}
+
+/* phi(x) = elu(x) + 1 when elu1, else x. */
+static double feature(double x, int elu1)
+{
+    if (!elu1) return x;
+    return x > 0.0 ? x + 1.0 : exp(x);
+}
+
+/* Bidirectional linear attention. flags bit 0: divide by Z; bit 1: phi = elu + 1 (else identity).
+ * q, k [B,H,L,Dk]; v, o [B,H,L,Dv]; kv [B,H,Dk,Dv] (KV, key-major, may be NULL). */
+int oracle_linattn_bidir(const double *q, const double *k, const double *v, double *o, double *kv,
+                         int B, int H, int L, int Dk, int Dv, int flags, int nthreads)
+{
+    const int used = set_threads(nthreads);
+    const long nslice = (long)B * H;
+    const int norm = flags & 1, elu1 = (flags >> 1) & 1;
+#pragma omp parallel for schedule(dynamic, 1)
+    for (long s = 0; s < nslice; ++s) {
+        double *KV = (double *)calloc((size_t)Dk * Dv + Dk + Dk, sizeof(double));
+        double *ksum = KV + (size_t)Dk * Dv;
+        double *fq = ksum + Dk;
+        /* KV = sum_n phi(k_n) v_n^T and the key sum, over the whole sequence */
+        for (int t = 0; t < L; ++t) {
+            const double *kt = k + ((size_t)s * L + t) * Dk;
+            const double *vt = v + ((size_t)s * L + t) * Dv;
+            for (int i = 0; i < Dk; ++i) {
+                const double fk = feature(kt[i], elu1);
+                ksum[i] += fk;
+                for (int j = 0; j < Dv; ++j) KV[(size_t)i * Dv + j] += fk * vt[j];
+            }
+        }
+        /* out_n = KV^T phi(q_n), then / Z_n */
+        for (int t = 0; t < L; ++t) {
+            const double *qt = q + ((size_t)s * L + t) * Dk;
+            double *ot = o + ((size_t)s * L + t) * Dv;
+            double z = 0.0;
+            for (int i = 0; i < Dk; ++i) {
+                fq[i] = feature(qt[i], elu1);
+                z += fq[i] * ksum[i];
+            }
+            for (int j = 0; j < Dv; ++j) {
+                double acc = 0.0;
+                for (int i = 0; i < Dk; ++i) acc += fq[i] * KV[(size_t)i * Dv + j];
+                ot[j] = norm ? acc / z : acc;
+            }
+        }
+        if (kv) memcpy(kv + (size_t)s * Dk * Dv, KV, sizeof(double) * (size_t)Dk * Dv);
+        free(KV);
     }
     return used;
 }
