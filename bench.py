@@ -169,6 +169,25 @@ def bench_prefill(torch, ops, cfg, steps, warmup, gdn=True, verbose=False, varia
     return res, (q, k, v, beta, la, h0, o, hf)
 
 
+def bench_bidir(torch, ops, cfg, steps, warmup):
+    """Bidirectional linear attention with the elu+1 feature map and the normaliser on raw N(0,1)
+    q and k of the linear-attention workload's shape."""
+    cfg = cfg.with_(qk="raw")
+    q, k, v, _, _, _ = prefill_device_inputs(torch, cfg, gates=False)
+    o = torch.empty_like(v)
+    ws = torch.empty(max(1, ops.linattn_bidir_workspace_size(cfg.B, cfg.H, cfg.L, cfg.Dk, q.dtype)),
+                     dtype=torch.uint8, device="cuda")
+    ms, wall = time_loop(torch, lambda: ops.linattn_bidir_fwd(q, k, v, o=o, workspace=ws), steps, warmup)
+    tok = cfg.B * cfg.H * cfg.L
+    flops = 2 * 2 * tok * cfg.Dk * cfg.Dv + 2 * 2 * tok * cfg.Dk      # phi(K)^T V and KV^T phi(q); key sums, Z
+    e = 2 if cfg.dtype == "bf16" else 4
+    nbytes = 3 * tok * cfg.Dk * e + tok * cfg.Dv * e
+    return {"workload": cfg.name + "_bidirectional_elu1_normalized", "ms": ms, "tokens_per_s": cfg.B * cfg.L / (ms * 1e-3),
+            "alg_tflops": flops / (ms * 1e-3) / 1e12, "mfma_frac": flops / (ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS,
+            "alg_bytes": nbytes, "hbm_GBps": nbytes / (ms * 1e-3) / 1e9,
+            "hbm_frac": nbytes / (ms * 1e-3) / 1e9 / PEAK_HBM_GBPS, "wall_s": wall}
+
+
 def bench_decode(torch, ops, cfg, steps):
     dt = torch.bfloat16 if cfg.dtype == "bf16" else torch.float32
     state = to_dev(torch, inputs.decode_state(cfg), torch.float32)
@@ -292,6 +311,8 @@ def main():
         r, b = bench_prefill(torch, ops, inputs.LINATTN_8K, max(5, args.steps // 2), 2, gdn=False)
         components["linattn"] = r
         del b
+        log("[bench] bidirectional linear attention")
+        components["linattn_bidir"] = bench_bidir(torch, ops, inputs.LINATTN_8K, max(5, args.steps // 2), 2)
         log("[bench] gdn 32K")
         r, b = bench_prefill(torch, ops, inputs.GDN_32K, max(5, args.steps // 2), 2)
         components["gdn_32k"] = r

@@ -8,6 +8,7 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libgdn.so")
 
 GDN_BF16, GDN_F32 = 0, 1
+GDN_BIDIR_NORMALIZE, GDN_BIDIR_ELU1 = 1, 2
 GDN_OK = 0
 
 # every symbol the header declares, with (restype, argtypes)
@@ -20,6 +21,8 @@ SIGNATURES = {
                                   _vp]),
     "linattn_prefill_fwd": (_i, [_vp, _vp, _vp, _fp, _fp, _fp, _vp, _fp, _i, _i, _i, _i, _i, _i, _vp, _sz, _vp]),
     "gdn_decode_step": (_i, [_vp, _vp, _vp, _fp, _fp, _fp, _vp, _i, _i, _i, _i, _i, _vp]),
+    "linattn_bidir_workspace_size": (_sz, [_i, _i, _i, _i, _i, _i]),
+    "linattn_bidir_fwd": (_i, [_vp, _vp, _vp, _vp, _fp, _i, _i, _i, _i, _i, _i, _i, _vp, _sz, _vp]),
 }
 
 _lib = None

@@ -146,6 +146,41 @@ int linattn_prefill_fwd(const void* q, const void* k, const void* v, const float
                    workspace_bytes, stream, false);
 }
 
+size_t linattn_bidir_workspace_size(int B, int H, int L, int Dk, int Dv, int dtype) {
+    if (check_dims(B, H, L, Dk, Dv, dtype) != GDN_OK) return 0;
+    return gdn::bidir_workspace_bytes((long)B * H, L, Dk, dtype);
+}
+
+int linattn_bidir_fwd(const void* q, const void* k, const void* v, void* o, float* kv_out, int B, int H, int L,
+                      int Dk, int Dv, int dtype, int flags, void* workspace, size_t workspace_bytes, void* stream) {
+    int st = check_dims(B, H, L, Dk, Dv, dtype);
+    if (st != GDN_OK) return st;
+    if (flags & ~(GDN_BIDIR_NORMALIZE | GDN_BIDIR_ELU1)) return GDN_ERR_SHAPE;
+    if (L > 0 && (!q || !k || !v || !o)) return GDN_ERR_NULL;
+    const void* ptrs[] = {q, k, v, o, kv_out};
+    for (const void* p : ptrs)
+        if (p && !aligned(p, 16)) return GDN_ERR_ALIGN;
+    const size_t need = gdn::bidir_workspace_bytes((long)B * H, L, Dk, dtype);
+    if (need > 0) {
+        if (!workspace || workspace_bytes < need) return GDN_ERR_WORKSPACE;
+        if (!aligned(workspace, 256)) return GDN_ERR_ALIGN;
+    }
+    const size_t esz = dtype == GDN_BF16 ? 2 : 4;
+    const size_t BH = (size_t)B * H, tok = BH * (size_t)L;
+    const Range in[] = {rng(q, tok * Dk * esz), rng(k, tok * Dk * esz), rng(v, tok * Dv * esz)};
+    const Range ro = rng(o, tok * Dv * esz), rk = rng(kv_out, kv_out ? BH * Dk * Dv * 4 : 0);
+    const Range rw = rng(workspace, workspace && need ? workspace_bytes : 0);
+    for (const Range& r : in)
+        if (overlap(ro, r) || overlap(rk, r) || overlap(rw, r)) return GDN_ERR_ALIAS;
+    if (overlap(ro, rk) || overlap(ro, rw) || overlap(rk, rw)) return GDN_ERR_ALIAS;
+    st = check_device();
+    if (st != GDN_OK) return st;
+    return gdn::launch_bidir(q, k, v, o, kv_out, (int)BH, L, Dk, dtype, flags, workspace,
+                             static_cast<hipStream_t>(stream)) == 0
+               ? GDN_OK
+               : GDN_ERR_LAUNCH;
+}
+
 int gdn_decode_step(const void* q, const void* k, const void* v, const float* beta, const float* log_alpha,
                     float* state, void* o, int N, int H, int Dk, int Dv, int dtype, void* stream) {
     if (dtype != GDN_BF16 && dtype != GDN_F32) return GDN_ERR_DTYPE;

@@ -16,4 +16,10 @@ int launch_prefill(const void* q, const void* k, const void* v, const float* bet
                    const unsigned char* keep, const float* h0, void* o, float* h_final, int BH, long L, int D,
                    int dtype, bool delta, void* ws, size_t ws_bytes, hipStream_t stream);
 
+// Bidirectional linear attention. kv_out: [BH][D][D] fp32 or NULL. flags bit 0: divide by Z,
+// bit 1: phi = elu + 1 (else identity). The workspace is bidir_workspace_bytes(...) bytes.
+size_t bidir_workspace_bytes(long BH, long L, int D, int dtype);
+int launch_bidir(const void* q, const void* k, const void* v, void* o, float* kv_out, int BH, long L, int D,
+                 int dtype, int flags, void* ws, hipStream_t stream);
+
 }  // namespace gdn

@@ -86,7 +86,7 @@ class PrefillConfig:
     Dv: int
     dtype: str            # "bf16" or "f32": dtype of q, k, v and o
     seed: int
-    qk: str = "l2"        # "l2": N(0,1) then L2-normalised per token; "elu1": elu(x)+1
+    qk: str = "l2"        # "l2": N(0,1) then L2-normalised per token; "elu1": elu(x)+1; "raw": N(0,1)
     gates: bool = True    # beta and log_alpha present (gated delta rule)
     gate_dist: str = "config"   # "config": log a = -softplus(N(0,1)+2); "long": -U(0, 0.01)
     h0: Optional[float] = 0.1   # std of the N(0, 0.01) initial state; None: no h0 (zeros)
@@ -138,7 +138,12 @@ def prefill_slice(cfg: PrefillConfig, b: int, h: int, L: Optional[int] = None) -
     out = {}
     for name, tid, d in (("q", TID_Q, cfg.Dk), ("k", TID_K, cfg.Dk)):
         x = _rng(cfg.seed, tid, idx).standard_normal((L, d))
-        x = _l2_normalise(x) if cfg.qk == "l2" else _elu_plus_one(x)
+        if cfg.qk == "l2":
+            x = _l2_normalise(x)
+        elif cfg.qk == "elu1":
+            x = _elu_plus_one(x)
+        elif cfg.qk != "raw":
+            raise ValueError(cfg.qk)
         out[name] = _round(x, cfg.dtype)
     out["v"] = _round(_rng(cfg.seed, TID_V, idx).standard_normal((L, cfg.Dv)), cfg.dtype)
     if cfg.gates:

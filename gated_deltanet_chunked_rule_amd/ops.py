@@ -130,3 +130,32 @@ def gdn_decode_step(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, beta: tor
                                      N, H, D, D, _code(dt), _stream(dev, stream))
     _lib.check(rc, "gdn_decode_step")
     return o
+
+
+def linattn_bidir_workspace_size(B: int, H: int, L: int, D: int, dtype: torch.dtype) -> int:
+    return int(_lib.load().linattn_bidir_workspace_size(B, H, L, D, D, _code(dtype)))
+
+
+def linattn_bidir_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, *, normalize: bool = True,
+                      elu1: bool = True, kv_out: bool = False, o: Optional[torch.Tensor] = None,
+                      workspace: Optional[torch.Tensor] = None, stream=None):
+    """Bidirectional (non-causal) linear attention: KV = sum_n phi(k_n) v_n^T, o_n = phi(q_n)^T KV,
+    divided by phi(q_n) . sum_m phi(k_m) when normalize; phi = elu + 1 when elu1, else identity.
+    Returns o, or (o, kv) with kv [B,H,D,D] fp32 when kv_out."""
+    B, H, L, D = q.shape
+    dev, dt = q.device, q.dtype
+    _req("q", q, (B, H, L, D), dt, dev)
+    _req("k", k, (B, H, L, D), dt, dev)
+    _req("v", v, (B, H, L, D), dt, dev)
+    o = torch.empty_like(v) if o is None else _req("o", o, (B, H, L, D), dt, dev)
+    kv = torch.empty((B, H, D, D), dtype=torch.float32, device=dev) if kv_out else None
+    if workspace is None:
+        workspace = torch.empty(max(linattn_bidir_workspace_size(B, H, L, D, dt), 1), dtype=torch.uint8, device=dev)
+    elif not workspace.is_cuda or not workspace.is_contiguous():
+        raise ValueError("workspace must be a contiguous device tensor")
+    flags = (_lib.GDN_BIDIR_NORMALIZE if normalize else 0) | (_lib.GDN_BIDIR_ELU1 if elu1 else 0)
+    rc = _lib.load().linattn_bidir_fwd(_p(q), _p(k), _p(v), _p(o), _p(kv), B, H, L, D, D, _code(dt), flags,
+                                       _p(workspace), workspace.numel() * workspace.element_size(),
+                                       _stream(dev, stream))
+    _lib.check(rc, "linattn_bidir_fwd")
+    return (o, kv) if kv_out else o

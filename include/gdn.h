@@ -127,6 +127,32 @@ int linattn_prefill_fwd(const void *q, const void *k, const void *v,
                         void *workspace, size_t workspace_bytes, void *stream);
 
 /*
+ * Bidirectional (non-causal) linear attention with a kernel feature map and an optional
+ * normaliser (the datadaily.news overview, section "Linear attention", its linear_attention
+ * function): per batch b and head h, over the whole sequence,
+ *   KV = sum_n phi(k_n) v_n^T  (Dk x Dv),   o_n = KV^T phi(q_n),
+ *   and with GDN_BIDIR_NORMALIZE  o_n /= Z_n,  Z_n = phi(q_n) . sum_m phi(k_m).
+ *   phi(x) = elu(x) + 1 (x + 1 for x > 0, exp(x) otherwise) with GDN_BIDIR_ELU1, else phi(x) = x
+ *   (features already applied by the caller).
+ *   q, k        [B,H,L,Dk] dtype        v, o   [B,H,L,Dv] dtype   (may be NULL when L = 0)
+ *   kv_out      [B,H,Dk,Dv] fp32 (key-major, element [i][j] = KV[i][j]), or NULL; L = 0 gives zeros
+ *   flags       GDN_BIDIR_NORMALIZE | GDN_BIDIR_ELU1 (other bits: GDN_ERR_SHAPE)
+ *   workspace   device buffer, 256-byte aligned, at least linattn_bidir_workspace_size(...) bytes
+ *               (none needed when L = 0); scratch, reusable once the call's work completes
+ * phi is evaluated in fp32 and rounded to dtype before the products; the sums accumulate in
+ * fp32 in a fixed order (results are bitwise reproducible). A zero Z gives IEEE inf/NaN
+ * outputs, as the division does; positive features (GDN_BIDIR_ELU1) keep Z > 0. Runs on
+ * `stream` only.
+ */
+enum { GDN_BIDIR_NORMALIZE = 1, GDN_BIDIR_ELU1 = 2 };
+
+size_t linattn_bidir_workspace_size(int B, int H, int L, int Dk, int Dv, int dtype);
+
+int linattn_bidir_fwd(const void *q, const void *k, const void *v, void *o, float *kv_out,
+                      int B, int H, int L, int Dk, int Dv, int dtype, int flags,
+                      void *workspace, size_t workspace_bytes, void *stream);
+
+/*
  * One recurrent decode step of the gated delta rule for N independent sequences:
  *   q, k [N,H,Dk] dtype;  v, o [N,H,Dv] dtype;  beta, log_alpha [N,H] fp32;
  *   state [N,H,Dk,Dv] fp32, read and overwritten IN PLACE with the state after the token.

@@ -110,3 +110,40 @@ def test_decode_host_validation(lib):
     assert call(o=0x60004) == ALIGN
     assert call(o=0x1000000 + 4096) == ALIAS           # o inside the state
     assert call(q=0x1000000) == ALIAS
+
+
+def _bidir(lib, **kw):
+    a = dict(q=0x10000, k=0x20000000, v=0x40000000, o=0x60000000, kv=None, B=1, H=2, L=300, D=128, dt=0, flags=3,
+             ws=0x100000000, wsb=1 << 30)
+    a.update(kw)
+    return lib.linattn_bidir_fwd(a["q"], a["k"], a["v"], a["o"], a["kv"], a["B"], a["H"], a["L"], a["D"], a["D"],
+                                 a["dt"], a["flags"], a["ws"], a["wsb"], None)
+
+
+def test_bidir_host_validation(lib):
+    assert _bidir(lib, q=None) == NULL
+    assert _bidir(lib, q=None, k=None, v=None, o=None, L=0, ws=None, wsb=0) not in (NULL, ALIGN, ALIAS, WORKSPACE)
+    assert _bidir(lib, flags=4) == SHAPE                        # unknown flag bit
+    assert _bidir(lib, D=96) == SHAPE
+    assert _bidir(lib, dt=2) == DTYPE
+    assert _bidir(lib, o=0x60000008) == ALIGN
+    assert _bidir(lib, kv=0x70000004) == ALIGN
+    assert _bidir(lib, ws=0x100000010) == ALIGN                # workspace needs 256-byte alignment
+    assert _bidir(lib, ws=None) == WORKSPACE
+    need = lib.linattn_bidir_workspace_size(1, 2, 300, 128, 128, 0)
+    assert _bidir(lib, wsb=need - 1) == WORKSPACE
+    assert _bidir(lib, wsb=need) not in (NULL, SHAPE, ALIGN, ALIAS, WORKSPACE)
+    assert _bidir(lib, o=0x20000000 + 256) == ALIAS            # o inside k
+    assert _bidir(lib, kv=0x60000000 + 512) == ALIAS           # kv inside o
+    assert _bidir(lib, ws=0x40000000 - 256) == ALIAS           # workspace runs into v
+
+
+def test_bidir_workspace_size(lib):
+    f = lib.linattn_bidir_workspace_size
+    assert f(1, 2, 0, 128, 128, 0) == 0
+    assert f(1, 2, 10, 96, 96, 0) == 0
+    # one head, one chunk: one block of 64 partial tiles, its key sums, 32 fragments, the key sums
+    assert f(1, 1, 64, 128, 128, 0) == (64 * 1024 + 512 + 32 * 1024 + 512 + 255) // 256 * 256
+    # grows with the number of heads and never shrinks with L
+    assert f(4, 16, 8192, 128, 128, 0) > f(1, 16, 8192, 128, 128, 0)
+    assert f(1, 1, 64 * 1000, 64, 64, 1) >= f(1, 1, 64 * 10, 64, 64, 1)
