@@ -57,21 +57,32 @@ __device__ __forceinline__ uint4 phi16(uint4 x) {
     }
 }
 
-// Stage rows [0, n) of a 64-row chunk (row stride D in global memory) into LDS with row stride
-// KP, phi applied; rows n .. 63 are zero. 256 threads, 16 bytes each per step.
-template <int D, class E, bool ELU1>
-__device__ __forceinline__ void stage_rows(typename E::T* dst, const typename E::T* src, int n, int tid) {
-    using T = typename E::T;
-    constexpr int KP = D + 8;
-    constexpr int EPU = 16 / sizeof(T), UPR = D / EPU;
+// A 64-row chunk (row stride D in global memory) in flight in registers: 256 threads, 16 bytes
+// each per step. Loading the next chunk while the current one is processed keeps more of HBM's
+// latency covered than the workgroups of one CU do alone.
+template <int D, class E>
+struct RowRegs {
+    static constexpr int EPU = 16 / sizeof(typename E::T), UPR = D / EPU, N = CH * UPR / 256;
+    uint4 x[N];
+    // rows [0, n) of src; the others are zero
+    __device__ __forceinline__ void load(const typename E::T* src, int n, int tid) {
 #pragma unroll
-    for (int i = 0; i < CH * UPR / 256; ++i) {
-        const int u = tid + 256 * i, r = u / UPR, cu = u % UPR;
-        uint4 x = {0u, 0u, 0u, 0u};
-        if (r < n) x = phi16<E, ELU1>(*reinterpret_cast<const uint4*>(src + (size_t)r * D + cu * EPU));
-        *reinterpret_cast<uint4*>(dst + r * KP + cu * EPU) = x;
+        for (int i = 0; i < N; ++i) {
+            const int u = tid + 256 * i, r = u / UPR, cu = u % UPR;
+            x[i] = uint4{0u, 0u, 0u, 0u};
+            if (r < n) x[i] = *reinterpret_cast<const uint4*>(src + (size_t)r * D + cu * EPU);
+        }
     }
-}
+    // into LDS with row stride D + 8, phi applied to rows [0, n) (the others stay zero)
+    template <bool ELU1>
+    __device__ __forceinline__ void store(typename E::T* dst, int n, int tid) const {
+#pragma unroll
+        for (int i = 0; i < N; ++i) {
+            const int u = tid + 256 * i, r = u / UPR, cu = u % UPR;
+            *reinterpret_cast<uint4*>(dst + r * (D + 8) + cu * EPU) = r < n ? phi16<E, ELU1>(x[i]) : x[i];
+        }
+    }
+};
 
 // LDS-only workgroup barrier (the waves exchange nothing through global memory)
 __device__ __forceinline__ void lds_sync() {
@@ -120,7 +131,7 @@ size_t bidir_workspace_bytes(long BH, long L, int D, int dtype) {
 // stage 1: per-block sums of phi(K)^T V and of phi(K)
 // ---------------------------------------------------------------------------------------------
 template <int D, class E, bool ELU1>
-__global__ __launch_bounds__(256) void bidir_kv_kernel(const typename E::T* __restrict__ k,
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(sizeof(typename E::T) == 2 ? 3 : 1))) void bidir_kv_kernel(const typename E::T* __restrict__ k,
                                                        const typename E::T* __restrict__ v, unsigned char* ws,
                                                        long L, int cpb, int nb) {
     using T = typename E::T;
@@ -158,12 +169,19 @@ __global__ __launch_bounds__(256) void bidir_kv_kernel(const typename E::T* __re
             t[st] = M::mma(row_frag_raw<E>(R + (16 * st + m) * KP, KB * (dt / FPD), j), sel, f32x4{0.f, 0.f, 0.f, 0.f});
     };
 
+    auto rows_of = [&](long c) { return (int)(L - c * CH < CH ? L - c * CH : CH); };
+    RowRegs<D, E> rk, rv;
+    rk.load(k + ((size_t)bh * L + c_begin * CH) * D, rows_of(c_begin), tid);
+    rv.load(v + ((size_t)bh * L + c_begin * CH) * D, rows_of(c_begin), tid);
     for (long c = c_begin; c < c_end; ++c) {
-        const long t0 = c * CH;
-        const int n = (int)(L - t0 < CH ? L - t0 : CH);
-        const size_t tok0 = (size_t)bh * L + t0;
-        stage_rows<D, E, ELU1>(Kr, k + tok0 * D, n, tid);
-        stage_rows<D, E, false>(Vr, v + tok0 * D, n, tid);
+        const int n = rows_of(c);
+        rk.template store<ELU1>(Kr, n, tid);
+        rv.template store<false>(Vr, n, tid);
+        if (c + 1 < c_end) {   // the next chunk's rows, in flight during this one
+            const size_t tok1 = (size_t)bh * L + (c + 1) * CH;
+            rk.load(k + tok1 * D, rows_of(c + 1), tid);
+            rv.load(v + tok1 * D, rows_of(c + 1), tid);
+        }
         lds_sync();
         // this wave's key tiles -> K^T fragments in LDS (and key sums); its value tiles -> V
         // fragments kept in registers
@@ -226,21 +244,39 @@ __global__ __launch_bounds__(256) void bidir_reduce_kernel(unsigned char* ws, fl
     unsigned char* hb = ws + (size_t)bh * Ly::head(nb);
     if (f < NDT * NKD) {
         const int vt = f / NKD, kd = f % NKD;
+        // the FPD tiles of the fragment summed over the blocks in block order, eight blocks'
+        // loads in flight per step
         f32x4 t[FPD];
 #pragma unroll
-        for (int u = 0; u < FPD; ++u) {
-            const int dt = FPD * kd + u;
-            f32x4 s = {0.f, 0.f, 0.f, 0.f};
-            for (int b = 0; b < nb; ++b) {
-                const f32x4 x = ld_frag<f32x4>(hb + ((size_t)b * NDT * NDT + dt * NDT + vt) * 1024, lane);
-                s = f32x4{s[0] + x[0], s[1] + x[1], s[2] + x[2], s[3] + x[3]};
-            }
-            t[u] = s;
-            if (kv_out) {
-                float* dst = kv_out + (size_t)bh * D * D;
+        for (int u = 0; u < FPD; ++u) t[u] = f32x4{0.f, 0.f, 0.f, 0.f};
+        auto tile_at = [&](int b, int u) {
+            return ld_frag<f32x4>(hb + ((size_t)b * NDT * NDT + (FPD * kd + u) * NDT + vt) * 1024, lane);
+        };
+        int b = 0;
+        for (; b + 8 <= nb; b += 8) {
+            f32x4 x[8][FPD];
 #pragma unroll
-                for (int e = 0; e < 4; ++e) dst[(size_t)(16 * dt + 4 * j + e) * D + 16 * vt + n] = s[e];
+            for (int i = 0; i < 8; ++i)
+#pragma unroll
+                for (int u = 0; u < FPD; ++u) x[i][u] = tile_at(b + i, u);
+#pragma unroll
+            for (int i = 0; i < 8; ++i)
+#pragma unroll
+                for (int u = 0; u < FPD; ++u)
+                    t[u] = f32x4{t[u][0] + x[i][u][0], t[u][1] + x[i][u][1], t[u][2] + x[i][u][2], t[u][3] + x[i][u][3]};
+        }
+        for (; b < nb; ++b)
+#pragma unroll
+            for (int u = 0; u < FPD; ++u) {
+                const f32x4 x = tile_at(b, u);
+                t[u] = f32x4{t[u][0] + x[0], t[u][1] + x[1], t[u][2] + x[2], t[u][3] + x[3]};
             }
+        if (kv_out) {
+            float* dst = kv_out + (size_t)bh * D * D;
+#pragma unroll
+            for (int u = 0; u < FPD; ++u)
+#pragma unroll
+                for (int e = 0; e < 4; ++e) dst[(size_t)(16 * (FPD * kd + u) + 4 * j + e) * D + 16 * vt + n] = t[u][e];
         }
         st_frag(hb + Ly::kvf(nb) + (size_t)f * 1024, lane, M::from_acc(t, 0));
     }
@@ -285,12 +321,19 @@ __global__ __launch_bounds__(256) void bidir_out_kernel(const typename E::T* __r
             kvf[i][kd] = ld_frag<frag>(hb + Ly::kvf(nb) + (size_t)((DW * w + i) * NKD + kd) * 1024, lane);
     if (NORM && tid < D) sks[tid] = reinterpret_cast<const float*>(hb + Ly::ks(nb))[tid];
 
-    for (long c = c_begin; c < c_end; ++c) {
+    auto rows_of = [&](long c) { return (int)(L - c * CH < CH ? L - c * CH : CH); };
+    auto chunk_q = [&](long c) { return q + ((size_t)bh * L + c * CH) * D; };
+    // two register sets: chunk c + 2 is loaded while chunk c + 1 is in flight and c is computed
+    RowRegs<D, E> ra, rb;
+    ra.load(chunk_q(c_begin), rows_of(c_begin), tid);
+    if (c_begin + 1 < c_end) rb.load(chunk_q(c_begin + 1), rows_of(c_begin + 1), tid);
+    auto step = [&](long c, RowRegs<D, E>& rq) {
         const long t0 = c * CH;
-        const int n = (int)(L - t0 < CH ? L - t0 : CH);
+        const int n = rows_of(c);
         const size_t tok0 = (size_t)bh * L + t0;
         if (c > c_begin) lds_sync();   // every wave is done with the previous chunk's rows
-        stage_rows<D, E, ELU1>(Qr, q + tok0 * D, n, tid);
+        rq.template store<ELU1>(Qr, n, tid);
+        if (c + 2 < c_end) rq.load(chunk_q(c + 2), rows_of(c + 2), tid);
         lds_sync();
 #pragma unroll
         for (int rt = 0; rt < 4; ++rt) {
@@ -327,6 +370,10 @@ __global__ __launch_bounds__(256) void bidir_out_kernel(const typename E::T* __r
             }
             __builtin_amdgcn_sched_barrier(0);
         }
+    };
+    for (long c = c_begin; c < c_end; c += 2) {
+        step(c, ra);
+        if (c + 1 < c_end) step(c + 1, rb);
     }
 }
 
