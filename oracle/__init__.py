@@ -15,6 +15,9 @@ this module only compiles it with gcc on first use and marshals NumPy arrays.
     gdn_decode_step(q, k, v, beta, log_alpha, state) -> (o, new_state)
     linattn_bidir(q, k, v, normalize, elu1)    -> (o, kv)        non-causal: KV = sum phi(k) v^T,
                                                                  o = phi(q) KV [/ phi(q).sum phi(k)]
+    gdn_prefill_banded(q, k, v, beta, log_alpha, h0, band)       chunked form with the intra-chunk
+                                                                 inverse cut to `band` blocks below
+                                                                 its diagonal (oracle/banded.py, NumPy)
 
 Shapes: q,k [B,H,L,Dk]; v [B,H,L,Dv]; beta, log_alpha [B,H,L]; h0/h_final [B,H,Dk,Dv]
 (key-major, element [i][j] = S[j][i]); decode: q,k [N,H,Dk], v [N,H,Dv], beta/log_alpha
@@ -189,3 +192,6 @@ def linattn_bidir(q, k, v, normalize: bool = True, elu1: bool = True, nthreads: 
     last_threads = _load().oracle_linattn_bidir(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(kv), B, H, L, Dk, Dv,
                                                 flags, nthreads)
     return o, kv
+
+
+from .banded import gdn_prefill_banded  # noqa: E402,F401
