@@ -128,7 +128,8 @@ def time_loop(torch, fn, steps, warmup):
 # ---------------------------------------------------------------------------------------------
 def bench_prefill(torch, ops, cfg, steps, warmup, gdn=True, verbose=False, variant=None, keep_rate=0.29):
     """variant None: gdn_prefill_fwd (gdn) or plain linattn_prefill_fwd; "gla": linattn_prefill_fwd with
-    per-token gates; "skip": gdn_prefill_skip_fwd with a seeded keep mask at keep_rate."""
+    per-token gates; "skip": gdn_prefill_skip_fwd with a seeded keep mask at keep_rate; "band1":
+    gdn_prefill_banded_fwd with band 1 (flops counted as for the exact rule)."""
     gates = gdn or variant == "gla"
     q, k, v, beta, la, h0 = prefill_device_inputs(torch, cfg, gates=gates, verbose=verbose)
     o = torch.empty_like(v)
@@ -143,6 +144,8 @@ def bench_prefill(torch, ops, cfg, steps, warmup, gdn=True, verbose=False, varia
         kept = int(keep_np.sum())
         keep = torch.from_numpy(keep_np).cuda()
         fn = lambda: ops.gdn_prefill_skip_fwd(q, k, v, beta, la, keep, h0, o=o, h_final=hf, workspace=ws)
+    elif variant == "band1":
+        fn = lambda: ops.gdn_prefill_banded_fwd(q, k, v, beta, la, h0, band=1, o=o, h_final=hf, workspace=ws)
     elif gdn:
         fn = lambda: ops.gdn_prefill_fwd(q, k, v, beta, la, h0, o=o, h_final=hf, workspace=ws)
     elif variant == "gla":
@@ -158,7 +161,8 @@ def bench_prefill(torch, ops, cfg, steps, warmup, gdn=True, verbose=False, varia
     nbytes = prefill_bytes(cfg, gates=gdn) + (cfg.B * cfg.H * cfg.L * 4 if variant == "gla" else 0)
     nbytes += nchunk if variant == "skip" else 0
     res = {
-        "workload": cfg.name + ({"gla": "_gated", "skip": f"_skip_keep{keep_rate}"}.get(variant, "")),
+        "workload": cfg.name + ({"gla": "_gated", "skip": f"_skip_keep{keep_rate}", "band1": "_banded1"}
+                                .get(variant, "")),
         "ms": ms, "tokens_per_s": cfg.B * cfg.L / (ms * 1e-3),
         "alg_tflops": flops / (ms * 1e-3) / 1e12, "mfma_frac": flops / (ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS,
         "alg_bytes": nbytes, "hbm_GBps": nbytes / (ms * 1e-3) / 1e9,
@@ -325,6 +329,10 @@ def main():
         log("[bench] gdn 128K with skipped chunk updates (29% kept)")
         r, b = bench_prefill(torch, ops, cfg, max(5, args.steps // 2), 2, variant="skip")
         components["gdn_128k_skip"] = r
+        del b
+        log("[bench] gdn 128K with the block-adjacent intra-chunk solve (band 1)")
+        r, b = bench_prefill(torch, ops, cfg, max(5, args.steps // 2), 2, variant="band1")
+        components["gdn_128k_banded1"] = r
         del b
 
     cpu, parity = (None, None)

@@ -89,13 +89,15 @@ int validate_prefill(const void* q, const void* k, const void* v, const float* b
 
 int prefill(const void* q, const void* k, const void* v, const float* beta, const float* log_alpha,
             const unsigned char* keep, bool skip, const float* h0, void* o, float* h_final, int B, int H, int L,
-            int Dk, int Dv, int dtype, void* workspace, size_t workspace_bytes, void* stream, bool delta) {
+            int Dk, int Dv, int dtype, void* workspace, size_t workspace_bytes, void* stream, bool delta,
+            int band = 3) {
+    if (band < 0 || band > 3) return GDN_ERR_SHAPE;
     int st = validate_prefill(q, k, v, beta, log_alpha, keep, skip, h0, o, h_final, B, H, L, Dk, Dv, dtype,
                               workspace, workspace_bytes, delta);
     if (st != GDN_OK) return st;
     st = check_device();
     if (st != GDN_OK) return st;
-    return gdn::launch_prefill(q, k, v, beta, log_alpha, keep, h0, o, h_final, B * H, L, Dk, dtype, delta,
+    return gdn::launch_prefill(q, k, v, beta, log_alpha, keep, h0, o, h_final, B * H, L, Dk, dtype, delta, band,
                                workspace, workspace_bytes, static_cast<hipStream_t>(stream)) == 0
                ? GDN_OK
                : GDN_ERR_LAUNCH;
@@ -137,6 +139,13 @@ int gdn_prefill_skip_fwd(const void* q, const void* k, const void* v, const floa
                          int Dk, int Dv, int dtype, void* workspace, size_t workspace_bytes, void* stream) {
     return prefill(q, k, v, beta, log_alpha, keep, true, h0, o, h_final, B, H, L, Dk, Dv, dtype, workspace,
                    workspace_bytes, stream, true);
+}
+
+int gdn_prefill_banded_fwd(const void* q, const void* k, const void* v, const float* beta, const float* log_alpha,
+                           const float* h0, void* o, float* h_final, int B, int H, int L, int Dk, int Dv, int dtype,
+                           int band, void* workspace, size_t workspace_bytes, void* stream) {
+    return prefill(q, k, v, beta, log_alpha, nullptr, false, h0, o, h_final, B, H, L, Dk, Dv, dtype, workspace,
+                   workspace_bytes, stream, true, band);
 }
 
 int linattn_prefill_fwd(const void* q, const void* k, const void* v, const float* beta, const float* log_alpha,

@@ -12,9 +12,10 @@ size_t prefill_workspace_bytes(long BH, long L, int D, int dtype);      // prefe
 size_t prefill_workspace_min_bytes(long BH, long L, int D, int dtype);  // smallest accepted
 
 // keep: [BH][ceil(L/64)] chunk keep mask (nonzero = apply the chunk's state update), or NULL (all)
+// band: 16 x 16 blocks of the intra-chunk inverse kept below its diagonal, 0 .. 3 (3 = exact)
 int launch_prefill(const void* q, const void* k, const void* v, const float* beta, const float* log_alpha,
                    const unsigned char* keep, const float* h0, void* o, float* h_final, int BH, long L, int D,
-                   int dtype, bool delta, void* ws, size_t ws_bytes, hipStream_t stream);
+                   int dtype, bool delta, int band, void* ws, size_t ws_bytes, hipStream_t stream);
 
 // Bidirectional linear attention. kv_out: [BH][D][D] fp32 or NULL. flags bit 0: divide by Z,
 // bit 1: phi = elu + 1 (else identity). The workspace is bidir_workspace_bytes(...) bytes.

@@ -108,6 +108,7 @@ struct PrefArgs {
     int segcap;          // records per slice in the buffer
     const unsigned char* keep;   // [BH][nchk] chunk keep mask, or NULL (keep all)
     int nchk;                    // chunks per slice of the whole sequence
+    int band;                    // 16 x 16 blocks of T kept below the diagonal (3: all, exact)
 };
 
 // inclusive prefix sum over the 64 lanes of a wave
@@ -349,10 +350,11 @@ __global__ __launch_bounds__(256) void prep_kernel(PrefArgs a) {
             }
         }
         // zero the above-diagonal 16 x 16 blocks of T (fragments of 32 tokens read some of them)
-        for (int i = tid; i < 6 * 256; i += 256) {
-            const int b = i >> 8, e = i & 255;
-            const int bi = b < 3 ? 0 : (b < 5 ? 1 : 2), bj = b < 3 ? b + 1 : (b < 5 ? b - 1 : 3);
-            Tm[(16 * bi + (e >> 4)) * AS + 16 * bj + (e & 15)] = 0.f;
+        // and, for the block-adjacent approximation, the blocks more than `band` below it
+#pragma unroll
+        for (int b = 0; b < 16; ++b) {
+            const int bi = b >> 2, bj = b & 3;
+            if (bj > bi || bi - bj > a.band) Tm[(16 * bi + (tid >> 4)) * AS + 16 * bj + (tid & 15)] = 0.f;
         }
         lds_barrier();
         // T = (I + A)^-1, blocked by 16: diagonal blocks by forward substitution (wave i inverts
@@ -376,7 +378,7 @@ __global__ __launch_bounds__(256) void prep_kernel(PrefArgs a) {
 #pragma unroll
         for (int lvl = 1; lvl < 4; ++lvl) {
             lds_barrier();
-            if (w + lvl < 4) inverse_block_t<AS>(Am, Tm, w + lvl, w, j, m);
+            if (w + lvl < 4 && lvl <= a.band) inverse_block_t<AS>(Am, Tm, w + lvl, w, j, m);
         }
         lds_barrier();
         // this wave's token tiles: T rows as fragments (rows 16 rt .. 16 rt + 15 of T are zero
@@ -1051,7 +1053,7 @@ static int launch_prefill_t(PrefArgs a, long nch, size_t ws_bytes, hipStream_t s
 
 int launch_prefill(const void* q, const void* k, const void* v, const float* beta, const float* log_alpha,
                    const unsigned char* keep, const float* h0, void* o, float* h_final, int BH, long L, int D,
-                   int dtype, bool delta, void* ws, size_t ws_bytes, hipStream_t stream) {
+                   int dtype, bool delta, int band, void* ws, size_t ws_bytes, hipStream_t stream) {
     if (L == 0) {
         const size_t n = (size_t)BH * D * D;
         if (h0 == h_final) return 0;
@@ -1059,7 +1061,8 @@ int launch_prefill(const void* q, const void* k, const void* v, const float* bet
         return hipGetLastError() == hipSuccess ? 0 : -1;
     }
     const long nch = (L + CH - 1) / CH;
-    PrefArgs a{q, k, v, beta, log_alpha, h0, o, h_final, static_cast<unsigned char*>(ws), L, BH, 0, 0, 0, keep, (int)nch};
+    PrefArgs a{q, k, v, beta, log_alpha, h0, o, h_final, static_cast<unsigned char*>(ws), L, BH, 0, 0, 0, keep, (int)nch,
+               band};
 #define GDN_PF(DD, EE)                                                                 \
     return delta ? launch_prefill_t<DD, EE, true>(a, nch, ws_bytes, stream)            \
                  : launch_prefill_t<DD, EE, false>(a, nch, ws_bytes, stream)

@@ -53,7 +53,7 @@ def prefill_workspace_size(B: int, H: int, L: int, D: int, dtype: torch.dtype) -
     return int(_lib.load().gdn_prefill_workspace_size(B, H, L, D, D, _code(dtype)))
 
 
-def _prefill(entry, q, k, v, beta, log_alpha, h0, o, h_final, workspace, stream, delta, keep=None):
+def _prefill(entry, q, k, v, beta, log_alpha, h0, o, h_final, workspace, stream, delta, keep=None, band=None):
     B, H, L, D = q.shape
     dev, dt = q.device, q.dtype
     _req("q", q, (B, H, L, D), dt, dev)
@@ -79,8 +79,8 @@ def _prefill(entry, q, k, v, beta, log_alpha, h0, o, h_final, workspace, stream,
     gates = (_p(q), _p(k), _p(v), _p(beta), _p(log_alpha))
     if entry == "gdn_prefill_skip_fwd":
         gates = gates + (_p(keep),)
-    rc = getattr(lib, entry)(*gates, _p(h0), _p(o), _p(h_final),
-                             B, H, L, D, D, _code(dt), _p(workspace),
+    dims = (B, H, L, D, D, _code(dt)) + ((band,) if entry == "gdn_prefill_banded_fwd" else ())
+    rc = getattr(lib, entry)(*gates, _p(h0), _p(o), _p(h_final), *dims, _p(workspace),
                              workspace.numel() * workspace.element_size(), _stream(dev, stream))
     _lib.check(rc, entry)
     return o, h_final
@@ -102,6 +102,17 @@ def gdn_prefill_skip_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, beta
     token still gets its output. keep: uint8 [B,H,ceil(L/64)]. Returns (o, h_final)."""
     return _prefill("gdn_prefill_skip_fwd", q, k, v, beta, log_alpha, h0, o, h_final, workspace, stream, True,
                     keep=keep)
+
+
+def gdn_prefill_banded_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, beta: torch.Tensor,
+                           log_alpha: torch.Tensor, h0: Optional[torch.Tensor] = None, *, band: int = 1,
+                           o: Optional[torch.Tensor] = None, h_final: Optional[torch.Tensor] = None,
+                           workspace: Optional[torch.Tensor] = None, stream=None) -> Tuple[torch.Tensor, torch.Tensor]:
+    """Gated delta rule with the block-adjacent intra-chunk solve: the blocks of each chunk's
+    (I + A)^-1 more than `band` 16 x 16 block rows below the diagonal are zero (band 3: exact).
+    Returns (o, h_final)."""
+    return _prefill("gdn_prefill_banded_fwd", q, k, v, beta, log_alpha, h0, o, h_final, workspace, stream, True,
+                    band=band)
 
 
 def linattn_prefill_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, h0: Optional[torch.Tensor] = None, *,

@@ -111,6 +111,21 @@ int gdn_prefill_skip_fwd(const void *q, const void *k, const void *v,
                          void *workspace, size_t workspace_bytes, void *stream);
 
 /*
+ * The gated delta rule with the block-adjacent intra-chunk solve (SparseGDN article,
+ * fileenergy.com, section on two-level sparsity: the delta system inside a chunk is solved only
+ * across neighbouring blocks, a fixed structured approximation). Each 64-token chunk's inverse
+ * T = (I + A)^-1 is formed in 16 x 16 blocks; blocks more than `band` block rows below the
+ * diagonal are set to zero instead of computed (their terms drop out of W and U), the others are
+ * the exact inverse's blocks. band in 0 .. 3; band = 3 is gdn_prefill_fwd bit for bit (other
+ * values: GDN_ERR_SHAPE). All other arguments, the workspace and the streams as gdn_prefill_fwd.
+ */
+int gdn_prefill_banded_fwd(const void *q, const void *k, const void *v,
+                           const float *beta, const float *log_alpha, const float *h0,
+                           void *o, float *h_final,
+                           int B, int H, int L, int Dk, int Dv, int dtype, int band,
+                           void *workspace, size_t workspace_bytes, void *stream);
+
+/*
  * Chunked prefill of causal linear attention without the delta term (the forpes.ru article on
  * linear attention, its recurrent form and the decay modifications listed after it):
  *   S_t = a_t S_{t-1} + v_t k_t^T,   o_t = S_t q_t,   a_t = exp(log_alpha_t),

@@ -147,3 +147,16 @@ def test_bidir_workspace_size(lib):
     # grows with the number of heads and never shrinks with L
     assert f(4, 16, 8192, 128, 128, 0) > f(1, 16, 8192, 128, 128, 0)
     assert f(1, 1, 64 * 1000, 64, 64, 1) >= f(1, 1, 64 * 10, 64, 64, 1)
+
+
+def test_banded_host_validation(lib):
+    def call(band, **kw):
+        a = dict(q=0x10000, k=0x20000000, v=0x40000000, beta=0x60000000, la=0x60100000, o=0x70000000,
+                 hf=0x7f000000)
+        a.update(kw)
+        return lib.gdn_prefill_banded_fwd(a["q"], a["k"], a["v"], a["beta"], a["la"], None, a["o"], a["hf"], 1, 2,
+                                          200, 128, 128, 0, band, 0x100000000, 1 << 30, None)
+    assert call(-1) == SHAPE and call(4) == SHAPE
+    for band in range(4):
+        assert call(band) not in (NULL, SHAPE, ALIGN, ALIAS, WORKSPACE)
+    assert call(1, beta=None) == NULL
