@@ -4,8 +4,9 @@ Only the tests, ``__graft_entry__.smoke()`` and the CPU-baseline leg of ``bench.
 import this package. The product path (``gated_deltanet_chunked_rule_amd``) never imports
 it, and it never imports the product path: the two share no code.
 
-The arithmetic lives in ``gdn_oracle.c`` (plain C, fp64, OpenMP over independent slices);
-this module only compiles it with gcc on first use and marshals NumPy arrays.
+The token-by-token arithmetic lives in ``gdn_oracle.c`` (plain C, fp64, OpenMP over
+independent slices); this module compiles it with gcc on first use and marshals NumPy arrays.
+The chunked form with the block-adjacent intra-chunk solve is NumPy fp64 in ``banded.py``.
 
     gdn_prefill(q, k, v, beta, log_alpha, h0)  -> (o, h_final)   gated delta rule
     linattn_prefill(q, k, v, h0)               -> (o, h_final)   S_t = S_{t-1} + v_t k_t^T
