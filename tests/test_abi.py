@@ -43,10 +43,16 @@ def test_workspace_size_query(lib):
     rec = f(1, 1, 64, 128, 128, 0)                     # one chunk record of one slice
     assert rec > 0
     assert f(1, 1, 64 * 100, 128, 128, 0) == 100 * rec   # short: the whole sequence, one segment
-    big = f(1, 16, 131072, 128, 128, 0)                  # long: two segment buffers
-    assert big % (2 * 16 * rec) == 0 and big < 2048 * 16 * rec
+    big = f(1, 16, 131072, 128, 128, 0)                  # long: two segment buffers, 256 B of counters
+    assert (big - 256) % (2 * 16 * rec) == 0 and big < 2048 * 16 * rec
     assert 150 << 20 < big <= 200 << 20
     assert f(1, 1, 65, 64, 64, 1) == 2 * f(1, 1, 64, 64, 64, 1)   # a ragged tail costs a whole chunk
+    # smallest accepted workspace: the whole sequence up to two chunks, else two one-chunk
+    # buffers and the counters
+    assert _prefill(lib, L=128, wsb=2 * rec - 1) == WORKSPACE
+    assert _prefill(lib, L=128, wsb=2 * rec) not in (NULL, ALIGN, ALIAS, WORKSPACE)
+    assert _prefill(lib, L=129, wsb=2 * rec) == WORKSPACE
+    assert _prefill(lib, L=129, wsb=2 * rec + 256) not in (NULL, ALIGN, ALIAS, WORKSPACE)
     assert f(1, 2, 0, 128, 128, 0) == 0
     assert f(1, 1, 64, 96, 96, 0) == 0        # unsupported head size
     assert f(1, 1, 64, 128, 64, 0) == 0       # Dk != Dv
