@@ -71,7 +71,7 @@ size_t prefill_record_bytes(int D, int dtype) {
 // SEG_TARGET bytes each, so that the three stages of consecutive segments overlap and the
 // buffers can stay resident in the 256 MB Infinity Cache between the stage that writes them
 // and the stage that reads them.
-static constexpr size_t SEG_TARGET = (size_t)80 << 20;
+static constexpr size_t SEG_TARGET = (size_t)72 << 20;
 static constexpr int NBUF = 2;
 // A segmented call keeps three 32-bit progress counters (prep, chain, output: segments done)
 // after its buffers; the streams wait on them (hipStreamWaitValue32) rather than on events,

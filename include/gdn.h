@@ -64,7 +64,7 @@ const char *gdn_status_string(int status);
  * linattn_prefill_fwd at this shape.
  * The workspace holds the per-chunk operands handed between the three prefill stages. A short
  * sequence is processed in one segment; a long one in segments whose stages overlap on two
- * internal streams, with two segment buffers of about 80 MB each followed by 256 bytes of
+ * internal streams, with two segment buffers of about 72 MB each followed by 256 bytes of
  * progress counters that order the streams. Any workspace that holds the whole sequence's
  * records, or two chunk records per (batch, head) plus those 256 bytes, is accepted; a smaller
  * one just means shorter segments. Returns 0 for an unsupported shape or L = 0. */
