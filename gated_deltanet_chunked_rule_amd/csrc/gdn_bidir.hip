@@ -33,11 +33,16 @@ namespace gdn {
 
 namespace {
 
-// phi: elu(x) + 1 = x + 1 for x > 0, exp(x) otherwise; or the identity
+// phi: elu(x) + 1 = x + 1 for x > 0, exp(x) otherwise; or the identity (both sides evaluated,
+// so no branch)
 template <bool ELU1>
 __device__ __forceinline__ float phi(float x) {
-    if constexpr (ELU1) return x > 0.f ? x + 1.f : __expf(x);
-    else return x;
+    if constexpr (ELU1) {
+        const float e = __expf(fminf(x, 0.f)), p = x + 1.f;
+        return x > 0.f ? p : e;
+    } else {
+        return x;
+    }
 }
 
 // 16-byte group of storage elements -> phi applied -> back to storage
@@ -57,29 +62,45 @@ __device__ __forceinline__ uint4 phi16(uint4 x) {
     }
 }
 
+// Buffer resource over `bytes` bytes at p (raw, stride 0): loads past the end return zero and
+// stores past the end are dropped by the hardware, so the ragged last chunk needs no branches.
+// Branch-free loads and stores let the compiler count outstanding memory operations exactly
+// instead of draining them all (vmcnt(0)) at every join of lane-masked blocks.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t rows_rsrc(const void* p, int bytes) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(p), 0, bytes, 0x00020000);
+}
+
+typedef int i32x4 __attribute__((ext_vector_type(4)));
+typedef int i32x2 __attribute__((ext_vector_type(2)));
+
 // A 64-row chunk (row stride D in global memory) in flight in registers: 256 threads, 16 bytes
 // each per step. Loading the next chunk while the current one is processed keeps more of HBM's
 // latency covered than the workgroups of one CU do alone.
 template <int D, class E>
 struct RowRegs {
-    static constexpr int EPU = 16 / sizeof(typename E::T), UPR = D / EPU, N = CH * UPR / 256;
+    static constexpr int ES = sizeof(typename E::T), EPU = 16 / ES, UPR = D / EPU, N = CH * UPR / 256;
     uint4 x[N];
     // rows [0, n) of src; the others are zero
     __device__ __forceinline__ void load(const typename E::T* src, int n, int tid) {
+        const __amdgpu_buffer_rsrc_t rs = rows_rsrc(src, n * D * ES);
 #pragma unroll
         for (int i = 0; i < N; ++i) {
-            const int u = tid + 256 * i, r = u / UPR, cu = u % UPR;
-            x[i] = uint4{0u, 0u, 0u, 0u};
-            if (r < n) x[i] = *reinterpret_cast<const uint4*>(src + (size_t)r * D + cu * EPU);
+            const int u = tid + 256 * i;
+            const i32x4 v = __builtin_amdgcn_raw_buffer_load_b128(rs, u * 16, 0, 0);
+            x[i] = uint4{(unsigned)v.x, (unsigned)v.y, (unsigned)v.z, (unsigned)v.w};
         }
     }
-    // into LDS with row stride D + 8, phi applied to rows [0, n) (the others stay zero)
+    // into LDS with row stride D + 8, phi applied to rows [0, n), the others zero (masked, not
+    // branched, so that the loads still in flight are not drained here)
     template <bool ELU1>
     __device__ __forceinline__ void store(typename E::T* dst, int n, int tid) const {
 #pragma unroll
         for (int i = 0; i < N; ++i) {
             const int u = tid + 256 * i, r = u / UPR, cu = u % UPR;
-            *reinterpret_cast<uint4*>(dst + r * (D + 8) + cu * EPU) = r < n ? phi16<E, ELU1>(x[i]) : x[i];
+            const unsigned keep = 0u - (unsigned)(r < n);
+            const uint4 y = phi16<E, ELU1>(x[i]);
+            *reinterpret_cast<uint4*>(dst + r * (D + 8) + cu * EPU) =
+                uint4{y.x & keep, y.y & keep, y.z & keep, y.w & keep};
         }
     }
 };
@@ -331,6 +352,7 @@ __global__ __launch_bounds__(256) void bidir_out_kernel(const typename E::T* __r
         const long t0 = c * CH;
         const int n = rows_of(c);
         const size_t tok0 = (size_t)bh * L + t0;
+        const __amdgpu_buffer_rsrc_t ors = rows_rsrc(o + tok0 * D, n * D * (int)sizeof(T));
         if (c > c_begin) lds_sync();   // every wave is done with the previous chunk's rows
         rq.template store<ELU1>(Qr, n, tid);
         if (c + 2 < c_end) rq.load(chunk_q(c + 2), rows_of(c + 2), tid);
@@ -356,16 +378,21 @@ __global__ __launch_bounds__(256) void bidir_out_kernel(const typename E::T* __r
                 z += __shfl_xor(z, 32);
             }
             const int r = 16 * rt + m;   // this lane's token
+            const float s = NORM ? 1.f / z : 1.f;
 #pragma unroll
             for (int i = 0; i < DW; ++i) {
                 f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
                 for (int kd = 0; kd < NKD; ++kd) acc = M::mma(kvf[i][kd], qf[kd], acc);
-                // lane (j, m): o[token r][16 vt + 4 j .. + 3]
-                if (r < n) {
-                    const float s = NORM ? 1.f / z : 1.f;
-                    store4(o + (tok0 + r) * D + 16 * (DW * w + i) + 4 * j,
-                           make_float4(acc[0] * s, acc[1] * s, acc[2] * s, acc[3] * s));
+                // lane (j, m): o[token r][16 vt + 4 j .. + 3]; tokens past the end are dropped
+                const int off = (r * D + 16 * (DW * w + i) + 4 * j) * (int)sizeof(T);
+                if constexpr (sizeof(T) == 2) {
+                    const i32x2 x = {(int)f2bf2(acc[0] * s, acc[1] * s), (int)f2bf2(acc[2] * s, acc[3] * s)};
+                    __builtin_amdgcn_raw_buffer_store_b64(x, ors, off, 0, 0);
+                } else {
+                    const i32x4 x = {__float_as_int(acc[0] * s), __float_as_int(acc[1] * s),
+                                     __float_as_int(acc[2] * s), __float_as_int(acc[3] * s)};
+                    __builtin_amdgcn_raw_buffer_store_b128(x, ors, off, 0, 0);
                 }
             }
             __builtin_amdgcn_sched_barrier(0);
