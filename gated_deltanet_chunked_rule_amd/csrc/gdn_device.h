@@ -52,4 +52,17 @@ __device__ __forceinline__ void store4(uint16_t* p, float4 x) {
 }
 __device__ __forceinline__ void store4(float* p, float4 x) { *reinterpret_cast<float4*>(p) = x; }
 
+// Raw buffer resource over `bytes` bytes at p (stride 0): loads past the end return zero and
+// stores past the end are dropped by the hardware. Staging a ragged chunk through one needs no
+// per-row branch, so all of a thread's row loads are issued back to back and stay in flight
+// together (behind a branch the compiler waits for each load before the next).
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t buffer_rsrc(const void* p, int bytes) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(p), 0, bytes, 0x00020000);
+}
+__device__ __forceinline__ uint4 buffer_load16(__amdgpu_buffer_rsrc_t r, int offset) {
+    typedef int i32x4_t __attribute__((ext_vector_type(4)));
+    const i32x4_t v = __builtin_amdgcn_raw_buffer_load_b128(r, offset, 0, 0);
+    return uint4{(unsigned)v.x, (unsigned)v.y, (unsigned)v.z, (unsigned)v.w};
+}
+
 }  // namespace gdn

@@ -234,18 +234,22 @@ __global__ __launch_bounds__(256) void prep_kernel(PrefArgs a) {
                 a.keep ? (a.keep[(size_t)bh * a.nchk + a.c0 + cl] != 0 ? 1u : 0u) : 1u;
         }
     }
-    {   // K and V rows, 16 bytes per lane; rows past the chunk's end are zero (identity steps)
-        constexpr int EPU = 16 / sizeof(T), UPR = D / EPU;
+    {   // K and V rows, 16 bytes per lane, all loads in flight at once; rows past the chunk's
+        // end read as zero (identity steps)
+        constexpr int EPU = 16 / sizeof(T), UPR = D / EPU, NU = CH * UPR / 256;
+        const __amdgpu_buffer_rsrc_t rk = buffer_rsrc(kp, n * D * (int)sizeof(T));
+        const __amdgpu_buffer_rsrc_t rv = buffer_rsrc(vp, n * D * (int)sizeof(T));
+        uint4 xk[NU], xv[NU];
 #pragma unroll
-        for (int i = 0; i < CH * UPR / 256; ++i) {
+        for (int i = 0; i < NU; ++i) {
+            xk[i] = buffer_load16(rk, (tid + 256 * i) * 16);
+            xv[i] = buffer_load16(rv, (tid + 256 * i) * 16);
+        }
+#pragma unroll
+        for (int i = 0; i < NU; ++i) {
             const int u = tid + 256 * i, r = u / UPR, cu = u % UPR;
-            uint4 xk = {0u, 0u, 0u, 0u}, xv = xk;
-            if (r < n) {
-                xk = *reinterpret_cast<const uint4*>(kp + (size_t)r * D + cu * EPU);
-                xv = *reinterpret_cast<const uint4*>(vp + (size_t)r * D + cu * EPU);
-            }
-            *reinterpret_cast<uint4*>(Kr + r * KP + cu * EPU) = xk;
-            *reinterpret_cast<uint4*>(Vr + r * KP + cu * EPU) = xv;
+            *reinterpret_cast<uint4*>(Kr + r * KP + cu * EPU) = xk[i];
+            *reinterpret_cast<uint4*>(Vr + r * KP + cu * EPU) = xv[i];
         }
     }
     lds_barrier();
@@ -799,36 +803,39 @@ __global__ __launch_bounds__(256) void output_kernel(PrefArgs a) {
     T* op = static_cast<T*>(a.o) + tok0 * D;
     const unsigned char* recB = a.ws + ((size_t)bh * a.segcap + cl) * Ly::REC + Ly::REC_A;
 
-    // this wave's value tiles vt = w, w + 4, ...: fetch the chunk-start state and U fragments
-    // first so their latency overlaps the P computation
-    constexpr int NVW = (NDT + 3) / 4;
-    frag Hc[NVW][NKD], Uf[NVW][NKT];
+    // Q and K rows (16 bytes per lane, rows past the chunk's end read as zero) are requested
+    // first, then the chunk-start state and U fragments of this wave's value tiles vt = w, w + 4,
+    // ...: the rows are waited for before the staging, the fragments stay in flight through the
+    // P computation
+    constexpr int EPU = 16 / sizeof(T), UPR = D / EPU, NU = CH * UPR / 256;
+    uint4 xq[NU], xk[NU];
+    {
+        const __amdgpu_buffer_rsrc_t rq = buffer_rsrc(qp, n * D * (int)sizeof(T));
+        const __amdgpu_buffer_rsrc_t rk = buffer_rsrc(kp, n * D * (int)sizeof(T));
 #pragma unroll
-    for (int iv = 0; iv < NVW; ++iv) {
-        const int vt = w + 4 * iv;
-        if (vt < NDT) {
-#pragma unroll
-            for (int kd = 0; kd < NKD; ++kd)
-                Hc[iv][kd] = ld_frag<frag>(recB + Ly::B_H + (size_t)(vt * NKD + kd) * Ly::FR, lane);
-#pragma unroll
-            for (int kt = 0; kt < NKT; ++kt)
-                Uf[iv][kt] = ld_frag<frag>(recB + Ly::B_U + (size_t)(vt * NKT + kt) * Ly::FR, lane);
+        for (int i = 0; i < NU; ++i) {
+            xq[i] = buffer_load16(rq, (tid + 256 * i) * 16);
+            xk[i] = buffer_load16(rk, (tid + 256 * i) * 16);
         }
     }
-    {   // Q and K tiles into LDS, 16 bytes per lane; rows past the chunk's end are zero
-        constexpr int EPU = 16 / sizeof(T);          // elements per 16-byte unit
-        constexpr int UPR = D / EPU;                 // units per row
+    static_assert(NDT % 4 == 0, "every wave owns the same number of value tiles");
+    constexpr int NVW = NDT / 4;
+    frag Hc[NVW][NKD], Uf[NVW][NKT];
 #pragma unroll
-        for (int i = 0; i < CH * UPR / 256; ++i) {
-            const int u = tid + 256 * i, r = u / UPR, cu = u % UPR;
-            uint4 xq = {0u, 0u, 0u, 0u}, xk = xq;
-            if (r < n) {
-                xq = *reinterpret_cast<const uint4*>(qp + (size_t)r * D + cu * EPU);
-                xk = *reinterpret_cast<const uint4*>(kp + (size_t)r * D + cu * EPU);
-            }
-            *reinterpret_cast<uint4*>(Qr + r * KP + cu * EPU) = xq;
-            *reinterpret_cast<uint4*>(Kr + r * KP + cu * EPU) = xk;
-        }
+    for (int iv = 0; iv < NVW; ++iv) {   // no branch here: the loads above must stay in flight
+        const int vt = w + 4 * iv;
+#pragma unroll
+        for (int kd = 0; kd < NKD; ++kd)
+            Hc[iv][kd] = ld_frag<frag>(recB + Ly::B_H + (size_t)(vt * NKD + kd) * Ly::FR, lane);
+#pragma unroll
+        for (int kt = 0; kt < NKT; ++kt)
+            Uf[iv][kt] = ld_frag<frag>(recB + Ly::B_U + (size_t)(vt * NKT + kt) * Ly::FR, lane);
+    }
+#pragma unroll
+    for (int i = 0; i < NU; ++i) {
+        const int u = tid + 256 * i, r = u / UPR, cu = u % UPR;
+        *reinterpret_cast<uint4*>(Qr + r * KP + cu * EPU) = xq[i];
+        *reinterpret_cast<uint4*>(Kr + r * KP + cu * EPU) = xk[i];
     }
     if (w == 0) {
         float la = 0.f;
