@@ -126,17 +126,22 @@ def time_loop(torch, fn, steps, warmup):
 # ---------------------------------------------------------------------------------------------
 # components
 # ---------------------------------------------------------------------------------------------
-def bench_prefill(torch, ops, cfg, steps, warmup, gdn=True, verbose=False, variant=None, keep_rate=0.29):
+def bench_prefill(torch, ops, cfg, steps, warmup, gdn=True, verbose=False, variant=None, keep_rate=0.29,
+                  one_segment=False):
     """variant None: gdn_prefill_fwd (gdn) or plain linattn_prefill_fwd; "gla": linattn_prefill_fwd with
     per-token gates; "skip": gdn_prefill_skip_fwd with a seeded keep mask at keep_rate; "band1":
-    gdn_prefill_banded_fwd with band 1 (flops counted as for the exact rule)."""
+    gdn_prefill_banded_fwd with band 1 (flops counted as for the exact rule). one_segment: hand over a
+    workspace for the whole sequence, so that the call runs its three kernels once each on one stream
+    (the launch that hardware-counter passes use: they serialise dispatches, which the multi-stream
+    segment pipeline's value waits do not allow)."""
     gates = gdn or variant == "gla"
     q, k, v, beta, la, h0 = prefill_device_inputs(torch, cfg, gates=gates, verbose=verbose)
     o = torch.empty_like(v)
     hf = torch.empty((cfg.B, cfg.H, cfg.Dk, cfg.Dv), device="cuda")
-    ws = torch.empty(ops.prefill_workspace_size(cfg.B, cfg.H, cfg.L, cfg.Dk, q.dtype), dtype=torch.uint8,
-                     device="cuda")
     nchk = (cfg.L + 63) // 64
+    wsb = (ops.prefill_workspace_size(1, 1, 64, cfg.Dk, q.dtype) * cfg.B * cfg.H * nchk if one_segment
+           else ops.prefill_workspace_size(cfg.B, cfg.H, cfg.L, cfg.Dk, q.dtype))
+    ws = torch.empty(wsb, dtype=torch.uint8, device="cuda")
     nchunk = cfg.B * cfg.H * nchk
     kept = nchunk
     if variant == "skip":
@@ -259,6 +264,8 @@ def main():
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--profile-steps", type=int, default=0,
                     help="only run this many prefill steps after warm-up (for profilers), no JSON")
+    ap.add_argument("--one-segment", action="store_true",
+                    help="with --profile-steps: whole-sequence workspace, one launch of each kernel per call")
     ap.add_argument("--profile-decode", type=int, default=0,
                     help="only run this many decode steps (for profilers), no JSON")
     ap.add_argument("--copy-calibrate", type=int, default=0, metavar="BYTES",
@@ -295,7 +302,8 @@ def main():
         return
     if args.profile_steps:
         log("generating inputs")
-        res, bufs = bench_prefill(torch, ops, cfg, args.profile_steps, args.warmup, verbose=True)
+        res, bufs = bench_prefill(torch, ops, cfg, args.profile_steps, args.warmup, verbose=True,
+                                  one_segment=args.one_segment)
         log(f"profiled {args.profile_steps} steps: {res['ms']:.3f} ms/step")
         return
 
@@ -362,7 +370,7 @@ def main():
         "mfma": {"alg_tflops": res["alg_tflops"], "peak_tflops": PEAK_BF16_TFLOPS, "frac": res["mfma_frac"]},
         # one gdn_prefill_fwd call is the unit: its three kernels run concurrently on three
         # streams, so the call (timed with HIP events on the caller's stream) is the launch
-        "roofline": {"bound": "hbm", "kernel": "gdn_prefill_fwd (prep, chain, output kernels)",
+        "roofline": {"bound": "hbm", "kernel": "gdn_prefill_fwd (prep and chain kernels)",
                      "achieved": res["hbm_GBps"], "peak": PEAK_HBM_GBPS, "unit": "GB/s",
                      "frac": res["hbm_frac"], "traffic": traffic, "alg_bytes_per_launch": res["alg_bytes"]},
         "cpu_baseline": cpu,

@@ -64,5 +64,24 @@ __device__ __forceinline__ uint4 buffer_load16(__amdgpu_buffer_rsrc_t r, int off
     const i32x4_t v = __builtin_amdgcn_raw_buffer_load_b128(r, offset, 0, 0);
     return uint4{(unsigned)v.x, (unsigned)v.y, (unsigned)v.z, (unsigned)v.w};
 }
+__device__ __forceinline__ uint2 buffer_load8(__amdgpu_buffer_rsrc_t r, int offset) {
+    typedef int i32x2_t __attribute__((ext_vector_type(2)));
+    const i32x2_t v = __builtin_amdgcn_raw_buffer_load_b64(r, offset, 0, 0);
+    return uint2{(unsigned)v.x, (unsigned)v.y};
+}
+__device__ __forceinline__ unsigned buffer_load4(__amdgpu_buffer_rsrc_t r, int offset) {
+    return (unsigned)__builtin_amdgcn_raw_buffer_load_b32(r, offset, 0, 0);
+}
+// 4 consecutive elements from fp32 (bf16: 8 bytes, round to nearest even; fp32: 16 bytes)
+__device__ __forceinline__ void buffer_store4(__amdgpu_buffer_rsrc_t r, int offset, float4 x, uint16_t) {
+    typedef int i32x2_t __attribute__((ext_vector_type(2)));
+    const i32x2_t v = {(int)f2bf2(x.x, x.y), (int)f2bf2(x.z, x.w)};
+    __builtin_amdgcn_raw_buffer_store_b64(v, r, offset, 0, 0);
+}
+__device__ __forceinline__ void buffer_store4(__amdgpu_buffer_rsrc_t r, int offset, float4 x, float) {
+    typedef int i32x4_t __attribute__((ext_vector_type(4)));
+    const i32x4_t v = {__float_as_int(x.x), __float_as_int(x.y), __float_as_int(x.z), __float_as_int(x.w)};
+    __builtin_amdgcn_raw_buffer_store_b128(v, r, offset, 0, 0);
+}
 
 }  // namespace gdn

@@ -3,7 +3,7 @@
 // The SparseGDN article (fileenergy.com, section "Why GDN prefill is expensive") splits chunked
 // GDN prefill into three sources of work: the intra-chunk delta-system solve, the sequential
 // chunk-to-chunk state pass for each head, and the outputs computed from every chunk's start
-// state. The three kernels below are those three stages.
+// state. Here the first is one kernel and the other two share the second.
 //
 // Per chunk of C = 64 tokens, with g the inclusive cumulative log-gate (restarting at each
 // chunk) and the key-major state H (Dk x Dv) at chunk start, the token recurrence
@@ -19,13 +19,15 @@
 // exact zeros instead of overflowing.
 //
 //   prep_kernel   (one workgroup per chunk and head, fully parallel): g, A, T = (I + A)^-1 by
-//                 a blocked inverse in LDS, -W, Khat^T and Ut, written as MFMA-ready fragments.
-//   chain_kernel  (one workgroup per head and 32 value columns): the sequential pass. The fp32
+//                 a blocked inverse in LDS, then -W, Khat^T, Ut, the gated causal P^T and Q,
+//                 written as MFMA-ready fragments into the chunk's record.
+//   chain_kernel  (one workgroup per head and 16 value columns): the sequential pass. The fp32
 //                 state stays in accumulator registers for the whole sequence while loader
-//                 waves stream the next chunks' operands into an LDS ring; per chunk it emits
-//                 the chunk-start state and U as fragments for the output stage.
-//   output_kernel (one workgroup per chunk and head): P = (Q K^T) gated and masked, then
-//                 O^T = H^T (e^g Q)^T + U^T P^T, stored four value columns per lane.
+//                 waves stream the next chunks' records into an LDS ring; output waves form
+//                 O^T = e^g H^T Q^T + U^T P^T from the state and U the compute waves hand them,
+//                 and store waves write it.
+// Long sequences run as segments through a pair of workspace buffers: prep of later segments
+// on a side stream beside the chain of the current one on the caller's stream.
 // Plain linear attention uses the same kernels with T = I, W = 0, Ut = V, g = 0.
 #include <mutex>
 #include <type_traits>
@@ -46,18 +48,22 @@ struct Layout {
     static constexpr int NKT = CH / KB;  // fragments along the chunk's tokens
     static constexpr int NDT = D / 16;   // 16-wide tiles along d
     static constexpr int FR = 1024;      // bytes per fragment
-    // prep record: -W [rt 4][NKD], Khat^T [dt NDT][NKT], Ut accumulators [vt NDT][rt 4][lane] (4 x T), decay
+    // chunk record, written by prep and read by the chain:
+    //   -W [rt 4][NKD] and Khat^T [dt NDT][NKT] fragments (streamed whole into the chain's LDS),
+    //   Ut accumulators [vt NDT][rt 4][lane] (4 x T), Q fragments [rt 4][NKD] (k = d, column =
+    //   token), the gated causal P^T fragments [rt 4][NKT] (kt <= kbmax(rt) written), e^g per
+    //   token, the chunk decay e^{g_C} and the keep flag
     static constexpr size_t A_W = 0;
     static constexpr size_t A_KH = A_W + (size_t)4 * NKD * FR;
     static constexpr size_t A_UT = A_KH + (size_t)NDT * NKT * FR;
-    static constexpr size_t A_DEC = A_UT + (size_t)NDT * 4 * 64 * 4 * sizeof(typename E::T);
-    static constexpr size_t A_KEEP = A_DEC + 4;   // chunk keep flag (u32, 0 = skipped state update)
-    static constexpr size_t REC_A = (A_KEEP + 4 + 255) / 256 * 256;
-    // chain record: chunk-start state [cg NDT][NKD], U [cg NDT][NKT]
-    static constexpr size_t B_H = 0;
-    static constexpr size_t B_U = (size_t)NDT * NKD * FR;
-    static constexpr size_t REC_B = B_U + (size_t)NDT * NKT * FR;
-    static constexpr size_t REC = REC_A + REC_B;
+    static constexpr size_t A_Q = A_UT + (size_t)NDT * 4 * 64 * 4 * sizeof(typename E::T);
+    static constexpr size_t A_P = A_Q + (size_t)4 * NKD * FR;
+    static constexpr size_t A_EG = A_P + (size_t)4 * NKT * FR;
+    static constexpr size_t A_DEC = A_EG + (size_t)CH * 4;
+    static constexpr size_t A_KEEP = A_DEC + 4;   // u32, 0 = skipped state update
+    static constexpr size_t REC = (A_KEEP + 4 + 255) / 256 * 256;
+    // last d-fragment of P^T's token-column tile rt that holds any s <= r
+    static constexpr int kbmax(int rt) { return (16 * rt + 15) / KB; }
 };
 
 size_t prefill_record_bytes(int D, int dtype) {
@@ -113,6 +119,8 @@ struct PrefArgs {
     const unsigned char* keep;   // [BH][nchk] chunk keep mask, or NULL (keep all)
     int nchk;                    // chunks per slice of the whole sequence
     int band;                    // 16 x 16 blocks of T kept below the diagonal (3: all, exact)
+    unsigned* flags;             // segment pipeline counters, or NULL (the call is one segment)
+    int sgi;                     // this launch's segment
 };
 
 // inclusive prefix sum over the 64 lanes of a wave
@@ -159,6 +167,64 @@ __device__ __forceinline__ void lds_barrier() {
 }
 
 // ---------------------------------------------------------------------------------------------
+// segment pipeline counters
+// ---------------------------------------------------------------------------------------------
+// A segmented call keeps 32-bit words in the workspace after its segment buffers: for each stage
+// the number of segments it has finished, the chain's arrival count and an error word. The side
+// streams wait on the counts with hipStreamWaitValue32; the chain kernel polls the prep count
+// itself and publishes its own, so that consecutive chain launches follow each other on their
+// stream with nothing queued between them.
+enum : int { FL_PREP = 0, FL_CHAIN = 1, FL_OUT = 2, FL_ERR = 3, FL_ARRIVE = 16, FL_WORDS = 64 };
+// about 10 s of the 100 MHz constant clock (s_memrealtime)
+static constexpr unsigned long long WAIT_TICKS = 1000000000ull;
+
+// Wait (the whole wave, polling one word) until flags[which] >= target, then acquire, so that
+// this wave's later loads see what the stage that published the count wrote. A wait longer than
+// WAIT_TICKS gives up and sets the error word rather than spin for ever; the call's outputs and
+// final state then come out NaN.
+__device__ __forceinline__ void wait_count(unsigned* flags, int which, unsigned target) {
+    auto rd = [&] { return __hip_atomic_load(flags + which, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM); };
+    if (rd() < target) {
+        const unsigned long long t0 = wall_clock64();
+        while (rd() < target) {
+            __builtin_amdgcn_s_sleep(1);
+            if (wall_clock64() - t0 > WAIT_TICKS) {
+                __hip_atomic_store(flags + FL_ERR, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
+                break;
+            }
+            // after one timeout the call's result is lost anyway: later waits end at once
+            if (__hip_atomic_load(flags + FL_ERR, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM)) break;
+        }
+    }
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+}
+
+// Count this wave in among the `waves` waves of a stage launch that only read the segment's
+// buffer; the last to arrive resets the arrival count (launches of a stage run in order on one
+// stream) and publishes `value`. The count licenses the next writer of the buffer, so it only has
+// to follow the wave's reads: the caller has waited for all of them (vmcnt 0), and nothing this
+// launch wrote is needed by that writer, so no cache write-back is needed either.
+__device__ __forceinline__ void publish_read(unsigned* flags, int which, unsigned value, unsigned waves, int lane) {
+    if (lane == 0) {
+        unsigned* arrive = flags + FL_ARRIVE + which;
+        const unsigned n = __hip_atomic_fetch_add(arrive, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        if (n + 1 == waves) {
+            __hip_atomic_store(arrive, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            __hip_atomic_store(flags + which, value, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
+        }
+    }
+}
+
+// nonzero once a wait of this call has timed out (scalar, for uniform branches)
+__device__ __forceinline__ unsigned call_failed(const PrefArgs& a) {
+    return a.flags ? __builtin_amdgcn_readfirstlane(
+                         __hip_atomic_load(a.flags + FL_ERR, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM))
+                   : 0u;
+}
+
+__global__ void flags_reset_kernel(unsigned* flags) { flags[threadIdx.x] = 0u; }
+
+// ---------------------------------------------------------------------------------------------
 // stage 1: intra-chunk delta-system solve and WY/UT transform
 // ---------------------------------------------------------------------------------------------
 // Work split of the prep workgroup's four waves. The d extent is cut into fragment groups of
@@ -176,9 +242,10 @@ struct PrepCfg {
     static constexpr int AS = CH + 4;                            // A / T row stride (floats)
     static constexpr size_t ROWS = (size_t)CH * KP * sizeof(typename E::T);
     static constexpr size_t MAT = (size_t)CH * AS * 4;
-    // region 0: K rows, then T; region 1: V rows, then A
+    // region 0: K rows, then T; region 1: V rows, then A; four per-token arrays; Q rows
     static constexpr size_t REGION = ((ROWS > MAT ? ROWS : MAT) + 15) / 16 * 16;
-    static constexpr size_t LDS = 2 * REGION + 4 * CH * 4;
+    static constexpr size_t O_Q = 2 * REGION + 4 * CH * 4;
+    static constexpr size_t LDS = O_Q + (ROWS + 15) / 16 * 16;
 };
 
 template <int D, class E, bool DELTA>
@@ -200,6 +267,7 @@ __global__ __launch_bounds__(256) void prep_kernel(PrefArgs a) {
     float* sbe = sg + CH;                                             // -beta e^g
     float* sb = sbe + CH;                                             // beta
     float* skh = sb + CH;                                             // e^{g_C - g}
+    T* Qr = reinterpret_cast<T*>(smem + P::O_Q);                      // [CH][KP] Q rows
 
     const int cl = blockIdx.x, bh = blockIdx.y;     // chunk within the segment, slice
     // The wave index lives in a scalar register so that every branch on it (token tiles,
@@ -212,6 +280,7 @@ __global__ __launch_bounds__(256) void prep_kernel(PrefArgs a) {
     const long t0 = (long)(a.c0 + cl) * CH;
     const int n = (int)min((long)CH, a.L - t0);
     const size_t tok0 = (size_t)bh * a.L + t0;
+    const T* qp = static_cast<const T*>(a.q) + tok0 * D;
     const T* kp = static_cast<const T*>(a.k) + tok0 * D;
     const T* vp = static_cast<const T*>(a.v) + tok0 * D;
     unsigned char* rec = a.ws + ((size_t)bh * a.segcap + cl) * Ly::REC;
@@ -224,35 +293,84 @@ __global__ __launch_bounds__(256) void prep_kernel(PrefArgs a) {
         }
         const float g = wave_scan(la, lane);
         const float gC = __shfl(g, 63);
+        const float eg = __expf(g);
         sg[lane] = g;
         sb[lane] = bt;
-        sbe[lane] = -bt * __expf(g);
+        sbe[lane] = -bt * eg;
         skh[lane] = __expf(gC - g);
+        reinterpret_cast<float*>(rec + Ly::A_EG)[lane] = eg;
         if (lane == 0) {
             *reinterpret_cast<float*>(rec + Ly::A_DEC) = a.log_alpha ? __expf(gC) : 1.f;
             *reinterpret_cast<unsigned*>(rec + Ly::A_KEEP) =
                 a.keep ? (a.keep[(size_t)bh * a.nchk + a.c0 + cl] != 0 ? 1u : 0u) : 1u;
         }
     }
-    {   // K and V rows, 16 bytes per lane, all loads in flight at once; rows past the chunk's
-        // end read as zero (identity steps)
+    {   // Q, K and V rows, 16 bytes per lane, all loads in flight at once; rows past the
+        // chunk's end read as zero (identity steps)
         constexpr int EPU = 16 / sizeof(T), UPR = D / EPU, NU = CH * UPR / 256;
+        const __amdgpu_buffer_rsrc_t rq = buffer_rsrc(qp, n * D * (int)sizeof(T));
         const __amdgpu_buffer_rsrc_t rk = buffer_rsrc(kp, n * D * (int)sizeof(T));
         const __amdgpu_buffer_rsrc_t rv = buffer_rsrc(vp, n * D * (int)sizeof(T));
-        uint4 xk[NU], xv[NU];
+        uint4 xq[NU], xk[NU], xv[NU];
 #pragma unroll
         for (int i = 0; i < NU; ++i) {
             xk[i] = buffer_load16(rk, (tid + 256 * i) * 16);
             xv[i] = buffer_load16(rv, (tid + 256 * i) * 16);
+            xq[i] = buffer_load16(rq, (tid + 256 * i) * 16);
         }
 #pragma unroll
         for (int i = 0; i < NU; ++i) {
             const int u = tid + 256 * i, r = u / UPR, cu = u % UPR;
             *reinterpret_cast<uint4*>(Kr + r * KP + cu * EPU) = xk[i];
             *reinterpret_cast<uint4*>(Vr + r * KP + cu * EPU) = xv[i];
+            *reinterpret_cast<uint4*>(Qr + r * KP + cu * EPU) = xq[i];
         }
     }
     lds_barrier();
+
+    // Q as MFMA fragments for the chain's H^T Q^T (one contiguous 1 KB load each there)
+    for (int f = w; f < 4 * NKD; f += 4)
+        st_frag(rec + Ly::A_Q + (size_t)f * Ly::FR, lane,
+                row_frag_raw<E>(Qr + (16 * (f / NKD) + m) * KP, (f % NKD) * KB, j));
+    // The chain computes the outputs; what it needs of the chunk beyond the state is the gated
+    // causal P^T. Fragment (rt, kt) packs the tiles (st, rt), st = FPD kt .. FPD kt + FPD - 1,
+    // whose lane (j, n) holds P[r = 16 rt + n][s = 16 st + 4 j + e] = exp(g_r - g_s) q_r.k_s for
+    // s <= r, else 0: the B operand (k = s, column r) of O^T += U^T P^T. Only kt <= kbmax(rt)
+    // is written (the rest is all zero and never read).
+    {
+        constexpr int NPFR = [] {
+            int c = 0;
+            for (int rt = 0; rt < 4; ++rt) c += Ly::kbmax(rt) + 1;
+            return c;
+        }();
+        for (int f = w; f < NPFR; f += 4) {   // w is scalar: so is every branch below
+            int rt = 0, kt = f;
+            while (kt > Ly::kbmax(rt)) { kt -= Ly::kbmax(rt) + 1; ++rt; }
+            f32x4 t[FPD];
+#pragma unroll
+            for (int i = 0; i < FPD; ++i) {
+                const int st = FPD * kt + i;
+                t[i] = f32x4{0.f, 0.f, 0.f, 0.f};
+                if (st <= rt) {
+                    // gates first, read for every lane (selected below, no lane-masked branch)
+                    const int r = 16 * rt + m;
+                    const float4 gs = *reinterpret_cast<const float4*>(sg + 16 * st + 4 * j);
+                    const float gr = sg[r];
+                    const int s0 = 16 * st + 4 * j;   // s <= r: exp(g_r - g_s); else exp(0), masked below
+                    const float ge[4] = {__expf(s0 <= r ? gr - gs.x : 0.f), __expf(s0 + 1 <= r ? gr - gs.y : 0.f),
+                                         __expf(s0 + 2 <= r ? gr - gs.z : 0.f), __expf(s0 + 3 <= r ? gr - gs.w : 0.f)};
+#pragma unroll
+                    for (int kd = 0; kd < NKD; ++kd)
+                        t[i] = M::mma(row_frag_raw<E>(Kr + (16 * st + m) * KP, kd * KB, j),
+                                      row_frag_raw<E>(Qr + (16 * rt + m) * KP, kd * KB, j), t[i]);
+#pragma unroll
+                    for (int e = 0; e < 4; ++e)   // t finite: the 0/1 factor masks exactly
+                        t[i][e] *= ge[e] * (float)(s0 + e <= r);
+                }
+            }
+            st_frag(rec + Ly::A_P + (size_t)(rt * NKT + kt) * Ly::FR, lane, M::from_acc(t, 0));
+        }
+    }
 
     // Rows to columns on the matrix core: kc[i][st] is the accumulator tile of tokens 16 st ..
     // 16 st + 15 and d-tile dt = FPD grp + i of K (lane (j, n): K[16 st + 4 j + e][16 dt + n]);
@@ -433,20 +551,28 @@ __global__ __launch_bounds__(256) void prep_kernel(PrefArgs a) {
 // The fp32 state of the column group (Dk x 16) is split by rows between the two compute waves,
 // each holding its half in accumulator registers for the whole sequence; per chunk they exchange
 // their fp32 partial products W H through LDS (4 KB each), so each wave's chain step is half the
-// MFMA work. The compute waves touch no global memory in their loop: the two loader waves
-//   - stream each chunk's -W and Khat^T fragments (contiguous at the start of its prep record,
-//     shared by all column groups of the slice), the group's Ut tiles and the decay into a ring
-//     of NS LDS slots, NS - 1 chunks ahead, and
-//   - store the chunk-start state and U fragments the compute waves leave in an LDS staging
-//     area (three steps deep) to the workspace for the output stage.
-// A CU's vector-memory path serves all its waves in order, so stores issued by the compute
-// waves would queue behind the loaders' streaming loads and stall the sequential chain; issued
-// by the loaders, they only delay loads that are steps ahead of their use.
+// MFMA work. The two loader waves stream each chunk's -W and Khat^T fragments (contiguous at
+// the start of its record, shared by all column groups of the slice) and the group's Ut tiles
+// into a ring of NS LDS slots, NS - 1 chunks ahead; they issue nothing else, so their waits are
+// fixed counts.
+//
+// The workgroup also produces the chunk's outputs for its 16 columns,
+//     O^T = e^g (H^T Q^T) + U^T P^T,
+// from the chunk-start state and U. Two further output waves do it: the compute waves stage
+// their bf16 state half and U fragments in LDS (three steps deep), and each output wave
+// finishes two token tiles ({0, 3} or {1, 2}: equal causal P work) one step later with the Q
+// and P^T fragments and e^g of the record, read into registers NSET chunks ahead. The finished
+// tiles go through LDS to two store waves, which write them to memory a step later: a wave's
+// loads and stores share one in-order completion count, so loads issued after stores could not
+// be waited for without also waiting for the stores. Waves are dealt to the four SIMDs in
+// order: compute 0, 1 and output 2, 3 on their own SIMDs, the loaders 4, 5 and store waves
+// 6, 7 beside them (they mostly wait). Where the staging does not fit beside the ring (fp32 at
+// Dk = 128) the compute waves form and store the outputs themselves, handing each other their
+// halves of H^T Q^T through LDS; that puts the output work on the chain's dependence path.
 template <int D, class E, bool DELTA>
 struct ChainCfg {
     using Ly = Layout<D, E>;
     static constexpr int NCW = D / 16;                                   // workgroups per slice
-    static constexpr int THREADS = 256;                                  // 2 compute waves, then 2 loaders
     static constexpr size_t SLOT = Ly::A_UT;                             // -W and Khat^T fragments
     static constexpr int NBLK = (int)(SLOT / 1024);                      // 1 KB wave blocks per slot
     static constexpr int BPW = NBLK / 2;                                 // blocks per loader wave
@@ -454,30 +580,33 @@ struct ChainCfg {
     static constexpr size_t UTSUB = (size_t)4 * 64 * 4 * sizeof(typename E::T);  // Ut bytes of 16 columns
     static constexpr int UTL = (int)(UTSUB / 2048);                      // Ut 1 KB loads per loader wave
     static_assert(UTSUB % 2048 == 0, "Ut splits into whole blocks per loader wave");
-    static constexpr size_t USLOT = UTSUB + 256;                         // Ut, then the decay (a dword per lane)
-    static constexpr int DMA_OPS = BPW + UTL + 1;                        // loads per loader wave and chunk
+    static constexpr int DMA_OPS = BPW + UTL;                            // loads per loader wave and chunk
     static constexpr size_t XHALF = (size_t)4 * 64 * 16;                 // one wave's partial W H
     static constexpr size_t XBYTES = DELTA ? (size_t)2 * 2 * XHALF : 0; // [step parity][half]
-    // per compute wave and step: its Dk/2 rows of the state (Ly::NKD / 2 fragments) and half of
-    // the U fragments
-    static constexpr int STG = Ly::NKD / 2 + Ly::NKT / 2;
-    static constexpr size_t STB = (size_t)STG * 1024;
-    // the loaders store them when the staging area fits beside two or more slots (not for fp32 at
-    // Dk = 128, whose compute waves store their own fragments)
-    static constexpr bool SL = (SLOT + USLOT) * 2 + XBYTES + 3 * 2 * STB <= 156 * 1024;
-    static constexpr size_t STAGE = SL ? 3 * 2 * STB : 0;                // [step % 3][wave][fragment]
-    static constexpr size_t FIXED = XBYTES + STAGE;
-    static constexpr int NS = (SLOT + USLOT) * 4 + FIXED <= 156 * 1024 ? 4 : ((SLOT + USLOT) * 3 + FIXED <= 156 * 1024 ? 3 : 2);
+    static constexpr size_t LDS_MAX = 160 * 1024;                        // gfx950: 160 KB per workgroup
+    // output waves: one step's staged bf16 H (both halves) and U fragments, three steps deep
+    static constexpr size_t STB = (size_t)(Ly::NKD + Ly::NKT) * 1024;
+    // and the finished output tiles for the store waves: [step parity][rt][lane], 4 elements
+    static constexpr size_t OTB = (size_t)4 * 64 * 4 * sizeof(typename E::T);
+    static constexpr size_t STAGE = 3 * STB + 2 * OTB;
+    static constexpr bool OUTW = (SLOT + UTSUB) * 2 + XBYTES + STAGE <= LDS_MAX;
+    static constexpr int THREADS = OUTW ? 512 : 256;
+    // waves per workgroup that read the records after the compute waves' last barrier and so
+    // count themselves in for the segment's "read" count: the loaders, and the output waves
+    static constexpr unsigned READERS = OUTW ? 4 : 2;
+    // outputs in the compute waves instead: H^T Q^T halves [parity][writer][tile][lane]
+    static constexpr size_t XOBYTES = (size_t)2 * 2 * 2 * 64 * 16;
+    static constexpr size_t FIXED = XBYTES + (OUTW ? STAGE : XOBYTES);
+    static constexpr int NS = (SLOT + UTSUB) * 4 + FIXED <= LDS_MAX ? 4 : ((SLOT + UTSUB) * 3 + FIXED <= LDS_MAX ? 3 : 2);
     static constexpr size_t O_X = NS * SLOT;                             // LDS offsets of the areas
-    static constexpr size_t O_UT = O_X + XBYTES;
-    static constexpr size_t O_ST = O_UT + NS * USLOT;
-    static constexpr size_t LDS = O_ST + STAGE;
-    static_assert(LDS <= 156 * 1024, "chain LDS");
-    static constexpr int INFLIGHT = NS - 2;                              // chunks still loading at a barrier
-    // a loader's vector-memory operations after chunk c + 1's loads when it waits for them:
-    // that chunk's iteration's stores, then INFLIGHT whole iterations
-    static constexpr int LST = SL ? STG : 0;                             // stores per loader iteration
-    static constexpr int WAITN = LST + INFLIGHT * (DMA_OPS + LST);
+    static constexpr size_t O_ST = O_X + XBYTES;                         // staging (output waves) or
+    static constexpr size_t O_OT = O_ST + 3 * STB;                       //   and their output tiles, or
+    static constexpr size_t O_XO = O_X + XBYTES;                         // H^T Q^T halves (in-wave outputs)
+    static constexpr size_t O_UT = O_X + FIXED;
+    static constexpr size_t LDS = O_UT + NS * UTSUB;
+    static_assert(LDS <= LDS_MAX, "chain LDS");
+    // a loader's loads still in flight when it waits for chunk c + 1: those of the NS - 2 later chunks
+    static constexpr int WAITN = (NS - 2) * DMA_OPS;
     static_assert(WAITN < 64, "vmcnt is 6 bits");
 };
 
@@ -496,7 +625,7 @@ __device__ __forceinline__ void wait_vmcnt() {
 // Direct-to-LDS load of 16 bytes per lane: lane l's bytes land at LDS address lds_base + 16 l.
 // Issued as inline assembly so that the compiler does not track it: the loader waves account
 // for these loads themselves (wait_vmcnt), and the compute waves, which only read LDS, must not
-// be made to wait on them or on their own global stores.
+// be made to wait on them.
 // M0 is a reserved register, so clang warns about the clobber; the kernels that call dma16 use
 // M0 for nothing else, and the asm sets it before each load.
 #pragma clang diagnostic push
@@ -506,12 +635,6 @@ __device__ __forceinline__ void dma16(const void* src, unsigned lds_base) {
     asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(src), "s"(lds_base)
                  : "memory", "m0");
 }
-// Same with 4 bytes per lane: lane l's dword lands at lds_base + 4 l.
-__device__ __forceinline__ void dma4(const void* src, unsigned lds_base) {
-    lds_base = __builtin_amdgcn_readfirstlane(lds_base);
-    asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dword %0, off" ::"v"(src), "s"(lds_base)
-                 : "memory", "m0");
-}
 #pragma clang diagnostic pop
 
 __device__ __forceinline__ unsigned lds_addr(const void* p) {
@@ -519,8 +642,7 @@ __device__ __forceinline__ unsigned lds_addr(const void* p) {
 }
 
 // Loader wave lw's share of chunk c's loads into slot s: BPW 1 KB blocks of the -W / Khat^T
-// fragments (interleaved with the other loader's), its half of the Ut tiles, and the decay
-// (both loaders load it; same bytes, same place).
+// fragments (interleaved with the other loader's) and its half of the Ut tiles.
 template <int D, class E, bool DELTA>
 __device__ __forceinline__ void chain_issue(unsigned char* smem, const unsigned char* rec, int s, int cg, int lw,
                                             int lane) {
@@ -532,47 +654,27 @@ __device__ __forceinline__ void chain_issue(unsigned char* smem, const unsigned 
         const unsigned blk = (unsigned)(lw + 2 * i) * 1024u;
         dma16(rec + blk + lane * 16, base + blk);
     }
-    const unsigned ubase = lds_addr(smem + C::O_UT + (size_t)s * C::USLOT);
+    const unsigned ubase = lds_addr(smem + C::O_UT + (size_t)s * C::UTSUB);
     const unsigned char* ut = rec + Ly::A_UT + (size_t)cg * C::UTSUB;
 #pragma unroll
     for (int i = 0; i < C::UTL; ++i) {
         const unsigned blk = (unsigned)(lw * C::UTL + i) * 1024u;
         dma16(ut + blk + lane * 16, ubase + blk);
     }
-    dma4(rec + Ly::A_DEC + 4 * (lane & 1), ubase + (unsigned)C::UTSUB);   // decay, keep flag, decay, ...
-}
-
-// Loader wave lw's stores of step c's staged fragments (those of compute wave lw): its rows of
-// the chunk-start state, then its U fragments (kt = lw, lw + 2, ...).
-template <int D, class E, bool DELTA>
-__device__ __forceinline__ void chain_store(const unsigned char* smem, unsigned char* recB, int c, int cg, int lw,
-                                            int lane) {
-    using C = ChainCfg<D, E, DELTA>;
-    using Ly = Layout<D, E>;
-    constexpr int HKD = Ly::NKD / 2;
-    const unsigned char* st = smem + C::O_ST + ((size_t)(c % 3) * 2 + lw) * C::STB;
-#pragma unroll
-    for (int i = 0; i < C::STG; ++i) {
-        const uint4 x = *reinterpret_cast<const uint4*>(st + (size_t)i * 1024 + lane * 16);
-        const size_t off = i < HKD ? Ly::B_H + (size_t)(cg * Ly::NKD + lw * HKD + i) * Ly::FR
-                                   : Ly::B_U + (size_t)(cg * Ly::NKT + lw + 2 * (i - HKD)) * Ly::FR;
-        *reinterpret_cast<uint4*>(recB + off + lane * 16) = x;
-    }
 }
 
 // Loader wave lw (0 or 1) of a chain workgroup. Iteration c (after barrier c - 1): issue chunk
 // c + NS - 1 into the slot of chunk c - 1 (whose fragments the compute waves read before
-// barrier c - 1), store step c - 2's staged fragments (complete since barrier c - 1), wait for
-// chunk c + 1 (read by the compute waves after barrier c), barrier c. Every iteration issues the
-// same operations, so the wait is a fixed count once the first NS iterations are past (those
-// drain fully). After the last step, one more barrier and the last two steps' stores.
+// barrier c - 1), wait for chunk c + 1 (read by the compute waves after barrier c), barrier c.
+// In a segmented call it first waits for the segment's prep count, and at the end counts itself
+// in for the chain's: the count tells the prep stage that this launch has read its buffer.
 template <int D, class E, bool DELTA>
-__device__ __forceinline__ void chain_loader(unsigned char* smem, const unsigned char* rec0, int nch, int cg, int lw,
-                                             int lane) {
+__device__ __forceinline__ void chain_loader(const PrefArgs& a, unsigned char* smem, const unsigned char* rec0, int nch,
+                                             int cg, int lw, int lane) {
     using Ly = Layout<D, E>;
     using C = ChainCfg<D, E, DELTA>;
     constexpr int NS = C::NS;
-    auto recb = [&](int c) { return const_cast<unsigned char*>(rec0) + (size_t)c * Ly::REC + Ly::REC_A; };
+    if (a.flags) wait_count(a.flags, FL_PREP, (unsigned)a.sgi + 1);   // the segment's records are written
     for (int c = 0; c < NS - 1; ++c)
         chain_issue<D, E, DELTA>(smem, rec0 + (size_t)min(c, nch - 1) * Ly::REC, c, cg, lw, lane);
     wait_vmcnt<0>();
@@ -580,33 +682,69 @@ __device__ __forceinline__ void chain_loader(unsigned char* smem, const unsigned
     for (int c = 0; c < nch; ++c) {
         const int cn = c + NS - 1;   // always issued (clamped to the last chunk): fixed counts
         chain_issue<D, E, DELTA>(smem, rec0 + (size_t)min(cn, nch - 1) * Ly::REC, cn % NS, cg, lw, lane);
-        // step c - 2's fragments (before step 0: step 0's record, rewritten with the real ones
-        // two iterations later by this same wave, in order)
-        if constexpr (C::SL) chain_store<D, E, DELTA>(smem, recb(max(c - 2, 0)), max(c - 2, 0), cg, lw, lane);
-        if (c < NS)
-            wait_vmcnt<0>();
-        else
-            wait_vmcnt<C::WAITN>();
+        wait_vmcnt<C::WAITN>();
         lds_barrier();
     }
-    lds_barrier();   // the compute waves' last step is staged
-    if constexpr (C::SL)
-        for (int c = max(nch - 2, 0); c < nch; ++c) chain_store<D, E, DELTA>(smem, recb(c), c, cg, lw, lane);
+    lds_barrier();   // matches the compute waves' last barrier
     wait_vmcnt<0>();   // no LDS write may land after the workgroup ends
+    if (a.flags) publish_read(a.flags, FL_CHAIN, (unsigned)a.sgi + 1, C::READERS * a.BH * C::NCW, lane);
+}
+
+// Output tile (O^T, lane (j, m): O[token 16 rt + m][16 cg + 4 j .. + 3]) of token tile rt of the
+// segment's chunk c; tokens past the end of the sequence are dropped.
+template <int D, class E>
+__device__ __forceinline__ void store_out(const PrefArgs& a, int bh, int cg, int c, int rt, int lane, const f32x4& v) {
+    using T = typename E::T;
+    const long t0 = (long)(a.c0 + c) * CH;
+    const int n = (int)min((long)CH, a.L - t0);
+    const __amdgpu_buffer_rsrc_t ro =
+        buffer_rsrc(static_cast<T*>(a.o) + ((size_t)bh * a.L + t0) * D, n * D * (int)sizeof(T));
+    const int j = lane >> 4, m = lane & 15;
+    buffer_store4(ro, ((16 * rt + m) * D + 16 * cg + 4 * j) * (int)sizeof(T), make_float4(v[0], v[1], v[2], v[3]), T{});
+}
+
+// Packed output tile element of this lane: 4 elements of T (8 or 16 bytes)
+template <class E>
+using OutPack = typename std::conditional<sizeof(typename E::T) == 2, uint2, uint4>::type;
+template <class E>
+__device__ __forceinline__ OutPack<E> pack_out(const f32x4& v) {
+    if constexpr (sizeof(typename E::T) == 2)
+        return uint2{f2bf2(v[0], v[1]), f2bf2(v[2], v[3])};
+    else
+        return uint4{__float_as_uint(v[0]), __float_as_uint(v[1]), __float_as_uint(v[2]), __float_as_uint(v[3])};
+}
+template <int D, class E>
+__device__ __forceinline__ void store_packed(const PrefArgs& a, int bh, int cg, int c, int rt, int lane, OutPack<E> x) {
+    using T = typename E::T;
+    const long t0 = (long)(a.c0 + c) * CH;
+    const int n = (int)min((long)CH, a.L - t0);
+    const __amdgpu_buffer_rsrc_t ro =
+        buffer_rsrc(static_cast<T*>(a.o) + ((size_t)bh * a.L + t0) * D, n * D * (int)sizeof(T));
+    const int j = lane >> 4, m = lane & 15;
+    const int off = ((16 * rt + m) * D + 16 * cg + 4 * j) * (int)sizeof(T);
+    if constexpr (sizeof(T) == 2) {
+        typedef int i32x2_t __attribute__((ext_vector_type(2)));
+        __builtin_amdgcn_raw_buffer_store_b64(i32x2_t{(int)x.x, (int)x.y}, ro, off, 0, 0);
+    } else {
+        typedef int i32x4_t __attribute__((ext_vector_type(4)));
+        __builtin_amdgcn_raw_buffer_store_b128(i32x4_t{(int)x.x, (int)x.y, (int)x.z, (int)x.w}, ro, off, 0, 0);
+    }
 }
 
 // Compute wave HH of a chain workgroup: it owns state rows [HH Dk/2, (HH + 1) Dk/2) of column
 // group cg. Per chunk c:
-//   A  Hf = bf16(H), staged for the output stage; partial product P_HH = (-W)[:, half] Hf, with
-//      Ut folded into the accumulators of token tiles 2 HH and 2 HH + 1; P_HH -> LDS;
-//      H *= chunk decay.
-//   B  U = P_HH + P_other (fp32 addition is commutative, so both waves hold the same U), its
-//      fragments half staged; H += Khat^T[half, :] bf16(U); then chunk c + 1's -W and Khat^T
-//      fragments are read from its slot (complete since barrier c), so neither product of the
-//      next step waits on LDS.
+//   A  Hf = bf16(H); partial product P_HH = (-W)[:, half] Hf, with Ut folded into the
+//      accumulators of token tiles 2 HH and 2 HH + 1; P_HH -> LDS; H *= chunk decay.
+//   B  U = P_HH + P_other (fp32 addition is commutative, so both waves hold the same U);
+//      H += Khat^T[half, :] bf16(U); chunk c + 1's -W and Khat^T fragments are read from its
+//      slot (complete since barrier c), so neither product of the next step waits on LDS.
+//   With output waves, bf16(H) is staged in A and bf16(U) in B. Without, B ends with the
+//      outputs: H^T Q^T over the wave's half of d for the four token tiles, the other wave's
+//      two to LDS, its own two scaled by e^g and U^T P^T added; the other wave's half for its
+//      own tiles of chunk c - 1 (stored before barrier c) completes chunk c - 1's outputs.
 // One barrier per step, between A and B: the partial products alternate between two LDS areas
 // by step parity, so an area is rewritten only after the partner has passed the next barrier.
-// Ut and the decay are read in A, before the barrier after which their slot may be refilled.
+// Ut is read in A, before the barrier after which its slot may be refilled.
 template <int D, class E, bool DELTA, int HH>
 __device__ __forceinline__ void chain_compute(const PrefArgs& a, unsigned char* smem, const unsigned char* rec0,
                                               int nch, int bh, int cg, int lane) {
@@ -617,8 +755,13 @@ __device__ __forceinline__ void chain_compute(const PrefArgs& a, unsigned char* 
     using frag = typename M::frag;
     constexpr int NKD = Ly::NKD, NKT = Ly::NKT, NDT = Ly::NDT, NS = C::NS;
     constexpr int HKD = NKD / 2, HDT = NDT / 2;   // fragments / tiles of one row half
+    // token tiles this wave finishes, and the P^T fragments they need
+    constexpr int R[2] = {HH == 0 ? 0 : 1, HH == 0 ? 3 : 2};
+    constexpr int RO[2] = {HH == 0 ? 1 : 0, HH == 0 ? 2 : 3};   // the other wave's
+    constexpr int NP0 = Ly::kbmax(R[0]) + 1, NPF = NP0 + Ly::kbmax(R[1]) + 1;
     f32x4* X0 = reinterpret_cast<f32x4*>(smem + C::O_X);                   // [parity][half][rt][lane]
     constexpr size_t XPAR = 2 * C::XHALF / sizeof(f32x4);
+    f32x4* XO = reinterpret_cast<f32x4*>(smem + C::O_XO);                  // [parity][writer][tile][lane]
     const int j = lane >> 4, m = lane & 15;
     const int col = 16 * cg + m;
     f32x4 H[HDT];   // lane (j, m): H[16 (HH HDT + t) + 4 j + e][col]
@@ -627,6 +770,36 @@ __device__ __forceinline__ void chain_compute(const PrefArgs& a, unsigned char* 
 #pragma unroll
         for (int e = 0; e < 4; ++e)
             H[t][e] = a.h0 ? a.h0[((size_t)bh * D + 16 * (HH * HDT + t) + 4 * j + e) * D + col] : 0.f;
+
+    // what a step reads from global memory, two chunks ahead
+    struct Pre {
+        frag qf[4][HKD];   // Q fragments, k = d over this wave's half, column = token
+        frag pf[NPF];      // P^T fragments of tiles R[0], R[1]
+        float eg[2];       // e^{g_r} of this lane's token in tiles R[0], R[1]
+        unsigned dec, keep;
+    };
+    auto load = [&](Pre& p, int c) {
+        c = min(c, nch - 1);   // past the segment: the last chunk again (unused)
+        const __amdgpu_buffer_rsrc_t rr = buffer_rsrc(rec0 + (size_t)c * Ly::REC, (int)Ly::REC);
+        // the decay and keep flag first: a step needs them first, and waits are in issue order
+        p.dec = buffer_load4(rr, (int)Ly::A_DEC);
+        p.keep = buffer_load4(rr, (int)Ly::A_KEEP);
+        if constexpr (C::OUTW) return;
+#pragma unroll
+        for (int rt = 0; rt < 4; ++rt)
+#pragma unroll
+            for (int kk = 0; kk < HKD; ++kk)
+                p.qf[rt][kk] = __builtin_bit_cast(
+                    frag, buffer_load16(rr, (int)Ly::A_Q + (rt * NKD + HH * HKD + kk) * Ly::FR + lane * 16));
+#pragma unroll
+        for (int i = 0; i < NPF; ++i) {
+            const int rt = i < NP0 ? R[0] : R[1], kt = i < NP0 ? i : i - NP0;
+            p.pf[i] = __builtin_bit_cast(frag, buffer_load16(rr, (int)Ly::A_P + (rt * NKT + kt) * Ly::FR + lane * 16));
+        }
+#pragma unroll
+        for (int i = 0; i < 2; ++i) p.eg[i] = __uint_as_float(buffer_load4(rr, (int)Ly::A_EG + (16 * R[i] + m) * 4));
+    };
+
     // -W and Khat^T fragments of the chunk in slot s
     frag wf[4 * HKD], kf[HDT * NKT];
     auto read_slot = [&](int s) {
@@ -644,26 +817,36 @@ __device__ __forceinline__ void chain_compute(const PrefArgs& a, unsigned char* 
             for (int kt = 0; kt < NKT; ++kt)
                 kf[t * NKT + kt] = ld_frag<frag>(slot + Ly::A_KH + (size_t)((HH * HDT + t) * NKT + kt) * Ly::FR, lane);
     };
+
+    f32x4 on[2];     // chunk c - 1's own tiles without the other wave's half of H^T Q^T
+    float egp[2];    // and their e^g
+    // the records may be read only after this barrier: before it the loaders wait for the
+    // segment's prep count (and acquire)
     lds_barrier();
+    // NSET register sets: chunk c's loads are issued at the start of step c - NSET + 1 (two
+    // for fp32 at Dk = 128, whose fragments are twice the size: four would spill)
+    constexpr int NSET = sizeof(T) == 4 && D == 128 ? 2 : 4;
+    Pre S[NSET];
+#pragma unroll
+    for (int i = 0; i < NSET - 1; ++i) load(S[i], i);
+    const float bad = call_failed(a) ? __builtin_nanf("") : 0.f;   // NaN outputs after a timed-out wait
     read_slot(0);
-    for (int c = 0; c < nch; ++c) {
+
+    auto step = [&](int c, Pre& S, Pre& N) {
+        load(N, c + NSET - 1);   // into the set of chunk c - 1, read in the step before
         f32x4* X = X0 + (c & 1) * XPAR;
-        const unsigned char* us = smem + C::O_UT + (size_t)(c % NS) * C::USLOT;
+        const unsigned char* us = smem + C::O_UT + (size_t)(c % NS) * C::UTSUB;
         const T* ut = reinterpret_cast<const T*>(us);   // [rt][lane][4]
-        unsigned char* st = smem + C::O_ST + ((size_t)(c % 3) * 2 + HH) * C::STB;
-        unsigned char* recB = const_cast<unsigned char*>(rec0) + (size_t)c * Ly::REC + Ly::REC_A;
+        unsigned char* st = smem + C::O_ST + (size_t)(c % 3) * C::STB;   // (output waves)
         frag Hf[HKD];
 #pragma unroll
         for (int kk = 0; kk < HKD; ++kk) {
             Hf[kk] = M::from_acc(H, kk);
-            if constexpr (C::SL)
-                st_frag(st + (size_t)kk * 1024, lane, Hf[kk]);
-            else
-                st_frag(recB + Ly::B_H + (size_t)(cg * NKD + HH * HKD + kk) * Ly::FR, lane, Hf[kk]);
+            if constexpr (C::OUTW) st_frag(st + (size_t)(HH * HKD + kk) * 1024, lane, Hf[kk]);
         }
         f32x4 P[4];
-        const float dec = *reinterpret_cast<const float*>(us + C::UTSUB);
-        const unsigned keep = __builtin_amdgcn_readfirstlane(*reinterpret_cast<const unsigned*>(us + C::UTSUB + 4));
+        const float dec = __uint_as_float(S.dec);
+        const unsigned keep = __builtin_amdgcn_readfirstlane(S.keep);
         if constexpr (DELTA) {
 #pragma unroll
             for (int rt = 0; rt < 4; ++rt) {
@@ -706,12 +889,8 @@ __device__ __forceinline__ void chain_compute(const PrefArgs& a, unsigned char* 
 #pragma unroll
         for (int kt = 0; kt < NKT; ++kt) {
             Uf[kt] = M::from_acc(U, kt);
-            if (kt % 2 == HH) {
-                if constexpr (C::SL)
-                    st_frag(st + (size_t)(HKD + kt / 2) * 1024, lane, Uf[kt]);
-                else
-                    st_frag(recB + Ly::B_U + (size_t)(cg * NKT + kt) * Ly::FR, lane, Uf[kt]);
-            }
+            if constexpr (C::OUTW)
+                if (kt % 2 == HH) st_frag(st + (size_t)(NKD + kt) * 1024, lane, Uf[kt]);
         }
         if (keep) {   // a skipped chunk's update leaves the decayed state (its U still feeds its outputs)
 #pragma unroll
@@ -720,8 +899,65 @@ __device__ __forceinline__ void chain_compute(const PrefArgs& a, unsigned char* 
                 for (int t = 0; t < HDT; ++t) H[t] = M::mma(kf[t * NKT + kt], Uf[kt], H[t]);
         }
         read_slot((c + 1) % NS);
+        __builtin_amdgcn_sched_barrier(0);
+        if constexpr (C::OUTW) return;
+        // outputs of chunk c: H^T Q^T over this wave's half of d
+        f32x4 qh[4];
+#pragma unroll
+        for (int rt = 0; rt < 4; ++rt) {
+            qh[rt] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int kk = 0; kk < HKD; ++kk) qh[rt] = M::mma(Hf[kk], S.qf[rt][kk], qh[rt]);
+        }
+        f32x4* xo = XO + ((size_t)((c & 1) * 2 + HH) * 2) * 64;
+        xo[lane] = qh[RO[0]];
+        xo[64 + lane] = qh[RO[1]];
+        f32x4 oc[2];
+#pragma unroll
+        for (int i = 0; i < 2; ++i) {
+            const float g = S.eg[i];
+            oc[i] = f32x4{qh[R[i]][0] * g, qh[R[i]][1] * g, qh[R[i]][2] * g, qh[R[i]][3] * g};
+#pragma unroll
+            for (int kt = 0; kt <= Ly::kbmax(R[i]); ++kt) oc[i] = M::mma(Uf[kt], S.pf[i == 0 ? kt : NP0 + kt], oc[i]);
+        }
+        // chunk c - 1: the other wave's half, stored before barrier c
+        if (c > 0) {
+            const f32x4* xp = XO + ((size_t)(((c - 1) & 1) * 2 + 1 - HH) * 2) * 64;
+#pragma unroll
+            for (int i = 0; i < 2; ++i) {
+                const f32x4 x = xp[i * 64 + lane];
+                store_out<D, E>(a, bh, cg, c - 1, R[i], lane,
+                                f32x4{on[i][0] + egp[i] * x[0] + bad, on[i][1] + egp[i] * x[1] + bad,
+                                      on[i][2] + egp[i] * x[2] + bad, on[i][3] + egp[i] * x[3] + bad});
+            }
+        }
+#pragma unroll
+        for (int i = 0; i < 2; ++i) {
+            on[i] = oc[i];
+            egp[i] = S.eg[i];
+        }
+        __builtin_amdgcn_sched_barrier(0);
+    };
+    for (int c = 0; c < nch; c += NSET) {
+#pragma unroll
+        for (int u = 0; u < NSET; ++u)
+            if (u == 0 || c + u < nch) step(c + u, S[u], S[(u + NSET - 1) % NSET]);
     }
-    lds_barrier();   // the last step's fragments are staged for the loaders
+    lds_barrier();   // the last step's H^T Q^T halves (or staged fragments) are in LDS
+    if constexpr (!C::OUTW) {
+        const int c = nch - 1;
+        const f32x4* xp = XO + ((size_t)((c & 1) * 2 + 1 - HH) * 2) * 64;
+#pragma unroll
+        for (int i = 0; i < 2; ++i) {
+            const f32x4 x = xp[i * 64 + lane];
+            store_out<D, E>(a, bh, cg, c, R[i], lane,
+                            f32x4{on[i][0] + egp[i] * x[0] + bad, on[i][1] + egp[i] * x[1] + bad,
+                                  on[i][2] + egp[i] * x[2] + bad, on[i][3] + egp[i] * x[3] + bad});
+        }
+    }
+    if (call_failed(a))
+#pragma unroll
+        for (int t = 0; t < HDT; ++t) H[t] = f32x4{__builtin_nanf(""), __builtin_nanf(""), __builtin_nanf(""), __builtin_nanf("")};
 #pragma unroll
     for (int t = 0; t < HDT; ++t)
 #pragma unroll
@@ -729,10 +965,124 @@ __device__ __forceinline__ void chain_compute(const PrefArgs& a, unsigned char* 
             a.h_final[((size_t)bh * D + 16 * (HH * HDT + t) + 4 * j + e) * D + col] = H[t][e];
 }
 
-// One workgroup per CU (its LDS ring). Waves 0 and 1 compute (row half w), waves 2 and 3 load
-// and store; the roles run separate loops with the same barrier sequence.
+// Output wave HH of a chain workgroup (with output waves): it finishes token tiles {0, 3}
+// (HH = 0) or {1, 2} of every chunk of the column group. Iteration c follows barrier c of the
+// compute waves, after which step c - 1's staged bf16 H and U are complete: O^T of chunk c - 1 =
+// e^g (H^T Q^T) + U^T P^T over all of d, then the loads of chunk c - 1 + NSET into the register
+// set just used, then the tiles into LDS for the store waves (the last chunk's it stores
+// itself). Its barrier sequence is the compute waves': the first, one per step, the last.
+template <int D, class E, bool DELTA, int HH>
+__device__ __forceinline__ void chain_output(const PrefArgs& a, unsigned char* smem, const unsigned char* rec0,
+                                             int nch, int bh, int cg, int lane) {
+    using M = MM<E>;
+    using Ly = Layout<D, E>;
+    using C = ChainCfg<D, E, DELTA>;
+    using frag = typename M::frag;
+    constexpr int NKD = Ly::NKD, NKT = Ly::NKT;
+    constexpr int R[2] = {HH == 0 ? 0 : 1, HH == 0 ? 3 : 2};
+    constexpr int NP0 = Ly::kbmax(R[0]) + 1, NPF = NP0 + Ly::kbmax(R[1]) + 1;
+    const int m = lane & 15;
+    struct Pre {
+        frag qf[2][NKD];   // Q fragments of tiles R[0], R[1] (k = d, column = token)
+        frag pf[NPF];      // P^T fragments of tiles R[0], R[1]
+        float eg[2];       // e^{g_r} of this lane's token in tiles R[0], R[1]
+    };
+    auto load = [&](Pre& p, int c) {
+        c = min(c, nch - 1);   // past the segment: the last chunk again (unused)
+        const __amdgpu_buffer_rsrc_t rr = buffer_rsrc(rec0 + (size_t)c * Ly::REC, (int)Ly::REC);
+#pragma unroll
+        for (int i = 0; i < 2; ++i)
+#pragma unroll
+            for (int kd = 0; kd < NKD; ++kd)
+                p.qf[i][kd] = __builtin_bit_cast(
+                    frag, buffer_load16(rr, (int)Ly::A_Q + (R[i] * NKD + kd) * Ly::FR + lane * 16));
+#pragma unroll
+        for (int i = 0; i < NPF; ++i) {
+            const int rt = i < NP0 ? R[0] : R[1], kt = i < NP0 ? i : i - NP0;
+            p.pf[i] = __builtin_bit_cast(frag, buffer_load16(rr, (int)Ly::A_P + (rt * NKT + kt) * Ly::FR + lane * 16));
+        }
+#pragma unroll
+        for (int i = 0; i < 2; ++i) p.eg[i] = __uint_as_float(buffer_load4(rr, (int)Ly::A_EG + (16 * R[i] + m) * 4));
+    };
+    float bad = 0.f;
+    OutPack<E> res[2];
+    auto out = [&](int c, const Pre& S) {
+        const unsigned char* st = smem + C::O_ST + (size_t)(c % 3) * C::STB;
+        frag Hf[NKD], Uf[NKT];
+#pragma unroll
+        for (int kd = 0; kd < NKD; ++kd) Hf[kd] = ld_frag<frag>(st + (size_t)kd * 1024, lane);
+#pragma unroll
+        for (int kt = 0; kt < NKT; ++kt) Uf[kt] = ld_frag<frag>(st + (size_t)(NKD + kt) * 1024, lane);
+#pragma unroll
+        for (int i = 0; i < 2; ++i) {
+            f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int kd = 0; kd < NKD; ++kd) acc = M::mma(Hf[kd], S.qf[i][kd], acc);
+            const float g = S.eg[i];
+            acc = f32x4{acc[0] * g, acc[1] * g, acc[2] * g, acc[3] * g};
+#pragma unroll
+            for (int kt = 0; kt <= Ly::kbmax(R[i]); ++kt) acc = M::mma(Uf[kt], S.pf[i == 0 ? kt : NP0 + kt], acc);
+            res[i] = pack_out<E>(f32x4{acc[0] + bad, acc[1] + bad, acc[2] + bad, acc[3] + bad});
+        }
+    };
+    constexpr int NSET = 3;
+    lds_barrier();   // the records may be read from here on (the loaders have seen the prep count)
+    bad = call_failed(a) ? __builtin_nanf("") : 0.f;
+    Pre S[NSET];
+#pragma unroll
+    for (int i = 0; i < NSET; ++i) load(S[i], i);
+    // iteration cc = 0 .. nch: barrier cc (cc = nch: the compute waves' last), then chunk cc - 1
+    for (int c = 0; c <= nch; c += NSET) {
+#pragma unroll
+        for (int u = 0; u < NSET; ++u) {
+            const int cc = c + u;
+            if (u == 0 || cc <= nch) {
+                lds_barrier();
+                if (cc > 0) {
+                    Pre& P = S[(u + NSET - 1) % NSET];   // chunk cc - 1's set
+                    out(cc - 1, P);
+                    load(P, cc - 1 + NSET);
+                    if (cc < nch) {
+                        OutPack<E>* ot = reinterpret_cast<OutPack<E>*>(smem + C::O_OT + (size_t)((cc - 1) & 1) * C::OTB);
+                        ot[R[0] * 64 + lane] = res[0];
+                        ot[R[1] * 64 + lane] = res[1];
+                    } else {
+                        store_packed<D, E>(a, bh, cg, cc - 1, R[0], lane, res[0]);
+                        store_packed<D, E>(a, bh, cg, cc - 1, R[1], lane, res[1]);
+                    }
+                }
+                __builtin_amdgcn_sched_barrier(0);
+            }
+        }
+    }
+    wait_vmcnt<0>();   // every record load used has returned
+    if (a.flags) publish_read(a.flags, FL_CHAIN, (unsigned)a.sgi + 1, C::READERS * a.BH * C::NCW, lane);
+}
+
+// Store wave HH of a chain workgroup (with output waves): iteration c follows barrier c, after
+// which the output tiles of chunk c - 2 are in LDS; it writes tiles {0, 3} (HH = 0) or {1, 2}
+// to memory. It loads nothing, so it never waits for its stores.
+template <int D, class E, bool DELTA, int HH>
+__device__ __forceinline__ void chain_storer(const PrefArgs& a, unsigned char* smem, int nch, int bh, int cg,
+                                             int lane) {
+    using C = ChainCfg<D, E, DELTA>;
+    constexpr int R[2] = {HH == 0 ? 0 : 1, HH == 0 ? 3 : 2};
+    lds_barrier();
+    for (int cc = 0; cc <= nch; ++cc) {
+        lds_barrier();
+        if (cc >= 2) {
+            const OutPack<E>* ot = reinterpret_cast<const OutPack<E>*>(smem + C::O_OT + (size_t)(cc & 1) * C::OTB);
+#pragma unroll
+            for (int i = 0; i < 2; ++i) store_packed<D, E>(a, bh, cg, cc - 2, R[i], lane, ot[R[i] * 64 + lane]);
+        }
+    }
+}
+
+// One workgroup per CU (its LDS ring). Waves 0 and 1 compute (row half w); with output waves,
+// waves 2 and 3 form the outputs, waves 4 and 5 load and waves 6 and 7 store the outputs, else
+// waves 2 and 3 load. The roles run separate loops with the same barrier sequence.
 template <int D, class E, bool DELTA>
-__global__ __launch_bounds__(256) void chain_kernel(PrefArgs a) {
+__global__ __launch_bounds__((ChainCfg<D, E, DELTA>::THREADS)) void chain_kernel(PrefArgs a) {
     using Ly = Layout<D, E>;
     using C = ChainCfg<D, E, DELTA>;
     extern __shared__ __align__(16) unsigned char smem[];
@@ -744,195 +1094,22 @@ __global__ __launch_bounds__(256) void chain_kernel(PrefArgs a) {
     const int lane = threadIdx.x & 63;
     const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);   // wave-uniform
     const unsigned char* rec0 = a.ws + (size_t)bh * a.segcap * Ly::REC;
-    if (w >= 2)
-        chain_loader<D, E, DELTA>(smem, rec0, a.nseg, cg, w - 2, lane);
+    constexpr int LW = C::OUTW ? 4 : 2;   // first loader wave
+    if (C::OUTW && w >= 6) {
+        if (w == 7)
+            chain_storer<D, E, DELTA, 1>(a, smem, a.nseg, bh, cg, lane);
+        else
+            chain_storer<D, E, DELTA, 0>(a, smem, a.nseg, bh, cg, lane);
+    } else if (w >= LW)
+        chain_loader<D, E, DELTA>(a, smem, rec0, a.nseg, cg, w - LW, lane);
+    else if (C::OUTW && w == 3)
+        chain_output<D, E, DELTA, 1>(a, smem, rec0, a.nseg, bh, cg, lane);
+    else if (C::OUTW && w == 2)
+        chain_output<D, E, DELTA, 0>(a, smem, rec0, a.nseg, bh, cg, lane);
     else if (w == 1)
         chain_compute<D, E, DELTA, 1>(a, smem, rec0, a.nseg, bh, cg, lane);
     else
         chain_compute<D, E, DELTA, 0>(a, smem, rec0, a.nseg, bh, cg, lane);
-}
-
-// ---------------------------------------------------------------------------------------------
-// stage 3: outputs from the chunk-start state
-// ---------------------------------------------------------------------------------------------
-// P^T tiles (st, rt) the output stage needs: every tile inside a token block that some P
-// fragment of token tile rt reads (tiles above the diagonal come out as zeros)
-template <class E>
-struct OutTiles {
-    static constexpr int FPD = MM<E>::KB / 16;
-    static constexpr int kbmax(int rt) { return (16 * rt + 15) / MM<E>::KB; }
-    static constexpr int count() {
-        int c = 0;
-        for (int rt = 0; rt < 4; ++rt) c += FPD * (kbmax(rt) + 1);
-        return c;
-    }
-    static constexpr int N = count();
-    static constexpr int PER_WAVE = (N + 3) / 4;
-    // tile i -> (rt, st), in order of rt then st
-    static __device__ __forceinline__ void tile(int i, int& rt, int& st) {
-        rt = 0;
-        while (i >= FPD * (kbmax(rt) + 1)) { i -= FPD * (kbmax(rt) + 1); ++rt; }
-        st = i;
-    }
-};
-
-template <int D, class E, bool DELTA>
-__global__ __launch_bounds__(256) void output_kernel(PrefArgs a) {
-    using T = typename E::T;
-    using M = MM<E>;
-    using Ly = Layout<D, E>;
-    using OT = OutTiles<E>;
-    using frag = typename M::frag;
-    constexpr int KB = M::KB, NKD = Ly::NKD, NKT = Ly::NKT, NDT = Ly::NDT, FPD = OT::FPD;
-    constexpr int KP = D + 8;   // row stride of the staged Q and K tiles (elements)
-    extern __shared__ __align__(16) unsigned char smem[];
-    T* Qr = reinterpret_cast<T*>(smem);                          // [CH][KP] Q rows
-    T* Kr = Qr + CH * KP;                                        // [CH][KP] K rows, then
-    unsigned char* sP = reinterpret_cast<unsigned char*>(Kr);    //   the P fragments [rt][kt]
-    float* sg = reinterpret_cast<float*>(Kr + CH * KP);          // g
-    static_assert((size_t)4 * NKT * 1024 <= (size_t)CH * KP * sizeof(T), "P fragments fit in the K rows");
-
-    const int cl = blockIdx.x, bh = blockIdx.y;
-    const int tid = threadIdx.x, lane = tid & 63, j = lane >> 4, m = lane & 15;
-    const int w = __builtin_amdgcn_readfirstlane(tid >> 6);   // scalar, as in prep_kernel
-    const long t0 = (long)(a.c0 + cl) * CH;
-    const int n = (int)min((long)CH, a.L - t0);
-    const size_t tok0 = (size_t)bh * a.L + t0;
-    const T* qp = static_cast<const T*>(a.q) + tok0 * D;
-    const T* kp = static_cast<const T*>(a.k) + tok0 * D;
-    T* op = static_cast<T*>(a.o) + tok0 * D;
-    const unsigned char* recB = a.ws + ((size_t)bh * a.segcap + cl) * Ly::REC + Ly::REC_A;
-
-    // Q and K rows (16 bytes per lane, rows past the chunk's end read as zero) are requested
-    // first, then the chunk-start state and U fragments of this wave's value tiles vt = w, w + 4,
-    // ...: the rows are waited for before the staging, the fragments stay in flight through the
-    // P computation
-    constexpr int EPU = 16 / sizeof(T), UPR = D / EPU, NU = CH * UPR / 256;
-    uint4 xq[NU], xk[NU];
-    {
-        const __amdgpu_buffer_rsrc_t rq = buffer_rsrc(qp, n * D * (int)sizeof(T));
-        const __amdgpu_buffer_rsrc_t rk = buffer_rsrc(kp, n * D * (int)sizeof(T));
-#pragma unroll
-        for (int i = 0; i < NU; ++i) {
-            xq[i] = buffer_load16(rq, (tid + 256 * i) * 16);
-            xk[i] = buffer_load16(rk, (tid + 256 * i) * 16);
-        }
-    }
-    static_assert(NDT % 4 == 0, "every wave owns the same number of value tiles");
-    constexpr int NVW = NDT / 4;
-    frag Hc[NVW][NKD], Uf[NVW][NKT];
-#pragma unroll
-    for (int iv = 0; iv < NVW; ++iv) {   // no branch here: the loads above must stay in flight
-        const int vt = w + 4 * iv;
-#pragma unroll
-        for (int kd = 0; kd < NKD; ++kd)
-            Hc[iv][kd] = ld_frag<frag>(recB + Ly::B_H + (size_t)(vt * NKD + kd) * Ly::FR, lane);
-#pragma unroll
-        for (int kt = 0; kt < NKT; ++kt)
-            Uf[iv][kt] = ld_frag<frag>(recB + Ly::B_U + (size_t)(vt * NKT + kt) * Ly::FR, lane);
-    }
-#pragma unroll
-    for (int i = 0; i < NU; ++i) {
-        const int u = tid + 256 * i, r = u / UPR, cu = u % UPR;
-        *reinterpret_cast<uint4*>(Qr + r * KP + cu * EPU) = xq[i];
-        *reinterpret_cast<uint4*>(Kr + r * KP + cu * EPU) = xk[i];
-    }
-    if (w == 0) {
-        float la = 0.f;
-        if (a.log_alpha && lane < n) la = a.log_alpha[tok0 + lane];
-        sg[lane] = wave_scan(la, lane);
-    }
-    lds_barrier();
-    // P^T tile (st, rt), lane (j, n): P[r = 16 rt + n][s = 16 st + 4 j + e] = exp(g_r - g_s) q_r.k_s
-    // for s <= r, else 0. Written straight into its half (bf16) or whole (fp32) of the P fragment
-    // [rt][st / FPD], whose lane (j, n) holds column r and k = s; the fragments take the place of
-    // the K rows once every wave has read those (35 KB of LDS: four workgroups per CU, not three).
-    f32x4 pts[OT::PER_WAVE];
-#pragma unroll
-    for (int x = 0; x < OT::PER_WAVE; ++x) {
-        const int ti = w + 4 * x;
-        if (ti < OT::N) {
-            int rt, st;
-            OT::tile(ti, rt, st);
-            f32x4& pt = pts[x];
-            pt = f32x4{0.f, 0.f, 0.f, 0.f};
-            if (st <= rt) {
-#pragma unroll
-                for (int kd = 0; kd < NKD; ++kd)
-                    pt = M::mma(row_frag_raw<E>(Kr + (16 * st + m) * KP, kd * KB, j),
-                                row_frag_raw<E>(Qr + (16 * rt + m) * KP, kd * KB, j), pt);
-                const int r = 16 * rt + m;
-                const float gr = sg[r];
-#pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    const int s2 = 16 * st + 4 * j + e;
-                    pt[e] = (s2 <= r) ? pt[e] * __expf(gr - sg[s2]) : 0.f;
-                }
-            }
-        }
-    }
-    lds_barrier();   // the K rows are read
-#pragma unroll
-    for (int x = 0; x < OT::PER_WAVE; ++x) {
-        const int ti = w + 4 * x;
-        if (ti < OT::N) {
-            int rt, st;
-            OT::tile(ti, rt, st);
-            const f32x4 pt = pts[x];
-            unsigned char* dst = sP + (size_t)(rt * NKT + st / FPD) * 1024 + lane * 16;
-            if constexpr (FPD == 2) {
-                *reinterpret_cast<uint2*>(dst + 8 * (st % 2)) = uint2{f2bf2(pt[0], pt[1]), f2bf2(pt[2], pt[3])};
-            } else {
-                *reinterpret_cast<f32x4*>(dst) = pt;
-            }
-        }
-    }
-    lds_barrier();
-    // O^T tiles (vt, rt) = H^T e^g Q^T + U^T P^T: the state product with raw Q fragments, scaled
-    // by e^{g_r} per token column, then the intra-chunk part accumulated on top. The Q fragments
-    // are read one token tile at a time (the scheduling barrier keeps the compiler from reading
-    // all sixteen ahead), which keeps the kernel within 128 VGPRs.
-    float eg[4];
-    f32x4 acc[NVW][4];
-#pragma unroll
-    for (int rt = 0; rt < 4; ++rt) {
-        eg[rt] = __expf(sg[16 * rt + m]);
-        frag qf[NKD];
-#pragma unroll
-        for (int kd = 0; kd < NKD; ++kd) qf[kd] = row_frag_raw<E>(Qr + (16 * rt + m) * KP, kd * KB, j);
-#pragma unroll
-        for (int iv = 0; iv < NVW; ++iv) {
-            acc[iv][rt] = f32x4{0.f, 0.f, 0.f, 0.f};
-            if (w + 4 * iv < NDT) {
-#pragma unroll
-                for (int kd = 0; kd < NKD; ++kd) acc[iv][rt] = M::mma(Hc[iv][kd], qf[kd], acc[iv][rt]);
-            }
-        }
-        __builtin_amdgcn_sched_barrier(0);
-    }
-#pragma unroll
-    for (int iv = 0; iv < NVW; ++iv) {
-        const int vt = w + 4 * iv;
-        if (vt >= NDT) break;
-#pragma unroll
-        for (int rt = 0; rt < 4; ++rt)
-            acc[iv][rt] = f32x4{acc[iv][rt][0] * eg[rt], acc[iv][rt][1] * eg[rt], acc[iv][rt][2] * eg[rt],
-                                acc[iv][rt][3] * eg[rt]};
-#pragma unroll
-        for (int kt = 0; kt < NKT; ++kt)
-#pragma unroll
-            for (int rt = 0; rt < 4; ++rt)
-                if (kt <= OT::kbmax(rt))
-                    acc[iv][rt] = M::mma(Uf[iv][kt], ld_frag<frag>(sP + (rt * NKT + kt) * 1024, lane), acc[iv][rt]);
-#pragma unroll
-        for (int rt = 0; rt < 4; ++rt) {
-            // lane (j, m): O[token 16 rt + m][16 vt + 4 j .. + 3]
-            const int r = 16 * rt + m;
-            if (r < n)
-                store4(op + (size_t)r * D + 16 * vt + 4 * j,
-                       make_float4(acc[iv][rt][0], acc[iv][rt][1], acc[iv][rt][2], acc[iv][rt][3]));
-        }
-    }
 }
 
 // h_final = h0 (or zeros) for L = 0
@@ -946,17 +1123,13 @@ struct Launch {
     using T = typename E::T;
     using Ly = Layout<D, E>;
     using CC = ChainCfg<D, E, DELTA>;
-    static constexpr int KP = D + 8;
     static constexpr size_t LDS_PREP = PrepCfg<D, E>::LDS;
     static constexpr size_t LDS_CHAIN = CC::LDS;
-    static constexpr size_t LDS_OUT = (size_t)2 * CH * KP * sizeof(T) + CH * 4;   // Q rows, K rows / P, g
-    // While the chain runs on some of the CUs, the prep and output stages beside it are held to
-    // three workgroups per CU by asking for more than a quarter of the CU's 160 KB of LDS: more
-    // concurrent stage work slows the latency-bound chain by more than it gains (B=1, H=16,
-    // L=128K: 2.82 ms at four per CU, 2.75 ms at three, 2.87 ms at two).
+    // While the chain runs on some of the CUs, the prep stage beside it is held to three
+    // workgroups per CU by asking for more than a quarter of the CU's 160 KB of LDS: more
+    // concurrent prep work slows the latency-bound chain by more than it gains.
     static constexpr size_t LDS_BESIDE = 41 * 1024;
     static constexpr size_t lds_prep(bool beside) { return beside && LDS_PREP < LDS_BESIDE ? LDS_BESIDE : LDS_PREP; }
-    static constexpr size_t lds_out(bool beside) { return beside && LDS_OUT < LDS_BESIDE ? LDS_BESIDE : LDS_OUT; }
 
     // raise the dynamic-LDS limits once per process (every caller sets the same values)
     static bool attributes() {
@@ -964,9 +1137,7 @@ struct Launch {
             hipFuncSetAttribute(reinterpret_cast<const void*>(&prep_kernel<D, E, DELTA>),
                                 hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds_prep(true)) == hipSuccess &&
             hipFuncSetAttribute(reinterpret_cast<const void*>(&chain_kernel<D, E, DELTA>),
-                                hipFuncAttributeMaxDynamicSharedMemorySize, (int)LDS_CHAIN) == hipSuccess &&
-            hipFuncSetAttribute(reinterpret_cast<const void*>(&output_kernel<D, E, DELTA>),
-                                hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds_out(true)) == hipSuccess;
+                                hipFuncAttributeMaxDynamicSharedMemorySize, (int)LDS_CHAIN) == hipSuccess;
         return ok;
     }
     static int chain_blocks(int BH) { return 8 * ((BH + 7) / 8) * CC::NCW; }
@@ -976,19 +1147,16 @@ struct Launch {
     static void chain(const PrefArgs& a, hipStream_t s) {
         hipLaunchKernelGGL((chain_kernel<D, E, DELTA>), dim3(chain_blocks(a.BH)), dim3(CC::THREADS), LDS_CHAIN, s, a);
     }
-    static void output(const PrefArgs& a, hipStream_t s, bool beside = false) {
-        hipLaunchKernelGGL((output_kernel<D, E, DELTA>), dim3(a.nseg, a.BH), dim3(256), lds_out(beside), s, a);
-    }
 };
 
-// Two streams and an event per device, created on first use and kept for the process: the
-// intra-chunk stage of later segments and the output stage of earlier ones run on them while
-// the chain works on the current segment on the caller's stream.
+// A stream and an event per device, created on first use and kept for the process: the
+// intra-chunk stage of later segments runs on it while the chain works on the current segment
+// on the caller's stream.
 struct StreamCtx {
     std::mutex mu;
     bool ready = false;
     int ncu = 0;   // compute units of the device
-    hipStream_t sp = nullptr, so = nullptr;
+    hipStream_t sp = nullptr;
     hipEvent_t start = nullptr;
 };
 
@@ -998,7 +1166,6 @@ static bool init_ctx(StreamCtx& c, int dev) {
     if (c.ready) return true;
     if (hipDeviceGetAttribute(&c.ncu, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return false;
     if (hipStreamCreateWithFlags(&c.sp, hipStreamNonBlocking) != hipSuccess) return false;
-    if (hipStreamCreateWithFlags(&c.so, hipStreamNonBlocking) != hipSuccess) return false;
     if (hipEventCreateWithFlags(&c.start, hipEventDisableTiming) != hipSuccess) return false;
     c.ready = true;
     return true;
@@ -1010,10 +1177,9 @@ static int launch_prefill_t(PrefArgs a, long nch, size_t ws_bytes, hipStream_t s
     if (!LN::attributes()) return -1;
     const size_t rec = Layout<D, E>::REC * (size_t)a.BH;
     if (ws_bytes >= (size_t)nch * rec) {   // whole sequence in one segment, caller's stream only
-        a.c0 = 0; a.nseg = (int)nch; a.segcap = (int)nch;
+        a.c0 = 0; a.nseg = (int)nch; a.segcap = (int)nch; a.flags = nullptr; a.sgi = 0;
         LN::prep(a, stream);
         LN::chain(a, stream);
-        LN::output(a, stream);
         return hipGetLastError() == hipSuccess ? 0 : -1;
     }
     const int seg = (int)((ws_bytes - FLAG_BYTES) / (NBUF * rec));   // >= 1 (validated)
@@ -1023,21 +1189,20 @@ static int launch_prefill_t(PrefArgs a, long nch, size_t ws_bytes, hipStream_t s
     StreamCtx& cx = g_ctx[dev];
     std::lock_guard<std::mutex> lk(cx.mu);
     if (!init_ctx(cx, dev)) return -1;
-    const bool beside = LN::chain_blocks(a.BH) < cx.ncu;   // the chain leaves CUs to the other stages
+    const bool beside = LN::chain_blocks(a.BH) < cx.ncu;   // the chain leaves CUs to prep
     unsigned char* ws0 = a.ws;
     const float* h0 = a.h0;
-    // progress counters after the buffers, cleared on the caller's stream; the internal streams
-    // start after that (and after the work already queued on the caller's stream)
-    unsigned* done = reinterpret_cast<unsigned*>(ws0 + NBUF * buf);   // [0] prep, [1] chain, [2] output
-    bool ok = true;
-    for (int i = 0; i < 3; ++i) ok = ok && hipStreamWriteValue32(stream, done + i, 0u, 0) == hipSuccess;
-    ok = ok && hipEventRecord(cx.start, stream) == hipSuccess && hipStreamWaitEvent(cx.sp, cx.start, 0) == hipSuccess &&
-         hipStreamWaitEvent(cx.so, cx.start, 0) == hipSuccess;
+    // progress counters after the buffers, cleared on the caller's stream; the side stream
+    // starts after that (and after the work already queued on the caller's stream)
+    unsigned* flags = reinterpret_cast<unsigned*>(ws0 + NBUF * buf);
+    static_assert(FL_WORDS * 4 <= FLAG_BYTES, "counters fit");
+    hipLaunchKernelGGL(flags_reset_kernel, dim3(1), dim3(FL_WORDS), 0, stream, flags);
+    bool ok = hipEventRecord(cx.start, stream) == hipSuccess && hipStreamWaitEvent(cx.sp, cx.start, 0) == hipSuccess;
     auto wait = [&](hipStream_t s, int which, int count) {
-        return hipStreamWaitValue32(s, done + which, (unsigned)count, hipStreamWaitValueGte, 0xffffffffu) == hipSuccess;
+        return hipStreamWaitValue32(s, flags + which, (unsigned)count, hipStreamWaitValueGte, 0xffffffffu) == hipSuccess;
     };
     auto mark = [&](hipStream_t s, int which, int count) {
-        return hipStreamWriteValue32(s, done + which, (unsigned)count, 0) == hipSuccess;
+        return hipStreamWriteValue32(s, flags + which, (unsigned)count, 0) == hipSuccess;
     };
     const int nsegs = (int)((nch + seg - 1) / seg);
     for (int sgi = 0; ok && sgi < nsegs; ++sgi) {
@@ -1047,21 +1212,25 @@ static int launch_prefill_t(PrefArgs a, long nch, size_t ws_bytes, hipStream_t s
         b.segcap = seg;
         b.ws = ws0 + (size_t)(sgi % NBUF) * buf;
         b.h0 = sgi == 0 ? h0 : a.h_final;   // later segments continue from the running state
-        // the buffer is free once the output stage of the segment NBUF back has read it. (Its
-        // halves are used by different stages, but letting prep start once that segment's chain
-        // is done puts three kernels on the memory system at once and slows the chain more than
-        // it saves.) Each counter is written after its stage's kernel completes, so a stage
-        // waiting for a count sees that kernel's results.
-        if (sgi >= NBUF) ok = ok && wait(cx.sp, 2, sgi - NBUF + 1);
+        b.flags = flags;
+        b.sgi = sgi;
+        // prep rewrites a buffer once the chain of the segment NBUF back has read it; the count
+        // it then writes (hipStreamWriteValue32, after its kernel on the side stream) makes its
+        // records visible to the chain, which waits for it inside its kernel and publishes its
+        // own count when its last wave is done, so consecutive chain launches follow each other
+        // directly. Every wait, in a kernel or on a stream, is for work queued before it, so the
+        // order holds even where streams share a hardware queue. When the chain occupies every
+        // CU its workgroups could keep prep's from starting, so then the stream waits instead.
+        if (sgi >= NBUF) ok = ok && wait(cx.sp, FL_CHAIN, sgi - NBUF + 1);
         LN::prep(b, cx.sp, beside);
-        ok = ok && mark(cx.sp, 0, sgi + 1) && wait(stream, 0, sgi + 1);
+        ok = ok && mark(cx.sp, FL_PREP, sgi + 1);
+        // hand the side stream's commands to the GPU now: left to itself the runtime holds
+        // them back, and the chain then waits for prep (B=1, H=16, L=128K: 2.44 -> 2.02 ms;
+        // doing the same on the caller's stream slows the chain's launches instead)
+        (void)hipStreamQuery(cx.sp);
+        if (!beside) ok = ok && wait(stream, FL_PREP, sgi + 1);
         LN::chain(b, stream);
-        ok = ok && mark(stream, 1, sgi + 1) && wait(cx.so, 1, sgi + 1);
-        LN::output(b, cx.so, beside);
-        ok = ok && mark(cx.so, 2, sgi + 1);
     }
-    // the caller's stream continues only after the last output stage
-    ok = ok && wait(stream, 2, nsegs);
     return ok && hipGetLastError() == hipSuccess ? 0 : -1;
 }
 

@@ -27,7 +27,7 @@
  *     every state are always fp32.
  *   - Launches are asynchronous on `stream` (a hipStream_t passed as void*; NULL = the null
  *     stream). A return of GDN_OK means the work was enqueued. The library never allocates
- *     device memory; long prefills also use two internal streams (see gdn_prefill_fwd).
+ *     device memory; long prefills also use an internal stream (see gdn_prefill_fwd).
  *   - Errors are returned as negative status codes; validation happens before any launch, so
  *     on an error nothing was enqueued and no output was touched.
  *   - Supported sizes: Dk = Dv in {64, 128}; the chunk length is fixed at 64 tokens; any
@@ -62,12 +62,13 @@ const char *gdn_status_string(int status);
 
 /* Preferred bytes of device workspace for gdn_prefill_fwd, gdn_prefill_skip_fwd and
  * linattn_prefill_fwd at this shape.
- * The workspace holds the per-chunk operands handed between the three prefill stages. A short
- * sequence is processed in one segment; a long one in segments whose stages overlap on two
- * internal streams, with two segment buffers of about 72 MB each followed by 256 bytes of
- * progress counters that order the streams. Any workspace that holds the whole sequence's
- * records, or two chunk records per (batch, head) plus those 256 bytes, is accepted; a smaller
- * one just means shorter segments. Returns 0 for an unsupported shape or L = 0. */
+ * The workspace holds the per-chunk operands the intra-chunk stage hands to the sequential
+ * stage. A short sequence is processed in one segment; a long one in segments whose stages
+ * overlap (the intra-chunk stage of later segments on an internal stream beside the sequential
+ * stage on `stream`), with two segment buffers of about 72 MB each followed by 256 bytes of
+ * progress counters that order the two. Any workspace that holds the whole sequence's records,
+ * or two chunk records per (batch, head) plus those 256 bytes, is accepted; a smaller one just
+ * means shorter segments. Returns 0 for an unsupported shape or L = 0. */
 size_t gdn_prefill_workspace_size(int B, int H, int L, int Dk, int Dv, int dtype);
 
 /*
@@ -80,10 +81,12 @@ size_t gdn_prefill_workspace_size(int B, int H, int L, int Dk, int Dv, int dtype
  *               overlap is GDN_ERR_ALIAS
  *   workspace   device buffer, 256-byte aligned, gdn_prefill_workspace_size(...) bytes preferred
  *               (see above for the minimum); scratch, reusable once the call's work completes
- * Streams: a call that needs more than one segment also runs work on two internal streams of
- * the current device (created on first use, default priority), ordered against `stream` with
- * events: it starts after the work already queued on `stream`, and work queued on `stream`
- * afterwards starts after all of it. Calls that run segments serialise on a per-device lock.
+ * Streams: a call that needs more than one segment also runs work on an internal stream of the
+ * current device (created on first use, default priority): it starts after the work already
+ * queued on `stream`, and work queued on `stream` afterwards starts after all of it. Calls that
+ * run segments serialise on a per-device lock. The stages wait for each other on progress
+ * counters in the workspace; a wait that lasts more than about 10 s (a device starved by other
+ * work) gives up, and the call's o and h_final then come out NaN.
  * L = 0 copies h0 (or zeros) into h_final. Non-finite inputs propagate; they are not checked.
  */
 int gdn_prefill_fwd(const void *q, const void *k, const void *v,
