@@ -151,8 +151,17 @@ int gdn_prefill_banded_fwd(const void* q, const void* k, const void* v, const fl
 int linattn_prefill_fwd(const void* q, const void* k, const void* v, const float* beta, const float* log_alpha,
                         const float* h0, void* o, float* h_final, int B, int H, int L, int Dk, int Dv, int dtype,
                         void* workspace, size_t workspace_bytes, void* stream) {
-    return prefill(q, k, v, beta, log_alpha, nullptr, false, h0, o, h_final, B, H, L, Dk, Dv, dtype, workspace,
-                   workspace_bytes, stream, false);
+    int st = validate_prefill(q, k, v, beta, log_alpha, nullptr, false, h0, o, h_final, B, H, L, Dk, Dv, dtype,
+                              workspace, workspace_bytes, false);
+    if (st != GDN_OK) return st;
+    st = check_device();
+    if (st != GDN_OK) return st;
+    const hipStream_t s = static_cast<hipStream_t>(stream);
+    const int rc = L == 0 ? gdn::launch_prefill(q, k, v, nullptr, nullptr, nullptr, h0, o, h_final, B * H, 0, Dk,
+                                                dtype, false, 3, workspace, workspace_bytes, s)
+                          : gdn::launch_linattn(q, k, v, log_alpha, h0, o, h_final, B * H, L, Dk, dtype, workspace,
+                                                workspace_bytes, s);
+    return rc == 0 ? GDN_OK : GDN_ERR_LAUNCH;
 }
 
 size_t linattn_bidir_workspace_size(int B, int H, int L, int Dk, int Dv, int dtype) {

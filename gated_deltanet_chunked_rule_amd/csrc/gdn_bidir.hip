@@ -27,7 +27,7 @@
 #include <stdint.h>
 
 #include "gdn_launch.h"
-#include "gdn_mfma.h"
+#include "gdn_rows.h"
 
 namespace gdn {
 
@@ -62,56 +62,14 @@ __device__ __forceinline__ uint4 phi16(uint4 x) {
     }
 }
 
-// Buffer resource over `bytes` bytes at p (raw, stride 0): loads past the end return zero and
-// stores past the end are dropped by the hardware, so the ragged last chunk needs no branches.
-// Branch-free loads and stores let the compiler count outstanding memory operations exactly
-// instead of draining them all (vmcnt(0)) at every join of lane-masked blocks.
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t rows_rsrc(const void* p, int bytes) {
-    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(p), 0, bytes, 0x00020000);
-}
+// phi on 16 bytes of storage elements, as a row-staging transform
+template <class E, bool ELU1>
+struct Phi16 {
+    __device__ __forceinline__ uint4 operator()(uint4 x) const { return phi16<E, ELU1>(x); }
+};
 
 typedef int i32x4 __attribute__((ext_vector_type(4)));
 typedef int i32x2 __attribute__((ext_vector_type(2)));
-
-// A 64-row chunk (row stride D in global memory) in flight in registers: 256 threads, 16 bytes
-// each per step. Loading the next chunk while the current one is processed keeps more of HBM's
-// latency covered than the workgroups of one CU do alone.
-template <int D, class E>
-struct RowRegs {
-    static constexpr int ES = sizeof(typename E::T), EPU = 16 / ES, UPR = D / EPU, N = CH * UPR / 256;
-    uint4 x[N];
-    // rows [0, n) of src; the others are zero
-    __device__ __forceinline__ void load(const typename E::T* src, int n, int tid) {
-        const __amdgpu_buffer_rsrc_t rs = rows_rsrc(src, n * D * ES);
-#pragma unroll
-        for (int i = 0; i < N; ++i) {
-            const int u = tid + 256 * i;
-            const i32x4 v = __builtin_amdgcn_raw_buffer_load_b128(rs, u * 16, 0, 0);
-            x[i] = uint4{(unsigned)v.x, (unsigned)v.y, (unsigned)v.z, (unsigned)v.w};
-        }
-    }
-    // into LDS with row stride D + 8, phi applied to rows [0, n), the others zero (masked, not
-    // branched, so that the loads still in flight are not drained here)
-    template <bool ELU1>
-    __device__ __forceinline__ void store(typename E::T* dst, int n, int tid) const {
-#pragma unroll
-        for (int i = 0; i < N; ++i) {
-            const int u = tid + 256 * i, r = u / UPR, cu = u % UPR;
-            const unsigned keep = 0u - (unsigned)(r < n);
-            const uint4 y = phi16<E, ELU1>(x[i]);
-            *reinterpret_cast<uint4*>(dst + r * (D + 8) + cu * EPU) =
-                uint4{y.x & keep, y.y & keep, y.z & keep, y.w & keep};
-        }
-    }
-};
-
-// LDS-only workgroup barrier (the waves exchange nothing through global memory)
-__device__ __forceinline__ void lds_sync() {
-    asm volatile("" ::: "memory");
-    __builtin_amdgcn_s_waitcnt(15 | (7 << 4) | (0 << 8) | (3 << 14));   // lgkmcnt(0)
-    __builtin_amdgcn_s_barrier();
-    asm volatile("" ::: "memory");
-}
 
 }  // namespace
 
@@ -196,8 +154,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(sizeof(type
     rv.load(v + ((size_t)bh * L + c_begin * CH) * D, rows_of(c_begin), tid);
     for (long c = c_begin; c < c_end; ++c) {
         const int n = rows_of(c);
-        rk.template store<ELU1>(Kr, n, tid);
-        rv.template store<false>(Vr, n, tid);
+        rk.store(Kr, n, tid, Phi16<E, ELU1>());
+        rv.store(Vr, n, tid);
         if (c + 1 < c_end) {   // the next chunk's rows, in flight during this one
             const size_t tok1 = (size_t)bh * L + (c + 1) * CH;
             rk.load(k + tok1 * D, rows_of(c + 1), tid);
@@ -352,9 +310,9 @@ __global__ __launch_bounds__(256) void bidir_out_kernel(const typename E::T* __r
         const long t0 = c * CH;
         const int n = rows_of(c);
         const size_t tok0 = (size_t)bh * L + t0;
-        const __amdgpu_buffer_rsrc_t ors = rows_rsrc(o + tok0 * D, n * D * (int)sizeof(T));
+        const __amdgpu_buffer_rsrc_t ors = buffer_rsrc(o + tok0 * D, n * D * (int)sizeof(T));
         if (c > c_begin) lds_sync();   // every wave is done with the previous chunk's rows
-        rq.template store<ELU1>(Qr, n, tid);
+        rq.store(Qr, n, tid, Phi16<E, ELU1>());
         if (c + 2 < c_end) rq.load(chunk_q(c + 2), rows_of(c + 2), tid);
         lds_sync();
 #pragma unroll

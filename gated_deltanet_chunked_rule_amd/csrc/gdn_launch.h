@@ -17,6 +17,12 @@ int launch_prefill(const void* q, const void* k, const void* v, const float* bet
                    const unsigned char* keep, const float* h0, void* o, float* h_final, int BH, long L, int D,
                    int dtype, bool delta, int band, void* ws, size_t ws_bytes, hipStream_t stream);
 
+// Causal linear attention, plain (log_alpha NULL) or with a per-token decay, block-parallel.
+// The workspace (at least prefill_workspace_min_bytes) holds the blocks' state tiles; a smaller
+// one means fewer, longer blocks.
+int launch_linattn(const void* q, const void* k, const void* v, const float* log_alpha, const float* h0, void* o,
+                   float* h_final, int BH, long L, int D, int dtype, void* ws, size_t ws_bytes, hipStream_t stream);
+
 // Bidirectional linear attention. kv_out: [BH][D][D] fp32 or NULL. flags bit 0: divide by Z,
 // bit 1: phi = elu + 1 (else identity). The workspace is bidir_workspace_bytes(...) bytes.
 size_t bidir_workspace_bytes(long BH, long L, int D, int dtype);

@@ -1,0 +1,430 @@
+// Block-parallel chunked prefill of causal linear attention, plain or with a per-token decay,
+// on gfx950.
+//
+// The recurrence S_t = a_t S_{t-1} + v_t k_t^T, o_t = S_t q_t (the forpes.ru article on linear
+// attention: its recurrent form and the decay modifications listed after it; a = 1 is the plain
+// form of the AI RnD Day channel post, tgstat.ru, section "Linear attention") has a scalar
+// transition, so the state at any token is a decayed sum of the chunks before it: the chunks'
+// contributions can be formed in parallel and only their sums need a sequential pass. With the
+// key-major state H = S^T, per chunk of C = 64 tokens and g the in-chunk inclusive prefix sum of
+// log a:
+//     O  = diag(e^g) Q H + (Q K^T .* Gamma) V,   Gamma[r][s] = e^{g_r - g_s} for s <= r, else 0
+//     H' = e^{g_C} H + Khat^T V,                 Khat[s] = e^{g_C - g_s} k_s
+// (only exponentials of non-positive differences are formed). Three kernels:
+//   1. la_kv_kernel: one workgroup per (block of chunks, slice) runs H' over its block from zero:
+//      S_b, the block's contribution to the state after it, and Lambda_b, its summed log a.
+//   2. la_scan_kernel: per slice and state element, H_0 = h0, H_{b+1} = e^{Lambda_b} H_b + S_b;
+//      H_b replaces S_b in the workspace and the last one is h_final.
+//   3. la_out_kernel: one workgroup per (block, slice) runs the block's chunks again from H_b and
+//      forms their outputs. Each wave keeps the fp32 state of a quarter of the value columns in
+//      accumulator registers, computes the gated causal P^T for one token tile and shares it and
+//      its quarter of the Khat^T fragments through LDS.
+// The products that contract over tokens (Khat^T V, V^T P^T) need fragments whose k index is the
+// token: K and V rows are staged in LDS and turned into columns by one MFMA per 16 x 16 tile
+// against a unit-column fragment, an exact transpose on the matrix core.
+#include <stdint.h>
+
+#include "gdn_launch.h"
+#include "gdn_rows.h"
+
+namespace gdn {
+
+namespace {
+
+// One block's state (or contribution) in the workspace: NDT x NDT fp32 accumulator tiles
+// (d_k tile dt, value tile vt) of 64 lanes x 4, lane (j, n) holding rows 16 dt + 4 j .. + 3 of
+// column 16 vt + n. The workspace holds [slices][blocks] of them, then [slices][blocks] fp32
+// Lambda.
+template <int D>
+struct LaLayout {
+    static constexpr int NDT = D / 16;
+    static constexpr size_t TILES = (size_t)NDT * NDT * 1024;
+};
+
+typedef int i32x2v __attribute__((ext_vector_type(2)));
+typedef int i32x4v __attribute__((ext_vector_type(4)));
+
+template <int D, class E>
+struct LaCfg {
+    using T = typename E::T;
+    static constexpr int KB = MM<E>::KB, NDT = D / 16, NKD = D / KB, NKT = CH / KB, FPD = KB / 16, KP = D + 8;
+    static constexpr int DW = NDT / 4;                                  // value (and key) tiles per wave
+    static constexpr size_t ROWS = (size_t)CH * KP * sizeof(T);         // one chunk's rows in LDS
+    static constexpr size_t KF = (size_t)NDT * NKT * 1024;              // Khat^T fragments
+    static constexpr size_t PF = (size_t)4 * NKT * 1024;                // P^T fragments
+    static constexpr size_t LDS_KV = 2 * ROWS + KF + CH * 4;
+    static constexpr size_t LDS_OUT = 3 * ROWS + KF + PF + 3 * CH * 4;
+    // register prefetch of the next chunk's rows only where it fits beside the fp32 fragments
+    static constexpr bool PREF = sizeof(T) == 2;
+};
+
+// transposed 16 x 16 tiles of d-tile dt of the rows R (row stride KP): lane (j, n) of t[st]
+// holds R[16 st + 4 j + e][16 dt + n]
+template <int D, class E>
+__device__ __forceinline__ void col_tiles(const typename E::T* R, int dt, int j, int m, f32x4 (&t)[4]) {
+    using C = LaCfg<D, E>;
+    using M = MM<E>;
+    const typename M::frag sel = unit_cols<E>(j, m, dt % C::FPD);
+#pragma unroll
+    for (int st = 0; st < 4; ++st)
+        t[st] = M::mma(row_frag_raw<E>(R + (16 * st + m) * C::KP, C::KB * (dt / C::FPD), j), sel, f32x4{0.f, 0.f, 0.f, 0.f});
+}
+
+}  // namespace
+
+// ---------------------------------------------------------------------------------------------
+// 1. each block's contribution to the state after it
+// ---------------------------------------------------------------------------------------------
+template <int D, class E, bool GATED>
+__global__ __launch_bounds__(256) void la_kv_kernel(const typename E::T* __restrict__ k,
+                                                    const typename E::T* __restrict__ v,
+                                                    const float* __restrict__ log_alpha, unsigned char* ws, long L,
+                                                    int cpb, int nb) {
+    using T = typename E::T;
+    using M = MM<E>;
+    using C = LaCfg<D, E>;
+    using frag = typename M::frag;
+    constexpr int NDT = C::NDT, NKT = C::NKT, FPD = C::FPD, DW = C::DW;
+    extern __shared__ __align__(16) unsigned char smem[];
+    T* Kr = reinterpret_cast<T*>(smem);                                   // [CH][KP]
+    T* Vr = reinterpret_cast<T*>(smem + C::ROWS);                         // [CH][KP]
+    unsigned char* sKf = smem + 2 * C::ROWS;                              // Khat^T fragments [dt][kt]
+    float* skh = reinterpret_cast<float*>(smem + 2 * C::ROWS + C::KF);    // e^{g_C - g}
+
+    const int blk = blockIdx.x, bh = blockIdx.y;
+    const int tid = threadIdx.x, lane = tid & 63, j = lane >> 4, m = lane & 15;
+    const int w = __builtin_amdgcn_readfirstlane(tid >> 6);   // scalar: no MFMA under a lane mask
+    const long nch = (L + CH - 1) / CH;
+    const long c_begin = (long)blk * cpb;
+    const long c_end = c_begin + cpb < nch ? c_begin + cpb : nch;
+
+    f32x4 acc[NDT][DW];   // contribution tiles (dt, value tile DW w + i)
+#pragma unroll
+    for (int dt = 0; dt < NDT; ++dt)
+#pragma unroll
+        for (int i = 0; i < DW; ++i) acc[dt][i] = f32x4{0.f, 0.f, 0.f, 0.f};
+    float lam = 0.f;   // the block's summed log a (the same in every lane)
+
+    auto rows_of = [&](long c) { return (int)(L - c * CH < CH ? L - c * CH : CH); };
+    RowRegs<D, E> rk, rv;
+    rk.load(k + ((size_t)bh * L + c_begin * CH) * D, rows_of(c_begin), tid);
+    rv.load(v + ((size_t)bh * L + c_begin * CH) * D, rows_of(c_begin), tid);
+    for (long c = c_begin; c < c_end; ++c) {
+        const int n = rows_of(c);
+        float la = 0.f;
+        if constexpr (GATED) la = lane < n ? log_alpha[(size_t)bh * L + c * CH + lane] : 0.f;
+        rk.store(Kr, n, tid);
+        rv.store(Vr, n, tid);
+        if (c + 1 < c_end) {   // the next chunk's rows, in flight during this one
+            const size_t tok1 = (size_t)bh * L + (c + 1) * CH;
+            rk.load(k + tok1 * D, rows_of(c + 1), tid);
+            rv.load(v + tok1 * D, rows_of(c + 1), tid);
+        }
+        float gC = 0.f;
+        if constexpr (GATED) {
+            const float g = wave_scan(la, lane);
+            gC = __shfl(g, 63);
+            if (w == 0) skh[lane] = __expf(gC - g);
+        }
+        lds_sync();
+        // this wave's key tiles -> Khat^T fragments in LDS; its value tiles -> V fragments
+        frag vf[DW][NKT];
+#pragma unroll
+        for (int i = 0; i < DW; ++i) {
+            const int dt = DW * w + i;
+            f32x4 t[4];
+            col_tiles<D, E>(Kr, dt, j, m, t);
+#pragma unroll
+            for (int kt = 0; kt < NKT; ++kt)
+                st_frag(sKf + (size_t)(dt * NKT + kt) * 1024, lane,
+                        GATED ? cols_frag<E>(&t[FPD * kt], skh + 16 * FPD * kt, j) : cols_frag<E>(&t[FPD * kt]));
+            col_tiles<D, E>(Vr, dt, j, m, t);
+#pragma unroll
+            for (int kt = 0; kt < NKT; ++kt) vf[i][kt] = cols_frag<E>(&t[FPD * kt]);
+        }
+        lds_sync();
+        if constexpr (GATED) {
+            const float dc = __expf(gC);
+            lam += gC;
+#pragma unroll
+            for (int dt = 0; dt < NDT; ++dt)
+#pragma unroll
+                for (int i = 0; i < DW; ++i)
+                    acc[dt][i] = f32x4{acc[dt][i][0] * dc, acc[dt][i][1] * dc, acc[dt][i][2] * dc, acc[dt][i][3] * dc};
+        }
+        // S = e^{g_C} S + Khat^T V over this wave's value tiles
+#pragma unroll
+        for (int dt = 0; dt < NDT; ++dt)
+#pragma unroll
+            for (int kt = 0; kt < NKT; ++kt) {
+                const frag kf = ld_frag<frag>(sKf + (size_t)(dt * NKT + kt) * 1024, lane);
+#pragma unroll
+                for (int i = 0; i < DW; ++i) acc[dt][i] = M::mma(kf, vf[i][kt], acc[dt][i]);
+            }
+    }
+    unsigned char* sb = ws + ((size_t)bh * nb + blk) * LaLayout<D>::TILES;
+#pragma unroll
+    for (int dt = 0; dt < NDT; ++dt)
+#pragma unroll
+        for (int i = 0; i < DW; ++i) st_frag(sb + (size_t)(dt * NDT + DW * w + i) * 1024, lane, acc[dt][i]);
+    if (GATED && tid == 0) {
+        float* lamb = reinterpret_cast<float*>(ws + (size_t)gridDim.y * nb * LaLayout<D>::TILES);
+        lamb[(size_t)bh * nb + blk] = lam;
+    }
+}
+
+// ---------------------------------------------------------------------------------------------
+// 2. block-start states: a sequential pass over the blocks, one thread per state element
+// ---------------------------------------------------------------------------------------------
+template <int D>
+__global__ __launch_bounds__(256) void la_scan_kernel(unsigned char* ws, const float* __restrict__ h0,
+                                                      float* h_final, int nb, int gated) {
+    constexpr int NDT = D / 16;
+    constexpr size_t TF = LaLayout<D>::TILES / 4;   // floats per block
+    const int bh = blockIdx.y;
+    const int u = blockIdx.x * 256 + threadIdx.x;   // element in tile order, < D * D
+    const int e = u & 3, lane = (u >> 2) & 63, tile = u >> 8;
+    const int row = 16 * (tile / NDT) + 4 * (lane >> 4) + e, col = 16 * (tile % NDT) + (lane & 15);
+    const size_t hix = ((size_t)bh * D + row) * D + col;
+    float* S = reinterpret_cast<float*>(ws + (size_t)bh * nb * LaLayout<D>::TILES) + u;
+    const float* lamb = reinterpret_cast<const float*>(ws + (size_t)gridDim.y * nb * LaLayout<D>::TILES) + (size_t)bh * nb;
+    float H = h0 ? h0[hix] : 0.f;   // read before h_final is written: they may be the same array
+    for (int b = 0; b < nb; ++b) {
+        const float s = S[b * TF];
+        S[b * TF] = H;
+        H = (gated ? __expf(lamb[b]) * H : H) + s;
+    }
+    h_final[hix] = H;
+}
+
+// ---------------------------------------------------------------------------------------------
+// 3. outputs from each block's start state
+// ---------------------------------------------------------------------------------------------
+template <int D, class E, bool GATED>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void la_out_kernel(const typename E::T* __restrict__ q,
+                                                     const typename E::T* __restrict__ k,
+                                                     const typename E::T* __restrict__ v,
+                                                     const float* __restrict__ log_alpha,
+                                                     const unsigned char* __restrict__ ws, typename E::T* __restrict__ o,
+                                                     long L, int cpb, int nb) {
+    using T = typename E::T;
+    using M = MM<E>;
+    using C = LaCfg<D, E>;
+    using frag = typename M::frag;
+    constexpr int KB = C::KB, NDT = C::NDT, NKD = C::NKD, NKT = C::NKT, FPD = C::FPD, KP = C::KP, DW = C::DW;
+    extern __shared__ __align__(16) unsigned char smem[];
+    T* Qr = reinterpret_cast<T*>(smem);                                           // [CH][KP]
+    T* Kr = reinterpret_cast<T*>(smem + C::ROWS);                                 // [CH][KP]
+    T* Vr = reinterpret_cast<T*>(smem + 2 * C::ROWS);                             // [CH][KP]
+    unsigned char* sKf = smem + 3 * C::ROWS;                                      // Khat^T fragments [dt][kt]
+    unsigned char* sPf = sKf + C::KF;                                             // P^T fragments [rt][kt]
+    float* sg = reinterpret_cast<float*>(sPf + C::PF);                            // g
+    float* seg = sg + CH;                                                         // e^g
+    float* skh = seg + CH;                                                        // e^{g_C - g}
+
+    const int blk = blockIdx.x, bh = blockIdx.y;
+    const int tid = threadIdx.x, lane = tid & 63, j = lane >> 4, m = lane & 15;
+    const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const long nch = (L + CH - 1) / CH;
+    const long c_begin = (long)blk * cpb;
+    const long c_end = c_begin + cpb < nch ? c_begin + cpb : nch;
+
+    // the block-start state of this wave's value tiles vt = DW w + i
+    f32x4 H[DW][NDT];
+    const unsigned char* hb = ws + ((size_t)bh * nb + blk) * LaLayout<D>::TILES;
+#pragma unroll
+    for (int i = 0; i < DW; ++i)
+#pragma unroll
+        for (int dt = 0; dt < NDT; ++dt) H[i][dt] = ld_frag<f32x4>(hb + (size_t)(dt * NDT + DW * w + i) * 1024, lane);
+
+    auto rows_of = [&](long c) { return (int)(L - c * CH < CH ? L - c * CH : CH); };
+    auto src = [&](const T* p, long c) { return p + ((size_t)bh * L + c * CH) * D; };
+    RowRegs<D, E> rq, rk, rv;
+    auto load_rows = [&](long c) {
+        const int n = rows_of(c);
+        rq.load(src(q, c), n, tid);
+        rk.load(src(k, c), n, tid);
+        rv.load(src(v, c), n, tid);
+    };
+    load_rows(c_begin);
+    for (long c = c_begin; c < c_end; ++c) {
+        const int n = rows_of(c);
+        const size_t tok0 = (size_t)bh * L + c * CH;
+        float la = 0.f;
+        if constexpr (GATED) la = lane < n ? log_alpha[tok0 + lane] : 0.f;
+        if (c > c_begin) lds_sync();   // every wave is done with the previous chunk's LDS data
+        rq.store(Qr, n, tid);
+        rk.store(Kr, n, tid);
+        rv.store(Vr, n, tid);
+        if (C::PREF && c + 1 < c_end) load_rows(c + 1);
+        float gC = 0.f;
+        if constexpr (GATED) {
+            const float g = wave_scan(la, lane);
+            gC = __shfl(g, 63);
+            if (w == 0) {
+                sg[lane] = g;
+                seg[lane] = __expf(g);
+                skh[lane] = __expf(gC - g);
+            }
+        }
+        lds_sync();
+        // this wave's key tiles -> Khat^T fragments in LDS; its value tiles -> V fragments
+        frag vf[DW][NKT];
+#pragma unroll
+        for (int i = 0; i < DW; ++i) {
+            const int dt = DW * w + i;
+            f32x4 t[4];
+            col_tiles<D, E>(Kr, dt, j, m, t);
+#pragma unroll
+            for (int kt = 0; kt < NKT; ++kt)
+                st_frag(sKf + (size_t)(dt * NKT + kt) * 1024, lane,
+                        GATED ? cols_frag<E>(&t[FPD * kt], skh + 16 * FPD * kt, j) : cols_frag<E>(&t[FPD * kt]));
+            col_tiles<D, E>(Vr, dt, j, m, t);
+#pragma unroll
+            for (int kt = 0; kt < NKT; ++kt) vf[i][kt] = cols_frag<E>(&t[FPD * kt]);
+        }
+        // P^T for token tile rt = w: lane (j, n) of t[st] holds k_s . q_r, s = 16 st + 4 j + e,
+        // r = 16 w + n, kept for s <= r and gated by e^{g_r - g_s}
+        {
+            f32x4 t[4];
+#pragma unroll
+            for (int st = 0; st < 4; ++st) {
+                t[st] = f32x4{0.f, 0.f, 0.f, 0.f};
+                if (st <= w) {
+#pragma unroll
+                    for (int kd = 0; kd < NKD; ++kd)
+                        t[st] = M::mma(row_frag_raw<E>(Kr + (16 * st + m) * KP, kd * KB, j),
+                                       row_frag_raw<E>(Qr + (16 * w + m) * KP, kd * KB, j), t[st]);
+                    const int r = 16 * w + m;
+                    const float gr = GATED ? sg[r] : 0.f;
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) {
+                        const int s = 16 * st + 4 * j + e;
+                        const float x = GATED ? t[st][e] * __expf(s <= r ? gr - sg[s] : 0.f) : t[st][e];
+                        t[st][e] = s <= r ? x : 0.f;
+                    }
+                }
+            }
+#pragma unroll
+            for (int kt = 0; kt < NKT; ++kt) st_frag(sPf + (size_t)(w * NKT + kt) * 1024, lane, cols_frag<E>(&t[FPD * kt]));
+        }
+        // the chunk-start state as A operands (rows = value columns, k = key)
+        frag Hf[DW][NKD];
+#pragma unroll
+        for (int i = 0; i < DW; ++i)
+#pragma unroll
+            for (int kd = 0; kd < NKD; ++kd) Hf[i][kd] = M::from_acc(H[i], kd);
+        lds_sync();
+        // O^T tiles (value tile DW w + i, token tile rt) = e^g (H^T Q^T) + V^T P^T
+        const __amdgpu_buffer_rsrc_t ors = buffer_rsrc(o + tok0 * D, n * D * (int)sizeof(T));
+#pragma unroll
+        for (int rt = 0; rt < 4; ++rt) {
+            frag qf[NKD];
+#pragma unroll
+            for (int kd = 0; kd < NKD; ++kd) qf[kd] = row_frag_raw<E>(Qr + (16 * rt + m) * KP, kd * KB, j);
+            frag pf[NKT];
+#pragma unroll
+            for (int kt = 0; kt < NKT; ++kt) pf[kt] = ld_frag<frag>(sPf + (size_t)(rt * NKT + kt) * 1024, lane);
+            const float egr = GATED ? seg[16 * rt + m] : 1.f;
+#pragma unroll
+            for (int i = 0; i < DW; ++i) {
+                f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                for (int kd = 0; kd < NKD; ++kd) acc = M::mma(Hf[i][kd], qf[kd], acc);
+                if constexpr (GATED) acc = f32x4{acc[0] * egr, acc[1] * egr, acc[2] * egr, acc[3] * egr};
+#pragma unroll
+                for (int kt = 0; kt < NKT; ++kt)
+                    if (kt * KB <= 16 * rt + 15) acc = M::mma(vf[i][kt], pf[kt], acc);
+                // lane (j, m): o[token 16 rt + m][16 vt + 4 j .. + 3]; tokens past the end are dropped
+                const int off = ((16 * rt + m) * D + 16 * (DW * w + i) + 4 * j) * (int)sizeof(T);
+                if constexpr (sizeof(T) == 2) {
+                    const i32x2v x = {(int)f2bf2(acc[0], acc[1]), (int)f2bf2(acc[2], acc[3])};
+                    __builtin_amdgcn_raw_buffer_store_b64(x, ors, off, 0, 0);
+                } else {
+                    const i32x4v x = {__float_as_int(acc[0]), __float_as_int(acc[1]), __float_as_int(acc[2]),
+                                      __float_as_int(acc[3])};
+                    __builtin_amdgcn_raw_buffer_store_b128(x, ors, off, 0, 0);
+                }
+            }
+        }
+        // H = e^{g_C} H + Khat^T V
+        if constexpr (GATED) {
+            const float dc = __expf(gC);
+#pragma unroll
+            for (int i = 0; i < DW; ++i)
+#pragma unroll
+                for (int dt = 0; dt < NDT; ++dt)
+                    H[i][dt] = f32x4{H[i][dt][0] * dc, H[i][dt][1] * dc, H[i][dt][2] * dc, H[i][dt][3] * dc};
+        }
+#pragma unroll
+        for (int dt = 0; dt < NDT; ++dt)
+#pragma unroll
+            for (int kt = 0; kt < NKT; ++kt) {
+                const frag kf = ld_frag<frag>(sKf + (size_t)(dt * NKT + kt) * 1024, lane);
+#pragma unroll
+                for (int i = 0; i < DW; ++i) H[i][dt] = M::mma(kf, vf[i][kt], H[i][dt]);
+            }
+        if (!C::PREF && c + 1 < c_end) load_rows(c + 1);
+    }
+}
+
+// ---------------------------------------------------------------------------------------------
+// launch
+// ---------------------------------------------------------------------------------------------
+namespace {
+
+// blocks of chunks per slice: about 1024 workgroups for stages 1 and 3, no more than the
+// workspace holds (at least one: the smallest workspace accepted holds two chunk records per
+// slice, each larger than one block's state tiles)
+int la_blocks(long BH, long nch, size_t tiles, size_t ws_bytes) {
+    long nb = (1024 + BH - 1) / BH;
+    if (nb > nch) nb = nch;
+    const long fit = (long)(ws_bytes / ((size_t)BH * (tiles + 4)));
+    if (nb > fit) nb = fit;
+    if (nb < 1) nb = 1;
+    const long cpb = (nch + nb - 1) / nb;
+    return (int)((nch + cpb - 1) / cpb);
+}
+
+}  // namespace
+
+template <int D, class E, bool GATED>
+static int launch_linattn_t(const void* q, const void* k, const void* v, const float* log_alpha, const float* h0,
+                            void* o, float* h_final, long BH, long L, unsigned char* ws, size_t ws_bytes,
+                            hipStream_t stream) {
+    using T = typename E::T;
+    using C = LaCfg<D, E>;
+    const long nch = (L + CH - 1) / CH;
+    const int nb = la_blocks(BH, nch, LaLayout<D>::TILES, ws_bytes);
+    if ((size_t)BH * nb * (LaLayout<D>::TILES + 4) > ws_bytes) return -1;
+    const int cpb = (int)((nch + nb - 1) / nb);
+    static const bool attr =
+        hipFuncSetAttribute(reinterpret_cast<const void*>(&la_kv_kernel<D, E, GATED>),
+                            hipFuncAttributeMaxDynamicSharedMemorySize, (int)C::LDS_KV) == hipSuccess &&
+        hipFuncSetAttribute(reinterpret_cast<const void*>(&la_out_kernel<D, E, GATED>),
+                            hipFuncAttributeMaxDynamicSharedMemorySize, (int)C::LDS_OUT) == hipSuccess;
+    if (!attr) return -1;
+    const dim3 grid((unsigned)nb, (unsigned)BH);
+    hipLaunchKernelGGL((la_kv_kernel<D, E, GATED>), grid, dim3(256), C::LDS_KV, stream, (const T*)k, (const T*)v,
+                       log_alpha, ws, L, cpb, nb);
+    hipLaunchKernelGGL((la_scan_kernel<D>), dim3(D * D / 256, (unsigned)BH), dim3(256), 0, stream, ws, h0, h_final, nb,
+                       GATED ? 1 : 0);
+    hipLaunchKernelGGL((la_out_kernel<D, E, GATED>), grid, dim3(256), C::LDS_OUT, stream, (const T*)q, (const T*)k,
+                       (const T*)v, log_alpha, (const unsigned char*)ws, (T*)o, L, cpb, nb);
+    return hipGetLastError() == hipSuccess ? 0 : -1;
+}
+
+int launch_linattn(const void* q, const void* k, const void* v, const float* log_alpha, const float* h0, void* o,
+                   float* h_final, int BH, long L, int D, int dtype, void* ws, size_t ws_bytes, hipStream_t stream) {
+    unsigned char* w = static_cast<unsigned char*>(ws);
+#define GDN_LA(DD, EE)                                                                                          \
+    return log_alpha ? launch_linattn_t<DD, EE, true>(q, k, v, log_alpha, h0, o, h_final, BH, L, w, ws_bytes, stream) \
+                     : launch_linattn_t<DD, EE, false>(q, k, v, nullptr, h0, o, h_final, BH, L, w, ws_bytes, stream)
+    if (D == 128 && dtype == 0) GDN_LA(128, BF16);
+    if (D == 128) GDN_LA(128, F32);
+    if (dtype == 0) GDN_LA(64, BF16);
+    GDN_LA(64, F32);
+#undef GDN_LA
+}
+
+}  // namespace gdn

@@ -32,8 +32,8 @@
 #include <mutex>
 #include <type_traits>
 
-#include "gdn_mfma.h"
 #include "gdn_launch.h"
+#include "gdn_rows.h"
 
 namespace gdn {
 
@@ -122,16 +122,6 @@ struct PrefArgs {
     unsigned* flags;             // segment pipeline counters, or NULL (the call is one segment)
     int sgi;                     // this launch's segment
 };
-
-// inclusive prefix sum over the 64 lanes of a wave
-__device__ __forceinline__ float wave_scan(float x, int lane) {
-#pragma unroll
-    for (int off = 1; off < 64; off <<= 1) {
-        const float y = __shfl_up(x, off);
-        if (lane >= off) x += y;
-    }
-    return x;
-}
 
 
 // Off-diagonal block (bi, bj), bi > bj, of T = (I + A)^-1 (16 x 16 blocks, fp32, row stride AS):

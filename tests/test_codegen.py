@@ -22,7 +22,7 @@ from gated_deltanet_chunked_rule_amd import build
 HIPCC = build.HIPCC
 pytestmark = pytest.mark.skipif(not shutil.which(HIPCC) and not os.path.exists(HIPCC), reason="hipcc not found")
 
-SOURCES = ["gdn_prefill.hip", "gdn_decode.hip", "gdn_bidir.hip"]
+SOURCES = ["gdn_prefill.hip", "gdn_decode.hip", "gdn_bidir.hip", "gdn_linattn.hip"]
 
 
 def _device_asm(src, tmp_path):
