@@ -112,7 +112,8 @@ __global__ __launch_bounds__(256) void la_kv_kernel(const typename E::T* __restr
     for (long c = c_begin; c < c_end; ++c) {
         const int n = rows_of(c);
         float la = 0.f;
-        if constexpr (GATED) la = lane < n ? log_alpha[(size_t)bh * L + c * CH + lane] : 0.f;
+        if constexpr (GATED)   // through a buffer resource: no branch, so no wait for older loads
+            la = __uint_as_float(buffer_load4(buffer_rsrc(log_alpha + (size_t)bh * L + c * CH, n * 4), lane * 4));
         rk.store(Kr, n, tid);
         rv.store(Vr, n, tid);
         if (c + 1 < c_end) {   // the next chunk's rows, in flight during this one
@@ -251,7 +252,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void l
         const int n = rows_of(c);
         const size_t tok0 = (size_t)bh * L + c * CH;
         float la = 0.f;
-        if constexpr (GATED) la = lane < n ? log_alpha[tok0 + lane] : 0.f;
+        if constexpr (GATED)   // through a buffer resource: no branch, so no wait for older loads
+            la = __uint_as_float(buffer_load4(buffer_rsrc(log_alpha + tok0, n * 4), lane * 4));
         if (c > c_begin) lds_sync();   // every wave is done with the previous chunk's LDS data
         rq.store(Qr, n, tid);
         rk.store(Kr, n, tid);
@@ -373,11 +375,11 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void l
 // ---------------------------------------------------------------------------------------------
 namespace {
 
-// blocks of chunks per slice: about 1024 workgroups for stages 1 and 3, no more than the
+// blocks of chunks per slice: about 512 workgroups for stages 1 and 3 (two per CU), no more than the
 // workspace holds (at least one: the smallest workspace accepted holds two chunk records per
 // slice, each larger than one block's state tiles)
 int la_blocks(long BH, long nch, size_t tiles, size_t ws_bytes) {
-    long nb = (1024 + BH - 1) / BH;
+    long nb = (512 + BH - 1) / BH;
     if (nb > nch) nb = nch;
     const long fit = (long)(ws_bytes / ((size_t)BH * (tiles + 4)));
     if (nb > fit) nb = fit;
