@@ -84,9 +84,25 @@ static constexpr int NBUF = 2;
 // which measured about 5 us less per cross-stream hand-off (128K: 2.75 -> 2.63 ms).
 static constexpr size_t FLAG_BYTES = 256;
 
+// Where the chain's workgroups fill every CU of the device, prep cannot run beside it and the two
+// stages alternate segment by segment; the fewest hand-offs then win, so the preferred workspace
+// holds the whole sequence's records if they take at most WHOLE_MAX bytes (B=1, H=32, L=32768:
+// 1.31 ms in 72 MB segments, 1.06 ms in one).
+static constexpr size_t WHOLE_MAX = (size_t)2 << 30;
+
+static int device_cus() {
+    int dev = 0, n = 0;
+    if (hipGetDevice(&dev) != hipSuccess || hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
+        return 0;
+    return n;
+}
+
 size_t prefill_workspace_bytes(long BH, long L, int D, int dtype) {
     const long nch = (L + CH - 1) / CH;
     const size_t rec = prefill_record_bytes(D, dtype) * (size_t)BH;   // one chunk of every slice
+    const long chain_wgs = 8 * ((BH + 7) / 8) * (D / 16);             // the chain's grid
+    const int ncu = device_cus();
+    if (ncu > 0 && chain_wgs >= ncu && (size_t)nch * rec <= WHOLE_MAX) return (size_t)nch * rec;
     long seg = (long)(SEG_TARGET / rec);
     seg = seg < 4 ? 4 : seg;
     if (nch <= NBUF * seg) return (size_t)nch * rec;                   // one segment

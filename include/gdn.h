@@ -66,9 +66,14 @@ const char *gdn_status_string(int status);
  * stage. A short sequence is processed in one segment; a long one in segments whose stages
  * overlap (the intra-chunk stage of later segments on an internal stream beside the sequential
  * stage on `stream`), with two segment buffers of about 72 MB each followed by 256 bytes of
- * progress counters that order the two. Any workspace that holds the whole sequence's records,
- * or two chunk records per (batch, head) plus those 256 bytes, is accepted; a smaller one just
- * means shorter segments. Returns 0 for an unsupported shape or L = 0. */
+ * progress counters that order the two. Where the sequential stage alone fills every compute
+ * unit of the current device (more than 24 (batch, head) slices at Dk = 128 on MI355X's 256
+ * CUs) the stages cannot overlap, and the preferred size holds the whole sequence's records if
+ * they take at most 2 GiB. Any workspace that holds the whole sequence's records, or two chunk
+ * records per (batch, head) plus those 256 bytes, is accepted; a smaller one just means shorter
+ * segments. linattn_prefill_fwd accepts the same sizes and keeps per-block partial states in
+ * the workspace instead (a smaller one means fewer, longer blocks).
+ * Returns 0 for an unsupported shape or L = 0. */
 size_t gdn_prefill_workspace_size(int B, int H, int L, int Dk, int Dv, int dtype);
 
 /*

@@ -152,19 +152,21 @@ def test_in_place_state_and_chaining():
     assert torch.equal(h, hf_full)
 
 
-@pytest.mark.parametrize("gdn", [True, False])
-def test_segmented_schedule_is_bitwise_identical(gdn):
-    """A small workspace forces many segments (stages overlapped on internal streams); every
-    chunk computes exactly the same arithmetic, so the result equals the one-segment run."""
-    cfg = (inputs.GDN_32K if gdn else inputs.LINATTN_8K).with_(name="seg", B=1, H=3, L=64 * 13 + 5, seed=31)
+def test_segmented_schedule_is_bitwise_identical():
+    """A small workspace forces many segments of the gated delta-rule prefill (stages overlapped on
+    internal streams); every chunk computes exactly the same arithmetic, so the result equals the
+    one-segment run. (Linear attention splits the sequence into blocks by workspace size instead,
+    which changes the order of its sums: tests/test_gpu_linattn_blocks.py checks small workspaces
+    against the oracle.)"""
+    cfg = inputs.GDN_32K.with_(name="seg", B=1, H=3, L=64 * 13 + 5, seed=31)
     x = inputs.prefill_inputs(cfg)
     dt = torch.bfloat16
     q, k, v = (dev_tensor(x[n], dt) for n in ("q", "k", "v"))
     h0 = dev_tensor(x["h0"], torch.float32)
-    args = (dev_tensor(x["beta"], torch.float32), dev_tensor(x["log_alpha"], torch.float32)) if gdn else ()
-    fn = ops.gdn_prefill_fwd if gdn else ops.linattn_prefill_fwd
+    args = (dev_tensor(x["beta"], torch.float32), dev_tensor(x["log_alpha"], torch.float32))
+    fn = ops.gdn_prefill_fwd
     rec = ops.prefill_workspace_size(1, 1, 64, 128, dt) * cfg.H
-    say(f"case segmented gdn={gdn}")
+    say("case segmented gdn")
     o1, h1 = fn(q, k, v, *args, h0)
     for seg in (1, 2, 5):   # segment length in chunks: two buffers of seg records and the counters
         ws = torch.empty(2 * seg * rec + 256, dtype=torch.uint8, device="cuda")
@@ -299,3 +301,16 @@ def test_decode_equals_prefill_of_one_token():
     torch.cuda.synchronize()
     assert max_rel_err(host(o_dec), o_pf[:, :, 0], axes=(2,)) < 1e-2
     assert max_rel_err(host(state), hf) < 1e-2
+
+
+def test_preferred_workspace_whole_sequence_when_chain_fills_device():
+    """With more (batch, head) slices than the sequential stage leaves CUs free for (32 heads at
+    d = 128 on 256 CUs), the preferred workspace holds the whole sequence's records; with 16 heads
+    it is two segment buffers."""
+    rec = ops.prefill_workspace_size(1, 1, 64, 128, torch.bfloat16)
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    full = ops.prefill_workspace_size(1, 32, 32768, 128, torch.bfloat16)
+    if 8 * 4 * 8 >= cus:
+        assert full == 512 * 32 * rec
+    seg = ops.prefill_workspace_size(1, 16, 131072, 128, torch.bfloat16)
+    assert seg < 2048 * 16 * rec and (seg - 256) % (2 * 16 * rec) == 0
