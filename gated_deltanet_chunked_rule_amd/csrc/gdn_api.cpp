@@ -87,17 +87,17 @@ int validate_prefill(const void* q, const void* k, const void* v, const float* b
     return GDN_OK;
 }
 
+// the gated delta-rule prefill entry points
 int prefill(const void* q, const void* k, const void* v, const float* beta, const float* log_alpha,
             const unsigned char* keep, bool skip, const float* h0, void* o, float* h_final, int B, int H, int L,
-            int Dk, int Dv, int dtype, void* workspace, size_t workspace_bytes, void* stream, bool delta,
-            int band = 3) {
+            int Dk, int Dv, int dtype, void* workspace, size_t workspace_bytes, void* stream, int band = 3) {
     if (band < 0 || band > 3) return GDN_ERR_SHAPE;
     int st = validate_prefill(q, k, v, beta, log_alpha, keep, skip, h0, o, h_final, B, H, L, Dk, Dv, dtype,
-                              workspace, workspace_bytes, delta);
+                              workspace, workspace_bytes, true);
     if (st != GDN_OK) return st;
     st = check_device();
     if (st != GDN_OK) return st;
-    return gdn::launch_prefill(q, k, v, beta, log_alpha, keep, h0, o, h_final, B * H, L, Dk, dtype, delta, band,
+    return gdn::launch_prefill(q, k, v, beta, log_alpha, keep, h0, o, h_final, B * H, L, Dk, dtype, band,
                                workspace, workspace_bytes, static_cast<hipStream_t>(stream)) == 0
                ? GDN_OK
                : GDN_ERR_LAUNCH;
@@ -131,21 +131,21 @@ int gdn_prefill_fwd(const void* q, const void* k, const void* v, const float* be
                     const float* h0, void* o, float* h_final, int B, int H, int L, int Dk, int Dv, int dtype,
                     void* workspace, size_t workspace_bytes, void* stream) {
     return prefill(q, k, v, beta, log_alpha, nullptr, false, h0, o, h_final, B, H, L, Dk, Dv, dtype, workspace,
-                   workspace_bytes, stream, true);
+                   workspace_bytes, stream);
 }
 
 int gdn_prefill_skip_fwd(const void* q, const void* k, const void* v, const float* beta, const float* log_alpha,
                          const unsigned char* keep, const float* h0, void* o, float* h_final, int B, int H, int L,
                          int Dk, int Dv, int dtype, void* workspace, size_t workspace_bytes, void* stream) {
     return prefill(q, k, v, beta, log_alpha, keep, true, h0, o, h_final, B, H, L, Dk, Dv, dtype, workspace,
-                   workspace_bytes, stream, true);
+                   workspace_bytes, stream);
 }
 
 int gdn_prefill_banded_fwd(const void* q, const void* k, const void* v, const float* beta, const float* log_alpha,
                            const float* h0, void* o, float* h_final, int B, int H, int L, int Dk, int Dv, int dtype,
                            int band, void* workspace, size_t workspace_bytes, void* stream) {
     return prefill(q, k, v, beta, log_alpha, nullptr, false, h0, o, h_final, B, H, L, Dk, Dv, dtype, workspace,
-                   workspace_bytes, stream, true, band);
+                   workspace_bytes, stream, band);
 }
 
 int linattn_prefill_fwd(const void* q, const void* k, const void* v, const float* beta, const float* log_alpha,
@@ -158,7 +158,7 @@ int linattn_prefill_fwd(const void* q, const void* k, const void* v, const float
     if (st != GDN_OK) return st;
     const hipStream_t s = static_cast<hipStream_t>(stream);
     const int rc = L == 0 ? gdn::launch_prefill(q, k, v, nullptr, nullptr, nullptr, h0, o, h_final, B * H, 0, Dk,
-                                                dtype, false, 3, workspace, workspace_bytes, s)
+                                                dtype, 3, workspace, workspace_bytes, s)
                           : gdn::launch_linattn(q, k, v, log_alpha, h0, o, h_final, B * H, L, Dk, dtype, workspace,
                                                 workspace_bytes, s);
     return rc == 0 ? GDN_OK : GDN_ERR_LAUNCH;

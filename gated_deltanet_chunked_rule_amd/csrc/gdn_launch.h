@@ -13,9 +13,10 @@ size_t prefill_workspace_min_bytes(long BH, long L, int D, int dtype);  // small
 
 // keep: [BH][ceil(L/64)] chunk keep mask (nonzero = apply the chunk's state update), or NULL (all)
 // band: 16 x 16 blocks of the intra-chunk inverse kept below its diagonal, 0 .. 3 (3 = exact)
+// L = 0 copies h0 (or zeros) to h_final.
 int launch_prefill(const void* q, const void* k, const void* v, const float* beta, const float* log_alpha,
                    const unsigned char* keep, const float* h0, void* o, float* h_final, int BH, long L, int D,
-                   int dtype, bool delta, int band, void* ws, size_t ws_bytes, hipStream_t stream);
+                   int dtype, int band, void* ws, size_t ws_bytes, hipStream_t stream);
 
 // Causal linear attention, plain (log_alpha NULL) or with a per-token decay, block-parallel.
 // The workspace (at least prefill_workspace_min_bytes) holds the blocks' state tiles; a smaller

@@ -1,4 +1,4 @@
-// Chunked prefill of the gated delta rule (and of plain causal linear attention) on gfx950.
+// Chunked prefill of the gated delta rule on gfx950.
 //
 // The SparseGDN article (fileenergy.com, section "Why GDN prefill is expensive") splits chunked
 // GDN prefill into three sources of work: the intra-chunk delta-system solve, the sequential
@@ -28,7 +28,6 @@
 //                 and store waves write it.
 // Long sequences run as segments through a pair of workspace buffers: prep of later segments
 // on a side stream beside the chain of the current one on the caller's stream.
-// Plain linear attention uses the same kernels with T = I, W = 0, Ut = V, g = 0.
 #include <mutex>
 #include <type_traits>
 
@@ -254,7 +253,7 @@ struct PrepCfg {
     static constexpr size_t LDS = O_Q + (ROWS + 15) / 16 * 16;
 };
 
-template <int D, class E, bool DELTA>
+template <int D, class E>
 __global__ __launch_bounds__(256) void prep_kernel(PrefArgs a) {
     using T = typename E::T;
     using M = MM<E>;
@@ -294,8 +293,8 @@ __global__ __launch_bounds__(256) void prep_kernel(PrefArgs a) {
     if (w == 0) {
         float la = 0.f, bt = 0.f;
         if (lane < n) {
-            if (a.log_alpha) la = a.log_alpha[tok0 + lane];   // optional without the delta term
-            if (DELTA) bt = a.beta[tok0 + lane];
+            la = a.log_alpha[tok0 + lane];
+            bt = a.beta[tok0 + lane];
         }
         const float g = wave_scan(la, lane);
         const float gC = __shfl(g, 63);
@@ -306,7 +305,7 @@ __global__ __launch_bounds__(256) void prep_kernel(PrefArgs a) {
         skh[lane] = __expf(gC - g);
         reinterpret_cast<float*>(rec + Ly::A_EG)[lane] = eg;
         if (lane == 0) {
-            *reinterpret_cast<float*>(rec + Ly::A_DEC) = a.log_alpha ? __expf(gC) : 1.f;
+            *reinterpret_cast<float*>(rec + Ly::A_DEC) = __expf(gC);
             *reinterpret_cast<unsigned*>(rec + Ly::A_KEEP) =
                 a.keep ? (a.keep[(size_t)bh * a.nchk + a.c0 + cl] != 0 ? 1u : 0u) : 1u;
         }
@@ -391,28 +390,7 @@ __global__ __launch_bounds__(256) void prep_kernel(PrefArgs a) {
             t[st] = M::mma(row_frag_raw<E>(R + (16 * st + m) * KP, KB * (dt / FPD), j), sel, f32x4{0.f, 0.f, 0.f, 0.f});
     };
 
-    if constexpr (!DELTA) {
-        // linear attention without the delta term: Khat = e^{g_C - g} K (K without gates), Ut = V
-#pragma unroll
-        for (int i = 0; i < DPW; ++i) {
-            const int dt = FPD * grp + i;
-            f32x4 kc[4], vc[4];
-            tiles(Kr, i, kc);
-            tiles(Vr, i, vc);
-#pragma unroll
-            for (int kt = 0; kt < NKT; ++kt)
-                if (kt % WPG == w % WPG)
-                    st_frag(rec + Ly::A_KH + (size_t)(dt * NKT + kt) * Ly::FR, lane,
-                            a.log_alpha ? cols_frag<E>(&kc[FPD * kt], skh + KB * kt, j) : cols_frag<E>(&kc[FPD * kt]));
-#pragma unroll
-            for (int r = 0; r < RPW; ++r) {
-                const int rt = rt0 + r;
-                T* dst = reinterpret_cast<T*>(rec + Ly::A_UT) + ((size_t)(dt * 4 + rt) * 64 + lane) * 4;
-                store4(dst, make_float4(vc[rt][0], vc[rt][1], vc[rt][2], vc[rt][3]));
-            }
-        }
-        return;
-    } else {
+    {
         // Gram tiles (rt, st), st <= rt, of K K^T: ten tiles over the four waves
         f32x4 gacc[3];
 #pragma unroll
@@ -575,7 +553,7 @@ __global__ __launch_bounds__(256) void prep_kernel(PrefArgs a) {
 // 6, 7 beside them (they mostly wait). Where the staging does not fit beside the ring (fp32 at
 // Dk = 128) the compute waves form and store the outputs themselves, handing each other their
 // halves of H^T Q^T through LDS; that puts the output work on the chain's dependence path.
-template <int D, class E, bool DELTA>
+template <int D, class E>
 struct ChainCfg {
     using Ly = Layout<D, E>;
     static constexpr int NCW = D / 16;                                   // workgroups per slice
@@ -588,7 +566,7 @@ struct ChainCfg {
     static_assert(UTSUB % 2048 == 0, "Ut splits into whole blocks per loader wave");
     static constexpr int DMA_OPS = BPW + UTL;                            // loads per loader wave and chunk
     static constexpr size_t XHALF = (size_t)4 * 64 * 16;                 // one wave's partial W H
-    static constexpr size_t XBYTES = DELTA ? (size_t)2 * 2 * XHALF : 0; // [step parity][half]
+    static constexpr size_t XBYTES = (size_t)2 * 2 * XHALF;             // [step parity][half]
     static constexpr size_t LDS_MAX = 160 * 1024;                        // gfx950: 160 KB per workgroup
     // output waves: one step's staged bf16 H (both halves) and U fragments, three steps deep
     static constexpr size_t STB = (size_t)(Ly::NKD + Ly::NKT) * 1024;
@@ -649,10 +627,10 @@ __device__ __forceinline__ unsigned lds_addr(const void* p) {
 
 // Loader wave lw's share of chunk c's loads into slot s: BPW 1 KB blocks of the -W / Khat^T
 // fragments (interleaved with the other loader's) and its half of the Ut tiles.
-template <int D, class E, bool DELTA>
+template <int D, class E>
 __device__ __forceinline__ void chain_issue(unsigned char* smem, const unsigned char* rec, int s, int cg, int lw,
                                             int lane) {
-    using C = ChainCfg<D, E, DELTA>;
+    using C = ChainCfg<D, E>;
     using Ly = Layout<D, E>;
     const unsigned base = lds_addr(smem + (size_t)s * C::SLOT);
 #pragma unroll
@@ -674,20 +652,20 @@ __device__ __forceinline__ void chain_issue(unsigned char* smem, const unsigned 
 // barrier c - 1), wait for chunk c + 1 (read by the compute waves after barrier c), barrier c.
 // In a segmented call it first waits for the segment's prep count, and at the end counts itself
 // in for the chain's: the count tells the prep stage that this launch has read its buffer.
-template <int D, class E, bool DELTA>
+template <int D, class E>
 __device__ __forceinline__ void chain_loader(const PrefArgs& a, unsigned char* smem, const unsigned char* rec0, int nch,
                                              int cg, int lw, int lane) {
     using Ly = Layout<D, E>;
-    using C = ChainCfg<D, E, DELTA>;
+    using C = ChainCfg<D, E>;
     constexpr int NS = C::NS;
     if (a.flags) wait_count(a.flags, FL_PREP, (unsigned)a.sgi + 1);   // the segment's records are written
     for (int c = 0; c < NS - 1; ++c)
-        chain_issue<D, E, DELTA>(smem, rec0 + (size_t)min(c, nch - 1) * Ly::REC, c, cg, lw, lane);
+        chain_issue<D, E>(smem, rec0 + (size_t)min(c, nch - 1) * Ly::REC, c, cg, lw, lane);
     wait_vmcnt<0>();
     lds_barrier();
     for (int c = 0; c < nch; ++c) {
         const int cn = c + NS - 1;   // always issued (clamped to the last chunk): fixed counts
-        chain_issue<D, E, DELTA>(smem, rec0 + (size_t)min(cn, nch - 1) * Ly::REC, cn % NS, cg, lw, lane);
+        chain_issue<D, E>(smem, rec0 + (size_t)min(cn, nch - 1) * Ly::REC, cn % NS, cg, lw, lane);
         wait_vmcnt<C::WAITN>();
         lds_barrier();
     }
@@ -751,13 +729,13 @@ __device__ __forceinline__ void store_packed(const PrefArgs& a, int bh, int cg, 
 // One barrier per step, between A and B: the partial products alternate between two LDS areas
 // by step parity, so an area is rewritten only after the partner has passed the next barrier.
 // Ut is read in A, before the barrier after which its slot may be refilled.
-template <int D, class E, bool DELTA, int HH>
+template <int D, class E, int HH>
 __device__ __forceinline__ void chain_compute(const PrefArgs& a, unsigned char* smem, const unsigned char* rec0,
                                               int nch, int bh, int cg, int lane) {
     using T = typename E::T;
     using M = MM<E>;
     using Ly = Layout<D, E>;
-    using C = ChainCfg<D, E, DELTA>;
+    using C = ChainCfg<D, E>;
     using frag = typename M::frag;
     constexpr int NKD = Ly::NKD, NKT = Ly::NKT, NDT = Ly::NDT, NS = C::NS;
     constexpr int HKD = NKD / 2, HDT = NDT / 2;   // fragments / tiles of one row half
@@ -810,13 +788,11 @@ __device__ __forceinline__ void chain_compute(const PrefArgs& a, unsigned char* 
     frag wf[4 * HKD], kf[HDT * NKT];
     auto read_slot = [&](int s) {
         const unsigned char* slot = smem + (size_t)s * C::SLOT;
-        if constexpr (DELTA) {
 #pragma unroll
-            for (int rt = 0; rt < 4; ++rt)
+        for (int rt = 0; rt < 4; ++rt)
 #pragma unroll
-                for (int kk = 0; kk < HKD; ++kk)
-                    wf[rt * HKD + kk] = ld_frag<frag>(slot + Ly::A_W + (size_t)(rt * NKD + HH * HKD + kk) * Ly::FR, lane);
-        }
+            for (int kk = 0; kk < HKD; ++kk)
+                wf[rt * HKD + kk] = ld_frag<frag>(slot + Ly::A_W + (size_t)(rt * NKD + HH * HKD + kk) * Ly::FR, lane);
 #pragma unroll
         for (int t = 0; t < HDT; ++t)
 #pragma unroll
@@ -853,43 +829,29 @@ __device__ __forceinline__ void chain_compute(const PrefArgs& a, unsigned char* 
         f32x4 P[4];
         const float dec = __uint_as_float(S.dec);
         const unsigned keep = __builtin_amdgcn_readfirstlane(S.keep);
-        if constexpr (DELTA) {
 #pragma unroll
-            for (int rt = 0; rt < 4; ++rt) {
-                if ((rt >> 1) == HH) {
-                    const float4 x = load4(ut + ((size_t)rt * 64 + lane) * 4);
-                    P[rt] = f32x4{x.x, x.y, x.z, x.w};
-                } else {
-                    P[rt] = f32x4{0.f, 0.f, 0.f, 0.f};
-                }
-            }
-#pragma unroll
-            for (int kk = 0; kk < HKD; ++kk)
-#pragma unroll
-                for (int rt = 0; rt < 4; ++rt) P[rt] = M::mma(wf[rt * HKD + kk], Hf[kk], P[rt]);
-#pragma unroll
-            for (int rt = 0; rt < 4; ++rt) X[(HH * 4 + rt) * 64 + lane] = P[rt];
-#pragma unroll
-            for (int t = 0; t < HDT; ++t) H[t] = f32x4{H[t][0] * dec, H[t][1] * dec, H[t][2] * dec, H[t][3] * dec};
-        } else {
-#pragma unroll
-            for (int rt = 0; rt < 4; ++rt) {
+        for (int rt = 0; rt < 4; ++rt) {
+            if ((rt >> 1) == HH) {
                 const float4 x = load4(ut + ((size_t)rt * 64 + lane) * 4);
                 P[rt] = f32x4{x.x, x.y, x.z, x.w};
+            } else {
+                P[rt] = f32x4{0.f, 0.f, 0.f, 0.f};
             }
-#pragma unroll
-            for (int t = 0; t < HDT; ++t) H[t] = f32x4{H[t][0] * dec, H[t][1] * dec, H[t][2] * dec, H[t][3] * dec};
         }
+#pragma unroll
+        for (int kk = 0; kk < HKD; ++kk)
+#pragma unroll
+            for (int rt = 0; rt < 4; ++rt) P[rt] = M::mma(wf[rt * HKD + kk], Hf[kk], P[rt]);
+#pragma unroll
+        for (int rt = 0; rt < 4; ++rt) X[(HH * 4 + rt) * 64 + lane] = P[rt];
+#pragma unroll
+        for (int t = 0; t < HDT; ++t) H[t] = f32x4{H[t][0] * dec, H[t][1] * dec, H[t][2] * dec, H[t][3] * dec};
         lds_barrier();   // partial products exchanged; chunk c + 1's slot is complete
         f32x4 U[4];
 #pragma unroll
         for (int rt = 0; rt < 4; ++rt) {
-            if constexpr (DELTA) {
-                const f32x4 po = X[((1 - HH) * 4 + rt) * 64 + lane];
-                U[rt] = f32x4{P[rt][0] + po[0], P[rt][1] + po[1], P[rt][2] + po[2], P[rt][3] + po[3]};
-            } else {
-                U[rt] = P[rt];
-            }
+            const f32x4 po = X[((1 - HH) * 4 + rt) * 64 + lane];
+            U[rt] = f32x4{P[rt][0] + po[0], P[rt][1] + po[1], P[rt][2] + po[2], P[rt][3] + po[3]};
         }
         frag Uf[NKT];
 #pragma unroll
@@ -977,12 +939,12 @@ __device__ __forceinline__ void chain_compute(const PrefArgs& a, unsigned char* 
 // e^g (H^T Q^T) + U^T P^T over all of d, then the loads of chunk c - 1 + NSET into the register
 // set just used, then the tiles into LDS for the store waves (the last chunk's it stores
 // itself). Its barrier sequence is the compute waves': the first, one per step, the last.
-template <int D, class E, bool DELTA, int HH>
+template <int D, class E, int HH>
 __device__ __forceinline__ void chain_output(const PrefArgs& a, unsigned char* smem, const unsigned char* rec0,
                                              int nch, int bh, int cg, int lane) {
     using M = MM<E>;
     using Ly = Layout<D, E>;
-    using C = ChainCfg<D, E, DELTA>;
+    using C = ChainCfg<D, E>;
     using frag = typename M::frag;
     constexpr int NKD = Ly::NKD, NKT = Ly::NKT;
     constexpr int R[2] = {HH == 0 ? 0 : 1, HH == 0 ? 3 : 2};
@@ -1068,10 +1030,10 @@ __device__ __forceinline__ void chain_output(const PrefArgs& a, unsigned char* s
 // Store wave HH of a chain workgroup (with output waves): iteration c follows barrier c, after
 // which the output tiles of chunk c - 2 are in LDS; it writes tiles {0, 3} (HH = 0) or {1, 2}
 // to memory. It loads nothing, so it never waits for its stores.
-template <int D, class E, bool DELTA, int HH>
+template <int D, class E, int HH>
 __device__ __forceinline__ void chain_storer(const PrefArgs& a, unsigned char* smem, int nch, int bh, int cg,
                                              int lane) {
-    using C = ChainCfg<D, E, DELTA>;
+    using C = ChainCfg<D, E>;
     constexpr int R[2] = {HH == 0 ? 0 : 1, HH == 0 ? 3 : 2};
     lds_barrier();
     for (int cc = 0; cc <= nch; ++cc) {
@@ -1087,10 +1049,10 @@ __device__ __forceinline__ void chain_storer(const PrefArgs& a, unsigned char* s
 // One workgroup per CU (its LDS ring). Waves 0 and 1 compute (row half w); with output waves,
 // waves 2 and 3 form the outputs, waves 4 and 5 load and waves 6 and 7 store the outputs, else
 // waves 2 and 3 load. The roles run separate loops with the same barrier sequence.
-template <int D, class E, bool DELTA>
-__global__ __launch_bounds__((ChainCfg<D, E, DELTA>::THREADS)) void chain_kernel(PrefArgs a) {
+template <int D, class E>
+__global__ __launch_bounds__((ChainCfg<D, E>::THREADS)) void chain_kernel(PrefArgs a) {
     using Ly = Layout<D, E>;
-    using C = ChainCfg<D, E, DELTA>;
+    using C = ChainCfg<D, E>;
     extern __shared__ __align__(16) unsigned char smem[];
     // blockIdx -> (slice, column group) so that all column groups of one slice run on the same
     // XCD (workgroups are dealt to the 8 XCDs round-robin) and share its L2.
@@ -1103,19 +1065,19 @@ __global__ __launch_bounds__((ChainCfg<D, E, DELTA>::THREADS)) void chain_kernel
     constexpr int LW = C::OUTW ? 4 : 2;   // first loader wave
     if (C::OUTW && w >= 6) {
         if (w == 7)
-            chain_storer<D, E, DELTA, 1>(a, smem, a.nseg, bh, cg, lane);
+            chain_storer<D, E, 1>(a, smem, a.nseg, bh, cg, lane);
         else
-            chain_storer<D, E, DELTA, 0>(a, smem, a.nseg, bh, cg, lane);
+            chain_storer<D, E, 0>(a, smem, a.nseg, bh, cg, lane);
     } else if (w >= LW)
-        chain_loader<D, E, DELTA>(a, smem, rec0, a.nseg, cg, w - LW, lane);
+        chain_loader<D, E>(a, smem, rec0, a.nseg, cg, w - LW, lane);
     else if (C::OUTW && w == 3)
-        chain_output<D, E, DELTA, 1>(a, smem, rec0, a.nseg, bh, cg, lane);
+        chain_output<D, E, 1>(a, smem, rec0, a.nseg, bh, cg, lane);
     else if (C::OUTW && w == 2)
-        chain_output<D, E, DELTA, 0>(a, smem, rec0, a.nseg, bh, cg, lane);
+        chain_output<D, E, 0>(a, smem, rec0, a.nseg, bh, cg, lane);
     else if (w == 1)
-        chain_compute<D, E, DELTA, 1>(a, smem, rec0, a.nseg, bh, cg, lane);
+        chain_compute<D, E, 1>(a, smem, rec0, a.nseg, bh, cg, lane);
     else
-        chain_compute<D, E, DELTA, 0>(a, smem, rec0, a.nseg, bh, cg, lane);
+        chain_compute<D, E, 0>(a, smem, rec0, a.nseg, bh, cg, lane);
 }
 
 // h_final = h0 (or zeros) for L = 0
@@ -1124,11 +1086,11 @@ __global__ void copy_state_kernel(const float* __restrict__ src, float* __restri
     if (i < n) dst[i] = src ? src[i] : 0.f;
 }
 
-template <int D, class E, bool DELTA>
+template <int D, class E>
 struct Launch {
     using T = typename E::T;
     using Ly = Layout<D, E>;
-    using CC = ChainCfg<D, E, DELTA>;
+    using CC = ChainCfg<D, E>;
     static constexpr size_t LDS_PREP = PrepCfg<D, E>::LDS;
     static constexpr size_t LDS_CHAIN = CC::LDS;
     // While the chain runs on some of the CUs, the prep stage beside it is held to three
@@ -1140,18 +1102,18 @@ struct Launch {
     // raise the dynamic-LDS limits once per process (every caller sets the same values)
     static bool attributes() {
         static const bool ok =
-            hipFuncSetAttribute(reinterpret_cast<const void*>(&prep_kernel<D, E, DELTA>),
+            hipFuncSetAttribute(reinterpret_cast<const void*>(&prep_kernel<D, E>),
                                 hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds_prep(true)) == hipSuccess &&
-            hipFuncSetAttribute(reinterpret_cast<const void*>(&chain_kernel<D, E, DELTA>),
+            hipFuncSetAttribute(reinterpret_cast<const void*>(&chain_kernel<D, E>),
                                 hipFuncAttributeMaxDynamicSharedMemorySize, (int)LDS_CHAIN) == hipSuccess;
         return ok;
     }
     static int chain_blocks(int BH) { return 8 * ((BH + 7) / 8) * CC::NCW; }
     static void prep(const PrefArgs& a, hipStream_t s, bool beside = false) {
-        hipLaunchKernelGGL((prep_kernel<D, E, DELTA>), dim3(a.nseg, a.BH), dim3(256), lds_prep(beside), s, a);
+        hipLaunchKernelGGL((prep_kernel<D, E>), dim3(a.nseg, a.BH), dim3(256), lds_prep(beside), s, a);
     }
     static void chain(const PrefArgs& a, hipStream_t s) {
-        hipLaunchKernelGGL((chain_kernel<D, E, DELTA>), dim3(chain_blocks(a.BH)), dim3(CC::THREADS), LDS_CHAIN, s, a);
+        hipLaunchKernelGGL((chain_kernel<D, E>), dim3(chain_blocks(a.BH)), dim3(CC::THREADS), LDS_CHAIN, s, a);
     }
 };
 
@@ -1177,9 +1139,9 @@ static bool init_ctx(StreamCtx& c, int dev) {
     return true;
 }
 
-template <int D, class E, bool DELTA>
+template <int D, class E>
 static int launch_prefill_t(PrefArgs a, long nch, size_t ws_bytes, hipStream_t stream) {
-    using LN = Launch<D, E, DELTA>;
+    using LN = Launch<D, E>;
     if (!LN::attributes()) return -1;
     const size_t rec = Layout<D, E>::REC * (size_t)a.BH;
     if (ws_bytes >= (size_t)nch * rec) {   // whole sequence in one segment, caller's stream only
@@ -1242,7 +1204,7 @@ static int launch_prefill_t(PrefArgs a, long nch, size_t ws_bytes, hipStream_t s
 
 int launch_prefill(const void* q, const void* k, const void* v, const float* beta, const float* log_alpha,
                    const unsigned char* keep, const float* h0, void* o, float* h_final, int BH, long L, int D,
-                   int dtype, bool delta, int band, void* ws, size_t ws_bytes, hipStream_t stream) {
+                   int dtype, int band, void* ws, size_t ws_bytes, hipStream_t stream) {
     if (L == 0) {
         const size_t n = (size_t)BH * D * D;
         if (h0 == h_final) return 0;
@@ -1252,14 +1214,10 @@ int launch_prefill(const void* q, const void* k, const void* v, const float* bet
     const long nch = (L + CH - 1) / CH;
     PrefArgs a{q, k, v, beta, log_alpha, h0, o, h_final, static_cast<unsigned char*>(ws), L, BH, 0, 0, 0, keep, (int)nch,
                band};
-#define GDN_PF(DD, EE)                                                                 \
-    return delta ? launch_prefill_t<DD, EE, true>(a, nch, ws_bytes, stream)            \
-                 : launch_prefill_t<DD, EE, false>(a, nch, ws_bytes, stream)
-    if (D == 128 && dtype == 0) GDN_PF(128, BF16);
-    if (D == 128) GDN_PF(128, F32);
-    if (dtype == 0) GDN_PF(64, BF16);
-    GDN_PF(64, F32);
-#undef GDN_PF
+    if (D == 128 && dtype == 0) return launch_prefill_t<128, BF16>(a, nch, ws_bytes, stream);
+    if (D == 128) return launch_prefill_t<128, F32>(a, nch, ws_bytes, stream);
+    if (dtype == 0) return launch_prefill_t<64, BF16>(a, nch, ws_bytes, stream);
+    return launch_prefill_t<64, F32>(a, nch, ws_bytes, stream);
 }
 
 }  // namespace gdn
