@@ -633,9 +633,15 @@ __device__ __forceinline__ void chain_issue(unsigned char* smem, const unsigned 
     using C = ChainCfg<D, E>;
     using Ly = Layout<D, E>;
     const unsigned base = lds_addr(smem + (size_t)s * C::SLOT);
+    // The column groups of a slice read the same fragments at about the same time; each starts at
+    // a different block, so that their requests go to different L2 channels at any moment rather
+    // than queueing eight deep on one (B=1 H=16 L=128K, chain alone: 2.0 -> 1.75 ms).
+    const int rot = (cg * C::BPW / C::NCW) % C::BPW;   // < BPW
 #pragma unroll
     for (int i = 0; i < C::BPW; ++i) {
-        const unsigned blk = (unsigned)(lw + 2 * i) * 1024u;
+        int ii = i + rot;
+        ii = ii >= C::BPW ? ii - C::BPW : ii;
+        const unsigned blk = (unsigned)(lw + 2 * ii) * 1024u;
         dma16(rec + blk + lane * 16, base + blk);
     }
     const unsigned ubase = lds_addr(smem + C::O_UT + (size_t)s * C::UTSUB);
