@@ -139,8 +139,12 @@ def bench_prefill(torch, ops, cfg, steps, warmup, gdn=True, verbose=False, varia
     o = torch.empty_like(v)
     hf = torch.empty((cfg.B, cfg.H, cfg.Dk, cfg.Dv), device="cuda")
     nchk = (cfg.L + 63) // 64
-    wsb = (ops.prefill_workspace_size(1, 1, 64, cfg.Dk, q.dtype) * cfg.B * cfg.H * nchk if one_segment
-           else ops.prefill_workspace_size(cfg.B, cfg.H, cfg.L, cfg.Dk, q.dtype))
+    if not gates or variant == "gla":   # linear attention: blocks of chunks
+        wsb = ops.linattn_prefill_workspace_size(cfg.B, cfg.H, cfg.L, cfg.Dk, q.dtype)
+    elif one_segment:
+        wsb = ops.prefill_workspace_size(1, 1, 64, cfg.Dk, q.dtype) * cfg.B * cfg.H * nchk
+    else:
+        wsb = ops.prefill_workspace_size(cfg.B, cfg.H, cfg.L, cfg.Dk, q.dtype)
     ws = torch.empty(wsb, dtype=torch.uint8, device="cuda")
     nchunk = cfg.B * cfg.H * nchk
     kept = nchunk

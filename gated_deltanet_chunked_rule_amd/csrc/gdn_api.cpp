@@ -56,6 +56,9 @@ int validate_prefill(const void* q, const void* k, const void* v, const float* b
                      int L, int Dk, int Dv, int dtype, void* workspace, size_t workspace_bytes, bool delta) {
     int st = check_dims(B, H, L, Dk, Dv, dtype);
     if (st != GDN_OK) return st;
+    // the smallest workspace the entry point accepts (0: none needed)
+    const size_t need = delta ? gdn::prefill_workspace_min_bytes((long)B * H, L, Dk, dtype)
+                              : gdn::linattn_workspace_min_bytes((long)B * H, L, Dk);
     if (!h_final) return GDN_ERR_NULL;
     if (L > 0 && (!q || !k || !v || !o)) return GDN_ERR_NULL;   // L = 0 reads no token data
     if (delta && L > 0 && (!beta || !log_alpha)) return GDN_ERR_NULL;
@@ -67,7 +70,6 @@ int validate_prefill(const void* q, const void* k, const void* v, const float* b
     const size_t esz = dtype == GDN_BF16 ? 2 : 4;
     const size_t BH = (size_t)B * H;
     const size_t tok = BH * (size_t)L;
-    const size_t need = gdn::prefill_workspace_min_bytes((long)BH, L, Dk, dtype);
     if (need > 0) {
         if (!workspace || workspace_bytes < need) return GDN_ERR_WORKSPACE;
         if (!aligned(workspace, 256)) return GDN_ERR_ALIGN;
@@ -162,6 +164,11 @@ int linattn_prefill_fwd(const void* q, const void* k, const void* v, const float
                           : gdn::launch_linattn(q, k, v, log_alpha, h0, o, h_final, B * H, L, Dk, dtype, workspace,
                                                 workspace_bytes, s);
     return rc == 0 ? GDN_OK : GDN_ERR_LAUNCH;
+}
+
+size_t linattn_prefill_workspace_size(int B, int H, int L, int Dk, int Dv, int dtype) {
+    if (check_dims(B, H, L, Dk, Dv, dtype) != GDN_OK) return 0;
+    return gdn::linattn_workspace_bytes((long)B * H, L, Dk);
 }
 
 size_t linattn_bidir_workspace_size(int B, int H, int L, int Dk, int Dv, int dtype) {

@@ -19,8 +19,10 @@ int launch_prefill(const void* q, const void* k, const void* v, const float* bet
                    int dtype, int band, void* ws, size_t ws_bytes, hipStream_t stream);
 
 // Causal linear attention, plain (log_alpha NULL) or with a per-token decay, block-parallel.
-// The workspace (at least prefill_workspace_min_bytes) holds the blocks' state tiles; a smaller
-// one means fewer, longer blocks.
+// The workspace holds each block's state tiles (one block per slice at the minimum; a smaller
+// workspace means fewer, longer blocks).
+size_t linattn_workspace_bytes(long BH, long L, int D);      // preferred
+size_t linattn_workspace_min_bytes(long BH, long L, int D);  // smallest accepted
 int launch_linattn(const void* q, const void* k, const void* v, const float* log_alpha, const float* h0, void* o,
                    float* h_final, int BH, long L, int D, int dtype, void* ws, size_t ws_bytes, hipStream_t stream);
 

@@ -390,6 +390,18 @@ int la_blocks(long BH, long nch, size_t tiles, size_t ws_bytes) {
 
 }  // namespace
 
+static size_t la_tiles(int D) { return D == 128 ? LaLayout<128>::TILES : LaLayout<64>::TILES; }
+
+size_t linattn_workspace_bytes(long BH, long L, int D) {
+    if (L <= 0) return 0;
+    const long nch = (L + CH - 1) / CH;
+    return (size_t)BH * la_blocks(BH, nch, la_tiles(D), ~(size_t)0) * (la_tiles(D) + 4);
+}
+
+size_t linattn_workspace_min_bytes(long BH, long L, int D) {
+    return L <= 0 ? 0 : (size_t)BH * (la_tiles(D) + 4);
+}
+
 template <int D, class E, bool GATED>
 static int launch_linattn_t(const void* q, const void* k, const void* v, const float* log_alpha, const float* h0,
                             void* o, float* h_final, long BH, long L, unsigned char* ws, size_t ws_bytes,

@@ -53,6 +53,10 @@ def prefill_workspace_size(B: int, H: int, L: int, D: int, dtype: torch.dtype) -
     return int(_lib.load().gdn_prefill_workspace_size(B, H, L, D, D, _code(dtype)))
 
 
+def linattn_prefill_workspace_size(B: int, H: int, L: int, D: int, dtype: torch.dtype) -> int:
+    return int(_lib.load().linattn_prefill_workspace_size(B, H, L, D, D, _code(dtype)))
+
+
 def _prefill(entry, q, k, v, beta, log_alpha, h0, o, h_final, workspace, stream, delta, keep=None, band=None):
     B, H, L, D = q.shape
     dev, dt = q.device, q.dtype
@@ -72,7 +76,8 @@ def _prefill(entry, q, k, v, beta, log_alpha, h0, o, h_final, workspace, stream,
         h_final = torch.empty((B, H, D, D), dtype=torch.float32, device=dev)
     _req("h_final", h_final, (B, H, D, D), torch.float32, dev)
     if workspace is None:   # the preferred size; any size the C ABI accepts works (it checks)
-        workspace = torch.empty(max(prefill_workspace_size(B, H, L, D, dt), 1), dtype=torch.uint8, device=dev)
+        size = prefill_workspace_size if delta else linattn_prefill_workspace_size
+        workspace = torch.empty(max(size(B, H, L, D, dt), 1), dtype=torch.uint8, device=dev)
     elif not workspace.is_cuda or not workspace.is_contiguous():
         raise ValueError("workspace must be a contiguous device tensor")
     lib = _lib.load()

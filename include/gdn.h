@@ -61,7 +61,7 @@ enum {
 const char *gdn_status_string(int status);
 
 /* Preferred bytes of device workspace for gdn_prefill_fwd, gdn_prefill_skip_fwd and
- * linattn_prefill_fwd at this shape.
+ * gdn_prefill_banded_fwd at this shape.
  * The workspace holds the per-chunk operands the intra-chunk stage hands to the sequential
  * stage. A short sequence is processed in one segment; a long one in segments whose stages
  * overlap (the intra-chunk stage of later segments on an internal stream beside the sequential
@@ -71,9 +71,7 @@ const char *gdn_status_string(int status);
  * CUs) the stages cannot overlap, and the preferred size holds the whole sequence's records if
  * they take at most 2 GiB. Any workspace that holds the whole sequence's records, or two chunk
  * records per (batch, head) plus those 256 bytes, is accepted; a smaller one just means shorter
- * segments. linattn_prefill_fwd accepts the same sizes and keeps per-block partial states in
- * the workspace instead (a smaller one means fewer, longer blocks).
- * Returns 0 for an unsupported shape or L = 0. */
+ * segments. Returns 0 for an unsupported shape or L = 0. */
 size_t gdn_prefill_workspace_size(int B, int H, int L, int Dk, int Dv, int dtype);
 
 /*
@@ -142,13 +140,22 @@ int gdn_prefill_banded_fwd(const void *q, const void *k, const void *v,
  * e^{g_r - g_s}) V  and  H <- e^{g_C} H0 + (e^{g_C - g} K)^T V  with g the in-chunk prefix
  * sum of log_alpha. log_alpha NULL means a = 1 (plain linear attention, AI RnD Day channel
  * post, tgstat.ru, section "Linear attention"). Same argument list as gdn_prefill_fwd; beta
- * must be NULL.
+ * must be NULL. The scalar transition lets the sequence be split into blocks of chunks whose
+ * contributions to the state are summed in parallel; the workspace holds one Dk x Dv fp32
+ * state and 4 bytes per block and (batch, head): at least B*H*(Dk*Dv*4 + 4) bytes when L > 0,
+ * linattn_prefill_workspace_size(...) preferred (more blocks). Results depend on the block
+ * split only through the order of fp32 sums. Runs on `stream` only; L = 0 copies h0 (or zeros)
+ * into h_final.
  */
 int linattn_prefill_fwd(const void *q, const void *k, const void *v,
                         const float *beta, const float *log_alpha, const float *h0,
                         void *o, float *h_final,
                         int B, int H, int L, int Dk, int Dv, int dtype,
                         void *workspace, size_t workspace_bytes, void *stream);
+
+/* Preferred bytes of device workspace for linattn_prefill_fwd at this shape (blocks of chunks
+ * for about 512 workgroups per stage); 0 for an unsupported shape or L = 0. */
+size_t linattn_prefill_workspace_size(int B, int H, int L, int Dk, int Dv, int dtype);
 
 /*
  * Bidirectional (non-causal) linear attention with a kernel feature map and an optional

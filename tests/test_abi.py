@@ -84,6 +84,20 @@ def test_prefill_host_validation(lib):
     assert _prefill(lib, h0=0x7f000000 + 16) == ALIAS  # partial h0 / h_final overlap
 
 
+def test_linattn_workspace(lib):
+    f = lib.linattn_prefill_workspace_size
+    blk = 128 * 128 * 4 + 4                             # one block's state and its summed log-gate
+    assert f(1, 1, 64, 128, 128, 0) == blk               # one chunk: one block
+    assert f(2, 2, 64 * 1000, 128, 128, 0) % (4 * blk) == 0
+    assert f(1, 1, 64 * 1000, 64, 64, 1) % (64 * 64 * 4 + 4) == 0
+    assert f(1, 1, 0, 128, 128, 0) == 0
+    assert f(1, 1, 64, 96, 96, 0) == 0
+    # smallest accepted: one block per (batch, head)
+    assert _prefill(lib, gdn=False, beta=None, H=3, L=1000, wsb=3 * blk - 1) == WORKSPACE
+    assert _prefill(lib, gdn=False, beta=None, H=3, L=1000, wsb=3 * blk) not in (NULL, ALIGN, ALIAS, WORKSPACE)
+    assert _prefill(lib, gdn=False, beta=None, L=0, ws=None, wsb=0) not in (NULL, ALIGN, ALIAS, WORKSPACE)
+
+
 def _prefill_skip(lib, keep=0x60200000, o=0x70000000, **kw):
     a = dict(q=0x10000, k=0x20000000, v=0x40000000, beta=0x60000000, la=0x60100000, h0=None, hf=0x7f000000,
              L=200, ws=0x100000000, wsb=1 << 30)

@@ -23,10 +23,13 @@ TD = {"bf16": torch.bfloat16, "f32": torch.float32}
 
 
 def _min_workspace(B, H, D, dt):
-    """The smallest workspace the prefill entry points accept for a sequence of more than two
-    chunks: two chunk records per slice and 256 bytes of counters."""
-    rec = ops.prefill_workspace_size(1, 1, 64, D, dt)
-    return torch.empty(2 * B * H * rec + 256, dtype=torch.uint8, device="cuda")
+    """The smallest workspace linattn_prefill_fwd accepts: one block (a D x D fp32 state and
+    4 bytes) per slice, so each slice is a single block of all its chunks."""
+    return torch.empty(B * H * (D * D * 4 + 4), dtype=torch.uint8, device="cuda")
+
+
+def _two_blocks_workspace(B, H, D, dt):
+    return torch.empty(2 * B * H * (D * D * 4 + 4), dtype=torch.uint8, device="cuda")
 
 
 @pytest.mark.parametrize("gated", [False, True])
@@ -41,19 +44,20 @@ def test_linattn_small_workspace_long_blocks(gated, dtype, D, L):
     q, k, v = (dev_tensor(x[n], dt) for n in ("q", "k", "v"))
     h0 = dev_tensor(x["h0"], torch.float32)
     la = dev_tensor(x["log_alpha"], torch.float32) if gated else None
-    ws = _min_workspace(cfg.B, cfg.H, D, dt)
-    o, hf = ops.linattn_prefill_fwd(q, k, v, h0, log_alpha=la, workspace=ws)
-    o2, hf2 = ops.linattn_prefill_fwd(q, k, v, h0, log_alpha=la, workspace=ws)
-    torch.cuda.synchronize()
-    assert torch.equal(o, o2) and torch.equal(hf, hf2)
     if gated:
         ro, rh = oracle.gla_prefill(x["q"], x["k"], x["v"], x["log_alpha"], x["h0"])
     else:
         ro, rh = oracle.linattn_prefill(x["q"], x["k"], x["v"], x["h0"])
     tol = TOL_BF16 if dtype == "bf16" else TOL_F32
-    eo, eh = max_rel_err(host(o), ro), max_rel_err(host(hf), rh)
-    say(f"  {cfg.name}: max rel err o {eo:.3e}, h_final {eh:.3e} (bound {tol:g})")
-    assert eo <= tol and eh <= tol, (eo, eh)
+    for mk in (_min_workspace, _two_blocks_workspace):
+        ws = mk(cfg.B, cfg.H, D, dt)
+        o, hf = ops.linattn_prefill_fwd(q, k, v, h0, log_alpha=la, workspace=ws)
+        o2, hf2 = ops.linattn_prefill_fwd(q, k, v, h0, log_alpha=la, workspace=ws)
+        torch.cuda.synchronize()
+        assert torch.equal(o, o2) and torch.equal(hf, hf2)
+        eo, eh = max_rel_err(host(o), ro), max_rel_err(host(hf), rh)
+        say(f"  {cfg.name} {mk.__name__}: max rel err o {eo:.3e}, h_final {eh:.3e} (bound {tol:g})")
+        assert eo <= tol and eh <= tol, (eo, eh)
 
 
 def test_linattn_in_place_state():
