@@ -12,7 +12,6 @@ roofline of the prefill, and the fp64 oracle timed on this host's cores on a bou
 from __future__ import annotations
 
 import argparse
-import glob
 import hashlib
 import json
 import os
@@ -31,22 +30,25 @@ PEAK_BF16_TFLOPS = 2500.0       # MI355X dense bf16 MFMA
 METRIC = "GDN prefill tokens/s at L=128K + % bf16 MFMA peak; decode state GB/s"
 
 # Memory traffic of one 128K prefill call, from rocprofv3 counter runs (FETCH_SIZE and WRITE_SIZE
-# summed over the call's prep, chain and output dispatches, each divided by what the counter
-# reads per byte for a plain copy of known size); profiles/gdn_prefill_B1H16L131072_traffic.md
-# holds the commands and the raw figures. Valid only for the kernel sources it was taken on:
-# bench.py reports it only while kernel_source_hash() still matches.
-TRAFFIC_128K = {"source_hash": "df05db91948e565e", "bytes_per_call": 6886429000}
+# summed over the call's prep and chain dispatches, each divided by what the counter reads per
+# byte for a plain copy of known size); profiles/gdn_prefill_B1H16L131072_traffic.md holds the
+# commands and the raw figures. Valid only for the kernel sources it was taken on: bench.py
+# reports it only while kernel_source_hash() still matches.
+TRAFFIC_128K = {"source_hash": "d0246ebbe0bbd210", "bytes_per_call": 6886434808}
+
+
+# the sources the gated delta-rule prefill's kernels and launches are built from
+PREFILL_SOURCES = ("gdn_api.cpp", "gdn_device.h", "gdn_launch.h", "gdn_mfma.h", "gdn_prefill.hip", "gdn_rows.h")
 
 
 def kernel_source_hash():
-    """sha256 over the HIP sources and headers of libgdn (sorted by name)."""
+    """sha256 over the sources of the gated delta-rule prefill (sorted by name)."""
     h = hashlib.sha256()
     csrc = os.path.join(ROOT, "gated_deltanet_chunked_rule_amd", "csrc")
-    for f in sorted(glob.glob(os.path.join(csrc, "*"))):
-        if f.endswith((".hip", ".h", ".cpp")):
-            h.update(os.path.basename(f).encode())
-            with open(f, "rb") as fh:
-                h.update(fh.read())
+    for name in sorted(PREFILL_SOURCES):
+        h.update(name.encode())
+        with open(os.path.join(csrc, name), "rb") as fh:
+            h.update(fh.read())
     return h.hexdigest()[:16]
 
 
@@ -272,6 +274,9 @@ def main():
                     help="with --profile-steps: whole-sequence workspace, one launch of each kernel per call")
     ap.add_argument("--profile-decode", type=int, default=0,
                     help="only run this many decode steps (for profilers), no JSON")
+    ap.add_argument("--profile-linattn", type=int, default=0,
+                    help="only run this many plain and this many gated linear-attention calls at "
+                         "B=4 H=16 L=8192 after warm-up (for profilers), no JSON")
     ap.add_argument("--copy-calibrate", type=int, default=0, metavar="BYTES",
                     help="only copy BYTES device-to-device three times (counter calibration), no JSON")
     ap.add_argument("--source-hash", action="store_true", help="print kernel_source_hash() and exit")
@@ -303,6 +308,13 @@ def main():
         c = inputs.DECODE_256x32
         r = bench_decode(torch, ops, c, args.profile_decode)
         log(f"profiled {args.profile_decode} decode steps: {r['ms_per_step']:.4f} ms/step")
+        return
+    if args.profile_linattn:
+        c = inputs.LINATTN_8K
+        r = bench_prefill(torch, ops, c, args.profile_linattn, args.warmup, gdn=False)[0]
+        rg = bench_prefill(torch, ops, c.with_(gates=True, gate_dist="long"), args.profile_linattn, args.warmup,
+                           gdn=False, variant="gla")[0]
+        log(f"profiled {args.profile_linattn} linear-attention calls: plain {r['ms']:.4f} ms, gated {rg['ms']:.4f} ms")
         return
     if args.profile_steps:
         log("generating inputs")
