@@ -73,14 +73,14 @@ size_t prefill_record_bytes(int D, int dtype) {
 }
 
 // Preferred workspace: the whole sequence if it is short, else NBUF segment buffers of about
-// SEG_TARGET bytes each, so that the three stages of consecutive segments overlap and the
-// buffers can stay resident in the 256 MB Infinity Cache between the stage that writes them
-// and the stage that reads them.
+// SEG_TARGET bytes each, so that the two stages of consecutive segments overlap and the buffers
+// can stay resident in the 256 MB Infinity Cache between the stage that writes them and the
+// stage that reads them.
 static constexpr size_t SEG_TARGET = (size_t)72 << 20;
 static constexpr int NBUF = 2;
-// A segmented call keeps three 32-bit progress counters (prep, chain, output: segments done)
-// after its buffers; the streams wait on them (hipStreamWaitValue32) rather than on events,
-// which measured about 5 us less per cross-stream hand-off (128K: 2.75 -> 2.63 ms).
+// A segmented call keeps 32-bit progress counters after its buffers; the streams wait on them
+// (hipStreamWaitValue32) rather than on events, which measured about 5 us less per cross-stream
+// hand-off.
 static constexpr size_t FLAG_BYTES = 256;
 
 // Where the chain's workgroups fill every CU of the device, prep cannot run beside it and the two
@@ -176,10 +176,10 @@ __device__ __forceinline__ void lds_barrier() {
 // ---------------------------------------------------------------------------------------------
 // A segmented call keeps 32-bit words in the workspace after its segment buffers: for each stage
 // the number of segments it has finished, the chain's arrival count and an error word. The side
-// streams wait on the counts with hipStreamWaitValue32; the chain kernel polls the prep count
-// itself and publishes its own, so that consecutive chain launches follow each other on their
-// stream with nothing queued between them.
-enum : int { FL_PREP = 0, FL_CHAIN = 1, FL_OUT = 2, FL_ERR = 3, FL_ARRIVE = 16, FL_WORDS = 64 };
+// stream waits on the chain's count with hipStreamWaitValue32; the chain kernel polls the prep
+// count itself and publishes its own, so that consecutive chain launches follow each other on
+// their stream with nothing queued between them.
+enum : int { FL_PREP = 0, FL_CHAIN = 1, FL_ERR = 3, FL_ARRIVE = 16, FL_WORDS = 64 };
 // about 10 s of the 100 MHz constant clock (s_memrealtime)
 static constexpr unsigned long long WAIT_TICKS = 1000000000ull;
 
