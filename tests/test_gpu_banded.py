@@ -56,12 +56,15 @@ def test_full_band_is_the_dense_path_bitwise():
 
 
 def test_banded_full_size_sampled_heads():
-    """The 32K GDN workload (B=1, H=32, L=32768, segmented) with band 1, long-memory gates."""
+    """The 32K GDN workload (B=1, H=32, L=32768) with band 1, long-memory gates, in segments of 30
+    chunks (the chain fills the device at 32 heads, so its segments alternate with prep's)."""
     cfg = inputs.GDN_32K.with_(gate_dist="long")
-    say(f"case {cfg.name} band 1")
+    say(f"case {cfg.name} band 1, segmented")
     x = inputs.prefill_inputs(cfg)
     q, k, v, beta, la, h0 = _dev(cfg, x)
-    o, hf = ops.gdn_prefill_banded_fwd(q, k, v, beta, la, h0, band=1)
+    rec = ops.prefill_workspace_size(1, 1, 64, 128, torch.bfloat16) * cfg.B * cfg.H
+    ws = torch.empty(2 * 30 * rec + 256, dtype=torch.uint8, device="cuda")
+    o, hf = ops.gdn_prefill_banded_fwd(q, k, v, beta, la, h0, band=1, workspace=ws)
     torch.cuda.synchronize()
     o, hf = host(o), host(hf)
     for h in (0, 21):
