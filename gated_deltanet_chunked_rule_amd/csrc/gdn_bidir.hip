@@ -117,7 +117,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(sizeof(type
     using M = MM<E>;
     using Ly = BidirLayout<D, E>;
     using frag = typename M::frag;
-    constexpr int KB = M::KB, NDT = Ly::NDT, NKT = CH / KB, FPD = KB / 16, KP = D + 8;
+    constexpr int KB = M::KB, NDT = Ly::NDT, NKT = CH / KB, FPD = KB / 16, KP = row_stride<D, E>();
     constexpr int DW = NDT / 4;   // key tiles a wave transposes = value tiles it owns
     extern __shared__ __align__(16) unsigned char smem[];
     T* Kr = reinterpret_cast<T*>(smem);                                   // [CH][KP]
@@ -278,7 +278,7 @@ __global__ __launch_bounds__(256) void bidir_out_kernel(const typename E::T* __r
     using M = MM<E>;
     using Ly = BidirLayout<D, E>;
     using frag = typename M::frag;
-    constexpr int KB = M::KB, NDT = Ly::NDT, NKD = Ly::NKD, KP = D + 8, EPF = M::EPF;
+    constexpr int KB = M::KB, NDT = Ly::NDT, NKD = Ly::NKD, KP = row_stride<D, E>(), EPF = M::EPF;
     constexpr int DW = NDT / 4;   // value tiles per wave
     extern __shared__ __align__(16) unsigned char smem[];
     T* Qr = reinterpret_cast<T*>(smem);                       // [CH][KP] phi(Q) rows
@@ -367,7 +367,7 @@ template <int D, class E>
 static int launch_bidir_t(const void* q, const void* k, const void* v, void* o, float* kv_out, long BH, long L,
                           int flags, unsigned char* ws, hipStream_t stream) {
     using T = typename E::T;
-    constexpr int KP = D + 8;
+    constexpr int KP = row_stride<D, E>();
     const long nch = (L + CH - 1) / CH;
     const int nb = bidir_blocks(BH, nch);
     const int cpb = (int)((nch + nb - 1) / nb);

@@ -47,7 +47,8 @@ typedef int i32x4v __attribute__((ext_vector_type(4)));
 template <int D, class E>
 struct LaCfg {
     using T = typename E::T;
-    static constexpr int KB = MM<E>::KB, NDT = D / 16, NKD = D / KB, NKT = CH / KB, FPD = KB / 16, KP = D + 8;
+    static constexpr int KB = MM<E>::KB, NDT = D / 16, NKD = D / KB, NKT = CH / KB, FPD = KB / 16,
+                         KP = row_stride<D, E>();
     static constexpr int DW = NDT / 4;                                  // value (and key) tiles per wave
     static constexpr size_t ROWS = (size_t)CH * KP * sizeof(T);         // one chunk's rows in LDS
     static constexpr size_t KF = (size_t)NDT * NKT * 1024;              // Khat^T fragments

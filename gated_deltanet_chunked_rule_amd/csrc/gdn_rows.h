@@ -25,6 +25,13 @@ __device__ __forceinline__ void lds_sync() {
     asm volatile("" ::: "memory");
 }
 
+// Row stride (elements) of a chunk's rows staged in LDS. The fragment reads take 8 bytes (bf16)
+// or 16 bytes (fp32) per lane from 16 consecutive rows at the same column; with a stride of
+// D + 4 elements (66 or 132 dwords, 2 or 4 mod 32) those rows fall on distinct banks of the
+// 32-bank LDS, where D + 8 (4 or 8 mod 32) put two rows on each bank.
+template <int D, class E>
+constexpr int row_stride() { return D + 4; }
+
 // 16 bytes of storage elements, unchanged
 struct AsIs {
     __device__ __forceinline__ uint4 operator()(uint4 x) const { return x; }
@@ -45,17 +52,20 @@ struct RowRegs {
 #pragma unroll
         for (int i = 0; i < N; ++i) x[i] = buffer_load16(rs, (tid + 256 * i) * 16);
     }
-    // into LDS with row stride D + 8, f applied to rows [0, n), the others zero (masked, not
-    // branched, so that the loads still in flight are not drained here)
+    // into LDS with row stride row_stride<D, E>() (rows 8-byte aligned: two 8-byte stores per
+    // 16 bytes), f applied to rows [0, n), the others zero (masked, not branched, so that the
+    // loads still in flight are not drained here)
     template <class F = AsIs>
     __device__ __forceinline__ void store(typename E::T* dst, int n, int tid, F f = F()) const {
+        constexpr int KP = row_stride<D, E>();
 #pragma unroll
         for (int i = 0; i < N; ++i) {
             const int u = tid + 256 * i, r = u / UPR, cu = u % UPR;
             const unsigned keep = 0u - (unsigned)(r < n);
             const uint4 y = f(x[i]);
-            *reinterpret_cast<uint4*>(dst + r * (D + 8) + cu * EPU) =
-                uint4{y.x & keep, y.y & keep, y.z & keep, y.w & keep};
+            uint2* d = reinterpret_cast<uint2*>(dst + r * KP + cu * EPU);
+            d[0] = uint2{y.x & keep, y.y & keep};
+            d[1] = uint2{y.z & keep, y.w & keep};
         }
     }
 };
