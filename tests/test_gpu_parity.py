@@ -248,6 +248,14 @@ def test_gdn_128k_full_workload_sampled():
     _check(o, hf, ro, rh, TOL_BF16, cfg.name)
 
 
+def test_gdn_128k_long_memory_gates_sampled():
+    """log a ~ -U(0, 0.01) at 128K: the state carries information across the whole 2048-chunk
+    chain (and 33 segments of the pipelined launch), so rounding errors can accumulate."""
+    cfg = inputs.GDN_128K.with_(name="gdn_128k_long_memory", gate_dist="long")
+    o, hf, ro, rh = _full_size(cfg, [(0, 9)])
+    _check(o, hf, ro, rh, TOL_BF16, cfg.name)
+
+
 # ---------------------------------------------------------------------------------------------
 # decode
 # ---------------------------------------------------------------------------------------------
