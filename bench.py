@@ -279,6 +279,9 @@ def main():
                          "B=4 H=16 L=8192 after warm-up (for profilers), no JSON")
     ap.add_argument("--copy-calibrate", type=int, default=0, metavar="BYTES",
                     help="only copy BYTES device-to-device three times (counter calibration), no JSON")
+    ap.add_argument("--copy-bandwidth", type=int, default=0, metavar="BYTES",
+                    help="only time device-to-device copies of BYTES (HIP events) and print the HBM rate "
+                         "(bytes read + written per second), no JSON")
     ap.add_argument("--source-hash", action="store_true", help="print kernel_source_hash() and exit")
     args = ap.parse_args()
     if args.source_hash:
@@ -303,6 +306,13 @@ def main():
             dst.copy_(src)
         torch.cuda.synchronize()
         log(f"copied {src.numel() * 4} bytes three times")
+        return
+    if args.copy_bandwidth:
+        src = torch.ones(args.copy_bandwidth // 4, dtype=torch.float32, device="cuda")
+        dst = torch.empty_like(src)
+        ms, _ = time_loop(torch, lambda: dst.copy_(src), 20, 3)
+        log(f"device copy of {src.numel() * 4} bytes: {ms:.4f} ms, {2 * src.numel() * 4 / (ms * 1e-3) / 1e9:.0f} GB/s "
+            f"read + written")
         return
     if args.profile_decode:
         c = inputs.DECODE_256x32
