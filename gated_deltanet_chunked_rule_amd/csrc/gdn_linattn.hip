@@ -377,8 +377,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void l
 namespace {
 
 // blocks of chunks per slice: about 512 workgroups for stages 1 and 3 (two per CU), no more than the
-// workspace holds (at least one: the smallest workspace accepted holds two chunk records per
-// slice, each larger than one block's state tiles)
+// workspace holds (at least one: the smallest workspace accepted holds one block's state tiles
+// and Lambda per slice)
 int la_blocks(long BH, long nch, size_t tiles, size_t ws_bytes) {
     long nb = (512 + BH - 1) / BH;
     if (nb > nch) nb = nch;
