@@ -11,14 +11,16 @@
 //     O  = diag(e^g) Q H + (Q K^T .* Gamma) V,   Gamma[r][s] = e^{g_r - g_s} for s <= r, else 0
 //     H' = e^{g_C} H + Khat^T V,                 Khat[s] = e^{g_C - g_s} k_s
 // (only exponentials of non-positive differences are formed). Three kernels:
-//   1. la_kv_kernel: one workgroup per (block of chunks, slice) runs H' over its block from zero:
-//      S_b, the block's contribution to the state after it, and Lambda_b, its summed log a.
+//   1. la_kv_kernel: one workgroup per (block of chunks, slice), all blocks but the last, runs H'
+//      over its block from zero: S_b, the block's contribution to the state after it, and
+//      Lambda_b, its summed log a.
 //   2. la_scan_kernel: per slice and state element, H_0 = h0, H_{b+1} = e^{Lambda_b} H_b + S_b;
-//      H_b replaces S_b in the workspace and the last one is h_final.
+//      H_b replaces S_b in the workspace.
 //   3. la_out_kernel: one workgroup per (block, slice) runs the block's chunks again from H_b and
-//      forms their outputs. Each wave keeps the fp32 state of a quarter of the value columns in
-//      accumulator registers, computes the gated causal P^T for one token tile and shares it and
-//      its quarter of the Khat^T fragments through LDS.
+//      forms their outputs; the last block's workgroups end with the final state and write
+//      h_final. Each wave keeps the fp32 state of a quarter of the value columns in accumulator
+//      registers, computes the gated causal P^T for one token tile and shares it and its quarter
+//      of the Khat^T fragments through LDS.
 // The products that contract over tokens (Khat^T V, V^T P^T) need fragments whose k index is the
 // token: K and V rows are staged in LDS and turned into columns by one MFMA per 16 x 16 tile
 // against a unit-column fragment, an exact transpose on the matrix core.
@@ -179,24 +181,24 @@ __global__ __launch_bounds__(256) void la_kv_kernel(const typename E::T* __restr
 // 2. block-start states: a sequential pass over the blocks, one thread per state element
 // ---------------------------------------------------------------------------------------------
 template <int D>
-__global__ __launch_bounds__(256) void la_scan_kernel(unsigned char* ws, const float* __restrict__ h0,
-                                                      float* h_final, int nb, int gated) {
+__global__ __launch_bounds__(256) void la_scan_kernel(unsigned char* ws, const float* __restrict__ h0, int nb,
+                                                      int gated) {
     constexpr int NDT = D / 16;
     constexpr size_t TF = LaLayout<D>::TILES / 4;   // floats per block
     const int bh = blockIdx.y;
     const int u = blockIdx.x * 256 + threadIdx.x;   // element in tile order, < D * D
     const int e = u & 3, lane = (u >> 2) & 63, tile = u >> 8;
     const int row = 16 * (tile / NDT) + 4 * (lane >> 4) + e, col = 16 * (tile % NDT) + (lane & 15);
-    const size_t hix = ((size_t)bh * D + row) * D + col;
     float* S = reinterpret_cast<float*>(ws + (size_t)bh * nb * LaLayout<D>::TILES) + u;
     const float* lamb = reinterpret_cast<const float*>(ws + (size_t)gridDim.y * nb * LaLayout<D>::TILES) + (size_t)bh * nb;
-    float H = h0 ? h0[hix] : 0.f;   // read before h_final is written: they may be the same array
-    for (int b = 0; b < nb; ++b) {
+    // h0 is read here, before stage 3 writes h_final: the two may be the same array
+    float H = h0 ? h0[((size_t)bh * D + row) * D + col] : 0.f;
+    for (int b = 0; b + 1 < nb; ++b) {
         const float s = S[b * TF];
         S[b * TF] = H;
         H = (gated ? __expf(lamb[b]) * H : H) + s;
     }
-    h_final[hix] = H;
+    S[(nb - 1) * TF] = H;   // the last block's start state (its own contribution is never formed)
 }
 
 // ---------------------------------------------------------------------------------------------
@@ -208,7 +210,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void l
                                                      const typename E::T* __restrict__ v,
                                                      const float* __restrict__ log_alpha,
                                                      const unsigned char* __restrict__ ws, typename E::T* __restrict__ o,
-                                                     long L, int cpb, int nb) {
+                                                     float* __restrict__ h_final, long L, int cpb, int nb) {
     using T = typename E::T;
     using M = MM<E>;
     using C = LaCfg<D, E>;
@@ -369,6 +371,15 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void l
             }
         if (!C::PREF && c + 1 < c_end) load_rows(c + 1);
     }
+    if (blk == nb - 1) {   // the final state: lane (j, n) of tile (dt, vt) holds rows 16 dt + 4 j .. + 3, column 16 vt + n
+        float* hf = h_final + (size_t)bh * D * D;
+#pragma unroll
+        for (int i = 0; i < DW; ++i)
+#pragma unroll
+            for (int dt = 0; dt < NDT; ++dt)
+#pragma unroll
+                for (int e = 0; e < 4; ++e) hf[(size_t)(16 * dt + 4 * j + e) * D + 16 * (DW * w + i) + m] = H[i][dt][e];
+    }
 }
 
 // ---------------------------------------------------------------------------------------------
@@ -420,12 +431,13 @@ static int launch_linattn_t(const void* q, const void* k, const void* v, const f
                             hipFuncAttributeMaxDynamicSharedMemorySize, (int)C::LDS_OUT) == hipSuccess;
     if (!attr) return -1;
     const dim3 grid((unsigned)nb, (unsigned)BH);
-    hipLaunchKernelGGL((la_kv_kernel<D, E, GATED>), grid, dim3(256), C::LDS_KV, stream, (const T*)k, (const T*)v,
-                       log_alpha, ws, L, cpb, nb);
-    hipLaunchKernelGGL((la_scan_kernel<D>), dim3(D * D / 256, (unsigned)BH), dim3(256), 0, stream, ws, h0, h_final, nb,
+    if (nb > 1)   // every block's contribution but the last one's
+        hipLaunchKernelGGL((la_kv_kernel<D, E, GATED>), dim3((unsigned)(nb - 1), (unsigned)BH), dim3(256), C::LDS_KV,
+                           stream, (const T*)k, (const T*)v, log_alpha, ws, L, cpb, nb);
+    hipLaunchKernelGGL((la_scan_kernel<D>), dim3(D * D / 256, (unsigned)BH), dim3(256), 0, stream, ws, h0, nb,
                        GATED ? 1 : 0);
     hipLaunchKernelGGL((la_out_kernel<D, E, GATED>), grid, dim3(256), C::LDS_OUT, stream, (const T*)q, (const T*)k,
-                       (const T*)v, log_alpha, (const unsigned char*)ws, (T*)o, L, cpb, nb);
+                       (const T*)v, log_alpha, (const unsigned char*)ws, (T*)o, h_final, L, cpb, nb);
     return hipGetLastError() == hipSuccess ? 0 : -1;
 }
 
