@@ -11,6 +11,8 @@ The chunked form with the block-adjacent intra-chunk solve is NumPy fp64 in ``ba
     gdn_prefill(q, k, v, beta, log_alpha, h0)  -> (o, h_final)   gated delta rule
     linattn_prefill(q, k, v, h0)               -> (o, h_final)   S_t = S_{t-1} + v_t k_t^T
     gla_prefill(q, k, v, log_alpha, h0)        -> (o, h_final)   S_t = a_t S_{t-1} + v_t k_t^T
+    gla_vec_prefill(q, k, v, log_alpha, h0)    -> (o, h_final)   S_t = S_{t-1} diag(a_t) + v_t k_t^T,
+                                                                 a gate per key dimension
     gdn_prefill_skip(q, k, v, beta, log_alpha, keep, h0, chunk)  gated delta rule, skipped chunks
                                                                  only decay the carried state
     gdn_decode_step(q, k, v, beta, log_alpha, state) -> (o, new_state)
@@ -21,7 +23,7 @@ The chunked form with the block-adjacent intra-chunk solve is NumPy fp64 in ``ba
                                                                  its diagonal (oracle/banded.py, NumPy)
 
 Shapes: q,k [B,H,L,Dk]; v [B,H,L,Dv]; beta, log_alpha [B,H,L]; h0/h_final [B,H,Dk,Dv]
-(key-major, element [i][j] = S[j][i]); decode: q,k [N,H,Dk], v [N,H,Dv], beta/log_alpha
+(key-major, element [i][j] = S[j][i]); gla_vec_prefill's log_alpha [B,H,L,Dk]; decode: q,k [N,H,Dk], v [N,H,Dv], beta/log_alpha
 [N,H], state [N,H,Dk,Dv]. All results are fp64.
 """
 from __future__ import annotations
@@ -64,11 +66,13 @@ def _load():
             lib.oracle_linattn_prefill.argtypes = [P, P, P, P, P, P, i, i, i, i, i, i]
             lib.oracle_gdn_decode_step.argtypes = [P, P, P, P, P, P, P, i, i, i, i, i]
             lib.oracle_gla_prefill.argtypes = [P, P, P, P, P, P, P, i, i, i, i, i, i]
+            lib.oracle_gla_vec_prefill.argtypes = [P, P, P, P, P, P, P, i, i, i, i, i, i]
             lib.oracle_linattn_bidir.argtypes = [P, P, P, P, P, i, i, i, i, i, i, i]
             IP = ctypes.POINTER(ctypes.c_int)
             lib.oracle_gdn_prefill_skip.argtypes = [P, P, P, P, P, P, IP, i, P, P, i, i, i, i, i, i]
             for f in (lib.oracle_gdn_prefill, lib.oracle_linattn_prefill, lib.oracle_gdn_decode_step,
-                      lib.oracle_gla_prefill, lib.oracle_gdn_prefill_skip, lib.oracle_linattn_bidir):
+                      lib.oracle_gla_prefill, lib.oracle_gla_vec_prefill, lib.oracle_gdn_prefill_skip,
+                      lib.oracle_linattn_bidir):
                 f.restype = ctypes.c_int
             _lib = lib
     return _lib
@@ -138,6 +142,24 @@ def gla_prefill(q, k, v, log_alpha, h0=None, nthreads: int = 0):
     hf = np.empty((B, H, Dk, Dv))
     last_threads = _load().oracle_gla_prefill(_ptr(q), _ptr(k), _ptr(v), _ptr(log_alpha), _ptr(h0), _ptr(o),
                                               _ptr(hf), B, H, L, Dk, Dv, nthreads)
+    return o, hf
+
+
+def gla_vec_prefill(q, k, v, log_alpha, h0=None, nthreads: int = 0):
+    """Gated linear attention with a gate per key dimension: S_t = S_{t-1} diag(exp(log_alpha_t))
+    + v_t k_t^T, o_t = S_t q_t; log_alpha [B,H,L,Dk]."""
+    global last_threads
+    q, k, v, log_alpha = (_as4(_f64(t), 4) for t in (q, k, v, log_alpha))
+    B, H, L, Dk = q.shape
+    Dv = v.shape[-1]
+    assert k.shape == q.shape and v.shape[:3] == (B, H, L) and log_alpha.shape == q.shape
+    if h0 is not None:
+        h0 = _as4(_f64(h0), 4)
+        assert h0.shape == (B, H, Dk, Dv)
+    o = np.empty((B, H, L, Dv))
+    hf = np.empty((B, H, Dk, Dv))
+    last_threads = _load().oracle_gla_vec_prefill(_ptr(q), _ptr(k), _ptr(v), _ptr(log_alpha), _ptr(h0), _ptr(o),
+                                                  _ptr(hf), B, H, L, Dk, Dv, nthreads)
     return o, hf
 
 

@@ -25,6 +25,11 @@
  *   modifications the forpes.ru article on linear attention lists after the recurrent form):
  *       S_t = a_t S_{t-1} + v_t k_t^T,   o_t = S_t q_t,   a_t = exp(log_alpha_t).
  *
+ *   Gated linear attention with a gate per key dimension (the forpes.ru article's survey of
+ *   linearised models: GLA, its gating applied over the key vectors):
+ *       S_t = S_{t-1} diag(a_t) + v_t k_t^T,   o_t = S_t q_t,   a_t[i] = exp(log_alpha_t[i]),
+ *   i.e. key dimension i of the state decays by its own factor a_t[i] before the write.
+ *
  *   Gated delta rule with skipped chunk updates (the SparseGDN article, fileenergy.com: the
  *   selector's skipped events, and its scan_with_skips illustration in the section on embedding
  *   the selector into an FLA pipeline). Tokens are grouped into chunks of C; at the start of
@@ -48,7 +53,8 @@
  * selector into an FLA pipeline), with the state's key dimension as the row index.
  *
  * Layouts (all row-major, fp64):
- *   q, k [B,H,L,Dk]; v, o [B,H,L,Dv]; beta, log_alpha [B,H,L]; h0, h_final [B,H,Dk,Dv].
+ *   q, k [B,H,L,Dk]; v, o [B,H,L,Dv]; beta, log_alpha [B,H,L]; h0, h_final [B,H,Dk,Dv];
+ *   the per-key-dimension log_alpha of gated linear attention [B,H,L,Dk].
  *   h0 == NULL means a zero initial state.
  * nthreads <= 0 uses the OpenMP default. Returns the number of threads used.
  */
@@ -125,6 +131,17 @@ static void gla_token(double *S, const double *k, const double *v, double log_al
     }
 }
 
+/* One gated linear-attention token, a gate per key dimension: S[j][i] <- a[i] S[j][i] + v[j] k[i]. */
+static void gla_vec_token(double *S, double *a, const double *k, const double *v, const double *log_alpha,
+                          int Dk, int Dv)
+{
+    for (int i = 0; i < Dk; ++i) a[i] = exp(log_alpha[i]);
+    for (int j = 0; j < Dv; ++j) {
+        double *row = S + (size_t)j * Dk;
+        for (int i = 0; i < Dk; ++i) row[i] = a[i] * row[i] + v[j] * k[i];
+    }
+}
+
 /* One plain linear-attention token: S <- S + v k^T. */
 static void la_token(double *S, const double *k, const double *v, int Dk, int Dv)
 {
@@ -192,6 +209,30 @@ int oracle_gla_prefill(const double *q, const double *k, const double *v, const 
         for (int t = 0; t < L; ++t) {
             const size_t tok = (size_t)s * L + t;
             gla_token(S, k + tok * Dk, v + tok * Dv, log_alpha[tok], Dk, Dv);
+            read_out(o + tok * Dv, S, q + tok * Dk, Dk, Dv);
+        }
+        store_state(h_final + (size_t)s * Dk * Dv, S, Dk, Dv);
+        free(S);
+    }
+    return used;
+}
+
+/* Gated linear attention with a gate per key dimension: log_alpha [B,H,L,Dk]; the rest as
+ * oracle_linattn_prefill. */
+int oracle_gla_vec_prefill(const double *q, const double *k, const double *v, const double *log_alpha,
+                           const double *h0, double *o, double *h_final,
+                           int B, int H, int L, int Dk, int Dv, int nthreads)
+{
+    const int used = set_threads(nthreads);
+    const long nslice = (long)B * H;
+#pragma omp parallel for schedule(dynamic, 1)
+    for (long s = 0; s < nslice; ++s) {
+        double *S = (double *)malloc(sizeof(double) * ((size_t)Dk * Dv + Dk));
+        double *a = S + (size_t)Dk * Dv;
+        load_state(S, h0 ? h0 + (size_t)s * Dk * Dv : NULL, Dk, Dv);
+        for (int t = 0; t < L; ++t) {
+            const size_t tok = (size_t)s * L + t;
+            gla_vec_token(S, a, k + tok * Dk, v + tok * Dv, log_alpha + tok * Dk, Dk, Dv);
             read_out(o + tok * Dv, S, q + tok * Dk, Dk, Dv);
         }
         store_state(h_final + (size_t)s * Dk * Dv, S, Dk, Dv);
