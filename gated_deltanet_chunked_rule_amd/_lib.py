@@ -24,6 +24,8 @@ SIGNATURES = {
     "linattn_prefill_fwd": (_i, [_vp, _vp, _vp, _fp, _fp, _fp, _vp, _fp, _i, _i, _i, _i, _i, _i, _vp, _sz, _vp]),
     "gdn_decode_step": (_i, [_vp, _vp, _vp, _fp, _fp, _fp, _vp, _i, _i, _i, _i, _i, _vp]),
     "linattn_prefill_workspace_size": (_sz, [_i, _i, _i, _i, _i, _i]),
+    "gla_prefill_fwd": (_i, [_vp, _vp, _vp, _fp, _fp, _vp, _fp, _i, _i, _i, _i, _i, _i, _vp, _sz, _vp]),
+    "gla_prefill_workspace_size": (_sz, [_i, _i, _i, _i, _i, _i]),
     "linattn_bidir_workspace_size": (_sz, [_i, _i, _i, _i, _i, _i]),
     "linattn_bidir_fwd": (_i, [_vp, _vp, _vp, _vp, _fp, _i, _i, _i, _i, _i, _i, _i, _vp, _sz, _vp]),
 }

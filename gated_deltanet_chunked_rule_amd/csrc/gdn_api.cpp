@@ -171,6 +171,48 @@ size_t linattn_prefill_workspace_size(int B, int H, int L, int Dk, int Dv, int d
     return gdn::linattn_workspace_bytes((long)B * H, L, Dk);
 }
 
+size_t gla_prefill_workspace_size(int B, int H, int L, int Dk, int Dv, int dtype) {
+    if (check_dims(B, H, L, Dk, Dv, dtype) != GDN_OK) return 0;
+    return gdn::gla_workspace_bytes((long)B * H, L, Dk);
+}
+
+int gla_prefill_fwd(const void* q, const void* k, const void* v, const float* log_alpha, const float* h0, void* o,
+                    float* h_final, int B, int H, int L, int Dk, int Dv, int dtype, void* workspace,
+                    size_t workspace_bytes, void* stream) {
+    int st = check_dims(B, H, L, Dk, Dv, dtype);
+    if (st != GDN_OK) return st;
+    if (!h_final) return GDN_ERR_NULL;
+    if (L > 0 && (!q || !k || !v || !o || !log_alpha)) return GDN_ERR_NULL;
+    const void* ptrs[] = {q, k, v, log_alpha, h0, o, h_final};
+    for (const void* p : ptrs)
+        if (p && !aligned(p, 16)) return GDN_ERR_ALIGN;
+    const size_t need = gdn::gla_workspace_min_bytes((long)B * H, L, Dk);
+    if (need > 0) {
+        if (!workspace || workspace_bytes < need) return GDN_ERR_WORKSPACE;
+        if (!aligned(workspace, 256)) return GDN_ERR_ALIGN;
+    }
+    const size_t esz = dtype == GDN_BF16 ? 2 : 4;
+    const size_t BH = (size_t)B * H, tok = BH * (size_t)L;
+    const Range in[] = {rng(q, tok * Dk * esz), rng(k, tok * Dk * esz), rng(v, tok * Dv * esz),
+                        rng(log_alpha, log_alpha ? tok * Dk * 4 : 0), rng(h0, h0 ? BH * Dk * Dv * 4 : 0)};
+    const Range ro = rng(o, tok * Dv * esz), rh = rng(h_final, BH * Dk * Dv * 4);
+    const Range rw = rng(workspace, workspace && need ? workspace_bytes : 0);
+    for (int i = 0; i < 5; ++i) {
+        if (overlap(ro, in[i]) || overlap(rw, in[i])) return GDN_ERR_ALIAS;
+        if (i == 4 && h0 == h_final) continue;  // in-place state update is allowed
+        if (overlap(rh, in[i])) return GDN_ERR_ALIAS;
+    }
+    if (overlap(ro, rh) || overlap(ro, rw) || overlap(rh, rw)) return GDN_ERR_ALIAS;
+    st = check_device();
+    if (st != GDN_OK) return st;
+    const hipStream_t s = static_cast<hipStream_t>(stream);
+    const int rc = L == 0 ? gdn::launch_prefill(q, k, v, nullptr, nullptr, nullptr, h0, o, h_final, B * H, 0, Dk,
+                                                dtype, 3, workspace, workspace_bytes, s)
+                          : gdn::launch_gla(q, k, v, log_alpha, h0, o, h_final, B * H, L, Dk, dtype, workspace,
+                                            workspace_bytes, s);
+    return rc == 0 ? GDN_OK : GDN_ERR_LAUNCH;
+}
+
 size_t linattn_bidir_workspace_size(int B, int H, int L, int Dk, int Dv, int dtype) {
     if (check_dims(B, H, L, Dk, Dv, dtype) != GDN_OK) return 0;
     return gdn::bidir_workspace_bytes((long)B * H, L, Dk, dtype);

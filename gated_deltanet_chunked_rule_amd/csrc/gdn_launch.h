@@ -26,6 +26,13 @@ size_t linattn_workspace_min_bytes(long BH, long L, int D);  // smallest accepte
 int launch_linattn(const void* q, const void* k, const void* v, const float* log_alpha, const float* h0, void* o,
                    float* h_final, int BH, long L, int D, int dtype, void* ws, size_t ws_bytes, hipStream_t stream);
 
+// Gated linear attention with a gate per key dimension: log_alpha [BH][L][D]; same workspace
+// scheme with a D-vector of summed log gates per block.
+size_t gla_workspace_bytes(long BH, long L, int D);
+size_t gla_workspace_min_bytes(long BH, long L, int D);
+int launch_gla(const void* q, const void* k, const void* v, const float* log_alpha, const float* h0, void* o,
+               float* h_final, int BH, long L, int D, int dtype, void* ws, size_t ws_bytes, hipStream_t stream);
+
 // Bidirectional linear attention. kv_out: [BH][D][D] fp32 or NULL. flags bit 0: divide by Z,
 // bit 1: phi = elu + 1 (else identity). The workspace is bidir_workspace_bytes(...) bytes.
 size_t bidir_workspace_bytes(long BH, long L, int D, int dtype);

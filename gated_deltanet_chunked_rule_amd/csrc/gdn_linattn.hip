@@ -383,17 +383,387 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void l
 }
 
 // ---------------------------------------------------------------------------------------------
+// Gated linear attention with a gate per key dimension (the forpes.ru article's survey of
+// linearised models: GLA, gating over the key vectors): H_t = diag(a_t) H_{t-1} + k_t v_t^T with
+// a_t in R^Dk. With G the in-chunk inclusive prefix sum of log a (a Dk-vector per token):
+//     O[r]  = (q_r .* e^{G_r})^T H + sum_{s<=r} (sum_d q_r[d] k_s[d] e^{G_r[d] - G_s[d]}) v_s
+//     H'    = diag(e^{G_C}) H + Khat^T V,   Khat[s][d] = k_s[d] e^{G_C[d] - G_s[d]}
+// The same three stages as above, with the block decay a Dk-vector. The intra-chunk products
+// take a reference token per pair of 16-token tiles: tile rt against an earlier tile st uses
+// st's last token, so both factors e^{G_r - G_ref} and e^{G_ref - G_s} are at most 1; a tile
+// against itself uses its middle token, so no factor exceeds e^{8 |log a|} (finite in fp32 for
+// per-token log gates above about -10).
+// ---------------------------------------------------------------------------------------------
+namespace {
+
+template <int D>
+struct GlaCfg {
+    static constexpr int GS = D + 4;                        // row stride of the cumulative gates (floats)
+    static constexpr size_t GSZ = (size_t)CH * GS * 4;       // the chunk's cumulative gates
+    static constexpr int NQ = 256 / D, TPQ = CH / NQ;       // gate-scan threads per column, tokens each
+    static constexpr size_t TOT = (size_t)NQ * D * 4;        // per-thread block totals
+};
+
+// Cumulative log gates of a chunk, sG[s][d] = sum_{s' <= s} la[s'][d] (rows past the end add
+// zero). Thread t takes column d = t % D and tokens [qq TPQ, (qq + 1) TPQ), qq = t / D: load,
+// local prefix and block total (then a workgroup barrier), then the earlier blocks' totals added.
+template <int D>
+struct GateScan {
+    using G = GlaCfg<D>;
+    float x[G::TPQ];
+    __device__ __forceinline__ void load(const float* la_chunk, int n, int tid) {
+        const __amdgpu_buffer_rsrc_t rs = buffer_rsrc(la_chunk, n * D * 4);
+        const int d = tid % D, s0 = (tid / D) * G::TPQ;
+#pragma unroll
+        for (int i = 0; i < G::TPQ; ++i) x[i] = __uint_as_float(buffer_load4(rs, ((s0 + i) * D + d) * 4));
+    }
+    __device__ __forceinline__ void prefix(float* tot, int tid) {
+#pragma unroll
+        for (int i = 1; i < G::TPQ; ++i) x[i] += x[i - 1];
+        tot[tid] = x[G::TPQ - 1];   // tot[qq][d]
+    }
+    // after the barrier; returns this thread's last cumulative value (G_C[d] for the last block)
+    __device__ __forceinline__ float store(float* sG, const float* tot, int tid) {
+        const int d = tid % D, qq = tid / D;
+        float carry = 0.f;
+        for (int q2 = 0; q2 < qq; ++q2) carry += tot[q2 * D + d];
+#pragma unroll
+        for (int i = 0; i < G::TPQ; ++i) sG[(qq * G::TPQ + i) * G::GS + d] = x[i] + carry;
+        return x[G::TPQ - 1] + carry;
+    }
+};
+
+// Fragment of row rp (k = d, the row_frag_raw order) with element d scaled by exp(gp[d] - gq[d])
+// (gq == nullptr: exp(gp[d])).
+template <class E>
+__device__ __forceinline__ typename MM<E>::frag row_frag_exp(const typename E::T* rp, const float* gp, const float* gq,
+                                                            int k0, int j) {
+    using M = MM<E>;
+    float x[M::EPF];
+#pragma unroll
+    for (int h = 0; h < M::EPF / 4; ++h) {
+        const int d0 = k0 + 16 * h + 4 * j;
+        const float4 a = load4(rp + d0);
+        const float4 p = *reinterpret_cast<const float4*>(gp + d0);
+        float4 r = make_float4(0.f, 0.f, 0.f, 0.f);
+        if (gq) r = *reinterpret_cast<const float4*>(gq + d0);
+        x[4 * h + 0] = a.x * __expf(p.x - r.x);
+        x[4 * h + 1] = a.y * __expf(p.y - r.y);
+        x[4 * h + 2] = a.z * __expf(p.z - r.z);
+        x[4 * h + 3] = a.w * __expf(p.w - r.w);
+    }
+    return M::pack(x);
+}
+
+}  // namespace
+
+// 1. block contributions (all blocks but the last) and their Dk-vector of summed log gates
+template <int D, class E>
+__global__ __launch_bounds__(256) void gla_kv_kernel(const typename E::T* __restrict__ k,
+                                                     const typename E::T* __restrict__ v,
+                                                     const float* __restrict__ log_alpha, unsigned char* ws, long L,
+                                                     int cpb, int nb) {
+    using T = typename E::T;
+    using M = MM<E>;
+    using C = LaCfg<D, E>;
+    using G = GlaCfg<D>;
+    using frag = typename M::frag;
+    constexpr int NDT = C::NDT, NKT = C::NKT, FPD = C::FPD, DW = C::DW, GS = G::GS;
+    extern __shared__ __align__(16) unsigned char smem[];
+    T* Kr = reinterpret_cast<T*>(smem);                                        // [CH][KP]
+    T* Vr = reinterpret_cast<T*>(smem + C::ROWS);                              // [CH][KP]
+    unsigned char* sKf = smem + 2 * C::ROWS;                                   // Khat^T fragments [dt][kt]
+    float* sG = reinterpret_cast<float*>(smem + 2 * C::ROWS + C::KF);          // [CH][GS] cumulative gates
+    float* sTot = reinterpret_cast<float*>(smem + 2 * C::ROWS + C::KF + G::GSZ);
+
+    const int blk = blockIdx.x, bh = blockIdx.y;
+    const int tid = threadIdx.x, lane = tid & 63, j = lane >> 4, m = lane & 15;
+    const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const long nch = (L + CH - 1) / CH;
+    const long c_begin = (long)blk * cpb;
+    const long c_end = c_begin + cpb < nch ? c_begin + cpb : nch;
+
+    f32x4 acc[NDT][DW];
+#pragma unroll
+    for (int dt = 0; dt < NDT; ++dt)
+#pragma unroll
+        for (int i = 0; i < DW; ++i) acc[dt][i] = f32x4{0.f, 0.f, 0.f, 0.f};
+    float lamv = 0.f;   // summed log gate of column tid % D (kept by the last token block's threads)
+
+    auto rows_of = [&](long c) { return (int)(L - c * CH < CH ? L - c * CH : CH); };
+    RowRegs<D, E> rk, rv;
+    rk.load(k + ((size_t)bh * L + c_begin * CH) * D, rows_of(c_begin), tid);
+    rv.load(v + ((size_t)bh * L + c_begin * CH) * D, rows_of(c_begin), tid);
+    GateScan<D> gsc;
+    for (long c = c_begin; c < c_end; ++c) {
+        const int n = rows_of(c);
+        const size_t tok0 = (size_t)bh * L + c * CH;
+        gsc.load(log_alpha + tok0 * D, n, tid);
+        rk.store(Kr, n, tid);
+        rv.store(Vr, n, tid);
+        if (c + 1 < c_end) {
+            rk.load(k + (tok0 + CH) * D, rows_of(c + 1), tid);
+            rv.load(v + (tok0 + CH) * D, rows_of(c + 1), tid);
+        }
+        gsc.prefix(sTot, tid);
+        lds_sync();
+        lamv += gsc.store(sG, sTot, tid);
+        lds_sync();
+        const float* gC = sG + (CH - 1) * GS;
+        frag vf[DW][NKT];
+#pragma unroll
+        for (int i = 0; i < DW; ++i) {
+            const int dt = DW * w + i;
+            f32x4 t[4];
+            col_tiles<D, E>(Kr, dt, j, m, t);
+            const float gcd = gC[16 * dt + m];
+#pragma unroll
+            for (int st = 0; st < 4; ++st)
+#pragma unroll
+                for (int e = 0; e < 4; ++e) t[st][e] *= __expf(gcd - sG[(16 * st + 4 * j + e) * GS + 16 * dt + m]);
+#pragma unroll
+            for (int kt = 0; kt < NKT; ++kt) st_frag(sKf + (size_t)(dt * NKT + kt) * 1024, lane, cols_frag<E>(&t[FPD * kt]));
+            col_tiles<D, E>(Vr, dt, j, m, t);
+#pragma unroll
+            for (int kt = 0; kt < NKT; ++kt) vf[i][kt] = cols_frag<E>(&t[FPD * kt]);
+        }
+        lds_sync();
+        // S = diag(e^{G_C}) S + Khat^T V; tile (dt, .) rows 16 dt + 4 j + e
+#pragma unroll
+        for (int dt = 0; dt < NDT; ++dt) {
+            const float4 gc = *reinterpret_cast<const float4*>(gC + 16 * dt + 4 * j);
+            const float f[4] = {__expf(gc.x), __expf(gc.y), __expf(gc.z), __expf(gc.w)};
+#pragma unroll
+            for (int i = 0; i < DW; ++i)
+                acc[dt][i] = f32x4{acc[dt][i][0] * f[0], acc[dt][i][1] * f[1], acc[dt][i][2] * f[2], acc[dt][i][3] * f[3]};
+        }
+#pragma unroll
+        for (int dt = 0; dt < NDT; ++dt)
+#pragma unroll
+            for (int kt = 0; kt < NKT; ++kt) {
+                const frag kf = ld_frag<frag>(sKf + (size_t)(dt * NKT + kt) * 1024, lane);
+#pragma unroll
+                for (int i = 0; i < DW; ++i) acc[dt][i] = M::mma(kf, vf[i][kt], acc[dt][i]);
+            }
+    }
+    unsigned char* sb = ws + ((size_t)bh * nb + blk) * LaLayout<D>::TILES;
+#pragma unroll
+    for (int dt = 0; dt < NDT; ++dt)
+#pragma unroll
+        for (int i = 0; i < DW; ++i) st_frag(sb + (size_t)(dt * NDT + DW * w + i) * 1024, lane, acc[dt][i]);
+    if (tid / D == G::NQ - 1) {   // the threads that hold the chunks' last cumulative gates
+        float* lamb = reinterpret_cast<float*>(ws + (size_t)gridDim.y * nb * LaLayout<D>::TILES);
+        lamb[((size_t)bh * nb + blk) * D + tid % D] = lamv;
+    }
+}
+
+// 2. block-start states with Dk-vector block decays
+template <int D>
+__global__ __launch_bounds__(256) void gla_scan_kernel(unsigned char* ws, const float* __restrict__ h0, int nb) {
+    constexpr int NDT = D / 16;
+    constexpr size_t TF = LaLayout<D>::TILES / 4;
+    const int bh = blockIdx.y;
+    const int u = blockIdx.x * 256 + threadIdx.x;
+    const int e = u & 3, lane = (u >> 2) & 63, tile = u >> 8;
+    const int row = 16 * (tile / NDT) + 4 * (lane >> 4) + e, col = 16 * (tile % NDT) + (lane & 15);
+    float* S = reinterpret_cast<float*>(ws + (size_t)bh * nb * LaLayout<D>::TILES) + u;
+    const float* lamb = reinterpret_cast<const float*>(ws + (size_t)gridDim.y * nb * LaLayout<D>::TILES) + (size_t)bh * nb * D;
+    float H = h0 ? h0[((size_t)bh * D + row) * D + col] : 0.f;   // before stage 3 writes h_final
+    for (int b = 0; b + 1 < nb; ++b) {
+        const float s = S[b * TF];
+        S[b * TF] = H;
+        H = __expf(lamb[(size_t)b * D + row]) * H + s;
+    }
+    S[(nb - 1) * TF] = H;
+}
+
+// 3. outputs from each block's start state; the last block writes h_final. At d = 128 its LDS
+// (the cumulative gates beside the rows) allows one workgroup per CU, so it may use every register.
+template <int D, class E>
+__global__ __launch_bounds__(256) void gla_out_kernel(
+    const typename E::T* __restrict__ q, const typename E::T* __restrict__ k, const typename E::T* __restrict__ v,
+    const float* __restrict__ log_alpha, const unsigned char* __restrict__ ws, typename E::T* __restrict__ o,
+    float* __restrict__ h_final, long L, int cpb, int nb) {
+    using T = typename E::T;
+    using M = MM<E>;
+    using C = LaCfg<D, E>;
+    using G = GlaCfg<D>;
+    using frag = typename M::frag;
+    constexpr int KB = C::KB, NDT = C::NDT, NKD = C::NKD, NKT = C::NKT, FPD = C::FPD, KP = C::KP, DW = C::DW,
+                  GS = G::GS;
+    extern __shared__ __align__(16) unsigned char smem[];
+    T* Qr = reinterpret_cast<T*>(smem);
+    T* Kr = reinterpret_cast<T*>(smem + C::ROWS);
+    T* Vr = reinterpret_cast<T*>(smem + 2 * C::ROWS);
+    unsigned char* sKf = smem + 3 * C::ROWS;
+    unsigned char* sPf = sKf + C::KF;
+    float* sTot = reinterpret_cast<float*>(sPf + C::PF);
+    // the cumulative gates take the V rows' space once V is in registers (fp32), else their own
+    float* sG = sizeof(T) == 4 ? reinterpret_cast<float*>(Vr) : reinterpret_cast<float*>(sPf + C::PF + G::TOT);
+
+    const int blk = blockIdx.x, bh = blockIdx.y;
+    const int tid = threadIdx.x, lane = tid & 63, j = lane >> 4, m = lane & 15;
+    const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const long nch = (L + CH - 1) / CH;
+    const long c_begin = (long)blk * cpb;
+    const long c_end = c_begin + cpb < nch ? c_begin + cpb : nch;
+
+    f32x4 H[DW][NDT];
+    const unsigned char* hb = ws + ((size_t)bh * nb + blk) * LaLayout<D>::TILES;
+#pragma unroll
+    for (int i = 0; i < DW; ++i)
+#pragma unroll
+        for (int dt = 0; dt < NDT; ++dt) H[i][dt] = ld_frag<f32x4>(hb + (size_t)(dt * NDT + DW * w + i) * 1024, lane);
+
+    auto rows_of = [&](long c) { return (int)(L - c * CH < CH ? L - c * CH : CH); };
+    auto src = [&](const T* p, long c) { return p + ((size_t)bh * L + c * CH) * D; };
+    RowRegs<D, E> rq, rk, rv;
+    auto load_rows = [&](long c) {
+        const int n = rows_of(c);
+        rq.load(src(q, c), n, tid);
+        rk.load(src(k, c), n, tid);
+        rv.load(src(v, c), n, tid);
+    };
+    load_rows(c_begin);
+    GateScan<D> gsc;
+    for (long c = c_begin; c < c_end; ++c) {
+        const int n = rows_of(c);
+        const size_t tok0 = (size_t)bh * L + c * CH;
+        gsc.load(log_alpha + tok0 * D, n, tid);
+        if (c > c_begin) lds_sync();   // every wave is done with the previous chunk's LDS data
+        rq.store(Qr, n, tid);
+        rk.store(Kr, n, tid);
+        rv.store(Vr, n, tid);
+        gsc.prefix(sTot, tid);
+        lds_sync();
+        // V fragments (k = token) into registers; V rows are not read after this
+        frag vf[DW][NKT];
+#pragma unroll
+        for (int i = 0; i < DW; ++i) {
+            f32x4 t[4];
+            col_tiles<D, E>(Vr, DW * w + i, j, m, t);
+#pragma unroll
+            for (int kt = 0; kt < NKT; ++kt) vf[i][kt] = cols_frag<E>(&t[FPD * kt]);
+        }
+        lds_sync();
+        gsc.store(sG, sTot, tid);
+        lds_sync();
+        const float* gC = sG + (CH - 1) * GS;
+        // Khat^T fragments of this wave's key tiles
+#pragma unroll
+        for (int i = 0; i < DW; ++i) {
+            const int dt = DW * w + i;
+            f32x4 t[4];
+            col_tiles<D, E>(Kr, dt, j, m, t);
+            const float gcd = gC[16 * dt + m];
+#pragma unroll
+            for (int st = 0; st < 4; ++st)
+#pragma unroll
+                for (int e = 0; e < 4; ++e) t[st][e] *= __expf(gcd - sG[(16 * st + 4 * j + e) * GS + 16 * dt + m]);
+#pragma unroll
+            for (int kt = 0; kt < NKT; ++kt) st_frag(sKf + (size_t)(dt * NKT + kt) * 1024, lane, cols_frag<E>(&t[FPD * kt]));
+        }
+        // P^T for token tile rt = w: lane (j, n) of t[st] holds sum_d k_s[d] q_r[d] e^{G_r[d] - G_s[d]},
+        // s = 16 st + 4 j + e, r = 16 w + n, kept for s <= r; both operands scaled against a
+        // reference token of tile st
+        {
+            f32x4 t[4];
+#pragma unroll
+            for (int st = 0; st < 4; ++st) {
+                t[st] = f32x4{0.f, 0.f, 0.f, 0.f};
+                if (st <= w) {
+                    const float* gref = sG + (16 * st + (st < w ? 15 : 7)) * GS;
+                    const float* gk = sG + (16 * st + m) * GS;   // this lane's key row (A operand row m)
+                    const float* gq = sG + (16 * w + m) * GS;    // and query row (B operand column m)
+#pragma unroll
+                    for (int kd = 0; kd < NKD; ++kd)
+                        t[st] = M::mma(row_frag_exp<E>(Kr + (16 * st + m) * KP, gref, gk, kd * KB, j),
+                                       row_frag_exp<E>(Qr + (16 * w + m) * KP, gq, gref, kd * KB, j), t[st]);
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) t[st][e] = 16 * st + 4 * j + e <= 16 * w + m ? t[st][e] : 0.f;
+                }
+            }
+#pragma unroll
+            for (int kt = 0; kt < NKT; ++kt) st_frag(sPf + (size_t)(w * NKT + kt) * 1024, lane, cols_frag<E>(&t[FPD * kt]));
+        }
+        frag Hf[DW][NKD];
+#pragma unroll
+        for (int i = 0; i < DW; ++i)
+#pragma unroll
+            for (int kd = 0; kd < NKD; ++kd) Hf[i][kd] = M::from_acc(H[i], kd);
+        lds_sync();
+        // O^T = H^T (Q .* e^G)^T + V^T P^T
+        const __amdgpu_buffer_rsrc_t ors = buffer_rsrc(o + tok0 * D, n * D * (int)sizeof(T));
+#pragma unroll
+        for (int rt = 0; rt < 4; ++rt) {
+            const float* gq = sG + (16 * rt + m) * GS;
+            frag qf[NKD];
+#pragma unroll
+            for (int kd = 0; kd < NKD; ++kd) qf[kd] = row_frag_exp<E>(Qr + (16 * rt + m) * KP, gq, nullptr, kd * KB, j);
+            frag pf[NKT];
+#pragma unroll
+            for (int kt = 0; kt < NKT; ++kt) pf[kt] = ld_frag<frag>(sPf + (size_t)(rt * NKT + kt) * 1024, lane);
+#pragma unroll
+            for (int i = 0; i < DW; ++i) {
+                f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                for (int kd = 0; kd < NKD; ++kd) acc = M::mma(Hf[i][kd], qf[kd], acc);
+#pragma unroll
+                for (int kt = 0; kt < NKT; ++kt)
+                    if (kt * KB <= 16 * rt + 15) acc = M::mma(vf[i][kt], pf[kt], acc);
+                const int off = ((16 * rt + m) * D + 16 * (DW * w + i) + 4 * j) * (int)sizeof(T);
+                if constexpr (sizeof(T) == 2) {
+                    const i32x2v x = {(int)f2bf2(acc[0], acc[1]), (int)f2bf2(acc[2], acc[3])};
+                    __builtin_amdgcn_raw_buffer_store_b64(x, ors, off, 0, 0);
+                } else {
+                    const i32x4v x = {__float_as_int(acc[0]), __float_as_int(acc[1]), __float_as_int(acc[2]),
+                                      __float_as_int(acc[3])};
+                    __builtin_amdgcn_raw_buffer_store_b128(x, ors, off, 0, 0);
+                }
+            }
+        }
+        // H = diag(e^{G_C}) H + Khat^T V
+#pragma unroll
+        for (int dt = 0; dt < NDT; ++dt) {
+            const float4 gc = *reinterpret_cast<const float4*>(gC + 16 * dt + 4 * j);
+            const float f[4] = {__expf(gc.x), __expf(gc.y), __expf(gc.z), __expf(gc.w)};
+#pragma unroll
+            for (int i = 0; i < DW; ++i)
+                H[i][dt] = f32x4{H[i][dt][0] * f[0], H[i][dt][1] * f[1], H[i][dt][2] * f[2], H[i][dt][3] * f[3]};
+        }
+#pragma unroll
+        for (int dt = 0; dt < NDT; ++dt)
+#pragma unroll
+            for (int kt = 0; kt < NKT; ++kt) {
+                const frag kf = ld_frag<frag>(sKf + (size_t)(dt * NKT + kt) * 1024, lane);
+#pragma unroll
+                for (int i = 0; i < DW; ++i) H[i][dt] = M::mma(kf, vf[i][kt], H[i][dt]);
+            }
+        if (c + 1 < c_end) load_rows(c + 1);
+    }
+    if (blk == nb - 1) {
+        float* hf = h_final + (size_t)bh * D * D;
+#pragma unroll
+        for (int i = 0; i < DW; ++i)
+#pragma unroll
+            for (int dt = 0; dt < NDT; ++dt)
+#pragma unroll
+                for (int e = 0; e < 4; ++e) hf[(size_t)(16 * dt + 4 * j + e) * D + 16 * (DW * w + i) + m] = H[i][dt][e];
+    }
+}
+
+// ---------------------------------------------------------------------------------------------
 // launch
 // ---------------------------------------------------------------------------------------------
 namespace {
 
 // blocks of chunks per slice: about 512 workgroups for stages 1 and 3 (two per CU), no more than the
-// workspace holds (at least one: the smallest workspace accepted holds one block's state tiles
-// and Lambda per slice)
-int la_blocks(long BH, long nch, size_t tiles, size_t ws_bytes) {
+// workspace holds at `per_block` bytes per block and slice (at least one: the smallest workspace
+// accepted holds one block's state tiles and summed log gates per slice)
+int la_blocks(long BH, long nch, size_t per_block, size_t ws_bytes) {
     long nb = (512 + BH - 1) / BH;
     if (nb > nch) nb = nch;
-    const long fit = (long)(ws_bytes / ((size_t)BH * (tiles + 4)));
+    const long fit = (long)(ws_bytes / ((size_t)BH * per_block));
     if (nb > fit) nb = fit;
     if (nb < 1) nb = 1;
     const long cpb = (nch + nb - 1) / nb;
@@ -407,7 +777,7 @@ static size_t la_tiles(int D) { return D == 128 ? LaLayout<128>::TILES : LaLayou
 size_t linattn_workspace_bytes(long BH, long L, int D) {
     if (L <= 0) return 0;
     const long nch = (L + CH - 1) / CH;
-    return (size_t)BH * la_blocks(BH, nch, la_tiles(D), ~(size_t)0) * (la_tiles(D) + 4);
+    return (size_t)BH * la_blocks(BH, nch, la_tiles(D) + 4, ~(size_t)0) * (la_tiles(D) + 4);
 }
 
 size_t linattn_workspace_min_bytes(long BH, long L, int D) {
@@ -421,7 +791,7 @@ static int launch_linattn_t(const void* q, const void* k, const void* v, const f
     using T = typename E::T;
     using C = LaCfg<D, E>;
     const long nch = (L + CH - 1) / CH;
-    const int nb = la_blocks(BH, nch, LaLayout<D>::TILES, ws_bytes);
+    const int nb = la_blocks(BH, nch, LaLayout<D>::TILES + 4, ws_bytes);
     if ((size_t)BH * nb * (LaLayout<D>::TILES + 4) > ws_bytes) return -1;
     const int cpb = (int)((nch + nb - 1) / nb);
     static const bool attr =
@@ -439,6 +809,59 @@ static int launch_linattn_t(const void* q, const void* k, const void* v, const f
     hipLaunchKernelGGL((la_out_kernel<D, E, GATED>), grid, dim3(256), C::LDS_OUT, stream, (const T*)q, (const T*)k,
                        (const T*)v, log_alpha, (const unsigned char*)ws, (T*)o, h_final, L, cpb, nb);
     return hipGetLastError() == hipSuccess ? 0 : -1;
+}
+
+// per-key-dimension gated linear attention: state tiles and a Dk-vector of summed log gates per block
+size_t gla_workspace_bytes(long BH, long L, int D) {
+    if (L <= 0) return 0;
+    const long nch = (L + CH - 1) / CH;
+    const size_t per = la_tiles(D) + (size_t)4 * D;
+    return (size_t)BH * la_blocks(BH, nch, per, ~(size_t)0) * per;
+}
+
+size_t gla_workspace_min_bytes(long BH, long L, int D) {
+    return L <= 0 ? 0 : (size_t)BH * (la_tiles(D) + (size_t)4 * D);
+}
+
+template <int D, class E>
+static int launch_gla_t(const void* q, const void* k, const void* v, const float* log_alpha, const float* h0,
+                        void* o, float* h_final, long BH, long L, unsigned char* ws, size_t ws_bytes,
+                        hipStream_t stream) {
+    using T = typename E::T;
+    using C = LaCfg<D, E>;
+    using G = GlaCfg<D>;
+    constexpr size_t LDS_KV = 2 * C::ROWS + C::KF + G::GSZ + G::TOT;
+    constexpr size_t LDS_OUT = 3 * C::ROWS + C::KF + C::PF + G::TOT + (sizeof(T) == 2 ? G::GSZ : 0);
+    static_assert(sizeof(T) == 2 || C::ROWS >= G::GSZ, "the cumulative gates fit in the V rows' space");
+    static_assert(LDS_KV <= 160 * 1024 && LDS_OUT <= 160 * 1024, "LDS");
+    const long nch = (L + CH - 1) / CH;
+    const size_t per = LaLayout<D>::TILES + (size_t)4 * D;
+    const int nb = la_blocks(BH, nch, per, ws_bytes);
+    if ((size_t)BH * nb * per > ws_bytes) return -1;
+    const int cpb = (int)((nch + nb - 1) / nb);
+    static const bool attr =
+        hipFuncSetAttribute(reinterpret_cast<const void*>(&gla_kv_kernel<D, E>),
+                            hipFuncAttributeMaxDynamicSharedMemorySize, (int)LDS_KV) == hipSuccess &&
+        hipFuncSetAttribute(reinterpret_cast<const void*>(&gla_out_kernel<D, E>),
+                            hipFuncAttributeMaxDynamicSharedMemorySize, (int)LDS_OUT) == hipSuccess;
+    if (!attr) return -1;
+    if (nb > 1)
+        hipLaunchKernelGGL((gla_kv_kernel<D, E>), dim3((unsigned)(nb - 1), (unsigned)BH), dim3(256), LDS_KV, stream,
+                           (const T*)k, (const T*)v, log_alpha, ws, L, cpb, nb);
+    hipLaunchKernelGGL((gla_scan_kernel<D>), dim3(D * D / 256, (unsigned)BH), dim3(256), 0, stream, ws, h0, nb);
+    hipLaunchKernelGGL((gla_out_kernel<D, E>), dim3((unsigned)nb, (unsigned)BH), dim3(256), LDS_OUT, stream,
+                       (const T*)q, (const T*)k, (const T*)v, log_alpha, (const unsigned char*)ws, (T*)o, h_final, L,
+                       cpb, nb);
+    return hipGetLastError() == hipSuccess ? 0 : -1;
+}
+
+int launch_gla(const void* q, const void* k, const void* v, const float* log_alpha, const float* h0, void* o,
+               float* h_final, int BH, long L, int D, int dtype, void* ws, size_t ws_bytes, hipStream_t stream) {
+    unsigned char* w = static_cast<unsigned char*>(ws);
+    if (D == 128 && dtype == 0) return launch_gla_t<128, BF16>(q, k, v, log_alpha, h0, o, h_final, BH, L, w, ws_bytes, stream);
+    if (D == 128) return launch_gla_t<128, F32>(q, k, v, log_alpha, h0, o, h_final, BH, L, w, ws_bytes, stream);
+    if (dtype == 0) return launch_gla_t<64, BF16>(q, k, v, log_alpha, h0, o, h_final, BH, L, w, ws_bytes, stream);
+    return launch_gla_t<64, F32>(q, k, v, log_alpha, h0, o, h_final, BH, L, w, ws_bytes, stream);
 }
 
 int launch_linattn(const void* q, const void* k, const void* v, const float* log_alpha, const float* h0, void* o,

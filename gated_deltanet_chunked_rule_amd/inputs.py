@@ -8,7 +8,7 @@ article, fileenergy.com, section on checking the selector against the native ker
 
 Recipe (one independent NumPy stream per tensor and per (batch, head) slice):
     rng = numpy.random.default_rng(SeedSequence([seed, tensor_id, stream_index]))
-    tensor_id: q=0, k=1, v=2, beta=3, log_alpha=4, h0/state=5
+    tensor_id: q=0, k=1, v=2, beta=3, log_alpha=4, h0/state=5, log_alpha per key dimension=6
     stream_index: b*H + h for prefill; the decode step index for per-step decode inputs
     (0 for the decode state).
 Values are drawn in fp64, transformed in fp64 and rounded once to the storage dtype
@@ -22,7 +22,7 @@ from typing import Optional
 
 import numpy as np
 
-TID_Q, TID_K, TID_V, TID_BETA, TID_LOGA, TID_H0 = range(6)
+TID_Q, TID_K, TID_V, TID_BETA, TID_LOGA, TID_H0, TID_LOGA_VEC = range(7)
 
 
 # ---------------------------------------------------------------------------
@@ -176,6 +176,25 @@ def prefill_inputs(cfg: PrefillConfig, L: Optional[int] = None) -> dict:
             out[key] = None
         else:
             out[key] = np.stack([np.stack([s[key] for s in row]) for row in sl])
+    return out
+
+
+def gate_vectors(cfg: PrefillConfig, L: Optional[int] = None) -> np.ndarray:
+    """Log gates with one value per token and key dimension, [B,H,L,Dk] fp32 (exact fp64
+    values): the config's gate distribution drawn independently for every key dimension, one
+    stream per (b, h) slice (tensor_id 6), rows filled in token order."""
+    L = cfg.L if L is None else L
+    out = np.empty((cfg.B, cfg.H, L, cfg.Dk))
+    for b in range(cfg.B):
+        for h in range(cfg.H):
+            r = _rng(cfg.seed, TID_LOGA_VEC, b * cfg.H + h)
+            if cfg.gate_dist == "config":
+                la = -_softplus(r.standard_normal((L, cfg.Dk)) + 2.0)
+            elif cfg.gate_dist == "long":
+                la = -r.uniform(0.0, 0.01, (L, cfg.Dk))
+            else:
+                raise ValueError(cfg.gate_dist)
+            out[b, h] = round_fp32(la)
     return out
 
 

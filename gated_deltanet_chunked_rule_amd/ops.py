@@ -129,6 +129,39 @@ def linattn_prefill_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, h0: O
     return _prefill("linattn_prefill_fwd", q, k, v, None, log_alpha, h0, o, h_final, workspace, stream, False)
 
 
+def gla_prefill_workspace_size(B: int, H: int, L: int, D: int, dtype: torch.dtype) -> int:
+    return int(_lib.load().gla_prefill_workspace_size(B, H, L, D, D, _code(dtype)))
+
+
+def gla_prefill_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, log_alpha: torch.Tensor,
+                    h0: Optional[torch.Tensor] = None, *, o: Optional[torch.Tensor] = None,
+                    h_final: Optional[torch.Tensor] = None, workspace: Optional[torch.Tensor] = None,
+                    stream=None) -> Tuple[torch.Tensor, torch.Tensor]:
+    """Gated linear attention with a gate per key dimension: S_t = S_{t-1} diag(exp(log_alpha_t))
+    + v_t k_t^T, o_t = S_t q_t; log_alpha fp32 [B,H,L,D]. Returns (o, h_final)."""
+    B, H, L, D = q.shape
+    dev, dt = q.device, q.dtype
+    _req("q", q, (B, H, L, D), dt, dev)
+    _req("k", k, (B, H, L, D), dt, dev)
+    _req("v", v, (B, H, L, D), dt, dev)
+    _req("log_alpha", log_alpha, (B, H, L, D), torch.float32, dev)
+    if h0 is not None:
+        _req("h0", h0, (B, H, D, D), torch.float32, dev)
+    o = torch.empty_like(v) if o is None else _req("o", o, (B, H, L, D), dt, dev)
+    if h_final is None:
+        h_final = torch.empty((B, H, D, D), dtype=torch.float32, device=dev)
+    _req("h_final", h_final, (B, H, D, D), torch.float32, dev)
+    if workspace is None:
+        workspace = torch.empty(max(gla_prefill_workspace_size(B, H, L, D, dt), 1), dtype=torch.uint8, device=dev)
+    elif not workspace.is_cuda or not workspace.is_contiguous():
+        raise ValueError("workspace must be a contiguous device tensor")
+    rc = _lib.load().gla_prefill_fwd(_p(q), _p(k), _p(v), _p(log_alpha), _p(h0), _p(o), _p(h_final), B, H, L, D, D,
+                                     _code(dt), _p(workspace), workspace.numel() * workspace.element_size(),
+                                     _stream(dev, stream))
+    _lib.check(rc, "gla_prefill_fwd")
+    return o, h_final
+
+
 def gdn_decode_step(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, beta: torch.Tensor,
                     log_alpha: torch.Tensor, state: torch.Tensor, *, o: Optional[torch.Tensor] = None,
                     stream=None) -> torch.Tensor:

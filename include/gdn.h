@@ -158,6 +158,28 @@ int linattn_prefill_fwd(const void *q, const void *k, const void *v,
 size_t linattn_prefill_workspace_size(int B, int H, int L, int Dk, int Dv, int dtype);
 
 /*
+ * Gated linear attention with a gate per key dimension (the forpes.ru article's survey of
+ * linearised models: GLA, its gating applied over the key vectors):
+ *   S_t = S_{t-1} diag(a_t) + v_t k_t^T,   o_t = S_t q_t,   a_t[i] = exp(log_alpha[t][i]),
+ * i.e. in the stored key-major state H = S^T, row i decays by a_t[i] before the write.
+ *   log_alpha   [B,H,L,Dk] fp32 (required when L > 0; log gates below about -10 per token and
+ *               dimension are outside the supported range: within a 16-token tile the kernel
+ *               scales operands by up to exp(8 |log a|))
+ * All other arguments as linattn_prefill_fwd; the workspace holds one Dk x Dv fp32 state and a
+ * Dk-vector of summed log gates per block and (batch, head): at least B*H*(Dk*Dv*4 + Dk*4) bytes
+ * when L > 0, gla_prefill_workspace_size(...) preferred. Runs on `stream` only; L = 0 copies h0
+ * (or zeros) into h_final.
+ */
+int gla_prefill_fwd(const void *q, const void *k, const void *v, const float *log_alpha,
+                    const float *h0, void *o, float *h_final,
+                    int B, int H, int L, int Dk, int Dv, int dtype,
+                    void *workspace, size_t workspace_bytes, void *stream);
+
+/* Preferred bytes of device workspace for gla_prefill_fwd at this shape; 0 for an unsupported
+ * shape or L = 0. */
+size_t gla_prefill_workspace_size(int B, int H, int L, int Dk, int Dv, int dtype);
+
+/*
  * Bidirectional (non-causal) linear attention with a kernel feature map and an optional
  * normaliser (the datadaily.news overview, section "Linear attention", its linear_attention
  * function): per batch b and head h, over the whole sequence,

@@ -180,3 +180,30 @@ def test_banded_host_validation(lib):
     for band in range(4):
         assert call(band) not in (NULL, SHAPE, ALIGN, ALIAS, WORKSPACE)
     assert call(1, beta=None) == NULL
+
+
+def _gla(lib, q=0x10000, k=0x20000000, v=0x40000000, la=0x60000000, h0=None, o=0x70000000, hf=0x7f000000, B=1,
+         H=1, L=64, D=128, dt=0, ws=0x100000000, wsb=1 << 30):
+    return lib.gla_prefill_fwd(q, k, v, la, h0, o, hf, B, H, L, D, D, dt, ws, wsb, None)
+
+
+def test_gla_host_validation(lib):
+    passed = (NULL, SHAPE, DTYPE, ALIGN, WORKSPACE, ALIAS)
+    assert _gla(lib) not in passed
+    assert _gla(lib, la=None) == NULL                  # the per-dimension gates are required
+    assert _gla(lib, L=0, q=None, k=None, v=None, la=None, o=None, ws=None, wsb=0) not in passed
+    assert _gla(lib, hf=None) == NULL
+    assert _gla(lib, D=96) == SHAPE
+    assert _gla(lib, dt=3) == DTYPE
+    assert _gla(lib, la=0x60000008) == ALIGN
+    assert _gla(lib, ws=0x100000010) == ALIGN
+    # log_alpha is [B,H,L,Dk] fp32: 64 x 128 x 4 bytes; an output inside it is an alias
+    assert _gla(lib, o=0x60000000 + 64 * 128 * 4 - 16) == ALIAS
+    assert _gla(lib, o=0x60000000 + 64 * 128 * 4) not in passed
+    blk = 128 * 128 * 4 + 128 * 4                      # one block's state and summed log gates
+    assert _gla(lib, H=3, L=1000, wsb=3 * blk - 1) == WORKSPACE
+    assert _gla(lib, H=3, L=1000, wsb=3 * blk) not in passed
+    f = lib.gla_prefill_workspace_size
+    assert f(1, 1, 64, 128, 128, 0) == blk
+    assert f(2, 2, 64 * 1000, 64, 64, 1) % (4 * (64 * 64 * 4 + 64 * 4)) == 0
+    assert f(1, 1, 0, 128, 128, 0) == 0 and f(1, 1, 64, 96, 96, 0) == 0
