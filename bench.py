@@ -34,11 +34,12 @@ METRIC = "GDN prefill tokens/s at L=128K + % bf16 MFMA peak; decode state GB/s"
 # byte for a plain copy of known size); profiles/gdn_prefill_B1H16L131072_traffic.md holds the
 # commands and the raw figures. Valid only for the kernel sources it was taken on: bench.py
 # reports it only while kernel_source_hash() still matches.
-TRAFFIC_128K = {"source_hash": "610b7a579f9566e2", "bytes_per_call": 6886434808}
+TRAFFIC_128K = {"source_hash": "78b26ac6b5e6fc5c", "bytes_per_call": 6886434808}
 
 
-# the sources the gated delta-rule prefill's kernels and launches are built from
-PREFILL_SOURCES = ("gdn_api.cpp", "gdn_device.h", "gdn_launch.h", "gdn_mfma.h", "gdn_prefill.hip", "gdn_rows.h")
+# the sources the gated delta-rule prefill's kernels and their launcher are built from (the host-side
+# argument checks and declarations do not change what the kernels read and write)
+PREFILL_SOURCES = ("gdn_device.h", "gdn_mfma.h", "gdn_prefill.hip", "gdn_rows.h")
 
 
 def kernel_source_hash():
@@ -131,17 +132,22 @@ def time_loop(torch, fn, steps, warmup):
 def bench_prefill(torch, ops, cfg, steps, warmup, gdn=True, verbose=False, variant=None, keep_rate=0.29,
                   one_segment=False):
     """variant None: gdn_prefill_fwd (gdn) or plain linattn_prefill_fwd; "gla": linattn_prefill_fwd with
-    per-token gates; "skip": gdn_prefill_skip_fwd with a seeded keep mask at keep_rate; "band1":
+    per-token gates; "gla_vec": gla_prefill_fwd with a gate per token and key dimension; "skip":
+    gdn_prefill_skip_fwd with a seeded keep mask at keep_rate; "band1":
     gdn_prefill_banded_fwd with band 1 (flops counted as for the exact rule). one_segment: hand over a
     workspace for the whole sequence, so that the call runs its three kernels once each on one stream
     (the launch that hardware-counter passes use: they serialise dispatches, which the multi-stream
     segment pipeline's value waits do not allow)."""
     gates = gdn or variant == "gla"
     q, k, v, beta, la, h0 = prefill_device_inputs(torch, cfg, gates=gates, verbose=verbose)
+    if variant == "gla_vec":
+        la = torch.from_numpy(inputs.gate_vectors(cfg).astype(np.float32)).cuda()
     o = torch.empty_like(v)
     hf = torch.empty((cfg.B, cfg.H, cfg.Dk, cfg.Dv), device="cuda")
     nchk = (cfg.L + 63) // 64
-    if not gates or variant == "gla":   # linear attention: blocks of chunks
+    if variant == "gla_vec":
+        wsb = ops.gla_prefill_workspace_size(cfg.B, cfg.H, cfg.L, cfg.Dk, q.dtype)
+    elif not gates or variant == "gla":   # linear attention: blocks of chunks
         wsb = ops.linattn_prefill_workspace_size(cfg.B, cfg.H, cfg.L, cfg.Dk, q.dtype)
     elif one_segment:
         wsb = ops.prefill_workspace_size(1, 1, 64, cfg.Dk, q.dtype) * cfg.B * cfg.H * nchk
@@ -161,6 +167,8 @@ def bench_prefill(torch, ops, cfg, steps, warmup, gdn=True, verbose=False, varia
         fn = lambda: ops.gdn_prefill_fwd(q, k, v, beta, la, h0, o=o, h_final=hf, workspace=ws)
     elif variant == "gla":
         fn = lambda: ops.linattn_prefill_fwd(q, k, v, h0, log_alpha=la, o=o, h_final=hf, workspace=ws)
+    elif variant == "gla_vec":
+        fn = lambda: ops.gla_prefill_fwd(q, k, v, la, h0, o=o, h_final=hf, workspace=ws)
     else:
         fn = lambda: ops.linattn_prefill_fwd(q, k, v, h0, o=o, h_final=hf, workspace=ws)
     ms, wall = time_loop(torch, fn, steps, warmup)
@@ -169,11 +177,11 @@ def bench_prefill(torch, ops, cfg, steps, warmup, gdn=True, verbose=False, varia
         flops = nchunk * gdn_flops_per_chunk(64, cfg.Dk) - (nchunk - kept) * 2 * 64 * cfg.Dk * cfg.Dv
     else:
         flops = nchunk * linattn_flops_per_chunk(64, cfg.Dk)
-    nbytes = prefill_bytes(cfg, gates=gdn) + (cfg.B * cfg.H * cfg.L * 4 if variant == "gla" else 0)
+    nbytes = prefill_bytes(cfg, gates=gdn) + cfg.B * cfg.H * cfg.L * 4 * {"gla": 1, "gla_vec": cfg.Dk}.get(variant, 0)
     nbytes += nchunk if variant == "skip" else 0
     res = {
-        "workload": cfg.name + ({"gla": "_gated", "skip": f"_skip_keep{keep_rate}", "band1": "_banded1"}
-                                .get(variant, "")),
+        "workload": cfg.name + ({"gla": "_gated", "gla_vec": "_gated_per_dim", "skip": f"_skip_keep{keep_rate}",
+                                 "band1": "_banded1"}.get(variant, "")),
         "ms": ms, "tokens_per_s": cfg.B * cfg.L / (ms * 1e-3),
         "alg_tflops": flops / (ms * 1e-3) / 1e12, "mfma_frac": flops / (ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS,
         "alg_bytes": nbytes, "hbm_GBps": nbytes / (ms * 1e-3) / 1e9,
@@ -275,8 +283,8 @@ def main():
     ap.add_argument("--profile-decode", type=int, default=0,
                     help="only run this many decode steps (for profilers), no JSON")
     ap.add_argument("--profile-linattn", type=int, default=0,
-                    help="only run this many plain and this many gated linear-attention calls at "
-                         "B=4 H=16 L=8192 after warm-up (for profilers), no JSON")
+                    help="only run this many plain, this many per-token gated and this many per-dimension "
+                         "gated linear-attention calls at B=4 H=16 L=8192 after warm-up (for profilers), no JSON")
     ap.add_argument("--copy-calibrate", type=int, default=0, metavar="BYTES",
                     help="only copy BYTES device-to-device three times (counter calibration), no JSON")
     ap.add_argument("--copy-bandwidth", type=int, default=0, metavar="BYTES",
@@ -324,7 +332,10 @@ def main():
         r = bench_prefill(torch, ops, c, args.profile_linattn, args.warmup, gdn=False)[0]
         rg = bench_prefill(torch, ops, c.with_(gates=True, gate_dist="long"), args.profile_linattn, args.warmup,
                            gdn=False, variant="gla")[0]
-        log(f"profiled {args.profile_linattn} linear-attention calls: plain {r['ms']:.4f} ms, gated {rg['ms']:.4f} ms")
+        rv = bench_prefill(torch, ops, c.with_(gate_dist="config"), args.profile_linattn, args.warmup, gdn=False,
+                           variant="gla_vec")[0]
+        log(f"profiled {args.profile_linattn} linear-attention calls: plain {r['ms']:.4f} ms, gated {rg['ms']:.4f} ms, "
+            f"gated per key dimension {rv['ms']:.4f} ms")
         return
     if args.profile_steps:
         log("generating inputs")
@@ -359,6 +370,11 @@ def main():
         r, b = bench_prefill(torch, ops, inputs.LINATTN_8K.with_(gates=True, gate_dist="long"),
                              max(5, args.steps // 2), 2, gdn=False, variant="gla")
         components["linattn_gated"] = r
+        del b
+        log("[bench] linear attention with a gate per key dimension")
+        r, b = bench_prefill(torch, ops, inputs.LINATTN_8K.with_(gate_dist="config"), max(5, args.steps // 2), 2,
+                             gdn=False, variant="gla_vec")
+        components["linattn_gated_per_dim"] = r
         del b
         log("[bench] gdn 128K with skipped chunk updates (29% kept)")
         r, b = bench_prefill(torch, ops, cfg, max(5, args.steps // 2), 2, variant="skip")
