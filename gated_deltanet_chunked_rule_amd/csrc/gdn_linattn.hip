@@ -495,10 +495,10 @@ __global__ __launch_bounds__(256) void gla_kv_kernel(const typename E::T* __rest
     rk.load(k + ((size_t)bh * L + c_begin * CH) * D, rows_of(c_begin), tid);
     rv.load(v + ((size_t)bh * L + c_begin * CH) * D, rows_of(c_begin), tid);
     GateScan<D> gsc;
+    gsc.load(log_alpha + ((size_t)bh * L + c_begin * CH) * D, rows_of(c_begin), tid);
     for (long c = c_begin; c < c_end; ++c) {
         const int n = rows_of(c);
         const size_t tok0 = (size_t)bh * L + c * CH;
-        gsc.load(log_alpha + tok0 * D, n, tid);
         rk.store(Kr, n, tid);
         rv.store(Vr, n, tid);
         if (c + 1 < c_end) {
@@ -508,6 +508,7 @@ __global__ __launch_bounds__(256) void gla_kv_kernel(const typename E::T* __rest
         gsc.prefix(sTot, tid);
         lds_sync();
         lamv += gsc.store(sG, sTot, tid);
+        if (c + 1 < c_end) gsc.load(log_alpha + (tok0 + CH) * D, rows_of(c + 1), tid);
         lds_sync();
         const float* gC = sG + (CH - 1) * GS;
         frag vf[DW][NKT];
@@ -626,10 +627,10 @@ __global__ __launch_bounds__(256) void gla_out_kernel(
     };
     load_rows(c_begin);
     GateScan<D> gsc;
+    gsc.load(log_alpha + ((size_t)bh * L + c_begin * CH) * D, rows_of(c_begin), tid);
     for (long c = c_begin; c < c_end; ++c) {
         const int n = rows_of(c);
         const size_t tok0 = (size_t)bh * L + c * CH;
-        gsc.load(log_alpha + tok0 * D, n, tid);
         if (c > c_begin) lds_sync();   // every wave is done with the previous chunk's LDS data
         rq.store(Qr, n, tid);
         rk.store(Kr, n, tid);
@@ -647,6 +648,7 @@ __global__ __launch_bounds__(256) void gla_out_kernel(
         }
         lds_sync();
         gsc.store(sG, sTot, tid);
+        if (c + 1 < c_end) gsc.load(log_alpha + (tok0 + CH) * D, rows_of(c + 1), tid);
         lds_sync();
         const float* gC = sG + (CH - 1) * GS;
         // Khat^T fragments of this wave's key tiles
@@ -686,6 +688,19 @@ __global__ __launch_bounds__(256) void gla_out_kernel(
 #pragma unroll
             for (int kt = 0; kt < NKT; ++kt) st_frag(sPf + (size_t)(w * NKT + kt) * 1024, lane, cols_frag<E>(&t[FPD * kt]));
         }
+        // Q rows of token tile w scaled by e^{G_r}, in place: after P^T no other wave reads them
+        {
+            const int r = 16 * w + (lane >> 2);
+            T* qp = Qr + r * KP;
+            const float* gp = sG + r * GS;
+#pragma unroll
+            for (int i = 0; i < D / 16; ++i) {
+                const int d0 = 4 * ((lane & 3) + 4 * i);
+                const float4 a = load4(qp + d0);
+                const float4 g = *reinterpret_cast<const float4*>(gp + d0);
+                store4(qp + d0, make_float4(a.x * __expf(g.x), a.y * __expf(g.y), a.z * __expf(g.z), a.w * __expf(g.w)));
+            }
+        }
         frag Hf[DW][NKD];
 #pragma unroll
         for (int i = 0; i < DW; ++i)
@@ -696,10 +711,9 @@ __global__ __launch_bounds__(256) void gla_out_kernel(
         const __amdgpu_buffer_rsrc_t ors = buffer_rsrc(o + tok0 * D, n * D * (int)sizeof(T));
 #pragma unroll
         for (int rt = 0; rt < 4; ++rt) {
-            const float* gq = sG + (16 * rt + m) * GS;
             frag qf[NKD];
 #pragma unroll
-            for (int kd = 0; kd < NKD; ++kd) qf[kd] = row_frag_exp<E>(Qr + (16 * rt + m) * KP, gq, nullptr, kd * KB, j);
+            for (int kd = 0; kd < NKD; ++kd) qf[kd] = row_frag_raw<E>(Qr + (16 * rt + m) * KP, kd * KB, j);
             frag pf[NKT];
 #pragma unroll
             for (int kt = 0; kt < NKT; ++kt) pf[kt] = ld_frag<frag>(sPf + (size_t)(rt * NKT + kt) * 1024, lane);
