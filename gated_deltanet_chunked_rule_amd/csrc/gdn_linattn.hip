@@ -389,9 +389,9 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void l
 //     O[r]  = (q_r .* e^{G_r})^T H + sum_{s<=r} (sum_d q_r[d] k_s[d] e^{G_r[d] - G_s[d]}) v_s
 //     H'    = diag(e^{G_C}) H + Khat^T V,   Khat[s][d] = k_s[d] e^{G_C[d] - G_s[d]}
 // The same three stages as above, with the block decay a Dk-vector. The intra-chunk products
-// take a reference token per pair of 16-token tiles: tile rt against an earlier tile st uses
-// st's last token, so both factors e^{G_r - G_ref} and e^{G_ref - G_s} are at most 1; a tile
-// against itself uses its middle token, so no factor exceeds e^{8 |log a|} (finite in fp32 for
+// take a reference token per pair of 16-token tiles: tile rt against any earlier tile uses the
+// last token before rt (one scaled query operand serves all of them), so both factors
+// e^{G_r - G_ref} and e^{G_ref - G_s} are at most 1; a tile against itself uses its middle token, so no factor exceeds e^{8 |log a|} (finite in fp32 for
 // per-token log gates above about -10).
 // ---------------------------------------------------------------------------------------------
 namespace {
@@ -666,17 +666,29 @@ __global__ __launch_bounds__(256) void gla_out_kernel(
             for (int kt = 0; kt < NKT; ++kt) st_frag(sKf + (size_t)(dt * NKT + kt) * 1024, lane, cols_frag<E>(&t[FPD * kt]));
         }
         // P^T for token tile rt = w: lane (j, n) of t[st] holds sum_d k_s[d] q_r[d] e^{G_r[d] - G_s[d]},
-        // s = 16 st + 4 j + e, r = 16 w + n, kept for s <= r; both operands scaled against a
-        // reference token of tile st
+        // s = 16 st + 4 j + e, r = 16 w + n, kept for s <= r. Both operands are scaled against a
+        // reference token: for the tiles before the diagonal the last token before tile w (so
+        // the query operand is shared by them), on the diagonal the tile's middle token.
         {
+            const float* gq = sG + (16 * w + m) * GS;    // this lane's query row (B operand column m)
             f32x4 t[4];
+            frag qo[NKD];
+            if (w > 0) {
+                const float* gb = sG + (16 * w - 1) * GS;
+#pragma unroll
+                for (int kd = 0; kd < NKD; ++kd) qo[kd] = row_frag_exp<E>(Qr + (16 * w + m) * KP, gq, gb, kd * KB, j);
+            }
 #pragma unroll
             for (int st = 0; st < 4; ++st) {
                 t[st] = f32x4{0.f, 0.f, 0.f, 0.f};
-                if (st <= w) {
-                    const float* gref = sG + (16 * st + (st < w ? 15 : 7)) * GS;
-                    const float* gk = sG + (16 * st + m) * GS;   // this lane's key row (A operand row m)
-                    const float* gq = sG + (16 * w + m) * GS;    // and query row (B operand column m)
+                const float* gk = sG + (16 * st + m) * GS;   // this lane's key row (A operand row m)
+                if (st < w) {
+                    const float* gb = sG + (16 * w - 1) * GS;
+#pragma unroll
+                    for (int kd = 0; kd < NKD; ++kd)
+                        t[st] = M::mma(row_frag_exp<E>(Kr + (16 * st + m) * KP, gb, gk, kd * KB, j), qo[kd], t[st]);
+                } else if (st == w) {
+                    const float* gref = sG + (16 * st + 7) * GS;
 #pragma unroll
                     for (int kd = 0; kd < NKD; ++kd)
                         t[st] = M::mma(row_frag_exp<E>(Kr + (16 * st + m) * KP, gref, gk, kd * KB, j),
