@@ -88,7 +88,7 @@ class PrefillConfig:
     seed: int
     qk: str = "l2"        # "l2": N(0,1) then L2-normalised per token; "elu1": elu(x)+1; "raw": N(0,1)
     gates: bool = True    # beta and log_alpha present (gated delta rule)
-    gate_dist: str = "config"   # "config": log a = -softplus(N(0,1)+2); "long": -U(0, 0.01)
+    gate_dist: str = "config"   # "config": log a = -softplus(N(0,1)+2); "long": -U(0, 0.01); "strong": -U(0, 8)
     h0: Optional[float] = 0.1   # std of the N(0, 0.01) initial state; None: no h0 (zeros)
     chunk: int = 64
 
@@ -153,6 +153,8 @@ def prefill_slice(cfg: PrefillConfig, b: int, h: int, L: Optional[int] = None) -
             la = -_softplus(r.standard_normal(L) + 2.0)
         elif cfg.gate_dist == "long":
             la = -r.uniform(0.0, 0.01, L)
+        elif cfg.gate_dist == "strong":
+            la = -r.uniform(0.0, 8.0, L)
         else:
             raise ValueError(cfg.gate_dist)
         out["log_alpha"] = round_fp32(la)
@@ -192,6 +194,8 @@ def gate_vectors(cfg: PrefillConfig, L: Optional[int] = None) -> np.ndarray:
                 la = -_softplus(r.standard_normal((L, cfg.Dk)) + 2.0)
             elif cfg.gate_dist == "long":
                 la = -r.uniform(0.0, 0.01, (L, cfg.Dk))
+            elif cfg.gate_dist == "strong":
+                la = -r.uniform(0.0, 8.0, (L, cfg.Dk))
             else:
                 raise ValueError(cfg.gate_dist)
             out[b, h] = round_fp32(la)

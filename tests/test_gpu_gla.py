@@ -139,3 +139,36 @@ def test_gla_full_8k_workload_sampled():
         say(f"  oracle on slice {(b, h)}")
         ro, rh = oracle.gla_vec_prefill(s["q"], s["k"], s["v"], lah[b, h], s["h0"])
         _check(cfg.with_(name=f"{cfg.name} slice {(b, h)}"), o[b:b + 1, h:h + 1], hf[b:b + 1, h:h + 1], ro, rh)
+
+
+@pytest.mark.parametrize("dtype,D", [("bf16", 128), ("f32", 64)])
+def test_gla_strong_gates(dtype, D):
+    """log a ~ -U(0, 8) per token and dimension: the in-chunk operands are scaled by up to e^{64}
+    on the diagonal tiles and the masked entries overflow; the result must still match."""
+    cfg = _cfg(f"gla_strong_{dtype}_d{D}", 1, 2, 333, D, dtype, 7600 + D, gate_dist="strong", qk="l2")
+    say(f"case {cfg.name}")
+    x = inputs.prefill_inputs(cfg)
+    la = inputs.gate_vectors(cfg)
+    q, k, v, lad, h0 = _dev(cfg, x, la)
+    o, hf = ops.gla_prefill_fwd(q, k, v, lad, h0)
+    torch.cuda.synchronize()
+    assert torch.isfinite(o.float()).all() and torch.isfinite(hf).all()
+    ro, rh = oracle.gla_vec_prefill(x["q"], x["k"], x["v"], la, x["h0"])
+    _check(cfg, o, hf, ro, rh)
+
+
+def test_gla_equal_gates_match_per_token_decay():
+    """The same gate on every key dimension is the per-token decay: gla_prefill_fwd against the
+    separate kernels of linattn_prefill_fwd with log_alpha [B,H,L] (both to the oracle's bound)."""
+    cfg = _cfg("gla_equal_gates", 2, 2, 500, 128, "bf16", 7700, gate_dist="config").with_(gates=True)
+    say(f"case {cfg.name}")
+    x = inputs.prefill_inputs(cfg)
+    la_vec = np.repeat(x["log_alpha"][..., None], 128, axis=-1)
+    q, k, v, lad, h0 = _dev(cfg, x, la_vec)
+    o1, h1 = ops.gla_prefill_fwd(q, k, v, lad, h0)
+    o2, h2 = ops.linattn_prefill_fwd(q, k, v, h0, log_alpha=dev_tensor(x["log_alpha"], torch.float32))
+    torch.cuda.synchronize()
+    ro, rh = oracle.gla_prefill(x["q"], x["k"], x["v"], x["log_alpha"], x["h0"])
+    _check(cfg.with_(name="gla_equal_gates per-dimension kernels"), o1, h1, ro, rh)
+    _check(cfg.with_(name="gla_equal_gates per-token kernels"), o2, h2, ro, rh)
+    assert max_rel_err(host(o1), host(o2)) <= TOL_BF16
