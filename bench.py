@@ -34,7 +34,7 @@ METRIC = "GDN prefill tokens/s at L=128K + % bf16 MFMA peak; decode state GB/s"
 # byte for a plain copy of known size); profiles/gdn_prefill_B1H16L131072_traffic.md holds the
 # commands and the raw figures. Valid only for the kernel sources it was taken on: bench.py
 # reports it only while kernel_source_hash() still matches.
-TRAFFIC_128K = {"source_hash": "78b26ac6b5e6fc5c", "bytes_per_call": 6886434808}
+TRAFFIC_128K = {"source_hash": "b64aca00947bf75b", "bytes_per_call": 6886434808}
 
 
 # the sources the gated delta-rule prefill's kernels and their launcher are built from (the host-side

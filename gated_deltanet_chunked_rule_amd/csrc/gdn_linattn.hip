@@ -396,20 +396,20 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void l
 // ---------------------------------------------------------------------------------------------
 namespace {
 
-template <int D>
+template <int D, int NT = 256>
 struct GlaCfg {
     static constexpr int GS = D + 4;                        // row stride of the cumulative gates (floats)
     static constexpr size_t GSZ = (size_t)CH * GS * 4;       // the chunk's cumulative gates
-    static constexpr int NQ = 256 / D, TPQ = CH / NQ;       // gate-scan threads per column, tokens each
+    static constexpr int NQ = NT / D, TPQ = CH / NQ;        // gate-scan threads per column, tokens each
     static constexpr size_t TOT = (size_t)NQ * D * 4;        // per-thread block totals
 };
 
 // Cumulative log gates of a chunk, sG[s][d] = sum_{s' <= s} la[s'][d] (rows past the end add
 // zero). Thread t takes column d = t % D and tokens [qq TPQ, (qq + 1) TPQ), qq = t / D: load,
 // local prefix and block total (then a workgroup barrier), then the earlier blocks' totals added.
-template <int D>
+template <int D, int NT = 256>
 struct GateScan {
-    using G = GlaCfg<D>;
+    using G = GlaCfg<D, NT>;
     float x[G::TPQ];
     __device__ __forceinline__ void load(const float* la_chunk, int n, int tid) {
         const __amdgpu_buffer_rsrc_t rs = buffer_rsrc(la_chunk, n * D * 4);
@@ -579,19 +579,23 @@ __global__ __launch_bounds__(256) void gla_scan_kernel(unsigned char* ws, const 
 }
 
 // 3. outputs from each block's start state; the last block writes h_final. At d = 128 its LDS
-// (the cumulative gates beside the rows) allows one workgroup per CU, so it may use every register.
-template <int D, class E>
-__global__ __launch_bounds__(256) void gla_out_kernel(
+// (the cumulative gates beside the rows) allows one workgroup per CU, which therefore has eight
+// waves (NW = 8: one value tile each, two per SIMD) rather than four.
+template <int D, class E, int NW>
+__global__ __launch_bounds__(64 * NW) void gla_out_kernel(
     const typename E::T* __restrict__ q, const typename E::T* __restrict__ k, const typename E::T* __restrict__ v,
     const float* __restrict__ log_alpha, const unsigned char* __restrict__ ws, typename E::T* __restrict__ o,
     float* __restrict__ h_final, long L, int cpb, int nb) {
     using T = typename E::T;
     using M = MM<E>;
     using C = LaCfg<D, E>;
-    using G = GlaCfg<D>;
+    constexpr int NT = 64 * NW;
+    using G = GlaCfg<D, NT>;
     using frag = typename M::frag;
-    constexpr int KB = C::KB, NDT = C::NDT, NKD = C::NKD, NKT = C::NKT, FPD = C::FPD, KP = C::KP, DW = C::DW,
-                  GS = G::GS;
+    constexpr int KB = C::KB, NDT = C::NDT, NKD = C::NKD, NKT = C::NKT, FPD = C::FPD, KP = C::KP, GS = G::GS;
+    constexpr int DW = NDT / NW;        // value and key tiles per wave
+    constexpr int SPW = 16 / NW;        // key tiles of P per wave (all four with four waves, two with eight)
+    static_assert(DW >= 1 && NDT % NW == 0 && (NW == 4 || NW == 8), "waves");
     extern __shared__ __align__(16) unsigned char smem[];
     T* Qr = reinterpret_cast<T*>(smem);
     T* Kr = reinterpret_cast<T*>(smem + C::ROWS);
@@ -618,7 +622,7 @@ __global__ __launch_bounds__(256) void gla_out_kernel(
 
     auto rows_of = [&](long c) { return (int)(L - c * CH < CH ? L - c * CH : CH); };
     auto src = [&](const T* p, long c) { return p + ((size_t)bh * L + c * CH) * D; };
-    RowRegs<D, E> rq, rk, rv;
+    RowRegs<D, E, NT> rq, rk, rv;
     auto load_rows = [&](long c) {
         const int n = rows_of(c);
         rq.load(src(q, c), n, tid);
@@ -626,7 +630,7 @@ __global__ __launch_bounds__(256) void gla_out_kernel(
         rv.load(src(v, c), n, tid);
     };
     load_rows(c_begin);
-    GateScan<D> gsc;
+    GateScan<D, NT> gsc;
     gsc.load(log_alpha + ((size_t)bh * L + c_begin * CH) * D, rows_of(c_begin), tid);
     for (long c = c_begin; c < c_end; ++c) {
         const int n = rows_of(c);
@@ -665,49 +669,59 @@ __global__ __launch_bounds__(256) void gla_out_kernel(
 #pragma unroll
             for (int kt = 0; kt < NKT; ++kt) st_frag(sKf + (size_t)(dt * NKT + kt) * 1024, lane, cols_frag<E>(&t[FPD * kt]));
         }
-        // P^T for token tile rt = w: lane (j, n) of t[st] holds sum_d k_s[d] q_r[d] e^{G_r[d] - G_s[d]},
-        // s = 16 st + 4 j + e, r = 16 w + n, kept for s <= r. Both operands are scaled against a
-        // reference token: for the tiles before the diagonal the last token before tile w (so
-        // the query operand is shared by them), on the diagonal the tile's middle token.
+        // P^T of token tile rt = w % 4, key tiles [SPW h, SPW h + SPW) (h = w / 4): lane (j, n) of
+        // t[st] holds sum_d k_s[d] q_r[d] e^{G_r[d] - G_s[d]}, s = 16 st + 4 j + e, r = 16 rt + n,
+        // kept for s <= r. Both operands are scaled against a reference token: for the tiles before
+        // the diagonal the last token before tile rt (so the query operand is shared by them), on
+        // the diagonal the tile's middle token.
         {
-            const float* gq = sG + (16 * w + m) * GS;    // this lane's query row (B operand column m)
+            const int rt_w = w & 3, st0 = SPW * (w >> 2);
+            const float* gq = sG + (16 * rt_w + m) * GS;    // this lane's query row (B operand column m)
             f32x4 t[4];
             frag qo[NKD];
-            if (w > 0) {
-                const float* gb = sG + (16 * w - 1) * GS;
+            if (st0 < rt_w) {
+                const float* gb = sG + (16 * rt_w - 1) * GS;
 #pragma unroll
-                for (int kd = 0; kd < NKD; ++kd) qo[kd] = row_frag_exp<E>(Qr + (16 * w + m) * KP, gq, gb, kd * KB, j);
+                for (int kd = 0; kd < NKD; ++kd) qo[kd] = row_frag_exp<E>(Qr + (16 * rt_w + m) * KP, gq, gb, kd * KB, j);
             }
 #pragma unroll
             for (int st = 0; st < 4; ++st) {
                 t[st] = f32x4{0.f, 0.f, 0.f, 0.f};
+                if (st < st0 || st >= st0 + SPW) continue;
                 const float* gk = sG + (16 * st + m) * GS;   // this lane's key row (A operand row m)
-                if (st < w) {
-                    const float* gb = sG + (16 * w - 1) * GS;
+                if (st < rt_w) {
+                    const float* gb = sG + (16 * rt_w - 1) * GS;
 #pragma unroll
                     for (int kd = 0; kd < NKD; ++kd)
                         t[st] = M::mma(row_frag_exp<E>(Kr + (16 * st + m) * KP, gb, gk, kd * KB, j), qo[kd], t[st]);
-                } else if (st == w) {
+                } else if (st == rt_w) {
                     const float* gref = sG + (16 * st + 7) * GS;
 #pragma unroll
                     for (int kd = 0; kd < NKD; ++kd)
                         t[st] = M::mma(row_frag_exp<E>(Kr + (16 * st + m) * KP, gref, gk, kd * KB, j),
-                                       row_frag_exp<E>(Qr + (16 * w + m) * KP, gq, gref, kd * KB, j), t[st]);
+                                       row_frag_exp<E>(Qr + (16 * rt_w + m) * KP, gq, gref, kd * KB, j), t[st]);
 #pragma unroll
-                    for (int e = 0; e < 4; ++e) t[st][e] = 16 * st + 4 * j + e <= 16 * w + m ? t[st][e] : 0.f;
+                    for (int e = 0; e < 4; ++e) t[st][e] = 16 * st + 4 * j + e <= 16 * rt_w + m ? t[st][e] : 0.f;
                 }
             }
+            // the fragments whose key tiles this wave owns (FPD tiles each)
 #pragma unroll
-            for (int kt = 0; kt < NKT; ++kt) st_frag(sPf + (size_t)(w * NKT + kt) * 1024, lane, cols_frag<E>(&t[FPD * kt]));
+            for (int kt = 0; kt < NKT; ++kt)
+                if (FPD * kt >= st0 && FPD * kt < st0 + SPW)
+                    st_frag(sPf + (size_t)(rt_w * NKT + kt) * 1024, lane, cols_frag<E>(&t[FPD * kt]));
         }
-        // Q rows of token tile w scaled by e^{G_r}, in place: after P^T no other wave reads them
+        // Q rows scaled by e^{G_r}, in place, 64 / NW rows per wave. With four waves a wave's rows
+        // are those of its own P tile, which no other wave reads; with eight, two waves read each
+        // tile's query rows, so all of P is formed first.
+        if constexpr (NW == 8) lds_sync();
         {
-            const int r = 16 * w + (lane >> 2);
+            constexpr int RPW = 64 / NW, LPR = 64 / RPW;
+            const int r = RPW * w + lane / LPR;
             T* qp = Qr + r * KP;
             const float* gp = sG + r * GS;
 #pragma unroll
-            for (int i = 0; i < D / 16; ++i) {
-                const int d0 = 4 * ((lane & 3) + 4 * i);
+            for (int i = 0; i < D / (4 * LPR); ++i) {
+                const int d0 = 4 * (lane % LPR + LPR * i);
                 const float4 a = load4(qp + d0);
                 const float4 g = *reinterpret_cast<const float4*>(gp + d0);
                 store4(qp + d0, make_float4(a.x * __expf(g.x), a.y * __expf(g.y), a.z * __expf(g.z), a.w * __expf(g.w)));
@@ -856,8 +870,10 @@ static int launch_gla_t(const void* q, const void* k, const void* v, const float
     using T = typename E::T;
     using C = LaCfg<D, E>;
     using G = GlaCfg<D>;
+    constexpr int NWO = D == 128 ? 8 : 4;   // waves of the output stage
+    using GO = GlaCfg<D, 64 * NWO>;
     constexpr size_t LDS_KV = 2 * C::ROWS + C::KF + G::GSZ + G::TOT;
-    constexpr size_t LDS_OUT = 3 * C::ROWS + C::KF + C::PF + G::TOT + (sizeof(T) == 2 ? G::GSZ : 0);
+    constexpr size_t LDS_OUT = 3 * C::ROWS + C::KF + C::PF + GO::TOT + (sizeof(T) == 2 ? G::GSZ : 0);
     static_assert(sizeof(T) == 2 || C::ROWS >= G::GSZ, "the cumulative gates fit in the V rows' space");
     static_assert(LDS_KV <= 160 * 1024 && LDS_OUT <= 160 * 1024, "LDS");
     const long nch = (L + CH - 1) / CH;
@@ -868,14 +884,14 @@ static int launch_gla_t(const void* q, const void* k, const void* v, const float
     static const bool attr =
         hipFuncSetAttribute(reinterpret_cast<const void*>(&gla_kv_kernel<D, E>),
                             hipFuncAttributeMaxDynamicSharedMemorySize, (int)LDS_KV) == hipSuccess &&
-        hipFuncSetAttribute(reinterpret_cast<const void*>(&gla_out_kernel<D, E>),
+        hipFuncSetAttribute(reinterpret_cast<const void*>(&gla_out_kernel<D, E, NWO>),
                             hipFuncAttributeMaxDynamicSharedMemorySize, (int)LDS_OUT) == hipSuccess;
     if (!attr) return -1;
     if (nb > 1)
         hipLaunchKernelGGL((gla_kv_kernel<D, E>), dim3((unsigned)(nb - 1), (unsigned)BH), dim3(256), LDS_KV, stream,
                            (const T*)k, (const T*)v, log_alpha, ws, L, cpb, nb);
     hipLaunchKernelGGL((gla_scan_kernel<D>), dim3(D * D / 256, (unsigned)BH), dim3(256), 0, stream, ws, h0, nb);
-    hipLaunchKernelGGL((gla_out_kernel<D, E>), dim3((unsigned)nb, (unsigned)BH), dim3(256), LDS_OUT, stream,
+    hipLaunchKernelGGL((gla_out_kernel<D, E, NWO>), dim3((unsigned)nb, (unsigned)BH), dim3(64 * NWO), LDS_OUT, stream,
                        (const T*)q, (const T*)k, (const T*)v, log_alpha, (const unsigned char*)ws, (T*)o, h_final, L,
                        cpb, nb);
     return hipGetLastError() == hipSuccess ? 0 : -1;

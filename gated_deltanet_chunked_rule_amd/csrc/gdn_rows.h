@@ -1,5 +1,5 @@
 // Row staging and small wave / workgroup helpers shared by the linear-attention kernels
-// (causal and bidirectional). gfx950 only; 64-lane wavefronts, 256-thread workgroups.
+// (causal and bidirectional). gfx950 only; 64-lane wavefronts, 256-thread workgroups unless stated.
 #pragma once
 #include "gdn_mfma.h"
 
@@ -37,20 +37,20 @@ struct AsIs {
     __device__ __forceinline__ uint4 operator()(uint4 x) const { return x; }
 };
 
-// A 64-row chunk (row stride D in global memory) in flight in registers: 256 threads, 16 bytes
-// each per step. Loading the next chunk while the current one is processed keeps more of HBM's
+// A 64-row chunk (row stride D in global memory) in flight in registers: NT threads (256 unless
+// stated), 16 bytes each per step. Loading the next chunk while the current one is processed keeps more of HBM's
 // latency covered than the workgroups of one CU do alone. Loads go through a buffer resource
 // over the chunk's valid rows, so the rows past the end of the sequence read as zero and no
 // load sits behind a branch.
-template <int D, class E>
+template <int D, class E, int NT = 256>
 struct RowRegs {
-    static constexpr int ES = sizeof(typename E::T), EPU = 16 / ES, UPR = D / EPU, N = CH * UPR / 256;
+    static constexpr int ES = sizeof(typename E::T), EPU = 16 / ES, UPR = D / EPU, N = CH * UPR / NT;
     uint4 x[N];
     // rows [0, n) of src; the others are zero
     __device__ __forceinline__ void load(const typename E::T* src, int n, int tid) {
         const __amdgpu_buffer_rsrc_t rs = buffer_rsrc(src, n * D * ES);
 #pragma unroll
-        for (int i = 0; i < N; ++i) x[i] = buffer_load16(rs, (tid + 256 * i) * 16);
+        for (int i = 0; i < N; ++i) x[i] = buffer_load16(rs, (tid + NT * i) * 16);
     }
     // into LDS with row stride row_stride<D, E>() (rows 8-byte aligned: two 8-byte stores per
     // 16 bytes), f applied to rows [0, n), the others zero (masked, not branched, so that the
@@ -60,7 +60,7 @@ struct RowRegs {
         constexpr int KP = row_stride<D, E>();
 #pragma unroll
         for (int i = 0; i < N; ++i) {
-            const int u = tid + 256 * i, r = u / UPR, cu = u % UPR;
+            const int u = tid + NT * i, r = u / UPR, cu = u % UPR;
             const unsigned keep = 0u - (unsigned)(r < n);
             const uint4 y = f(x[i]);
             uint2* d = reinterpret_cast<uint2*>(dst + r * KP + cu * EPU);
