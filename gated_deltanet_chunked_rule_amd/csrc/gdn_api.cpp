@@ -70,16 +70,16 @@ int validate_prefill(const void* q, const void* k, const void* v, const float* b
     const size_t esz = dtype == GDN_BF16 ? 2 : 4;
     const size_t BH = (size_t)B * H;
     const size_t tok = BH * (size_t)L;
-    if (need > 0) {
-        if (!workspace || workspace_bytes < need) return GDN_ERR_WORKSPACE;
-        if (!aligned(workspace, 256)) return GDN_ERR_ALIGN;
-    }
+    if (need > 0 && (!workspace || workspace_bytes < need)) return GDN_ERR_WORKSPACE;
+    // a workspace is optional where none is needed, but one that is handed over is used
+    const bool use_ws = workspace && workspace_bytes > 0;
+    if (use_ws && !aligned(workspace, 256)) return GDN_ERR_ALIGN;
     const size_t nchk = ((size_t)L + 63) / 64;
     const Range in[] = {rng(q, tok * Dk * esz), rng(k, tok * Dk * esz), rng(v, tok * Dv * esz),
                         rng(beta, beta ? tok * 4 : 0), rng(log_alpha, log_alpha ? tok * 4 : 0),
                         rng(keep, keep ? BH * nchk : 0), rng(h0, h0 ? BH * Dk * Dv * 4 : 0)};
     const Range ro = rng(o, tok * Dv * esz), rh = rng(h_final, BH * Dk * Dv * 4);
-    const Range rw = rng(workspace, workspace && need ? workspace_bytes : 0);
+    const Range rw = rng(workspace, use_ws ? workspace_bytes : 0);
     for (int i = 0; i < 7; ++i) {
         if (overlap(ro, in[i]) || overlap(rw, in[i])) return GDN_ERR_ALIAS;
         if (i == 6 && h0 == h_final) continue;  // in-place state update is allowed

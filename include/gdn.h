@@ -27,7 +27,7 @@
  *     every state are always fp32.
  *   - Launches are asynchronous on `stream` (a hipStream_t passed as void*; NULL = the null
  *     stream). A return of GDN_OK means the work was enqueued. The library never allocates
- *     device memory; long prefills also use an internal stream (see gdn_prefill_fwd).
+ *     device memory and uses no stream but the caller's.
  *   - Errors are returned as negative status codes; validation happens before any launch, so
  *     on an error nothing was enqueued and no output was touched.
  *   - Supported sizes: Dk = Dv in {64, 128}; the chunk length is fixed at 64 tokens; any
@@ -62,35 +62,34 @@ const char *gdn_status_string(int status);
 
 /* Preferred bytes of device workspace for gdn_prefill_fwd, gdn_prefill_skip_fwd and
  * gdn_prefill_banded_fwd at this shape.
- * The workspace holds the per-chunk operands the intra-chunk stage hands to the sequential
- * stage. A short sequence is processed in one segment; a long one in segments whose stages
- * overlap (the intra-chunk stage of later segments on an internal stream beside the sequential
- * stage on `stream`), with two segment buffers of about 72 MB each followed by 256 bytes of
- * progress counters that order the two. Where the sequential stage alone fills every compute
- * unit of the current device (more than 24 (batch, head) slices at Dk = 128 on MI355X's 256
- * CUs) the stages cannot overlap, and the preferred size holds the whole sequence's records if
- * they take at most 2 GiB. Any workspace that holds the whole sequence's records, or two chunk
- * records per (batch, head) plus those 256 bytes, is accepted; a smaller one just means shorter
- * segments. Returns 0 for an unsupported shape or L = 0. */
+ * The prefill cuts each (batch, head) sequence into NB blocks of whole 64-token chunks. Each
+ * block's affine state map (the composition of its chunks' maps S -> A S + B, SparseGDN article,
+ * section on embedding the selector into FLA) is formed for all blocks in parallel, a short
+ * sequential pass over the blocks gives every block's start state, and the blocks' outputs are
+ * then formed in parallel. The workspace holds, per (batch, head), the maps of NB - 1 blocks and
+ * NB block-start states: (2 NB - 1) * 4 * Dk * Dv bytes. The preferred NB gives about two
+ * output workgroups per compute unit of the current device (one block, i.e. no workspace, when
+ * the (batch, head) slices alone give every compute unit one). Any workspace is accepted, none
+ * included: the call uses the largest NB up to the preferred one whose bytes fit, and with no
+ * workspace each slice runs its chunks in sequence in one workgroup. Results depend on NB only
+ * through rounding. Returns 0 for an unsupported shape or L = 0. */
 size_t gdn_prefill_workspace_size(int B, int H, int L, int Dk, int Dv, int dtype);
 
 /*
  * Chunked prefill of the gated delta rule.
  *   q, k        [B,H,L,Dk] dtype        v, o   [B,H,L,Dv] dtype   (may be NULL when L = 0)
  *   beta        [B,H,L] fp32            log_alpha [B,H,L] fp32 (log of the forget gate, <= 0
- *                                        in normal use; exp(log_alpha) is the gate)
+ *                                        in normal use; exp(log_alpha) is the gate; -inf is a
+ *                                        zero gate, which clears the state before the token's write)
  *   h0          [B,H,Dk,Dv] fp32 initial state, or NULL for zeros
  *   h_final     [B,H,Dk,Dv] fp32 final state; may equal h0 (in-place update), any other
  *               overlap is GDN_ERR_ALIAS
- *   workspace   device buffer, 256-byte aligned, gdn_prefill_workspace_size(...) bytes preferred
- *               (see above for the minimum); scratch, reusable once the call's work completes
- * Streams: a call that needs more than one segment also runs work on an internal stream of the
- * current device (created on first use, default priority): it starts after the work already
- * queued on `stream`, and work queued on `stream` afterwards starts after all of it. Calls that
- * run segments serialise on a per-device lock. The stages wait for each other on progress
- * counters in the workspace; a wait that lasts more than about 10 s (a device starved by other
- * work) gives up, and the call's o and h_final then come out NaN.
- * L = 0 copies h0 (or zeros) into h_final. Non-finite inputs propagate; they are not checked.
+ *   workspace   device buffer, 256-byte aligned, or NULL; gdn_prefill_workspace_size(...) bytes
+ *               preferred (see above); scratch, reusable once the call's work completes
+ * Up to three kernels run in order on `stream` (block maps, the pass over blocks, outputs); the
+ * library keeps no state between calls and waits for nothing outside the stream's order.
+ * L = 0 copies h0 (or zeros) into h_final. Non-finite inputs other than a log gate of -inf
+ * propagate; they are not checked.
  */
 int gdn_prefill_fwd(const void *q, const void *k, const void *v,
                     const float *beta, const float *log_alpha, const float *h0,
@@ -109,7 +108,9 @@ int gdn_prefill_fwd(const void *q, const void *k, const void *v,
  *   keep        [B,H,ceil(L/64)] uint8 device array (any alignment; read, never written); NULL
  *               only when L = 0. A head-pair selector is expressed by repeating its mask.
  * All other arguments, the workspace and the stream behaviour as gdn_prefill_fwd. With every
- * keep byte nonzero the result equals gdn_prefill_fwd's bit for bit.
+ * keep byte nonzero and the same workspace size the result equals gdn_prefill_fwd's bit for bit.
+ * A skipped chunk's state map is a scalar decay, so blocks of skipped chunks cost little in the
+ * map stage.
  */
 int gdn_prefill_skip_fwd(const void *q, const void *k, const void *v,
                          const float *beta, const float *log_alpha, const unsigned char *keep,
@@ -123,8 +124,9 @@ int gdn_prefill_skip_fwd(const void *q, const void *k, const void *v,
  * across neighbouring blocks, a fixed structured approximation). Each 64-token chunk's inverse
  * T = (I + A)^-1 is formed in 16 x 16 blocks; blocks more than `band` block rows below the
  * diagonal are set to zero instead of computed (their terms drop out of W and U), the others are
- * the exact inverse's blocks. band in 0 .. 3; band = 3 is gdn_prefill_fwd bit for bit (other
- * values: GDN_ERR_SHAPE). All other arguments, the workspace and the streams as gdn_prefill_fwd.
+ * the exact inverse's blocks. band in 0 .. 3; band = 3 is gdn_prefill_fwd bit for bit at the
+ * same workspace size (other values: GDN_ERR_SHAPE). All other arguments, the workspace and the
+ * stream as gdn_prefill_fwd.
  */
 int gdn_prefill_banded_fwd(const void *q, const void *k, const void *v,
                            const float *beta, const float *log_alpha, const float *h0,

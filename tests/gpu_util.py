@@ -44,3 +44,10 @@ def max_rel_err(got, ref, axes=None):
 
 TOL_BF16 = 2e-2   # bf16 inputs: max relative error bound per (b, h) slice, o and final state
 TOL_F32 = 1e-4    # fp32 inputs
+
+
+def prefill_workspace(torch, B, H, D, nblocks):
+    """A gated delta-rule prefill workspace that holds `nblocks` blocks per (batch, head): the call
+    then uses that many blocks (at most its preferred count and one per chunk)."""
+    n = B * H * (2 * nblocks - 1) * 4 * D * D
+    return torch.empty(max(n, 1), dtype=torch.uint8, device="cuda")

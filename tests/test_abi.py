@@ -39,25 +39,25 @@ def test_status_strings(lib):
 
 
 def test_workspace_size_query(lib):
+    """The prefill workspace holds (2 NB - 1) block records of 4 Dk Dv bytes per slice for NB blocks;
+    the preferred NB gives about two output workgroups per CU (256 CUs when no GPU answers)."""
     f = lib.gdn_prefill_workspace_size
-    rec = f(1, 1, 64, 128, 128, 0)                     # one chunk record of one slice
-    assert rec > 0
-    assert f(1, 1, 64 * 100, 128, 128, 0) == 100 * rec   # short: the whole sequence, one segment
-    big = f(1, 16, 131072, 128, 128, 0)                  # long: two segment buffers, 256 B of counters
-    assert (big - 256) % (2 * 16 * rec) == 0 and big < 2048 * 16 * rec
-    assert 130 << 20 < big <= 200 << 20
-    assert f(1, 1, 65, 64, 64, 1) == 2 * f(1, 1, 64, 64, 64, 1)   # a ragged tail costs a whole chunk
-    # smallest accepted workspace: the whole sequence up to two chunks, else two one-chunk
-    # buffers and the counters
-    assert _prefill(lib, L=128, wsb=2 * rec - 1) == WORKSPACE
-    assert _prefill(lib, L=128, wsb=2 * rec) not in (NULL, ALIGN, ALIAS, WORKSPACE)
-    assert _prefill(lib, L=129, wsb=2 * rec) == WORKSPACE
-    assert _prefill(lib, L=129, wsb=2 * rec + 256) not in (NULL, ALIGN, ALIAS, WORKSPACE)
+    rec = lambda d: 4 * d * d
+    assert f(1, 1, 64, 128, 128, 0) == 0                  # one chunk: one block, no workspace
+    assert f(1, 1, 64 * 5, 128, 128, 0) == 9 * rec(128)     # five chunks, five blocks of one
+    big = f(1, 16, 131072, 128, 128, 0)                    # 2048 chunks: 32 blocks of 64 per slice
+    assert big == 16 * (2 * 32 - 1) * rec(128)
+    assert f(1, 32, 32768, 128, 128, 0) == 32 * (2 * 16 - 1) * rec(128)
+    assert f(1, 16, 131072, 64, 64, 1) == 16 * (2 * 32 - 1) * rec(64)   # sizes do not depend on dtype
+    assert f(2, 128, 4096, 128, 128, 0) == 0                # 256 slices fill the device alone
     assert f(1, 2, 0, 128, 128, 0) == 0
     assert f(1, 1, 64, 96, 96, 0) == 0        # unsupported head size
     assert f(1, 1, 64, 128, 64, 0) == 0       # Dk != Dv
     assert f(1, 1, 64, 128, 128, 2) == 0      # bad dtype
     assert f(0, 1, 64, 128, 128, 0) == 0
+    # any workspace is accepted, none included (one block per slice then)
+    for ws, wsb in ((None, 0), (0x100000000, 1), (0x100000000, 1 << 30)):
+        assert _prefill(lib, L=4096, ws=ws, wsb=wsb) not in (NULL, ALIGN, ALIAS, WORKSPACE)
 
 
 def _prefill(lib, q=0x10000, k=0x20000000, v=0x40000000, beta=0x60000000, la=0x60100000, h0=None,
@@ -77,8 +77,8 @@ def test_prefill_host_validation(lib):
     assert _prefill(lib, dt=5) == DTYPE
     assert _prefill(lib, q=0x10008) == ALIGN
     assert _prefill(lib, ws=0x100000010) == ALIGN      # workspace needs 256-byte alignment
-    assert _prefill(lib, ws=None) == WORKSPACE
-    assert _prefill(lib, wsb=1000) == WORKSPACE
+    assert _prefill(lib, ws=0x100000010, wsb=0) not in (NULL, ALIGN, ALIAS, WORKSPACE)   # an empty one is unused
+    assert _prefill(lib, ws=0x40000000 - 256) == ALIAS  # workspace runs into v
     assert _prefill(lib, o=0x20000000) == ALIAS        # o == k
     assert _prefill(lib, hf=0x40000000 + 4096) == ALIAS  # h_final inside v
     assert _prefill(lib, h0=0x7f000000 + 16) == ALIAS  # partial h0 / h_final overlap

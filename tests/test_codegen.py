@@ -27,7 +27,7 @@ SOURCES = ["gdn_prefill.hip", "gdn_decode.hip", "gdn_bidir.hip", "gdn_linattn.hi
 
 def _device_asm(src, tmp_path):
     out = tmp_path / (src + ".s")
-    flags = [f for f in build.FLAGS if f not in ("-shared", "-fPIC")]
+    flags = [f for f in build.flags_for(src) if f != "-fPIC"]
     cmd = [HIPCC] + flags + ["--cuda-device-only", "-S", "-o", str(out), os.path.join(build.CSRC, src)]
     r = subprocess.run(cmd, capture_output=True, text=True)
     assert r.returncode == 0, r.stderr[-2000:]

@@ -6,7 +6,7 @@ import pytest
 
 import oracle
 from gated_deltanet_chunked_rule_amd import inputs
-from gpu_util import TOL_BF16, TOL_F32, dev_tensor, host, max_rel_err, say
+from gpu_util import TOL_BF16, TOL_F32, dev_tensor, host, max_rel_err, prefill_workspace, say
 
 torch = pytest.importorskip("torch")
 pytestmark = pytest.mark.gpu
@@ -56,14 +56,13 @@ def test_full_band_is_the_dense_path_bitwise():
 
 
 def test_banded_full_size_sampled_heads():
-    """The 32K GDN workload (B=1, H=32, L=32768) with band 1, long-memory gates, in segments of 30
-    chunks (the chain fills the device at 32 heads, so its segments alternate with prep's)."""
+    """The 32K GDN workload (B=1, H=32, L=32768) with band 1, long-memory gates, its sequences in 7
+    blocks (of 74 chunks, the last one shorter)."""
     cfg = inputs.GDN_32K.with_(gate_dist="long")
-    say(f"case {cfg.name} band 1, segmented")
+    say(f"case {cfg.name} band 1, 7 blocks")
     x = inputs.prefill_inputs(cfg)
     q, k, v, beta, la, h0 = _dev(cfg, x)
-    rec = ops.prefill_workspace_size(1, 1, 64, 128, torch.bfloat16) * cfg.B * cfg.H
-    ws = torch.empty(2 * 30 * rec + 256, dtype=torch.uint8, device="cuda")
+    ws = prefill_workspace(torch, cfg.B, cfg.H, 128, 7)
     o, hf = ops.gdn_prefill_banded_fwd(q, k, v, beta, la, h0, band=1, workspace=ws)
     torch.cuda.synchronize()
     o, hf = host(o), host(hf)

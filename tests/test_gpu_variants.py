@@ -13,7 +13,7 @@ import pytest
 
 import oracle
 from gated_deltanet_chunked_rule_amd import inputs
-from gpu_util import TOL_BF16, TOL_F32, dev_tensor, host, max_rel_err, say
+from gpu_util import TOL_BF16, TOL_F32, dev_tensor, host, max_rel_err, prefill_workspace, say
 
 torch = pytest.importorskip("torch")
 pytestmark = pytest.mark.gpu
@@ -124,20 +124,22 @@ def test_skip_all_kept_is_the_dense_path_bitwise():
     assert torch.equal(o1, o2) and torch.equal(h1, h2)
 
 
-def test_skip_segmented_schedule_is_bitwise_identical():
-    """The keep mask is indexed across segment boundaries: short segments give the same bits."""
-    cfg = inputs.GDN_32K.with_(name="skip_segments", B=1, H=2, L=2000, seed=7200)
+def test_skip_block_counts_match_the_oracle():
+    """The keep mask is indexed across block boundaries: one, two, five and 32 blocks per slice
+    (blocks that begin or end with skipped chunks, blocks with nothing kept) agree with the oracle."""
+    cfg = inputs.GDN_32K.with_(name="skip_blocks", B=1, H=2, L=2000, seed=7200, gate_dist="long")
     say(f"case {cfg.name}")
     x = inputs.prefill_inputs(cfg)
     q, k, v, beta, la, h0 = _dev(cfg, x)
-    keep = torch.from_numpy(_keep(7200, 1, 2, 2000, 0.4)).cuda()
-    o1, h1 = ops.gdn_prefill_skip_fwd(q, k, v, beta, la, keep, h0)
-    rec = ops.prefill_workspace_size(1, 2, 64, 128, torch.bfloat16)
-    for seg in (1, 3):
-        ws = torch.empty(2 * seg * rec + 256, dtype=torch.uint8, device="cuda")
-        o2, h2 = ops.gdn_prefill_skip_fwd(q, k, v, beta, la, keep, h0, workspace=ws)
+    keep_np = _keep(7200, 1, 2, 2000, 0.4)
+    keep_np[0, 1, 8:16] = 0    # a whole block skipped at 5 blocks
+    keep = torch.from_numpy(keep_np).cuda()
+    ro, rh = oracle.gdn_prefill_skip(x["q"], x["k"], x["v"], x["beta"], x["log_alpha"], keep_np, x["h0"])
+    for nb in (1, 2, 5, 32):
+        ws = prefill_workspace(torch, 1, 2, 128, nb) if nb > 1 else None
+        o, hf = ops.gdn_prefill_skip_fwd(q, k, v, beta, la, keep, h0, workspace=ws)
         torch.cuda.synchronize()
-        assert torch.equal(o1, o2) and torch.equal(h1, h2), seg
+        _check(host(o), host(hf), ro, rh, TOL_BF16, f"{nb} blocks")
 
 
 def test_skip_full_size_sampled_heads():
