@@ -48,7 +48,7 @@ namespace gdn {
 constexpr size_t cmax(size_t a, size_t b) { return a > b ? a : b; }
 constexpr size_t up16(size_t x) { return (x + 15) / 16 * 16; }
 
-template <int D, class E, bool OUT = false>
+template <int D, class E, int NW_ = 4>
 struct Cfg {
     using T = typename E::T;
     using M = MM<E>;
@@ -57,12 +57,10 @@ struct Cfg {
     static constexpr int NDT = D / 16;                        // 16-wide tiles along d
     static constexpr int NKD = D / KB;                        // fragments along d
     static constexpr int NKT = CH / KB;                       // fragments along a chunk's tokens
-    // waves per workgroup: four for the bf16 output kernel (two workgroups share a CU, so one's
-    // serial phases overlap the other's matrix work), eight at Dk = 128 otherwise (the map
-    // kernel's two state blocks, and fp32 operands, need the registers of two waves per tile)
-    static constexpr int NW = NDT >= 8 && (!OUT || sizeof(T) == 4) ? 8 : 4;
+    static constexpr int NW = NW_;                            // waves sharing the d (value) tiles
     static constexpr int NT = 64 * NW;                        // their threads
     static constexpr int VPW = NDT / NW;                      // d (and value) tiles per wave
+    static_assert(NDT % NW == 0, "whole tiles per wave");
     static constexpr int SVPW = NDT / 4;                      // row tiles per wave of the scan
     static constexpr int NSPLIT = sizeof(T) == 2 ? 2 : 1;     // bf16 operands as high + low parts
     static constexpr int KP = row_stride<D, E>();             // row stride of staged rows (elements)
@@ -78,6 +76,24 @@ struct Cfg {
         for (int rt = 0; rt < 4; ++rt) c += (16 * rt + 15) / KB + 1;
         return c;
     }();
+};
+
+// Waves per workgroup of the output kernel: four for bf16 (two workgroups share a CU, so one's
+// serial phases overlap the other's matrix work), eight for fp32 at Dk = 128 (its operands
+// need the registers of two waves per value tile).
+template <int D, class E>
+constexpr int out_waves() { return D == 128 && sizeof(typename E::T) == 4 ? 8 : 4; }
+
+// The map kernel holds two fp32 state blocks, so at Dk = 128 it runs eight waves, one value tile
+// each. With bf16 it works on chunks in pairs: each half of the workgroup (four waves) does the
+// intra-chunk solve of one chunk of the pair in its own LDS slot, so the two serial solves run
+// side by side, and then all eight waves apply both chunks to the state in order.
+template <int D, class E>
+struct MapCfg {
+    static constexpr bool PAIR = D == 128 && sizeof(typename E::T) == 2;
+    static constexpr int NWS = D == 128 ? 8 : 4;     // waves holding the state
+    static constexpr int NWP = PAIR ? 4 : NWS;       // waves per chunk's solve
+    static constexpr int NH = PAIR ? 2 : 1;          // chunks per iteration
 };
 
 // per-token gate arrays of the chunk in LDS
@@ -237,9 +253,9 @@ __device__ __forceinline__ f32x4 scale4(const f32x4& t, float s) { return f32x4{
 // fragments straight from memory (only its own tiles are transposed, so V never goes through
 // LDS), and for wave 0 the gates. Loads go through buffer resources over the chunk's valid
 // tokens: rows past the end of the sequence read as zero.
-template <int D, class E, bool OUT>
+template <int D, class E, bool OUT, int NW>
 struct Fetch {
-    using C = Cfg<D, E, OUT>;
+    using C = Cfg<D, E, NW>;
     using T = typename E::T;
     using frag = typename MM<E>::frag;
     static constexpr int NGW = C::VPW >= C::FPD ? C::VPW / C::FPD : 1;   // fragment groups of V a wave owns
@@ -316,12 +332,12 @@ __device__ __forceinline__ void inverse_block(const float* Am, float* Tm, int bj
 //     (scaled by beta into `vb`);
 // then T = (I + A)^-1 blocked by 16 (blocks more than `band` below the diagonal zero). Returns
 // after the barrier that completes T. Wave w owns d (and value) tiles VPW w .. VPW w + VPW - 1.
-template <int D, class E, bool OUT>
+template <int D, class E, bool OUT, int NW>
 __device__ __forceinline__ void intra_solve(unsigned char* smem, int band, int w, int lane,
-                                            const typename MM<E>::frag (&vf)[Fetch<D, E, OUT>::NGW][4],
-                                            typename MM<E>::frag (&kbe)[Cfg<D, E, OUT>::VPW][Cfg<D, E, OUT>::NKT],
-                                            typename MM<E>::frag (&vb)[Cfg<D, E, OUT>::VPW][Cfg<D, E, OUT>::NKT]) {
-    using C = Cfg<D, E, OUT>;
+                                            const typename MM<E>::frag (&vf)[Fetch<D, E, OUT, NW>::NGW][4],
+                                            typename MM<E>::frag (&kbe)[Cfg<D, E, NW>::VPW][Cfg<D, E, NW>::NKT],
+                                            typename MM<E>::frag (&vb)[Cfg<D, E, NW>::VPW][Cfg<D, E, NW>::NKT]) {
+    using C = Cfg<D, E, NW>;
     using L = Lds<D, E, OUT>;
     using M = MM<E>;
     using T = typename E::T;
@@ -487,22 +503,33 @@ __device__ __forceinline__ void intra_solve(unsigned char* smem, int band, int w
 //   Psi[t][vt] lane (j, n): Psi[16 (VPW w + t) + 4 j + e][16 vt + n]
 // Per kept chunk (last to first):  Y = Khat Z (Z as high + low bf16 parts),  Psi += Y^T Ut,
 // Z <- e^{g_C} Z - W^T Y. A skipped chunk (SparseGDN: the state only decays) is Z <- e^{g_C} Z.
+// Each iteration takes NH chunks (c, c - 1, ...); half h of the workgroup solves chunk c - h in
+// LDS slot h (a half with no chunk, or a skipped one, runs through the same barriers on whatever
+// its slot holds, and nothing reads the result).
+template <int D, class E>
+constexpr size_t map_lds() {
+    return MapCfg<D, E>::NH * ((Lds<D, E, false>::BYTES + 255) / 256 * 256);
+}
+
 template <int D, class E>
 __global__ __launch_bounds__(512) void map_kernel(PrefArgs a) {
-    using C = Cfg<D, E, false>;
+    using MC = MapCfg<D, E>;
+    using C = Cfg<D, E, MC::NWS>;    // the state's distribution over the waves
+    using CP = Cfg<D, E, MC::NWP>;   // the solve's, within a half
     using L = Lds<D, E, false>;
     using M = MM<E>;
     using T = typename E::T;
     using frag = typename M::frag;
     constexpr int KB = C::KB, NKD = C::NKD, NKT = C::NKT, NDT = C::NDT, VPW = C::VPW, KP = C::KP, AS = C::AS;
+    constexpr int NH = MC::NH;
+    constexpr size_t SLOT = (L::BYTES + 255) / 256 * 256;
     extern __shared__ __align__(16) unsigned char smem[];
     const int b = blockIdx.x, bh = blockIdx.y;
-    const int tid = threadIdx.x, lane = tid & 63, j = lane >> 4, m = lane & 15;
-    const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int lane0 = threadIdx.x & 63, j0 = lane0 >> 4, m0 = lane0 & 15;
+    const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int half = NH == 2 ? w / 4 : 0, hw = NH == 2 ? w % 4 : w;   // scalars
     const int c0 = b * a.m, c1 = min(a.nch, c0 + a.m);   // chunks [c0, c1), processed last to first
-    T* Kr = reinterpret_cast<T*>(smem + L::O_K);
-    const float* Tm = reinterpret_cast<const float*>(smem + L::O_T);
-    Gates* gt = reinterpret_cast<Gates*>(smem + L::O_G);
+    unsigned char* my = smem + (size_t)half * SLOT;      // this half's slot
 
     f32x4 Z[VPW][NDT], Psi[VPW][NDT];
 #pragma unroll
@@ -511,40 +538,42 @@ __global__ __launch_bounds__(512) void map_kernel(PrefArgs a) {
         for (int lt = 0; lt < NDT; ++lt) {
             Psi[t][lt] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-            for (int e = 0; e < 4; ++e) Z[t][lt][e] = (16 * lt + 4 * j + e == 16 * (VPW * w + t) + m) ? 1.f : 0.f;
+            for (int e = 0; e < 4; ++e) Z[t][lt][e] = (16 * lt + 4 * j0 + e == 16 * (VPW * w + t) + m0) ? 1.f : 0.f;
         }
 
-    Fetch<D, E, false> fx;
-    unsigned keep = keep_chunk(a, bh, c1 - 1);
-    fx.issue(a, bh, c1 - 1, keep, tid, w);
-    for (int c = c1 - 1; c >= c0; --c) {
-        const int tid = 64 * w + opaque(threadIdx.x & 63), lane = tid & 63, j = lane >> 4, m = lane & 15;
-        if (keep) {
-            fx.rk.store(Kr, fx.n, tid);
+    Fetch<D, E, false, MC::NWP> fx;
+    unsigned keep = 0;
+    if (c1 - 1 - half >= c0) {
+        keep = keep_chunk(a, bh, c1 - 1 - half);
+        fx.issue(a, bh, c1 - 1 - half, keep, 64 * hw + lane0, hw);
+    }
+    for (int c = c1 - 1; c >= c0; c -= NH) {
+        const int lane = opaque(threadIdx.x & 63), j = lane >> 4, m = lane & 15, htid = 64 * hw + lane;
+        const int mine = c - half;                     // this half's chunk (scalar)
+        T* Kr = reinterpret_cast<T*>(my + L::O_K);
+        Gates* gt = reinterpret_cast<Gates*>(my + L::O_G);
+        if (mine >= c0) {
+            if (keep) fx.rk.store(Kr, fx.n, htid);
+            if (hw == 0) gate_scan(gt, fx.la, fx.bt, lane);
         }
-        if (w == 0) gate_scan(gt, fx.la, fx.bt, lane);
         lds_sync();
-        const unsigned keep_c = keep;
-        const float dec = gt->dec;
-        if (!keep_c) {
+        // the iteration's chunks and whether each updates the state (scalars, the same in every wave)
+        unsigned kp[NH];
+        bool any = false;
 #pragma unroll
-            for (int t = 0; t < VPW; ++t)
-#pragma unroll
-                for (int lt = 0; lt < NDT; ++lt) Z[t][lt] = scale4(Z[t][lt], dec);
-            if (c > c0) {
-                keep = keep_chunk(a, bh, c - 1);
-                fx.issue(a, bh, c - 1, keep, tid, w);
-            }
-            lds_sync();
-            continue;
+        for (int p = 0; p < NH; ++p) {
+            kp[p] = c - p >= c0 ? keep_chunk(a, bh, c - p) : 0u;
+            any = any || kp[p];
         }
-        frag kbe[VPW][NKT], vb[VPW][NKT];
-        intra_solve<D, E, false>(smem, a.band, w, lane, fx.vf, kbe, vb);
-        // -W (token tiles x this wave's d tiles) and Ut (x this wave's value tiles), then the
-        // fragments the chain step reads: -W^T [dt][kt] (A: rows d, k = token) and Ut [kt][vt]
-        // (B: k = token, columns v)
-        {
-            f32x4 wn[VPW][4], ua[VPW][4];
+        if (any) {
+            frag kbe[CP::VPW][NKT], vb[CP::VPW][NKT];
+            intra_solve<D, E, false, MC::NWP>(my, a.band, hw, lane, fx.vf, kbe, vb);
+            // -W (token tiles x this wave's d tiles) and Ut (x its value tiles) of the half's
+            // chunk, then the fragments the state step reads: -W^T [dt][kt] (A: rows d, k = token)
+            // and Ut [kt][vt] (B: k = token, columns v). A (in the V-row space) was last read
+            // before intra_solve's final barrier.
+            const float* Tm = reinterpret_cast<const float*>(my + L::O_T);
+            f32x4 wn[CP::VPW][4], ua[CP::VPW][4];
 #pragma unroll
             for (int rt = 0; rt < 4; ++rt) {
                 frag Tf[NKT];
@@ -552,7 +581,7 @@ __global__ __launch_bounds__(512) void map_kernel(PrefArgs a) {
                 for (int kt = 0; kt < NKT; ++kt)
                     if (kt <= C::kbmax(rt)) Tf[kt] = row_frag_f32<E>(Tm + (16 * rt + m) * AS, kt * KB, j);
 #pragma unroll
-                for (int t = 0; t < VPW; ++t) {
+                for (int t = 0; t < CP::VPW; ++t) {
                     wn[t][rt] = f32x4{0.f, 0.f, 0.f, 0.f};
                     ua[t][rt] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
@@ -563,73 +592,87 @@ __global__ __launch_bounds__(512) void map_kernel(PrefArgs a) {
                         }
                 }
             }
-            // A (in the V-row space) was last read before intra_solve's final barrier
 #pragma unroll
-            for (int t = 0; t < VPW; ++t)
+            for (int t = 0; t < CP::VPW; ++t)
 #pragma unroll
                 for (int kt = 0; kt < NKT; ++kt) {
-                    const int dt = VPW * w + t;
-                    st_frag(smem + L::O_V + (size_t)(dt * NKT + kt) * C::FR, lane, M::from_acc(wn[t], kt));
-                    st_frag(smem + L::O_UT + (size_t)(kt * NDT + dt) * C::FR, lane, M::from_acc(ua[t], kt));
+                    const int dt = CP::VPW * hw + t;
+                    st_frag(my + L::O_V + (size_t)(dt * NKT + kt) * C::FR, lane, M::from_acc(wn[t], kt));
+                    st_frag(my + L::O_UT + (size_t)(kt * NDT + dt) * C::FR, lane, M::from_acc(ua[t], kt));
                 }
         }
         lds_sync();
-        // the previous chunk's rows and gates load while this one's step runs
-        if (c > c0) {
-            keep = keep_chunk(a, bh, c - 1);
-            fx.issue(a, bh, c - 1, keep, tid, w);
+        // the next iteration's rows and gates load while this one's state steps run
+        if (mine - NH >= c0) {
+            keep = keep_chunk(a, bh, mine - NH);
+            fx.issue(a, bh, mine - NH, keep, htid, hw);
         }
-        // Y = Khat Z
-        f32x4 Y[VPW][4];
 #pragma unroll
-        for (int t = 0; t < VPW; ++t)
+        for (int p = 0; p < NH; ++p) {
+            if (c - p < c0) break;   // scalar
+            const unsigned char* sl = smem + (size_t)p * SLOT;
+            const T* Ks = reinterpret_cast<const T*>(sl + L::O_K);
+            const Gates* gs = reinterpret_cast<const Gates*>(sl + L::O_G);
+            const float dec = gs->dec;
+            if (!kp[p]) {
 #pragma unroll
-            for (int rt = 0; rt < 4; ++rt) Y[t][rt] = f32x4{0.f, 0.f, 0.f, 0.f};
+                for (int t = 0; t < VPW; ++t)
 #pragma unroll
-        for (int kd = 0; kd < NKD; ++kd) {
-            frag zh[VPW], zl[VPW];
-#pragma unroll
-            for (int t = 0; t < VPW; ++t) {
-                zh[t] = M::from_acc(Z[t], kd);
-                if constexpr (C::NSPLIT == 2) zl[t] = lo_from_acc<E>(Z[t], kd);
+                    for (int lt = 0; lt < NDT; ++lt) Z[t][lt] = scale4(Z[t][lt], dec);
+                continue;
             }
+            // Y = Khat Z
+            f32x4 Y[VPW][4];
 #pragma unroll
-            for (int rt = 0; rt < 4; ++rt) {
-                const frag kf = row_frag<E>(Kr + (16 * rt + m) * KP, kd * KB, j, gt->kh[16 * rt + m]);
+            for (int t = 0; t < VPW; ++t)
+#pragma unroll
+                for (int rt = 0; rt < 4; ++rt) Y[t][rt] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int kd = 0; kd < NKD; ++kd) {
+                frag zh[VPW], zl[VPW];
 #pragma unroll
                 for (int t = 0; t < VPW; ++t) {
-                    Y[t][rt] = M::mma(kf, zh[t], Y[t][rt]);
-                    if constexpr (C::NSPLIT == 2) Y[t][rt] = M::mma(kf, zl[t], Y[t][rt]);
+                    zh[t] = M::from_acc(Z[t], kd);
+                    if constexpr (C::NSPLIT == 2) zl[t] = lo_from_acc<E>(Z[t], kd);
+                }
+#pragma unroll
+                for (int rt = 0; rt < 4; ++rt) {
+                    const frag kf = row_frag<E>(Ks + (16 * rt + m) * KP, kd * KB, j, gs->kh[16 * rt + m]);
+#pragma unroll
+                    for (int t = 0; t < VPW; ++t) {
+                        Y[t][rt] = M::mma(kf, zh[t], Y[t][rt]);
+                        if constexpr (C::NSPLIT == 2) Y[t][rt] = M::mma(kf, zl[t], Y[t][rt]);
+                    }
+                }
+            }
+            frag Yf[VPW][NKT];
+#pragma unroll
+            for (int t = 0; t < VPW; ++t)
+#pragma unroll
+                for (int kt = 0; kt < NKT; ++kt) Yf[t][kt] = M::from_acc(Y[t], kt);
+            // Psi += Y^T Ut
+#pragma unroll
+            for (int vt = 0; vt < NDT; ++vt)
+#pragma unroll
+                for (int kt = 0; kt < NKT; ++kt) {
+                    const frag uf = ld_frag<frag>(sl + L::O_UT + (size_t)(kt * NDT + vt) * C::FR, lane);
+#pragma unroll
+                    for (int t = 0; t < VPW; ++t) Psi[t][vt] = M::mma(Yf[t][kt], uf, Psi[t][vt]);
+                }
+            // Z <- e^{g_C} Z - W^T Y
+#pragma unroll
+            for (int lt = 0; lt < NDT; ++lt) {
+#pragma unroll
+                for (int t = 0; t < VPW; ++t) Z[t][lt] = scale4(Z[t][lt], dec);
+#pragma unroll
+                for (int kt = 0; kt < NKT; ++kt) {
+                    const frag wf = ld_frag<frag>(sl + L::O_V + (size_t)(lt * NKT + kt) * C::FR, lane);
+#pragma unroll
+                    for (int t = 0; t < VPW; ++t) Z[t][lt] = M::mma(wf, Yf[t][kt], Z[t][lt]);
                 }
             }
         }
-        frag Yf[VPW][NKT];
-#pragma unroll
-        for (int t = 0; t < VPW; ++t)
-#pragma unroll
-            for (int kt = 0; kt < NKT; ++kt) Yf[t][kt] = M::from_acc(Y[t], kt);
-        // Psi += Y^T Ut
-#pragma unroll
-        for (int vt = 0; vt < NDT; ++vt)
-#pragma unroll
-            for (int kt = 0; kt < NKT; ++kt) {
-                const frag uf = ld_frag<frag>(smem + L::O_UT + (size_t)(kt * NDT + vt) * C::FR, lane);
-#pragma unroll
-                for (int t = 0; t < VPW; ++t) Psi[t][vt] = M::mma(Yf[t][kt], uf, Psi[t][vt]);
-            }
-        // Z <- e^{g_C} Z - W^T Y
-#pragma unroll
-        for (int lt = 0; lt < NDT; ++lt) {
-#pragma unroll
-            for (int t = 0; t < VPW; ++t) Z[t][lt] = scale4(Z[t][lt], dec);
-#pragma unroll
-            for (int kt = 0; kt < NKT; ++kt) {
-                const frag wf = ld_frag<frag>(smem + L::O_V + (size_t)(lt * NKT + kt) * C::FR, lane);
-#pragma unroll
-                for (int t = 0; t < VPW; ++t) Z[t][lt] = M::mma(wf, Yf[t][kt], Z[t][lt]);
-            }
-        }
-        lds_sync();   // the chunk's LDS is free for the next one
+        lds_sync();   // the slots are free for the next chunks
     }
     // Phi = Z^T as A operands (rows i = this wave's columns of Z, k = l) and Psi as tiles
     unsigned char* phi = ws_phi<D, E>(a, bh, b);
@@ -639,11 +682,11 @@ __global__ __launch_bounds__(512) void map_kernel(PrefArgs a) {
         const int it = VPW * w + t;
 #pragma unroll
         for (int kd = 0; kd < NKD; ++kd) {
-            st_frag(phi + ((size_t)(it * NKD + kd) * C::NSPLIT) * C::FR, lane, M::from_acc(Z[t], kd));
-            if constexpr (C::NSPLIT == 2) st_frag(phi + ((size_t)(it * NKD + kd) * 2 + 1) * C::FR, lane, lo_from_acc<E>(Z[t], kd));
+            st_frag(phi + ((size_t)(it * NKD + kd) * C::NSPLIT) * C::FR, lane0, M::from_acc(Z[t], kd));
+            if constexpr (C::NSPLIT == 2) st_frag(phi + ((size_t)(it * NKD + kd) * 2 + 1) * C::FR, lane0, lo_from_acc<E>(Z[t], kd));
         }
 #pragma unroll
-        for (int vt = 0; vt < NDT; ++vt) psi[(it * NDT + vt) * 64 + lane] = Psi[t][vt];
+        for (int vt = 0; vt < NDT; ++vt) psi[(it * NDT + vt) * 64 + lane0] = Psi[t][vt];
     }
 }
 
@@ -728,7 +771,7 @@ __global__ __launch_bounds__(256) void scan_kernel(PrefArgs a) {
 // (a skipped chunk's update leaves the decayed state; its outputs still use U).
 template <int D, class E>
 __global__ __launch_bounds__(512) void out_kernel(PrefArgs a) {
-    using C = Cfg<D, E, true>;
+    using C = Cfg<D, E, out_waves<D, E>()>;
     using L = Lds<D, E, true>;
     using M = MM<E>;
     using T = typename E::T;
@@ -762,7 +805,7 @@ __global__ __launch_bounds__(512) void out_kernel(PrefArgs a) {
         }
     }
 
-    Fetch<D, E, true> fx;
+    Fetch<D, E, true, C::NW> fx;
     fx.issue(a, bh, c0, true, tid, w);
     for (int c = c0; c < c1; ++c) {
         const int tid = 64 * w + opaque(threadIdx.x & 63), lane = tid & 63, j = lane >> 4, m = lane & 15;
@@ -773,7 +816,7 @@ __global__ __launch_bounds__(512) void out_kernel(PrefArgs a) {
         lds_sync();
         const unsigned keep = keep_chunk(a, bh, c);
         frag kbe[VPW][NKT], vb[VPW][NKT];
-        intra_solve<D, E, true>(smem, a.band, w, lane, fx.vf, kbe, vb);
+        intra_solve<D, E, true, C::NW>(smem, a.band, w, lane, fx.vf, kbe, vb);
         // -W fragments [rt][kd] (A: rows token, k = d), each d tile filling its part, and Ut
         f32x4 U[VPW][4];
         {
@@ -934,19 +977,19 @@ struct Launch {
     static bool attributes() {
         static const bool ok =
             hipFuncSetAttribute(reinterpret_cast<const void*>(&map_kernel<D, E>), hipFuncAttributeMaxDynamicSharedMemorySize,
-                                (int)Lds<D, E, false>::BYTES) == hipSuccess &&
+                                (int)map_lds<D, E>()) == hipSuccess &&
             hipFuncSetAttribute(reinterpret_cast<const void*>(&out_kernel<D, E>), hipFuncAttributeMaxDynamicSharedMemorySize,
                                 (int)Lds<D, E, true>::BYTES) == hipSuccess;
         return ok;
     }
     static int run(const PrefArgs& a, hipStream_t s) {
         if (!attributes()) return -1;
-        constexpr size_t lds_map = Lds<D, E, false>::BYTES, lds_out = Lds<D, E, true>::BYTES;
+        constexpr size_t lds_map = map_lds<D, E>(), lds_out = Lds<D, E, true>::BYTES;
         if (a.NB > 1) {
-            hipLaunchKernelGGL((map_kernel<D, E>), dim3(a.NB - 1, a.BH), dim3(Cfg<D, E, false>::NT), lds_map, s, a);
+            hipLaunchKernelGGL((map_kernel<D, E>), dim3(a.NB - 1, a.BH), dim3(64 * MapCfg<D, E>::NWS), lds_map, s, a);
             hipLaunchKernelGGL((scan_kernel<D, E>), dim3(D / 16, a.BH), dim3(256), 0, s, a);
         }
-        hipLaunchKernelGGL((out_kernel<D, E>), dim3(a.NB, a.BH), dim3(Cfg<D, E, true>::NT), lds_out, s, a);
+        hipLaunchKernelGGL((out_kernel<D, E>), dim3(a.NB, a.BH), dim3(64 * out_waves<D, E>()), lds_out, s, a);
         return hipGetLastError() == hipSuccess ? 0 : -1;
     }
 };
