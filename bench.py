@@ -63,6 +63,11 @@ def gdn_flops_per_chunk(C=64, d=128):
             + C * (C + 1) * d + C ** 3 / 3)
 
 
+def gdn_dense_tile_flops_per_chunk(C=64, d=128):
+    """The same products on whole 64 x 64 tiles (what MFMA tiles execute at the least)."""
+    return 6 * C * d * d + 10 * C * C * d + C ** 3 / 3
+
+
 def linattn_flops_per_chunk(C=64, d=128):
     return 4 * C * d * d + 2 * C * (C + 1) * d
 
@@ -130,14 +135,14 @@ def time_loop(torch, fn, steps, warmup):
 # components
 # ---------------------------------------------------------------------------------------------
 def bench_prefill(torch, ops, cfg, steps, warmup, gdn=True, verbose=False, variant=None, keep_rate=0.29,
-                  one_segment=False):
+                  kernel_times=False):
     """variant None: gdn_prefill_fwd (gdn) or plain linattn_prefill_fwd; "gla": linattn_prefill_fwd with
     per-token gates; "gla_vec": gla_prefill_fwd with a gate per token and key dimension; "skip":
     gdn_prefill_skip_fwd with a seeded keep mask at keep_rate; "band1":
-    gdn_prefill_banded_fwd with band 1 (flops counted as for the exact rule). one_segment: hand over a
-    workspace for the whole sequence, so that the call runs its three kernels once each on one stream
-    (the launch that hardware-counter passes use: they serialise dispatches, which the multi-stream
-    segment pipeline's value waits do not allow)."""
+    gdn_prefill_banded_fwd with band 1 (flops counted as for the exact rule). kernel_times (gated
+    delta rule only): after the timed loop, time `steps` more calls with the library's per-kernel HIP
+    events (recorded on the call's stream around each of its kernels) and report each kernel's
+    average launch duration."""
     gates = gdn or variant == "gla"
     q, k, v, beta, la, h0 = prefill_device_inputs(torch, cfg, gates=gates, verbose=verbose)
     if variant == "gla_vec":
@@ -149,8 +154,6 @@ def bench_prefill(torch, ops, cfg, steps, warmup, gdn=True, verbose=False, varia
         wsb = ops.gla_prefill_workspace_size(cfg.B, cfg.H, cfg.L, cfg.Dk, q.dtype)
     elif not gates or variant == "gla":   # linear attention: blocks of chunks
         wsb = ops.linattn_prefill_workspace_size(cfg.B, cfg.H, cfg.L, cfg.Dk, q.dtype)
-    elif one_segment:
-        wsb = ops.prefill_workspace_size(1, 1, 64, cfg.Dk, q.dtype) * cfg.B * cfg.H * nchk
     else:
         wsb = ops.prefill_workspace_size(cfg.B, cfg.H, cfg.L, cfg.Dk, q.dtype)
     ws = torch.empty(wsb, dtype=torch.uint8, device="cuda")
@@ -172,6 +175,18 @@ def bench_prefill(torch, ops, cfg, steps, warmup, gdn=True, verbose=False, varia
     else:
         fn = lambda: ops.linattn_prefill_fwd(q, k, v, h0, o=o, h_final=hf, workspace=ws)
     ms, wall = time_loop(torch, fn, steps, warmup)
+    kern = None
+    if kernel_times and gdn:
+        ops.gdn_prefill_kernel_times()            # clear
+        ops.gdn_prefill_timing(True)
+        try:
+            for _ in range(steps):
+                fn()
+            torch.cuda.synchronize()
+        finally:
+            ops.gdn_prefill_timing(False)
+        kt = ops.gdn_prefill_kernel_times()
+        kern = {n: {"launches": x["launches"], "ms_avg": x["ms"] / x["launches"]} for n, x in kt.items() if x["launches"]}
     if gdn:
         # a skipped chunk saves its state write, Khat^T U (2 C d_k d_v flop)
         flops = nchunk * gdn_flops_per_chunk(64, cfg.Dk) - (nchunk - kept) * 2 * 64 * cfg.Dk * cfg.Dv
@@ -180,13 +195,18 @@ def bench_prefill(torch, ops, cfg, steps, warmup, gdn=True, verbose=False, varia
     nbytes = prefill_bytes(cfg, gates=gdn) + cfg.B * cfg.H * cfg.L * 4 * {"gla": 1, "gla_vec": cfg.Dk}.get(variant, 0)
     nbytes += nchunk if variant == "skip" else 0
     res = {
-        "workload": cfg.name + ({"gla": "_gated", "gla_vec": "_gated_per_dim", "skip": f"_skip_keep{keep_rate}",
+        "workload": cfg.name + ("_long_memory_gates" if gdn and cfg.gate_dist == "long" else "")
+        + ({"gla": "_gated", "gla_vec": "_gated_per_dim", "skip": f"_skip_keep{keep_rate}",
                                  "band1": "_banded1"}.get(variant, "")),
         "ms": ms, "tokens_per_s": cfg.B * cfg.L / (ms * 1e-3),
         "alg_tflops": flops / (ms * 1e-3) / 1e12, "mfma_frac": flops / (ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS,
         "alg_bytes": nbytes, "hbm_GBps": nbytes / (ms * 1e-3) / 1e9,
         "hbm_frac": nbytes / (ms * 1e-3) / 1e9 / PEAK_HBM_GBPS, "wall_s": wall,
     }
+    if gdn:
+        res["dense_tile_tflops"] = nchunk * gdn_dense_tile_flops_per_chunk(64, cfg.Dk) / (ms * 1e-3) / 1e12
+    if kern is not None:
+        res["kernels"] = kern
     if variant == "skip":
         res["kept_fraction"] = kept / nchunk
     return res, (q, k, v, beta, la, h0, o, hf)
@@ -278,8 +298,9 @@ def main():
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--profile-steps", type=int, default=0,
                     help="only run this many prefill steps after warm-up (for profilers), no JSON")
-    ap.add_argument("--one-segment", action="store_true",
-                    help="with --profile-steps: whole-sequence workspace, one launch of each kernel per call")
+    ap.add_argument("--gate-dist", default="config", choices=("config", "long"),
+                    help="with --profile-steps: the log-gate distribution (config: -softplus(N(0,1)+2); "
+                         "long: -U(0, 0.01), a long memory)")
     ap.add_argument("--profile-decode", type=int, default=0,
                     help="only run this many decode steps (for profilers), no JSON")
     ap.add_argument("--profile-linattn", type=int, default=0,
@@ -339,14 +360,16 @@ def main():
         return
     if args.profile_steps:
         log("generating inputs")
-        res, bufs = bench_prefill(torch, ops, cfg, args.profile_steps, args.warmup, verbose=True,
-                                  one_segment=args.one_segment)
-        log(f"profiled {args.profile_steps} steps: {res['ms']:.3f} ms/step")
+        res, bufs = bench_prefill(torch, ops, cfg.with_(gate_dist=args.gate_dist), args.profile_steps, args.warmup,
+                                  verbose=True, kernel_times=True)
+        log(f"profiled {args.profile_steps} steps: {res['ms']:.3f} ms/step; kernels (HIP events): "
+            + ", ".join(f"{n} {x['ms_avg']:.4f} ms" for n, x in res["kernels"].items()))
         return
 
     log(f"[bench] {cfg.name}: generating inputs")
-    res, bufs = bench_prefill(torch, ops, cfg, args.steps, args.warmup)
-    log(f"[bench] {cfg.name}: {res['ms']:.3f} ms/step, {res['tokens_per_s']:.3e} tokens/s")
+    res, bufs = bench_prefill(torch, ops, cfg, args.steps, args.warmup, kernel_times=True)
+    log(f"[bench] {cfg.name}: {res['ms']:.3f} ms/step, {res['tokens_per_s']:.3e} tokens/s; kernels: "
+        + ", ".join(f"{n} {x['ms_avg']:.4f} ms" for n, x in res["kernels"].items()))
     gpu_o = bufs[6]
 
     components = {}
@@ -375,6 +398,10 @@ def main():
         r, b = bench_prefill(torch, ops, inputs.LINATTN_8K.with_(gate_dist="config"), max(5, args.steps // 2), 2,
                              gdn=False, variant="gla_vec")
         components["linattn_gated_per_dim"] = r
+        del b
+        log("[bench] gdn 128K with long-memory gates")
+        r, b = bench_prefill(torch, ops, cfg.with_(gate_dist="long"), max(5, args.steps // 2), 2, kernel_times=True)
+        components["gdn_128k_long_memory"] = r
         del b
         log("[bench] gdn 128K with skipped chunk updates (29% kept)")
         r, b = bench_prefill(torch, ops, cfg, max(5, args.steps // 2), 2, variant="skip")

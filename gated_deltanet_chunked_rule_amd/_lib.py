@@ -27,6 +27,8 @@ SIGNATURES = {
     "gla_prefill_fwd": (_i, [_vp, _vp, _vp, _fp, _fp, _vp, _fp, _i, _i, _i, _i, _i, _i, _vp, _sz, _vp]),
     "gla_prefill_workspace_size": (_sz, [_i, _i, _i, _i, _i, _i]),
     "linattn_bidir_workspace_size": (_sz, [_i, _i, _i, _i, _i, _i]),
+    "gdn_prefill_timing": (_i, [_i]),
+    "gdn_prefill_kernel_times": (_i, [_vp, _vp]),
     "linattn_bidir_fwd": (_i, [_vp, _vp, _vp, _vp, _fp, _i, _i, _i, _i, _i, _i, _i, _vp, _sz, _vp]),
 }
 

@@ -109,6 +109,15 @@ int prefill(const void* q, const void* k, const void* v, const float* beta, cons
 
 extern "C" {
 
+int gdn_prefill_timing(int enable) {
+    gdn::prefill_timing(enable != 0);
+    return GDN_OK;
+}
+
+int gdn_prefill_kernel_times(float* ms, int* launches) {
+    return gdn::prefill_kernel_times(ms, launches) == 0 ? GDN_OK : GDN_ERR_LAUNCH;
+}
+
 const char* gdn_status_string(int status) {
     switch (status) {
         case GDN_OK: return "GDN_OK";

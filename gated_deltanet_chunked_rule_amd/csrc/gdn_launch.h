@@ -18,6 +18,12 @@ int launch_prefill(const void* q, const void* k, const void* v, const float* bet
                    const unsigned char* keep, const float* h0, void* o, float* h_final, int BH, long L, int D,
                    int dtype, int band, void* ws, size_t ws_bytes, hipStream_t stream);
 
+// Per-kernel timing of launch_prefill: when on, HIP events bracket each launch on its stream.
+// prefill_kernel_times waits for them and returns summed ms and launch counts per stage (block
+// maps, pass over blocks, outputs), then clears the record.
+void prefill_timing(bool enable);
+int prefill_kernel_times(float* ms, int* launches);
+
 // Causal linear attention, plain (log_alpha NULL) or with a per-token decay, block-parallel.
 // The workspace holds each block's state tiles (one block per slice at the minimum; a smaller
 // workspace means fewer, longer blocks).

@@ -37,6 +37,11 @@
 // then cannot be differenced, so each token also carries the index of the last zero gate at or
 // before it: exp(g_r - g_s) is taken over the finite gates only, and is zero when a zero gate
 // lies in (s, r]. Only exponentials of non-positive differences are formed.
+#include <atomic>
+#include <mutex>
+#include <utility>
+#include <vector>
+
 #include "gdn_launch.h"
 #include "gdn_rows.h"
 
@@ -530,6 +535,7 @@ __global__ __launch_bounds__(512) void map_kernel(PrefArgs a) {
     const int half = NH == 2 ? w / 4 : 0, hw = NH == 2 ? w % 4 : w;   // scalars
     const int c0 = b * a.m, c1 = min(a.nch, c0 + a.m);   // chunks [c0, c1), processed last to first
     unsigned char* my = smem + (size_t)half * SLOT;      // this half's slot
+    __shared__ unsigned zf[MC::NWS];                     // per wave: its columns of Z are all zero
 
     f32x4 Z[VPW][NDT], Psi[VPW][NDT];
 #pragma unroll
@@ -672,7 +678,24 @@ __global__ __launch_bounds__(512) void map_kernel(PrefArgs a) {
                 }
             }
         }
+        // Once every column of Z is exactly zero the earlier chunks cannot change Phi or Psi
+        // (each of their steps multiplies Z), so the block's map is complete. With strong decay
+        // this happens after a chunk or two: the product of a chunk's gates falls below fp32's
+        // smallest subnormal.
+        unsigned nz = 0;
+#pragma unroll
+        for (int t = 0; t < VPW; ++t)
+#pragma unroll
+            for (int lt = 0; lt < NDT; ++lt)
+#pragma unroll
+                for (int e = 0; e < 4; ++e) nz |= __float_as_uint(Z[t][lt][e]) & 0x7fffffffu;
+        const bool wzero = __builtin_amdgcn_ballot_w64(nz != 0u) == 0;
+        if (lane0 == 0) zf[w] = wzero ? 1u : 0u;
         lds_sync();   // the slots are free for the next chunks
+        unsigned done = 1u;
+#pragma unroll
+        for (int i = 0; i < MC::NWS; ++i) done &= zf[i];
+        if (__builtin_amdgcn_readfirstlane(done)) break;   // the same decision in every wave
     }
     // Phi = Z^T as A operands (rows i = this wave's columns of Z, k = l) and Psi as tiles
     unsigned char* phi = ws_phi<D, E>(a, bh, b);
@@ -972,6 +995,73 @@ size_t prefill_workspace_bytes(long BH, long L, int D, int /*dtype*/) {
 // no workspace is needed: the whole sequence then runs as one block per slice
 size_t prefill_workspace_min_bytes(long, long, int, int) { return 0; }
 
+// Optional per-kernel timing: HIP events recorded around each launch on the caller's stream.
+namespace {
+struct StageTimer {
+    std::mutex mu;
+    std::atomic<bool> on{false};
+    std::vector<hipEvent_t> pool;
+    std::vector<std::pair<int, std::pair<hipEvent_t, hipEvent_t>>> rec;   // (stage, (begin, end))
+    hipEvent_t get() {
+        if (!pool.empty()) {
+            hipEvent_t e = pool.back();
+            pool.pop_back();
+            return e;
+        }
+        hipEvent_t e = nullptr;
+        return hipEventCreate(&e) == hipSuccess ? e : nullptr;
+    }
+};
+StageTimer& timer() {
+    static StageTimer t;
+    return t;
+}
+// launches one kernel through f(), bracketed by events when timing is on; true if the launch
+// was accepted
+template <class F>
+bool timed(int stage, hipStream_t s, F&& f) {
+    StageTimer& t = timer();
+    if (!t.on.load(std::memory_order_relaxed)) {
+        f();
+        return hipGetLastError() == hipSuccess;
+    }
+    std::lock_guard<std::mutex> g(t.mu);
+    hipEvent_t e0 = t.get(), e1 = t.get();
+    if (e0) hipEventRecord(e0, s);
+    f();
+    const bool ok = hipGetLastError() == hipSuccess;
+    if (e1) hipEventRecord(e1, s);
+    if (e0 && e1) t.rec.push_back({stage, {e0, e1}});
+    return ok;
+}
+}  // namespace
+
+void prefill_timing(bool enable) { timer().on.store(enable); }
+
+int prefill_kernel_times(float* ms, int* launches) {
+    StageTimer& t = timer();
+    std::lock_guard<std::mutex> g(t.mu);
+    float sum[3] = {0.f, 0.f, 0.f};
+    int cnt[3] = {0, 0, 0};
+    bool ok = true;
+    for (auto& r : t.rec) {
+        float x = 0.f;
+        if (hipEventSynchronize(r.second.second) != hipSuccess ||
+            hipEventElapsedTime(&x, r.second.first, r.second.second) != hipSuccess)
+            ok = false;
+        sum[r.first] += x;
+        cnt[r.first] += 1;
+        t.pool.push_back(r.second.first);
+        t.pool.push_back(r.second.second);
+    }
+    t.rec.clear();
+    for (int i = 0; i < 3; ++i) {
+        if (ms) ms[i] = sum[i];
+        if (launches) launches[i] = cnt[i];
+    }
+    return ok ? 0 : -1;
+}
+
 template <int D, class E>
 struct Launch {
     static bool attributes() {
@@ -986,11 +1076,20 @@ struct Launch {
         if (!attributes()) return -1;
         constexpr size_t lds_map = map_lds<D, E>(), lds_out = Lds<D, E, true>::BYTES;
         if (a.NB > 1) {
-            hipLaunchKernelGGL((map_kernel<D, E>), dim3(a.NB - 1, a.BH), dim3(64 * MapCfg<D, E>::NWS), lds_map, s, a);
-            hipLaunchKernelGGL((scan_kernel<D, E>), dim3(D / 16, a.BH), dim3(256), 0, s, a);
+            if (!timed(0, s, [&] {
+                    hipLaunchKernelGGL((map_kernel<D, E>), dim3(a.NB - 1, a.BH), dim3(64 * MapCfg<D, E>::NWS), lds_map,
+                                       s, a);
+                }))
+                return -1;
+            if (!timed(1, s, [&] { hipLaunchKernelGGL((scan_kernel<D, E>), dim3(D / 16, a.BH), dim3(256), 0, s, a); }))
+                return -1;
         }
-        hipLaunchKernelGGL((out_kernel<D, E>), dim3(a.NB, a.BH), dim3(64 * out_waves<D, E>()), lds_out, s, a);
-        return hipGetLastError() == hipSuccess ? 0 : -1;
+        return timed(2, s, [&] {
+                   hipLaunchKernelGGL((out_kernel<D, E>), dim3(a.NB, a.BH), dim3(64 * out_waves<D, E>()), lds_out, s,
+                                      a);
+               })
+                   ? 0
+                   : -1;
     }
 };
 

@@ -53,6 +53,22 @@ def prefill_workspace_size(B: int, H: int, L: int, D: int, dtype: torch.dtype) -
     return int(_lib.load().gdn_prefill_workspace_size(B, H, L, D, D, _code(dtype)))
 
 
+def gdn_prefill_timing(enable: bool) -> None:
+    """Turn per-kernel HIP-event timing of the gated delta-rule prefill calls on or off."""
+    _lib.check(_lib.load().gdn_prefill_timing(1 if enable else 0), "gdn_prefill_timing")
+
+
+def gdn_prefill_kernel_times() -> dict:
+    """Summed ms and launch counts of the block-map, block-pass and output kernels since the last
+    query (waits for the recorded events, then clears them)."""
+    import ctypes
+    ms = (ctypes.c_float * 3)()
+    n = (ctypes.c_int * 3)()
+    _lib.check(_lib.load().gdn_prefill_kernel_times(ctypes.addressof(ms), ctypes.addressof(n)),
+               "gdn_prefill_kernel_times")
+    return {name: {"ms": float(ms[i]), "launches": int(n[i])} for i, name in enumerate(("map", "scan", "out"))}
+
+
 def linattn_prefill_workspace_size(B: int, H: int, L: int, D: int, dtype: torch.dtype) -> int:
     return int(_lib.load().linattn_prefill_workspace_size(B, H, L, D, D, _code(dtype)))
 

@@ -75,6 +75,18 @@ const char *gdn_status_string(int status);
  * through rounding. Returns 0 for an unsupported shape or L = 0. */
 size_t gdn_prefill_workspace_size(int B, int H, int L, int Dk, int Dv, int dtype);
 
+/* Per-kernel timing of the gated delta-rule prefill, for benchmarks. After
+ * gdn_prefill_timing(1), every gdn_prefill_fwd, gdn_prefill_skip_fwd and gdn_prefill_banded_fwd
+ * call records a HIP event before and after each of its kernels on the caller's stream, until
+ * gdn_prefill_timing(0). gdn_prefill_kernel_times waits for the recorded events, writes the
+ * summed milliseconds of the block-map, block-pass and output kernels to ms[0..2] and their
+ * launch counts to launches[0..2] (either pointer may be NULL), and clears the record. The
+ * events are host objects the library keeps in a pool until the process ends (no device
+ * memory). Returns GDN_OK, or GDN_ERR_LAUNCH if an event could not be read (its time then
+ * counts as 0). Timing is process-wide state: calls from several host threads share it. */
+int gdn_prefill_timing(int enable);
+int gdn_prefill_kernel_times(float *ms, int *launches);
+
 /*
  * Chunked prefill of the gated delta rule.
  *   q, k        [B,H,L,Dk] dtype        v, o   [B,H,L,Dv] dtype   (may be NULL when L = 0)

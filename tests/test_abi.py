@@ -38,6 +38,18 @@ def test_status_strings(lib):
     assert _lib.status_string(17) == "unknown status"
 
 
+def test_prefill_timing_switch(lib):
+    """Turning per-kernel timing on and off touches no device; with nothing recorded the
+    query returns zero time and zero launches for all three kernels."""
+    ms = (ctypes.c_float * 3)(1.0, 2.0, 3.0)
+    n = (ctypes.c_int * 3)(7, 7, 7)
+    assert lib.gdn_prefill_timing(1) == OK
+    assert lib.gdn_prefill_timing(0) == OK
+    assert lib.gdn_prefill_kernel_times(ctypes.addressof(ms), ctypes.addressof(n)) == OK
+    assert list(ms) == [0.0, 0.0, 0.0] and list(n) == [0, 0, 0]
+    assert lib.gdn_prefill_kernel_times(None, None) == OK
+
+
 def test_workspace_size_query(lib):
     """The prefill workspace holds (2 NB - 1) block records of 4 Dk Dv bytes per slice for NB blocks;
     the preferred NB gives about two output workgroups per CU (256 CUs when no GPU answers)."""

@@ -176,6 +176,37 @@ def test_block_counts_match_the_oracle(D):
 
 
 @pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_blocks_that_forget_partway(dtype):
+    """Long-memory gates except one chunk of strong decay (log a = -3 per token, a chunk product
+    of e^-192, which is 0 in fp32) at a different place in each block: a block's map is complete
+    once its composed transition is exactly zero, which here happens after 1, 2, 3 or 4 of its
+    chunk pairs (or never, in the block without such a chunk). Every split matches the oracle and
+    the one-block sequential pass, which composes no maps."""
+    cfg = inputs.GDN_32K.with_(name=f"forget_{dtype}", B=1, H=2, L=64 * 47 + 9, dtype=dtype, seed=43,
+                               gate_dist="long")
+    x = inputs.prefill_inputs(cfg)
+    la = x["log_alpha"].copy()
+    # 48 chunks, 6 blocks of 8 (the last chunk ragged), each block's chunks taken in pairs from its
+    # end: the decaying chunk sits at offset 7, 5, 3, 1 and 6 of blocks 0..4; block 5 has none
+    for blk, off in zip(range(5), (7, 5, 3, 1, 6)):
+        c = 8 * blk + off
+        la[:, :, 64 * c:64 * c + 64] = -3.0
+    x["log_alpha"] = la
+    dt = TD[dtype]
+    q, k, v = (dev_tensor(x[n], dt) for n in ("q", "k", "v"))
+    h0 = dev_tensor(x["h0"], torch.float32)
+    beta, lad = dev_tensor(x["beta"], torch.float32), dev_tensor(la, torch.float32)
+    ro, rh = _oracle(x)
+    tol = TOL_BF16 if dtype == "bf16" else TOL_F32
+    for nb in (1, 6, 7):
+        say(f"case {cfg.name}: {nb} blocks")
+        ws = prefill_workspace(torch, 1, 2, 128, nb) if nb > 1 else None
+        o, hf = ops.gdn_prefill_fwd(q, k, v, beta, lad, h0, workspace=ws)
+        torch.cuda.synchronize()
+        _check(host(o), host(hf), ro, rh, tol, f"{nb} blocks")
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
 def test_zero_gates_reset_the_state(dtype):
     """log a = -inf (a zero gate) clears the state before the token's write; the cumulative gate
     sums cannot be differenced across it. Zero gates at chunk starts, ends and inside chunks, in
