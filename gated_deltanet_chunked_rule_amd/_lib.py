@@ -10,6 +10,7 @@ LIB_PATH = os.path.join(_HERE, "libgdn.so")
 GDN_BF16, GDN_F32 = 0, 1
 GDN_BIDIR_NORMALIZE, GDN_BIDIR_ELU1 = 1, 2
 GDN_OK = 0
+GDN_PREFILL_NOALLOC_MAX_BYTES = 80 << 20
 
 # every symbol the header declares, with (restype, argtypes)
 _vp, _fp, _i, _sz = ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int, ctypes.c_size_t
@@ -17,6 +18,7 @@ SIGNATURES = {
     "gdn_status_string": (ctypes.c_char_p, [_i]),
     "gdn_prefill_workspace_size": (_sz, [_i, _i, _i, _i, _i, _i]),
     "gdn_prefill_fwd": (_i, [_vp, _vp, _vp, _fp, _fp, _fp, _vp, _fp, _i, _i, _i, _i, _i, _i, _vp, _sz, _vp]),
+    "gdn_prefill_fwd_noalloc": (_i, [_vp, _vp, _vp, _fp, _fp, _fp, _vp, _fp, _i, _i, _i, _i, _i, _i, _sz, _vp]),
     "gdn_prefill_skip_fwd": (_i, [_vp, _vp, _vp, _fp, _fp, _vp, _fp, _vp, _fp, _i, _i, _i, _i, _i, _i, _vp, _sz,
                                   _vp]),
     "gdn_prefill_banded_fwd": (_i, [_vp, _vp, _vp, _fp, _fp, _fp, _vp, _fp, _i, _i, _i, _i, _i, _i, _i, _vp, _sz,

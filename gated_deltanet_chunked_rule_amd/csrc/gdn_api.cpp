@@ -129,6 +129,8 @@ const char* gdn_status_string(int status) {
         case GDN_ERR_WORKSPACE: return "GDN_ERR_WORKSPACE: workspace missing or too small";
         case GDN_ERR_LAUNCH: return "GDN_ERR_LAUNCH: HIP runtime error";
         case GDN_ERR_DEVICE: return "GDN_ERR_DEVICE: current device is not gfx950";
+        case GDN_ERR_SCRATCH:
+            return "GDN_ERR_SCRATCH: scratch_bytes exceeds the library's static scratch (GDN_PREFILL_NOALLOC_MAX_BYTES)";
         default: return "unknown status";
     }
 }
@@ -143,6 +145,24 @@ int gdn_prefill_fwd(const void* q, const void* k, const void* v, const float* be
                     void* workspace, size_t workspace_bytes, void* stream) {
     return prefill(q, k, v, beta, log_alpha, nullptr, false, h0, o, h_final, B, H, L, Dk, Dv, dtype, workspace,
                    workspace_bytes, stream);
+}
+
+int gdn_prefill_fwd_noalloc(const void* q, const void* k, const void* v, const float* beta, const float* log_alpha,
+                            const float* h0, void* o, float* h_final, int B, int H, int L, int Dk, int Dv, int dtype,
+                            size_t scratch_bytes, void* stream) {
+    if (scratch_bytes > GDN_PREFILL_NOALLOC_MAX_BYTES) return GDN_ERR_SCRATCH;
+    // the arguments first (no workspace: none is required), then the scratch's address
+    int st = validate_prefill(q, k, v, beta, log_alpha, nullptr, false, h0, o, h_final, B, H, L, Dk, Dv, dtype,
+                              nullptr, 0, true);
+    if (st != GDN_OK) return st;
+    st = check_device();
+    if (st != GDN_OK) return st;
+    void* ws = nullptr;
+    if (scratch_bytes > 0 && gdn::prefill_scratch(&ws) != 0) return GDN_ERR_LAUNCH;
+    return gdn::launch_prefill(q, k, v, beta, log_alpha, nullptr, h0, o, h_final, B * H, L, Dk, dtype, 3, ws,
+                               scratch_bytes, static_cast<hipStream_t>(stream)) == 0
+               ? GDN_OK
+               : GDN_ERR_LAUNCH;
 }
 
 int gdn_prefill_skip_fwd(const void* q, const void* k, const void* v, const float* beta, const float* log_alpha,

@@ -18,6 +18,10 @@ int launch_prefill(const void* q, const void* k, const void* v, const float* bet
                    const unsigned char* keep, const float* h0, void* o, float* h_final, int BH, long L, int D,
                    int dtype, int band, void* ws, size_t ws_bytes, hipStream_t stream);
 
+// Device address of the current device's copy of the static prefill scratch
+// (GDN_PREFILL_NOALLOC_MAX_BYTES bytes), looked up once per device; 0 or -1.
+int prefill_scratch(void** ptr);
+
 // Per-kernel timing of launch_prefill: when on, HIP events bracket each launch on its stream.
 // prefill_kernel_times waits for them and returns summed ms and launch counts per stage (block
 // maps, pass over blocks, outputs), then clears the record.

@@ -42,6 +42,7 @@
 #include <utility>
 #include <vector>
 
+#include "../../include/gdn.h"
 #include "gdn_launch.h"
 #include "gdn_rows.h"
 
@@ -994,6 +995,26 @@ size_t prefill_workspace_bytes(long BH, long L, int D, int /*dtype*/) {
 
 // no workspace is needed: the whole sequence then runs as one block per slice
 size_t prefill_workspace_min_bytes(long, long, int, int) { return 0; }
+
+// Static scratch for the prefill entry point that allocates nothing: it holds that call's block
+// maps and block start states, laid out as a caller's workspace. Each device holds its own copy
+// from the time the library's code is loaded on it until the process ends.
+static __device__ __align__(256) unsigned char scratch[GDN_PREFILL_NOALLOC_MAX_BYTES];
+
+int prefill_scratch(void** ptr) {
+    constexpr int MAXDEV = 64;
+    static std::atomic<void*> addr[MAXDEV];
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= MAXDEV) return -1;
+    void* p = addr[dev].load(std::memory_order_acquire);
+    if (!p) {
+        // the device address of this device's copy (the array's name is only a host-side handle)
+        if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) return -1;
+        addr[dev].store(p, std::memory_order_release);
+    }
+    *ptr = p;
+    return 0;
+}
 
 // Optional per-kernel timing: HIP events recorded around each launch on the caller's stream.
 namespace {

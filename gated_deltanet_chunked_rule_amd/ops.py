@@ -115,6 +115,32 @@ def gdn_prefill_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, beta: tor
     return _prefill("gdn_prefill_fwd", q, k, v, beta, log_alpha, h0, o, h_final, workspace, stream, True)
 
 
+def gdn_prefill_fwd_noalloc(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, beta: torch.Tensor,
+                            log_alpha: torch.Tensor, h0: Optional[torch.Tensor], o: torch.Tensor,
+                            h_final: torch.Tensor, scratch_bytes: Optional[int] = None, *,
+                            stream=None) -> Tuple[torch.Tensor, torch.Tensor]:
+    """gdn_prefill_fwd with the library's static per-device scratch as its workspace; allocates
+    nothing (o and h_final are required). scratch_bytes: how much of the scratch to use, default
+    the preferred workspace size capped at GDN_PREFILL_NOALLOC_MAX_BYTES. Returns (o, h_final)."""
+    B, H, L, D = q.shape
+    dev, dt = q.device, q.dtype
+    for name, t in (("q", q), ("k", k), ("v", v)):
+        _req(name, t, (B, H, L, D), dt, dev)
+    _req("beta", beta, (B, H, L), torch.float32, dev)
+    _req("log_alpha", log_alpha, (B, H, L), torch.float32, dev)
+    if h0 is not None:
+        _req("h0", h0, (B, H, D, D), torch.float32, dev)
+    _req("o", o, (B, H, L, D), dt, dev)
+    _req("h_final", h_final, (B, H, D, D), torch.float32, dev)
+    if scratch_bytes is None:
+        scratch_bytes = min(prefill_workspace_size(B, H, L, D, dt), _lib.GDN_PREFILL_NOALLOC_MAX_BYTES)
+    rc = _lib.load().gdn_prefill_fwd_noalloc(_p(q), _p(k), _p(v), _p(beta), _p(log_alpha), _p(h0), _p(o),
+                                             _p(h_final), B, H, L, D, D, _code(dt), int(scratch_bytes),
+                                             _stream(dev, stream))
+    _lib.check(rc, "gdn_prefill_fwd_noalloc")
+    return o, h_final
+
+
 def gdn_prefill_skip_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, beta: torch.Tensor,
                          log_alpha: torch.Tensor, keep: torch.Tensor, h0: Optional[torch.Tensor] = None, *,
                          o: Optional[torch.Tensor] = None, h_final: Optional[torch.Tensor] = None,

@@ -54,7 +54,8 @@ enum {
     GDN_ERR_ALIAS = -5,      /* an output overlaps an input or another output */
     GDN_ERR_WORKSPACE = -6,  /* workspace missing or smaller than the size query returned */
     GDN_ERR_LAUNCH = -7,     /* the HIP runtime refused a launch or a device query */
-    GDN_ERR_DEVICE = -8      /* the current device is not a gfx950 GPU */
+    GDN_ERR_DEVICE = -8,     /* the current device is not a gfx950 GPU */
+    GDN_ERR_SCRATCH = -9     /* more static scratch requested than the library holds */
 };
 
 /* Human-readable name of a status code (static string, never NULL). */
@@ -108,6 +109,31 @@ int gdn_prefill_fwd(const void *q, const void *k, const void *v,
                     void *o, float *h_final,
                     int B, int H, int L, int Dk, int Dv, int dtype,
                     void *workspace, size_t workspace_bytes, void *stream);
+
+/* Size of the device array that gdn_prefill_fwd_noalloc uses as its workspace (80 MiB). */
+#define GDN_PREFILL_NOALLOC_MAX_BYTES ((size_t)80 << 20)
+
+/*
+ * gdn_prefill_fwd for callers that cannot allocate device memory: code under HIP graph capture,
+ * serving loops that must not call hipMalloc, harnesses that forbid allocation. The arguments and
+ * results are those of gdn_prefill_fwd, except that the workspace is the first scratch_bytes
+ * bytes of a static array the library holds on each device (GDN_PREFILL_NOALLOC_MAX_BYTES bytes,
+ * held from the library's first use on that device until the process ends). scratch_bytes plays
+ * the part of workspace_bytes: pass gdn_prefill_workspace_size(...) for the preferred block
+ * count, any smaller value (0 included) for fewer blocks. Given the same number of bytes, results
+ * are bitwise those of gdn_prefill_fwd with a workspace of that size.
+ * A scratch_bytes above GDN_PREFILL_NOALLOC_MAX_BYTES is rejected with GDN_ERR_SCRATCH before
+ * anything is enqueued. On a 256-CU MI355X the preferred size of every shape fits (the largest,
+ * at D = 128 and B*H = 255, is 79.7 MiB). The call allocates nothing: the first call on a
+ * device looks up that device's copy of the array once (hipGetSymbolAddress).
+ * Every call on one device shares that device's array and leaves the last call's contents in it;
+ * nothing in it needs clearing (each call writes what it reads). Calls on one device whose work
+ * can overlap (different streams, or host threads) race on the array: order them on one stream.
+ */
+int gdn_prefill_fwd_noalloc(const void *q, const void *k, const void *v,
+                            const float *beta, const float *log_alpha, const float *h0,
+                            void *o, float *h_final, int B, int H, int L, int Dk, int Dv,
+                            int dtype, size_t scratch_bytes, void *stream);
 
 /*
  * The gated delta rule with skipped chunk updates (SparseGDN article, fileenergy.com: events the

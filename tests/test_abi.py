@@ -33,7 +33,7 @@ def test_header_symbols_exported(lib):
 
 
 def test_status_strings(lib):
-    for code in (0, -1, -2, -3, -4, -5, -6, -7, -8):
+    for code in (0, -1, -2, -3, -4, -5, -6, -7, -8, -9):
         assert _lib.status_string(code).startswith("GDN_")
     assert _lib.status_string(17) == "unknown status"
 
@@ -94,6 +94,23 @@ def test_prefill_host_validation(lib):
     assert _prefill(lib, o=0x20000000) == ALIAS        # o == k
     assert _prefill(lib, hf=0x40000000 + 4096) == ALIAS  # h_final inside v
     assert _prefill(lib, h0=0x7f000000 + 16) == ALIAS  # partial h0 / h_final overlap
+
+
+def test_noalloc_host_validation(lib):
+    """The prefill entry point without a workspace argument: a request for more static scratch
+    than the library holds is refused first; the other checks are gdn_prefill_fwd's."""
+    f = lib.gdn_prefill_fwd_noalloc
+    SCRATCH = -9
+    args = lambda q=0x10000, D=128, L=64, sb=0: (q, 0x20000000, 0x40000000, 0x60000000, 0x60100000, None,
+                                                 0x70000000, 0x7f000000, 1, 1, L, D, D, 0, sb, None)
+    assert _lib.GDN_PREFILL_NOALLOC_MAX_BYTES == 80 << 20
+    assert f(*args(sb=(80 << 20) + 1)) == SCRATCH
+    assert f(*args(q=None, sb=(80 << 20) + 1)) == SCRATCH
+    assert f(*args(q=None)) == NULL
+    assert f(*args(D=96)) == SHAPE
+    assert f(*args(q=0x10008)) == ALIGN
+    for sb in (0, 1 << 20, 80 << 20):
+        assert f(*args(L=4096, sb=sb)) not in (NULL, SHAPE, ALIGN, ALIAS, WORKSPACE, SCRATCH)
 
 
 def test_linattn_workspace(lib):
