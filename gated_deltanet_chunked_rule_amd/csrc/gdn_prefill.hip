@@ -268,36 +268,52 @@ struct Fetch {
     RowRegs<D, E, C::NT> rq, rk;
     frag vf[NGW][4];   // V row fragments [own group][token tile]
     float la, bt;
-    int n;   // valid tokens
-    __device__ __forceinline__ void issue(const PrefArgs& a, int bh, int c, bool rows, int tid, int w) {
+    int n;         // valid tokens
+    size_t tok0;   // first token of the chunk in its slice's rows
+    __device__ __forceinline__ void start(const PrefArgs& a, int bh, int c) {
         const long t0 = (long)c * CH;
         n = (int)min((long)CH, a.L - t0);
-        const size_t tok0 = (size_t)bh * a.L + t0;
-        if (rows) {
-            rk.load(static_cast<const T*>(a.k) + tok0 * D, n, tid);
-            if constexpr (OUT) rq.load(static_cast<const T*>(a.q) + tok0 * D, n, tid);
-            const __amdgpu_buffer_rsrc_t rv = buffer_rsrc(static_cast<const T*>(a.v) + tok0 * D, n * D * (int)sizeof(T));
-            const int lane = tid & 63, j = lane >> 4, m = lane & 15;
-            const int g0 = C::VPW * w / C::FPD;
+        tok0 = (size_t)bh * a.L + t0;
+    }
+    __device__ __forceinline__ void load_k(const PrefArgs& a, int tid) {
+        rk.load(static_cast<const T*>(a.k) + tok0 * D, n, tid);
+    }
+    __device__ __forceinline__ void load_q(const PrefArgs& a, int tid) {
+        rq.load(static_cast<const T*>(a.q) + tok0 * D, n, tid);
+    }
+    __device__ __forceinline__ void load_v(const PrefArgs& a, int tid, int w) {
+        const __amdgpu_buffer_rsrc_t rv = buffer_rsrc(static_cast<const T*>(a.v) + tok0 * D, n * D * (int)sizeof(T));
+        const int lane = tid & 63, j = lane >> 4, m = lane & 15;
+        const int g0 = C::VPW * w / C::FPD;
 #pragma unroll
-            for (int gi = 0; gi < NGW; ++gi)
+        for (int gi = 0; gi < NGW; ++gi)
 #pragma unroll
-                for (int st = 0; st < 4; ++st) {
-                    const int e0 = (16 * st + m) * D + (g0 + gi) * C::KB + 4 * j;   // element offset
-                    if constexpr (sizeof(T) == 2) {
-                        const uint2 x = buffer_load8(rv, e0 * 2), y = buffer_load8(rv, (e0 + 16) * 2);
-                        vf[gi][st] = __builtin_bit_cast(frag, uint4{x.x, x.y, y.x, y.y});
-                    } else {
-                        vf[gi][st] = __builtin_bit_cast(frag, buffer_load16(rv, e0 * 4));
-                    }
+            for (int st = 0; st < 4; ++st) {
+                const int e0 = (16 * st + m) * D + (g0 + gi) * C::KB + 4 * j;   // element offset
+                if constexpr (sizeof(T) == 2) {
+                    const uint2 x = buffer_load8(rv, e0 * 2), y = buffer_load8(rv, (e0 + 16) * 2);
+                    vf[gi][st] = __builtin_bit_cast(frag, uint4{x.x, x.y, y.x, y.y});
+                } else {
+                    vf[gi][st] = __builtin_bit_cast(frag, buffer_load16(rv, e0 * 4));
                 }
-        }
+            }
+    }
+    __device__ __forceinline__ void load_gates(const PrefArgs& a, int tid) {
         if (tid < 64) {   // wave 0 scans the gates
             const __amdgpu_buffer_rsrc_t rl = buffer_rsrc(a.log_alpha + tok0, n * 4);
             const __amdgpu_buffer_rsrc_t rb = buffer_rsrc(a.beta + tok0, n * 4);
             la = __uint_as_float(buffer_load4(rl, tid * 4));
             bt = __uint_as_float(buffer_load4(rb, tid * 4));
         }
+    }
+    __device__ __forceinline__ void issue(const PrefArgs& a, int bh, int c, bool rows, int tid, int w) {
+        start(a, bh, c);
+        if (rows) {
+            load_k(a, tid);
+            if constexpr (OUT) load_q(a, tid);
+            load_v(a, tid, w);
+        }
+        load_gates(a, tid);
     }
 };
 
@@ -326,6 +342,39 @@ __device__ __forceinline__ void inverse_block(const float* Am, float* Tm, int bj
     for (int e = 0; e < 4; ++e) Tm[(16 * bi + 4 * j + e) * AS + 16 * bj + m] = -y[e];
 }
 
+// The lower-left 32 x 32 quadrant of T from its two diagonal 32 x 32 blocks (each already
+// inverted):  T_ij = -sum_{k=2}^{i} T_ik X_kj  with  X_kj = sum_{l=j}^{1} A_kl T_lj,
+// i in {2, 3}, j in {0, 1}; wave q computes tile (2 + q / 2, q % 2), recomputing the X it needs
+// (so the quadrant takes one barrier). fp32 MFMA; all four diagonal blocks and T_10, T_32 must be
+// final.
+template <int AS>
+__device__ __forceinline__ void inverse_quadrant(const float* Am, float* Tm, int q, int j, int m) {
+    const bool i3 = (q >> 1) != 0;   // scalars
+    const int bj = q & 1, bi = i3 ? 3 : 2;
+    auto arow = [&](const float* X, int r, int l) {   // A operand: tile (r, l), lane (m, j): row m, k = 4 j ..
+        const float4 x = *reinterpret_cast<const float4*>(X + (16 * r + m) * AS + 16 * l + 4 * j);
+        return f32x4{x.x, x.y, x.z, x.w};
+    };
+    auto bcol = [&](int l, int c) {   // B operand: tile (l, c) of T, lane (m, j): k = 4 j + e, column m
+        f32x4 v;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) v[e] = Tm[(16 * l + 4 * j + e) * AS + 16 * c + m];
+        return v;
+    };
+    const f32x4 z = {0.f, 0.f, 0.f, 0.f};
+    const f32x4 a2j = arow(Am, 2, bj), tjj = bcol(bj, bj), ti2 = arow(Tm, bi, 2);
+    f32x4 x2 = MM<F32>::mma(a2j, tjj, z);
+    if (bj == 0) x2 = MM<F32>::mma(arow(Am, 2, 1), bcol(1, 0), x2);
+    f32x4 y = MM<F32>::mma(ti2, x2, z);
+    if (i3) {
+        f32x4 x3 = MM<F32>::mma(arow(Am, 3, bj), tjj, z);
+        if (bj == 0) x3 = MM<F32>::mma(arow(Am, 3, 1), bcol(1, 0), x3);
+        y = MM<F32>::mma(arow(Tm, 3, 3), x3, y);
+    }
+#pragma unroll
+    for (int e = 0; e < 4; ++e) Tm[(16 * bi + 4 * j + e) * AS + 16 * bj + m] = -y[e];
+}
+
 // ---------------------------------------------------------------------------------------------
 // the intra-chunk solve, shared by both kernels
 // ---------------------------------------------------------------------------------------------
@@ -336,8 +385,10 @@ __device__ __forceinline__ void inverse_block(const float* Am, float* Tm, int bj
 //   - its own d tiles of K transposed on the matrix core (scaled by -beta e^g into `kbe`, and
 //     for OUT by e^{g_C - g} into the Khat^T fragments) and its own value tiles of V from `vf`
 //     (scaled by beta into `vb`);
-// then T = (I + A)^-1 blocked by 16 (blocks more than `band` below the diagonal zero). Returns
-// after the barrier that completes T. Wave w owns d (and value) tiles VPW w .. VPW w + VPW - 1.
+// then T = (I + A)^-1 blocked by 16: the diagonal blocks by forward substitution, then (exact)
+// the two 32 x 32 diagonal blocks and the quadrant below them, or (band < 3) the blocks within
+// `band` of the diagonal level by level, the others zero. Returns after the barrier that
+// completes T. Wave w owns d (and value) tiles VPW w .. VPW w + VPW - 1.
 template <int D, class E, bool OUT, int NW>
 __device__ __forceinline__ void intra_solve(unsigned char* smem, int band, int w, int lane,
                                             const typename MM<E>::frag (&vf)[Fetch<D, E, OUT, NW>::NGW][4],
@@ -456,13 +507,14 @@ __device__ __forceinline__ void intra_solve(unsigned char* smem, int band, int w
             asm volatile("" : "+v"(vb[t][kt]));
         }
     lds_sync();   // A is complete, and K rows are no longer read (OUT: T takes their space)
-    // the above-diagonal 16 x 16 blocks of T are zero (token fragments of 32 read some of them),
-    // and so are, for the block-adjacent approximation, those more than `band` below it
+    // T's blocks (0, 1) and (2, 3) above the diagonal are zero (the token fragments of 32 that
+    // the products with T read cover them; no other block above the diagonal is read), and so
+    // are, for the block-adjacent approximation, the blocks more than `band` below it
     const int tid = 64 * w + lane;
 #pragma unroll
     for (int i = 0; i < 16 * 256 / C::NT; ++i) {
         const int el = tid + C::NT * i, b = el >> 8, bi = b >> 2, bj = b & 3;
-        if (bj > bi || bi - bj > band) Tm[(16 * bi + ((el & 255) >> 4)) * AS + 16 * bj + (el & 15)] = 0.f;
+        if ((bj == bi + 1 && (bi & 1) == 0) || bi - bj > band) Tm[(16 * bi + ((el & 255) >> 4)) * AS + 16 * bj + (el & 15)] = 0.f;
     }
     // diagonal blocks by forward substitution (wave i inverts block i, lane c < 16 owns column c),
     // then T_ij = -T_ii sum_{k=j}^{i-1} A_ik T_kj level by level on fp32 MFMA. The substitution
@@ -492,12 +544,19 @@ __device__ __forceinline__ void intra_solve(unsigned char* smem, int band, int w
         }
     }
     lds_sync();
-    if (w + 1 < 4 && 1 <= band) inverse_block<AS, 1>(Am, Tm, w, j, m);
-    lds_sync();
-    if (w + 2 < 4 && 2 <= band) inverse_block<AS, 2>(Am, Tm, w, j, m);
-    lds_sync();
-    if (w + 3 < 4 && 3 <= band) inverse_block<AS, 3>(Am, Tm, w, j, m);
-    lds_sync();
+    if (band >= 3) {
+        // exact: blocks (1, 0) and (3, 2), then the lower-left quadrant
+        if (w < 2) inverse_block<AS, 1>(Am, Tm, 2 * w, j, m);
+        lds_sync();
+        if (w < 4) inverse_quadrant<AS>(Am, Tm, w, j, m);
+        lds_sync();
+    } else {
+        // block-adjacent: the blocks within `band` of the diagonal, level by level
+        if (w + 1 < 4 && 1 <= band) inverse_block<AS, 1>(Am, Tm, w, j, m);
+        lds_sync();
+        if (w + 2 < 4 && 2 <= band) inverse_block<AS, 2>(Am, Tm, w, j, m);
+        lds_sync();
+    }
 }
 
 // ---------------------------------------------------------------------------------------------
@@ -874,8 +933,14 @@ __global__ __launch_bounds__(512) void out_kernel(PrefArgs a) {
         }
         lds_sync();
         // the next chunk's rows and gates load while this one's chain step runs (the solve's
-        // registers are free by now)
-        if (c + 1 < c1) fx.issue(a, bh, c + 1, true, tid, w);
+        // registers are free by now), spread over its phases so that no phase waits long to
+        // issue its loads
+        const bool more = c + 1 < c1;
+        if (more) {
+            fx.start(a, bh, c + 1);
+            fx.load_gates(a, tid);
+            fx.load_k(a, tid);
+        }
         const float dec = gt->dec;
         // U = Ut - W H
         frag Hf[VPW][NKD];
@@ -896,6 +961,7 @@ __global__ __launch_bounds__(512) void out_kernel(PrefArgs a) {
         for (int t = 0; t < VPW; ++t)
 #pragma unroll
             for (int kt = 0; kt < NKT; ++kt) Uf[t][kt] = M::from_acc(U[t], kt);
+        if (more) fx.load_q(a, tid);
         // O^T = e^g (H^T Q^T) + U^T P^T, lane (j, n): O[16 rt + n][16 vt + 4 j .. + 3]
         {
             const long t0 = (long)c * CH;
@@ -928,6 +994,7 @@ __global__ __launch_bounds__(512) void out_kernel(PrefArgs a) {
                                   make_float4(ot[t][0], ot[t][1], ot[t][2], ot[t][3]), T{});
             }
         }
+        if (more) fx.load_v(a, tid, w);
         // H <- e^{g_C} H + Khat^T U
 #pragma unroll
         for (int lt = 0; lt < NDT; ++lt) {
