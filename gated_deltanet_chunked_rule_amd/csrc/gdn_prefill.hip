@@ -342,6 +342,25 @@ __device__ __forceinline__ void inverse_block(const float* Am, float* Tm, int bj
     for (int e = 0; e < 4; ++e) Tm[(16 * bi + 4 * j + e) * AS + 16 * bj + m] = -y[e];
 }
 
+// Steps s = 4 S .. 4 S + 3 of the forward substitution of a diagonal 16 x 16 block of T (block
+// origin i0), lane (c, g) = (lane / 4, lane % 4) holding rows 4 g .. 4 g + 3 of column c in x:
+// the lane of the quad with g = S owns row s, and the quad broadcast gives its final value.
+template <int S, int AS>
+__device__ __forceinline__ void subst_stage(const float* Am, int i0, int g, float (&x)[4]) {
+    float4 av[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) av[i] = *reinterpret_cast<const float4*>(Am + (i0 + 4 * g + i) * AS + i0 + 4 * S);
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+        const float v = __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, x[k]), S * 0x55, 0xF, 0xF, false));
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const float ak = k == 0 ? av[i].x : k == 1 ? av[i].y : k == 2 ? av[i].z : av[i].w;
+            x[i] = fmaf(-ak, v, x[i]);
+        }
+    }
+}
+
 // The lower-left 32 x 32 quadrant of T from its two diagonal 32 x 32 blocks (each already
 // inverted):  T_ij = -sum_{k=2}^{i} T_ik X_kj  with  X_kj = sum_{l=j}^{1} A_kl T_lj,
 // i in {2, 3}, j in {0, 1}; wave q computes tile (2 + q / 2, q % 2), recomputing the X it needs
@@ -407,57 +426,61 @@ __device__ __forceinline__ void intra_solve(unsigned char* smem, int band, int w
     float* Am = reinterpret_cast<float*>(smem + L::O_V);
     const Gates* gt = reinterpret_cast<const Gates*>(smem + L::O_G);
 
-    // Row tile rw of the Gram matrix (and of P^T). With four waves each does its row of both; with
-    // eight, waves 0-3 take the Gram rows and waves 4-7 the P^T rows (the map kernel, which has
-    // no P^T, splits each Gram row over two waves). Every branch below is on scalars.
+    // Row tile rw of the Gram matrix and row tile rp of P^T: only their tiles on and below the
+    // diagonal are formed (st <= rw, st <= rp). With four waves wave w takes Gram row w and P^T
+    // row 3 - w, five tiles each; with eight, waves 0-3 take the Gram rows and waves 4-7 the P^T
+    // rows (the map kernel, which has no P^T, splits each Gram row over two waves). Every branch
+    // below is on scalars.
     constexpr bool SPLIT = C::NW == 8;
-    const int rw = w & 3;
+    const int rw = w & 3, rp = SPLIT ? rw : 3 - rw;
     const bool do_gram = !OUT || !SPLIT || w < 4;
     const bool do_p = OUT && (!SPLIT || w >= 4);
     constexpr int NST = !OUT && SPLIT ? 2 : 4;               // key tiles per wave
     const int st0 = !OUT && SPLIT ? 2 * (w >> 2) : 0;
-    // operands of row tile rw, and the gates of this lane's rows: r = 16 rw + 4 j + e in the Gram
-    // tiles (accumulator rows), r = 16 rw + m in the P^T tiles (accumulator columns)
+    // operands of row tiles rw (K) and rp (Q), and the gates of this lane's rows: r = 16 rw + 4 j + e
+    // in the Gram tiles (accumulator rows), r = 16 rp + m in the P^T tiles (accumulator columns)
     frag kw[NKD], qw[NKD];
 #pragma unroll
     for (int kd = 0; kd < NKD; ++kd) {
         if (do_gram) kw[kd] = row_frag_raw<E>(Kr + (16 * rw + m) * KP, kd * KB, j);
         if constexpr (OUT)
-            if (do_p) qw[kd] = row_frag_raw<E>(Qr + (16 * rw + m) * KP, kd * KB, j);
+            if (do_p) qw[kd] = row_frag_raw<E>(Qr + (16 * rp + m) * KP, kd * KB, j);
     }
     const float4 gr4 = *reinterpret_cast<const float4*>(gt->g + 16 * rw + 4 * j);
     const int4 rho4 = *reinterpret_cast<const int4*>(gt->rho + 16 * rw + 4 * j);
     const float4 b4 = *reinterpret_cast<const float4*>(gt->b + 16 * rw + 4 * j);
-    const float grm = gt->g[16 * rw + m];
-    const int rhom = gt->rho[16 * rw + m];
+    const float grm = gt->g[16 * rp + m];
+    const int rhom = gt->rho[16 * rp + m];
     f32x4 pt[4];
 #pragma unroll
     for (int i = 0; i < NST; ++i) {
         const int st = st0 + i;
+        const bool g_on = do_gram && st <= rw, p_on = do_p && st <= rp;
+        pt[i] = f32x4{0.f, 0.f, 0.f, 0.f};
+        if (!g_on && !p_on) continue;
         frag kf[NKD];
 #pragma unroll
         for (int kd = 0; kd < NKD; ++kd) kf[kd] = row_frag_raw<E>(Kr + (16 * st + m) * KP, kd * KB, j);
-        if (do_gram) {
-            // Gram tile (rw, st): lane (j, n) holds k_r . k_s, r = 16 rw + 4 j + e, s = 16 st + n
+        if (g_on) {
+            // Gram tile (rw, st): lane (j, n) holds k_r . k_s, r = 16 rw + 4 j + e, s = 16 st + n;
+            // A[r][s] = beta_r exp(g_r - g_s) k_r.k_s for s < r
             f32x4 g = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
             for (int kd = 0; kd < NKD; ++kd) g = M::mma(kw[kd], kf[kd], g);
-            if (st <= rw) {   // A[r][s] = beta_r exp(g_r - g_s) k_r.k_s for s < r (blocks on and below the diagonal)
-                const int s = 16 * st + m;
-                const float gs = gt->g[s];
-                const float rg[4] = {gr4.x, gr4.y, gr4.z, gr4.w}, rb[4] = {b4.x, b4.y, b4.z, b4.w};
-                const int rr[4] = {rho4.x, rho4.y, rho4.z, rho4.w};
+            const int s = 16 * st + m;
+            const float gs = gt->g[s];
+            const float rg[4] = {gr4.x, gr4.y, gr4.z, gr4.w}, rb[4] = {b4.x, b4.y, b4.z, b4.w};
+            const int rr[4] = {rho4.x, rho4.y, rho4.z, rho4.w};
 #pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    const int r = 16 * rw + 4 * j + e;
-                    Am[r * AS + s] = (s < r && s >= rr[e]) ? rb[e] * __expf(rg[e] - gs) * g[e] : 0.f;
-                }
+            for (int e = 0; e < 4; ++e) {
+                const int r = 16 * rw + 4 * j + e;
+                Am[r * AS + s] = (s < r && s >= rr[e]) ? rb[e] * __expf(rg[e] - gs) * g[e] : 0.f;
             }
         }
         if constexpr (OUT) {
-            if (do_p) {
-                // P^T tile (st, rw): lane (j, n) holds exp(g_r - g_s) q_r.k_s at s = 16 st + 4 j + e,
-                // r = 16 rw + n (zero for s > r or a zero gate in (s, r])
+            if (p_on) {
+                // P^T tile (st, rp): lane (j, n) holds exp(g_r - g_s) q_r.k_s at s = 16 st + 4 j + e,
+                // r = 16 rp + n (zero for s > r or a zero gate in (s, r])
                 f32x4 p = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
                 for (int kd = 0; kd < NKD; ++kd) p = M::mma(kf[kd], qw[kd], p);
@@ -465,17 +488,17 @@ __device__ __forceinline__ void intra_solve(unsigned char* smem, int band, int w
                 const float gs[4] = {gs4.x, gs4.y, gs4.z, gs4.w};
 #pragma unroll
                 for (int e = 0; e < 4; ++e) {
-                    const int s2 = 16 * st + 4 * j + e, r = 16 * rw + m;
+                    const int s2 = 16 * st + 4 * j + e, r = 16 * rp + m;
                     pt[i][e] = (s2 <= r && s2 >= rhom) ? __expf(grm - gs[e]) * p[e] : 0.f;
                 }
             }
         }
     }
     if constexpr (OUT) {
-        // P^T fragments [rt = rw][kt]: the B operand (k = s, column r) of O^T += U^T P^T
+        // P^T fragments [rt = rp][kt]: the B operand (k = s, column r) of O^T += U^T P^T
         if (do_p) {
 #pragma unroll
-            for (int kt = 0; kt < NKT; ++kt) st_frag(smem + L::O_P + (size_t)(rw * NKT + kt) * C::FR, lane, M::from_acc(pt, kt));
+            for (int kt = 0; kt < NKT; ++kt) st_frag(smem + L::O_P + (size_t)(rp * NKT + kt) * C::FR, lane, M::from_acc(pt, kt));
         }
     }
     __builtin_amdgcn_sched_barrier(0);
@@ -512,36 +535,33 @@ __device__ __forceinline__ void intra_solve(unsigned char* smem, int band, int w
     // are, for the block-adjacent approximation, the blocks more than `band` below it
     const int tid = 64 * w + lane;
 #pragma unroll
-    for (int i = 0; i < 16 * 256 / C::NT; ++i) {
-        const int el = tid + C::NT * i, b = el >> 8, bi = b >> 2, bj = b & 3;
-        if ((bj == bi + 1 && (bi & 1) == 0) || bi - bj > band) Tm[(16 * bi + ((el & 255) >> 4)) * AS + 16 * bj + (el & 15)] = 0.f;
+    for (int b = 0; b < 16; ++b) {
+        constexpr int NZ = C::NT < 256 ? 256 / C::NT : 1;   // elements per thread
+        const int bi = b >> 2, bj = b & 3;                   // compile-time block, scalar test
+        if (((bj == bi + 1 && (bi & 1) == 0) || bi - bj > band) && (C::NT <= 256 || w < 4)) {
+#pragma unroll
+            for (int z = 0; z < NZ; ++z) {
+                const int el = tid + (NZ > 1 ? C::NT * z : 0);
+                Tm[(16 * bi + (el >> 4)) * AS + 16 * bj + (el & 15)] = 0.f;
+            }
+        }
     }
-    // diagonal blocks by forward substitution (wave i inverts block i, lane c < 16 owns column c),
-    // then T_ij = -T_ii sum_{k=j}^{i-1} A_ik T_kj level by level on fp32 MFMA. The substitution
-    // runs in outer-product order: once x_s is final it updates every later row, so the dependent
-    // chain is one multiply-add per row instead of a growing dot product per row; A is read two
-    // columns at a time (rows as 8-byte reads).
+    // Diagonal blocks by forward substitution in outer-product order: wave i inverts block i,
+    // lane (c, g) = (lane / 4, lane % 4) holds rows 4 g .. 4 g + 3 of column c. Step s takes the
+    // final x_s from the lane of its quad that owns row s (a quad broadcast) and updates every
+    // row of the lane with A[r][s] (zero on and above the diagonal, so rows at or before s are
+    // left as they are); A is read four columns at a time.
     if (w < 4) {
-        const int i0 = 16 * w, c = lane & 15;
-        float x[16];
+        const int i0 = 16 * w, g = lane & 3, c = lane >> 2;
+        float x[4];
 #pragma unroll
-        for (int r = 0; r < 16; ++r) x[r] = r == c ? 1.f : 0.f;
+        for (int i = 0; i < 4; ++i) x[i] = 4 * g + i == c ? 1.f : 0.f;
+        subst_stage<0, AS>(Am, i0, g, x);
+        subst_stage<1, AS>(Am, i0, g, x);
+        subst_stage<2, AS>(Am, i0, g, x);
+        subst_stage<3, AS>(Am, i0, g, x);
 #pragma unroll
-        for (int q = 0; q < 8; ++q) {
-            float2 ac[16];
-#pragma unroll
-            for (int r = 0; r < 16; ++r) ac[r] = *reinterpret_cast<const float2*>(Am + (i0 + r) * AS + i0 + 2 * q);
-#pragma unroll
-            for (int r = 0; r < 16; ++r)
-                if (r > 2 * q) x[r] -= ac[r].x * x[2 * q];
-#pragma unroll
-            for (int r = 0; r < 16; ++r)
-                if (r > 2 * q + 1) x[r] -= ac[r].y * x[2 * q + 1];
-        }
-        if (lane < 16) {
-#pragma unroll
-            for (int r = 0; r < 16; ++r) Tm[(i0 + r) * AS + i0 + c] = x[r];
-        }
+        for (int i = 0; i < 4; ++i) Tm[(i0 + 4 * g + i) * AS + i0 + c] = x[i];
     }
     lds_sync();
     if (band >= 3) {
@@ -1115,10 +1135,10 @@ bool timed(int stage, hipStream_t s, F&& f) {
     }
     std::lock_guard<std::mutex> g(t.mu);
     hipEvent_t e0 = t.get(), e1 = t.get();
-    if (e0) hipEventRecord(e0, s);
+    if (e0) (void)hipEventRecord(e0, s);
     f();
     const bool ok = hipGetLastError() == hipSuccess;
-    if (e1) hipEventRecord(e1, s);
+    if (e1) (void)hipEventRecord(e1, s);
     if (e0 && e1) t.rec.push_back({stage, {e0, e1}});
     return ok;
 }
