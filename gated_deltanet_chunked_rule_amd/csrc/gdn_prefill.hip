@@ -39,6 +39,7 @@
 // lies in (s, r]. Only exponentials of non-positive differences are formed.
 #include <atomic>
 #include <mutex>
+#include <type_traits>
 #include <utility>
 #include <vector>
 
@@ -871,8 +872,9 @@ __global__ __launch_bounds__(256) void scan_kernel(PrefArgs a) {
 //   H[t][lt] lane (j, n): H[16 lt + 4 j + e][16 (VPW w + t) + n]
 // Per chunk, after the intra-chunk solve:
 //   U = Ut - W H;  O^T = e^g (H^T Q^T) + U^T P^T (stored);  H <- e^{g_C} H + Khat^T U
-// (a skipped chunk's update leaves the decayed state; its outputs still use U).
-template <int D, class E>
+// (a skipped chunk's update leaves the decayed state; its outputs still use U). SKIP: the
+// launch has a keep mask (the state update then follows the outputs, under a scalar branch).
+template <int D, class E, bool SKIP>
 __global__ __launch_bounds__(512) void out_kernel(PrefArgs a) {
     using C = Cfg<D, E, out_waves<D, E>()>;
     using L = Lds<D, E, true>;
@@ -917,7 +919,7 @@ __global__ __launch_bounds__(512) void out_kernel(PrefArgs a) {
         fx.rk.store(Kr, n, tid);
         if (w == 0) gate_scan(gt, fx.la, fx.bt, lane);
         lds_sync();
-        const unsigned keep = keep_chunk(a, bh, c);
+        const unsigned keep = SKIP ? keep_chunk(a, bh, c) : 1u;
         frag kbe[VPW][NKT], vb[VPW][NKT];
         intra_solve<D, E, true, C::NW>(smem, a.band, w, lane, fx.vf, kbe, vb);
         // -W fragments [rt][kd] (A: rows token, k = d), each d tile filling its part, and Ut
@@ -982,11 +984,14 @@ __global__ __launch_bounds__(512) void out_kernel(PrefArgs a) {
 #pragma unroll
             for (int kt = 0; kt < NKT; ++kt) Uf[t][kt] = M::from_acc(U[t], kt);
         if (more) fx.load_q(a, tid);
-        // O^T = e^g (H^T Q^T) + U^T P^T, lane (j, n): O[16 rt + n][16 vt + 4 j .. + 3]
-        {
-            const long t0 = (long)c * CH;
-            const __amdgpu_buffer_rsrc_t ro =
-                buffer_rsrc(static_cast<T*>(a.o) + ((size_t)bh * a.L + t0) * D, n * D * (int)sizeof(T));
+        // O^T = e^g (H^T Q^T) + U^T P^T, lane (j, n): O[16 rt + n][16 vt + 4 j .. + 3], and
+        // H <- e^{g_C} H + Khat^T U (H itself is no longer read: the products use Hf). The two
+        // are interleaved, two value tiles of the update per output tile, so that the update's
+        // independent products fill the output's dependent chains; `KEEP` is the chunk's keep flag.
+        const long t0 = (long)c * CH;
+        const __amdgpu_buffer_rsrc_t ro =
+            buffer_rsrc(static_cast<T*>(a.o) + ((size_t)bh * a.L + t0) * D, n * D * (int)sizeof(T));
+        auto out_and_update = [&](auto KEEP) {
 #pragma unroll
             for (int rt = 0; rt < 4; ++rt) {
                 f32x4 ot[VPW];
@@ -997,6 +1002,20 @@ __global__ __launch_bounds__(512) void out_kernel(PrefArgs a) {
                     const frag qf = row_frag_raw<E>(Qr + (16 * rt + m) * KP, kd * KB, j);
 #pragma unroll
                     for (int t = 0; t < VPW; ++t) ot[t] = M::mma(Hf[t][kd], qf, ot[t]);
+                }
+#pragma unroll
+                for (int l = 0; l < NDT / 4; ++l) {
+                    const int lt = (NDT / 4) * rt + l;
+#pragma unroll
+                    for (int t = 0; t < VPW; ++t) H[t][lt] = scale4(H[t][lt], dec);
+                    if constexpr (decltype(KEEP)::value) {
+#pragma unroll
+                        for (int kt = 0; kt < NKT; ++kt) {
+                            const frag kf = ld_frag<frag>(smem + L::O_KH + (size_t)(lt * NKT + kt) * C::FR, lane);
+#pragma unroll
+                            for (int t = 0; t < VPW; ++t) H[t][lt] = M::mma(kf, Uf[t][kt], H[t][lt]);
+                        }
+                    }
                 }
                 const float eg = gt->eg[16 * rt + m];
 #pragma unroll
@@ -1012,23 +1031,25 @@ __global__ __launch_bounds__(512) void out_kernel(PrefArgs a) {
                 for (int t = 0; t < VPW; ++t)
                     buffer_store4(ro, ((16 * rt + m) * D + 16 * (VPW * w + t) + 4 * j) * (int)sizeof(T),
                                   make_float4(ot[t][0], ot[t][1], ot[t][2], ot[t][3]), T{});
+                __builtin_amdgcn_sched_barrier(0);   // keeps each tile's operand loads in its step
             }
-        }
-        if (more) fx.load_v(a, tid, w);
-        // H <- e^{g_C} H + Khat^T U
-#pragma unroll
-        for (int lt = 0; lt < NDT; ++lt) {
-#pragma unroll
-            for (int t = 0; t < VPW; ++t) H[t][lt] = scale4(H[t][lt], dec);
+        };
+        if constexpr (SKIP) {
+            out_and_update(std::false_type{});
             if (keep) {
 #pragma unroll
-                for (int kt = 0; kt < NKT; ++kt) {
-                    const frag kf = ld_frag<frag>(smem + L::O_KH + (size_t)(lt * NKT + kt) * C::FR, lane);
+                for (int lt = 0; lt < NDT; ++lt)
 #pragma unroll
-                    for (int t = 0; t < VPW; ++t) H[t][lt] = M::mma(kf, Uf[t][kt], H[t][lt]);
-                }
+                    for (int kt = 0; kt < NKT; ++kt) {
+                        const frag kf = ld_frag<frag>(smem + L::O_KH + (size_t)(lt * NKT + kt) * C::FR, lane);
+#pragma unroll
+                        for (int t = 0; t < VPW; ++t) H[t][lt] = M::mma(kf, Uf[t][kt], H[t][lt]);
+                    }
             }
+        } else {
+            out_and_update(std::true_type{});
         }
+        if (more) fx.load_v(a, tid, w);
         lds_sync();   // the chunk's LDS is free for the next one
     }
     if (b == a.NB - 1) {
@@ -1176,8 +1197,10 @@ struct Launch {
         static const bool ok =
             hipFuncSetAttribute(reinterpret_cast<const void*>(&map_kernel<D, E>), hipFuncAttributeMaxDynamicSharedMemorySize,
                                 (int)map_lds<D, E>()) == hipSuccess &&
-            hipFuncSetAttribute(reinterpret_cast<const void*>(&out_kernel<D, E>), hipFuncAttributeMaxDynamicSharedMemorySize,
-                                (int)Lds<D, E, true>::BYTES) == hipSuccess;
+            hipFuncSetAttribute(reinterpret_cast<const void*>(&out_kernel<D, E, false>),
+                                hipFuncAttributeMaxDynamicSharedMemorySize, (int)Lds<D, E, true>::BYTES) == hipSuccess &&
+            hipFuncSetAttribute(reinterpret_cast<const void*>(&out_kernel<D, E, true>),
+                                hipFuncAttributeMaxDynamicSharedMemorySize, (int)Lds<D, E, true>::BYTES) == hipSuccess;
         return ok;
     }
     static int run(const PrefArgs& a, hipStream_t s) {
@@ -1193,8 +1216,12 @@ struct Launch {
                 return -1;
         }
         return timed(2, s, [&] {
-                   hipLaunchKernelGGL((out_kernel<D, E>), dim3(a.NB, a.BH), dim3(64 * out_waves<D, E>()), lds_out, s,
-                                      a);
+                   if (a.keep)
+                       hipLaunchKernelGGL((out_kernel<D, E, true>), dim3(a.NB, a.BH), dim3(64 * out_waves<D, E>()),
+                                          lds_out, s, a);
+                   else
+                       hipLaunchKernelGGL((out_kernel<D, E, false>), dim3(a.NB, a.BH), dim3(64 * out_waves<D, E>()),
+                                          lds_out, s, a);
                })
                    ? 0
                    : -1;
