@@ -127,7 +127,7 @@ __global__ __launch_bounds__(256) void la_kv_kernel(const typename E::T* __restr
         float gC = 0.f;
         if constexpr (GATED) {
             const float g = wave_scan(la, lane);
-            gC = __shfl(g, 63);
+            gC = wave_last(g);
             if (w == 0) skh[lane] = __expf(gC - g);
         }
         lds_sync();
@@ -265,7 +265,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void l
         float gC = 0.f;
         if constexpr (GATED) {
             const float g = wave_scan(la, lane);
-            gC = __shfl(g, 63);
+            gC = wave_last(g);
             if (w == 0) {
                 sg[lane] = g;
                 seg[lane] = __expf(g);

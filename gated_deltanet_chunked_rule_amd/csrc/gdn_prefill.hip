@@ -188,14 +188,9 @@ __device__ __forceinline__ int opaque(int x) {
     return x;
 }
 
-// inclusive max-scan over the 64 lanes of a wave
-__device__ __forceinline__ int wave_max_scan(int x, int lane) {
-#pragma unroll
-    for (int off = 1; off < 64; off <<= 1) {
-        const int y = __shfl_up(x, off);
-        if (lane >= off) x = max(x, y);
-    }
-    return x;
+// inclusive max-scan over the 64 lanes of a wave (values >= -1)
+__device__ __forceinline__ int wave_max_scan(int x, int /*lane*/) {
+    return wave_scan_dpp(x, -1, [](int a, int b) { return max(a, b); });
 }
 
 // Gate arrays of a chunk, computed by one wave (lane = token; past the end la = 0, bt = 0).
@@ -203,8 +198,8 @@ __device__ __forceinline__ void gate_scan(Gates* gt, float la, float bt, int lan
     const bool zero = la == -__builtin_inff();
     const float g = wave_scan(zero ? 0.f : la, lane);
     const int rho = wave_max_scan(zero ? lane : -1, lane);
-    const float gC = __shfl(g, 63);
-    const int rhoC = __shfl(rho, 63);
+    const float gC = wave_last(g);
+    const int rhoC = __builtin_amdgcn_readlane(rho, 63);
     const float eg = rho < 0 ? __expf(g) : 0.f;
     gt->g[lane] = g;
     gt->rho[lane] = rho;

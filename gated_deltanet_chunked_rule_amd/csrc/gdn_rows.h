@@ -5,14 +5,37 @@
 
 namespace gdn {
 
-// inclusive prefix sum over the 64 lanes of a wave
-__device__ __forceinline__ float wave_scan(float x, int lane) {
-#pragma unroll
-    for (int off = 1; off < 64; off <<= 1) {
-        const float y = __shfl_up(x, off);
-        if (lane >= off) x += y;
-    }
+// One step of a wave scan on DPP: the value `ctrl` moves into each lane (rows outside
+// `row_mask`, and lanes with no source, receive `id`).
+template <int CTRL, int ROW_MASK>
+__device__ __forceinline__ int dpp_move(int x, int id) {
+    return __builtin_amdgcn_update_dpp(id, x, CTRL, ROW_MASK, 0xF, false);
+}
+
+// Inclusive scan over the 64 lanes of a wave (op associative, id its identity): shifts right by
+// 1, 2, 4 and 8 lanes within each row of 16, then the totals of rows 0 and 2 (lanes 15 and 47)
+// into rows 1 and 3, then the total of rows 0-1 (lane 31) into rows 2 and 3.
+template <class V, class Op>
+__device__ __forceinline__ V wave_scan_dpp(V x, V id, Op op) {
+    const int idb = __builtin_bit_cast(int, id);
+    auto step = [&](auto y) { x = op(x, __builtin_bit_cast(V, y)); };
+    step(dpp_move<0x111, 0xF>(__builtin_bit_cast(int, x), idb));   // row_shr:1
+    step(dpp_move<0x112, 0xF>(__builtin_bit_cast(int, x), idb));   // row_shr:2
+    step(dpp_move<0x114, 0xF>(__builtin_bit_cast(int, x), idb));   // row_shr:4
+    step(dpp_move<0x118, 0xF>(__builtin_bit_cast(int, x), idb));   // row_shr:8
+    step(dpp_move<0x142, 0xA>(__builtin_bit_cast(int, x), idb));   // row_bcast:15
+    step(dpp_move<0x143, 0xC>(__builtin_bit_cast(int, x), idb));   // row_bcast:31
     return x;
+}
+
+// inclusive prefix sum over the 64 lanes of a wave
+__device__ __forceinline__ float wave_scan(float x, int /*lane*/) {
+    return wave_scan_dpp(x, 0.f, [](float a, float b) { return a + b; });
+}
+
+// value of lane 63 (the inclusive total), in every lane
+__device__ __forceinline__ float wave_last(float x) {
+    return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, x), 63));
 }
 
 // LDS-only workgroup barrier: waits for this wave's LDS operations (lgkmcnt) and nothing else,
