@@ -2,12 +2,18 @@
 """Benchmark of the gated delta-rule hot path on one MI355X.
 
 A step is one chunked GDN prefill of the long-context workload (B=1, H=16, L=131072, d=128,
-chunk 64: bf16 q/k/v, fp32 gates and state) through the C ABI, inputs resident in HBM. The JSON
-line also carries the decode step (256 sequences x 32 heads, 100 in-place steps, state GB/s),
-plain causal linear attention (B=4, H=16, L=8192) and the 32K GDN workload as components, the
-roofline of the prefill, and the fp64 oracle timed on this host's cores on a bounded sample.
+chunk 64: bf16 q/k/v, fp32 gates and state) through the C ABI, inputs resident in HBM. The call
+runs three kernels in order on one stream (block maps, the pass over blocks, outputs); the
+roofline is that of the output kernel, which does every step of the chunked algorithm for every
+chunk and dominates the call, timed live with the library's per-kernel HIP events. The JSON line
+also carries the decode step (256 sequences x 32 heads, 100 in-place steps, state GB/s), plain
+causal linear attention (B=4, H=16, L=8192), the 32K GDN workload, the 128K workload with
+long-memory gates, the skip and banded variants as components, hardware-counter figures taken
+with rocprofv3 on the same kernel sources, and the fp64 oracle timed on this host's cores on a
+bounded sample.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W]
+    python bench.py --counters DIR   # per-kernel bytes and MFMA work from rocprofv3 counter CSVs
 """
 from __future__ import annotations
 
@@ -29,17 +35,48 @@ PEAK_HBM_GBPS = 8000.0          # MI355X HBM3E
 PEAK_BF16_TFLOPS = 2500.0       # MI355X dense bf16 MFMA
 METRIC = "GDN prefill tokens/s at L=128K + % bf16 MFMA peak; decode state GB/s"
 
-# Memory traffic of one 128K prefill call, from rocprofv3 counter runs (FETCH_SIZE and WRITE_SIZE
-# summed over the call's prep and chain dispatches, each divided by what the counter reads per
-# byte for a plain copy of known size); profiles/gdn_prefill_B1H16L131072_traffic.md holds the
-# commands and the raw figures. Valid only for the kernel sources it was taken on: bench.py
-# reports it only while kernel_source_hash() still matches.
-TRAFFIC_128K = {"source_hash": "b64aca00947bf75b", "bytes_per_call": 6886434808}
+# Hardware counters of one 128K prefill call per kernel (rocprofv3 --pmc runs of
+# `bench.py --profile-steps 2 --warmup 1`, one counter set per run, read with
+# `bench.py --counters DIR`): HBM bytes = FETCH_SIZE and WRITE_SIZE, each divided by what the
+# counter reads per byte of a plain device copy of 1 GiB; MFMA flops = 512 x the MOPS counters.
+# The commands and raw figures are in profiles/gdn_prefill_B1H16L131072_counters.md. Valid only
+# for the kernel sources they were taken on: bench.py reports them only while
+# kernel_source_hash() still matches.
+COUNTERS_128K = {
+    "source_hash": "dabaae1509a440c6",
+    "fetch_factor": 0.500016,
+    "write_factor": 1.0,
+    "map": {
+        "fetch_kib": 32432.0,
+        "write_kib": 63488.0,
+        "hbm_bytes": 131430000.0,
+        "mfma_bf16_flops": 11572100000.0,
+        "mfma_f32_flops": 154403000.0,
+        "mfma_busy_frac": 0.106184
+    },
+    "scan": {
+        "fetch_kib": 143887.0,
+        "write_kib": 32768.0,
+        "hbm_bytes": 328226000.0,
+        "mfma_bf16_flops": 6241120000.0,
+        "mfma_f32_flops": 0.0,
+        "mfma_busy_frac": 0.0473495
+    },
+    "out": {
+        "fetch_kib": 811173.0,
+        "write_kib": 525314.0,
+        "hbm_bytes": 2199150000.0,
+        "mfma_bf16_flops": 360777000000.0,
+        "mfma_f32_flops": 5100270000.0,
+        "mfma_busy_frac": 0.297675
+    }
+}
 
 
 # the sources the gated delta-rule prefill's kernels and their launcher are built from (the host-side
 # argument checks and declarations do not change what the kernels read and write)
 PREFILL_SOURCES = ("gdn_device.h", "gdn_mfma.h", "gdn_prefill.hip", "gdn_rows.h")
+KERNELS = {"map": "map_kernel", "scan": "scan_kernel", "out": "out_kernel"}
 
 
 def kernel_source_hash():
@@ -83,11 +120,85 @@ def prefill_bytes(cfg, gates=True):
     return b
 
 
+def out_kernel_bytes(cfg):
+    """Algorithmic bytes of the output kernel when the call uses several blocks per slice: every
+    token's q, k, v, beta and log_alpha read and o written once, and the final state written (the
+    initial state is read by the pass over blocks)."""
+    st = cfg.B * cfg.H * cfg.Dk * cfg.Dv * 4
+    return prefill_bytes(cfg) - (st if cfg.h0 is not None else 0)
+
+
 def decode_bytes(cfg):
     S = cfg.N * cfg.H
     e = 2 if cfg.dtype == "bf16" else 4
     state = S * cfg.Dk * cfg.Dv * 4
     return 2 * state + S * (2 * cfg.Dk + 2 * cfg.Dv) * e + 2 * S * 4, 2 * state
+
+
+# ---------------------------------------------------------------------------------------------
+# hardware counters (rocprofv3 CSVs)
+# ---------------------------------------------------------------------------------------------
+def _counter_rows(path):
+    import csv
+    rows = {}
+    for r in csv.DictReader(open(path)):
+        rows.setdefault((r["Kernel_Name"], r["Counter_Name"]), []).append(float(r["Counter_Value"]))
+    return rows
+
+
+def _find_csv(d, sub):
+    for root, _, files in os.walk(os.path.join(d, sub)):
+        for f in files:
+            if f.endswith("counter_collection.csv"):
+                return os.path.join(root, f)
+    raise FileNotFoundError(os.path.join(d, sub))
+
+
+def counters_from(d):
+    """Per-launch counter figures of the prefill kernels from rocprofv3 runs under directory d:
+    fetch/ (FETCH_SIZE), write/ (WRITE_SIZE), cfetch/ and cwrite/ (the same counters on a 1 GiB
+    device copy, `bench.py --copy-calibrate 1073741824`), mfma/ (SQ_INSTS_VALU_MFMA_MOPS_BF16,
+    SQ_INSTS_VALU_MFMA_MOPS_F32, SQ_VALU_MFMA_BUSY_CYCLES, GRBM_GUI_ACTIVE), and source_hash.txt
+    (`bench.py --source-hash` run with them). The first call of each kernel (warm-up) is dropped
+    and the others averaged."""
+    gib_kib = float(1 << 20)
+
+    def calib(sub, counter):
+        rows = _counter_rows(_find_csv(d, sub))
+        vals = [v for (k, c), vs in rows.items() if "copyBuffer" in k and c == counter for v in vs if v > 0.4 * gib_kib]
+        return sum(vals) / len(vals) / gib_kib     # counter KiB per KiB copied
+
+    f_fetch, f_write = calib("cfetch", "FETCH_SIZE"), calib("cwrite", "WRITE_SIZE")
+    runs = {"fetch": _counter_rows(_find_csv(d, "fetch")), "write": _counter_rows(_find_csv(d, "write"))}
+    try:
+        runs["mfma"] = _counter_rows(_find_csv(d, "mfma"))
+    except FileNotFoundError:
+        runs["mfma"] = {}
+    # the kernel sources the runs were taken on (written next to them by `bench.py --source-hash`)
+    hp = os.path.join(d, "source_hash.txt")
+    out = {"source_hash": open(hp).read().strip() if os.path.exists(hp) else None,
+           "fetch_factor": f_fetch, "write_factor": f_write}
+    for short, kname in KERNELS.items():
+        def avg(run, counter):
+            vals = [vs for (k, c), vs in runs[run].items() if f"gdn::{kname}<128, gdn::BF16" in k and c == counter]
+            if not vals:
+                return None
+            v = vals[0][1:] if len(vals[0]) > 1 else vals[0]
+            return sum(v) / len(v)
+        fk, wk = avg("fetch", "FETCH_SIZE"), avg("write", "WRITE_SIZE")
+        if fk is None:
+            continue
+        rec = {"fetch_kib": fk, "write_kib": wk, "hbm_bytes": (fk / f_fetch + wk / f_write) * 1024}
+        mb, mf = avg("mfma", "SQ_INSTS_VALU_MFMA_MOPS_BF16"), avg("mfma", "SQ_INSTS_VALU_MFMA_MOPS_F32")
+        if mb is not None:
+            rec["mfma_bf16_flops"] = 512 * mb
+            rec["mfma_f32_flops"] = 512 * (mf or 0.0)
+            busy, active = avg("mfma", "SQ_VALU_MFMA_BUSY_CYCLES"), avg("mfma", "GRBM_GUI_ACTIVE")
+            if busy is not None and active:
+                # GRBM_GUI_ACTIVE comes summed over the 8 XCDs; busy cycles summed over all 1024 SIMDs
+                rec["mfma_busy_frac"] = busy / (active / 8 * 4 * 256)
+        out[short] = rec
+    return out
 
 
 # ---------------------------------------------------------------------------------------------
@@ -255,31 +366,53 @@ def bench_decode(torch, ops, cfg, steps):
             "hbm_GBps": total / (ms * 1e-3) / 1e9, "hbm_frac": total / (ms * 1e-3) / 1e9 / PEAK_HBM_GBPS}
 
 
+def _cpu_model():
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return None
+
+
 def cpu_baseline(cfg, target_s, gpu_out=None):
-    """The fp64 oracle on this host, all heads of the workload over its first L_s tokens, with
-    L_s calibrated so the run takes about `target_s` seconds."""
+    """The fp64 oracle on this host: all heads of the workload over its first L_s tokens on up to
+    16 OpenMP threads (one per head), L_s calibrated so the run takes about `target_s` seconds;
+    then one head of the same sample on one thread (its rate per head, times the heads, is the
+    one-thread figure)."""
     import oracle
     threads = min(os.cpu_count() or 1, 16, cfg.B * cfg.H)
 
-    def sample(L):
-        sl = [inputs.prefill_slice(cfg, 0, h, L) for h in range(cfg.H)]
+    def sample(L, heads):
+        sl = [inputs.prefill_slice(cfg, 0, h, L) for h in heads]
         st = lambda key: np.stack([s[key] for s in sl])[None]
         return st("q"), st("k"), st("v"), st("beta"), st("log_alpha"), st("h0")
 
     L = 1024
-    x = sample(L)
+    x = sample(L, range(cfg.H))
     t0 = time.perf_counter()
     oracle.gdn_prefill(*x, nthreads=threads)
     t = time.perf_counter() - t0
     L = int(min(cfg.L, max(1024, (target_s / max(t, 1e-3)) * L)) // 1024 * 1024)
-    x = sample(L)
+    x = sample(L, range(cfg.H))
     t0 = time.perf_counter()
     ro, rh = oracle.gdn_prefill(*x, nthreads=threads)
     t = time.perf_counter() - t0
     used = oracle.last_threads
+    # one thread, one head, a quarter of the sample's tokens
+    L1 = max(1024, L // 4 // 1024 * 1024)
+    x1 = sample(L1, [0])
+    t1s = time.perf_counter()
+    oracle.gdn_prefill(*x1, nthreads=1)
+    t1 = time.perf_counter() - t1s
     out = {"value": cfg.B * L / t, "unit": "tokens/s", "cores": used, "kind": "oracle",
            "sample": f"{cfg.name}: all {cfg.H} heads, first {L} of {cfg.L} tokens, fp64 token recurrence, "
-                     f"{used} OpenMP threads, {t:.1f} s"}
+                     f"{used} OpenMP threads (one per head), {t:.1f} s",
+           "nproc": os.cpu_count(), "cpu_model": _cpu_model(),
+           "one_thread": {"value": L1 / t1 / cfg.H, "unit": "tokens/s",
+                          "sample": f"head 0, first {L1} tokens, 1 thread, {t1:.2f} s; tokens/s of the whole "
+                                    f"workload (all {cfg.H} heads) at that rate"}}
     parity = None
     if gpu_out is not None:
         o = gpu_out[0, :, :L].float().cpu().numpy()
@@ -291,8 +424,9 @@ def cpu_baseline(cfg, target_s, gpu_out=None):
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=30,
+                    help="untimed calls first (the clocks settle over the first tens of milliseconds)")
     ap.add_argument("--no-components", action="store_true", help="time only the 128K prefill")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
@@ -312,9 +446,14 @@ def main():
                     help="only time device-to-device copies of BYTES (HIP events) and print the HBM rate "
                          "(bytes read + written per second), no JSON")
     ap.add_argument("--source-hash", action="store_true", help="print kernel_source_hash() and exit")
+    ap.add_argument("--counters", metavar="DIR", help="print the per-kernel counter figures of the rocprofv3 runs "
+                    "under DIR (see counters_from) and exit; no GPU needed")
     args = ap.parse_args()
     if args.source_hash:
         print(kernel_source_hash())
+        return
+    if args.counters:
+        print(json.dumps(counters_from(args.counters), indent=1))
         return
     if args.gpus != 1:
         print("bench.py measures one GPU: this build has no multi-GPU path (heads and sequences shard "
@@ -417,9 +556,28 @@ def main():
         log("[bench] cpu baseline (fp64 oracle)")
         cpu, parity = cpu_baseline(cfg, args.cpu_seconds, gpu_out=gpu_o)
 
-    traffic = None
-    if TRAFFIC_128K is not None and TRAFFIC_128K["source_hash"] == kernel_source_hash():
-        traffic = TRAFFIC_128K["bytes_per_call"]
+    # roofline of the output kernel (the call's dominant kernel): its algorithmic bytes and flops
+    # per launch over its average launch time, measured with HIP events on the call's stream
+    ko = res["kernels"]["out"]
+    t_out = ko["ms_avg"] * 1e-3
+    nchunk = cfg.B * cfg.H * ((cfg.L + 63) // 64)
+    ob = out_kernel_bytes(cfg)
+    oflops = nchunk * gdn_flops_per_chunk(64, cfg.Dk)
+    cnt = COUNTERS_128K if COUNTERS_128K is not None and COUNTERS_128K["source_hash"] == kernel_source_hash() else None
+    traffic = cnt["out"]["hbm_bytes"] if cnt else None
+    mfma_counted = None
+    if cnt and "mfma_bf16_flops" in cnt["out"]:
+        c = cnt["out"]
+        mfma_counted = {"bf16_flops_per_launch": c["mfma_bf16_flops"], "f32_flops_per_launch": c["mfma_f32_flops"],
+                        "bf16_tflops": c["mfma_bf16_flops"] / t_out / 1e12,
+                        "frac_of_bf16_peak": c["mfma_bf16_flops"] / t_out / 1e12 / PEAK_BF16_TFLOPS,
+                        "busy_frac": c.get("mfma_busy_frac")}
+    call_traffic = None
+    if cnt:
+        call_traffic = {"bytes": sum(cnt[k]["hbm_bytes"] for k in KERNELS if k in cnt),
+                        "alg_bytes": res["alg_bytes"]}
+        call_traffic["ratio"] = call_traffic["bytes"] / call_traffic["alg_bytes"]
+        call_traffic["per_kernel"] = {k: cnt[k]["hbm_bytes"] for k in KERNELS if k in cnt}
     line = {
         "metric": METRIC,
         "value": res["tokens_per_s"],
@@ -436,12 +594,18 @@ def main():
                 "log a=-softplus(N+2), h0 N(0,0.01))",
         "config": {"workload": "gdn_prefill_B1_H16_L131072_d128_chunk64", "B": cfg.B, "H": cfg.H,
                    "L": cfg.L, "d_k": cfg.Dk, "d_v": cfg.Dv, "chunk": 64, "qkv": "bf16", "gates_state": "fp32"},
-        "mfma": {"alg_tflops": res["alg_tflops"], "peak_tflops": PEAK_BF16_TFLOPS, "frac": res["mfma_frac"]},
-        # one gdn_prefill_fwd call is the unit: its three kernels run concurrently on three
-        # streams, so the call (timed with HIP events on the caller's stream) is the launch
-        "roofline": {"bound": "hbm", "kernel": "gdn_prefill_fwd (prep and chain kernels)",
-                     "achieved": res["hbm_GBps"], "peak": PEAK_HBM_GBPS, "unit": "GB/s",
-                     "frac": res["hbm_frac"], "traffic": traffic, "alg_bytes_per_launch": res["alg_bytes"]},
+        # the whole call: algorithmic flops (triangles exact) and whole 64 x 64 tiles over the call's time
+        "mfma": {"alg_tflops": res["alg_tflops"], "dense_tile_tflops": res["dense_tile_tflops"],
+                 "peak_tflops": PEAK_BF16_TFLOPS, "frac": res["mfma_frac"],
+                 "dense_tile_frac": res["dense_tile_tflops"] / PEAK_BF16_TFLOPS,
+                 "out_kernel_alg_frac": oflops / t_out / 1e12 / PEAK_BF16_TFLOPS,
+                 "counted_out_kernel": mfma_counted},
+        "roofline": {"bound": "hbm", "kernel": "out_kernel<128, BF16> (outputs and final state of each block)",
+                     "achieved": ob / t_out / 1e9, "peak": PEAK_HBM_GBPS, "unit": "GB/s",
+                     "frac": ob / t_out / 1e9 / PEAK_HBM_GBPS, "traffic": traffic,
+                     "alg_bytes_per_launch": ob, "launch_ms": ko["ms_avg"], "launches": ko["launches"]},
+        "kernels_ms": {k: v["ms_avg"] for k, v in res["kernels"].items()},
+        "call_traffic": call_traffic,
         "cpu_baseline": cpu,
         "parity_sample": parity,
         "components": components,
