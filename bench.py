@@ -432,6 +432,8 @@ def main():
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--profile-steps", type=int, default=0,
                     help="only run this many prefill steps after warm-up (for profilers), no JSON")
+    ap.add_argument("--variant", default=None, choices=("skip", "band1"),
+                    help="with --profile-steps: time gdn_prefill_skip_fwd (29%% kept) or gdn_prefill_banded_fwd (band 1)")
     ap.add_argument("--gate-dist", default="config", choices=("config", "long"),
                     help="with --profile-steps: the log-gate distribution (config: -softplus(N(0,1)+2); "
                          "long: -U(0, 0.01), a long memory)")
@@ -500,7 +502,7 @@ def main():
     if args.profile_steps:
         log("generating inputs")
         res, bufs = bench_prefill(torch, ops, cfg.with_(gate_dist=args.gate_dist), args.profile_steps, args.warmup,
-                                  verbose=True, kernel_times=True)
+                                  verbose=True, kernel_times=True, variant=args.variant)
         log(f"profiled {args.profile_steps} steps: {res['ms']:.3f} ms/step; kernels (HIP events): "
             + ", ".join(f"{n} {x['ms_avg']:.4f} ms" for n, x in res["kernels"].items()))
         return
@@ -519,35 +521,40 @@ def main():
         components["decode"] = bench_decode(torch, ops, inputs.DECODE_256x32, inputs.DECODE_256x32.steps)
         log(f"[bench] decode: {components['decode']['ms_per_step']:.4f} ms/step")
         log("[bench] linear attention")
-        r, b = bench_prefill(torch, ops, inputs.LINATTN_8K, max(5, args.steps // 2), 2, gdn=False)
+        r, b = bench_prefill(torch, ops, inputs.LINATTN_8K, max(5, args.steps // 2), args.warmup, gdn=False)
         components["linattn"] = r
         del b
         log("[bench] bidirectional linear attention")
-        components["linattn_bidir"] = bench_bidir(torch, ops, inputs.LINATTN_8K, max(5, args.steps // 2), 2)
+        components["linattn_bidir"] = bench_bidir(torch, ops, inputs.LINATTN_8K, max(5, args.steps // 2), args.warmup)
         log("[bench] gdn 32K")
-        r, b = bench_prefill(torch, ops, inputs.GDN_32K, max(5, args.steps // 2), 2)
+        r, b = bench_prefill(torch, ops, inputs.GDN_32K, max(5, args.steps // 2), args.warmup)
         components["gdn_32k"] = r
         del b
         log("[bench] linear attention with per-token gates")
         r, b = bench_prefill(torch, ops, inputs.LINATTN_8K.with_(gates=True, gate_dist="long"),
-                             max(5, args.steps // 2), 2, gdn=False, variant="gla")
+                             max(5, args.steps // 2), args.warmup, gdn=False, variant="gla")
         components["linattn_gated"] = r
         del b
         log("[bench] linear attention with a gate per key dimension")
-        r, b = bench_prefill(torch, ops, inputs.LINATTN_8K.with_(gate_dist="config"), max(5, args.steps // 2), 2,
+        r, b = bench_prefill(torch, ops, inputs.LINATTN_8K.with_(gate_dist="config"), max(5, args.steps // 2), args.warmup,
                              gdn=False, variant="gla_vec")
         components["linattn_gated_per_dim"] = r
         del b
         log("[bench] gdn 128K with long-memory gates")
-        r, b = bench_prefill(torch, ops, cfg.with_(gate_dist="long"), max(5, args.steps // 2), 2, kernel_times=True)
+        r, b = bench_prefill(torch, ops, cfg.with_(gate_dist="long"), max(5, args.steps // 2), args.warmup, kernel_times=True)
         components["gdn_128k_long_memory"] = r
         del b
         log("[bench] gdn 128K with skipped chunk updates (29% kept)")
-        r, b = bench_prefill(torch, ops, cfg, max(5, args.steps // 2), 2, variant="skip")
+        r, b = bench_prefill(torch, ops, cfg, max(5, args.steps // 2), args.warmup, variant="skip", kernel_times=True)
         components["gdn_128k_skip"] = r
         del b
+        log("[bench] gdn 128K with long-memory gates and skipped chunk updates (29% kept)")
+        r, b = bench_prefill(torch, ops, cfg.with_(gate_dist="long"), max(5, args.steps // 2), args.warmup,
+                             variant="skip", kernel_times=True)
+        components["gdn_128k_long_memory_skip"] = r
+        del b
         log("[bench] gdn 128K with the block-adjacent intra-chunk solve (band 1)")
-        r, b = bench_prefill(torch, ops, cfg, max(5, args.steps // 2), 2, variant="band1")
+        r, b = bench_prefill(torch, ops, cfg, max(5, args.steps // 2), args.warmup, variant="band1", kernel_times=True)
         components["gdn_128k_banded1"] = r
         del b
 
