@@ -376,7 +376,7 @@ def _cpu_model():
     return None
 
 
-def cpu_baseline(cfg, target_s, gpu_out=None):
+def cpu_baseline(cfg, target_s, gpu_out=None, gpu_hf=None):
     """The fp64 oracle on this host: all heads of the workload over its first L_s tokens on up to
     16 OpenMP threads (one per head), L_s calibrated so the run takes about `target_s` seconds;
     then one head of the same sample on one thread (its rate per head, times the heads, is the
@@ -418,6 +418,10 @@ def cpu_baseline(cfg, target_s, gpu_out=None):
         o = gpu_out[0, :, :L].float().cpu().numpy()
         err = np.abs(o - ro[0]).max(axis=(1, 2)) / np.abs(ro[0]).max(axis=(1, 2))
         parity = {"max_rel_err_o": float(err.max()), "sample": f"first {L} tokens of all heads"}
+        if gpu_hf is not None and L == cfg.L:
+            h = gpu_hf[0].float().cpu().numpy()
+            eh = np.abs(h - rh[0]).max(axis=(1, 2)) / np.abs(rh[0]).max(axis=(1, 2))
+            parity["max_rel_err_h_final"] = float(eh.max())
     return out, parity
 
 
@@ -511,7 +515,7 @@ def main():
     res, bufs = bench_prefill(torch, ops, cfg, args.steps, args.warmup, kernel_times=True)
     log(f"[bench] {cfg.name}: {res['ms']:.3f} ms/step, {res['tokens_per_s']:.3e} tokens/s; kernels: "
         + ", ".join(f"{n} {x['ms_avg']:.4f} ms" for n, x in res["kernels"].items()))
-    gpu_o = bufs[6]
+    gpu_o, gpu_hf = bufs[6], bufs[7]
 
     components = {}
     if not args.no_components:
@@ -561,7 +565,7 @@ def main():
     cpu, parity = (None, None)
     if not args.no_cpu_baseline:
         log("[bench] cpu baseline (fp64 oracle)")
-        cpu, parity = cpu_baseline(cfg, args.cpu_seconds, gpu_out=gpu_o)
+        cpu, parity = cpu_baseline(cfg, args.cpu_seconds, gpu_out=gpu_o, gpu_hf=gpu_hf)
 
     # roofline of the output kernel (the call's dominant kernel): its algorithmic bytes and flops
     # per launch over its average launch time, measured with HIP events on the call's stream

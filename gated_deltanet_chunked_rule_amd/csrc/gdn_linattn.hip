@@ -116,7 +116,7 @@ __global__ __launch_bounds__(256) void la_kv_kernel(const typename E::T* __restr
         const int n = rows_of(c);
         float la = 0.f;
         if constexpr (GATED)   // through a buffer resource: no branch, so no wait for older loads
-            la = __uint_as_float(buffer_load4(buffer_rsrc(log_alpha + (size_t)bh * L + c * CH, n * 4), lane * 4));
+            la = floor_log_gate(__uint_as_float(buffer_load4(buffer_rsrc(log_alpha + (size_t)bh * L + c * CH, n * 4), lane * 4)));
         rk.store(Kr, n, tid);
         rv.store(Vr, n, tid);
         if (c + 1 < c_end) {   // the next chunk's rows, in flight during this one
@@ -256,7 +256,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void l
         const size_t tok0 = (size_t)bh * L + c * CH;
         float la = 0.f;
         if constexpr (GATED)   // through a buffer resource: no branch, so no wait for older loads
-            la = __uint_as_float(buffer_load4(buffer_rsrc(log_alpha + tok0, n * 4), lane * 4));
+            la = floor_log_gate(__uint_as_float(buffer_load4(buffer_rsrc(log_alpha + tok0, n * 4), lane * 4)));
         if (c > c_begin) lds_sync();   // every wave is done with the previous chunk's LDS data
         rq.store(Qr, n, tid);
         rk.store(Kr, n, tid);
@@ -391,8 +391,10 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void l
 // The same three stages as above, with the block decay a Dk-vector. The intra-chunk products
 // take a reference token per pair of 16-token tiles: tile rt against any earlier tile uses the
 // last token before rt (one scaled query operand serves all of them), so both factors
-// e^{G_r - G_ref} and e^{G_ref - G_s} are at most 1; a tile against itself uses its middle token, so no factor exceeds e^{8 |log a|} (finite in fp32 for
-// per-token log gates above about -10).
+// e^{G_r - G_ref} and e^{G_ref - G_s} are at most 1. A tile against itself uses its middle token
+// when the chunk's gates fall by at most GLA_WIDE across every tile (no factor above e^{GLA_WIDE});
+// otherwise it is split by the highest bit in which the pair's positions differ, with a
+// reference between the two tokens of every pair (gla_diag_tile), so any gates are exact.
 // ---------------------------------------------------------------------------------------------
 namespace {
 
@@ -418,9 +420,19 @@ struct GateScan {
         for (int i = 0; i < G::TPQ; ++i) x[i] = __uint_as_float(buffer_load4(rs, ((s0 + i) * D + d) * 4));
     }
     __device__ __forceinline__ void prefix(float* tot, int tid) {
+        x[0] = floor_log_gate(x[0]);
 #pragma unroll
-        for (int i = 1; i < G::TPQ; ++i) x[i] += x[i - 1];
+        for (int i = 1; i < G::TPQ; ++i) x[i] = floor_log_gate(x[i]) + x[i - 1];
         tot[tid] = x[G::TPQ - 1];   // tot[qq][d]
+    }
+    // whether the cumulative gate falls by more than `lim` across one of this thread's 16-token
+    // tiles (after prefix; differences within the thread's tokens need no carry)
+    __device__ __forceinline__ bool tile_span_over(float lim) const {
+        static_assert(G::TPQ % 16 == 0, "whole tiles per thread");
+        bool over = false;
+#pragma unroll
+        for (int i = 0; i + 15 < G::TPQ; i += 16) over = over || x[i] - x[i + 15] > lim;
+        return over;
     }
     // after the barrier; returns this thread's last cumulative value (G_C[d] for the last block)
     __device__ __forceinline__ float store(float* sG, const float* tot, int tid) {
@@ -453,6 +465,57 @@ __device__ __forceinline__ typename MM<E>::frag row_frag_exp(const typename E::T
         x[4 * h + 3] = a.w * __expf(p.w - r.w);
     }
     return M::pack(x);
+}
+
+// Largest fall of the cumulative log gates across a 16-token tile for which a diagonal tile is
+// formed in one product against its middle token (operand factors up to e^{64}).
+constexpr float GLA_WIDE = 64.f;
+
+// P^T tile of a 16-token tile against itself (lane (j, n): key s = 4 j + e, query r = n of the
+// tile, s <= r), with no factor above 1 whatever the gates. A pair s < r is taken by the pass b
+// (8, 4, 2, 1) of the highest bit in which s and r differ: s in the first and r in the second
+// half of a group of 2b tokens. Pass b scales each key row in a first half by e^{G_ref - G_s} and
+// each query row in a second half by e^{G_r - G_ref}, ref the last token of the group's first half
+// (s <= ref < r); the other rows are zero (selected, not multiplied) and the product's entries
+// outside the pass's pairs are dropped. The diagonal s = r is q_r . k_r.
+template <class E, int D, int KP, int GS>
+__device__ __forceinline__ f32x4 gla_diag_tile(const typename E::T* Kr, const typename E::T* Qr, const float* sG,
+                                               int tile, int j, int m) {
+    using M = MM<E>;
+    using frag = typename M::frag;
+    constexpr int KB = M::KB, NKD = D / KB;
+    const int r0 = 16 * tile;
+    const typename E::T* kr = Kr + (r0 + m) * KP;   // key row m (A operand row m)
+    const typename E::T* qr = Qr + (r0 + m) * KP;   // query row m (B operand column m)
+    const float* gm = sG + (r0 + m) * GS;
+    f32x4 t = {0.f, 0.f, 0.f, 0.f};
+    {
+        f32x4 p = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int kd = 0; kd < NKD; ++kd) p = M::mma(row_frag_raw<E>(kr, kd * KB, j), row_frag_raw<E>(qr, kd * KB, j), p);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) t[e] = 4 * j + e == m ? p[e] : 0.f;
+    }
+#pragma unroll
+    for (int b = 8; b >= 1; b >>= 1) {
+        __builtin_amdgcn_sched_barrier(0);   // one pass's operands at a time
+        const bool first = (m % (2 * b)) < b;                     // row m in the first half of its group
+        const float* gref = sG + (r0 + m - m % (2 * b) + b - 1) * GS;
+        f32x4 p = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int kd = 0; kd < NKD; ++kd) {
+            const frag kf = row_frag_exp<E>(kr, gref, gm, kd * KB, j);   // e^{G_ref - G_s}, key rows in first halves
+            const frag qf = row_frag_exp<E>(qr, gm, gref, kd * KB, j);   // e^{G_r - G_ref}, query rows in second halves
+            p = M::mma(first ? kf : frag{}, first ? frag{} : qf, p);
+        }
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            const int s = 4 * j + e;
+            const bool pair = s / (2 * b) == m / (2 * b) && s % (2 * b) < b && m % (2 * b) >= b;
+            t[e] += pair ? p[e] : 0.f;
+        }
+    }
+    return t;
 }
 
 }  // namespace
@@ -609,6 +672,10 @@ __global__ __launch_bounds__(64 * NW) void gla_out_kernel(
     const int blk = blockIdx.x, bh = blockIdx.y;
     const int tid = threadIdx.x, lane = tid & 63, j = lane >> 4, m = lane & 15;
     const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+    // per chunk parity: set when a 16-token tile's cumulative gates span more than WIDE in some
+    // key dimension; the diagonal tiles then take the exact pass-by-pass form
+    __shared__ unsigned s_wide[2];
+    if (tid == 0) s_wide[0] = s_wide[1] = 0u;
     const long nch = (L + CH - 1) / CH;
     const long c_begin = (long)blk * cpb;
     const long c_end = c_begin + cpb < nch ? c_begin + cpb : nch;
@@ -651,9 +718,12 @@ __global__ __launch_bounds__(64 * NW) void gla_out_kernel(
             for (int kt = 0; kt < NKT; ++kt) vf[i][kt] = cols_frag<E>(&t[FPD * kt]);
         }
         lds_sync();
+        if (gsc.tile_span_over(GLA_WIDE)) s_wide[c & 1] = 1u;
         gsc.store(sG, sTot, tid);
         if (c + 1 < c_end) gsc.load(log_alpha + (tok0 + CH) * D, rows_of(c + 1), tid);
         lds_sync();
+        const bool wide = __builtin_amdgcn_readfirstlane(s_wide[c & 1]) != 0u;   // scalar
+        if (tid == 0) s_wide[(c + 1) & 1] = 0u;   // every wave read it in the previous chunk
         const float* gC = sG + (CH - 1) * GS;
         // Khat^T fragments of this wave's key tiles
 #pragma unroll
@@ -671,9 +741,9 @@ __global__ __launch_bounds__(64 * NW) void gla_out_kernel(
         }
         // P^T of token tile rt = w % 4, key tiles [SPW h, SPW h + SPW) (h = w / 4): lane (j, n) of
         // t[st] holds sum_d k_s[d] q_r[d] e^{G_r[d] - G_s[d]}, s = 16 st + 4 j + e, r = 16 rt + n,
-        // kept for s <= r. Both operands are scaled against a reference token: for the tiles before
-        // the diagonal the last token before tile rt (so the query operand is shared by them), on
-        // the diagonal the tile's middle token.
+        // kept for s <= r. Both operands are scaled against a reference token between s and r: for
+        // the tiles before the diagonal the last token before tile rt (so the query operand is
+        // shared by them), on the diagonal per pass of gla_diag_tile.
         {
             const int rt_w = w & 3, st0 = SPW * (w >> 2);
             const float* gq = sG + (16 * rt_w + m) * GS;    // this lane's query row (B operand column m)
@@ -695,13 +765,19 @@ __global__ __launch_bounds__(64 * NW) void gla_out_kernel(
                     for (int kd = 0; kd < NKD; ++kd)
                         t[st] = M::mma(row_frag_exp<E>(Kr + (16 * st + m) * KP, gb, gk, kd * KB, j), qo[kd], t[st]);
                 } else if (st == rt_w) {
-                    const float* gref = sG + (16 * st + 7) * GS;
+                    if (wide) {
+                        t[st] = gla_diag_tile<E, D, KP, GS>(Kr, Qr, sG, st, j, m);
+                    } else {
+                        // one product against the tile's middle token: no factor exceeds
+                        // e^{GLA_WIDE} (finite, and the pair's two factors multiply to at most 1)
+                        const float* gref = sG + (16 * st + 7) * GS;
 #pragma unroll
-                    for (int kd = 0; kd < NKD; ++kd)
-                        t[st] = M::mma(row_frag_exp<E>(Kr + (16 * st + m) * KP, gref, gk, kd * KB, j),
-                                       row_frag_exp<E>(Qr + (16 * rt_w + m) * KP, gq, gref, kd * KB, j), t[st]);
+                        for (int kd = 0; kd < NKD; ++kd)
+                            t[st] = M::mma(row_frag_exp<E>(Kr + (16 * st + m) * KP, gref, gk, kd * KB, j),
+                                           row_frag_exp<E>(Qr + (16 * rt_w + m) * KP, gq, gref, kd * KB, j), t[st]);
 #pragma unroll
-                    for (int e = 0; e < 4; ++e) t[st][e] = 16 * st + 4 * j + e <= 16 * rt_w + m ? t[st][e] : 0.f;
+                        for (int e = 0; e < 4; ++e) t[st][e] = 16 * st + 4 * j + e <= 16 * rt_w + m ? t[st][e] : 0.f;
+                    }
                 }
             }
             // the fragments whose key tiles this wave owns (FPD tiles each)

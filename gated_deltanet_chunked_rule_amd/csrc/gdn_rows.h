@@ -5,6 +5,14 @@
 
 namespace gdn {
 
+// Log gates below this bound are taken as the bound. Any product of gates that contains one is
+// then exp(x) with x <= -110 (log a <= 0 otherwise), which is exactly zero in fp32 (below half the
+// smallest subnormal), so such a gate, a zero gate (log a = -inf) included, closes the state
+// exactly while every cumulative sum stays finite: no -inf - (-inf) in their differences. NaN is
+// kept (it propagates).
+constexpr float LOG_GATE_FLOOR = -110.f;
+__device__ __forceinline__ float floor_log_gate(float x) { return x < LOG_GATE_FLOOR ? LOG_GATE_FLOOR : x; }
+
 // One step of a wave scan on DPP: the value `ctrl` moves into each lane (rows outside
 // `row_mask`, and lanes with no source, receive `id`).
 template <int CTRL, int ROW_MASK>

@@ -179,7 +179,10 @@ int gdn_prefill_banded_fwd(const void *q, const void *k, const void *v,
  * i.e. per chunk  O = diag(e^g) Q H0 + (Q K^T masked causally, diagonal included, times
  * e^{g_r - g_s}) V  and  H <- e^{g_C} H0 + (e^{g_C - g} K)^T V  with g the in-chunk prefix
  * sum of log_alpha. log_alpha NULL means a = 1 (plain linear attention, AI RnD Day channel
- * post, tgstat.ru, section "Linear attention"). Same argument list as gdn_prefill_fwd; beta
+ * post, tgstat.ru, section "Linear attention"). Log gates must be <= 0; one of -inf (a = 0)
+ * clears the state before the token's write, and any log gate below -110 is taken as -110, whose
+ * exponential (and that of every sum containing it) is exactly 0 in fp32, so it acts as a = 0
+ * too. NaN propagates. Same argument list as gdn_prefill_fwd; beta
  * must be NULL. The scalar transition lets the sequence be split into blocks of chunks whose
  * contributions to the state are summed in parallel; the workspace holds one Dk x Dv fp32
  * state and 4 bytes per block and (batch, head): at least B*H*(Dk*Dv*4 + 4) bytes when L > 0,
@@ -202,9 +205,10 @@ size_t linattn_prefill_workspace_size(int B, int H, int L, int Dk, int Dv, int d
  * linearised models: GLA, its gating applied over the key vectors):
  *   S_t = S_{t-1} diag(a_t) + v_t k_t^T,   o_t = S_t q_t,   a_t[i] = exp(log_alpha[t][i]),
  * i.e. in the stored key-major state H = S^T, row i decays by a_t[i] before the write.
- *   log_alpha   [B,H,L,Dk] fp32 (required when L > 0; log gates below about -10 per token and
- *               dimension are outside the supported range: within a 16-token tile the kernel
- *               scales operands by up to exp(8 |log a|))
+ *   log_alpha   [B,H,L,Dk] fp32 (required when L > 0), <= 0: any magnitude is supported (every
+ *               factor the kernel forms is exp of a non-positive sum); -inf (a = 0) closes the
+ *               dimension, and log gates below -110 are taken as -110, which acts the same way
+ *               (its exponential is exactly 0 in fp32). NaN propagates.
  * All other arguments as linattn_prefill_fwd; the workspace holds one Dk x Dv fp32 state and a
  * Dk-vector of summed log gates per block and (batch, head): at least B*H*(Dk*Dv*4 + Dk*4) bytes
  * when L > 0, gla_prefill_workspace_size(...) preferred. Runs on `stream` only; L = 0 copies h0

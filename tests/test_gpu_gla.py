@@ -58,7 +58,7 @@ def test_gla_ragged(gate_dist, dtype, D, L):
     _check(cfg, o, hf, ro, rh)
 
 
-@pytest.mark.parametrize("dtype,D,L", [("bf16", 128, 1500), ("f32", 64, 900), ("bf16", 64, 129)])
+@pytest.mark.parametrize("dtype,D,L", [("bf16", 128, 1500), ("f32", 64, 900), ("f32", 128, 900), ("bf16", 64, 129)])
 def test_gla_small_workspace_long_blocks(dtype, D, L):
     """The smallest workspace (one block of all chunks per slice) and one of two blocks; each
     result checked, and a second call with the same workspace bitwise equal."""
@@ -141,11 +141,13 @@ def test_gla_full_8k_workload_sampled():
         _check(cfg.with_(name=f"{cfg.name} slice {(b, h)}"), o[b:b + 1, h:h + 1], hf[b:b + 1, h:h + 1], ro, rh)
 
 
-@pytest.mark.parametrize("dtype,D", [("bf16", 128), ("f32", 64)])
-def test_gla_strong_gates(dtype, D):
-    """log a ~ -U(0, 8) per token and dimension: the in-chunk operands are scaled by up to e^{64}
-    on the diagonal tiles and the masked entries overflow; the result must still match."""
-    cfg = _cfg(f"gla_strong_{dtype}_d{D}", 1, 2, 333, D, dtype, 7600 + D, gate_dist="strong", qk="l2")
+@pytest.mark.parametrize("gate_dist", ["strong", "very_strong"])
+@pytest.mark.parametrize("dtype,D", [("bf16", 128), ("f32", 64), ("f32", 128)])
+def test_gla_strong_gates(dtype, D, gate_dist):
+    """log a ~ -U(0, 8) and -U(0, 40) per token and dimension: a chunk's cumulative gates reach
+    -2,560, far past exp's range in fp32; every factor the kernels form must stay at most 1."""
+    cfg = _cfg(f"gla_{gate_dist}_{dtype}_d{D}", 1, 2, 333, D, dtype, 7600 + D + (gate_dist == "very_strong"),
+               gate_dist=gate_dist, qk="l2")
     say(f"case {cfg.name}")
     x = inputs.prefill_inputs(cfg)
     la = inputs.gate_vectors(cfg)
@@ -155,6 +157,32 @@ def test_gla_strong_gates(dtype, D):
     assert torch.isfinite(o.float()).all() and torch.isfinite(hf).all()
     ro, rh = oracle.gla_vec_prefill(x["q"], x["k"], x["v"], la, x["h0"])
     _check(cfg, o, hf, ro, rh)
+
+
+@pytest.mark.parametrize("dtype,D", [("bf16", 128), ("f32", 128), ("bf16", 64), ("f32", 64)])
+def test_gla_closed_dimensions(dtype, D):
+    """Zero gates (log a = -inf): a quarter of the key dimensions closed at every token (their
+    state rows hold only the latest token), an eighth closed at random tokens (each one clears
+    that row), the rest long-memory; two blocks per slice, against the oracle, which computes
+    exp(-inf) = 0."""
+    cfg = _cfg(f"gla_closed_{dtype}_d{D}", 1, 2, 64 * 9 + 21, D, dtype, 7650 + D, gate_dist="long", qk="l2")
+    say(f"case {cfg.name}")
+    x = inputs.prefill_inputs(cfg)
+    la = inputs.gate_vectors(cfg).copy()
+    rng = np.random.default_rng(D)
+    la[:, :, :, : D // 4] = -np.inf
+    sparse = rng.random(la[:, :, :, D // 4: D // 4 + D // 8].shape) < 0.05
+    la[:, :, :, D // 4: D // 4 + D // 8][sparse] = -np.inf
+    q, k, v, lad, h0 = _dev(cfg, x, la)
+    ws = torch.empty(max(1, 2 * 2 * (D * D * 4 + D * 4)), dtype=torch.uint8, device="cuda")
+    o, hf = ops.gla_prefill_fwd(q, k, v, lad, h0, workspace=ws)
+    torch.cuda.synchronize()
+    assert torch.isfinite(o.float()).all() and torch.isfinite(hf).all()
+    ro, rh = oracle.gla_vec_prefill(x["q"], x["k"], x["v"], la, x["h0"])
+    assert np.isfinite(ro).all() and np.isfinite(rh).all()
+    _check(cfg, o, hf, ro, rh)
+    # the always-closed rows of the final state are the last token's k v^T exactly in the oracle
+    assert np.allclose(rh[:, :, : D // 4], x["k"][:, :, -1, : D // 4, None] * x["v"][:, :, -1, None, :])
 
 
 def test_gla_equal_gates_match_per_token_decay():

@@ -75,6 +75,33 @@ def test_gated_linattn_zero_gate_matches_plain():
     assert max_rel_err(host(o2), host(o1)) <= 1e-6 and max_rel_err(host(h2), host(h1)) <= 1e-6
 
 
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_gated_linattn_closed_gates(dtype):
+    """Per-token zero gates (log a = -inf: the state is cleared before the token's write) at chunk
+    starts, ends and inside chunks, and gates of -U(0, 40) elsewhere in one head, long-memory gates
+    in the other; two and several blocks per slice, against the oracle (exp(-inf) = 0)."""
+    cfg = inputs.LINATTN_8K.with_(name=f"gla_closed_{dtype}", B=1, H=2, L=64 * 9 + 17, dtype=dtype, seed=6150,
+                                  h0=0.1)
+    say(f"case {cfg.name}")
+    x = inputs.prefill_inputs(cfg)
+    rng = np.random.default_rng(6151)
+    la = np.empty((1, 2, cfg.L))
+    la[0, 0] = (-rng.uniform(0.0, 40.0, cfg.L)).astype(np.float32)
+    la[0, 1] = (-rng.uniform(0.0, 0.01, cfg.L)).astype(np.float32)
+    for t in (0, 5, 63, 64, 100, 250, 511, 590):
+        la[0, :, t] = -np.inf
+    dt = TD[dtype]
+    q, k, v = (dev_tensor(x[n], dt) for n in ("q", "k", "v"))
+    h0 = dev_tensor(x["h0"], torch.float32)
+    ro, rh = oracle.gla_prefill(x["q"], x["k"], x["v"], la, x["h0"])
+    for nbytes in (None, 2 * (128 * 128 * 4 + 4) * 2):
+        ws = None if nbytes is None else torch.empty(nbytes, dtype=torch.uint8, device="cuda")
+        o, hf = ops.linattn_prefill_fwd(q, k, v, h0, log_alpha=dev_tensor(la, torch.float32), workspace=ws)
+        torch.cuda.synchronize()
+        assert torch.isfinite(o.float()).all() and torch.isfinite(hf).all()
+        _check(host(o), host(hf), ro, rh, TOL_BF16 if dtype == "bf16" else TOL_F32, f"{cfg.name} ws={nbytes}")
+
+
 def test_gated_linattn_full_size_sampled_heads():
     """The linear-attention workload's shape (B=4, H=16, L=8192) with long-memory gates."""
     cfg = inputs.LINATTN_8K
