@@ -5,7 +5,8 @@ import ctypes
 import os
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(_HERE, "libgdn.so")
+# the in-tree build; GDN_LIBRARY names another build of the same sources (an instrumented one)
+LIB_PATH = os.environ.get("GDN_LIBRARY") or os.path.join(_HERE, "libgdn.so")
 
 GDN_BF16, GDN_F32 = 0, 1
 GDN_BIDIR_NORMALIZE, GDN_BIDIR_ELU1 = 1, 2
