@@ -154,10 +154,13 @@ struct PrefArgs {
     int band;                    // 16 x 16 blocks of T kept below the diagonal (3: all, exact)
 };
 
+// bytes per slice of the blocks' "map is not zero" flags (one int per block but the last)
+__host__ __device__ __forceinline__ size_t flag_bytes(int NB) { return NB <= 1 ? 0 : ((size_t)(NB - 1) * 4 + 255) / 256 * 256; }
+
 template <int D, class E>
 __device__ __forceinline__ size_t slice_ws(const PrefArgs& a) {
     using C = Cfg<D, E>;
-    return (size_t)(a.NB - 1) * C::PHI + (size_t)a.NB * C::HS;
+    return (size_t)(a.NB - 1) * C::PHI + (size_t)a.NB * C::HS + flag_bytes(a.NB);
 }
 template <int D, class E>
 __device__ __forceinline__ unsigned char* ws_phi(const PrefArgs& a, int bh, int b) {
@@ -169,6 +172,14 @@ __device__ __forceinline__ f32x4* ws_hs(const PrefArgs& a, int bh, int s) {
     using C = Cfg<D, E>;
     return reinterpret_cast<f32x4*>(a.ws + (size_t)bh * slice_ws<D, E>(a) + (size_t)(a.NB - 1) * C::PHI +
                                     (size_t)s * C::HS);
+}
+
+// flag of block b (< NB - 1) of a slice: nonzero when its map's transition Phi_b is not zero
+template <int D, class E>
+__device__ __forceinline__ int* ws_flag(const PrefArgs& a, int bh, int b) {
+    using C = Cfg<D, E>;
+    return reinterpret_cast<int*>(a.ws + (size_t)bh * slice_ws<D, E>(a) + (size_t)(a.NB - 1) * C::PHI +
+                                  (size_t)a.NB * C::HS) + b;
 }
 
 __device__ __forceinline__ unsigned keep_chunk(const PrefArgs& a, int bh, int c) {
@@ -390,6 +401,30 @@ __device__ __forceinline__ void inverse_quadrant(const float* Am, float* Tm, int
     for (int e = 0; e < 4; ++e) Tm[(16 * bi + 4 * j + e) * AS + 16 * bj + m] = -y[e];
 }
 
+// Operand fragment (k = token, in the fragment k-order) of columns n0 .. n0 + 15 and tokens
+// k0 .. k0 + 31 of a token-major bf16 array in LDS (row stride kp elements), by two transposing
+// reads: within each 16-lane group, lane s supplies row k0 + 4 j + s / 4 (+ 16) at column
+// n0 + 4 (s % 4), and lane m receives column n0 + m of the group's four rows.
+__device__ __forceinline__ bf16x8 tr_frag(const uint16_t* base, int kp, int k0, int n0, int j, int m) {
+    typedef short v4s __attribute__((ext_vector_type(4)));
+    typedef __attribute__((address_space(3))) v4s lds_v4s;
+    const int row = k0 + 4 * j + (m >> 2), col = n0 + 4 * (m & 3);
+    const v4s a = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4s*)(base + row * kp + col));
+    const v4s b = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4s*)(base + (row + 16) * kp + col));
+    return bf16x8{a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]};
+}
+
+// bf16 fragment with element e (k = k0 + kofs(j, e)) multiplied by sk[k] in fp32, rounded once
+__device__ __forceinline__ bf16x8 scale_frag(const bf16x8& f, const float* sk, int j) {
+    const float4 s0 = *reinterpret_cast<const float4*>(sk + 4 * j);
+    const float4 s1 = *reinterpret_cast<const float4*>(sk + 16 + 4 * j);
+    const float s[8] = {s0.x, s0.y, s0.z, s0.w, s1.x, s1.y, s1.z, s1.w};
+    float x[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) x[e] = bf2f((uint16_t)f[e]) * s[e];
+    return MM<BF16>::pack(x);
+}
+
 // ---------------------------------------------------------------------------------------------
 // the intra-chunk solve, shared by both kernels
 // ---------------------------------------------------------------------------------------------
@@ -498,8 +533,9 @@ __device__ __forceinline__ void intra_solve(unsigned char* smem, int band, int w
         }
     }
     __builtin_amdgcn_sched_barrier(0);
-    // rows to columns on the matrix core: tile st of d (value) tile dt, lane (j, n) holding
-    // rows 16 st + 4 j .. + 3 of column 16 dt + n
+    // rows to columns: tile st of d (value) tile dt, lane (j, n) holding rows 16 st + 4 j .. + 3
+    // of column 16 dt + n. K (bf16) with gfx950's transposing LDS reads, V (in registers) and
+    // fp32 K on the matrix core.
 #pragma unroll
     for (int t = 0; t < VPW; ++t) {
         const int dt = VPW * w + t;
@@ -507,15 +543,22 @@ __device__ __forceinline__ void intra_solve(unsigned char* smem, int band, int w
         f32x4 kc[4], vc[4];
 #pragma unroll
         for (int st = 0; st < 4; ++st) {
-            kc[st] = M::mma(row_frag_raw<E>(Kr + (16 * st + m) * KP, KB * (dt / FPD), j), sel, f32x4{0.f, 0.f, 0.f, 0.f});
+            if constexpr (sizeof(T) != 2)
+                kc[st] = M::mma(row_frag_raw<E>(Kr + (16 * st + m) * KP, KB * (dt / FPD), j), sel, f32x4{0.f, 0.f, 0.f, 0.f});
             vc[st] = M::mma(vf[VPW >= FPD ? t / FPD : 0][st], sel, f32x4{0.f, 0.f, 0.f, 0.f});
         }
 #pragma unroll
         for (int kt = 0; kt < NKT; ++kt) {
-            kbe[t][kt] = cols_frag<E>(&kc[FPD * kt], gt->nbe + KB * kt, j);
+            if constexpr (sizeof(T) == 2) {
+                const frag kr = tr_frag(Kr, KP, KB * kt, 16 * dt, j, m);
+                kbe[t][kt] = scale_frag(kr, gt->nbe + KB * kt, j);
+                if constexpr (OUT) st_frag(smem + L::O_KH + (size_t)(dt * NKT + kt) * C::FR, lane, scale_frag(kr, gt->kh + KB * kt, j));
+            } else {
+                kbe[t][kt] = cols_frag<E>(&kc[FPD * kt], gt->nbe + KB * kt, j);
+                if constexpr (OUT)
+                    st_frag(smem + L::O_KH + (size_t)(dt * NKT + kt) * C::FR, lane, cols_frag<E>(&kc[FPD * kt], gt->kh + KB * kt, j));
+            }
             vb[t][kt] = cols_frag<E>(&vc[FPD * kt], gt->b + KB * kt, j);
-            if constexpr (OUT)
-                st_frag(smem + L::O_KH + (size_t)(dt * NKT + kt) * C::FR, lane, cols_frag<E>(&kc[FPD * kt], gt->kh + KB * kt, j));
         }
     }
 #pragma unroll
@@ -624,6 +667,7 @@ __global__ __launch_bounds__(512) void map_kernel(PrefArgs a) {
         }
 
     Fetch<D, E, false, MC::NWP> fx;
+    bool zero = false;   // the composed transition is exactly zero (scalar)
     unsigned keep = 0;
     if (c1 - 1 - half >= c0) {
         keep = keep_chunk(a, bh, c1 - 1 - half);
@@ -771,18 +815,26 @@ __global__ __launch_bounds__(512) void map_kernel(PrefArgs a) {
         unsigned done = 1u;
 #pragma unroll
         for (int i = 0; i < MC::NWS; ++i) done &= zf[i];
-        if (__builtin_amdgcn_readfirstlane(done)) break;   // the same decision in every wave
+        if (__builtin_amdgcn_readfirstlane(done)) {   // the same decision in every wave
+            zero = true;
+            break;
+        }
     }
-    // Phi = Z^T as A operands (rows i = this wave's columns of Z, k = l) and Psi as tiles
+    // Phi = Z^T as A operands (rows i = this wave's columns of Z, k = l), unless it is zero (the
+    // flag says so and the pass over blocks does not read it), and Psi as tiles
     unsigned char* phi = ws_phi<D, E>(a, bh, b);
     f32x4* psi = ws_hs<D, E>(a, bh, b + 1);
+    if (threadIdx.x == 0) *ws_flag<D, E>(a, bh, b) = zero ? 0 : 1;
 #pragma unroll
     for (int t = 0; t < VPW; ++t) {
         const int it = VPW * w + t;
+        if (!zero) {
 #pragma unroll
-        for (int kd = 0; kd < NKD; ++kd) {
-            st_frag(phi + ((size_t)(it * NKD + kd) * C::NSPLIT) * C::FR, lane0, M::from_acc(Z[t], kd));
-            if constexpr (C::NSPLIT == 2) st_frag(phi + ((size_t)(it * NKD + kd) * 2 + 1) * C::FR, lane0, lo_from_acc<E>(Z[t], kd));
+            for (int kd = 0; kd < NKD; ++kd) {
+                st_frag(phi + ((size_t)(it * NKD + kd) * C::NSPLIT) * C::FR, lane0, M::from_acc(Z[t], kd));
+                if constexpr (C::NSPLIT == 2)
+                    st_frag(phi + ((size_t)(it * NKD + kd) * 2 + 1) * C::FR, lane0, lo_from_acc<E>(Z[t], kd));
+            }
         }
 #pragma unroll
         for (int vt = 0; vt < NDT; ++vt) psi[(it * NDT + vt) * 64 + lane0] = Psi[t][vt];
@@ -815,7 +867,19 @@ __global__ __launch_bounds__(256) void scan_kernel(PrefArgs a) {
             H[t][e] = a.h0 ? a.h0[((size_t)bh * D + 16 * lt + 4 * j + e) * D + 16 * vt + m] : 0.f;
         ws_hs<D, E>(a, bh, 0)[(lt * NDT + vt) * 64 + lane] = H[t];
     }
+    // A block whose map is zero leaves H_{b+1} = Psi_b, which its slot already holds: such blocks
+    // cost one flag read, and H is reloaded from the slot before the next block that needs it.
+    bool have = true;   // H holds H_b (scalar)
+    int steps = 0;      // products formed so far: the LDS buffer alternates with them
     for (int b = 0; b + 1 < a.NB; ++b) {
+        if (__builtin_amdgcn_readfirstlane(*ws_flag<D, E>(a, bh, b)) == 0) {
+            have = false;
+            continue;
+        }
+        if (!have) {
+#pragma unroll
+            for (int t = 0; t < VPW; ++t) H[t] = ws_hs<D, E>(a, bh, b)[((VPW * w + t) * NDT + vt) * 64 + lane];
+        }
         const unsigned char* phi = ws_phi<D, E>(a, bh, b);
         f32x4* slot = ws_hs<D, E>(a, bh, b + 1);
         // Psi_b and this wave's Phi_b operands first: they do not depend on H
@@ -830,7 +894,9 @@ __global__ __launch_bounds__(256) void scan_kernel(PrefArgs a) {
 #pragma unroll
                 for (int s = 0; s < NS; ++s) ph[t][kd][s] = ld_frag<frag>(phi + ((size_t)(it * NKD + kd) * NS + s) * 1024, lane);
         }
-        unsigned char* buf = hb + (size_t)(b & 1) * NKD * NS * 1024;
+        unsigned char* buf = hb + (size_t)(steps & 1) * NKD * NS * 1024;
+        ++steps;
+        have = true;
 #pragma unroll
         for (int t = 0; t < VPW; ++t) {
             const int lt = VPW * w + t;
@@ -1075,7 +1141,7 @@ static int device_cus() {
 }
 
 // bytes of workspace per slice for NB blocks (none for one block)
-static size_t ws_per_slice(int NB, int D) { return NB <= 1 ? 0 : (size_t)(2 * NB - 1) * 4 * D * D; }
+static size_t ws_per_slice(int NB, int D) { return NB <= 1 ? 0 : (size_t)(2 * NB - 1) * 4 * D * D + flag_bytes(NB); }
 
 // Blocks per slice: one where the slices alone give every CU a workgroup (the sequential pass per
 // head in one workgroup, no map work), else enough for about two output workgroups per CU, at

@@ -67,8 +67,10 @@ const char *gdn_status_string(int status);
  * block's affine state map (the composition of its chunks' maps S -> A S + B, SparseGDN article,
  * section on embedding the selector into FLA) is formed for all blocks in parallel, a short
  * sequential pass over the blocks gives every block's start state, and the blocks' outputs are
- * then formed in parallel. The workspace holds, per (batch, head), the maps of NB - 1 blocks and
- * NB block-start states: (2 NB - 1) * 4 * Dk * Dv bytes. The preferred NB gives about two
+ * then formed in parallel. The workspace holds, per (batch, head), the maps of NB - 1 blocks, NB
+ * block-start states and a flag per map (whether its transition is zero):
+ * (2 NB - 1) * 4 * Dk * Dv + F bytes, F = 4 (NB - 1) rounded up to a multiple of 256 (F = 0 for
+ * NB = 1). The preferred NB gives about two
  * output workgroups per compute unit of the current device (one block, i.e. no workspace, when
  * the (batch, head) slices alone give every compute unit one). Any workspace is accepted, none
  * included: the call uses the largest NB up to the preferred one whose bytes fit, and with no
@@ -124,7 +126,7 @@ int gdn_prefill_fwd(const void *q, const void *k, const void *v,
  * are bitwise those of gdn_prefill_fwd with a workspace of that size.
  * A scratch_bytes above GDN_PREFILL_NOALLOC_MAX_BYTES is rejected with GDN_ERR_SCRATCH before
  * anything is enqueued. On a 256-CU MI355X the preferred size of every shape fits (the largest,
- * at D = 128 and B*H = 255, is 79.7 MiB). The call allocates nothing: the first call on a
+ * at D = 128 and B*H = 255, is 79.8 MiB). The call allocates nothing: the first call on a
  * device looks up that device's copy of the array once (hipGetSymbolAddress).
  * Every call on one device shares that device's array and leaves the last call's contents in it;
  * nothing in it needs clearing (each call writes what it reads). Calls on one device whose work

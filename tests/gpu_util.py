@@ -49,5 +49,6 @@ TOL_F32 = 1e-4    # fp32 inputs
 def prefill_workspace(torch, B, H, D, nblocks):
     """A gated delta-rule prefill workspace that holds `nblocks` blocks per (batch, head): the call
     then uses that many blocks (at most its preferred count and one per chunk)."""
-    n = B * H * (2 * nblocks - 1) * 4 * D * D
+    flags = 0 if nblocks <= 1 else ((nblocks - 1) * 4 + 255) // 256 * 256
+    n = B * H * ((2 * nblocks - 1) * 4 * D * D + flags)
     return torch.empty(max(n, 1), dtype=torch.uint8, device="cuda")

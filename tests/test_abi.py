@@ -51,16 +51,18 @@ def test_prefill_timing_switch(lib):
 
 
 def test_workspace_size_query(lib):
-    """The prefill workspace holds (2 NB - 1) block records of 4 Dk Dv bytes per slice for NB blocks;
-    the preferred NB gives about two output workgroups per CU (256 CUs when no GPU answers)."""
+    """The prefill workspace holds (2 NB - 1) block records of 4 Dk Dv bytes per slice for NB blocks
+    and NB - 1 four-byte flags rounded up to 256 bytes; the preferred NB gives about two output
+    workgroups per CU (256 CUs when no GPU answers)."""
     f = lib.gdn_prefill_workspace_size
     rec = lambda d: 4 * d * d
     assert f(1, 1, 64, 128, 128, 0) == 0                  # one chunk: one block, no workspace
-    assert f(1, 1, 64 * 5, 128, 128, 0) == 9 * rec(128)     # five chunks, five blocks of one
+    assert f(1, 1, 64 * 5, 128, 128, 0) == 9 * rec(128) + 256     # five chunks, five blocks of one
     big = f(1, 16, 131072, 128, 128, 0)                    # 2048 chunks: 32 blocks of 64 per slice
-    assert big == 16 * (2 * 32 - 1) * rec(128)
-    assert f(1, 32, 32768, 128, 128, 0) == 32 * (2 * 16 - 1) * rec(128)
-    assert f(1, 16, 131072, 64, 64, 1) == 16 * (2 * 32 - 1) * rec(64)   # sizes do not depend on dtype
+    assert big == 16 * ((2 * 32 - 1) * rec(128) + 256)
+    assert f(1, 32, 32768, 128, 128, 0) == 32 * ((2 * 16 - 1) * rec(128) + 256)
+    assert f(1, 16, 131072, 64, 64, 1) == 16 * ((2 * 32 - 1) * rec(64) + 256)   # sizes do not depend on dtype
+    assert f(1, 1, 64 * 100, 128, 128, 0) == 199 * rec(128) + 512    # 100 blocks: 99 flags, 396 bytes
     assert f(2, 128, 4096, 128, 128, 0) == 0                # 256 slices fill the device alone
     assert f(1, 2, 0, 128, 128, 0) == 0
     assert f(1, 1, 64, 96, 96, 0) == 0        # unsupported head size

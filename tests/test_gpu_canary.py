@@ -66,7 +66,7 @@ def test_gdn_prefill_guard_bands(variant, dtype, D, gates):
     o = Guarded(d["v"].shape, TD[dtype])
     hf = Guarded(d["h0"].shape, torch.float32)
     nb = 4   # four blocks per slice: map, scan and output kernels all run
-    wsb = 3 * (2 * nb - 1) * 4 * D * D
+    wsb = 3 * ((2 * nb - 1) * 4 * D * D + 256)
     ws = Guarded((wsb,), torch.uint8)
     args = (d["q"], d["k"], d["v"], d["beta"], d["log_alpha"])
     keep = None

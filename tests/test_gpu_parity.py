@@ -374,5 +374,6 @@ def test_preferred_workspace_follows_the_device():
     once the (batch, head) slices alone give every CU one."""
     cus = torch.cuda.get_device_properties(0).multi_processor_count
     nb = -(-2 * cus // 16)
-    assert ops.prefill_workspace_size(1, 16, 131072, 128, torch.bfloat16) == 16 * (2 * nb - 1) * 4 * 128 * 128
+    flags = ((nb - 1) * 4 + 255) // 256 * 256
+    assert ops.prefill_workspace_size(1, 16, 131072, 128, torch.bfloat16) == 16 * ((2 * nb - 1) * 4 * 128 * 128 + flags)
     assert ops.prefill_workspace_size(1, cus, 4096, 128, torch.bfloat16) == 0
