@@ -1188,16 +1188,21 @@ int prefill_scratch(void** ptr) {
 // Optional per-kernel timing: HIP events recorded around each launch on the caller's stream.
 namespace {
 struct StageTimer {
+    struct Rec {
+        int stage, dev;
+        hipEvent_t begin, end;
+    };
     std::mutex mu;
     std::atomic<bool> on{false};
-    std::vector<hipEvent_t> pool;
-    std::vector<std::pair<int, std::pair<hipEvent_t, hipEvent_t>>> rec;   // (stage, (begin, end))
-    hipEvent_t get() {
-        if (!pool.empty()) {
-            hipEvent_t e = pool.back();
-            pool.pop_back();
-            return e;
-        }
+    std::vector<std::pair<int, hipEvent_t>> pool;   // (device, event): events belong to a device
+    std::vector<Rec> rec;
+    hipEvent_t get(int dev) {
+        for (size_t i = pool.size(); i-- > 0;)
+            if (pool[i].first == dev) {
+                hipEvent_t e = pool[i].second;
+                pool.erase(pool.begin() + (long)i);
+                return e;
+            }
         hipEvent_t e = nullptr;
         return hipEventCreate(&e) == hipSuccess ? e : nullptr;
     }
@@ -1216,12 +1221,19 @@ bool timed(int stage, hipStream_t s, F&& f) {
         return hipGetLastError() == hipSuccess;
     }
     std::lock_guard<std::mutex> g(t.mu);
-    hipEvent_t e0 = t.get(), e1 = t.get();
-    if (e0) (void)hipEventRecord(e0, s);
+    int dev = 0;
+    (void)hipGetDevice(&dev);
+    hipEvent_t e0 = t.get(dev), e1 = t.get(dev);
+    if (e0 && e1) (void)hipEventRecord(e0, s);
     f();
     const bool ok = hipGetLastError() == hipSuccess;
-    if (e1) (void)hipEventRecord(e1, s);
-    if (e0 && e1) t.rec.push_back({stage, {e0, e1}});
+    if (e0 && e1) {
+        (void)hipEventRecord(e1, s);
+        t.rec.push_back({stage, dev, e0, e1});
+    } else {   // an event could not be created: this launch goes untimed
+        if (e0) t.pool.push_back({dev, e0});
+        if (e1) t.pool.push_back({dev, e1});
+    }
     return ok;
 }
 }  // namespace
@@ -1236,13 +1248,11 @@ int prefill_kernel_times(float* ms, int* launches) {
     bool ok = true;
     for (auto& r : t.rec) {
         float x = 0.f;
-        if (hipEventSynchronize(r.second.second) != hipSuccess ||
-            hipEventElapsedTime(&x, r.second.first, r.second.second) != hipSuccess)
-            ok = false;
-        sum[r.first] += x;
-        cnt[r.first] += 1;
-        t.pool.push_back(r.second.first);
-        t.pool.push_back(r.second.second);
+        if (hipEventSynchronize(r.end) != hipSuccess || hipEventElapsedTime(&x, r.begin, r.end) != hipSuccess) ok = false;
+        sum[r.stage] += x;
+        cnt[r.stage] += 1;
+        t.pool.push_back({r.dev, r.begin});
+        t.pool.push_back({r.dev, r.end});
     }
     t.rec.clear();
     for (int i = 0; i < 3; ++i) {
