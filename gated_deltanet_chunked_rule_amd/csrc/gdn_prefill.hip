@@ -468,8 +468,8 @@ __device__ __forceinline__ void intra_solve(unsigned char* smem, int band, int w
     const bool do_p = OUT && (!SPLIT || w >= 4);
     constexpr int NST = !OUT && SPLIT ? 2 : 4;               // key tiles per wave
     const int st0 = !OUT && SPLIT ? 2 * (w >> 2) : 0;
-    // operands of row tiles rw (K) and rp (Q), and the gates of this lane's rows: r = 16 rw + 4 j + e
-    // in the Gram tiles (accumulator rows), r = 16 rp + m in the P^T tiles (accumulator columns)
+    // operands of row tiles rw (K) and rp (Q), and the gates of this lane's rows: r = 16 rw + m in
+    // the transposed Gram tiles and r = 16 rp + m in the P^T tiles (accumulator columns in both)
     frag kw[NKD], qw[NKD];
 #pragma unroll
     for (int kd = 0; kd < NKD; ++kd) {
@@ -477,9 +477,8 @@ __device__ __forceinline__ void intra_solve(unsigned char* smem, int band, int w
         if constexpr (OUT)
             if (do_p) qw[kd] = row_frag_raw<E>(Qr + (16 * rp + m) * KP, kd * KB, j);
     }
-    const float4 gr4 = *reinterpret_cast<const float4*>(gt->g + 16 * rw + 4 * j);
-    const int4 rho4 = *reinterpret_cast<const int4*>(gt->rho + 16 * rw + 4 * j);
-    const float4 b4 = *reinterpret_cast<const float4*>(gt->b + 16 * rw + 4 * j);
+    const float grw = gt->g[16 * rw + m], brw = gt->b[16 * rw + m];
+    const int rhow = gt->rho[16 * rw + m];
     const float grm = gt->g[16 * rp + m];
     const int rhom = gt->rho[16 * rp + m];
     f32x4 pt[4];
@@ -493,20 +492,22 @@ __device__ __forceinline__ void intra_solve(unsigned char* smem, int band, int w
 #pragma unroll
         for (int kd = 0; kd < NKD; ++kd) kf[kd] = row_frag_raw<E>(Kr + (16 * st + m) * KP, kd * KB, j);
         if (g_on) {
-            // Gram tile (rw, st): lane (j, n) holds k_r . k_s, r = 16 rw + 4 j + e, s = 16 st + n;
-            // A[r][s] = beta_r exp(g_r - g_s) k_r.k_s for s < r
+            // Gram tile (rw, st), transposed: lane (j, n) holds k_s . k_r at s = 16 st + 4 j + e,
+            // r = 16 rw + n, so that the four A[r][s] of a lane are adjacent in A's row r (one
+            // 16-byte store); A[r][s] = beta_r exp(g_r - g_s) k_r.k_s for s < r
             f32x4 g = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-            for (int kd = 0; kd < NKD; ++kd) g = M::mma(kw[kd], kf[kd], g);
-            const int s = 16 * st + m;
-            const float gs = gt->g[s];
-            const float rg[4] = {gr4.x, gr4.y, gr4.z, gr4.w}, rb[4] = {b4.x, b4.y, b4.z, b4.w};
-            const int rr[4] = {rho4.x, rho4.y, rho4.z, rho4.w};
+            for (int kd = 0; kd < NKD; ++kd) g = M::mma(kf[kd], kw[kd], g);
+            const int r = 16 * rw + m;
+            const float4 gs4 = *reinterpret_cast<const float4*>(gt->g + 16 * st + 4 * j);
+            const float gs[4] = {gs4.x, gs4.y, gs4.z, gs4.w};
+            float av[4];
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
-                const int r = 16 * rw + 4 * j + e;
-                Am[r * AS + s] = (s < r && s >= rr[e]) ? rb[e] * __expf(rg[e] - gs) * g[e] : 0.f;
+                const int s = 16 * st + 4 * j + e;
+                av[e] = (s < r && s >= rhow) ? brw * __expf(grw - gs[e]) * g[e] : 0.f;
             }
+            *reinterpret_cast<float4*>(Am + r * AS + 16 * st + 4 * j) = make_float4(av[0], av[1], av[2], av[3]);
         }
         if constexpr (OUT) {
             if (p_on) {
@@ -979,10 +980,25 @@ __global__ __launch_bounds__(512) void out_kernel(PrefArgs a) {
         fx.rq.store(Qr, n, tid);
         fx.rk.store(Kr, n, tid);
         if (w == 0) gate_scan(gt, fx.la, fx.bt, lane);
+        // the next chunk's K and Q rows and gates load while this whole chunk runs (their
+        // registers are free once stored); its V fragments follow once the solve has used this
+        // chunk's
+        const bool more = c + 1 < c1;
+        if (more) {
+            fx.start(a, bh, c + 1);
+            fx.load_gates(a, tid);
+            fx.load_k(a, tid);
+            fx.load_q(a, tid);
+        }
         lds_sync();
         const unsigned keep = SKIP ? keep_chunk(a, bh, c) : 1u;
         frag kbe[VPW][NKT], vb[VPW][NKT];
+        // The solve up to W and Ut is this workgroup's serial path; the other workgroup on the CU
+        // is usually in its matrix-heavy state phase then. A higher wave priority lets the solve's
+        // dependent steps issue first, and the state phase takes the idle cycles between them.
+        __builtin_amdgcn_s_setprio(2);
         intra_solve<D, E, true, C::NW>(smem, a.band, w, lane, fx.vf, kbe, vb);
+        if (more) fx.load_v(a, tid, w);
         // -W fragments [rt][kd] (A: rows token, k = d), each d tile filling its part, and Ut
         f32x4 U[VPW][4];
         {
@@ -1015,15 +1031,7 @@ __global__ __launch_bounds__(512) void out_kernel(PrefArgs a) {
                 }
         }
         lds_sync();
-        // the next chunk's rows and gates load while this one's chain step runs (the solve's
-        // registers are free by now), spread over its phases so that no phase waits long to
-        // issue its loads
-        const bool more = c + 1 < c1;
-        if (more) {
-            fx.start(a, bh, c + 1);
-            fx.load_gates(a, tid);
-            fx.load_k(a, tid);
-        }
+        __builtin_amdgcn_s_setprio(0);
         const float dec = gt->dec;
         // U = Ut - W H
         frag Hf[VPW][NKD];
@@ -1044,7 +1052,6 @@ __global__ __launch_bounds__(512) void out_kernel(PrefArgs a) {
         for (int t = 0; t < VPW; ++t)
 #pragma unroll
             for (int kt = 0; kt < NKT; ++kt) Uf[t][kt] = M::from_acc(U[t], kt);
-        if (more) fx.load_q(a, tid);
         // O^T = e^g (H^T Q^T) + U^T P^T, lane (j, n): O[16 rt + n][16 vt + 4 j .. + 3], and
         // H <- e^{g_C} H + Khat^T U (H itself is no longer read: the products use Hf). The two
         // are interleaved, two value tiles of the update per output tile, so that the update's
@@ -1110,7 +1117,6 @@ __global__ __launch_bounds__(512) void out_kernel(PrefArgs a) {
         } else {
             out_and_update(std::true_type{});
         }
-        if (more) fx.load_v(a, tid, w);
         lds_sync();   // the chunk's LDS is free for the next one
     }
     if (b == a.NB - 1) {
