@@ -667,6 +667,18 @@ __global__ __launch_bounds__(512) void map_kernel(PrefArgs a) {
             for (int e = 0; e < 4; ++e) Z[t][lt][e] = (16 * lt + 4 * j0 + e == 16 * (VPW * w + t) + m0) ? 1.f : 0.f;
         }
 
+    // whether this wave's columns of Z are all exactly zero (the same answer in every lane)
+    auto z_zero = [&]() {
+        unsigned nz = 0;
+#pragma unroll
+        for (int t = 0; t < VPW; ++t)
+#pragma unroll
+            for (int lt = 0; lt < NDT; ++lt)
+#pragma unroll
+                for (int e = 0; e < 4; ++e) nz |= __float_as_uint(Z[t][lt][e]) & 0x7fffffffu;
+        return __builtin_amdgcn_ballot_w64(nz != 0u) == 0;
+    };
+
     Fetch<D, E, false, MC::NWP> fx;
     bool zero = false;   // the composed transition is exactly zero (scalar)
     unsigned keep = 0;
@@ -737,6 +749,10 @@ __global__ __launch_bounds__(512) void map_kernel(PrefArgs a) {
 #pragma unroll
         for (int p = 0; p < NH; ++p) {
             if (c - p < c0) break;   // scalar
+            // A wave's step touches only its columns of Z and its rows of Psi; once those columns
+            // are exactly zero, Y's columns are zero and the step leaves both as they are (with
+            // strong decay, the pair's second step after the first has underflowed Z).
+            if (p > 0 && z_zero()) continue;
             const unsigned char* sl = smem + (size_t)p * SLOT;
             const T* Ks = reinterpret_cast<const T*>(sl + L::O_K);
             const Gates* gs = reinterpret_cast<const Gates*>(sl + L::O_G);
@@ -803,14 +819,7 @@ __global__ __launch_bounds__(512) void map_kernel(PrefArgs a) {
         // (each of their steps multiplies Z), so the block's map is complete. With strong decay
         // this happens after a chunk or two: the product of a chunk's gates falls below fp32's
         // smallest subnormal.
-        unsigned nz = 0;
-#pragma unroll
-        for (int t = 0; t < VPW; ++t)
-#pragma unroll
-            for (int lt = 0; lt < NDT; ++lt)
-#pragma unroll
-                for (int e = 0; e < 4; ++e) nz |= __float_as_uint(Z[t][lt][e]) & 0x7fffffffu;
-        const bool wzero = __builtin_amdgcn_ballot_w64(nz != 0u) == 0;
+        const bool wzero = z_zero();
         if (lane0 == 0) zf[w] = wzero ? 1u : 0u;
         lds_sync();   // the slots are free for the next chunks
         unsigned done = 1u;
