@@ -265,7 +265,9 @@ __device__ __forceinline__ f32x4 scale4(const f32x4& t, float s) { return f32x4{
 // Q and K rows for LDS (Q only for the output kernel), the wave's own value tiles of V as row
 // fragments straight from memory (only its own tiles are transposed, so V never goes through
 // LDS), and for wave 0 the gates. Loads go through buffer resources over the chunk's valid
-// tokens: rows past the end of the sequence read as zero.
+// tokens: rows past the end of the sequence read as zero. A bf16 V fragment holds 8 adjacent
+// columns per lane (one 16-byte load): lane (j, m) takes row m at columns 8 j .. 8 j + 7 of its
+// 32-column group, the order v_unit_cols transposes.
 template <int D, class E, bool OUT, int NW>
 struct Fetch {
     using C = Cfg<D, E, NW>;
@@ -296,11 +298,11 @@ struct Fetch {
         for (int gi = 0; gi < NGW; ++gi)
 #pragma unroll
             for (int st = 0; st < 4; ++st) {
-                const int e0 = (16 * st + m) * D + (g0 + gi) * C::KB + 4 * j;   // element offset
                 if constexpr (sizeof(T) == 2) {
-                    const uint2 x = buffer_load8(rv, e0 * 2), y = buffer_load8(rv, (e0 + 16) * 2);
-                    vf[gi][st] = __builtin_bit_cast(frag, uint4{x.x, x.y, y.x, y.y});
+                    const int e0 = (16 * st + m) * D + (g0 + gi) * C::KB + 8 * j;   // element offset
+                    vf[gi][st] = __builtin_bit_cast(frag, buffer_load16(rv, e0 * 2));
                 } else {
+                    const int e0 = (16 * st + m) * D + (g0 + gi) * C::KB + 4 * j;
                     vf[gi][st] = __builtin_bit_cast(frag, buffer_load16(rv, e0 * 4));
                 }
             }
@@ -425,6 +427,16 @@ __device__ __forceinline__ bf16x8 scale_frag(const bf16x8& f, const float* sk, i
     return MM<BF16>::pack(x);
 }
 
+// B operand that transposes a bf16 V fragment of Fetch::load_v on the matrix core: element e of
+// lane (j, n) is 1 where 8 j + e = n + 16 q, so the product lands columns 16 q .. 16 q + 15 of
+// the fragment's 32-column group in an accumulator tile (exact: one nonzero term per output).
+__device__ __forceinline__ bf16x8 v_unit_cols(int j, int n, int q) {
+    float x[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) x[e] = 8 * j + e == n + 16 * q ? 1.f : 0.f;
+    return MM<BF16>::pack(x);
+}
+
 // ---------------------------------------------------------------------------------------------
 // the intra-chunk solve, shared by both kernels
 // ---------------------------------------------------------------------------------------------
@@ -540,7 +552,9 @@ __device__ __forceinline__ void intra_solve(unsigned char* smem, int band, int w
 #pragma unroll
     for (int t = 0; t < VPW; ++t) {
         const int dt = VPW * w + t;
-        const frag sel = unit_cols<E>(j, m, dt % FPD);
+        frag sel;
+        if constexpr (sizeof(T) == 2) sel = v_unit_cols(j, m, dt % FPD);
+        else sel = unit_cols<E>(j, m, dt % FPD);
         f32x4 kc[4], vc[4];
 #pragma unroll
         for (int st = 0; st < 4; ++st) {
@@ -991,7 +1005,7 @@ __global__ __launch_bounds__(512) void out_kernel(PrefArgs a) {
         if (w == 0) gate_scan(gt, fx.la, fx.bt, lane);
         // the next chunk's K and Q rows and gates load while this whole chunk runs (their
         // registers are free once stored); its V fragments follow once the solve has used this
-        // chunk's
+        // chunk's (after W and Ut)
         const bool more = c + 1 < c1;
         if (more) {
             fx.start(a, bh, c + 1);
@@ -1007,7 +1021,6 @@ __global__ __launch_bounds__(512) void out_kernel(PrefArgs a) {
         // dependent steps issue first, and the state phase takes the idle cycles between them.
         __builtin_amdgcn_s_setprio(2);
         intra_solve<D, E, true, C::NW>(smem, a.band, w, lane, fx.vf, kbe, vb);
-        if (more) fx.load_v(a, tid, w);
         // -W fragments [rt][kd] (A: rows token, k = d), each d tile filling its part, and Ut
         f32x4 U[VPW][4];
         {
@@ -1041,6 +1054,7 @@ __global__ __launch_bounds__(512) void out_kernel(PrefArgs a) {
         }
         lds_sync();
         __builtin_amdgcn_s_setprio(0);
+        if (more) fx.load_v(a, tid, w);   // apart from the burst of K and Q loads at the top
         const float dec = gt->dec;
         // U = Ut - W H
         frag Hf[VPW][NKD];
