@@ -87,7 +87,7 @@ __global__ __launch_bounds__(256) void la_kv_kernel(const typename E::T* __restr
     using M = MM<E>;
     using C = LaCfg<D, E>;
     using frag = typename M::frag;
-    constexpr int NDT = C::NDT, NKT = C::NKT, FPD = C::FPD, DW = C::DW;
+    constexpr int KB = C::KB, NDT = C::NDT, NKT = C::NKT, FPD = C::FPD, DW = C::DW;
     extern __shared__ __align__(16) unsigned char smem[];
     T* Kr = reinterpret_cast<T*>(smem);                                   // [CH][KP]
     T* Vr = reinterpret_cast<T*>(smem + C::ROWS);                         // [CH][KP]
@@ -136,15 +136,24 @@ __global__ __launch_bounds__(256) void la_kv_kernel(const typename E::T* __restr
 #pragma unroll
         for (int i = 0; i < DW; ++i) {
             const int dt = DW * w + i;
-            f32x4 t[4];
-            col_tiles<D, E>(Kr, dt, j, m, t);
+            if constexpr (sizeof(T) == 2) {   // bf16: gfx950's transposing LDS reads
 #pragma unroll
-            for (int kt = 0; kt < NKT; ++kt)
-                st_frag(sKf + (size_t)(dt * NKT + kt) * 1024, lane,
-                        GATED ? cols_frag<E>(&t[FPD * kt], skh + 16 * FPD * kt, j) : cols_frag<E>(&t[FPD * kt]));
-            col_tiles<D, E>(Vr, dt, j, m, t);
+                for (int kt = 0; kt < NKT; ++kt) {
+                    const frag kr = tr_frag(Kr, C::KP, KB * kt, 16 * dt, j, m);
+                    st_frag(sKf + (size_t)(dt * NKT + kt) * 1024, lane, GATED ? scale_frag(kr, skh + KB * kt, j) : kr);
+                    vf[i][kt] = tr_frag(Vr, C::KP, KB * kt, 16 * dt, j, m);
+                }
+            } else {   // fp32: transposed on the matrix core
+                f32x4 t[4];
+                col_tiles<D, E>(Kr, dt, j, m, t);
 #pragma unroll
-            for (int kt = 0; kt < NKT; ++kt) vf[i][kt] = cols_frag<E>(&t[FPD * kt]);
+                for (int kt = 0; kt < NKT; ++kt)
+                    st_frag(sKf + (size_t)(dt * NKT + kt) * 1024, lane,
+                            GATED ? cols_frag<E>(&t[FPD * kt], skh + 16 * FPD * kt, j) : cols_frag<E>(&t[FPD * kt]));
+                col_tiles<D, E>(Vr, dt, j, m, t);
+#pragma unroll
+                for (int kt = 0; kt < NKT; ++kt) vf[i][kt] = cols_frag<E>(&t[FPD * kt]);
+            }
         }
         lds_sync();
         if constexpr (GATED) {
@@ -278,15 +287,24 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void l
 #pragma unroll
         for (int i = 0; i < DW; ++i) {
             const int dt = DW * w + i;
-            f32x4 t[4];
-            col_tiles<D, E>(Kr, dt, j, m, t);
+            if constexpr (sizeof(T) == 2) {   // bf16: gfx950's transposing LDS reads
 #pragma unroll
-            for (int kt = 0; kt < NKT; ++kt)
-                st_frag(sKf + (size_t)(dt * NKT + kt) * 1024, lane,
-                        GATED ? cols_frag<E>(&t[FPD * kt], skh + 16 * FPD * kt, j) : cols_frag<E>(&t[FPD * kt]));
-            col_tiles<D, E>(Vr, dt, j, m, t);
+                for (int kt = 0; kt < NKT; ++kt) {
+                    const frag kr = tr_frag(Kr, C::KP, KB * kt, 16 * dt, j, m);
+                    st_frag(sKf + (size_t)(dt * NKT + kt) * 1024, lane, GATED ? scale_frag(kr, skh + KB * kt, j) : kr);
+                    vf[i][kt] = tr_frag(Vr, C::KP, KB * kt, 16 * dt, j, m);
+                }
+            } else {   // fp32: transposed on the matrix core
+                f32x4 t[4];
+                col_tiles<D, E>(Kr, dt, j, m, t);
 #pragma unroll
-            for (int kt = 0; kt < NKT; ++kt) vf[i][kt] = cols_frag<E>(&t[FPD * kt]);
+                for (int kt = 0; kt < NKT; ++kt)
+                    st_frag(sKf + (size_t)(dt * NKT + kt) * 1024, lane,
+                            GATED ? cols_frag<E>(&t[FPD * kt], skh + 16 * FPD * kt, j) : cols_frag<E>(&t[FPD * kt]));
+                col_tiles<D, E>(Vr, dt, j, m, t);
+#pragma unroll
+                for (int kt = 0; kt < NKT; ++kt) vf[i][kt] = cols_frag<E>(&t[FPD * kt]);
+            }
         }
         // P^T for token tile rt = w: lane (j, n) of t[st] holds k_s . q_r, s = 16 st + 4 j + e,
         // r = 16 w + n, kept for s <= r and gated by e^{g_r - g_s}
@@ -445,6 +463,18 @@ struct GateScan {
     }
 };
 
+// Khat^T fragment (k = token s = s0 + kofs(j, e), column d = 16 dt + m) of a per-key-dimension
+// gated chunk from K's transposed bf16 fragment: k_s[d] e^{G_C[d] - G_s[d]} (gcd = G_C[d], sG the
+// cumulative gates, row stride GS), multiplied in fp32 and rounded once.
+template <int D, int GS>
+__device__ __forceinline__ bf16x8 khat_frag(const bf16x8& kr, const float* sG, float gcd, int s0, int dt, int j, int m) {
+    float x[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e)
+        x[e] = bf2f((uint16_t)kr[e]) * __expf(gcd - sG[(s0 + MM<BF16>::kofs(j, e)) * GS + 16 * dt + m]);
+    return MM<BF16>::pack(x);
+}
+
 // Fragment of row rp (k = d, the row_frag_raw order) with element d scaled by exp(gp[d] - gq[d])
 // (gq == nullptr: exp(gp[d])).
 template <class E>
@@ -578,18 +608,27 @@ __global__ __launch_bounds__(256) void gla_kv_kernel(const typename E::T* __rest
 #pragma unroll
         for (int i = 0; i < DW; ++i) {
             const int dt = DW * w + i;
-            f32x4 t[4];
-            col_tiles<D, E>(Kr, dt, j, m, t);
             const float gcd = gC[16 * dt + m];
+            if constexpr (sizeof(T) == 2) {   // bf16: gfx950's transposing LDS reads
 #pragma unroll
-            for (int st = 0; st < 4; ++st)
+                for (int kt = 0; kt < NKT; ++kt) {
+                    st_frag(sKf + (size_t)(dt * NKT + kt) * 1024, lane,
+                            khat_frag<D, GS>(tr_frag(Kr, C::KP, C::KB * kt, 16 * dt, j, m), sG, gcd, C::KB * kt, dt, j, m));
+                    vf[i][kt] = tr_frag(Vr, C::KP, C::KB * kt, 16 * dt, j, m);
+                }
+            } else {
+                f32x4 t[4];
+                col_tiles<D, E>(Kr, dt, j, m, t);
 #pragma unroll
-                for (int e = 0; e < 4; ++e) t[st][e] *= __expf(gcd - sG[(16 * st + 4 * j + e) * GS + 16 * dt + m]);
+                for (int st = 0; st < 4; ++st)
 #pragma unroll
-            for (int kt = 0; kt < NKT; ++kt) st_frag(sKf + (size_t)(dt * NKT + kt) * 1024, lane, cols_frag<E>(&t[FPD * kt]));
-            col_tiles<D, E>(Vr, dt, j, m, t);
+                    for (int e = 0; e < 4; ++e) t[st][e] *= __expf(gcd - sG[(16 * st + 4 * j + e) * GS + 16 * dt + m]);
 #pragma unroll
-            for (int kt = 0; kt < NKT; ++kt) vf[i][kt] = cols_frag<E>(&t[FPD * kt]);
+                for (int kt = 0; kt < NKT; ++kt) st_frag(sKf + (size_t)(dt * NKT + kt) * 1024, lane, cols_frag<E>(&t[FPD * kt]));
+                col_tiles<D, E>(Vr, dt, j, m, t);
+#pragma unroll
+                for (int kt = 0; kt < NKT; ++kt) vf[i][kt] = cols_frag<E>(&t[FPD * kt]);
+            }
         }
         lds_sync();
         // S = diag(e^{G_C}) S + Khat^T V; tile (dt, .) rows 16 dt + 4 j + e
@@ -712,10 +751,15 @@ __global__ __launch_bounds__(64 * NW) void gla_out_kernel(
         frag vf[DW][NKT];
 #pragma unroll
         for (int i = 0; i < DW; ++i) {
-            f32x4 t[4];
-            col_tiles<D, E>(Vr, DW * w + i, j, m, t);
+            if constexpr (sizeof(T) == 2) {   // bf16: gfx950's transposing LDS reads
 #pragma unroll
-            for (int kt = 0; kt < NKT; ++kt) vf[i][kt] = cols_frag<E>(&t[FPD * kt]);
+                for (int kt = 0; kt < NKT; ++kt) vf[i][kt] = tr_frag(Vr, KP, KB * kt, 16 * (DW * w + i), j, m);
+            } else {
+                f32x4 t[4];
+                col_tiles<D, E>(Vr, DW * w + i, j, m, t);
+#pragma unroll
+                for (int kt = 0; kt < NKT; ++kt) vf[i][kt] = cols_frag<E>(&t[FPD * kt]);
+            }
         }
         lds_sync();
         if (gsc.tile_span_over(GLA_WIDE)) s_wide[c & 1] = 1u;
@@ -729,15 +773,22 @@ __global__ __launch_bounds__(64 * NW) void gla_out_kernel(
 #pragma unroll
         for (int i = 0; i < DW; ++i) {
             const int dt = DW * w + i;
-            f32x4 t[4];
-            col_tiles<D, E>(Kr, dt, j, m, t);
             const float gcd = gC[16 * dt + m];
+            if constexpr (sizeof(T) == 2) {   // bf16: gfx950's transposing LDS reads
 #pragma unroll
-            for (int st = 0; st < 4; ++st)
+                for (int kt = 0; kt < NKT; ++kt)
+                    st_frag(sKf + (size_t)(dt * NKT + kt) * 1024, lane,
+                            khat_frag<D, GS>(tr_frag(Kr, KP, KB * kt, 16 * dt, j, m), sG, gcd, KB * kt, dt, j, m));
+            } else {
+                f32x4 t[4];
+                col_tiles<D, E>(Kr, dt, j, m, t);
 #pragma unroll
-                for (int e = 0; e < 4; ++e) t[st][e] *= __expf(gcd - sG[(16 * st + 4 * j + e) * GS + 16 * dt + m]);
+                for (int st = 0; st < 4; ++st)
 #pragma unroll
-            for (int kt = 0; kt < NKT; ++kt) st_frag(sKf + (size_t)(dt * NKT + kt) * 1024, lane, cols_frag<E>(&t[FPD * kt]));
+                    for (int e = 0; e < 4; ++e) t[st][e] *= __expf(gcd - sG[(16 * st + 4 * j + e) * GS + 16 * dt + m]);
+#pragma unroll
+                for (int kt = 0; kt < NKT; ++kt) st_frag(sKf + (size_t)(dt * NKT + kt) * 1024, lane, cols_frag<E>(&t[FPD * kt]));
+            }
         }
         // P^T of token tile rt = w % 4, key tiles [SPW h, SPW h + SPW) (h = w / 4): lane (j, n) of
         // t[st] holds sum_d k_s[d] q_r[d] e^{G_r[d] - G_s[d]}, s = 16 st + 4 j + e, r = 16 rt + n,

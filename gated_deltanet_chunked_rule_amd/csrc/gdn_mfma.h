@@ -170,4 +170,28 @@ __device__ __forceinline__ typename MM<E>::frag cols_frag(const f32x4* t) {
     return M::pack(x);
 }
 
+// Operand fragment (k = token, in the fragment k-order) of columns n0 .. n0 + 15 and tokens
+// k0 .. k0 + 31 of a token-major bf16 array in LDS (row stride kp elements), by two transposing
+// reads: within each 16-lane group, lane s supplies row k0 + 4 j + s / 4 (+ 16) at column
+// n0 + 4 (s % 4), and lane m receives column n0 + m of the group's four rows.
+__device__ __forceinline__ bf16x8 tr_frag(const uint16_t* base, int kp, int k0, int n0, int j, int m) {
+    typedef short v4s __attribute__((ext_vector_type(4)));
+    typedef __attribute__((address_space(3))) v4s lds_v4s;
+    const int row = k0 + 4 * j + (m >> 2), col = n0 + 4 * (m & 3);
+    const v4s a = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4s*)(base + row * kp + col));
+    const v4s b = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4s*)(base + (row + 16) * kp + col));
+    return bf16x8{a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]};
+}
+
+// bf16 fragment with element e (k = k0 + kofs(j, e)) multiplied by sk[k] in fp32, rounded once
+__device__ __forceinline__ bf16x8 scale_frag(const bf16x8& f, const float* sk, int j) {
+    const float4 s0 = *reinterpret_cast<const float4*>(sk + 4 * j);
+    const float4 s1 = *reinterpret_cast<const float4*>(sk + 16 + 4 * j);
+    const float s[8] = {s0.x, s0.y, s0.z, s0.w, s1.x, s1.y, s1.z, s1.w};
+    float x[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) x[e] = bf2f((uint16_t)f[e]) * s[e];
+    return MM<BF16>::pack(x);
+}
+
 }  // namespace gdn
