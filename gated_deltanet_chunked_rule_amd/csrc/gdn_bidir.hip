@@ -10,9 +10,9 @@
 // Three kernels, all on the matrix cores:
 //   1. bidir_kv_kernel: one workgroup per (block of chunks, head) sums phi(K)^T V over its
 //      chunks. The products contract over tokens, so both operands need fragments whose k index
-//      is the token: K and V rows are staged in LDS and turned into columns by one MFMA per
-//      16 x 16 tile against a unit-column fragment (the same exact transpose the GDN prep stage
-//      uses). Each wave transposes a quarter of the key dimensions and publishes them in LDS, and
+//      is the token: K and V rows are staged in LDS and read as columns by gfx950's transposing
+//      LDS reads (bf16), or turned into columns by one MFMA per 16 x 16 tile against a
+//      unit-column fragment (fp32, an exact transpose). Each wave transposes a quarter of the key dimensions and publishes them in LDS, and
 //      transposes its own value tiles, which it keeps; it owns the KV tiles of its value columns.
 //      The per-block sums (and key sums) go to the workspace in accumulator-tile layout.
 //   2. bidir_reduce_kernel: one wave per KV operand fragment sums the blocks' tiles in a fixed
@@ -168,15 +168,31 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(sizeof(type
 #pragma unroll
         for (int i = 0; i < DW; ++i) {
             const int dt = DW * w + i;
-            f32x4 t[4];
-            tiles(Kr, dt, t);
+            if constexpr (sizeof(T) == 2) {
+                // bf16: gfx950's transposing LDS reads; fragment kt's elements 0-3 and 4-7 are the
+                // lane's tokens of 16-token tiles 2 kt and 2 kt + 1, summed in that tile order
 #pragma unroll
-            for (int st = 0; st < 4; ++st) ksp[i] += (t[st][0] + t[st][1]) + (t[st][2] + t[st][3]);
+                for (int kt = 0; kt < NKT; ++kt) {
+                    const frag kr = tr_frag(Kr, KP, KB * kt, 16 * dt, j, m);
+                    float x[8];
 #pragma unroll
-            for (int kt = 0; kt < NKT; ++kt) st_frag(sKf + (size_t)(dt * NKT + kt) * 1024, lane, cols_frag<E>(&t[FPD * kt]));
-            tiles(Vr, dt, t);
+                    for (int e = 0; e < 8; ++e) x[e] = bf2f((uint16_t)kr[e]);
+                    ksp[i] += (x[0] + x[1]) + (x[2] + x[3]);
+                    ksp[i] += (x[4] + x[5]) + (x[6] + x[7]);
+                    st_frag(sKf + (size_t)(dt * NKT + kt) * 1024, lane, kr);
+                    vf[i][kt] = tr_frag(Vr, KP, KB * kt, 16 * dt, j, m);
+                }
+            } else {   // fp32: transposed on the matrix core
+                f32x4 t[4];
+                tiles(Kr, dt, t);
 #pragma unroll
-            for (int kt = 0; kt < NKT; ++kt) vf[i][kt] = cols_frag<E>(&t[FPD * kt]);
+                for (int st = 0; st < 4; ++st) ksp[i] += (t[st][0] + t[st][1]) + (t[st][2] + t[st][3]);
+#pragma unroll
+                for (int kt = 0; kt < NKT; ++kt) st_frag(sKf + (size_t)(dt * NKT + kt) * 1024, lane, cols_frag<E>(&t[FPD * kt]));
+                tiles(Vr, dt, t);
+#pragma unroll
+                for (int kt = 0; kt < NKT; ++kt) vf[i][kt] = cols_frag<E>(&t[FPD * kt]);
+            }
         }
         lds_sync();
         // KV tiles (dt, value tile) += phi(K)^T[dt rows][tokens] V[tokens][value columns]
