@@ -1,6 +1,7 @@
 // Row staging and small wave / workgroup helpers shared by the linear-attention kernels
 // (causal and bidirectional). gfx950 only; 64-lane wavefronts, 256-thread workgroups unless stated.
 #pragma once
+#include <type_traits>
 #include "gdn_mfma.h"
 
 namespace gdn {
@@ -84,19 +85,28 @@ struct RowRegs {
         for (int i = 0; i < N; ++i) x[i] = buffer_load16(rs, (tid + NT * i) * 16);
     }
     // into LDS with row stride row_stride<D, E>() (rows 8-byte aligned: two 8-byte stores per
-    // 16 bytes), f applied to rows [0, n), the others zero (masked, not branched, so that the
-    // loads still in flight are not drained here)
+    // 16 bytes), f applied to rows [0, n), the others zero. Unit u = tid + NT i is row u / UPR,
+    // column unit u % UPR; NT is a multiple of UPR, so step i moves NT / UPR rows down from one
+    // base address. Rows past n already hold zeros (their loads were out of range); only a
+    // transform f, which need not map zero to zero, needs the mask (masked, not branched, so that
+    // the loads still in flight are not drained here).
     template <class F = AsIs>
     __device__ __forceinline__ void store(typename E::T* dst, int n, int tid, F f = F()) const {
         constexpr int KP = row_stride<D, E>();
+        static_assert(NT % UPR == 0, "whole rows per step");
+        constexpr bool MASK = !std::is_same<F, AsIs>::value;
+        const unsigned ut = (unsigned)tid, r0 = ut / UPR;
+        typename E::T* base = dst + r0 * KP + (ut % UPR) * EPU;
 #pragma unroll
         for (int i = 0; i < N; ++i) {
-            const int u = tid + NT * i, r = u / UPR, cu = u % UPR;
-            const unsigned keep = 0u - (unsigned)(r < n);
-            const uint4 y = f(x[i]);
-            uint2* d = reinterpret_cast<uint2*>(dst + r * KP + cu * EPU);
-            d[0] = uint2{y.x & keep, y.y & keep};
-            d[1] = uint2{y.z & keep, y.w & keep};
+            uint4 y = f(x[i]);
+            if constexpr (MASK) {
+                const unsigned keep = 0u - (unsigned)((int)(r0 + (NT / UPR) * i) < n);
+                y = uint4{y.x & keep, y.y & keep, y.z & keep, y.w & keep};
+            }
+            uint2* d = reinterpret_cast<uint2*>(base + (NT / UPR) * i * KP);
+            d[0] = uint2{y.x, y.y};
+            d[1] = uint2{y.z, y.w};
         }
     }
 };
