@@ -868,11 +868,19 @@ __global__ __launch_bounds__(256) void scan_kernel(PrefArgs a) {
         ws_hs<D, E>(a, bh, 0)[(lt * NDT + vt) * 64 + lane] = H[t];
     }
     // A block whose map is zero leaves H_{b+1} = Psi_b, which its slot already holds: such blocks
-    // cost one flag read, and H is reloaded from the slot before the next block that needs it.
+    // are skipped, and H is reloaded from the slot before the next block that needs it. The flags
+    // of 64 blocks at a time come in one load (lane i takes block b0 + i) and one ballot, so the
+    // pass does not wait on one flag read per block.
     bool have = true;   // H holds H_b (scalar)
     int steps = 0;      // products formed so far: the LDS buffer alternates with them
+    unsigned long long live = 0;   // nonzero flags of blocks b0 .. b0 + 63 (bit i: block b0 + i)
     for (int b = 0; b + 1 < a.NB; ++b) {
-        if (__builtin_amdgcn_readfirstlane(*ws_flag<D, E>(a, bh, b)) == 0) {
+        if ((b & 63) == 0) {
+            const int nf = min(64, a.NB - 1 - b);
+            const __amdgpu_buffer_rsrc_t rf = buffer_rsrc(ws_flag<D, E>(a, bh, b), nf * 4);
+            live = __builtin_amdgcn_ballot_w64(buffer_load4(rf, lane * 4) != 0u);
+        }
+        if (((live >> (b & 63)) & 1ull) == 0) {
             have = false;
             continue;
         }
