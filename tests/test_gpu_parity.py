@@ -233,6 +233,65 @@ def test_zero_gates_reset_the_state(dtype):
         _check(host(o), host(hf), ro, rh, tol, f"{nb} blocks")
 
 
+def test_map_waves_with_zero_columns():
+    """A zero gate on a block's last token with that token's key zero in key dimensions 0-15 (the
+    columns of Z that the map's first wave holds, at d = 128 in bf16): after the block's last
+    chunk only that wave's columns of Z are exactly zero, so it alone skips the second chunk of
+    the pair while the other waves apply it. Head 1 zeroes dimensions 16-47 instead (two waves).
+    Three blocks of four chunks against the oracle and against the one-block sequential pass."""
+    cfg = inputs.GDN_32K.with_(name="map_zero_columns", B=1, H=2, L=64 * 12, seed=47, gate_dist="long")
+    say(f"case {cfg.name}")
+    x = inputs.prefill_inputs(cfg)
+    la, kk = x["log_alpha"].copy(), x["k"].copy()
+    for c in (3, 7, 11):   # the last chunk of each block of four
+        t = 64 * c + 63
+        la[0, :, t] = -np.inf
+        kk[0, 0, t, 0:16] = 0.0
+        kk[0, 1, t, 16:48] = 0.0
+    x["log_alpha"], x["k"] = la, kk
+    q, k, v = (dev_tensor(x[n], torch.bfloat16) for n in ("q", "k", "v"))
+    h0 = dev_tensor(x["h0"], torch.float32)
+    beta, lad = dev_tensor(x["beta"], torch.float32), dev_tensor(la, torch.float32)
+    ro, rh = _oracle(x)
+    res = {}
+    for nb in (1, 3):
+        ws = prefill_workspace(torch, 1, 2, 128, nb) if nb > 1 else None
+        o, hf = ops.gdn_prefill_fwd(q, k, v, beta, lad, h0, workspace=ws)
+        torch.cuda.synchronize()
+        res[nb] = (host(o), host(hf))
+        _check(res[nb][0], res[nb][1], ro, rh, TOL_BF16, f"{nb} blocks")
+    # the split changes only the order of fp32 sums
+    assert max_rel_err(res[3][0], res[1][0]) <= 1e-2 and max_rel_err(res[3][1], res[1][1]) <= 1e-2
+
+
+def test_many_blocks_mixed_maps():
+    """70 blocks of two chunks in one slice, every third block with long-memory gates (its map is
+    not zero) and the others with the configured strong decay (map exactly zero after one
+    chunk): the pass over blocks reads the zero flags in groups of 64, and the mix of skipped and
+    applied maps crosses the group boundary. Against the oracle and the one-block pass."""
+    cfg = inputs.GDN_32K.with_(name="many_blocks", B=1, H=1, L=64 * 140, seed=53)
+    say(f"case {cfg.name}")
+    x = inputs.prefill_inputs(cfg)
+    la = x["log_alpha"].copy()
+    rng = np.random.default_rng(54)
+    for blk in range(0, 70, 3):
+        t0 = 128 * blk
+        la[0, 0, t0:t0 + 128] = (-rng.uniform(0.0, 0.01, 128)).astype(np.float32)
+    x["log_alpha"] = la
+    q, k, v = (dev_tensor(x[n], torch.bfloat16) for n in ("q", "k", "v"))
+    h0 = dev_tensor(x["h0"], torch.float32)
+    beta, lad = dev_tensor(x["beta"], torch.float32), dev_tensor(la, torch.float32)
+    ro, rh = _oracle(x)
+    res = {}
+    for nb in (1, 70):
+        ws = prefill_workspace(torch, 1, 1, 128, nb) if nb > 1 else None
+        o, hf = ops.gdn_prefill_fwd(q, k, v, beta, lad, h0, workspace=ws)
+        torch.cuda.synchronize()
+        res[nb] = (host(o), host(hf))
+        _check(res[nb][0], res[nb][1], ro, rh, TOL_BF16, f"{nb} blocks")
+    assert max_rel_err(res[70][0], res[1][0]) <= 1e-2 and max_rel_err(res[70][1], res[1][1]) <= 1e-2
+
+
 def test_deterministic():
     cfg = inputs.GDN_32K.with_(name="det", B=1, H=4, L=777, seed=5)
     x = inputs.prefill_inputs(cfg)
