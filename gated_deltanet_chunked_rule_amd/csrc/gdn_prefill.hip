@@ -205,7 +205,9 @@ __device__ __forceinline__ int wave_max_scan(int x, int /*lane*/) {
 }
 
 // Gate arrays of a chunk, computed by one wave (lane = token; past the end la = 0, bt = 0).
-__device__ __forceinline__ void gate_scan(Gates* gt, float la, float bt, int lane) {
+// upd = false (a skipped chunk of the output kernel) sets Khat's factors e^{g_C - g} to zero, so
+// the state update adds nothing to the decayed state.
+__device__ __forceinline__ void gate_scan(Gates* gt, float la, float bt, int lane, bool upd = true) {
     const bool zero = la == -__builtin_inff();
     const float g = wave_scan(zero ? 0.f : la, lane);
     const int rho = wave_max_scan(zero ? lane : -1, lane);
@@ -216,7 +218,7 @@ __device__ __forceinline__ void gate_scan(Gates* gt, float la, float bt, int lan
     gt->rho[lane] = rho;
     gt->b[lane] = bt;
     gt->nbe[lane] = -bt * eg;
-    gt->kh[lane] = rhoC <= lane ? __expf(gC - g) : 0.f;
+    gt->kh[lane] = upd && rhoC <= lane ? __expf(gC - g) : 0.f;
     gt->eg[lane] = eg;
     if (lane == 0) gt->dec = rhoC < 0 ? __expf(gC) : 0.f;
 }
@@ -942,7 +944,8 @@ __global__ __launch_bounds__(256) void scan_kernel(PrefArgs a) {
 // Per chunk, after the intra-chunk solve:
 //   U = Ut - W H;  O^T = e^g (H^T Q^T) + U^T P^T (stored);  H <- e^{g_C} H + Khat^T U
 // (a skipped chunk's update leaves the decayed state; its outputs still use U). SKIP: the
-// launch has a keep mask (the state update then follows the outputs, under a scalar branch).
+// launch has a keep mask; a skipped chunk's Khat is zero (its gate scan zeroes e^{g_C - g}), so
+// the same fused update leaves e^{g_C} H exactly.
 template <int D, class E, bool SKIP>
 __global__ __launch_bounds__(512) void out_kernel(PrefArgs a) {
     using C = Cfg<D, E, out_waves<D, E>()>;
@@ -986,7 +989,8 @@ __global__ __launch_bounds__(512) void out_kernel(PrefArgs a) {
         const int n = fx.n;
         fx.rq.store(Qr, n, tid);
         fx.rk.store(Kr, n, tid);
-        if (w == 0) gate_scan(gt, fx.la, fx.bt, lane);
+        const unsigned keep = SKIP ? keep_chunk(a, bh, c) : 1u;
+        if (w == 0) gate_scan(gt, fx.la, fx.bt, lane, keep != 0u);
         // the next chunk's K and Q rows and gates load while this whole chunk runs (their
         // registers are free once stored); its V fragments follow once the solve has used this
         // chunk's (after W and Ut)
@@ -998,7 +1002,6 @@ __global__ __launch_bounds__(512) void out_kernel(PrefArgs a) {
             fx.load_q(a, tid);
         }
         lds_sync();
-        const unsigned keep = SKIP ? keep_chunk(a, bh, c) : 1u;
         frag kbe[VPW][NKT], vb[VPW][NKT];
         // The solve up to W and Ut is this workgroup's serial path; the other workgroup on the CU
         // is usually in its matrix-heavy state phase then. A higher wave priority lets the solve's
@@ -1062,11 +1065,11 @@ __global__ __launch_bounds__(512) void out_kernel(PrefArgs a) {
         // O^T = e^g (H^T Q^T) + U^T P^T, lane (j, n): O[16 rt + n][16 vt + 4 j .. + 3], and
         // H <- e^{g_C} H + Khat^T U (H itself is no longer read: the products use Hf). The two
         // are interleaved, two value tiles of the update per output tile, so that the update's
-        // independent products fill the output's dependent chains; `KEEP` is the chunk's keep flag.
+        // independent products fill the output's dependent chains.
         const long t0 = (long)c * CH;
         const __amdgpu_buffer_rsrc_t ro =
             buffer_rsrc(static_cast<T*>(a.o) + ((size_t)bh * a.L + t0) * D, n * D * (int)sizeof(T));
-        auto out_and_update = [&](auto KEEP) {
+        {
 #pragma unroll
             for (int rt = 0; rt < 4; ++rt) {
                 f32x4 ot[VPW];
@@ -1083,13 +1086,11 @@ __global__ __launch_bounds__(512) void out_kernel(PrefArgs a) {
                     const int lt = (NDT / 4) * rt + l;
 #pragma unroll
                     for (int t = 0; t < VPW; ++t) H[t][lt] = scale4(H[t][lt], dec);
-                    if constexpr (decltype(KEEP)::value) {
 #pragma unroll
-                        for (int kt = 0; kt < NKT; ++kt) {
-                            const frag kf = ld_frag<frag>(smem + L::O_KH + (size_t)(lt * NKT + kt) * C::FR, lane);
+                    for (int kt = 0; kt < NKT; ++kt) {
+                        const frag kf = ld_frag<frag>(smem + L::O_KH + (size_t)(lt * NKT + kt) * C::FR, lane);
 #pragma unroll
-                            for (int t = 0; t < VPW; ++t) H[t][lt] = M::mma(kf, Uf[t][kt], H[t][lt]);
-                        }
+                        for (int t = 0; t < VPW; ++t) H[t][lt] = M::mma(kf, Uf[t][kt], H[t][lt]);
                     }
                 }
                 const float eg = gt->eg[16 * rt + m];
@@ -1108,21 +1109,6 @@ __global__ __launch_bounds__(512) void out_kernel(PrefArgs a) {
                                   make_float4(ot[t][0], ot[t][1], ot[t][2], ot[t][3]), T{});
                 __builtin_amdgcn_sched_barrier(0);   // keeps each tile's operand loads in its step
             }
-        };
-        if constexpr (SKIP) {
-            out_and_update(std::false_type{});
-            if (keep) {
-#pragma unroll
-                for (int lt = 0; lt < NDT; ++lt)
-#pragma unroll
-                    for (int kt = 0; kt < NKT; ++kt) {
-                        const frag kf = ld_frag<frag>(smem + L::O_KH + (size_t)(lt * NKT + kt) * C::FR, lane);
-#pragma unroll
-                        for (int t = 0; t < VPW; ++t) H[t][lt] = M::mma(kf, Uf[t][kt], H[t][lt]);
-                    }
-            }
-        } else {
-            out_and_update(std::true_type{});
         }
         lds_sync();   // the chunk's LDS is free for the next one
     }
