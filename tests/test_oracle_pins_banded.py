@@ -5,8 +5,9 @@ when the band keeps every block, and wherever the approximation is exact by cons
 chunk inside one 16-token block, chunks of at most 32 tokens with band >= 1, beta = 0 (no delta
 system). The band itself is pinned to the block structure of a triangular inverse: the kept
 diagonal blocks are the inverses of the diagonal blocks of I + A, the first sub-diagonal block
-is -T_ii A_i,i-1 T_i-1,i-1, and the rest are zero. For band < 3 on general inputs there is no
-independent value to compare with: that case is parity unpinned.
+is -T_ii A_i,i-1 T_i-1,i-1, and the rest are zero. Every band on general inputs is pinned to a
+second formulation that never forms T: windows of the token recurrence (see
+_windowed_chunk_form).
 """
 import numpy as np
 import pytest
@@ -88,3 +89,62 @@ def test_band_is_an_approximation_with_long_memory():
     o0, _ = oracle.gdn_prefill_banded(q, k, v, beta, la, h0, band=0)
     o3, _ = oracle.gdn_prefill_banded(q, k, v, beta, la, h0, band=3)
     assert np.abs(o0 - o3).max() > 1e-3 * np.abs(o3).max()
+
+
+def _windowed_chunk_form(q, k, v, beta, la, h0, band, chunk=64, block=16):
+    """The block-adjacent solve restated through the token recurrence, for one (b, h) slice.
+
+    T = (I + A)^-1 is lower triangular, so any contiguous run of its diagonal blocks is the
+    inverse of the same run of I + A. Keeping T's blocks (i, i - band) .. (i, i) therefore makes
+    the pseudo-values u of block i those of the exact delta rule run over blocks i - band .. i
+    alone, started from the chunk-start state decayed to the window's start. Here that run is the
+    C oracle's decode step, token by token, and u_r is read back from two successive states
+    (S_r - a_r S_{r-1} = k_r u_r^T). The chunk's outputs and next state are then the plain sums
+        o_r = e^{g_r} H^T q_r + sum_{s <= r} e^{g_r - g_s} (q_r . k_s) u_s
+        H'  = e^{g_C} H + sum_s e^{g_C - g_s} k_s u_s^T.
+    """
+    L, D = k.shape
+    H = np.array(h0, dtype=np.float64)
+    o = np.zeros((L, v.shape[1]))
+    one = lambda x: np.asarray(x, dtype=np.float64).reshape(1, 1, -1)
+    for t0 in range(0, L, chunk):
+        n = min(chunk, L - t0)
+        g = np.cumsum(la[t0:t0 + n])
+        u = np.zeros((n, v.shape[1]))
+        for i0 in range(0, n, block):
+            w0 = max(0, i0 - band * block)
+            S = (np.exp(g[w0 - 1]) if w0 > 0 else 1.0) * H
+            for r in range(w0, min(n, i0 + block)):
+                t = t0 + r
+                _, S1 = oracle.gdn_decode_step(one(q[t]), one(k[t]), one(v[t]), np.full((1, 1), beta[t]),
+                                               np.full((1, 1), la[t]), S[None, None])
+                S1 = S1[0, 0]
+                if r >= i0:
+                    u[r] = (S1 - np.exp(la[t]) * S).T @ k[t] / (k[t] @ k[t])
+                S = S1
+        for r in range(n):
+            acc = np.exp(g[r]) * (H.T @ q[t0 + r])
+            for s in range(r + 1):
+                acc = acc + np.exp(g[r] - g[s]) * (q[t0 + r] @ k[t0 + s]) * u[s]
+            o[t0 + r] = acc
+        Hn = np.exp(g[-1]) * H
+        for s in range(n):
+            Hn = Hn + np.exp(g[-1] - g[s]) * np.outer(k[t0 + s], u[s])
+        H = Hn
+    return o, H
+
+
+@pytest.mark.parametrize("band", [0, 1, 2, 3])
+@pytest.mark.parametrize("L,long_memory", [(64, True), (150, True), (200, False)])
+def test_band_equals_windowed_recurrence(band, L, long_memory):
+    """Every band on general inputs (unit keys that interact across blocks, h0 != 0, ragged
+    tails): the oracle's banded chunked form against the windowed token recurrence above."""
+    q, k, v, beta, la, h0 = _inputs(100 + L + band, 1, 2, L, 8, long_memory)
+    o, hf = oracle.gdn_prefill_banded(q, k, v, beta, la, h0, band=band)
+    for h in range(2):
+        ro, rh = _windowed_chunk_form(q[0, h], k[0, h], v[0, h], beta[0, h], la[0, h], h0[0, h], band)
+        np.testing.assert_allclose(o[0, h], ro, rtol=1e-9, atol=1e-11)
+        np.testing.assert_allclose(hf[0, h], rh, rtol=1e-9, atol=1e-11)
+    if band == 3:   # the window of the full band is the whole chunk: the plain recurrence
+        ro, rh = oracle.gdn_prefill(q, k, v, beta, la, h0)
+        np.testing.assert_allclose(o, ro, rtol=1e-10, atol=1e-12)
