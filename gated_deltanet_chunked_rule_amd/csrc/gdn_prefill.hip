@@ -117,7 +117,7 @@ struct Gates {
 
 // LDS of a workgroup of the map (OUT = false) or output (OUT = true) kernel:
 //   OUT:  Q rows | K rows, then T | V rows, then A, then -W fragments | Khat^T fragments |
-//         P^T fragments | gates
+//         P^T fragments | gates of two chunks (the current one and the next, by chunk parity)
 //   map:  K rows | V rows, then A, then -W^T fragments | T | Ut fragments | gates
 template <int D, class E, bool OUT>
 struct Lds {
@@ -131,7 +131,8 @@ struct Lds {
     static constexpr size_t O_P = O_KH + (size_t)C::NDT * C::NKT * C::FR;   // OUT: P^T fragments [rt][kt]
     static constexpr size_t O_UT = 3 * REG;                    // map: Ut fragments [kt][vt]
     static constexpr size_t O_G = OUT ? O_P + (size_t)4 * C::NKT * C::FR : O_UT + (size_t)C::NKT * C::NDT * C::FR;
-    static constexpr size_t BYTES = O_G + sizeof(Gates);
+    static constexpr size_t GSZ = up16(sizeof(Gates));
+    static constexpr size_t BYTES = O_G + (OUT ? 2 : 1) * GSZ;
     static_assert(BYTES <= 160 * 1024, "LDS");
 };
 
@@ -279,12 +280,18 @@ struct Fetch {
     RowRegs<D, E, C::NT> rq, rk;
     frag vf[NGW][4];   // V row fragments [own group][token tile]
     float la, bt;
-    int n;         // valid tokens
-    size_t tok0;   // first token of the chunk in its slice's rows
+    unsigned kp = 1;   // OUT: the chunk's keep flag (nonzero: its update is kept)
+    int n;             // valid tokens
+    size_t tok0;       // first token of the chunk in its slice's rows
+    size_t kidx;       // the chunk's entry in the keep mask
+    // the wave that loads (and scans) the gates: wave 0 for the map kernel; for the output kernel
+    // the last wave, which has no block of T to form in the first step after the substitution
+    static constexpr int GW = OUT ? NW - 1 : 0;
     __device__ __forceinline__ void start(const PrefArgs& a, int bh, int c) {
         const long t0 = (long)c * CH;
         n = (int)min((long)CH, a.L - t0);
         tok0 = (size_t)bh * a.L + t0;
+        kidx = (size_t)bh * a.nch + c;
     }
     __device__ __forceinline__ void load_k(const PrefArgs& a, int tid) {
         rk.load(static_cast<const T*>(a.k) + tok0 * D, n, tid);
@@ -310,11 +317,12 @@ struct Fetch {
             }
     }
     __device__ __forceinline__ void load_gates(const PrefArgs& a, int tid) {
-        if (tid < 64) {   // wave 0 scans the gates
+        if ((tid >> 6) == GW) {   // lane = token
             const __amdgpu_buffer_rsrc_t rl = buffer_rsrc(a.log_alpha + tok0, n * 4);
             const __amdgpu_buffer_rsrc_t rb = buffer_rsrc(a.beta + tok0, n * 4);
-            la = __uint_as_float(buffer_load4(rl, tid * 4));
-            bt = __uint_as_float(buffer_load4(rb, tid * 4));
+            la = __uint_as_float(buffer_load4(rl, (tid & 63) * 4));
+            bt = __uint_as_float(buffer_load4(rb, (tid & 63) * 4));
+            if constexpr (OUT) kp = a.keep ? (unsigned)a.keep[kidx] : 1u;
         }
     }
     __device__ __forceinline__ void issue(const PrefArgs& a, int bh, int c, bool rows, int tid, int w) {
@@ -428,9 +436,11 @@ __device__ __forceinline__ bf16x8 v_unit_cols(int j, int n, int q) {
 // then T = (I + A)^-1 blocked by 16: the diagonal blocks by forward substitution, then (exact)
 // the two 32 x 32 diagonal blocks and the quadrant below them, or (band < 3) the blocks within
 // `band` of the diagonal level by level, the others zero. Returns after the barrier that
-// completes T. Wave w owns d (and value) tiles VPW w .. VPW w + VPW - 1.
-template <int D, class E, bool OUT, int NW>
-__device__ __forceinline__ void intra_solve(unsigned char* smem, int band, int w, int lane,
+// completes T. Wave w owns d (and value) tiles VPW w .. VPW w + VPW - 1. The chunk's gate arrays
+// are `gt`. The last wave has no block of T to form in the step after the diagonal substitution
+// and runs `side()` there instead (work of its own that touches none of the solve's LDS).
+template <int D, class E, bool OUT, int NW, class Side>
+__device__ __forceinline__ void intra_solve(unsigned char* smem, const Gates* gt, int band, int w, int lane, Side&& side,
                                             const typename MM<E>::frag (&vf)[Fetch<D, E, OUT, NW>::NGW][4],
                                             typename MM<E>::frag (&kbe)[Cfg<D, E, NW>::VPW][Cfg<D, E, NW>::NKT],
                                             typename MM<E>::frag (&vb)[Cfg<D, E, NW>::VPW][Cfg<D, E, NW>::NKT]) {
@@ -445,7 +455,6 @@ __device__ __forceinline__ void intra_solve(unsigned char* smem, int band, int w
     const T* Qr = reinterpret_cast<const T*>(smem + L::O_Q);
     float* Tm = reinterpret_cast<float*>(smem + L::O_T);
     float* Am = reinterpret_cast<float*>(smem + L::O_V);
-    const Gates* gt = reinterpret_cast<const Gates*>(smem + L::O_G);
 
     // Row tile rw of the Gram matrix and row tile rp of P^T: only their tiles on and below the
     // diagonal are formed (st <= rw, st <= rp). With four waves wave w takes Gram row w and P^T
@@ -554,6 +563,25 @@ __device__ __forceinline__ void intra_solve(unsigned char* smem, int band, int w
             vb[t][kt] = cols_frag<E>(&vc[FPD * kt], gt->b + KB * kt, j);
         }
     }
+    // Diagonal block rw of T by forward substitution in outer-product order, by the wave that
+    // formed A's diagonal tile (rw, rw) above: it reads only its own LDS writes, so it needs no
+    // barrier and overlaps the other waves' tiles (T_ii is stored once K's rows are free). Lane
+    // (c, g) = (lane / 4, lane % 4) holds rows 4 g .. 4 g + 3 of column c. Step s takes the final
+    // x_s from the lane of its quad that owns row s (a quad broadcast) and updates every row of
+    // the lane with A[r][s] (zero on and above the diagonal, so rows at or before s are left as
+    // they are); A is read four columns at a time.
+    const bool diag = do_gram && st0 <= rw && rw < st0 + NST;   // scalar; every wave when NW = 4
+    float xd[4];
+    if (C::NW == 4 || diag) {
+        asm volatile("" ::: "memory");
+        const int i0 = 16 * rw, g = lane & 3, c = lane >> 2;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) xd[i] = 4 * g + i == c ? 1.f : 0.f;
+        subst_stage<0, AS>(Am, i0, g, xd);
+        subst_stage<1, AS>(Am, i0, g, xd);
+        subst_stage<2, AS>(Am, i0, g, xd);
+        subst_stage<3, AS>(Am, i0, g, xd);
+    }
 #pragma unroll
     for (int t = 0; t < VPW; ++t)
 #pragma unroll
@@ -578,33 +606,23 @@ __device__ __forceinline__ void intra_solve(unsigned char* smem, int band, int w
             }
         }
     }
-    // Diagonal blocks by forward substitution in outer-product order: wave i inverts block i,
-    // lane (c, g) = (lane / 4, lane % 4) holds rows 4 g .. 4 g + 3 of column c. Step s takes the
-    // final x_s from the lane of its quad that owns row s (a quad broadcast) and updates every
-    // row of the lane with A[r][s] (zero on and above the diagonal, so rows at or before s are
-    // left as they are); A is read four columns at a time.
-    if (w < 4) {
-        const int i0 = 16 * w, g = lane & 3, c = lane >> 2;
-        float x[4];
+    if (C::NW == 4 || diag) {
+        const int i0 = 16 * rw, g = lane & 3, c = lane >> 2;
 #pragma unroll
-        for (int i = 0; i < 4; ++i) x[i] = 4 * g + i == c ? 1.f : 0.f;
-        subst_stage<0, AS>(Am, i0, g, x);
-        subst_stage<1, AS>(Am, i0, g, x);
-        subst_stage<2, AS>(Am, i0, g, x);
-        subst_stage<3, AS>(Am, i0, g, x);
-#pragma unroll
-        for (int i = 0; i < 4; ++i) Tm[(i0 + 4 * g + i) * AS + i0 + c] = x[i];
+        for (int i = 0; i < 4; ++i) Tm[(i0 + 4 * g + i) * AS + i0 + c] = xd[i];
     }
     lds_sync();
     if (band >= 3) {
         // exact: blocks (1, 0) and (3, 2), then the lower-left quadrant
         if (w < 2) inverse_block<AS, 1>(Am, Tm, 2 * w, j, m);
+        else if (w == NW - 1) side();
         lds_sync();
         if (w < 4) inverse_quadrant<AS>(Am, Tm, w, j, m);
         lds_sync();
     } else {
         // block-adjacent: the blocks within `band` of the diagonal, level by level
         if (w + 1 < 4 && 1 <= band) inverse_block<AS, 1>(Am, Tm, w, j, m);
+        else if (w == NW - 1) side();
         lds_sync();
         if (w + 2 < 4 && 2 <= band) inverse_block<AS, 2>(Am, Tm, w, j, m);
         lds_sync();
@@ -698,7 +716,7 @@ __global__ __launch_bounds__(512) void map_kernel(PrefArgs a) {
         }
         if (any) {
             frag kbe[CP::VPW][NKT], vb[CP::VPW][NKT];
-            intra_solve<D, E, false, MC::NWP>(my, a.band, hw, lane, fx.vf, kbe, vb);
+            intra_solve<D, E, false, MC::NWP>(my, gt, a.band, hw, lane, [] {}, fx.vf, kbe, vb);
             // -W (token tiles x this wave's d tiles) and Ut (x its value tiles) of the half's
             // chunk, then the fragments the state step reads: -W^T [dt][kt] (A: rows d, k = token)
             // and Ut [kt][vt] (B: k = token, columns v). A (in the V-row space) was last read
@@ -963,7 +981,7 @@ __global__ __launch_bounds__(512) void out_kernel(PrefArgs a) {
     T* Qr = reinterpret_cast<T*>(smem + L::O_Q);
     T* Kr = reinterpret_cast<T*>(smem + L::O_K);
     const float* Tm = reinterpret_cast<const float*>(smem + L::O_T);
-    Gates* gt = reinterpret_cast<Gates*>(smem + L::O_G);
+    constexpr int GW = Fetch<D, E, true, C::NW>::GW;   // the wave that loads and scans the gates
 
     // the block's start state: h0 (or zeros) for a single block, else the scan's slot
     f32x4 H[VPW][NDT];
@@ -987,10 +1005,14 @@ __global__ __launch_bounds__(512) void out_kernel(PrefArgs a) {
     for (int c = c0; c < c1; ++c) {
         const int tid = 64 * w + opaque(threadIdx.x & 63), lane = tid & 63, j = lane >> 4, m = lane & 15;
         const int n = fx.n;
+        // the gate arrays of chunk c and of chunk c + 1 (two LDS slots by chunk parity)
+        Gates* gt = reinterpret_cast<Gates*>(smem + L::O_G + (size_t)((c - c0) & 1) * L::GSZ);
+        Gates* gn = reinterpret_cast<Gates*>(smem + L::O_G + (size_t)((c - c0 + 1) & 1) * L::GSZ);
         fx.rq.store(Qr, n, tid);
         fx.rk.store(Kr, n, tid);
-        const unsigned keep = SKIP ? keep_chunk(a, bh, c) : 1u;
-        if (w == 0) gate_scan(gt, fx.la, fx.bt, lane, keep != 0u);
+        // the first chunk's gates are scanned here; every later chunk's during the solve of the
+        // chunk before it (side work of wave GW, below)
+        if (c == c0 && w == GW) gate_scan(gt, fx.la, fx.bt, lane, !SKIP || fx.kp != 0u);
         // the next chunk's K and Q rows and gates load while this whole chunk runs (their
         // registers are free once stored); its V fragments follow once the solve has used this
         // chunk's (after W and Ut)
@@ -1007,7 +1029,9 @@ __global__ __launch_bounds__(512) void out_kernel(PrefArgs a) {
         // is usually in its matrix-heavy state phase then. A higher wave priority lets the solve's
         // dependent steps issue first, and the state phase takes the idle cycles between them.
         __builtin_amdgcn_s_setprio(2);
-        intra_solve<D, E, true, C::NW>(smem, a.band, w, lane, fx.vf, kbe, vb);
+        intra_solve<D, E, true, C::NW>(smem, gt, a.band, w, lane, [&] {
+            if (more) gate_scan(gn, fx.la, fx.bt, lane, !SKIP || fx.kp != 0u);
+        }, fx.vf, kbe, vb);
         // -W fragments [rt][kd] (A: rows token, k = d), each d tile filling its part, and Ut
         f32x4 U[VPW][4];
         {
