@@ -105,7 +105,7 @@ struct MapCfg {
 
 // per-token gate arrays of the chunk in LDS
 struct Gates {
-    float g[CH];     // cumulative log gate over the finite gates
+    float g[CH];     // cumulative log gate over the finite gates, in log2 units (times log2 e)
     int rho[CH];     // last token <= r with a zero gate (log a = -inf), or -1
     float b[CH];     // beta
     float nbe[CH];   // -beta e^{g_r} (zero after a zero gate)
@@ -205,28 +205,27 @@ __device__ __forceinline__ int wave_max_scan(int x, int /*lane*/) {
     return wave_scan_dpp(x, -1, [](int a, int b) { return max(a, b); });
 }
 
+// 2^x by the hardware's base-2 exponential (what expf(x) reduces to after scaling x by log2 e)
+__device__ __forceinline__ float exp2_hw(float x) { return __builtin_amdgcn_exp2f(x); }
+
 // Gate arrays of a chunk, computed by one wave (lane = token; past the end la = 0, bt = 0).
-// upd = false (a skipped chunk of the output kernel) sets Khat's factors e^{g_C - g} to zero, so
-// the state update adds nothing to the decayed state.
+// The cumulative log gates are kept in log2 units, so every factor exp(g_r - g_s) is one base-2
+// exponential of a difference. upd = false (a skipped chunk of the output kernel) sets Khat's
+// factors e^{g_C - g} to zero, so the state update adds nothing to the decayed state.
 __device__ __forceinline__ void gate_scan(Gates* gt, float la, float bt, int lane, bool upd = true) {
     const bool zero = la == -__builtin_inff();
-    const float g = wave_scan(zero ? 0.f : la, lane);
+    const float g = wave_scan(zero ? 0.f : la, lane) * 1.44269504088896341f;
     const int rho = wave_max_scan(zero ? lane : -1, lane);
     const float gC = wave_last(g);
     const int rhoC = __builtin_amdgcn_readlane(rho, 63);
-    const float eg = rho < 0 ? __expf(g) : 0.f;
+    const float eg = rho < 0 ? exp2_hw(g) : 0.f;
     gt->g[lane] = g;
     gt->rho[lane] = rho;
     gt->b[lane] = bt;
     gt->nbe[lane] = -bt * eg;
-    gt->kh[lane] = upd && rhoC <= lane ? __expf(gC - g) : 0.f;
+    gt->kh[lane] = upd && rhoC <= lane ? exp2_hw(gC - g) : 0.f;
     gt->eg[lane] = eg;
-    if (lane == 0) gt->dec = rhoC < 0 ? __expf(gC) : 0.f;
-}
-
-// exp(g_r - g_s) for s <= r with no zero gate in (s, r], else 0
-__device__ __forceinline__ float gamma_rs(const Gates* gt, int r, float gr, int s) {
-    return (s <= r && s >= gt->rho[r]) ? __expf(gr - gt->g[s]) : 0.f;
+    if (lane == 0) gt->dec = rhoC < 0 ? exp2_hw(gC) : 0.f;
 }
 
 // The part of an operand fragment that one 16 x 16 accumulator tile fills: elements 4 h .. 4 h + 3
@@ -504,7 +503,7 @@ __device__ __forceinline__ void intra_solve(unsigned char* smem, const Gates* gt
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
                 const int s = 16 * st + 4 * j + e;
-                av[e] = (s < r && s >= rhow) ? brw * __expf(grw - gs[e]) * g[e] : 0.f;
+                av[e] = (s < r && s >= rhow) ? brw * exp2_hw(grw - gs[e]) * g[e] : 0.f;
             }
             *reinterpret_cast<float4*>(Am + r * AS + 16 * st + 4 * j) = make_float4(av[0], av[1], av[2], av[3]);
         }
@@ -520,7 +519,7 @@ __device__ __forceinline__ void intra_solve(unsigned char* smem, const Gates* gt
 #pragma unroll
                 for (int e = 0; e < 4; ++e) {
                     const int s2 = 16 * st + 4 * j + e, r = 16 * rp + m;
-                    pt[i][e] = (s2 <= r && s2 >= rhom) ? __expf(grm - gs[e]) * p[e] : 0.f;
+                    pt[i][e] = (s2 <= r && s2 >= rhom) ? exp2_hw(grm - gs[e]) * p[e] : 0.f;
                 }
             }
         }
@@ -1089,11 +1088,15 @@ __global__ __launch_bounds__(512) void out_kernel(PrefArgs a) {
         // O^T = e^g (H^T Q^T) + U^T P^T, lane (j, n): O[16 rt + n][16 vt + 4 j .. + 3], and
         // H <- e^{g_C} H + Khat^T U (H itself is no longer read: the products use Hf). The two
         // are interleaved, two value tiles of the update per output tile, so that the update's
-        // independent products fill the output's dependent chains.
+        // independent products fill the output's dependent chains. When e^{g_C} is exactly zero
+        // (strong decay: the chunk's gates multiply below fp32's smallest subnormal) the decayed
+        // state is zero and the update starts from zero instead of scaling H: one straight-line
+        // copy of the loop per case, chosen by a scalar branch.
         const long t0 = (long)c * CH;
         const __amdgpu_buffer_rsrc_t ro =
             buffer_rsrc(static_cast<T*>(a.o) + ((size_t)bh * a.L + t0) * D, n * D * (int)sizeof(T));
-        {
+        auto outputs_and_update = [&](auto dz) {
+            constexpr bool DZ = decltype(dz)::value;
 #pragma unroll
             for (int rt = 0; rt < 4; ++rt) {
                 f32x4 ot[VPW];
@@ -1109,7 +1112,7 @@ __global__ __launch_bounds__(512) void out_kernel(PrefArgs a) {
                 for (int l = 0; l < NDT / 4; ++l) {
                     const int lt = (NDT / 4) * rt + l;
 #pragma unroll
-                    for (int t = 0; t < VPW; ++t) H[t][lt] = scale4(H[t][lt], dec);
+                    for (int t = 0; t < VPW; ++t) H[t][lt] = DZ ? f32x4{0.f, 0.f, 0.f, 0.f} : scale4(H[t][lt], dec);
 #pragma unroll
                     for (int kt = 0; kt < NKT; ++kt) {
                         const frag kf = ld_frag<frag>(smem + L::O_KH + (size_t)(lt * NKT + kt) * C::FR, lane);
@@ -1133,7 +1136,9 @@ __global__ __launch_bounds__(512) void out_kernel(PrefArgs a) {
                                   make_float4(ot[t][0], ot[t][1], ot[t][2], ot[t][3]), T{});
                 __builtin_amdgcn_sched_barrier(0);   // keeps each tile's operand loads in its step
             }
-        }
+        };
+        if (__builtin_amdgcn_readfirstlane(__float_as_uint(dec)) == 0u) outputs_and_update(std::true_type{});
+        else outputs_and_update(std::false_type{});
         lds_sync();   // the chunk's LDS is free for the next one
     }
     if (b == a.NB - 1) {
