@@ -640,6 +640,26 @@ __device__ __forceinline__ void intra_solve(unsigned char* smem, const Gates* gt
 // Each iteration takes NH chunks (c, c - 1, ...); half h of the workgroup solves chunk c - h in
 // LDS slot h (a half with no chunk, or a skipped one, runs through the same barriers on whatever
 // its slot holds, and nothing reads the result).
+// Khat = diag(e^{g_C - g}) K over a chunk's staged K rows, in place, by NT threads: each element
+// rounded once from its product, the value the state steps' operand loads would otherwise form
+// per use.
+template <int D, class E, int NT>
+__device__ __forceinline__ void scale_rows(typename E::T* R, const float* kh, int tid) {
+    using T = typename E::T;
+    constexpr int KP = row_stride<D, E>(), EPU = 4 / (int)sizeof(T) * 2;   // elements per 8 bytes
+    constexpr int UPR = D / EPU, N = CH * UPR / NT;
+    static_assert(CH * UPR % NT == 0, "whole units per thread");
+#pragma unroll
+    for (int i = 0; i < N; ++i) {
+        const int u = tid + NT * i, r = u / UPR;
+        uint2* p = reinterpret_cast<uint2*>(R + r * KP + (u % UPR) * EPU);
+        const float sc = kh[r];
+        const float4 x = load4(reinterpret_cast<const T*>(p));
+        if constexpr (sizeof(T) == 2) store4(reinterpret_cast<T*>(p), make_float4(x.x * sc, x.y * sc, x.z * sc, x.w * sc));
+        else *p = uint2{__float_as_uint(x.x * sc), __float_as_uint(x.y * sc)};
+    }
+}
+
 template <int D, class E>
 constexpr size_t map_lds() {
     return MapCfg<D, E>::NH * ((Lds<D, E, false>::BYTES + 255) / 256 * 256);
@@ -748,6 +768,8 @@ __global__ __launch_bounds__(512) void map_kernel(PrefArgs a) {
                     st_frag(my + L::O_V + (size_t)(dt * NKT + kt) * C::FR, lane, M::from_acc(wn[t], kt));
                     st_frag(my + L::O_UT + (size_t)(kt * NDT + dt) * C::FR, lane, M::from_acc(ua[t], kt));
                 }
+            // the solve is done with this half's K rows: scale them into Khat for the state steps
+            if (mine >= c0 && (half ? kp[NH - 1] : kp[0])) scale_rows<D, E, 64 * MC::NWP>(Kr, gt->kh, 64 * hw + lane);
         }
         lds_sync();
         // the next iteration's rows and gates load while this one's state steps run
@@ -789,7 +811,7 @@ __global__ __launch_bounds__(512) void map_kernel(PrefArgs a) {
                 }
 #pragma unroll
                 for (int rt = 0; rt < 4; ++rt) {
-                    const frag kf = row_frag<E>(Ks + (16 * rt + m) * KP, kd * KB, j, gs->kh[16 * rt + m]);
+                    const frag kf = row_frag_raw<E>(Ks + (16 * rt + m) * KP, kd * KB, j);   // Khat rows
 #pragma unroll
                     for (int t = 0; t < VPW; ++t) {
                         Y[t][rt] = M::mma(kf, zh[t], Y[t][rt]);
