@@ -896,7 +896,13 @@ __global__ __launch_bounds__(256) void scan_kernel(PrefArgs a) {
     using frag = typename M::frag;
     constexpr int NKD = C::NKD, NDT = C::NDT, VPW = C::SVPW, FPD = C::FPD, NS = C::NSPLIT;
     __shared__ __align__(16) unsigned char hb[2 * NKD * NS * 1024];
-    const int vt = blockIdx.x, bh = blockIdx.y;
+    // Workgroup L of the 1-D grid takes value tile vt of slice bh. Workgroups go to the 8 XCDs in
+    // turn (L mod 8), and each reads all of its slice's Phi_b: with a multiple of 8 slices the
+    // NDT tiles of a slice share an XCD (and its L2), else the plain order.
+    const int L = blockIdx.x;
+    const bool xcd = a.BH % 8 == 0;
+    const int vt = xcd ? (L >> 3) % NDT : L % NDT;
+    const int bh = xcd ? ((L >> 3) / NDT) * 8 + (L & 7) : L / NDT;
     const int tid = threadIdx.x, lane = tid & 63, j = lane >> 4, m = lane & 15;
     const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
     f32x4 H[VPW];
@@ -911,9 +917,26 @@ __global__ __launch_bounds__(256) void scan_kernel(PrefArgs a) {
     // A block whose map is zero leaves H_{b+1} = Psi_b, which its slot already holds: such blocks
     // are skipped, and H is reloaded from the slot before the next block that needs it. The flags
     // of 64 blocks at a time come in one load (lane i takes block b0 + i) and one ballot, so the
-    // pass does not wait on one flag read per block.
+    // pass does not wait on one flag read per block. Phi_b and Psi_b do not depend on H: the next
+    // live block's are loaded while this block's product runs (within the same 64 flags).
+    frag ph[VPW][NKD][NS], pn[VPW][NKD][NS];   // this block's and the next live block's Phi operands
+    f32x4 ps[VPW], psn[VPW];                   // their Psi tiles
+    auto load_block = [&](int bb, frag (&p)[VPW][NKD][NS], f32x4 (&q)[VPW]) {
+        const unsigned char* phi = ws_phi<D, E>(a, bh, bb);
+        const f32x4* slot = ws_hs<D, E>(a, bh, bb + 1);
+#pragma unroll
+        for (int t = 0; t < VPW; ++t) {
+            const int it = VPW * w + t;
+            q[t] = slot[(it * NDT + vt) * 64 + lane];
+#pragma unroll
+            for (int kd = 0; kd < NKD; ++kd)
+#pragma unroll
+                for (int s = 0; s < NS; ++s) p[t][kd][s] = ld_frag<frag>(phi + ((size_t)(it * NKD + kd) * NS + s) * 1024, lane);
+        }
+    };
     bool have = true;   // H holds H_b (scalar)
     int steps = 0;      // products formed so far: the LDS buffer alternates with them
+    int pre = -1;       // the block whose operands are in pn / psn (scalar)
     unsigned long long live = 0;   // nonzero flags of blocks b0 .. b0 + 63 (bit i: block b0 + i)
     for (int b = 0; b + 1 < a.NB; ++b) {
         if ((b & 63) == 0) {
@@ -929,20 +952,28 @@ __global__ __launch_bounds__(256) void scan_kernel(PrefArgs a) {
 #pragma unroll
             for (int t = 0; t < VPW; ++t) H[t] = ws_hs<D, E>(a, bh, b)[((VPW * w + t) * NDT + vt) * 64 + lane];
         }
-        const unsigned char* phi = ws_phi<D, E>(a, bh, b);
         f32x4* slot = ws_hs<D, E>(a, bh, b + 1);
-        // Psi_b and this wave's Phi_b operands first: they do not depend on H
-        f32x4 acc[VPW];
-        frag ph[VPW][NKD][NS];
+        if (pre == b) {
 #pragma unroll
-        for (int t = 0; t < VPW; ++t) {
-            const int it = VPW * w + t;
-            acc[t] = slot[(it * NDT + vt) * 64 + lane];
+            for (int t = 0; t < VPW; ++t) {
+                ps[t] = psn[t];
 #pragma unroll
-            for (int kd = 0; kd < NKD; ++kd)
+                for (int kd = 0; kd < NKD; ++kd)
 #pragma unroll
-                for (int s = 0; s < NS; ++s) ph[t][kd][s] = ld_frag<frag>(phi + ((size_t)(it * NKD + kd) * NS + s) * 1024, lane);
+                    for (int s = 0; s < NS; ++s) ph[t][kd][s] = pn[t][kd][s];
+            }
+        } else {
+            load_block(b, ph, ps);
         }
+        // the next live block of this window, if any: its operands load during this product
+        const unsigned long long above = (b & 63) == 63 ? 0ull : live >> ((b & 63) + 1);
+        if (above != 0ull) {
+            pre = b + 1 + (int)__builtin_ctzll(above);
+            load_block(pre, pn, psn);
+        }
+        f32x4 acc[VPW];
+#pragma unroll
+        for (int t = 0; t < VPW; ++t) acc[t] = ps[t];
         unsigned char* buf = hb + (size_t)(steps & 1) * NKD * NS * 1024;
         ++steps;
         have = true;
@@ -1333,7 +1364,7 @@ struct Launch {
                                        s, a);
                 }))
                 return -1;
-            if (!timed(1, s, [&] { hipLaunchKernelGGL((scan_kernel<D, E>), dim3(D / 16, a.BH), dim3(256), 0, s, a); }))
+            if (!timed(1, s, [&] { hipLaunchKernelGGL((scan_kernel<D, E>), dim3(D / 16 * a.BH), dim3(256), 0, s, a); }))
                 return -1;
         }
         return timed(2, s, [&] {
