@@ -462,7 +462,7 @@ def main():
         print(json.dumps(counters_from(args.counters), indent=1))
         return
     if args.gpus != 1:
-        print("bench.py measures one GPU: this build has no multi-GPU path (heads and sequences shard "
+        print("bench.py measures one GPU: the library has no multi-GPU path (heads and sequences shard "
               "across GPUs with no communication; see the design notes). Run with --gpus 1.", file=sys.stderr)
         sys.exit(2)
 
