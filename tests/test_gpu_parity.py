@@ -292,6 +292,38 @@ def test_many_blocks_mixed_maps():
     assert max_rel_err(res[70][0], res[1][0]) <= 1e-2 and max_rel_err(res[70][1], res[1][1]) <= 1e-2
 
 
+
+def test_many_blocks_mixed_maps_eight_slices():
+    """Eight slices (B=2, H=4: the pass over blocks then runs each slice's value tiles together on
+    one XCD and loads the next live block's map during the current product) of 70 blocks of two
+    chunks, each slice with its own pattern of long-memory blocks (maps not zero) among strongly
+    decaying ones (maps exactly zero): every block live in one slice, none in another, every
+    k-th block in the rest, so live blocks follow live, skipped and reloaded blocks and cross the
+    64-flag group boundary. Against the oracle and the one-block pass."""
+    cfg = inputs.GDN_32K.with_(name="many_blocks_8", B=2, H=4, L=64 * 140, seed=57)
+    say(f"case {cfg.name}")
+    x = inputs.prefill_inputs(cfg)
+    la = x["log_alpha"].copy()
+    rng = np.random.default_rng(58)
+    for sl, every in enumerate((1, 0, 2, 3, 5, 7, 11, 64)):
+        b, h = divmod(sl, 4)
+        for blk in range(70):
+            if every and blk % every == 0:
+                la[b, h, 128 * blk:128 * blk + 128] = (-rng.uniform(0.0, 0.01, 128)).astype(np.float32)
+    x["log_alpha"] = la
+    q, k, v = (dev_tensor(x[n], torch.bfloat16) for n in ("q", "k", "v"))
+    h0 = dev_tensor(x["h0"], torch.float32)
+    beta, lad = dev_tensor(x["beta"], torch.float32), dev_tensor(la, torch.float32)
+    ro, rh = _oracle(x)
+    res = {}
+    for nb in (1, 70):
+        ws = prefill_workspace(torch, 2, 4, 128, nb) if nb > 1 else None
+        o, hf = ops.gdn_prefill_fwd(q, k, v, beta, lad, h0, workspace=ws)
+        torch.cuda.synchronize()
+        res[nb] = (host(o), host(hf))
+        _check(res[nb][0], res[nb][1], ro, rh, TOL_BF16, f"{nb} blocks")
+    assert max_rel_err(res[70][0], res[1][0]) <= 1e-2 and max_rel_err(res[70][1], res[1][1]) <= 1e-2
+
 def test_deterministic():
     cfg = inputs.GDN_32K.with_(name="det", B=1, H=4, L=777, seed=5)
     x = inputs.prefill_inputs(cfg)
