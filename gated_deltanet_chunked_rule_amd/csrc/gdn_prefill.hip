@@ -654,9 +654,13 @@ __device__ __forceinline__ void scale_rows(typename E::T* R, const float* kh, in
         const int u = tid + NT * i, r = u / UPR;
         uint2* p = reinterpret_cast<uint2*>(R + r * KP + (u % UPR) * EPU);
         const float sc = kh[r];
-        const float4 x = load4(reinterpret_cast<const T*>(p));
-        if constexpr (sizeof(T) == 2) store4(reinterpret_cast<T*>(p), make_float4(x.x * sc, x.y * sc, x.z * sc, x.w * sc));
-        else *p = uint2{__float_as_uint(x.x * sc), __float_as_uint(x.y * sc)};
+        if constexpr (sizeof(T) == 2) {   // four bf16
+            const float4 x = load4(reinterpret_cast<const T*>(p));
+            store4(reinterpret_cast<T*>(p), make_float4(x.x * sc, x.y * sc, x.z * sc, x.w * sc));
+        } else {                          // two fp32
+            const uint2 y = *p;
+            *p = uint2{__float_as_uint(__uint_as_float(y.x) * sc), __float_as_uint(__uint_as_float(y.y) * sc)};
+        }
     }
 }
 
