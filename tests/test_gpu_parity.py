@@ -408,6 +408,38 @@ def test_gdn_128k_long_memory_gates_all_heads():
     _check(o, hf, ro, rh, TOL_BF16, cfg.name)
 
 
+
+@pytest.mark.parametrize("gate_dist", ["config", "long"])
+def test_gdn_million_token_sequence_window(gate_dist):
+    """One slice of 2^20 + 37 tokens (16,385 chunks, the last ragged; about 500 blocks and a pass
+    over blocks spanning eight 64-flag groups): token offsets and block indices far beyond the
+    other workloads'. The whole sequence runs once and its first L - W tokens once more; the
+    oracle, started from the second call's final state, recomputes the last W tokens, which must
+    match the first call's outputs there and its final state, and the two calls' outputs agree on
+    the shared prefix (their blocks split it differently)."""
+    L, W = 2 ** 20 + 37, 64 * 64 + 37
+    cfg = inputs.GDN_128K.with_(name=f"gdn_1m_{gate_dist}", H=1, L=L, seed=61, gate_dist=gate_dist)
+    say(f"case {cfg.name}: inputs")
+    s = inputs.prefill_slice(cfg, 0, 0)
+    dt = TD[cfg.dtype]
+    t = lambda a, d: dev_tensor(a[None, None], d)
+    q, k, v = t(s["q"], dt), t(s["k"], dt), t(s["v"], dt)
+    beta, la, h0 = t(s["beta"], torch.float32), t(s["log_alpha"], torch.float32), t(s["h0"], torch.float32)
+    say(f"case {cfg.name}: GPU, whole sequence and prefix")
+    o, hf = ops.gdn_prefill_fwd(q, k, v, beta, la, h0)
+    P = L - W
+    pre = lambda x: x[:, :, :P].contiguous()
+    o_p, h_p = ops.gdn_prefill_fwd(pre(q), pre(k), pre(v), pre(beta), pre(la), h0)
+    torch.cuda.synchronize()
+    win = lambda a: a[P:][None, None]
+    say(f"case {cfg.name}: oracle over the last {W} tokens")
+    ro, rh = oracle.gdn_prefill(win(s["q"]), win(s["k"]), win(s["v"]), win(s["beta"]), win(s["log_alpha"]),
+                                host(h_p))
+    _check(host(o[:, :, P:]), host(hf), ro, rh, TOL_BF16, f"{cfg.name} window")
+    e = max_rel_err(host(o_p), host(o[:, :, :P]))
+    say(f"  prefix outputs of the two calls: max rel diff {e:.3e}")
+    assert e <= TOL_BF16
+
 # ---------------------------------------------------------------------------------------------
 # decode
 # ---------------------------------------------------------------------------------------------
