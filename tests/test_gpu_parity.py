@@ -440,6 +440,38 @@ def test_gdn_million_token_sequence_window(gate_dist):
     say(f"  prefix outputs of the two calls: max rel diff {e:.3e}")
     assert e <= TOL_BF16
 
+
+@pytest.mark.parametrize("gated", [False, True])
+def test_linattn_million_token_sequence_window(gated):
+    """Linear attention, plain and with a per-token decay (long-memory gates), over one slice of
+    2^20 + 37 tokens: the last W tokens' outputs and the final state against the oracle started
+    from a prefix call's final state, and the two calls' prefix outputs against each other."""
+    L, W = 2 ** 20 + 37, 64 * 64 + 37
+    cfg = inputs.LINATTN_8K.with_(name=f"la_1m_{'gated' if gated else 'plain'}", B=1, H=1, L=L, seed=67,
+                                  gates=gated, gate_dist="long")
+    say(f"case {cfg.name}: inputs")
+    s = inputs.prefill_slice(cfg, 0, 0)
+    dt = TD[cfg.dtype]
+    t = lambda a, d: None if a is None else dev_tensor(a[None, None], d)
+    q, k, v = t(s["q"], dt), t(s["k"], dt), t(s["v"], dt)
+    la = t(s["log_alpha"], torch.float32)
+    say(f"case {cfg.name}: GPU, whole sequence and prefix")
+    o, hf = ops.linattn_prefill_fwd(q, k, v, None, log_alpha=la)
+    P = L - W
+    pre = lambda x: None if x is None else x[:, :, :P].contiguous()
+    o_p, h_p = ops.linattn_prefill_fwd(pre(q), pre(k), pre(v), None, log_alpha=pre(la))
+    torch.cuda.synchronize()
+    win = lambda a: a[P:][None, None]
+    say(f"case {cfg.name}: oracle over the last {W} tokens")
+    if gated:
+        ro, rh = oracle.gla_prefill(win(s["q"]), win(s["k"]), win(s["v"]), win(s["log_alpha"]), host(h_p))
+    else:
+        ro, rh = oracle.linattn_prefill(win(s["q"]), win(s["k"]), win(s["v"]), host(h_p))
+    _check(host(o[:, :, P:]), host(hf), ro, rh, TOL_BF16, f"{cfg.name} window")
+    e = max_rel_err(host(o_p), host(o[:, :, :P]))
+    say(f"  prefix outputs of the two calls: max rel diff {e:.3e}")
+    assert e <= TOL_BF16
+
 # ---------------------------------------------------------------------------------------------
 # decode
 # ---------------------------------------------------------------------------------------------
