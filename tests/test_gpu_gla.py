@@ -200,3 +200,33 @@ def test_gla_equal_gates_match_per_token_decay():
     _check(cfg.with_(name="gla_equal_gates per-dimension kernels"), o1, h1, ro, rh)
     _check(cfg.with_(name="gla_equal_gates per-token kernels"), o2, h2, ro, rh)
     assert max_rel_err(host(o1), host(o2)) <= TOL_BF16
+
+
+def test_gla_million_token_sequence_window():
+    """A gate per key dimension (long-memory gates) over one slice of 2^20 + 37 tokens: the last W
+    tokens' outputs and the final state against the oracle started from a prefix call's final
+    state, and the two calls' prefix outputs against each other."""
+    L, W = 2 ** 20 + 37, 64 * 64 + 37
+    cfg = _cfg("gla_1m", 1, 1, L, 128, "bf16", 71, gate_dist="long")
+    say(f"case {cfg.name}: inputs")
+    s = inputs.prefill_slice(cfg, 0, 0)
+    la_np = inputs.gate_vectors(cfg)[0, 0]
+    t = lambda a, d: dev_tensor(a[None, None], d)
+    q, k, v = t(s["q"], torch.bfloat16), t(s["k"], torch.bfloat16), t(s["v"], torch.bfloat16)
+    la = t(la_np, torch.float32)
+    h0 = t(s["h0"], torch.float32)
+    say(f"case {cfg.name}: GPU, whole sequence and prefix")
+    o, hf = ops.gla_prefill_fwd(q, k, v, la, h0)
+    P = L - W
+    pre = lambda x: x[:, :, :P].contiguous()
+    o_p, h_p = ops.gla_prefill_fwd(pre(q), pre(k), pre(v), pre(la), h0)
+    torch.cuda.synchronize()
+    win = lambda a: a[P:][None, None]
+    say(f"case {cfg.name}: oracle over the last {W} tokens")
+    ro, rh = oracle.gla_vec_prefill(win(s["q"]), win(s["k"]), win(s["v"]), win(la_np), host(h_p))
+    eo, eh = max_rel_err(host(o[:, :, P:]), ro), max_rel_err(host(hf), rh)
+    say(f"  window: max rel err o {eo:.3e}, h_final {eh:.3e}")
+    assert eo <= TOL_BF16 and eh <= TOL_BF16
+    e = max_rel_err(host(o_p), host(o[:, :, :P]))
+    say(f"  prefix outputs of the two calls: max rel diff {e:.3e}")
+    assert e <= TOL_BF16
