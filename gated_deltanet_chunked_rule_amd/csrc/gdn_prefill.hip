@@ -36,7 +36,8 @@
 // A log gate of -inf (a zero gate) clears the state before its token's write. Cumulative sums
 // then cannot be differenced, so each token also carries the index of the last zero gate at or
 // before it: exp(g_r - g_s) is taken over the finite gates only, and is zero when a zero gate
-// lies in (s, r]. Only exponentials of non-positive differences are formed.
+// lies in (s, r]. Finite log gates below -110 are taken as -110 (exp of any sum holding one is
+// exactly zero in fp32). Only exponentials of non-positive differences are formed.
 #include <atomic>
 #include <mutex>
 #include <type_traits>
@@ -210,11 +211,14 @@ __device__ __forceinline__ float exp2_hw(float x) { return __builtin_amdgcn_exp2
 
 // Gate arrays of a chunk, computed by one wave (lane = token; past the end la = 0, bt = 0).
 // The cumulative log gates are kept in log2 units, so every factor exp(g_r - g_s) is one base-2
-// exponential of a difference. upd = false (a skipped chunk of the output kernel) sets Khat's
+// exponential of a difference. A finite log gate below -110 is taken as -110: every factor whose
+// interval holds it is exactly zero in fp32 either way, and the cumulative sums stay small
+// enough to keep their precision (a gate of, say, -1e6 would leave later sums with no bits for
+// the other gates). upd = false (a skipped chunk of the output kernel) sets Khat's
 // factors e^{g_C - g} to zero, so the state update adds nothing to the decayed state.
 __device__ __forceinline__ void gate_scan(Gates* gt, float la, float bt, int lane, bool upd = true) {
     const bool zero = la == -__builtin_inff();
-    const float g = wave_scan(zero ? 0.f : la, lane) * 1.44269504088896341f;
+    const float g = wave_scan(zero ? 0.f : floor_log_gate(la), lane) * 1.44269504088896341f;
     const int rho = wave_max_scan(zero ? lane : -1, lane);
     const float gC = wave_last(g);
     const int rhoC = __builtin_amdgcn_readlane(rho, 63);

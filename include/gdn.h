@@ -95,7 +95,9 @@ int gdn_prefill_kernel_times(float *ms, int *launches);
  *   q, k        [B,H,L,Dk] dtype        v, o   [B,H,L,Dv] dtype   (may be NULL when L = 0)
  *   beta        [B,H,L] fp32            log_alpha [B,H,L] fp32 (log of the forget gate, <= 0
  *                                        in normal use; exp(log_alpha) is the gate; -inf is a
- *                                        zero gate, which clears the state before the token's write)
+ *                                        zero gate, which clears the state before the token's write;
+ *                                        a finite log gate below -110 is taken as -110, whose gate,
+ *                                        like that of any sum holding it, is exactly 0 in fp32)
  *   h0          [B,H,Dk,Dv] fp32 initial state, or NULL for zeros
  *   h_final     [B,H,Dk,Dv] fp32 final state; may equal h0 (in-place update), any other
  *               overlap is GDN_ERR_ALIAS

@@ -207,6 +207,35 @@ def test_blocks_that_forget_partway(dtype):
 
 
 @pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_very_negative_gates(dtype):
+    """Finite log gates far below the others at single tokens (-1e6, -1e3 and -200, below the
+    -110 floor; -60, above it) and a run of -30 whose sum passes -110 inside a chunk, among
+    long-memory gates, in one and several blocks: factors over an interval holding such a gate
+    are exactly zero and the later cumulative sums keep their precision. Against the oracle, which
+    forms exp(-1e6) = 0 in fp64."""
+    cfg = inputs.GDN_32K.with_(name=f"neg_gates_{dtype}", B=1, H=2, L=64 * 9 + 17, dtype=dtype, seed=49,
+                               gate_dist="long")
+    x = inputs.prefill_inputs(cfg)
+    la = x["log_alpha"].copy()
+    la[0, 0, [5, 130, 300]] = [-1e6, -1e3, -200.0]
+    la[0, 1, [64, 200]] = [-60.0, -1e6]
+    la[0, 1, 450:460] = -30.0
+    x["log_alpha"] = la
+    dt = TD[dtype]
+    q, k, v = (dev_tensor(x[n], dt) for n in ("q", "k", "v"))
+    h0 = dev_tensor(x["h0"], torch.float32)
+    beta, lad = dev_tensor(x["beta"], torch.float32), dev_tensor(la, torch.float32)
+    ro, rh = _oracle(x)
+    tol = TOL_BF16 if dtype == "bf16" else TOL_F32
+    for nb in (1, 4):
+        say(f"case {cfg.name}: {nb} blocks")
+        ws = prefill_workspace(torch, 1, 2, 128, nb) if nb > 1 else None
+        o, hf = ops.gdn_prefill_fwd(q, k, v, beta, lad, h0, workspace=ws)
+        torch.cuda.synchronize()
+        _check(host(o), host(hf), ro, rh, tol, f"{nb} blocks")
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
 def test_zero_gates_reset_the_state(dtype):
     """log a = -inf (a zero gate) clears the state before the token's write; the cumulative gate
     sums cannot be differenced across it. Zero gates at chunk starts, ends and inside chunks, in
