@@ -556,6 +556,15 @@ def test_decode_equals_prefill_of_one_token():
     assert max_rel_err(host(state), hf) < 1e-2
 
 
+def test_many_slices_one_block_each():
+    """B=8, H=40: 320 (batch, head) slices, more than the device has CUs, so the call takes no
+    workspace and runs one output workgroup per slice over its whole sequence (no maps, no pass
+    over blocks); sampled slices in every batch against the oracle."""
+    cfg = inputs.GDN_32K.with_(name="many_slices", B=8, H=40, L=64 * 3 + 11, seed=59)
+    say(f"case {cfg.name}")
+    o, hf, ro, rh = _full_size(cfg, [(b, (7 * b) % 40) for b in range(8)] + [(7, 39)])
+    _check(o, hf, ro, rh, TOL_BF16, cfg.name)
+
 def test_preferred_workspace_follows_the_device():
     """The preferred workspace gives about two output workgroups per CU of this device, and none
     once the (batch, head) slices alone give every CU one."""
