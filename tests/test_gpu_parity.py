@@ -540,6 +540,36 @@ def test_decode_fp32(D):
     assert eo <= TOL_F32 and eh <= TOL_F32
 
 
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_decode_extreme_gates(dtype):
+    """Decode steps where some (sequence, head) pairs take a zero gate (log a = -inf), a gate of
+    -1e6 or a gate of 0 (a = 1), beta of 0 or 1, against the oracle step by step."""
+    cfg = inputs.DECODE_256x32.with_(name=f"decode_gates_{dtype}", N=4, H=4, Dk=128, Dv=128, dtype=dtype, seed=6100)
+    dt = TD[dtype]
+    st = inputs.decode_state(cfg)
+    state = dev_tensor(st, torch.float32)
+    ref = st.copy()
+    tol = TOL_BF16 if dtype == "bf16" else TOL_F32
+    say(f"case {cfg.name}")
+    for step in range(6):
+        x = inputs.decode_token(cfg, step)
+        la, beta = x["log_alpha"].copy(), x["beta"].copy()
+        la[step % 4, 0] = -np.inf
+        la[(step + 1) % 4, 1] = -1e6
+        la[(step + 2) % 4, 2] = 0.0
+        beta[(step + 3) % 4, 3] = 0.0
+        beta[step % 4, 3] = 1.0
+        args = [dev_tensor(x[n], dt) for n in ("q", "k", "v")] + [dev_tensor(beta, torch.float32),
+                                                                 dev_tensor(la, torch.float32)]
+        o = ops.gdn_decode_step(*args, state)
+        ro, ref = oracle.gdn_decode_step(x["q"], x["k"], x["v"], beta, la, ref)
+        torch.cuda.synchronize()
+        eo = max_rel_err(host(o)[:, :, None], ro[:, :, None])
+        assert eo <= tol, (step, eo)
+    eh = max_rel_err(host(state), ref)
+    say(f"  state after 6 steps: max rel err {eh:.3e}")
+    assert eh <= tol
+
 def test_decode_equals_prefill_of_one_token():
     cfg = inputs.GDN_32K.with_(name="one_token", B=1, H=4, L=1, seed=9)
     x = inputs.prefill_inputs(cfg)
