@@ -56,10 +56,36 @@ struct LaCfg {
     static constexpr size_t KF = (size_t)NDT * NKT * 1024;              // Khat^T fragments
     static constexpr size_t PF = (size_t)4 * NKT * 1024;                // P^T fragments
     static constexpr size_t LDS_KV = 2 * ROWS + KF + CH * 4;
-    static constexpr size_t LDS_OUT = 3 * ROWS + KF + PF + 3 * CH * 4;
+    static constexpr size_t LDS_OUT = 3 * ROWS + KF + PF + 4 * CH * 4;
     // register prefetch of the next chunk's rows only where it fits beside the fp32 fragments
     static constexpr bool PREF = sizeof(T) == 2;
 };
+
+// Inclusive prefix sum over the 64 lanes of a wave carried as an unevaluated sum hi + lo (the
+// return value and `lo`): every step adds exactly (the rounding error of each fp32 addition is
+// recovered and carried in lo), so a difference of two prefix sums formed as
+// (hi_r - hi_s) + (lo_r - lo_s) keeps fp32 precision relative to the difference even where the
+// sums themselves are large (strong decay: a chunk's log gates summing to -10^3).
+__device__ __forceinline__ float wave_scan2(float x, float& lo) {
+    float hi = x;
+    lo = 0.f;
+    auto add = [&](float h2, float l2) {   // (hi, lo) += (h2, l2), hi + h2 exactly
+        const float s = hi + h2, bb = s - hi, e = (hi - (s - bb)) + (h2 - bb);
+        lo = lo + l2 + e;
+        hi = s;
+    };
+#define GDN_SCAN2_STEP(CTRL, MASK)                                                                     \
+    add(__builtin_bit_cast(float, dpp_move<CTRL, MASK>(__builtin_bit_cast(int, hi), 0)),              \
+        __builtin_bit_cast(float, dpp_move<CTRL, MASK>(__builtin_bit_cast(int, lo), 0)));
+    GDN_SCAN2_STEP(0x111, 0xF)   // row_shr:1
+    GDN_SCAN2_STEP(0x112, 0xF)   // row_shr:2
+    GDN_SCAN2_STEP(0x114, 0xF)   // row_shr:4
+    GDN_SCAN2_STEP(0x118, 0xF)   // row_shr:8
+    GDN_SCAN2_STEP(0x142, 0xA)   // row_bcast:15
+    GDN_SCAN2_STEP(0x143, 0xC)   // row_bcast:31
+#undef GDN_SCAN2_STEP
+    return hi;
+}
 
 // transposed 16 x 16 tiles of d-tile dt of the rows R (row stride KP): lane (j, n) of t[st]
 // holds R[16 st + 4 j + e][16 dt + n]
@@ -125,10 +151,11 @@ __global__ __launch_bounds__(256) void la_kv_kernel(const typename E::T* __restr
             rv.load(v + tok1 * D, rows_of(c + 1), tid);
         }
         float gC = 0.f;
-        if constexpr (GATED) {
-            const float g = wave_scan(la, lane);
+        if constexpr (GATED) {   // fp32 inputs: sums as exact hi + lo pairs (see wave_scan2)
+            float glo = 0.f;
+            const float g = sizeof(T) == 4 ? wave_scan2(la, glo) : wave_scan(la, lane);
             gC = wave_last(g);
-            if (w == 0) skh[lane] = __expf(gC - g);
+            if (w == 0) skh[lane] = __expf(sizeof(T) == 4 ? (gC - g) + (wave_last(glo) - glo) : gC - g);
         }
         lds_sync();
         // this wave's key tiles -> Khat^T fragments in LDS; its value tiles -> V fragments
@@ -234,6 +261,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void l
     float* sg = reinterpret_cast<float*>(sPf + C::PF);                            // g
     float* seg = sg + CH;                                                         // e^g
     float* skh = seg + CH;                                                        // e^{g_C - g}
+    float* slo = skh + CH;                                                        // g's low part
 
     const int blk = blockIdx.x, bh = blockIdx.y;
     const int tid = threadIdx.x, lane = tid & 63, j = lane >> 4, m = lane & 15;
@@ -270,15 +298,20 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void l
         rq.store(Qr, n, tid);
         rk.store(Kr, n, tid);
         rv.store(Vr, n, tid);
-        if (C::PREF && c + 1 < c_end) load_rows(c + 1);
         float gC = 0.f;
+        if (C::PREF && c + 1 < c_end) load_rows(c + 1);
         if constexpr (GATED) {
-            const float g = wave_scan(la, lane);
+            // fp32 inputs, whose bound is tight: the sums as exact hi + lo pairs, so that their
+            // differences keep fp32 precision where the sums are large (see wave_scan2)
+            constexpr bool PAIR = sizeof(T) == 4;
+            float glo = 0.f;
+            const float g = PAIR ? wave_scan2(la, glo) : wave_scan(la, lane);
             gC = wave_last(g);
             if (w == 0) {
                 sg[lane] = g;
-                seg[lane] = __expf(g);
-                skh[lane] = __expf(gC - g);
+                if constexpr (PAIR) slo[lane] = glo;
+                seg[lane] = __expf(PAIR ? g + glo : g);
+                skh[lane] = __expf(PAIR ? (gC - g) + (wave_last(glo) - glo) : gC - g);
             }
         }
         lds_sync();
@@ -319,11 +352,12 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void l
                         t[st] = M::mma(row_frag_raw<E>(Kr + (16 * st + m) * KP, kd * KB, j),
                                        row_frag_raw<E>(Qr + (16 * w + m) * KP, kd * KB, j), t[st]);
                     const int r = 16 * w + m;
-                    const float gr = GATED ? sg[r] : 0.f;
+                    const float gr = GATED ? sg[r] : 0.f, grl = GATED && sizeof(T) == 4 ? slo[r] : 0.f;
 #pragma unroll
                     for (int e = 0; e < 4; ++e) {
                         const int s = 16 * st + 4 * j + e;
-                        const float x = GATED ? t[st][e] * __expf(s <= r ? gr - sg[s] : 0.f) : t[st][e];
+                        const float d = sizeof(T) == 4 ? (gr - sg[s]) + (grl - slo[s]) : gr - sg[s];
+                        const float x = GATED ? t[st][e] * __expf(s <= r ? d : 0.f) : t[st][e];
                         t[st][e] = s <= r ? x : 0.f;
                     }
                 }

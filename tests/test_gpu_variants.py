@@ -102,6 +102,23 @@ def test_gated_linattn_closed_gates(dtype):
         _check(host(o), host(hf), ro, rh, TOL_BF16 if dtype == "bf16" else TOL_F32, f"{cfg.name} ws={nbytes}")
 
 
+@pytest.mark.parametrize("B,H,L,D,seed", [(2, 3, 1468, 128, 9216), (1, 35, 122, 64, 10347)])
+def test_gated_linattn_strong_decay_fp32(B, H, L, D, seed):
+    """Per-token gates of -U(0, 40) throughout, fp32: a chunk's cumulative log gates reach about
+    -1,300, where one fp32 ulp is about 1e-4, so plain differences of them put the final state
+    just past the 1e-4 bound (1.1e-4 on these inputs); the kernels carry each sum as an exact
+    hi + lo pair and keep the differences precise."""
+    cfg = inputs.GDN_32K.with_(name=f"la_strong_f32_B{B}H{H}L{L}d{D}", B=B, H=H, L=L, Dk=D, Dv=D, dtype="f32",
+                               seed=seed, gate_dist="very_strong", h0=0.1)
+    say(f"case {cfg.name}")
+    x = inputs.prefill_inputs(cfg)
+    q, k, v = (dev_tensor(x[n], torch.float32) for n in ("q", "k", "v"))
+    h0 = dev_tensor(x["h0"], torch.float32)
+    ro, rh = oracle.gla_prefill(x["q"], x["k"], x["v"], x["log_alpha"], x["h0"])
+    o, hf = ops.linattn_prefill_fwd(q, k, v, h0, log_alpha=dev_tensor(x["log_alpha"], torch.float32))
+    torch.cuda.synchronize()
+    _check(host(o), host(hf), ro, rh, TOL_F32, cfg.name)
+
 def test_gated_linattn_full_size_sampled_heads():
     """The linear-attention workload's shape (B=4, H=16, L=8192) with long-memory gates."""
     cfg = inputs.LINATTN_8K
