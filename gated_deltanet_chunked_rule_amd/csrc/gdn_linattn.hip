@@ -61,32 +61,6 @@ struct LaCfg {
     static constexpr bool PREF = sizeof(T) == 2;
 };
 
-// Inclusive prefix sum over the 64 lanes of a wave carried as an unevaluated sum hi + lo (the
-// return value and `lo`): every step adds exactly (the rounding error of each fp32 addition is
-// recovered and carried in lo), so a difference of two prefix sums formed as
-// (hi_r - hi_s) + (lo_r - lo_s) keeps fp32 precision relative to the difference even where the
-// sums themselves are large (strong decay: a chunk's log gates summing to -10^3).
-__device__ __forceinline__ float wave_scan2(float x, float& lo) {
-    float hi = x;
-    lo = 0.f;
-    auto add = [&](float h2, float l2) {   // (hi, lo) += (h2, l2), hi + h2 exactly
-        const float s = hi + h2, bb = s - hi, e = (hi - (s - bb)) + (h2 - bb);
-        lo = lo + l2 + e;
-        hi = s;
-    };
-#define GDN_SCAN2_STEP(CTRL, MASK)                                                                     \
-    add(__builtin_bit_cast(float, dpp_move<CTRL, MASK>(__builtin_bit_cast(int, hi), 0)),              \
-        __builtin_bit_cast(float, dpp_move<CTRL, MASK>(__builtin_bit_cast(int, lo), 0)));
-    GDN_SCAN2_STEP(0x111, 0xF)   // row_shr:1
-    GDN_SCAN2_STEP(0x112, 0xF)   // row_shr:2
-    GDN_SCAN2_STEP(0x114, 0xF)   // row_shr:4
-    GDN_SCAN2_STEP(0x118, 0xF)   // row_shr:8
-    GDN_SCAN2_STEP(0x142, 0xA)   // row_bcast:15
-    GDN_SCAN2_STEP(0x143, 0xC)   // row_bcast:31
-#undef GDN_SCAN2_STEP
-    return hi;
-}
-
 // transposed 16 x 16 tiles of d-tile dt of the rows R (row stride KP): lane (j, n) of t[st]
 // holds R[16 st + 4 j + e][16 dt + n]
 template <int D, class E>

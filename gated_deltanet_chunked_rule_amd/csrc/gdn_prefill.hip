@@ -116,6 +116,15 @@ struct Gates {
     float pad[3];
 };
 
+// fp32 inputs, whose bound is tight: the cumulative log gates also carry their low parts (g + glo
+// is the exact prefix sum, see wave_scan2), so that differences of them keep fp32 precision where
+// the sums themselves are large (strong decay: a chunk's log gates summing to -10^3)
+struct GatesLo : Gates {
+    float glo[CH];
+};
+template <class E>
+using GatesOf = std::conditional_t<sizeof(typename E::T) == 4, GatesLo, Gates>;
+
 // LDS of a workgroup of the map (OUT = false) or output (OUT = true) kernel:
 //   OUT:  Q rows | K rows, then T | V rows, then A, then -W fragments | Khat^T fragments |
 //         P^T fragments | gates of two chunks (the current one and the next, by chunk parity)
@@ -132,7 +141,7 @@ struct Lds {
     static constexpr size_t O_P = O_KH + (size_t)C::NDT * C::NKT * C::FR;   // OUT: P^T fragments [rt][kt]
     static constexpr size_t O_UT = 3 * REG;                    // map: Ut fragments [kt][vt]
     static constexpr size_t O_G = OUT ? O_P + (size_t)4 * C::NKT * C::FR : O_UT + (size_t)C::NKT * C::NDT * C::FR;
-    static constexpr size_t GSZ = up16(sizeof(Gates));
+    static constexpr size_t GSZ = up16(sizeof(GatesOf<E>));
     static constexpr size_t BYTES = O_G + (OUT ? 2 : 1) * GSZ;
     static_assert(BYTES <= 160 * 1024, "LDS");
 };
@@ -216,20 +225,42 @@ __device__ __forceinline__ float exp2_hw(float x) { return __builtin_amdgcn_exp2
 // enough to keep their precision (a gate of, say, -1e6 would leave later sums with no bits for
 // the other gates). upd = false (a skipped chunk of the output kernel) sets Khat's
 // factors e^{g_C - g} to zero, so the state update adds nothing to the decayed state.
-__device__ __forceinline__ void gate_scan(Gates* gt, float la, float bt, int lane, bool upd = true) {
+template <class G>
+__device__ __forceinline__ void gate_scan(G* gt, float la, float bt, int lane, bool upd = true) {
+    constexpr float LOG2E = 1.44269504088896341f;
     const bool zero = la == -__builtin_inff();
-    const float g = wave_scan(zero ? 0.f : floor_log_gate(la), lane) * 1.44269504088896341f;
-    const int rho = wave_max_scan(zero ? lane : -1, lane);
-    const float gC = wave_last(g);
-    const int rhoC = __builtin_amdgcn_readlane(rho, 63);
-    const float eg = rho < 0 ? exp2_hw(g) : 0.f;
-    gt->g[lane] = g;
-    gt->rho[lane] = rho;
-    gt->b[lane] = bt;
-    gt->nbe[lane] = -bt * eg;
-    gt->kh[lane] = upd && rhoC <= lane ? exp2_hw(gC - g) : 0.f;
-    gt->eg[lane] = eg;
-    if (lane == 0) gt->dec = rhoC < 0 ? exp2_hw(gC) : 0.f;
+    if constexpr (std::is_same<G, GatesLo>::value) {
+        // g + lo exactly; scaled to log2 units with the product's rounding error kept in lo
+        float lo;
+        const float gn = wave_scan2(zero ? 0.f : floor_log_gate(la), lo);
+        const float g = gn * LOG2E;
+        lo = __builtin_fmaf(lo, LOG2E, __builtin_fmaf(gn, LOG2E, -g));
+        const int rho = wave_max_scan(zero ? lane : -1, lane);
+        const float gC = wave_last(g), gClo = wave_last(lo);
+        const int rhoC = __builtin_amdgcn_readlane(rho, 63);
+        const float eg = rho < 0 ? exp2_hw(g + lo) : 0.f;
+        gt->g[lane] = g;
+        gt->glo[lane] = lo;
+        gt->rho[lane] = rho;
+        gt->b[lane] = bt;
+        gt->nbe[lane] = -bt * eg;
+        gt->kh[lane] = upd && rhoC <= lane ? exp2_hw((gC - g) + (gClo - lo)) : 0.f;
+        gt->eg[lane] = eg;
+        if (lane == 0) gt->dec = rhoC < 0 ? exp2_hw(gC + gClo) : 0.f;
+    } else {
+        const float g = wave_scan(zero ? 0.f : floor_log_gate(la), lane) * LOG2E;
+        const int rho = wave_max_scan(zero ? lane : -1, lane);
+        const float gC = wave_last(g);
+        const int rhoC = __builtin_amdgcn_readlane(rho, 63);
+        const float eg = rho < 0 ? exp2_hw(g) : 0.f;
+        gt->g[lane] = g;
+        gt->rho[lane] = rho;
+        gt->b[lane] = bt;
+        gt->nbe[lane] = -bt * eg;
+        gt->kh[lane] = upd && rhoC <= lane ? exp2_hw(gC - g) : 0.f;
+        gt->eg[lane] = eg;
+        if (lane == 0) gt->dec = rhoC < 0 ? exp2_hw(gC) : 0.f;
+    }
 }
 
 // The part of an operand fragment that one 16 x 16 accumulator tile fills: elements 4 h .. 4 h + 3
@@ -443,7 +474,7 @@ __device__ __forceinline__ bf16x8 v_unit_cols(int j, int n, int q) {
 // are `gt`. The last wave has no block of T to form in the step after the diagonal substitution
 // and runs `side()` there instead (work of its own that touches none of the solve's LDS).
 template <int D, class E, bool OUT, int NW, class Side>
-__device__ __forceinline__ void intra_solve(unsigned char* smem, const Gates* gt, int band, int w, int lane, Side&& side,
+__device__ __forceinline__ void intra_solve(unsigned char* smem, const GatesOf<E>* gt, int band, int w, int lane, Side&& side,
                                             const typename MM<E>::frag (&vf)[Fetch<D, E, OUT, NW>::NGW][4],
                                             typename MM<E>::frag (&kbe)[Cfg<D, E, NW>::VPW][Cfg<D, E, NW>::NKT],
                                             typename MM<E>::frag (&vb)[Cfg<D, E, NW>::VPW][Cfg<D, E, NW>::NKT]) {
@@ -483,6 +514,8 @@ __device__ __forceinline__ void intra_solve(unsigned char* smem, const Gates* gt
     const int rhow = gt->rho[16 * rw + m];
     const float grm = gt->g[16 * rp + m];
     const int rhom = gt->rho[16 * rp + m];
+    // fp32 inputs: the exponents g_r - g_s of the gate factors with the sums' low parts
+    constexpr bool LO = std::is_same<GatesOf<E>, GatesLo>::value;
     f32x4 pt[4];
 #pragma unroll
     for (int i = 0; i < NST; ++i) {
@@ -507,7 +540,12 @@ __device__ __forceinline__ void intra_solve(unsigned char* smem, const Gates* gt
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
                 const int s = 16 * st + 4 * j + e;
-                av[e] = (s < r && s >= rhow) ? brw * exp2_hw(grw - gs[e]) * g[e] : 0.f;
+                if constexpr (LO) {
+                    const float d = (grw - gs[e]) + (gt->glo[r] - gt->glo[s]);
+                    av[e] = (s < r && s >= rhow) ? brw * exp2_hw(d) * g[e] : 0.f;
+                } else {
+                    av[e] = (s < r && s >= rhow) ? brw * exp2_hw(grw - gs[e]) * g[e] : 0.f;
+                }
             }
             *reinterpret_cast<float4*>(Am + r * AS + 16 * st + 4 * j) = make_float4(av[0], av[1], av[2], av[3]);
         }
@@ -523,7 +561,12 @@ __device__ __forceinline__ void intra_solve(unsigned char* smem, const Gates* gt
 #pragma unroll
                 for (int e = 0; e < 4; ++e) {
                     const int s2 = 16 * st + 4 * j + e, r = 16 * rp + m;
-                    pt[i][e] = (s2 <= r && s2 >= rhom) ? exp2_hw(grm - gs[e]) * p[e] : 0.f;
+                    if constexpr (LO) {
+                        const float d = (grm - gs[e]) + (gt->glo[r] - gt->glo[s2]);
+                        pt[i][e] = (s2 <= r && s2 >= rhom) ? exp2_hw(d) * p[e] : 0.f;
+                    } else {
+                        pt[i][e] = (s2 <= r && s2 >= rhom) ? exp2_hw(grm - gs[e]) * p[e] : 0.f;
+                    }
                 }
             }
         }
@@ -727,7 +770,7 @@ __global__ __launch_bounds__(512) void map_kernel(PrefArgs a) {
         const int lane = opaque(threadIdx.x & 63), j = lane >> 4, m = lane & 15, htid = 64 * hw + lane;
         const int mine = c - half;                     // this half's chunk (scalar)
         T* Kr = reinterpret_cast<T*>(my + L::O_K);
-        Gates* gt = reinterpret_cast<Gates*>(my + L::O_G);
+        GatesOf<E>* gt = reinterpret_cast<GatesOf<E>*>(my + L::O_G);
         if (mine >= c0) {
             if (keep) fx.rk.store(Kr, fx.n, htid);
             if (hw == 0) gate_scan(gt, fx.la, fx.bt, lane);
@@ -1066,8 +1109,8 @@ __global__ __launch_bounds__(512) void out_kernel(PrefArgs a) {
         const int tid = 64 * w + opaque(threadIdx.x & 63), lane = tid & 63, j = lane >> 4, m = lane & 15;
         const int n = fx.n;
         // the gate arrays of chunk c and of chunk c + 1 (two LDS slots by chunk parity)
-        Gates* gt = reinterpret_cast<Gates*>(smem + L::O_G + (size_t)((c - c0) & 1) * L::GSZ);
-        Gates* gn = reinterpret_cast<Gates*>(smem + L::O_G + (size_t)((c - c0 + 1) & 1) * L::GSZ);
+        GatesOf<E>* gt = reinterpret_cast<GatesOf<E>*>(smem + L::O_G + (size_t)((c - c0) & 1) * L::GSZ);
+        GatesOf<E>* gn = reinterpret_cast<GatesOf<E>*>(smem + L::O_G + (size_t)((c - c0 + 1) & 1) * L::GSZ);
         fx.rq.store(Qr, n, tid);
         fx.rk.store(Kr, n, tid);
         // the first chunk's gates are scanned here; every later chunk's during the solve of the

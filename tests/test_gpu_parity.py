@@ -235,6 +235,35 @@ def test_very_negative_gates(dtype):
         _check(host(o), host(hf), ro, rh, tol, f"{nb} blocks")
 
 
+@pytest.mark.parametrize("B,H,L,D,seed,h0", [(1, 2, 118, 64, 9026, None), (2, 1, 104, 128, 9784, 0.1),
+                                               (2, 2, 64 * 12 + 31, 64, 10023, 0.1)])
+def test_strong_decay_fp32(B, H, L, D, seed, h0):
+    """Per-token gates of -U(0, 40), fp32 inputs: a chunk's cumulative log gates reach about
+    -1,300, where one fp32 ulp is about 1e-4, so plain differences of them carried the final state
+    or the outputs past the 1e-4 bound (1.1e-4 to 1.5e-4 on these inputs, found by a random
+    sweep); the kernels keep each sum as an exact hi + lo pair for fp32 inputs. Dense in one and
+    several blocks, and the block-adjacent solve at bands 1 and 2."""
+    cfg = inputs.GDN_32K.with_(name=f"strong_f32_B{B}H{H}L{L}d{D}", B=B, H=H, L=L, Dk=D, Dv=D, dtype="f32",
+                               seed=seed, gate_dist="very_strong", h0=h0)
+    x = inputs.prefill_inputs(cfg)
+    q, k, v = (dev_tensor(x[n], torch.float32) for n in ("q", "k", "v"))
+    hd = dev_tensor(x["h0"], torch.float32) if h0 is not None else None
+    beta, la = dev_tensor(x["beta"], torch.float32), dev_tensor(x["log_alpha"], torch.float32)
+    ro, rh = _oracle(x)
+    for nb in (1, 3):
+        say(f"case {cfg.name}: {nb} blocks")
+        ws = prefill_workspace(torch, B, H, D, nb) if nb > 1 else None
+        o, hf = ops.gdn_prefill_fwd(q, k, v, beta, la, hd, workspace=ws)
+        torch.cuda.synchronize()
+        _check(host(o), host(hf), ro, rh, TOL_F32, f"{nb} blocks")
+    for band in (1, 2):
+        say(f"case {cfg.name}: band {band}")
+        o, hf = ops.gdn_prefill_banded_fwd(q, k, v, beta, la, hd, band=band)
+        torch.cuda.synchronize()
+        bo, bh = oracle.gdn_prefill_banded(x["q"], x["k"], x["v"], x["beta"], x["log_alpha"], x["h0"], band=band)
+        _check(host(o), host(hf), bo, bh, TOL_F32, f"band {band}")
+
+
 @pytest.mark.parametrize("dtype", ["bf16", "f32"])
 def test_zero_gates_reset_the_state(dtype):
     """log a = -inf (a zero gate) clears the state before the token's write; the cumulative gate
