@@ -31,7 +31,7 @@ def band_mask(n: int, band: int, block: int = 16) -> np.ndarray:
 def chunk_inverse(k, beta, g, band: int = 3, block: int = 16):
     """T = (I + A)^-1 of one chunk with blocks beyond `band` below the diagonal set to zero."""
     n = len(beta)
-    gamma = np.exp(g[:, None] - g[None, :])
+    gamma = np.exp(np.minimum(g[:, None] - g[None, :], 0.0))   # only s <= r is kept below (exponent <= 0)
     A = np.tril(beta[:, None] * gamma * (k @ k.T), -1)
     T = np.linalg.inv(np.eye(n) + A)
     return np.where(band_mask(n, band, block), T, 0.0), A
@@ -55,7 +55,7 @@ def gdn_prefill_banded(q, k, v, beta, log_alpha, h0=None, band: int = 3, chunk: 
                 T, _ = chunk_inverse(kc, bc, g, band, block)
                 W = T @ ((bc * np.exp(g))[:, None] * kc)
                 U = T @ (bc[:, None] * vc) - W @ H
-                P = np.tril(qc @ kc.T) * np.tril(np.exp(g[:, None] - g[None, :]))
+                P = np.tril(qc @ kc.T) * np.tril(np.exp(np.minimum(g[:, None] - g[None, :], 0.0)))
                 o[b, h, sl] = np.exp(g)[:, None] * (qc @ H) + P @ U
                 H = np.exp(g[-1]) * H + (np.exp(g[-1] - g)[:, None] * kc).T @ U
             hf[b, h] = H
