@@ -238,3 +238,31 @@ def test_gla_host_validation(lib):
     assert f(1, 1, 64, 128, 128, 0) == blk
     assert f(2, 2, 64 * 1000, 64, 64, 1) % (4 * (64 * 64 * 4 + 64 * 4)) == 0
     assert f(1, 1, 0, 128, 128, 0) == 0 and f(1, 1, 64, 96, 96, 0) == 0
+
+
+# HIP runtime calls the library may make. Kernel launches, their error check, device queries,
+# kernel attributes and the scratch's device address; events only for the opt-in per-kernel timing
+# (gdn_prefill_timing) and its query. No allocation, free, memset, copy or stream/device
+# synchronisation: a call records only kernel launches on the caller's stream, so it can be
+# captured into a HIP graph and needs no memory of its own.
+HIP_CALLS_ALLOWED = {
+    "hipLaunchKernelGGL", "hipGetLastError", "hipGetDevice", "hipGetDeviceProperties", "hipDeviceGetAttribute",
+    "hipFuncSetAttribute", "hipGetSymbolAddress",
+    "hipEventCreate", "hipEventRecord", "hipEventSynchronize", "hipEventElapsedTime",
+}
+
+
+def test_library_makes_only_launch_query_and_timing_calls():
+    csrc = os.path.join(ROOT, "gated_deltanet_chunked_rule_amd", "csrc")
+    used = {}
+    for name in sorted(os.listdir(csrc)):
+        text = open(os.path.join(csrc, name)).read()
+        text = re.sub(r"//[^\n]*|/\*.*?\*/", "", text, flags=re.S)
+        for call in re.findall(r"\b(hip[A-Z]\w*)\s*\(", text):
+            used.setdefault(call, set()).add(name)
+    assert "hipLaunchKernelGGL" in used
+    extra = {c: sorted(f) for c, f in used.items() if c not in HIP_CALLS_ALLOWED}
+    assert not extra, f"HIP calls outside the allowed set: {extra}"
+    # the events belong to the timing switch in the prefill's launch code only
+    for c in ("hipEventCreate", "hipEventRecord", "hipEventSynchronize", "hipEventElapsedTime"):
+        assert used.get(c, {"gdn_prefill.hip"}) == {"gdn_prefill.hip"}, c
