@@ -83,3 +83,29 @@ def test_slices_beyond_two_to_the_31_elements(kind):
     say(f"  last slice window: max rel err o {eo:.3e}, h_final {eh:.3e} (bound {TOL_BF16:g})")
     assert eo <= TOL_BF16 and eh <= TOL_BF16
     torch.cuda.empty_cache()
+
+
+def test_bidirectional_slices_beyond_two_to_the_31_elements():
+    """Bidirectional linear attention (elu + 1, normalised) on the same 17 identical slices: every
+    slice's outputs and KV equal the first slice's bit for bit, and the last slice's outputs and KV
+    match the oracle over the whole slice."""
+    cfg = inputs.LINATTN_8K.with_(name="large_offsets_bidir", B=1, H=1, L=L, seed=83, qk="raw")
+    say(f"case {cfg.name}: inputs (one slice, repeated {H} times on the device)")
+    s = inputs.prefill_slice(cfg, 0, 0)
+    rep = lambda a: dev_tensor(a[None, None], BF).expand(1, H, L, D).contiguous()
+    q, k, v = rep(s["q"]), rep(s["k"]), rep(s["v"])
+    say(f"case {cfg.name}: GPU, {H} slices of {L} tokens")
+    o, kv = ops.linattn_bidir_fwd(q, k, v, normalize=True, elu1=True, kv_out=True)
+    torch.cuda.synchronize()
+    del q, k, v
+    for h in range(1, H):
+        assert torch.equal(o[0, h], o[0, 0]), f"slice {h} outputs differ from slice 0"
+        assert torch.equal(kv[0, h], kv[0, 0]), f"slice {h} KV differs from slice 0"
+    say(f"case {cfg.name}: oracle over the last slice ({L} tokens)")
+    ro, rkv = oracle.linattn_bidir(s["q"][None, None], s["k"][None, None], s["v"][None, None], normalize=True,
+                                   elu1=True)
+    eo, ekv = max_rel_err(host(o[:, H - 1:]), ro), max_rel_err(host(kv[:, H - 1:]), rkv)
+    say(f"  last slice: max rel err o {eo:.3e}, KV {ekv:.3e} (bound {TOL_BF16:g})")
+    assert eo <= TOL_BF16 and ekv <= TOL_BF16
+    del o, kv
+    torch.cuda.empty_cache()
