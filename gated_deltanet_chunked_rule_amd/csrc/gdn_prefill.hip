@@ -230,7 +230,12 @@ __device__ __forceinline__ void gate_scan(G* gt, float la, float bt, int lane, b
     constexpr float LOG2E = 1.44269504088896341f;
     const bool zero = la == -__builtin_inff();
     if constexpr (std::is_same<G, GatesLo>::value) {
-        // g + lo exactly; scaled to log2 units with the product's rounding error kept in lo
+        // g + lo exactly; scaled to log2 units with the product's rounding error kept in lo. No
+        // contraction here: fused into a later subtraction (gC - g as fma(-gn, LOG2E, gC)), the
+        // product would enter unrounded where the pair's bookkeeping assumes the rounded g, and
+        // e^{g_C - g_s} would be off by up to half an ulp of the sums (e.g. 7.5e-5 for the last
+        // token's own factor, which must be exactly 1, where a chunk's sums reach 10^3).
+#pragma clang fp contract(off)
         float lo;
         const float gn = wave_scan2(zero ? 0.f : floor_log_gate(la), lo);
         const float g = gn * LOG2E;
