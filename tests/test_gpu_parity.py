@@ -632,3 +632,23 @@ def test_preferred_workspace_follows_the_device():
     flags = ((nb - 1) * 4 + 255) // 256 * 256
     assert ops.prefill_workspace_size(1, 16, 131072, 128, torch.bfloat16) == 16 * ((2 * nb - 1) * 4 * 128 * 128 + flags)
     assert ops.prefill_workspace_size(1, cus, 4096, 128, torch.bfloat16) == 0
+
+
+def test_fp32_gate_factors_exact_under_strong_decay():
+    """One chunk of 64 tokens with log a ~ -U(0, 40) and beta zero before the last token: the final
+    state is then beta_C k_C v_C^T (key-major) and every gate factor that reaches it is e^0 = 1.
+    fp32 inputs must give it to rounding (bound 1e-5, ten times under the fp32 path's 1e-4):
+    cumulative gate sums of ~10^3 kept as exact hi + lo pairs leave that factor exactly 1, but one
+    unrounded product inside the pair's bookkeeping (floating-point contraction) made it
+    e^{+-half an ulp of the sums}, 7.5e-5 off."""
+    cfg = inputs.GDN_32K.with_(name="fp32_last_token_factor", B=1, H=3, L=64, dtype="f32", seed=9354,
+                               gate_dist="very_strong", h0=None)
+    x = inputs.prefill_inputs(cfg)
+    beta = x["beta"].copy()
+    beta[..., :-1] = 0.0
+    say(f"case {cfg.name}")
+    d = {n: dev_tensor(x[n], torch.float32) for n in ("q", "k", "v", "log_alpha")}
+    o, hf = ops.gdn_prefill_fwd(d["q"], d["k"], d["v"], dev_tensor(beta, torch.float32), d["log_alpha"], None)
+    torch.cuda.synchronize()
+    ro, rh = oracle.gdn_prefill(x["q"], x["k"], x["v"], beta, x["log_alpha"], None)
+    _check(host(o), host(hf), ro, rh, 1e-5, cfg.name)
